@@ -1,0 +1,171 @@
+/*
+ * poetx.h -- C ABI of libpoetx, the POET-X linear layer on AMD MI355X (gfx950).
+ *
+ * The layer (POET-X summary page, Method §1, eq. 3, input-centric form) is
+ *
+ *     z = G_P^T ( W' ( G_R^T x ) )
+ *
+ * where W' is the frozen weight with the two weight-side permutations merged
+ * in (Method §2), and G_R, G_P are block-diagonal with b x b blocks built by
+ * the Cayley-Neumann parameterization (Method §4, eq. 9)
+ *
+ *     G = I + 2 (Q + Q^2 + Q^2.Q) + Q^2.Q^2,   Q skew,
+ *
+ * each Q stored as its packed strict upper triangle (b(b-1)/2 floats).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Layouts are row-major and contiguous.  Activations are token-major:
+ *    x[N][d_in], z[N][d_out].  The weight is w[d_out][d_in] (torch nn.Linear).
+ *    Block j of G_R covers input features [j*b, (j+1)*b) of the permuted
+ *    input; G_R is stored g_r[n_R][b][b] with g_r[j][r][c] the (r, c) entry
+ *    of block j (n_R = d_in / b, n_P = d_out / b).
+ *  - Packed theta: theta[j][k] = Q_j[r][c] for r < c, k running row-major over
+ *    the strict upper triangle; Q_j[c][r] = -theta[j][k].
+ *  - Token-major form of the layer, with Gather(x)[i] = x[perm_in[i]] and
+ *    Scatter(y)[perm_out[i]] = y[i]:
+ *        A = Gather(X) . Diag(G_R)        (a = G_R^T x, Method §5)
+ *        B = A . W'^T                     (b = W' a)
+ *        Z = Scatter(B . Diag(G_P))       (z = G_P^T b)
+ *    perm_in / perm_out may be NULL (identity): then the call is exactly the
+ *    three-product chain above with no activation permutation.
+ *  - All pointers are DEVICE pointers unless marked [host].  Device pointers
+ *    must be 16-byte aligned.  The caller owns every buffer; the library never
+ *    allocates or frees device memory.  Inputs are read-only, outputs are
+ *    overwritten (never accumulated into); inputs and outputs must not alias.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL = the default stream) and never synchronizes.
+ *  - Workspace: calls taking (ws, ws_bytes) report the bytes they need when
+ *    called with ws == NULL (writing *ws_bytes, launching nothing).  With
+ *    ws != NULL, *ws_bytes below the requirement is POETX_ERR_WORKSPACE.
+ *  - Errors: arguments are validated on the host before any launch; on a
+ *    validation error nothing is launched and outputs are untouched.  A failed
+ *    launch returns POETX_ERR_HIP; faults during execution surface at the
+ *    caller's next synchronization.  poetx_status_string() names a code.
+ *  - Supported block sizes: b in {2..512} with b | d_in and b | d_out and
+ *    b % 16 == 0 for bf16 layers; any b >= 2 dividing the widths for fp32.
+ */
+#ifndef POETX_H
+#define POETX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  POETX_OK = 0,
+  POETX_ERR_INVALID_ARG = -1, /* NULL where a buffer is required, bad enum, n < 0 */
+  POETX_ERR_SHAPE = -2,       /* b does not divide a width, b out of range       */
+  POETX_ERR_UNSUPPORTED = -3, /* a combination the library does not implement    */
+  POETX_ERR_WORKSPACE = -4,   /* *ws_bytes smaller than required                 */
+  POETX_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed      */
+} poetx_status;
+
+typedef enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2 } poetx_dtype;
+typedef enum { POETX_FAST = 0, POETX_MEM = 1 } poetx_variant;
+typedef enum { POETX_CNP_FWD = 0, POETX_CNP_BWD = 1 } poetx_cnp_dir;
+
+/* [host] description of one layer.  Pointers inside are device pointers. */
+typedef struct {
+  int64_t d_in, d_out, b;      /* widths and block size                              */
+  int32_t act_dtype;           /* poetx_dtype of x, z, dz, dx, saved_b: F32 or BF16  */
+  int32_t w_dtype;             /* F32, BF16 (same as act) or I8 (BF16 act, MEM only) */
+  int32_t g_dtype;             /* dtype of g_r / g_p: F32 or BF16 (== act_dtype)     */
+  int32_t variant;             /* poetx_variant                                     */
+  const void *w_merged;        /* [d_out][d_in] W' from poetx_merge_perm            */
+  const float *w_scale;        /* [d_out] per-row scale of an I8 W', else NULL      */
+  const int32_t *perm_in;      /* [d_in]  or NULL (identity)                        */
+  const int32_t *perm_out;     /* [d_out] or NULL (identity)                        */
+  const float *theta_r;        /* [n_R][b(b-1)/2] packed Q of G_R                   */
+  const float *theta_p;        /* [n_P][b(b-1)/2] packed Q of G_P                   */
+  const void *g_r;             /* [n_R][b][b] from poetx_cnp(FWD, theta_r)          */
+  const void *g_p;             /* [n_P][b][b] from poetx_cnp(FWD, theta_p)          */
+} poetx_layer;
+
+/*
+ * poetx_merge_perm -- Method §2 (permutation merge, once per inner phase):
+ *     w_merged[i][k] = w[perm_out[i]][perm_in[k]]
+ * and for an I8 weight with per-output-row scales also
+ *     w_scale_merged[i] = w_scale[perm_out[i]]   (exact: a row scale moves with its row).
+ * w: [d_out][d_in] of w_dtype (F32, BF16 or I8); w_scale: [d_out] (I8 only, else NULL);
+ * perm_out: [d_out], perm_in: [d_in] (each may be NULL = identity; entries must form a
+ * permutation -- not checked on the device).  Output w_merged has w's dtype and shape.
+ * Bit-exact data movement.  Errors: NULL w/w_merged, I8 without both scale pointers,
+ * d_out or d_in < 1 -> POETX_ERR_INVALID_ARG.
+ */
+int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64_t d_out,
+                     int64_t d_in, const int32_t *perm_out, const int32_t *perm_in,
+                     void *w_merged, float *w_scale_merged, void *stream);
+
+/*
+ * poetx_cnp -- Method §4 (Cayley-Neumann parameterization, eq. 9) on nblocks
+ * independent b x b blocks.
+ *   dir == POETX_CNP_FWD: g[n][b][b] = I + 2(Q + Q^2 + Q^2.Q) + Q^2.Q^2 from packed
+ *     theta[n][b(b-1)/2]; g in g_dtype (F32 or BF16, rounded to nearest even).
+ *     dg, dtheta unused (may be NULL).
+ *   dir == POETX_CNP_BWD: dtheta[n][b(b-1)/2] = dL/dtheta given dg = dL/dG
+ *     ([n][b][b], dg_dtype F32), the exact adjoint of eq. 9 (the page leaves
+ *     its eq. 10 unprinted); g unused.
+ * Products are evaluated to float32 accuracy (split-bf16 MFMA passes), whatever
+ * g_dtype is.  Workspace: query with ws == NULL.
+ * Errors: b < 2 or b > 512 -> POETX_ERR_SHAPE; NULL theta / output -> INVALID_ARG.
+ */
+int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *theta, void *g,
+              int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta, void *ws,
+              size_t *ws_bytes, void *stream);
+
+/*
+ * poetx_forward -- Method §1 eq. 3 with §2 and §3 (batched block-diagonal
+ * products), token-major:  z[N][d_out] from x[N][d_in] (see the chain above).
+ * L->g_r, L->g_p must hold poetx_cnp(FWD) of L->theta_r, L->theta_p.
+ * saved_b: FAST variant -> output B = A.W'^T [N][d_out] in act dtype, kept for
+ * the backward (Method §5, POET-X_fast); MEM variant -> must be NULL (B is
+ * recomputed in the backward, POET-X_mem).  n_tokens == 0 is a no-op.
+ * Errors: I8 weight with FAST -> POETX_ERR_UNSUPPORTED (Method §6: POET-XQ
+ * builds on the recomputing variant); shape errors -> POETX_ERR_SHAPE.
+ */
+int poetx_forward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void *x, void *z,
+                  void *saved_b, void *ws, size_t *ws_bytes, void *stream);
+
+/*
+ * poetx_backward -- chain rule through poetx_forward (Method §1: W gets no
+ * gradient; only the block-diagonal G_R, G_P do), then the CNP backward:
+ *     dZ~ = Gather_out(dz);  dB = dZ~ . Diag(G_P)^T;  dG_P[j] = sum_t B_j^T dZ~_j
+ *     dA  = dB . W';          dX~ = dA . Diag(G_R)^T;  dG_R[j] = sum_t X~_j^T dA_j
+ *     dx  = Scatter_in(dX~);  dtheta_* = CNP backward of dG_*.
+ * saved_b: FAST -> the B written by poetx_forward; MEM -> NULL (recomputed).
+ * dx [N][d_in] act dtype; dtheta_r [n_R][p], dtheta_p [n_P][p] float32 (overwritten,
+ * sums over all N tokens).  dg_r [n_R][b][b], dg_p [n_P][b][b] float32 are optional
+ * outputs of the block gradients (NULL = not written).  Reductions over tokens run
+ * in a fixed order: results are bitwise reproducible run to run.
+ */
+int poetx_backward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void *x,
+                   const void *dz, const void *saved_b, void *dx, float *dtheta_r,
+                   float *dtheta_p, float *dg_r, float *dg_p, void *ws, size_t *ws_bytes,
+                   void *stream);
+
+/* Human-readable name of a poetx_status code (static string). */
+const char *poetx_status_string(int status);
+
+/* Library version, e.g. "0.1.0" (static string). */
+const char *poetx_version(void);
+
+/*
+ * Measurement hooks (not part of the layer's math).  poetx_prof_enable(1)
+ * makes every later kernel launch of the library record a pair of HIP events
+ * on its stream; poetx_prof_read() synchronizes those events and writes one
+ * line per kernel name, "name launches total_ms\n", into buf (truncated to
+ * len bytes, NUL-terminated), then clears the record.  poetx_prof_enable(0)
+ * stops recording.  Host-side state shared by all callers; not thread-safe.
+ * Returns POETX_OK or POETX_ERR_HIP.
+ */
+int poetx_prof_enable(int32_t on);
+int poetx_prof_read(char *buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* POETX_H */

@@ -1,0 +1,271 @@
+"""Thin ctypes binding over libpoetx (include/poetx.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch supplies device memory (its caching allocator) and the
+current HIP stream.  A nonzero status from the library raises ``PoetxError``.
+If the shared library is missing this module raises at import: there is no
+fallback path.
+
+Python names mirror the C entry points:
+    poetx_merge_perm, poetx_cnp, poetx_forward, poetx_backward
+plus ``Layer`` (the poetx_layer descriptor) and the measurement hooks.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpoetx.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build it with `python -m orthogonal_reparameterized_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+POETX_OK, POETX_ERR_INVALID_ARG, POETX_ERR_SHAPE = 0, -1, -2
+POETX_ERR_UNSUPPORTED, POETX_ERR_WORKSPACE, POETX_ERR_HIP = -3, -4, -5
+POETX_F32, POETX_BF16, POETX_I8 = 0, 1, 2
+POETX_FAST, POETX_MEM = 0, 1
+POETX_CNP_FWD, POETX_CNP_BWD = 0, 1
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+
+class PoetxLayerC(ctypes.Structure):
+    _fields_ = [
+        ("d_in", _i64), ("d_out", _i64), ("b", _i64),
+        ("act_dtype", _i32), ("w_dtype", _i32), ("g_dtype", _i32), ("variant", _i32),
+        ("w_merged", _vp), ("w_scale", _vp), ("perm_in", _vp), ("perm_out", _vp),
+        ("theta_r", _vp), ("theta_p", _vp), ("g_r", _vp), ("g_p", _vp),
+    ]
+
+
+_lib.poetx_merge_perm.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+_lib.poetx_cnp.argtypes = [_i32, _i64, _i64, _vp, _vp, _i32, _vp, _i32, _vp, _vp,
+                           ctypes.POINTER(_sz), _vp]
+_lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp,
+                               ctypes.POINTER(_sz), _vp]
+_lib.poetx_backward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _vp, _vp, _vp, ctypes.POINTER(_sz), _vp]
+_lib.poetx_status_string.argtypes = [ctypes.c_int]
+_lib.poetx_status_string.restype = ctypes.c_char_p
+_lib.poetx_version.restype = ctypes.c_char_p
+_lib.poetx_prof_enable.argtypes = [_i32]
+_lib.poetx_prof_read.argtypes = [ctypes.c_char_p, _sz]
+for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward",
+           "poetx_prof_enable", "poetx_prof_read"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward",
+            "poetx_status_string", "poetx_version", "poetx_prof_enable", "poetx_prof_read")
+
+
+class PoetxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.poetx_status_string(status).decode()} ({status})")
+
+
+def _check(st: int, where: str):
+    if st != POETX_OK:
+        raise PoetxError(st, where)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def version() -> str:
+    return _lib.poetx_version().decode()
+
+
+_DT = {torch.float32: POETX_F32, torch.bfloat16: POETX_BF16, torch.int8: POETX_I8}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError("tensor must be 16-byte aligned")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+# A per-device scratch tensor, grown on demand and reused between calls on the
+# same stream (stream order makes reuse safe).
+_ws_cache: dict = {}
+
+
+def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    key = (dev.index if dev.index is not None else torch.cuda.current_device())
+    t = _ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = t
+    return t
+
+
+def release_workspace():
+    _ws_cache.clear()
+
+
+# --------------------------------------------------------------------------
+def poetx_merge_perm(w: torch.Tensor, perm_out=None, perm_in=None, w_scale=None,
+                     out: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None):
+    """W'[i][k] = W[perm_out[i]][perm_in[k]] (and s'[i] = s[perm_out[i]] for int8)."""
+    d_out, d_in = w.shape
+    out = torch.empty_like(w) if out is None else out
+    if w.dtype == torch.int8 and out_scale is None:
+        out_scale = torch.empty_like(w_scale)
+    st = _lib.poetx_merge_perm(_ptr(w), _ptr(w_scale), _dt(w), d_out, d_in, _ptr(perm_out),
+                               _ptr(perm_in), _ptr(out), _ptr(out_scale) if w.dtype == torch.int8 else None,
+                               _stream(w.device))
+    _check(st, "poetx_merge_perm")
+    return out, (out_scale if w.dtype == torch.int8 else None)
+
+
+def poetx_cnp(direction: int, theta: torch.Tensor, b: int, *, g: Optional[torch.Tensor] = None,
+              g_dtype: torch.dtype = torch.bfloat16, dg: Optional[torch.Tensor] = None,
+              dtheta: Optional[torch.Tensor] = None):
+    """FWD: returns G [n][b][b] in g_dtype; BWD: returns dtheta [n][b(b-1)/2] from dg."""
+    n = theta.shape[0]
+    dev = theta.device
+    if direction == POETX_CNP_FWD:
+        g = torch.empty((n, b, b), dtype=g_dtype, device=dev) if g is None else g
+        gdt, dgdt = _dt(g), POETX_F32
+    else:
+        dtheta = torch.empty_like(theta) if dtheta is None else dtheta
+        gdt, dgdt = POETX_F32, _dt(dg)
+    nbytes = _sz(0)
+    _check(_lib.poetx_cnp(direction, n, b, None, None, gdt, None, dgdt, None, None,
+                          ctypes.byref(nbytes), None), "poetx_cnp(size)")
+    ws = _workspace(dev, nbytes.value)
+    nb = _sz(ws.numel())
+    st = _lib.poetx_cnp(direction, n, b, _ptr(theta), _ptr(g), gdt, _ptr(dg), dgdt, _ptr(dtheta),
+                        _ptr(ws), ctypes.byref(nb), _stream(dev))
+    _check(st, "poetx_cnp")
+    return g if direction == POETX_CNP_FWD else dtheta
+
+
+@dataclass
+class Layer:
+    """Python view of poetx_layer: the tensors stay owned by the caller."""
+    w_merged: torch.Tensor
+    theta_r: torch.Tensor
+    theta_p: torch.Tensor
+    g_r: torch.Tensor
+    g_p: torch.Tensor
+    b: int
+    act_dtype: torch.dtype = torch.bfloat16
+    variant: int = POETX_FAST
+    w_scale: Optional[torch.Tensor] = None
+    perm_in: Optional[torch.Tensor] = None
+    perm_out: Optional[torch.Tensor] = None
+
+    @property
+    def d_out(self):
+        return self.w_merged.shape[0]
+
+    @property
+    def d_in(self):
+        return self.w_merged.shape[1]
+
+    def to_c(self) -> PoetxLayerC:
+        c = PoetxLayerC()
+        c.d_in, c.d_out, c.b = self.d_in, self.d_out, self.b
+        c.act_dtype = _DT[self.act_dtype]
+        c.w_dtype = _dt(self.w_merged)
+        c.g_dtype = _dt(self.g_r)
+        c.variant = self.variant
+        for name in ("w_merged", "w_scale", "perm_in", "perm_out", "theta_r", "theta_p", "g_r", "g_p"):
+            p = _ptr(getattr(self, name))
+            setattr(c, name, p.value if p is not None else None)
+        return c
+
+
+def poetx_forward(layer: Layer, x: torch.Tensor, z: Optional[torch.Tensor] = None,
+                  saved_b: Optional[torch.Tensor] = None):
+    """Returns (z, saved_b); saved_b is None for the mem variant."""
+    L = layer.to_c()
+    n = x.shape[0]
+    dev = x.device
+    z = torch.empty((n, layer.d_out), dtype=layer.act_dtype, device=dev) if z is None else z
+    if layer.variant == POETX_FAST and saved_b is None:
+        saved_b = torch.empty((n, layer.d_out), dtype=layer.act_dtype, device=dev)
+    if layer.variant == POETX_MEM:
+        saved_b = None
+    nbytes = _sz(0)
+    _check(_lib.poetx_forward(ctypes.byref(L), n, None, None, None, None, ctypes.byref(nbytes), None),
+           "poetx_forward(size)")
+    ws = _workspace(dev, nbytes.value)
+    nb = _sz(ws.numel())
+    st = _lib.poetx_forward(ctypes.byref(L), n, _ptr(x), _ptr(z), _ptr(saved_b), _ptr(ws),
+                            ctypes.byref(nb), _stream(dev))
+    _check(st, "poetx_forward")
+    return z, saved_b
+
+
+def poetx_backward(layer: Layer, x: torch.Tensor, dz: torch.Tensor,
+                   saved_b: Optional[torch.Tensor] = None, *, dx=None, dtheta_r=None, dtheta_p=None,
+                   want_dg: bool = False):
+    """Returns dict(dx, dtheta_r, dtheta_p[, dg_r, dg_p])."""
+    L = layer.to_c()
+    n = x.shape[0]
+    dev = x.device
+    dx = torch.empty((n, layer.d_in), dtype=layer.act_dtype, device=dev) if dx is None else dx
+    dtheta_r = torch.empty_like(layer.theta_r) if dtheta_r is None else dtheta_r
+    dtheta_p = torch.empty_like(layer.theta_p) if dtheta_p is None else dtheta_p
+    dg_r = dg_p = None
+    if want_dg:
+        b = layer.b
+        dg_r = torch.empty((layer.d_in // b, b, b), dtype=torch.float32, device=dev)
+        dg_p = torch.empty((layer.d_out // b, b, b), dtype=torch.float32, device=dev)
+    nbytes = _sz(0)
+    _check(_lib.poetx_backward(ctypes.byref(L), n, None, None, None, None, None, None, _ptr(dg_r),
+                               _ptr(dg_p), None, ctypes.byref(nbytes), None), "poetx_backward(size)")
+    ws = _workspace(dev, nbytes.value)
+    nb = _sz(ws.numel())
+    st = _lib.poetx_backward(ctypes.byref(L), n, _ptr(x), _ptr(dz), _ptr(saved_b), _ptr(dx),
+                             _ptr(dtheta_r), _ptr(dtheta_p), _ptr(dg_r), _ptr(dg_p), _ptr(ws),
+                             ctypes.byref(nb), _stream(dev))
+    _check(st, "poetx_backward")
+    out = dict(dx=dx, dtheta_r=dtheta_r, dtheta_p=dtheta_p)
+    if want_dg:
+        out.update(dg_r=dg_r, dg_p=dg_p)
+    return out
+
+
+def prof_enable(on: bool = True):
+    _check(_lib.poetx_prof_enable(1 if on else 0), "poetx_prof_enable")
+
+
+def prof_read() -> dict:
+    """{kernel name: (launches, total_ms)} since the last read."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(_lib.poetx_prof_read(buf, len(buf)), "poetx_prof_read")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, ms = line.split()
+        out[name] = (int(n), float(ms))
+    return out
+
+
+# Raw handle for tests of the host-side validation (calls that fail before any launch).
+raw = _lib

@@ -1,0 +1,474 @@
+// libpoetx C ABI: argument validation, workspace carving and kernel sequencing
+// for the POET-X layer (declarations and contracts in include/poetx.h).
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace poetx;
+
+// ============================================================ measurement ====
+namespace poetx {
+namespace {
+struct ProfRec {
+  const char *name;
+  hipEvent_t a, b;
+};
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+const char *g_pending = nullptr;
+hipEvent_t g_pending_ev = nullptr;
+
+hipEvent_t pool_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+bool prof_on() { return g_prof; }
+void prof_begin(const char *name, hipStream_t s) {
+  g_pending = name;
+  g_pending_ev = pool_get();
+  if (g_pending_ev) hipEventRecord(g_pending_ev, s);
+}
+void prof_end(hipStream_t s) {
+  hipEvent_t e = pool_get();
+  if (!g_pending_ev || !e) return;
+  hipEventRecord(e, s);
+  g_recs.push_back({g_pending, g_pending_ev, e});
+  g_pending_ev = nullptr;
+}
+}  // namespace poetx
+
+extern "C" int poetx_prof_enable(int32_t on) {
+  g_prof = on != 0;
+  return POETX_OK;
+}
+
+extern "C" int poetx_prof_read(char *buf, size_t len) {
+  struct Acc { std::string name; long n; double ms; };
+  std::vector<Acc> acc;
+  int st = POETX_OK;
+  for (auto &r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      st = POETX_ERR_HIP;
+    bool found = false;
+    for (auto &a : acc)
+      if (a.name == r.name) { a.n++; a.ms += ms; found = true; break; }
+    if (!found) acc.push_back({r.name, 1, (double)ms});
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  std::string out;
+  char line[256];
+  for (auto &a : acc) {
+    snprintf(line, sizeof line, "%s %ld %.6f\n", a.name.c_str(), a.n, a.ms);
+    out += line;
+  }
+  if (buf && len) {
+    size_t n = out.size() < len - 1 ? out.size() : len - 1;
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  return st;
+}
+
+extern "C" const char *poetx_status_string(int st) {
+  switch (st) {
+    case POETX_OK: return "POETX_OK";
+    case POETX_ERR_INVALID_ARG: return "POETX_ERR_INVALID_ARG";
+    case POETX_ERR_SHAPE: return "POETX_ERR_SHAPE";
+    case POETX_ERR_UNSUPPORTED: return "POETX_ERR_UNSUPPORTED";
+    case POETX_ERR_WORKSPACE: return "POETX_ERR_WORKSPACE";
+    case POETX_ERR_HIP: return "POETX_ERR_HIP";
+    default: return "POETX_UNKNOWN_STATUS";
+  }
+}
+
+extern "C" const char *poetx_version(void) { return "0.1.0"; }
+
+// ============================================================ permutation ====
+extern "C" int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype,
+                                int64_t d_out, int64_t d_in, const int32_t *perm_out,
+                                const int32_t *perm_in, void *w_merged, float *w_scale_merged,
+                                void *stream) {
+  if (!w || !w_merged || d_out < 1 || d_in < 1) return POETX_ERR_INVALID_ARG;
+  if (w_dtype != POETX_F32 && w_dtype != POETX_BF16 && w_dtype != POETX_I8) return POETX_ERR_INVALID_ARG;
+  if (w_dtype == POETX_I8 && (!w_scale || !w_scale_merged)) return POETX_ERR_INVALID_ARG;
+  if ((size_t)d_in * dtype_size(w_dtype) > 65536) return POETX_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  POETX_TRY(permute_cols(w, w_merged, d_out, d_in, (int)dtype_size(w_dtype), perm_out, perm_in, false, s));
+  if (w_dtype == POETX_I8) POETX_TRY(gather_f32(w_scale, w_scale_merged, d_out, perm_out, s));
+  return POETX_OK;
+}
+
+// ==================================================================== CNP ====
+// Float32 steps of the Cayley-Neumann map (Method §4, eq. 9), Horner form
+//   G = I + 2Q + S (2I + 2Q + S),  S = Q^2,
+// and its adjoint (derived from eq. 9; the page does not print eq. 10):
+//   Qbar = C0 + Q C1 + S C2 + Q S C3 with
+//   C0 = 2Gb - 2GbQ + 2GbS - GbSQ, C1 = -2Gb + 2GbQ - GbS, C2 = 2Gb - GbQ, C3 = -Gb,
+// evaluated as (C0 + S C2) + Q (C1 + S C3).
+namespace {
+
+GemmDesc batched_f32(int64_t n, int64_t b, const float *A, const float *B, void *C, int c_dt) {
+  GemmDesc g;
+  g.M = g.N = g.K = b;
+  g.batch = n;
+  g.A = A; g.a_dt = POETX_F32; g.sAb = b * b; g.sAm = b; g.sAk = 1;
+  g.B = B; g.b_dt = POETX_F32; g.sBb = b * b; g.sBk = b; g.sBn = 1;
+  g.C = C; g.c_dt = c_dt; g.sCb = b * b; g.sCm = b; g.sCn = 1;
+  return g;
+}
+
+size_t cnp_ws_bytes(int dir, int64_t n, int64_t b) {
+  Arena ar(nullptr);
+  size_t blk = (size_t)n * b * b * 4;
+  int bufs = dir == POETX_CNP_FWD ? 4 : 6;
+  for (int i = 0; i < bufs; ++i) ar.take(blk);
+  return ar.used;
+}
+
+int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype, void *ws,
+                 hipStream_t s) {
+  Arena ar(ws);
+  size_t blk = (size_t)n * b * b * 4;
+  float *Q = (float *)ar.take(blk), *S = (float *)ar.take(blk);
+  float *T = (float *)ar.take(blk), *U = (float *)ar.take(blk);
+  POETX_TRY(unpack_skew(theta, Q, n, b, s));
+  POETX_TRY(gemm_generic(batched_f32(n, b, Q, Q, S, POETX_F32), s));
+  POETX_TRY(lincomb(T, n, b, 2.f, Q, 2.f, S, 1.f, nullptr, 0.f, nullptr, 0.f, s));
+  POETX_TRY(lincomb(U, n, b, 1.f, Q, 2.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
+  GemmDesc gg = batched_f32(n, b, S, T, g, g_dtype);
+  gg.D = U; gg.sDb = b * b; gg.sDm = b; gg.sDn = 1; gg.beta = 1.f;
+  return gemm_generic(gg, s);
+}
+
+int cnp_bwd_impl(int64_t n, int64_t b, const float *theta, const float *dg, float *dtheta, void *ws,
+                 hipStream_t s) {
+  Arena ar(ws);
+  size_t blk = (size_t)n * b * b * 4;
+  float *Q = (float *)ar.take(blk), *S = (float *)ar.take(blk), *Y = (float *)ar.take(blk);
+  float *Y2 = (float *)ar.take(blk), *Y3 = (float *)ar.take(blk), *B0 = (float *)ar.take(blk);
+  POETX_TRY(unpack_skew(theta, Q, n, b, s));
+  POETX_TRY(gemm_generic(batched_f32(n, b, Q, Q, S, POETX_F32), s));
+  POETX_TRY(gemm_generic(batched_f32(n, b, dg, Q, Y, POETX_F32), s));    // Gb Q
+  POETX_TRY(gemm_generic(batched_f32(n, b, dg, S, Y2, POETX_F32), s));   // Gb S
+  POETX_TRY(gemm_generic(batched_f32(n, b, Y2, Q, Y3, POETX_F32), s));   // Gb S Q
+  POETX_TRY(lincomb(B0, n, b, 0.f, dg, 2.f, Y, -2.f, Y2, 2.f, Y3, -1.f, s));   // C0
+  POETX_TRY(lincomb(Y3, n, b, 0.f, dg, -2.f, Y, 2.f, Y2, -1.f, nullptr, 0.f, s)); // C1
+  POETX_TRY(lincomb(Y2, n, b, 0.f, dg, 2.f, Y, -1.f, nullptr, 0.f, nullptr, 0.f, s)); // C2
+  GemmDesc v = batched_f32(n, b, S, dg, Y, POETX_F32);  // V = C1 - S Gb
+  v.alpha = -1.f; v.D = Y3; v.sDb = b * b; v.sDm = b; v.sDn = 1; v.beta = 1.f;
+  POETX_TRY(gemm_generic(v, s));
+  GemmDesc u = batched_f32(n, b, S, Y2, B0, POETX_F32);  // U = C0 + S C2
+  u.D = B0; u.sDb = b * b; u.sDm = b; u.sDn = 1; u.beta = 1.f;
+  POETX_TRY(gemm_generic(u, s));
+  GemmDesc q = batched_f32(n, b, Q, Y, Y2, POETX_F32);  // Qbar = U + Q V
+  q.D = B0; q.sDb = b * b; q.sDm = b; q.sDn = 1; q.beta = 1.f;
+  POETX_TRY(gemm_generic(q, s));
+  return pack_skew_grad(Y2, dtheta, n, b, s);
+}
+
+}  // namespace
+
+extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *theta, void *g,
+                         int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta,
+                         void *ws, size_t *ws_bytes, void *stream) {
+  if (dir != POETX_CNP_FWD && dir != POETX_CNP_BWD) return POETX_ERR_INVALID_ARG;
+  if (nblocks < 0 || !ws_bytes) return POETX_ERR_INVALID_ARG;
+  if (b < 2 || b > 512) return POETX_ERR_SHAPE;
+  if (dir == POETX_CNP_FWD) {
+    if (g_dtype != POETX_F32 && g_dtype != POETX_BF16) return POETX_ERR_INVALID_ARG;
+  } else {
+    if (dg_dtype != POETX_F32) return POETX_ERR_UNSUPPORTED;
+  }
+  size_t need = cnp_ws_bytes(dir, nblocks, b);
+  if (!ws) {
+    *ws_bytes = need;
+    return POETX_OK;
+  }
+  if (!theta) return POETX_ERR_INVALID_ARG;
+  if (dir == POETX_CNP_FWD && !g) return POETX_ERR_INVALID_ARG;
+  if (dir == POETX_CNP_BWD && (!dg || !dtheta)) return POETX_ERR_INVALID_ARG;
+  if (*ws_bytes < need) return POETX_ERR_WORKSPACE;
+  if (nblocks == 0) return POETX_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (dir == POETX_CNP_FWD) return cnp_fwd_impl(nblocks, b, theta, g, g_dtype, ws, s);
+  return cnp_bwd_impl(nblocks, b, theta, (const float *)dg, dtheta, ws, s);
+}
+
+// ================================================================== layer ====
+namespace {
+
+struct Plan {
+  int64_t N, din, dout, b, nr, np;
+  int act, w, gdt;
+  bool mem, mfma;
+  size_t ae;  // activation element size
+};
+
+int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
+  if (!L || n_tokens < 0) return POETX_ERR_INVALID_ARG;
+  if (L->d_in < 1 || L->d_out < 1) return POETX_ERR_INVALID_ARG;
+  if (L->b < 2 || L->b > 512) return POETX_ERR_SHAPE;
+  if (L->d_in % L->b || L->d_out % L->b) return POETX_ERR_SHAPE;
+  if (L->act_dtype != POETX_F32 && L->act_dtype != POETX_BF16) return POETX_ERR_INVALID_ARG;
+  if (L->w_dtype != POETX_F32 && L->w_dtype != POETX_BF16 && L->w_dtype != POETX_I8) return POETX_ERR_INVALID_ARG;
+  if (L->g_dtype != L->act_dtype) return POETX_ERR_UNSUPPORTED;
+  if (L->variant != POETX_FAST && L->variant != POETX_MEM) return POETX_ERR_INVALID_ARG;
+  if (L->w_dtype == POETX_I8) {
+    if (L->act_dtype != POETX_BF16) return POETX_ERR_UNSUPPORTED;
+    if (L->variant == POETX_FAST) return POETX_ERR_UNSUPPORTED;
+  } else if (L->w_dtype != L->act_dtype) {
+    return POETX_ERR_UNSUPPORTED;
+  }
+  if ((size_t)(L->d_in > L->d_out ? L->d_in : L->d_out) * dtype_size(L->act_dtype) > 65536)
+    return POETX_ERR_UNSUPPORTED;
+  p.N = n_tokens; p.din = L->d_in; p.dout = L->d_out; p.b = L->b;
+  p.nr = L->d_in / L->b; p.np = L->d_out / L->b;
+  p.act = L->act_dtype; p.w = L->w_dtype; p.gdt = L->g_dtype;
+  p.mem = L->variant == POETX_MEM;
+  p.ae = dtype_size(p.act);
+  p.mfma = p.act == POETX_BF16 && p.b % 128 == 0 && p.din % 128 == 0 && p.dout % 128 == 0;
+  return POETX_OK;
+}
+
+int check_layer_ptrs(const poetx_layer *L) {
+  if (!L->w_merged || !L->theta_r || !L->theta_p || !L->g_r || !L->g_p) return POETX_ERR_INVALID_ARG;
+  if (L->w_dtype == POETX_I8 && !L->w_scale) return POETX_ERR_INVALID_ARG;
+  return POETX_OK;
+}
+
+// Y[:, jb:(j+1)b] = X[:, jb:(j+1)b] . G[j]  (transposed: . G[j]^T), for all blocks j.
+int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y, bool transposed,
+                const float *scaleN, hipStream_t s) {
+  int64_t b = p.b, nb = d / b;
+  if (p.N == 0) return POETX_OK;
+  if (p.mfma) {
+    MfmaDesc m;
+    m.M = p.N; m.N = b; m.K = b; m.batch = nb;
+    m.A = X; m.a_km = false; m.lda = d; m.sAb = b;
+    m.B = G; m.b_km = !transposed; m.b_dt = POETX_BF16; m.ldb = b; m.sBb = b * b;
+    m.C = Y; m.c_dt = p.act; m.ldc = d; m.sCb = b;
+    m.scaleN = scaleN;
+    return gemm_mfma(m, s);
+  }
+  GemmDesc g;
+  g.M = p.N; g.N = b; g.K = b; g.batch = nb;
+  g.A = X; g.a_dt = p.act; g.sAb = b; g.sAm = d; g.sAk = 1;
+  g.B = G; g.b_dt = p.gdt; g.sBb = b * b;
+  if (transposed) { g.sBk = 1; g.sBn = b; } else { g.sBk = b; g.sBn = 1; }
+  g.C = Y; g.c_dt = p.act; g.sCb = b; g.sCm = d; g.sCn = 1;
+  g.scaleN = scaleN;
+  return gemm_generic(g, s);
+}
+
+// dG[j] = X[:, jb:(j+1)b]^T . Y[:, jb:(j+1)b]  (sum over tokens), as fp32 partials over
+// token chunks of grad_chunk(...) tokens (a multiple of 64), summed later in a fixed order.
+int64_t grad_chunk(const Plan &p, int64_t nb) {
+  if (!p.mfma || p.N == 0) return p.N > 0 ? p.N : 1;
+  int64_t tiles = nb * (p.b / 128) * (p.b / 128);
+  int64_t want = cdiv(512, tiles);
+  int64_t kc = cdiv(cdiv(p.N, want), 64) * 64;
+  return kc < 256 ? 256 : kc;
+}
+
+int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, float *parts, int64_t kc,
+               hipStream_t s) {
+  int64_t b = p.b, nb = d / b;
+  if (p.mfma) {
+    MfmaDesc m;
+    m.M = b; m.N = b; m.K = p.N; m.batch = nb;
+    m.splits = cdiv(p.N, kc); m.kchunk = kc;
+    m.A = X; m.a_km = true; m.lda = d; m.sAb = b;
+    m.B = Y; m.b_km = true; m.b_dt = POETX_BF16; m.ldb = d; m.sBb = b;
+    m.C = parts; m.c_dt = POETX_F32; m.ldc = b; m.sCb = b * b; m.sCsplit = nb * b * b;
+    return gemm_mfma(m, s);
+  }
+  GemmDesc g;
+  g.M = b; g.N = b; g.K = p.N; g.batch = nb;
+  g.A = X; g.a_dt = p.act; g.sAb = b; g.sAm = 1; g.sAk = d;
+  g.B = Y; g.b_dt = p.act; g.sBb = b; g.sBk = d; g.sBn = 1;
+  g.C = parts; g.c_dt = POETX_F32; g.sCb = b * b; g.sCm = b; g.sCn = 1;
+  return gemm_generic(g, s);
+}
+
+// B = A . W'^T (scaled per output row of W' for int8 weights)
+int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, hipStream_t s) {
+  if (p.N == 0) return POETX_OK;
+  if (p.mfma) {
+    MfmaDesc m;
+    m.M = p.N; m.N = p.dout; m.K = p.din;
+    m.A = A; m.a_km = false; m.lda = p.din;
+    m.B = L->w_merged; m.b_km = false; m.b_dt = p.w; m.ldb = p.din;
+    m.C = B; m.c_dt = p.act; m.ldc = p.dout;
+    m.scaleN = p.w == POETX_I8 ? L->w_scale : nullptr;
+    return gemm_mfma(m, s);
+  }
+  GemmDesc g;
+  g.M = p.N; g.N = p.dout; g.K = p.din;
+  g.A = A; g.a_dt = p.act; g.sAm = p.din; g.sAk = 1;
+  g.B = L->w_merged; g.b_dt = p.w; g.sBk = 1; g.sBn = p.din;
+  g.C = B; g.c_dt = p.act; g.sCm = p.dout; g.sCn = 1;
+  g.scaleN = p.w == POETX_I8 ? L->w_scale : nullptr;
+  return gemm_generic(g, s);
+}
+
+// dA = dB' . W'  (dB' already carries the int8 row scales)
+int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, hipStream_t s) {
+  if (p.N == 0) return POETX_OK;
+  if (p.mfma) {
+    MfmaDesc m;
+    m.M = p.N; m.N = p.din; m.K = p.dout;
+    m.A = dB; m.a_km = false; m.lda = p.dout;
+    m.B = L->w_merged; m.b_km = true; m.b_dt = p.w; m.ldb = p.din;
+    m.C = dA; m.c_dt = p.act; m.ldc = p.din;
+    return gemm_mfma(m, s);
+  }
+  GemmDesc g;
+  g.M = p.N; g.N = p.din; g.K = p.dout;
+  g.A = dB; g.a_dt = p.act; g.sAm = p.dout; g.sAk = 1;
+  g.B = L->w_merged; g.b_dt = p.w; g.sBk = p.din; g.sBn = 1;
+  g.C = dA; g.c_dt = p.act; g.sCm = p.din; g.sCn = 1;
+  return gemm_generic(g, s);
+}
+
+struct FwdBufs {
+  void *xg = nullptr, *a = nullptr, *bt = nullptr, *zt = nullptr;
+};
+
+// Carve forward intermediates.  `want_b` asks for B in the workspace.
+void carve_fwd(Arena &ar, const Plan &p, const poetx_layer *L, bool want_b, FwdBufs &f) {
+  size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
+  if (L->perm_in) f.xg = ar.take(xin);
+  f.a = ar.take(xin);
+  if (want_b) f.bt = ar.take(xout);
+  if (L->perm_out) f.zt = ar.take(xout);
+}
+
+// Gather(X) -> Xg ; A = Xg . Diag(G_R) ; B = A . W'^T
+int run_front(const Plan &p, const poetx_layer *L, const void *x, const FwdBufs &f, void *bt,
+              hipStream_t s) {
+  const void *xg = x;
+  if (L->perm_in) {
+    POETX_TRY(permute_cols(x, f.xg, p.N, p.din, (int)p.ae, nullptr, L->perm_in, false, s));
+    xg = f.xg;
+  }
+  POETX_TRY(block_apply(p, p.din, xg, L->g_r, f.a, false, nullptr, s));
+  return gemm_fwd(p, L, f.a, bt, s);
+}
+
+}  // namespace
+
+extern "C" int poetx_forward(const poetx_layer *L, int64_t n_tokens, const void *x, void *z,
+                             void *saved_b, void *ws, size_t *ws_bytes, void *stream) {
+  Plan p;
+  POETX_TRY(validate(L, n_tokens, p));
+  if (!ws_bytes) return POETX_ERR_INVALID_ARG;
+  if (p.mem && saved_b) return POETX_ERR_INVALID_ARG;
+  Arena ar(ws);
+  FwdBufs f;
+  carve_fwd(ar, p, L, p.mem, f);
+  if (!ws) {
+    *ws_bytes = ar.used;
+    return POETX_OK;
+  }
+  POETX_TRY(check_layer_ptrs(L));
+  if (p.N > 0 && (!x || !z || (!p.mem && !saved_b))) return POETX_ERR_INVALID_ARG;
+  if (*ws_bytes < ar.used) return POETX_ERR_WORKSPACE;
+  if (p.N == 0) return POETX_OK;
+  hipStream_t s = (hipStream_t)stream;
+  void *bt = p.mem ? f.bt : saved_b;
+  POETX_TRY(run_front(p, L, x, f, bt, s));
+  void *zt = L->perm_out ? f.zt : z;
+  POETX_TRY(block_apply(p, p.dout, bt, L->g_p, zt, false, nullptr, s));
+  if (L->perm_out) POETX_TRY(permute_cols(zt, z, p.N, p.dout, (int)p.ae, nullptr, L->perm_out, true, s));
+  return POETX_OK;
+}
+
+extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void *x, const void *dz,
+                              const void *saved_b, void *dx, float *dtheta_r, float *dtheta_p,
+                              float *dg_r, float *dg_p, void *ws, size_t *ws_bytes, void *stream) {
+  Plan p;
+  POETX_TRY(validate(L, n_tokens, p));
+  if (!ws_bytes) return POETX_ERR_INVALID_ARG;
+  if (p.mem && saved_b) return POETX_ERR_INVALID_ARG;
+  const int64_t b = p.b, bb = b * b;
+  const int64_t kcr = grad_chunk(p, p.nr), kcp = grad_chunk(p, p.np);
+  const int64_t sr = p.N > 0 ? cdiv(p.N, kcr) : 1, sp = p.N > 0 ? cdiv(p.N, kcp) : 1;
+  size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
+  Arena ar(ws);
+  FwdBufs f;
+  carve_fwd(ar, p, L, p.mem, f);
+  void *dzt = L->perm_out ? ar.take(xout) : nullptr;
+  void *dbuf = ar.take(xout);
+  void *da = ar.take(xin);
+  void *dxt = L->perm_in ? ar.take(xin) : nullptr;
+  float *part_r = (float *)ar.take((size_t)sr * p.nr * bb * 4);
+  float *part_p = (float *)ar.take((size_t)sp * p.np * bb * 4);
+  float *gr = dg_r ? dg_r : (float *)ar.take((size_t)p.nr * bb * 4);
+  float *gp = dg_p ? dg_p : (float *)ar.take((size_t)p.np * bb * 4);
+  size_t cws_r = cnp_ws_bytes(POETX_CNP_BWD, p.nr, b), cws_p = cnp_ws_bytes(POETX_CNP_BWD, p.np, b);
+  void *cws = ar.take(cws_r > cws_p ? cws_r : cws_p);
+  if (!ws) {
+    *ws_bytes = ar.used;
+    return POETX_OK;
+  }
+  POETX_TRY(check_layer_ptrs(L));
+  if (!dtheta_r || !dtheta_p) return POETX_ERR_INVALID_ARG;
+  if (p.N > 0 && (!x || !dz || !dx || (!p.mem && !saved_b))) return POETX_ERR_INVALID_ARG;
+  if (*ws_bytes < ar.used) return POETX_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+
+  // B (kept by the fast variant, recomputed by the mem variant) and X~ = Gather(X)
+  const void *bt = saved_b;
+  const void *xg = x;
+  if (p.N > 0) {
+    if (p.mem) {
+      POETX_TRY(run_front(p, L, x, f, f.bt, s));
+      bt = f.bt;
+    } else if (L->perm_in) {
+      POETX_TRY(permute_cols(x, f.xg, p.N, p.din, (int)p.ae, nullptr, L->perm_in, false, s));
+    }
+    if (L->perm_in) xg = f.xg;
+  }
+  // P side: dZ~ = Gather_out(dZ); dB = dZ~ Diag(G_P)^T; dG_P = sum_t B^T dZ~
+  const void *dzg = dz;
+  if (p.N > 0 && L->perm_out) {
+    POETX_TRY(permute_cols(dz, dzt, p.N, p.dout, (int)p.ae, nullptr, L->perm_out, false, s));
+    dzg = dzt;
+  }
+  if (p.N > 0) {
+    POETX_TRY(block_apply(p, p.dout, dzg, L->g_p, dbuf, true,
+                          p.w == POETX_I8 ? L->w_scale : nullptr, s));
+    POETX_TRY(block_grad(p, p.dout, bt, dzg, part_p, kcp, s));
+    POETX_TRY(reduce_parts(part_p, gp, p.np * bb, sp, p.np * bb, s));
+    // dA = dB W'
+    POETX_TRY(gemm_bwd(p, L, dbuf, da, s));
+    // R side: dX~ = dA Diag(G_R)^T; dG_R = sum_t X~^T dA; dX = Scatter_in(dX~)
+    void *dxw = L->perm_in ? dxt : dx;
+    POETX_TRY(block_apply(p, p.din, da, L->g_r, dxw, true, nullptr, s));
+    if (L->perm_in) POETX_TRY(permute_cols(dxt, dx, p.N, p.din, (int)p.ae, nullptr, L->perm_in, true, s));
+    POETX_TRY(block_grad(p, p.din, xg, da, part_r, kcr, s));
+    POETX_TRY(reduce_parts(part_r, gr, p.nr * bb, sr, p.nr * bb, s));
+  } else {
+    POETX_TRY(lincomb(gr, p.nr, b, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
+    POETX_TRY(lincomb(gp, p.np, b, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
+  }
+  // CNP backward on both sides (Method §4)
+  POETX_TRY(cnp_bwd_impl(p.nr, b, L->theta_r, gr, dtheta_r, cws, s));
+  POETX_TRY(cnp_bwd_impl(p.np, b, L->theta_p, gp, dtheta_p, cws, s));
+  return POETX_OK;
+}

@@ -1,0 +1,79 @@
+// Shared internals of libpoetx: status plumbing, launch bookkeeping, bf16 helpers,
+// workspace carving.  Not part of the public ABI (see include/poetx.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/poetx.h"
+
+namespace poetx {
+
+// ------------------------------------------------------------------ status ----
+#define POETX_TRY(expr)                  \
+  do {                                   \
+    int _st = (expr);                    \
+    if (_st != POETX_OK) return _st;     \
+  } while (0)
+
+// Launch bookkeeping: every kernel launch goes through begin_launch / end_launch,
+// which check for launch errors and, when measurement is on, bracket the launch
+// with HIP events (see poetx_prof_enable).
+void prof_begin(const char *name, hipStream_t s);
+void prof_end(hipStream_t s);
+bool prof_on();
+
+template <typename F>
+inline int launch(const char *name, hipStream_t s, F &&f) {
+  if (prof_on()) prof_begin(name, s);
+  f();
+  hipError_t e = hipGetLastError();
+  if (prof_on()) prof_end(s);
+  return e == hipSuccess ? POETX_OK : POETX_ERR_HIP;
+}
+
+// ------------------------------------------------------------- bf16 bits ----
+typedef uint16_t bf16_t;
+
+__host__ __device__ inline float bf16_to_f32(bf16_t h) {
+  union { uint32_t u; float f; } v;
+  v.u = (uint32_t)h << 16;
+  return v.f;
+}
+
+// Round-to-nearest-even (finite inputs; NaN is not produced by the layer's math).
+__host__ __device__ inline bf16_t f32_to_bf16(float f) {
+  union { uint32_t u; float f; } v;
+  v.f = f;
+  uint32_t r = 0x7FFFu + ((v.u >> 16) & 1u);
+  return (bf16_t)((v.u + r) >> 16);
+}
+
+// Element loaders widening any stored dtype to float.
+__device__ inline float ld_f(const float *p) { return *p; }
+__device__ inline float ld_f(const bf16_t *p) { return bf16_to_f32(*p); }
+__device__ inline float ld_f(const int8_t *p) { return (float)*p; }
+__device__ inline void st_f(float *p, float v) { *p = v; }
+__device__ inline void st_f(bf16_t *p, float v) { *p = f32_to_bf16(v); }
+
+inline size_t dtype_size(int dt) { return dt == POETX_F32 ? 4 : dt == POETX_BF16 ? 2 : 1; }
+
+// --------------------------------------------------------------- workspace ----
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures (used for the ws == NULL size query).
+struct Arena {
+  char *base;
+  size_t used = 0;
+  explicit Arena(void *b) : base((char *)b) {}
+  void *take(size_t bytes) {
+    size_t off = (used + 255) & ~(size_t)255;
+    used = off + ((bytes + 255) & ~(size_t)255);
+    return base ? (void *)(base + off) : nullptr;
+  }
+};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace poetx

@@ -1,0 +1,243 @@
+// Vector-ALU kernels of libpoetx: the strided float32-accumulating product, the
+// LDS-staged column permutation, packed-skew helpers and fixed-order reductions.
+#include "kernels.h"
+
+namespace poetx {
+
+// ===================================================================== GEMM ====
+// 64 x 64 output tile per 256-thread workgroup, 16-deep k slices staged in LDS
+// as float; every thread owns a 4 x 4 patch.  Bounds are checked everywhere, so
+// any M, N, K and any strides work (this is the correctness path, not the fast one).
+template <typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256) void k_gemm_generic(GemmDesc g) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int64_t z = blockIdx.z;
+  const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+  const TA *A = (const TA *)g.A + z * g.sAb;
+  const TB *B = (const TB *)g.B + z * g.sBb;
+  float acc[4][4] = {};
+  for (int64_t k0 = 0; k0 < g.K; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int e = tid + 256 * i;
+      int mm = e >> 4, kk = e & 15;
+      int64_t m = m0 + mm, k = k0 + kk;
+      float v = 0.f;
+      if (m < g.M && k < g.K) {
+        v = ld_f(A + m * g.sAm + k * g.sAk);
+        if (g.scaleK) v *= g.scaleK[k];
+      }
+      As[kk][mm] = v;
+      int kb = e >> 6, nn = e & 63;
+      int64_t n = n0 + nn, k2 = k0 + kb;
+      Bs[kb][nn] = (n < g.N && k2 < g.K) ? ld_f(B + k2 * g.sBk + n * g.sBn) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  TC *C = (TC *)g.C + z * g.sCb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int64_t m = m0 + ty * 4 + i;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t n = n0 + tx * 4 + j;
+      if (n >= g.N) continue;
+      float v = g.alpha * acc[i][j];
+      if (g.scaleN) v *= g.scaleN[n];
+      if (g.D) v += g.beta * g.D[z * g.sDb + m * g.sDm + n * g.sDn];
+      st_f(C + m * g.sCm + n * g.sCn, v);
+    }
+  }
+}
+
+template <typename TA, typename TB>
+static int gemm_generic_c(const GemmDesc &g, hipStream_t s) {
+  dim3 grid((unsigned)cdiv(g.N, 64), (unsigned)cdiv(g.M, 64), (unsigned)g.batch);
+  if (g.c_dt == POETX_F32)
+    return launch("gemm_generic", s, [&] { k_gemm_generic<TA, TB, float><<<grid, 256, 0, s>>>(g); });
+  return launch("gemm_generic", s, [&] { k_gemm_generic<TA, TB, bf16_t><<<grid, 256, 0, s>>>(g); });
+}
+
+template <typename TA>
+static int gemm_generic_b(const GemmDesc &g, hipStream_t s) {
+  switch (g.b_dt) {
+    case POETX_F32: return gemm_generic_c<TA, float>(g, s);
+    case POETX_BF16: return gemm_generic_c<TA, bf16_t>(g, s);
+    default: return gemm_generic_c<TA, int8_t>(g, s);
+  }
+}
+
+int gemm_generic(const GemmDesc &g, hipStream_t s) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return POETX_OK;
+  if (g.batch > 65535 || cdiv(g.M, 64) > 65535) return POETX_ERR_UNSUPPORTED;
+  switch (g.a_dt) {
+    case POETX_F32: return gemm_generic_b<float>(g, s);
+    case POETX_BF16: return gemm_generic_b<bf16_t>(g, s);
+    default: return gemm_generic_b<int8_t>(g, s);
+  }
+}
+
+// ============================================================== permutation ====
+// One token row at a time goes through LDS: the global reads and writes are
+// contiguous and only the LDS side is indexed by the permutation.
+template <typename T>
+__global__ __launch_bounds__(256) void k_permute_cols(const T *__restrict__ in, T *__restrict__ out,
+                                                      int64_t rows, int64_t cols,
+                                                      const int32_t *__restrict__ rperm,
+                                                      const int32_t *__restrict__ cperm, int scatter) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  T *row = (T *)lds_raw;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    if (!scatter) {
+      int64_t src = rperm ? rperm[r] : r;
+      for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) row[c] = in[src * cols + c];
+      __syncthreads();
+      for (int64_t c = threadIdx.x; c < cols; c += blockDim.x)
+        out[r * cols + c] = row[cperm ? cperm[c] : c];
+    } else {
+      for (int64_t c = threadIdx.x; c < cols; c += blockDim.x)
+        row[cperm ? cperm[c] : c] = in[r * cols + c];
+      __syncthreads();
+      for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) out[r * cols + c] = row[c];
+    }
+    __syncthreads();
+  }
+}
+
+int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esize,
+                 const int32_t *rperm, const int32_t *cperm, bool scatter, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return POETX_OK;
+  size_t lds = (size_t)cols * esize;
+  if (lds > 65536) return POETX_ERR_UNSUPPORTED;
+  unsigned grid = (unsigned)(rows < 4096 ? rows : 4096);
+  int sc = scatter ? 1 : 0;
+  switch (esize) {
+    case 4:
+      return launch("permute_cols", s, [&] {
+        k_permute_cols<uint32_t><<<grid, 256, lds, s>>>((const uint32_t *)in, (uint32_t *)out, rows, cols, rperm, cperm, sc);
+      });
+    case 2:
+      return launch("permute_cols", s, [&] {
+        k_permute_cols<uint16_t><<<grid, 256, lds, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols, rperm, cperm, sc);
+      });
+    default:
+      return launch("permute_cols", s, [&] {
+        k_permute_cols<uint8_t><<<grid, 256, lds, s>>>((const uint8_t *)in, (uint8_t *)out, rows, cols, rperm, cperm, sc);
+      });
+  }
+}
+
+__global__ void k_gather_f32(const float *__restrict__ src, float *__restrict__ out, int64_t n,
+                             const int32_t *__restrict__ perm) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = src[perm ? perm[i] : i];
+}
+
+int gather_f32(const float *src, float *out, int64_t n, const int32_t *perm, hipStream_t s) {
+  if (n <= 0) return POETX_OK;
+  return launch("gather_f32", s, [&] { k_gather_f32<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(src, out, n, perm); });
+}
+
+// ============================================================= packed skew ====
+// Offset of (r, c), r < c, in the row-major strict upper triangle of a b x b block.
+__device__ inline int64_t triu_index(int64_t r, int64_t c, int64_t b) {
+  return r * b - r * (r + 1) / 2 + (c - r - 1);
+}
+
+__global__ void k_unpack_skew(const float *__restrict__ theta, float *__restrict__ Q, int64_t n,
+                              int64_t b) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t bb = b * b;
+  if (e >= n * bb) return;
+  int64_t j = e / bb, rc = e % bb, r = rc / b, c = rc % b;
+  const float *t = theta + j * (b * (b - 1) / 2);
+  float v = 0.f;
+  if (r < c) v = t[triu_index(r, c, b)];
+  else if (r > c) v = -t[triu_index(c, r, b)];
+  Q[e] = v;
+}
+
+int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t s) {
+  int64_t tot = n * b * b;
+  if (tot <= 0) return POETX_OK;
+  return launch("unpack_skew", s, [&] { k_unpack_skew<<<(unsigned)cdiv(tot, 256), 256, 0, s>>>(theta, Q, n, b); });
+}
+
+__global__ void k_pack_skew_grad(const float *__restrict__ M, float *__restrict__ dtheta, int64_t n,
+                                 int64_t b) {
+  int64_t p = b * (b - 1) / 2;
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n * p) return;
+  int64_t j = e / p, k = e % p;
+  // invert the row-major triangle offset: find r with start(r) <= k < start(r+1)
+  int64_t r = 0, start = 0;
+  while (start + (b - 1 - r) <= k) { start += b - 1 - r; ++r; }
+  int64_t c = r + 1 + (k - start);
+  const float *Mj = M + j * b * b;
+  dtheta[e] = Mj[r * b + c] - Mj[c * b + r];
+}
+
+int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s) {
+  int64_t tot = n * (b * (b - 1) / 2);
+  if (tot <= 0) return POETX_OK;
+  return launch("pack_skew_grad", s, [&] { k_pack_skew_grad<<<(unsigned)cdiv(tot, 256), 256, 0, s>>>(M, dtheta, n, b); });
+}
+
+__global__ void k_lincomb(float *__restrict__ out, int64_t n, int64_t b, float cI, const float *X0,
+                          float c0, const float *X1, float c1, const float *X2, float c2,
+                          const float *X3, float c3) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t bb = b * b;
+  if (e >= n * bb) return;
+  int64_t rc = e % bb;
+  float v = (rc / b == rc % b) ? cI : 0.f;
+  if (X0) v += c0 * X0[e];
+  if (X1) v += c1 * X1[e];
+  if (X2) v += c2 * X2[e];
+  if (X3) v += c3 * X3[e];
+  out[e] = v;
+}
+
+int lincomb(float *out, int64_t n, int64_t b, float cI, const float *X0, float c0, const float *X1,
+            float c1, const float *X2, float c2, const float *X3, float c3, hipStream_t s) {
+  int64_t tot = n * b * b;
+  if (tot <= 0) return POETX_OK;
+  return launch("lincomb", s, [&] {
+    k_lincomb<<<(unsigned)cdiv(tot, 256), 256, 0, s>>>(out, n, b, cI, X0, c0, X1, c1, X2, c2, X3, c3);
+  });
+}
+
+__global__ void k_reduce_parts(const float *__restrict__ in, float *__restrict__ out, int64_t elems,
+                               int64_t parts, int64_t stride) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= elems) return;
+  float acc = 0.f;
+  for (int64_t p = 0; p < parts; ++p) acc += in[p * stride + e];
+  out[e] = acc;
+}
+
+int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int64_t stride,
+                 hipStream_t s) {
+  if (elems <= 0) return POETX_OK;
+  return launch("reduce_parts", s, [&] {
+    k_reduce_parts<<<(unsigned)cdiv(elems, 256), 256, 0, s>>>(in, out, elems, parts, stride);
+  });
+}
+
+}  // namespace poetx

@@ -1,0 +1,70 @@
+// Host-side launchers of the HIP kernels (internal to libpoetx).
+#pragma once
+
+#include "common.h"
+
+namespace poetx {
+
+// ---------------------------------------------------------------------------
+// Strided batched product on the vector ALUs with float32 accumulation:
+//   C[z][m][n] = alpha * scaleN[n] * sum_k (A[z][m][k] * scaleK[k]) * B[z][k][n]
+//                + beta * D[z][m][n]
+// Any strides; A/B dtypes F32, BF16 or I8; C dtype F32 or BF16; D float32 (optional).
+// Used for float32 layers, for shapes outside the MFMA kernels' tiling, and as
+// the building block of the float32 Cayley-Neumann steps.
+// ---------------------------------------------------------------------------
+struct GemmDesc {
+  int64_t M = 0, N = 0, K = 0, batch = 1;
+  const void *A = nullptr; int a_dt = POETX_F32; int64_t sAb = 0, sAm = 0, sAk = 0;
+  const void *B = nullptr; int b_dt = POETX_F32; int64_t sBb = 0, sBk = 0, sBn = 0;
+  void *C = nullptr;       int c_dt = POETX_F32; int64_t sCb = 0, sCm = 0, sCn = 0;
+  const float *D = nullptr; int64_t sDb = 0, sDm = 0, sDn = 0;
+  float alpha = 1.f, beta = 0.f;
+  const float *scaleN = nullptr, *scaleK = nullptr;
+};
+int gemm_generic(const GemmDesc &g, hipStream_t s);
+
+// Column permutation of a row-major [rows][cols] matrix of esize-byte elements:
+//   gather : out[r][i] = in[rperm ? rperm[r] : r][cperm[i]]
+//   scatter: out[r][cperm[i]] = in[r][i]
+int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esize,
+                 const int32_t *rperm, const int32_t *cperm, bool scatter, hipStream_t s);
+// out[i] = src[perm[i]] for float32 vectors
+int gather_f32(const float *src, float *out, int64_t n, const int32_t *perm, hipStream_t s);
+
+// Packed skew helpers (Method §4 storage).
+int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t s);
+int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s);
+// out = c0*X0 + c1*X1 + c2*X2 + c3*X3 + cI*I over n blocks of b x b (null X_i skipped)
+int lincomb(float *out, int64_t n, int64_t b, float cI, const float *X0, float c0,
+            const float *X1, float c1, const float *X2, float c2, const float *X3, float c3,
+            hipStream_t s);
+// out[e] = sum_{p < parts} in[p * stride + e], in a fixed order (deterministic)
+int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int64_t stride,
+                 hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA products (gfx950 v_mfma_f32_16x16x32_bf16), float32 accumulation.
+//   C[z][m][n] = scaleN[n] * sum_k A[z][m][k] * B[z][k][n]
+// Operand layouts in memory:
+//   A: a_km == false -> element (m, k) at A + z*sAb + m*lda + k      (k contiguous)
+//      a_km == true  -> element (m, k) at A + z*sAb + k*lda + m      (m contiguous)
+//   B: b_km == false -> element (k, n) at B + z*sBb + n*ldb + k      (k contiguous)
+//      b_km == true  -> element (k, n) at B + z*sBb + k*ldb + n      (n contiguous)
+//   C: element (m, n) at C + z*sCb + m*ldc + n, bf16 or float32
+// Split-K: k range [kz*kchunk, (kz+1)*kchunk) of split kz goes to C + kz*sCsplit
+// (kchunk a multiple of 64, splits == ceil(K / kchunk)).
+// Requirements (checked): N % 64 == 0, K % 64 == 0 (per split), M any (masked).
+// B may be I8 (converted exactly to bf16 in the kernel).
+// ---------------------------------------------------------------------------
+struct MfmaDesc {
+  int64_t M = 0, N = 0, K = 0, batch = 1, splits = 1, kchunk = 0;
+  const void *A = nullptr; bool a_km = false; int64_t lda = 0, sAb = 0;
+  const void *B = nullptr; bool b_km = false; int b_dt = POETX_BF16; int64_t ldb = 0, sBb = 0;
+  void *C = nullptr; int c_dt = POETX_BF16; int64_t ldc = 0, sCb = 0, sCsplit = 0;
+  const float *scaleN = nullptr;
+};
+bool mfma_supported(const MfmaDesc &d);
+int gemm_mfma(const MfmaDesc &d, hipStream_t s);
+
+}  // namespace poetx

@@ -1,0 +1,77 @@
+"""One POET-X layer step on the GPU through the C ABI: CNP forward (both sides),
+layer forward, layer backward (which ends with the CNP backward).
+
+Holds the device tensors of one layer (merged weight, packed thetas, G's,
+activations and gradient buffers) so that steps can be repeated without
+re-uploading.  Marshalling only; the arithmetic is in libpoetx.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def upload(arr, dtype: str, device="cuda"):
+    if arr is None:
+        return None
+    a = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+class LayerStep:
+    def __init__(self, wl, inputs: dict, variant: str = "fast", device="cuda", perms: bool = True):
+        self.wl = wl
+        self.variant = B.POETX_FAST if variant == "fast" else B.POETX_MEM
+        act = _TORCH[wl.act]
+        self.act = act
+        dev = torch.device(device)
+        self.dev = dev
+        self.perm_in = upload(inputs["perm_in"], "i32", dev) if perms and inputs["perm_in"] is not None else None
+        self.perm_out = upload(inputs["perm_out"], "i32", dev) if perms and inputs["perm_out"] is not None else None
+        if wl.w == "i8":
+            w = upload(inputs["w_q"], "i8", dev)
+            s = upload(inputs["w_s"], "f32", dev)
+        else:
+            w = upload(inputs["w"], wl.w, dev)
+            s = None
+        # phase start: merge the weight-side permutations into W once (Method §2)
+        self.w_merged, self.w_scale = B.poetx_merge_perm(w, self.perm_out, self.perm_in, s)
+        del w
+        self.theta_r = upload(inputs["theta_r"], "f32", dev)
+        self.theta_p = upload(inputs["theta_p"], "f32", dev)
+        self.x = upload(inputs["x"], wl.act, dev)
+        self.dz = upload(inputs["dz"], wl.act, dev)
+        n, b = self.x.shape[0], wl.b
+        self.g_r = torch.empty((wl.d_in // b, b, b), dtype=act, device=dev)
+        self.g_p = torch.empty((wl.d_out // b, b, b), dtype=act, device=dev)
+        self.z = torch.empty((n, wl.d_out), dtype=act, device=dev)
+        self.saved_b = torch.empty((n, wl.d_out), dtype=act, device=dev) if self.variant == B.POETX_FAST else None
+        self.dx = torch.empty((n, wl.d_in), dtype=act, device=dev)
+        self.dtheta_r = torch.empty_like(self.theta_r)
+        self.dtheta_p = torch.empty_like(self.theta_p)
+        self.layer = B.Layer(self.w_merged, self.theta_r, self.theta_p, self.g_r, self.g_p, b,
+                             act_dtype=act, variant=self.variant, w_scale=self.w_scale,
+                             perm_in=self.perm_in, perm_out=self.perm_out)
+
+    def cnp(self):
+        B.poetx_cnp(B.POETX_CNP_FWD, self.theta_r, self.wl.b, g=self.g_r)
+        B.poetx_cnp(B.POETX_CNP_FWD, self.theta_p, self.wl.b, g=self.g_p)
+
+    def forward(self):
+        B.poetx_forward(self.layer, self.x, self.z, self.saved_b)
+
+    def backward(self, want_dg=False):
+        return B.poetx_backward(self.layer, self.x, self.dz, self.saved_b, dx=self.dx,
+                                dtheta_r=self.dtheta_r, dtheta_p=self.dtheta_p, want_dg=want_dg)
+
+    def step(self, want_dg=False):
+        self.cnp()
+        self.forward()
+        return self.backward(want_dg)

@@ -1,0 +1,68 @@
+"""Shared test helpers: host<->device marshalling, oracle runs, error metrics."""
+
+import numpy as np
+
+from oracle import poetx_oracle as O
+from orthogonal_reparameterized_amd import workloads as WL
+
+
+def to_dev(arr, dtype: str):
+    """Host array in storage dtype -> torch tensor on cuda:0 (bf16 from its bit pattern)."""
+    import torch
+    if arr is None:
+        return None
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def to_host_f64(t):
+    """Device tensor -> exact float64 numpy array."""
+    import torch
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def norm_max_err(got, ref):
+    """||got - ref||_inf / ||ref||_inf."""
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def rel_fro(got, ref):
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def rel_fro_per_block(got, ref):
+    """max over blocks of ||got_j - ref_j||_F / ||ref_j||_F."""
+    g = got.reshape(got.shape[0], -1)
+    r = ref.reshape(ref.shape[0], -1)
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(num / den))
+
+
+def bf16_ulp(v):
+    """Spacing of bfloat16 numbers at |v| (8 significant bits)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def oracle_layer(inp, wl, n=None):
+    """Run the oracle's full step on stored inputs (exact float64 widening)."""
+    x = WL.to_f64(inp["x"], wl.act)
+    dz = WL.to_f64(inp["dz"], wl.act)
+    if n is not None:
+        x, dz = x[:n], dz[:n]
+    if wl.w == "i8":
+        qm, sm = O.merge_perm_int8(inp["w_q"], inp["w_s"], inp["perm_out"], inp["perm_in"])
+        wm = O.dequantize_rows(qm, sm)
+    else:
+        wm = O.merge_perm(WL.to_f64(inp["w"], wl.w), inp["perm_out"], inp["perm_in"])
+    return O.poetx_step(x, dz, wm, inp["theta_r"].astype(np.float64), inp["theta_p"].astype(np.float64),
+                        wl.b, inp["perm_in"], inp["perm_out"])

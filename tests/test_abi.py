@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, answers workspace queries, and rejects bad arguments on the
+host with the documented status codes before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "poetx.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from orthogonal_reparameterized_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(poetx_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(B):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    lib = ctypes.CDLL(B.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(B):
+    assert re.match(r"\d+\.\d+\.\d+", B.version())
+    for code, name in ((0, "POETX_OK"), (-1, "POETX_ERR_INVALID_ARG"), (-2, "POETX_ERR_SHAPE"),
+                       (-3, "POETX_ERR_UNSUPPORTED"), (-4, "POETX_ERR_WORKSPACE"), (-5, "POETX_ERR_HIP")):
+        assert B.raw.poetx_status_string(code).decode() == name
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def layer(B, **kw):
+    c = B.PoetxLayerC()
+    c.d_in, c.d_out, c.b = kw.get("d_in", 512), kw.get("d_out", 768), kw.get("b", 256)
+    c.act_dtype = kw.get("act", B.POETX_BF16)
+    c.w_dtype = kw.get("w", B.POETX_BF16)
+    c.g_dtype = kw.get("g", B.POETX_BF16)
+    c.variant = kw.get("variant", B.POETX_FAST)
+    for f in ("w_merged", "theta_r", "theta_p", "g_r", "g_p"):
+        setattr(c, f, kw.get(f, FAKE))
+    c.w_scale = kw.get("w_scale", None)
+    return c
+
+
+def fwd(B, c, n=64, ws=None, ws_bytes=0, x=FAKE, z=FAKE, saved=FAKE):
+    nb = ctypes.c_size_t(ws_bytes)
+    st = B.raw.poetx_forward(ctypes.byref(c), n, x, z, saved, ws, ctypes.byref(nb), None)
+    return st, nb.value
+
+
+def bwd(B, c, n=64, ws=None, ws_bytes=0, saved=FAKE, dtr=FAKE, dtp=FAKE):
+    nb = ctypes.c_size_t(ws_bytes)
+    st = B.raw.poetx_backward(ctypes.byref(c), n, FAKE, FAKE, saved, FAKE, dtr, dtp, None, None, ws,
+                              ctypes.byref(nb), None)
+    return st, nb.value
+
+
+def test_workspace_queries(B):
+    st, need_fast = fwd(B, layer(B))
+    assert st == B.POETX_OK and need_fast > 0
+    st, need_mem = fwd(B, layer(B, variant=B.POETX_MEM), saved=None)
+    assert st == B.POETX_OK and need_mem > need_fast  # mem keeps B in the workspace
+    st, need_b = bwd(B, layer(B))
+    assert st == B.POETX_OK and need_b > 0
+    nb = ctypes.c_size_t(0)
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 16, 256, None, None, B.POETX_BF16, None, B.POETX_F32, None,
+                           None, ctypes.byref(nb), None) == B.POETX_OK
+    assert nb.value >= 16 * 256 * 256 * 4
+
+
+def test_validation_codes(B):
+    ok = layer(B)
+    # shape errors
+    assert fwd(B, layer(B, b=100))[0] == B.POETX_ERR_SHAPE          # 100 does not divide 512
+    assert fwd(B, layer(B, b=1))[0] == B.POETX_ERR_SHAPE
+    assert fwd(B, layer(B, b=1024, d_in=2048, d_out=2048))[0] == B.POETX_ERR_SHAPE
+    # invalid arguments
+    assert fwd(B, layer(B, act=7))[0] == B.POETX_ERR_INVALID_ARG
+    assert fwd(B, layer(B, variant=5))[0] == B.POETX_ERR_INVALID_ARG
+    assert fwd(B, ok, n=-1)[0] == B.POETX_ERR_INVALID_ARG
+    assert fwd(B, layer(B, w_merged=None), ws=FAKE, ws_bytes=1 << 40)[0] == B.POETX_ERR_INVALID_ARG
+    assert fwd(B, ok, ws=FAKE, ws_bytes=1 << 40, x=None)[0] == B.POETX_ERR_INVALID_ARG
+    assert fwd(B, ok, ws=FAKE, ws_bytes=1 << 40, saved=None)[0] == B.POETX_ERR_INVALID_ARG
+    assert fwd(B, layer(B, variant=B.POETX_MEM))[0] == B.POETX_ERR_INVALID_ARG  # mem with saved_b
+    assert bwd(B, ok, ws=FAKE, ws_bytes=1 << 40, dtr=None)[0] == B.POETX_ERR_INVALID_ARG
+    # unsupported combinations: int8 weight with the fast variant (POET-XQ needs recompute)
+    assert fwd(B, layer(B, w=B.POETX_I8, w_scale=FAKE))[0] == B.POETX_ERR_UNSUPPORTED
+    assert fwd(B, layer(B, w=B.POETX_F32))[0] == B.POETX_ERR_UNSUPPORTED    # mixed fp32 weight, bf16 act
+    assert fwd(B, layer(B, g=B.POETX_F32))[0] == B.POETX_ERR_UNSUPPORTED
+    # workspace too small
+    st, need = fwd(B, ok)
+    assert fwd(B, ok, ws=FAKE, ws_bytes=need - 1)[0] == B.POETX_ERR_WORKSPACE
+    st, need = bwd(B, ok)
+    assert bwd(B, ok, ws=FAKE, ws_bytes=need - 1)[0] == B.POETX_ERR_WORKSPACE
+    # CNP
+    nb = ctypes.c_size_t(1 << 40)
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 1, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+                           ctypes.byref(nb), None) == B.POETX_ERR_SHAPE
+    assert B.raw.poetx_cnp(9, 4, 64, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+                           ctypes.byref(nb), None) == B.POETX_ERR_INVALID_ARG
+    assert B.raw.poetx_cnp(B.POETX_CNP_BWD, 4, 64, FAKE, None, 0, None, B.POETX_F32, FAKE, FAKE,
+                           ctypes.byref(nb), None) == B.POETX_ERR_INVALID_ARG   # dg missing
+    small = ctypes.c_size_t(16)
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 64, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+                           ctypes.byref(small), None) == B.POETX_ERR_WORKSPACE
+    # merge
+    assert B.raw.poetx_merge_perm(None, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, None) == B.POETX_ERR_INVALID_ARG
+    assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_I8, 4, 4, None, None, FAKE, None, None) == B.POETX_ERR_INVALID_ARG

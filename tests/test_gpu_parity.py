@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Tolerances (derived in the design doc):
+  * float32 CNP outputs (G in fp32, dtheta from an identical dG): max over blocks
+    of the relative Frobenius error <= 1e-5.
+  * bf16 G: every element within one bf16 ulp of the oracle's value (absolute
+    floor 2^-20 for entries near zero).
+  * bf16 layer outputs and gradients: ||got - ref||_inf / ||ref||_inf <= 2e-2.
+  * float32 layer (workload 1): the same metric <= 1e-4.
+  * integer / byte work (the permutation merge): bit-exact.
+"""
+
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from oracle import poetx_oracle as O  # noqa: E402
+from orthogonal_reparameterized_amd import workloads as WL  # noqa: E402
+from tests.helpers import (bf16_ulp, norm_max_err, oracle_layer, rel_fro,  # noqa: E402
+                           rel_fro_per_block, to_host_f64)
+
+TOL_BF16 = 2e-2
+TOL_F32_LAYER = 1e-4
+TOL_CNP_F32 = 1e-5
+
+
+@pytest.fixture(scope="module")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from orthogonal_reparameterized_amd import binding
+    return binding
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------- CNP ----
+
+@pytest.mark.parametrize("n,b,std", [(8, 32, 0.02), (3, 256, 0.01), (2, 512, 0.01), (5, 48, 0.05)])
+def test_cnp_forward_f32(B, n, b, std):
+    _say(f"cnp fwd f32 n={n} b={b}")
+    theta, _ = WL.make_cnp_inputs(n, b, std, seed=100 + b)
+    g = B.poetx_cnp(B.POETX_CNP_FWD, torch.from_numpy(theta).cuda(), b, g_dtype=torch.float32)
+    ref = O.cnp_forward(theta.astype(np.float64), b)
+    assert rel_fro_per_block(to_host_f64(g), ref) <= TOL_CNP_F32
+
+
+@pytest.mark.parametrize("n,b", [(4, 256), (2, 512)])
+def test_cnp_forward_bf16_ulp(B, n, b):
+    _say(f"cnp fwd bf16 n={n} b={b}")
+    theta, _ = WL.make_cnp_inputs(n, b, 0.01, seed=200 + b)
+    g = B.poetx_cnp(B.POETX_CNP_FWD, torch.from_numpy(theta).cuda(), b, g_dtype=torch.bfloat16)
+    ref = O.cnp_forward(theta.astype(np.float64), b)
+    got = to_host_f64(g)
+    bound = np.maximum(bf16_ulp(ref), 2.0 ** -20)
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_cnp_zero_is_identity(B):
+    b = 256
+    th = torch.zeros((3, b * (b - 1) // 2), device="cuda")
+    for dt in (torch.float32, torch.bfloat16):
+        g = B.poetx_cnp(B.POETX_CNP_FWD, th, b, g_dtype=dt)
+        assert torch.equal(g.float().cpu(), torch.eye(b).expand(3, b, b))
+
+
+@pytest.mark.parametrize("n,b,std", [(8, 32, 0.02), (3, 256, 0.01), (2, 512, 0.01)])
+def test_cnp_backward_f32(B, n, b, std):
+    _say(f"cnp bwd f32 n={n} b={b}")
+    theta, dg = WL.make_cnp_inputs(n, b, std, seed=300 + b)
+    d = B.poetx_cnp(B.POETX_CNP_BWD, torch.from_numpy(theta).cuda(), b, dg=torch.from_numpy(dg).cuda())
+    ref = O.cnp_backward(theta.astype(np.float64), dg.astype(np.float64), b)
+    assert rel_fro_per_block(to_host_f64(d), ref) <= TOL_CNP_F32
+
+
+def test_cnp_workload2_sampled(B):
+    """Workload 2 at full size (4096 blocks, b=256): G and dtheta on sampled blocks."""
+    wl = WL.WORKLOADS[2]
+    _say("cnp workload 2 full size")
+    theta, dg = WL.make_cnp_inputs(wl.nblocks, wl.b, wl.theta_std, seed=WL.BASE_SEED + 2)
+    th_d = torch.from_numpy(theta).cuda()
+    g = B.poetx_cnp(B.POETX_CNP_FWD, th_d, wl.b, g_dtype=torch.bfloat16)
+    d = B.poetx_cnp(B.POETX_CNP_BWD, th_d, wl.b, dg=torch.from_numpy(dg).cuda())
+    torch.cuda.synchronize()
+    idx = np.array([0, 1, 777, 2048, 4095])
+    ref_g = O.cnp_forward(theta[idx].astype(np.float64), wl.b)
+    got_g = to_host_f64(g[torch.from_numpy(idx).cuda()])
+    assert np.all(np.abs(got_g - ref_g) <= np.maximum(bf16_ulp(ref_g), 2.0 ** -20))
+    ref_d = O.cnp_backward(theta[idx].astype(np.float64), dg[idx].astype(np.float64), wl.b)
+    assert rel_fro_per_block(to_host_f64(d[torch.from_numpy(idx).cuda()]), ref_d) <= TOL_CNP_F32
+
+
+# ----------------------------------------------------------------- merge ----
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "i8"])
+def test_merge_bit_exact(B, dt):
+    rng = np.random.default_rng(5)
+    d_out, d_in = 384, 640
+    pin, pout = rng.permutation(d_in).astype(np.int32), rng.permutation(d_out).astype(np.int32)
+    if dt == "i8":
+        w = rng.integers(-127, 128, size=(d_out, d_in)).astype(np.int8)
+        s = rng.random(d_out).astype(np.float32)
+        wm, sm = B.poetx_merge_perm(torch.from_numpy(w).cuda(), torch.from_numpy(pout).cuda(),
+                                    torch.from_numpy(pin).cuda(), torch.from_numpy(s).cuda())
+        qr, sr = O.merge_perm_int8(w, s, pout, pin)
+        assert np.array_equal(wm.cpu().numpy(), qr) and np.array_equal(sm.cpu().numpy(), sr)
+        return
+    w = rng.standard_normal((d_out, d_in)).astype(np.float32)
+    if dt == "bf16":
+        bits = WL.f32_to_bf16_bits(w)
+        wt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        ref = O.merge_perm(bits, pout, pin)
+        wm, _ = B.poetx_merge_perm(wt, torch.from_numpy(pout).cuda(), torch.from_numpy(pin).cuda())
+        assert np.array_equal(wm.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+    else:
+        wm, _ = B.poetx_merge_perm(torch.from_numpy(w).cuda(), torch.from_numpy(pout).cuda(),
+                                   torch.from_numpy(pin).cuda())
+        assert np.array_equal(wm.cpu().numpy(), O.merge_perm(w, pout, pin))
+
+
+# ----------------------------------------------------------------- layer ----
+
+def _run_step(wl, inp, variant, perms=True):
+    from orthogonal_reparameterized_amd.step import LayerStep
+    st = LayerStep(wl, inp, variant, perms=perms)
+    out = st.step(want_dg=True)
+    torch.cuda.synchronize()
+    return st, out
+
+
+def _compare(st, out, ref, tol, label):
+    errs = {
+        "G_R": norm_max_err(to_host_f64(st.g_r), ref["G_R"]),
+        "G_P": norm_max_err(to_host_f64(st.g_p), ref["G_P"]),
+        "Z": norm_max_err(to_host_f64(st.z), ref["Z"]),
+        "dX": norm_max_err(to_host_f64(out["dx"]), ref["dX"]),
+        "dG_R": norm_max_err(to_host_f64(out["dg_r"]), ref["dG_R"]),
+        "dG_P": norm_max_err(to_host_f64(out["dg_p"]), ref["dG_P"]),
+        "dtheta_R": norm_max_err(to_host_f64(out["dtheta_r"]), ref["dtheta_R"]),
+        "dtheta_P": norm_max_err(to_host_f64(out["dtheta_p"]), ref["dtheta_P"]),
+    }
+    fro = {k: rel_fro(to_host_f64(v), ref[r]) for k, v, r in
+           (("Z", st.z, "Z"), ("dX", out["dx"], "dX"), ("dtheta_R", out["dtheta_r"], "dtheta_R"))}
+    _say(f"{label}: normalized max errors {errs} rel-fro {fro}")
+    for k, e in errs.items():
+        assert e <= tol, f"{label} {k}: {e} > {tol}"
+
+
+@pytest.mark.parametrize("variant", ["fast", "mem"])
+def test_layer_workload1_f32(B, variant):
+    wl = WL.WORKLOADS[1]
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    st, out = _run_step(wl, inp, variant)
+    _compare(st, out, ref, TOL_F32_LAYER, f"workload1 {variant}")
+
+
+SMALL_BF16 = [
+    # (n_tokens, d_in, d_out, b, perms) -- several 128-wide tiles and ragged token tails
+    (257, 512, 768, 256, True),
+    (130, 1024, 512, 512, True),
+    (64, 256, 256, 128, False),
+    (1, 384, 256, 128, True),
+]
+
+
+@pytest.mark.parametrize("n,d_in,d_out,b,perms", SMALL_BF16)
+@pytest.mark.parametrize("variant", ["fast", "mem"])
+def test_layer_bf16_small(B, n, d_in, d_out, b, perms, variant):
+    wl = WL.Workload(90, "small bf16", n, d_in, d_out, b, "bf16", "bf16", "bf16", 0.01, d_in, perms=perms)
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    st, out = _run_step(wl, inp, variant)
+    _compare(st, out, ref, TOL_BF16, f"small n={n} {d_in}->{d_out} b={b} perms={perms} {variant}")
+
+
+def test_layer_bf16_generic_block(B):
+    """b = 48 (not a multiple of 128) goes through the vector-ALU path."""
+    wl = WL.Workload(91, "small bf16 b48", 70, 96, 144, 48, "bf16", "bf16", "bf16", 0.02, 96)
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    st, out = _run_step(wl, inp, "fast")
+    _compare(st, out, ref, TOL_BF16, "b=48 generic")
+
+
+def test_layer_int8_small(B):
+    wl = WL.Workload(92, "small int8", 200, 512, 768, 256, "bf16", "i8", "bf16", 0.01, 512, variants=("mem",))
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    st, out = _run_step(wl, inp, "mem")
+    _compare(st, out, ref, TOL_BF16, "int8 small")
+
+
+def test_int8_fast_rejected(B):
+    wl = WL.Workload(93, "int8 fast", 16, 256, 256, 128, "bf16", "i8", "bf16", 0.01, 256)
+    inp = WL.make_layer_inputs(wl)
+    from orthogonal_reparameterized_amd.step import LayerStep
+    st = LayerStep(wl, inp, "mem")
+    st.layer.variant = B.POETX_FAST
+    with pytest.raises(B.PoetxError) as e:
+        B.poetx_forward(st.layer, st.x, st.z, torch.empty_like(st.z))
+    assert e.value.status == B.POETX_ERR_UNSUPPORTED
+
+
+@functools.lru_cache(maxsize=None)
+def _full(key):
+    wl = WL.WORKLOADS[key]
+    inp = WL.make_layer_inputs(wl)
+    _say(f"oracle for workload {key} ...")
+    ref = oracle_layer(inp, wl)
+    _say(f"oracle for workload {key} done")
+    return wl, inp, ref
+
+
+@pytest.mark.parametrize("key,variant", [(3, "fast"), (3, "mem"), (4, "fast"), (4, "mem"), (5, "mem")])
+def test_layer_full_size(B, key, variant):
+    wl, inp, ref = _full(key)
+    _say(f"workload {key} {variant} on GPU")
+    st, out = _run_step(wl, inp, variant)
+    _compare(st, out, ref, TOL_BF16, f"workload{key} {variant}")
+
+
+def test_fast_mem_identical_and_deterministic(B):
+    wl = WL.Workload(94, "det", 300, 512, 512, 256, "bf16", "bf16", "bf16", 0.01, 512)
+    inp = WL.make_layer_inputs(wl)
+    st_f, out_f = _run_step(wl, inp, "fast")
+    z1, dx1, r1, p1 = st_f.z.clone(), out_f["dx"].clone(), out_f["dtheta_r"].clone(), out_f["dtheta_p"].clone()
+    out_f2 = st_f.step()
+    torch.cuda.synchronize()
+    assert torch.equal(st_f.z, z1) and torch.equal(out_f2["dx"], dx1)
+    assert torch.equal(out_f2["dtheta_r"], r1) and torch.equal(out_f2["dtheta_p"], p1)
+    st_m, out_m = _run_step(wl, inp, "mem")
+    assert torch.equal(st_m.z, z1) and torch.equal(out_m["dx"], dx1)
+    assert torch.equal(out_m["dtheta_r"], r1) and torch.equal(out_m["dtheta_p"], p1)
+
+
+def test_null_perm_equals_identity_perm(B):
+    wl = WL.Workload(95, "idperm", 100, 256, 512, 128, "bf16", "bf16", "bf16", 0.01, 256)
+    inp = WL.make_layer_inputs(wl, perms=False)
+    st0, out0 = _run_step(wl, inp, "fast", perms=False)
+    inp_id = dict(inp)
+    inp_id["perm_in"] = np.arange(wl.d_in, dtype=np.int32)
+    inp_id["perm_out"] = np.arange(wl.d_out, dtype=np.int32)
+    st1, out1 = _run_step(wl, inp_id, "fast", perms=True)
+    assert torch.equal(st0.z, st1.z) and torch.equal(out0["dx"], out1["dx"])
+    assert torch.equal(out0["dtheta_r"], out1["dtheta_r"])
+
+
+def test_zero_tokens(B):
+    wl = WL.Workload(96, "empty", 0, 256, 256, 128, "bf16", "bf16", "bf16", 0.01, 256)
+    inp = WL.make_layer_inputs(wl)
+    st, out = _run_step(wl, inp, "fast")
+    assert st.z.shape == (0, 256)
+    assert torch.count_nonzero(out["dtheta_r"]) == 0 and torch.count_nonzero(out["dtheta_p"]) == 0
