@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""POET-X layer forward+backward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 3]
+
+A step is one pass of the layer's hot path on one batch: CNP forward of G_R and
+G_P, the layer forward, the layer backward (which ends with the CNP backward).
+The permutation merge runs once per inner phase, before the timed region, and
+is timed separately.  Inputs are seeded synthetic data resident in HBM before
+timing starts.  Prints ONE JSON line.
+
+Extra modes used to make the committed profile summaries:
+    --copy-calibration   time a plain 1 GiB device copy (the HBM counter calibration)
+    --no-cpu             skip the CPU-oracle baseline leg
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "POET-X layer fwd+bwd tokens/s (4096², b=256) + % of MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+DOMINANT = "gemm_nt"
+
+
+def algorithmic(wl, variant, n):
+    """Per-step algorithmic flops and HBM bytes of each kernel label."""
+    di, do, b = wl.d_in, wl.d_out, wl.b
+    nr, np_ = di // b, do // b
+    ae = 2 if wl.act == "bf16" else 4
+    we = {"bf16": 2, "f32": 4, "i8": 1}[wl.w]
+    mem = variant == "mem"
+    ops = {}
+
+    def add(name, flops, nbytes):
+        f, y = ops.get(name, (0.0, 0.0))
+        ops[name] = (f + flops, y + nbytes)
+
+    g_bytes_r, g_bytes_p = nr * b * b * ae, np_ * b * b * ae
+    fronts = 2 if mem else 1  # mem recomputes gather, R-side apply and the forward GEMM
+    for _ in range(fronts):
+        add("permute_cols", 0, 2 * n * di * ae)
+        add("block_apply", 2.0 * n * di * b, 2 * n * di * ae + g_bytes_r)
+        add("gemm_nt", 2.0 * n * di * do, n * di * ae + do * di * we + n * do * ae)
+    if not mem:
+        add("permute_cols", 0, 2 * n * di * ae)          # backward re-gathers X for dG_R
+    add("block_apply", 2.0 * n * do * b, 2 * n * do * ae + g_bytes_p)            # Z~ = B G_P
+    add("permute_cols", 0, 2 * n * do * ae)                                       # scatter Z
+    add("permute_cols", 0, 2 * n * do * ae)                                       # gather dZ
+    add("block_apply_t", 2.0 * n * do * b, 2 * n * do * ae + g_bytes_p)          # dB
+    add("block_grad", 2.0 * n * do * b, 2 * n * do * ae)                          # dG_P
+    add("gemm_nn", 2.0 * n * di * do, n * do * ae + do * di * we + n * di * ae)   # dA
+    add("block_apply_t", 2.0 * n * di * b, 2 * n * di * ae + g_bytes_r)          # dX~
+    add("permute_cols", 0, 2 * n * di * ae)                                       # scatter dX
+    add("block_grad", 2.0 * n * di * b, 2 * n * di * ae)                          # dG_R
+    p = b * (b - 1) // 2
+    add("cnp_fwd", 4.0 * b ** 3 * (nr + np_), (nr + np_) * (4 * p + ae * b * b))
+    add("cnp_bwd", 14.0 * b ** 3 * (nr + np_), (nr + np_) * (4 * p + 4 * b * b + 4 * p))
+    return ops
+
+
+def step_flops(wl, variant, n):
+    return sum(f for f, _ in algorithmic(wl, variant, n).values())
+
+
+def layer_roofline_ms(wl, variant, n):
+    t = 0.0
+    for f, y in algorithmic(wl, variant, n).values():
+        t += max(f / (PEAK_BF16_TFLOPS * 1e12), y / (PEAK_HBM_GBS * 1e9))
+    return t * 1e3
+
+
+def time_steps(st, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        st.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def profile_steps(st, steps):
+    """Per-kernel-label launch counts and average durations (HIP events on the
+    library's launch stream, recorded around each launch)."""
+    import torch
+    from orthogonal_reparameterized_amd import binding as B
+    B.prof_read()  # clear
+    B.prof_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    B.prof_enable(False)
+    rec = B.prof_read()
+    return {k: (n / steps, ms / n) for k, (n, ms) in rec.items()}, wall
+
+
+def merge_time_ms(wl, inputs, reps=10):
+    import torch
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.step import upload
+    w = upload(inputs["w"] if wl.w != "i8" else inputs["w_q"], wl.w if wl.w != "i8" else "i8")
+    s = upload(inputs.get("w_s"), "f32") if wl.w == "i8" else None
+    pin, pout = upload(inputs["perm_in"], "i32"), upload(inputs["perm_out"], "i32")
+    out = torch.empty_like(w)
+    so = torch.empty_like(s) if s is not None else None
+    B.poetx_merge_perm(w, pout, pin, s, out, so)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        B.poetx_merge_perm(w, pout, pin, s, out, so)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * w.numel() * w.element_size()
+    return ms, nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(wl, inputs, target_s=15.0):
+    """The fp64 oracle on host cores on a bounded token sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import poetx_oracle as O
+    from orthogonal_reparameterized_amd import workloads as WL
+    wm = O.merge_perm(WL.to_f64(inputs["w"], wl.w), inputs["perm_out"], inputs["perm_in"])
+    tr, tp = inputs["theta_r"].astype(np.float64), inputs["theta_p"].astype(np.float64)
+
+    def run(n):
+        x = WL.to_f64(inputs["x"][:n], wl.act)
+        dz = WL.to_f64(inputs["dz"][:n], wl.act)
+        t0 = time.perf_counter()
+        O.poetx_step(x, dz, wm, tr, tp, wl.b, inputs["perm_in"], inputs["perm_out"])
+        return time.perf_counter() - t0
+
+    n = 256
+    t = run(n)
+    while t < target_s / 4 and n < wl.n_tokens:
+        n = min(wl.n_tokens, n * 4)
+        t = run(n)
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {wl.n_tokens} tokens of the workload, one full oracle step "
+                      f"(CNP fwd, layer fwd, layer bwd, CNP bwd) in float64 NumPy, {t:.1f} s"}
+
+
+def load_traffic(kernel, workload_key):
+    """HBM bytes per launch from the committed counter summary, if it matches this source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_workload{workload_key}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "orthogonal_reparameterized_amd", "csrc", "k_mfma.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("k_mfma_sha") != sha or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                      "GB_s_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-mem", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard by tokens with an all-reduce of dtheta).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    from orthogonal_reparameterized_amd import workloads as WL
+    from orthogonal_reparameterized_amd.step import LayerStep
+
+    wl = WL.WORKLOADS[args.workload]
+    inputs = WL.make_layer_inputs(wl)
+    n = wl.n_tokens
+    variants = {}
+    phases = {}
+    for variant in wl.variants:
+        if variant == "mem" and args.no_mem and "fast" in wl.variants:
+            continue
+        st = LayerStep(wl, inputs, variant)
+        ms = time_steps(st, args.steps, args.warmup)
+        prof, prof_wall = profile_steps(st, args.steps)
+        alg = algorithmic(wl, variant, n)
+        variants[variant] = {"ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+                             "layer_roofline_ms": layer_roofline_ms(wl, variant, n),
+                             "roofline_frac": layer_roofline_ms(wl, variant, n) / ms,
+                             "ms_per_step_with_event_hooks": prof_wall}
+        ph = {}
+        for name, (launches, avg_ms) in sorted(prof.items()):
+            ph[name] = {"launches_per_step": launches, "avg_ms": avg_ms}
+            if name in alg:
+                f, y = alg[name]
+                per = launches if launches else 1
+                ph[name]["tflops"] = f / per / (avg_ms * 1e-3) / 1e12
+                ph[name]["gbs"] = y / per / (avg_ms * 1e-3) / 1e9
+        phases[variant] = ph
+        del st
+        torch.cuda.empty_cache()
+
+    head = "fast" if "fast" in variants else "mem"
+    ms = variants[head]["ms_per_step"]
+    dom = phases[head].get(DOMINANT)
+    roof = None
+    if dom:
+        flops_launch = 2.0 * n * wl.d_in * wl.d_out
+        achieved = flops_launch / (dom["avg_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(DOMINANT, wl.key),
+                "kernel": DOMINANT, "avg_launch_ms": dom["avg_ms"],
+                "algorithmic_flops_per_launch": flops_launch}
+    merge_ms, merge_gbs = merge_time_ms(wl, inputs) if wl.w != "i8" else (None, None)
+    out = {
+        "metric": METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.act, "data": "synthetic",
+        "config": {"workload": wl.name, "n_tokens": n, "d_in": wl.d_in, "d_out": wl.d_out, "b": wl.b,
+                   "variant": head, "activation_permutations": wl.perms, "weight": wl.w},
+        "roofline": roof,
+        "variants": variants,
+        "phases": phases,
+        "merge_per_phase": {"ms": merge_ms, "GB_s": merge_gbs},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, inputs)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

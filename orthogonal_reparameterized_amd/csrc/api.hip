@@ -124,6 +124,7 @@ namespace {
 
 GemmDesc batched_f32(int64_t n, int64_t b, const float *A, const float *B, void *C, int c_dt) {
   GemmDesc g;
+  g.name = "cnp_product";
   g.M = g.N = g.K = b;
   g.batch = n;
   g.A = A; g.a_dt = POETX_F32; g.sAb = b * b; g.sAm = b; g.sAk = 1;
@@ -262,7 +263,9 @@ int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y,
     m.A = X; m.a_km = false; m.lda = d; m.sAb = b;
     m.B = G; m.b_km = !transposed; m.b_dt = POETX_BF16; m.ldb = b; m.sBb = b * b;
     m.C = Y; m.c_dt = p.act; m.ldc = d; m.sCb = b;
-    m.scaleN = scaleN;
+    m.scaleN = scaleN; m.sSNb = b;
+    m.name = transposed ? "block_apply_t" : "block_apply";
+    m.role = transposed ? MFMA_BLOCK_APPLY_T : MFMA_BLOCK_APPLY;
     return gemm_mfma(m, s);
   }
   GemmDesc g;
@@ -271,7 +274,8 @@ int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y,
   g.B = G; g.b_dt = p.gdt; g.sBb = b * b;
   if (transposed) { g.sBk = 1; g.sBn = b; } else { g.sBk = b; g.sBn = 1; }
   g.C = Y; g.c_dt = p.act; g.sCb = b; g.sCm = d; g.sCn = 1;
-  g.scaleN = scaleN;
+  g.scaleN = scaleN; g.sSNb = b;
+  g.name = transposed ? "block_apply_t_generic" : "block_apply_generic";
   return gemm_generic(g, s);
 }
 
@@ -295,6 +299,8 @@ int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, float *pa
     m.A = X; m.a_km = true; m.lda = d; m.sAb = b;
     m.B = Y; m.b_km = true; m.b_dt = POETX_BF16; m.ldb = d; m.sBb = b;
     m.C = parts; m.c_dt = POETX_F32; m.ldc = b; m.sCb = b * b; m.sCsplit = nb * b * b;
+    m.name = "block_grad";
+    m.role = MFMA_BLOCK_GRAD;
     return gemm_mfma(m, s);
   }
   GemmDesc g;
@@ -302,6 +308,7 @@ int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, float *pa
   g.A = X; g.a_dt = p.act; g.sAb = b; g.sAm = 1; g.sAk = d;
   g.B = Y; g.b_dt = p.act; g.sBb = b; g.sBk = d; g.sBn = 1;
   g.C = parts; g.c_dt = POETX_F32; g.sCb = b * b; g.sCm = b; g.sCn = 1;
+  g.name = "block_grad_generic";
   return gemm_generic(g, s);
 }
 
@@ -315,6 +322,8 @@ int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, hipStr
     m.B = L->w_merged; m.b_km = false; m.b_dt = p.w; m.ldb = p.din;
     m.C = B; m.c_dt = p.act; m.ldc = p.dout;
     m.scaleN = p.w == POETX_I8 ? L->w_scale : nullptr;
+    m.name = "gemm_nt";
+    m.role = MFMA_GEMM_NT;
     return gemm_mfma(m, s);
   }
   GemmDesc g;
@@ -323,6 +332,7 @@ int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, hipStr
   g.B = L->w_merged; g.b_dt = p.w; g.sBk = 1; g.sBn = p.din;
   g.C = B; g.c_dt = p.act; g.sCm = p.dout; g.sCn = 1;
   g.scaleN = p.w == POETX_I8 ? L->w_scale : nullptr;
+  g.name = "gemm_nt_generic";
   return gemm_generic(g, s);
 }
 
@@ -335,6 +345,8 @@ int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, hipS
     m.A = dB; m.a_km = false; m.lda = p.dout;
     m.B = L->w_merged; m.b_km = true; m.b_dt = p.w; m.ldb = p.din;
     m.C = dA; m.c_dt = p.act; m.ldc = p.din;
+    m.name = "gemm_nn";
+    m.role = MFMA_GEMM_NN;
     return gemm_mfma(m, s);
   }
   GemmDesc g;
@@ -342,6 +354,7 @@ int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, hipS
   g.A = dB; g.a_dt = p.act; g.sAm = p.dout; g.sAk = 1;
   g.B = L->w_merged; g.b_dt = p.w; g.sBk = p.din; g.sBn = 1;
   g.C = dA; g.c_dt = p.act; g.sCm = p.din; g.sCn = 1;
+  g.name = "gemm_nn_generic";
   return gemm_generic(g, s);
 }
 

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(GemmDesc g) {
       int64_t n = n0 + tx * 4 + j;
       if (n >= g.N) continue;
       float v = g.alpha * acc[i][j];
-      if (g.scaleN) v *= g.scaleN[n];
+      if (g.scaleN) v *= g.scaleN[z * g.sSNb + n];
       if (g.D) v += g.beta * g.D[z * g.sDb + m * g.sDm + n * g.sDn];
       st_f(C + m * g.sCm + n * g.sCn, v);
     }
@@ -70,8 +70,8 @@ template <typename TA, typename TB>
 static int gemm_generic_c(const GemmDesc &g, hipStream_t s) {
   dim3 grid((unsigned)cdiv(g.N, 64), (unsigned)cdiv(g.M, 64), (unsigned)g.batch);
   if (g.c_dt == POETX_F32)
-    return launch("gemm_generic", s, [&] { k_gemm_generic<TA, TB, float><<<grid, 256, 0, s>>>(g); });
-  return launch("gemm_generic", s, [&] { k_gemm_generic<TA, TB, bf16_t><<<grid, 256, 0, s>>>(g); });
+    return launch(g.name, s, [&] { k_gemm_generic<TA, TB, float><<<grid, 256, 0, s>>>(g); });
+  return launch(g.name, s, [&] { k_gemm_generic<TA, TB, bf16_t><<<grid, 256, 0, s>>>(g); });
 }
 
 template <typename TA>

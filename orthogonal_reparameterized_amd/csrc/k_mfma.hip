@@ -32,6 +32,7 @@ struct KArgs {
   const void *B; int64_t ldb, sBb;
   void *C; int64_t ldc, sCb, sCsplit;
   const float *scaleN;
+  int64_t sSNb;
 };
 
 __device__ inline uint32_t i8pair_to_bf16x2(int8_t lo, int8_t hi) {
@@ -151,7 +152,8 @@ __device__ inline bf16x8 frag_km(const bf16_t *t, int c0, int ks) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <bool AKM, bool BKM, bool BI8, bool OUTF32>
+// ROLE only separates the instantiations per use (distinct kernel symbols in traces).
+template <int ROLE, bool AKM, bool BKM, bool BI8, bool OUTF32>
 __global__ __launch_bounds__(NT) void k_mfma_gemm(KArgs a) {
   __shared__ __align__(16) bf16_t sA[2][TILE_ELEMS];
   __shared__ __align__(16) bf16_t sB[2][TILE_ELEMS];
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(NT) void k_mfma_gemm(KArgs a) {
       int64_t n = n0 + wn + 16 * j + 4 * (l >> 4);
       f32x4 v = acc[i][j];
       if (a.scaleN) {
-        float4 s = *(const float4 *)(a.scaleN + n);
+        float4 s = *(const float4 *)(a.scaleN + bidx * a.sSNb + n);
         v[0] *= s.x; v[1] *= s.y; v[2] *= s.z; v[3] *= s.w;
       }
       if constexpr (OUTF32) {
@@ -255,11 +257,11 @@ bool mfma_supported(const MfmaDesc &d) {
   return true;
 }
 
-template <bool AKM, bool BKM, bool BI8>
+template <int ROLE, bool AKM, bool BKM, bool BI8>
 static int run_c(const KArgs &k, const MfmaDesc &d, dim3 grid, hipStream_t s) {
   if (d.c_dt == POETX_F32)
-    return launch("mfma_gemm", s, [&] { k_mfma_gemm<AKM, BKM, BI8, true><<<grid, NT, 0, s>>>(k); });
-  return launch("mfma_gemm", s, [&] { k_mfma_gemm<AKM, BKM, BI8, false><<<grid, NT, 0, s>>>(k); });
+    return launch(d.name, s, [&] { k_mfma_gemm<ROLE, AKM, BKM, BI8, true><<<grid, NT, 0, s>>>(k); });
+  return launch(d.name, s, [&] { k_mfma_gemm<ROLE, AKM, BKM, BI8, false><<<grid, NT, 0, s>>>(k); });
 }
 
 int gemm_mfma(const MfmaDesc &d, hipStream_t s) {
@@ -273,14 +275,31 @@ int gemm_mfma(const MfmaDesc &d, hipStream_t s) {
   k.B = d.B; k.ldb = d.ldb; k.sBb = d.sBb;
   k.C = d.C; k.ldc = d.ldc; k.sCb = d.sCb; k.sCsplit = d.sCsplit;
   k.scaleN = d.scaleN;
+  k.sSNb = d.sSNb;
   dim3 grid((unsigned)(d.N / BN), (unsigned)cdiv(d.M, BM), (unsigned)(d.batch * d.splits));
   const bool i8 = d.b_dt == POETX_I8;
-  if (d.a_km) {
-    if (d.b_km) return i8 ? run_c<true, true, true>(k, d, grid, s) : run_c<true, true, false>(k, d, grid, s);
-    return i8 ? run_c<true, false, true>(k, d, grid, s) : run_c<true, false, false>(k, d, grid, s);
+  // the operand layouts each use needs; anything else is rejected
+  switch (d.role) {
+    case MFMA_GEMM_NT:
+      if (d.a_km || d.b_km) return POETX_ERR_UNSUPPORTED;
+      return i8 ? run_c<MFMA_GEMM_NT, false, false, true>(k, d, grid, s)
+                : run_c<MFMA_GEMM_NT, false, false, false>(k, d, grid, s);
+    case MFMA_GEMM_NN:
+      if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
+      return i8 ? run_c<MFMA_GEMM_NN, false, true, true>(k, d, grid, s)
+                : run_c<MFMA_GEMM_NN, false, true, false>(k, d, grid, s);
+    case MFMA_BLOCK_APPLY:
+      if (d.a_km || !d.b_km || i8) return POETX_ERR_UNSUPPORTED;
+      return run_c<MFMA_BLOCK_APPLY, false, true, false>(k, d, grid, s);
+    case MFMA_BLOCK_APPLY_T:
+      if (d.a_km || d.b_km || i8) return POETX_ERR_UNSUPPORTED;
+      return run_c<MFMA_BLOCK_APPLY_T, false, false, false>(k, d, grid, s);
+    case MFMA_BLOCK_GRAD:
+      if (!d.a_km || !d.b_km || i8) return POETX_ERR_UNSUPPORTED;
+      return run_c<MFMA_BLOCK_GRAD, true, true, false>(k, d, grid, s);
+    default:
+      return POETX_ERR_UNSUPPORTED;
   }
-  if (d.b_km) return i8 ? run_c<false, true, true>(k, d, grid, s) : run_c<false, true, false>(k, d, grid, s);
-  return i8 ? run_c<false, false, true>(k, d, grid, s) : run_c<false, false, false>(k, d, grid, s);
 }
 
 }  // namespace poetx

@@ -7,7 +7,7 @@ namespace poetx {
 
 // ---------------------------------------------------------------------------
 // Strided batched product on the vector ALUs with float32 accumulation:
-//   C[z][m][n] = alpha * scaleN[n] * sum_k (A[z][m][k] * scaleK[k]) * B[z][k][n]
+//   C[z][m][n] = alpha * scaleN[z*sSNb + n] * sum_k (A[z][m][k] * scaleK[k]) * B[z][k][n]
 //                + beta * D[z][m][n]
 // Any strides; A/B dtypes F32, BF16 or I8; C dtype F32 or BF16; D float32 (optional).
 // Used for float32 layers, for shapes outside the MFMA kernels' tiling, and as
@@ -21,6 +21,8 @@ struct GemmDesc {
   const float *D = nullptr; int64_t sDb = 0, sDm = 0, sDn = 0;
   float alpha = 1.f, beta = 0.f;
   const float *scaleN = nullptr, *scaleK = nullptr;
+  int64_t sSNb = 0;  // batch stride of scaleN
+  const char *name = "gemm_generic";  // label for the measurement hooks
 };
 int gemm_generic(const GemmDesc &g, hipStream_t s);
 
@@ -45,7 +47,7 @@ int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int6
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA products (gfx950 v_mfma_f32_16x16x32_bf16), float32 accumulation.
-//   C[z][m][n] = scaleN[n] * sum_k A[z][m][k] * B[z][k][n]
+//   C[z][m][n] = scaleN[z*sSNb + n] * sum_k A[z][m][k] * B[z][k][n]
 // Operand layouts in memory:
 //   A: a_km == false -> element (m, k) at A + z*sAb + m*lda + k      (k contiguous)
 //      a_km == true  -> element (m, k) at A + z*sAb + k*lda + m      (m contiguous)
@@ -57,12 +59,16 @@ int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int6
 // Requirements (checked): N % 64 == 0, K % 64 == 0 (per split), M any (masked).
 // B may be I8 (converted exactly to bf16 in the kernel).
 // ---------------------------------------------------------------------------
+enum MfmaRole { MFMA_GEMM_NT = 0, MFMA_GEMM_NN, MFMA_BLOCK_APPLY, MFMA_BLOCK_APPLY_T, MFMA_BLOCK_GRAD };
 struct MfmaDesc {
+  int role = MFMA_GEMM_NT;
   int64_t M = 0, N = 0, K = 0, batch = 1, splits = 1, kchunk = 0;
   const void *A = nullptr; bool a_km = false; int64_t lda = 0, sAb = 0;
   const void *B = nullptr; bool b_km = false; int b_dt = POETX_BF16; int64_t ldb = 0, sBb = 0;
   void *C = nullptr; int c_dt = POETX_BF16; int64_t ldc = 0, sCb = 0, sCsplit = 0;
   const float *scaleN = nullptr;
+  int64_t sSNb = 0;  // batch stride of scaleN
+  const char *name = "mfma_gemm";  // label for the measurement hooks
 };
 bool mfma_supported(const MfmaDesc &d);
 int gemm_mfma(const MfmaDesc &d, hipStream_t s);
