@@ -12,6 +12,10 @@ timing starts.  Prints ONE JSON line.
 Extra modes used to make the committed profile summaries:
     --copy-calibration   time a plain 1 GiB device copy (the HBM counter calibration)
     --no-cpu             skip the CPU-oracle baseline leg
+    --summarize-trace DB             markdown kernel table from a rocprofv3 --kernel-trace database
+    --summarize-counters F W CF CW   HBM traffic of the dominant kernel from four rocprofv3 --pmc
+                                     databases (FETCH_SIZE, WRITE_SIZE; then the same two counters
+                                     taken on --copy-calibration)
 """
 
 from __future__ import annotations
@@ -197,6 +201,62 @@ def copy_calibration():
                       "GB_s_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}))
 
 
+KERNEL_SYMBOL = {  # kernel label -> substring of its symbol in traces
+    "gemm_nt": "k_mfma_gemm<0,", "gemm_nn": "k_mfma_gemm<1,", "block_apply": "k_mfma_gemm<2,",
+    "block_apply_t": "k_mfma_gemm<3,", "block_grad": "k_mfma_gemm<4,",
+}
+
+
+def summarize_trace(db):
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), "
+                       "sum(duration) from kernels group by name order by sum(duration) desc").fetchall()
+    tot = sum(r[5] for r in rows)
+    print("| kernel | calls | avg us | min us | max us | share |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name, n, avg, mn, mx, sm in rows:
+        short = name.replace("(poetx::KArgs)", "").replace("poetx::", "")[:90]
+        print(f"| `{short}` | {n} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | {100 * sm / tot:.1f}% |")
+
+
+def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, label=DOMINANT):
+    import sqlite3
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        return con.execute("select kernel_name, count(*), avg(value) from counters_collection "
+                           "where counter_name = ? group by kernel_name", (counter,)).fetchall()
+
+    def pick(rows, match):
+        for name, n, v in rows:
+            if match in name.replace(" ", ""):
+                return n, v
+        raise SystemExit(f"no kernel matching {match}")
+
+    copy_kib = float(1 << 30) / 1024
+    _, cf = pick(per_kernel(copy_fetch_db, "FETCH_SIZE"), "copyBuffer")
+    _, cw = pick(per_kernel(copy_write_db, "WRITE_SIZE"), "copyBuffer")
+    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    sym = KERNEL_SYMBOL[label]
+    nf, f = pick(per_kernel(fetch_db, "FETCH_SIZE"), sym)
+    nw, w = pick(per_kernel(write_db, "WRITE_SIZE"), sym)
+    src = os.path.join(ROOT, "orthogonal_reparameterized_amd", "csrc", "k_mfma.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    print(f"kernel_label = {label}")
+    print(f"kernel_symbol_match = {sym}")
+    print(f"dispatches_fetch = {nf}")
+    print(f"dispatches_write = {nw}")
+    print(f"fetch_kib_per_dispatch_raw = {f:.1f}")
+    print(f"write_kib_per_dispatch_raw = {w:.1f}")
+    print(f"copy_fetch_kib_raw = {cf:.1f}  (1 GiB copy reads {copy_kib:.0f} KiB)")
+    print(f"copy_write_kib_raw = {cw:.1f}  (1 GiB copy writes {copy_kib:.0f} KiB)")
+    print(f"fetch_scale = {f_scale:.4f}")
+    print(f"write_scale = {w_scale:.4f}")
+    print(f"traffic_bytes_per_launch = {(f * f_scale + w * w_scale) * 1024:.0f}")
+    print(f"k_mfma_sha = {sha}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,7 +266,15 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mem", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DB")
+    ap.add_argument("--summarize-counters", nargs=4, metavar="DB")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the layer would shard by tokens with an all-reduce of dtheta).", file=sys.stderr)
