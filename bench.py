@@ -66,9 +66,11 @@ def algorithmic(wl, variant, n):
     add("block_apply_t", 2.0 * n * di * b, 2 * n * di * ae + g_bytes_r)          # dX~
     add("permute_cols", 0, 2 * n * di * ae)                                       # scatter dX
     add("block_grad", 2.0 * n * di * b, 2 * n * di * ae)                          # dG_R
-    p = b * (b - 1) // 2
-    add("cnp_fwd", 4.0 * b ** 3 * (nr + np_), (nr + np_) * (4 * p + ae * b * b))
-    add("cnp_bwd", 14.0 * b ** 3 * (nr + np_), (nr + np_) * (4 * p + 4 * b * b + 4 * p))
+    # CNP: forward = 2 float32-accurate b^3 products per block (Q.Q, S.T), backward = 6;
+    # bytes are the float32 operands each product reads and writes (A, B, epilogue terms, C).
+    nb = nr + np_
+    add("cnp_fwd_mm", 4.0 * b ** 3 * nb, nb * b * b * (8 + 4 + 12 + ae))
+    add("cnp_bwd_mm", 12.0 * b ** 3 * nb, nb * b * b * 4 * (3 + 3 + 3 + 4 + 6 + 7))
     return ops
 
 

@@ -114,12 +114,17 @@ extern "C" int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_d
 }
 
 // ==================================================================== CNP ====
-// Float32 steps of the Cayley-Neumann map (Method §4, eq. 9), Horner form
+// Cayley-Neumann map (Method §4, eq. 9) in Horner form
 //   G = I + 2Q + S (2I + 2Q + S),  S = Q^2,
-// and its adjoint (derived from eq. 9; the page does not print eq. 10):
-//   Qbar = C0 + Q C1 + S C2 + Q S C3 with
-//   C0 = 2Gb - 2GbQ + 2GbS - GbSQ, C1 = -2Gb + 2GbQ - GbS, C2 = 2Gb - GbQ, C3 = -Gb,
-// evaluated as (C0 + S C2) + Q (C1 + S C3).
+// and its adjoint (the page does not print eq. 10; this is the exact adjoint of
+// eq. 9).  With P = Q^T = -Q and Gb = dL/dG,
+//   Qbar = sum_{j+l<=3} a_{j+l+1} P^j Gb P^l,   a = (2, 2, 2, 1),
+// grouped by j and evaluated by Horner in P:
+//   K1 = Gb P, K2 = K1 P, K3 = K2 P,
+//   H2 = (2Gb + K1) + P Gb, H1 = (2Gb + 2K1 + K2) + P H2, Qbar = (2Gb + 2K1 + 2K2 + K3) + P H1,
+// then dtheta[k(i,j)] = Qbar[i][j] - Qbar[j][i].
+// For b % 64 == 0 every product runs on split-bf16 MFMA (k_cnp.hip); other b use
+// the float32 vector-ALU product.
 namespace {
 
 GemmDesc batched_f32(int64_t n, int64_t b, const float *A, const float *B, void *C, int c_dt) {
@@ -132,6 +137,13 @@ GemmDesc batched_f32(int64_t n, int64_t b, const float *A, const float *B, void 
   g.C = C; g.c_dt = c_dt; g.sCb = b * b; g.sCm = b; g.sCn = 1;
   return g;
 }
+
+GemmDesc with_terms(GemmDesc g, const float *D, float beta, float alpha) {
+  g.D = D; g.sDb = g.sCb; g.sDm = g.sCm; g.sDn = 1; g.beta = beta; g.alpha = alpha;
+  return g;
+}
+
+bool cnp_use_mfma(int64_t b) { return b % 64 == 0; }
 
 size_t cnp_ws_bytes(int dir, int64_t n, int64_t b) {
   Arena ar(nullptr);
@@ -148,38 +160,95 @@ int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype,
   float *Q = (float *)ar.take(blk), *S = (float *)ar.take(blk);
   float *T = (float *)ar.take(blk), *U = (float *)ar.take(blk);
   POETX_TRY(unpack_skew(theta, Q, n, b, s));
+  if (cnp_use_mfma(b)) {
+    CnpMMArgs a;
+    a.b = (int)b;
+    a.name = "cnp_fwd_mm";
+    a.seg[0].A = Q; a.seg[0].B = Q; a.seg[0].C = S; a.seg[0].nblk = n;
+    POETX_TRY(cnp_mm(a, s));                                                        // S = Q Q
+    POETX_TRY(lincomb(T, n, b, 2.f, Q, 2.f, S, 1.f, nullptr, 0.f, nullptr, 0.f, s)); // T = 2I + 2Q + S
+    CnpMMArgs c;
+    c.b = (int)b;
+    c.name = "cnp_fwd_mm";
+    c.cI = 1.f; c.ce[0] = 2.f;
+    c.seg[0].A = S; c.seg[0].B = T; c.seg[0].E[0] = Q; c.seg[0].nblk = n;
+    if (g_dtype == POETX_F32) c.seg[0].C = (float *)g;
+    else c.seg[0].Cb = (bf16_t *)g;
+    return cnp_mm(c, s);                                                            // G = I + 2Q + S T
+  }
   POETX_TRY(gemm_generic(batched_f32(n, b, Q, Q, S, POETX_F32), s));
   POETX_TRY(lincomb(T, n, b, 2.f, Q, 2.f, S, 1.f, nullptr, 0.f, nullptr, 0.f, s));
   POETX_TRY(lincomb(U, n, b, 1.f, Q, 2.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
-  GemmDesc gg = batched_f32(n, b, S, T, g, g_dtype);
-  gg.D = U; gg.sDb = b * b; gg.sDm = b; gg.sDn = 1; gg.beta = 1.f;
-  return gemm_generic(gg, s);
+  return gemm_generic(with_terms(batched_f32(n, b, S, T, g, g_dtype), U, 1.f, 1.f), s);
 }
 
-int cnp_bwd_impl(int64_t n, int64_t b, const float *theta, const float *dg, float *dtheta, void *ws,
-                 hipStream_t s) {
+struct CnpBwdSide {
+  int64_t n = 0;
+  const float *theta = nullptr, *dg = nullptr;
+  float *dtheta = nullptr;
+};
+
+// CNP backward of up to two independent sides sharing b (the R and P sides of a layer).
+int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
   Arena ar(ws);
-  size_t blk = (size_t)n * b * b * 4;
-  float *Q = (float *)ar.take(blk), *S = (float *)ar.take(blk), *Y = (float *)ar.take(blk);
-  float *Y2 = (float *)ar.take(blk), *Y3 = (float *)ar.take(blk), *B0 = (float *)ar.take(blk);
-  POETX_TRY(unpack_skew(theta, Q, n, b, s));
-  POETX_TRY(gemm_generic(batched_f32(n, b, Q, Q, S, POETX_F32), s));
-  POETX_TRY(gemm_generic(batched_f32(n, b, dg, Q, Y, POETX_F32), s));    // Gb Q
-  POETX_TRY(gemm_generic(batched_f32(n, b, dg, S, Y2, POETX_F32), s));   // Gb S
-  POETX_TRY(gemm_generic(batched_f32(n, b, Y2, Q, Y3, POETX_F32), s));   // Gb S Q
-  POETX_TRY(lincomb(B0, n, b, 0.f, dg, 2.f, Y, -2.f, Y2, 2.f, Y3, -1.f, s));   // C0
-  POETX_TRY(lincomb(Y3, n, b, 0.f, dg, -2.f, Y, 2.f, Y2, -1.f, nullptr, 0.f, s)); // C1
-  POETX_TRY(lincomb(Y2, n, b, 0.f, dg, 2.f, Y, -1.f, nullptr, 0.f, nullptr, 0.f, s)); // C2
-  GemmDesc v = batched_f32(n, b, S, dg, Y, POETX_F32);  // V = C1 - S Gb
-  v.alpha = -1.f; v.D = Y3; v.sDb = b * b; v.sDm = b; v.sDn = 1; v.beta = 1.f;
-  POETX_TRY(gemm_generic(v, s));
-  GemmDesc u = batched_f32(n, b, S, Y2, B0, POETX_F32);  // U = C0 + S C2
-  u.D = B0; u.sDb = b * b; u.sDm = b; u.sDn = 1; u.beta = 1.f;
-  POETX_TRY(gemm_generic(u, s));
-  GemmDesc q = batched_f32(n, b, Q, Y, Y2, POETX_F32);  // Qbar = U + Q V
-  q.D = B0; q.sDb = b * b; q.sDm = b; q.sDn = 1; q.beta = 1.f;
-  POETX_TRY(gemm_generic(q, s));
-  return pack_skew_grad(Y2, dtheta, n, b, s);
+  struct Bufs { float *Q, *K1, *K2, *K3, *Ha, *Hb; } B[2] = {};
+  SkewSegs un;
+  for (int i = 0; i < nside; ++i) {
+    size_t blk = (size_t)side[i].n * b * b * 4;
+    B[i] = {(float *)ar.take(blk), (float *)ar.take(blk), (float *)ar.take(blk),
+            (float *)ar.take(blk), (float *)ar.take(blk), (float *)ar.take(blk)};
+    un.src[i] = side[i].theta; un.dst[i] = B[i].Q; un.n[i] = side[i].n;
+  }
+  POETX_TRY(unpack_skew2(un, b, s));
+  if (cnp_use_mfma(b)) {
+    auto run = [&](auto fill, float alpha, float c0, float c1, float c2, float c3) {
+      CnpMMArgs a;
+      a.b = (int)b;
+      a.name = "cnp_bwd_mm";
+      a.alpha = alpha;
+      a.ce[0] = c0; a.ce[1] = c1; a.ce[2] = c2; a.ce[3] = c3;
+      for (int i = 0; i < nside; ++i) {
+        fill(a.seg[i], side[i], B[i]);
+        a.seg[i].nblk = side[i].n;
+      }
+      return cnp_mm(a, s);
+    };
+    // K1 = Gb P = -Gb Q ; K2 = -K1 Q ; K3 = -K2 Q
+    POETX_TRY(run([](CnpMMSeg &g, const CnpBwdSide &sd, Bufs &u) { g.A = sd.dg; g.B = u.Q; g.C = u.K1; }, -1.f, 0, 0, 0, 0));
+    POETX_TRY(run([](CnpMMSeg &g, const CnpBwdSide &sd, Bufs &u) { g.A = u.K1; g.B = u.Q; g.C = u.K2; }, -1.f, 0, 0, 0, 0));
+    POETX_TRY(run([](CnpMMSeg &g, const CnpBwdSide &sd, Bufs &u) { g.A = u.K2; g.B = u.Q; g.C = u.K3; }, -1.f, 0, 0, 0, 0));
+    // H2 = 2Gb + K1 - Q Gb
+    POETX_TRY(run([](CnpMMSeg &g, const CnpBwdSide &sd, Bufs &u) {
+      g.A = u.Q; g.B = sd.dg; g.C = u.Ha; g.E[0] = sd.dg; g.E[1] = u.K1; }, -1.f, 2.f, 1.f, 0, 0));
+    // H1 = 2Gb + 2K1 + K2 - Q H2
+    POETX_TRY(run([](CnpMMSeg &g, const CnpBwdSide &sd, Bufs &u) {
+      g.A = u.Q; g.B = u.Ha; g.C = u.Hb; g.E[0] = sd.dg; g.E[1] = u.K1; g.E[2] = u.K2; }, -1.f, 2.f, 2.f, 1.f, 0));
+    // Qbar = 2Gb + 2K1 + 2K2 + K3 - Q H1
+    POETX_TRY(run([](CnpMMSeg &g, const CnpBwdSide &sd, Bufs &u) {
+      g.A = u.Q; g.B = u.Hb; g.C = u.Ha; g.E[0] = sd.dg; g.E[1] = u.K1; g.E[2] = u.K2; g.E[3] = u.K3; },
+      -1.f, 2.f, 2.f, 2.f, 1.f));
+    SkewSegs pk;
+    for (int i = 0; i < nside; ++i) { pk.src[i] = B[i].Ha; pk.dst[i] = side[i].dtheta; pk.n[i] = side[i].n; }
+    return pack_skew_grad2(pk, b, s);
+  }
+  for (int i = 0; i < nside; ++i) {
+    const int64_t n = side[i].n;
+    const float *dg = side[i].dg;
+    Bufs &u = B[i];
+    if (n == 0) continue;
+    POETX_TRY(gemm_generic(with_terms(batched_f32(n, b, dg, u.Q, u.K1, POETX_F32), nullptr, 0.f, -1.f), s));
+    POETX_TRY(gemm_generic(with_terms(batched_f32(n, b, u.K1, u.Q, u.K2, POETX_F32), nullptr, 0.f, -1.f), s));
+    POETX_TRY(gemm_generic(with_terms(batched_f32(n, b, u.K2, u.Q, u.K3, POETX_F32), nullptr, 0.f, -1.f), s));
+    POETX_TRY(lincomb(u.Hb, n, b, 0.f, dg, 2.f, u.K1, 1.f, nullptr, 0.f, nullptr, 0.f, s));
+    POETX_TRY(gemm_generic(with_terms(batched_f32(n, b, u.Q, dg, u.Ha, POETX_F32), u.Hb, 1.f, -1.f), s));
+    POETX_TRY(lincomb(u.K1, n, b, 0.f, dg, 2.f, u.K1, 2.f, u.K2, 1.f, nullptr, 0.f, s));  // R1 (K1 -> 2Gb + 2K1 + K2)
+    POETX_TRY(gemm_generic(with_terms(batched_f32(n, b, u.Q, u.Ha, u.Hb, POETX_F32), u.K1, 1.f, -1.f), s));
+    // R0 = 2Gb + 2K1 + 2K2 + K3 = R1 + K2 + K3 (u.K1 now holds R1)
+    POETX_TRY(lincomb(u.K2, n, b, 0.f, u.K1, 1.f, u.K2, 1.f, u.K3, 1.f, nullptr, 0.f, s));
+    POETX_TRY(gemm_generic(with_terms(batched_f32(n, b, u.Q, u.Hb, u.Ha, POETX_F32), u.K2, 1.f, -1.f), s));
+    POETX_TRY(pack_skew_grad(u.Ha, side[i].dtheta, n, b, s));
+  }
+  return POETX_OK;
 }
 
 }  // namespace
@@ -207,7 +276,9 @@ extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *t
   if (nblocks == 0) return POETX_OK;
   hipStream_t s = (hipStream_t)stream;
   if (dir == POETX_CNP_FWD) return cnp_fwd_impl(nblocks, b, theta, g, g_dtype, ws, s);
-  return cnp_bwd_impl(nblocks, b, theta, (const float *)dg, dtheta, ws, s);
+  CnpBwdSide sd;
+  sd.n = nblocks; sd.theta = theta; sd.dg = (const float *)dg; sd.dtheta = dtheta;
+  return cnp_bwd_impl(b, &sd, 1, ws, s);
 }
 
 // ================================================================== layer ====
@@ -433,8 +504,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   float *part_p = (float *)ar.take((size_t)sp * p.np * bb * 4);
   float *gr = dg_r ? dg_r : (float *)ar.take((size_t)p.nr * bb * 4);
   float *gp = dg_p ? dg_p : (float *)ar.take((size_t)p.np * bb * 4);
-  size_t cws_r = cnp_ws_bytes(POETX_CNP_BWD, p.nr, b), cws_p = cnp_ws_bytes(POETX_CNP_BWD, p.np, b);
-  void *cws = ar.take(cws_r > cws_p ? cws_r : cws_p);
+  void *cws = ar.take(cnp_ws_bytes(POETX_CNP_BWD, p.nr, b) + cnp_ws_bytes(POETX_CNP_BWD, p.np, b));
   if (!ws) {
     *ws_bytes = ar.used;
     return POETX_OK;
@@ -481,7 +551,8 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
     POETX_TRY(lincomb(gp, p.np, b, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
   }
   // CNP backward on both sides (Method §4)
-  POETX_TRY(cnp_bwd_impl(p.nr, b, L->theta_r, gr, dtheta_r, cws, s));
-  POETX_TRY(cnp_bwd_impl(p.np, b, L->theta_p, gp, dtheta_p, cws, s));
-  return POETX_OK;
+  CnpBwdSide sides[2];
+  sides[0].n = p.nr; sides[0].theta = L->theta_r; sides[0].dg = gr; sides[0].dtheta = dtheta_r;
+  sides[1].n = p.np; sides[1].theta = L->theta_p; sides[1].dg = gp; sides[1].dtheta = dtheta_p;
+  return cnp_bwd_impl(b, sides, 2, cws, s);
 }

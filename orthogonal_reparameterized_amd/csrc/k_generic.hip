@@ -120,13 +120,103 @@ __global__ __launch_bounds__(256) void k_permute_cols(const T *__restrict__ in, 
   }
 }
 
+// Vectorized form: 16-byte global accesses, RB rows staged in LDS per pass, and the
+// permutation indices a thread needs kept in registers across all of its rows.
+// Requires cols % (16 / sizeof(T)) == 0 and cols / (16 / sizeof(T)) <= 8 * blockDim.
+template <typename T, int RB>
+__global__ __launch_bounds__(256) void k_permute_cols_v(const T *__restrict__ in, T *__restrict__ out,
+                                                        int64_t rows, int64_t cols,
+                                                        const int32_t *__restrict__ rperm,
+                                                        const int32_t *__restrict__ cperm, int scatter) {
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int MAXC = 8;            // chunks per thread per row
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  T *buf = (T *)lds_raw;
+  const int64_t nch = cols / V;
+  int idx[MAXC][V];
+#pragma unroll
+  for (int u = 0; u < MAXC; ++u) {
+    const int64_t ch = threadIdx.x + (int64_t)u * blockDim.x;
+#pragma unroll
+    for (int e = 0; e < V; ++e) idx[u][e] = ch < nch ? (cperm ? cperm[ch * V + e] : (int)(ch * V + e)) : 0;
+  }
+  for (int64_t r0 = (int64_t)blockIdx.x * RB; r0 < rows; r0 += (int64_t)gridDim.x * RB) {
+    const int nr = (int)(rows - r0 < RB ? rows - r0 : RB);
+    if (!scatter) {
+      for (int rr = 0; rr < nr; ++rr) {
+        const int64_t src = rperm ? rperm[r0 + rr] : r0 + rr;
+        for (int64_t ch = threadIdx.x; ch < nch; ch += blockDim.x)
+          *(uint4 *)(buf + rr * cols + ch * V) = *(const uint4 *)(in + src * cols + ch * V);
+      }
+      __syncthreads();
+      for (int rr = 0; rr < nr; ++rr) {
+#pragma unroll
+        for (int u = 0; u < MAXC; ++u) {
+          const int64_t ch = threadIdx.x + (int64_t)u * blockDim.x;
+          if (ch < nch) {
+            union { uint4 q; T v[V]; } o;
+#pragma unroll
+            for (int e = 0; e < V; ++e) o.v[e] = buf[rr * cols + idx[u][e]];
+            *(uint4 *)(out + (r0 + rr) * cols + ch * V) = o.q;
+          }
+        }
+      }
+    } else {
+      for (int rr = 0; rr < nr; ++rr) {
+#pragma unroll
+        for (int u = 0; u < MAXC; ++u) {
+          const int64_t ch = threadIdx.x + (int64_t)u * blockDim.x;
+          if (ch < nch) {
+            union { uint4 q; T v[V]; } o;
+            o.q = *(const uint4 *)(in + (r0 + rr) * cols + ch * V);
+#pragma unroll
+            for (int e = 0; e < V; ++e) buf[rr * cols + idx[u][e]] = o.v[e];
+          }
+        }
+      }
+      __syncthreads();
+      for (int rr = 0; rr < nr; ++rr)
+        for (int64_t ch = threadIdx.x; ch < nch; ch += blockDim.x)
+          *(uint4 *)(out + (r0 + rr) * cols + ch * V) = *(const uint4 *)(buf + rr * cols + ch * V);
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T>
+static int permute_v(const void *in, void *out, int64_t rows, int64_t cols, const int32_t *rperm,
+                     const int32_t *cperm, int sc, hipStream_t s) {
+  constexpr int V = 16 / sizeof(T);
+  const size_t row_bytes = (size_t)cols * sizeof(T);
+  const unsigned grid = (unsigned)(cdiv(rows, 2) < 2048 ? cdiv(rows, 2) : 2048);
+  if (row_bytes * 4 <= 65536) {
+    return launch("permute_cols", s, [&] {
+      k_permute_cols_v<T, 4><<<grid, 256, row_bytes * 4, s>>>((const T *)in, (T *)out, rows, cols, rperm, cperm, sc);
+    });
+  }
+  (void)V;
+  return launch("permute_cols", s, [&] {
+    k_permute_cols_v<T, 2><<<grid, 256, row_bytes * 2, s>>>((const T *)in, (T *)out, rows, cols, rperm, cperm, sc);
+  });
+}
+
 int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esize,
                  const int32_t *rperm, const int32_t *cperm, bool scatter, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return POETX_OK;
   size_t lds = (size_t)cols * esize;
   if (lds > 65536) return POETX_ERR_UNSUPPORTED;
-  unsigned grid = (unsigned)(rows < 4096 ? rows : 4096);
   int sc = scatter ? 1 : 0;
+  const int V = 16 / esize;
+  const bool vec_ok = cols % V == 0 && cols / V <= 8 * 256 && lds * 2 <= 65536 &&
+                      ((uintptr_t)in % 16) == 0 && ((uintptr_t)out % 16) == 0;
+  if (vec_ok) {
+    switch (esize) {
+      case 4: return permute_v<uint32_t>(in, out, rows, cols, rperm, cperm, sc, s);
+      case 2: return permute_v<uint16_t>(in, out, rows, cols, rperm, cperm, sc, s);
+      default: return permute_v<uint8_t>(in, out, rows, cols, rperm, cperm, sc, s);
+    }
+  }
+  unsigned grid = (unsigned)(rows < 4096 ? rows : 4096);
   switch (esize) {
     case 4:
       return launch("permute_cols", s, [&] {
@@ -160,43 +250,89 @@ __device__ inline int64_t triu_index(int64_t r, int64_t c, int64_t b) {
   return r * b - r * (r + 1) / 2 + (c - r - 1);
 }
 
-__global__ void k_unpack_skew(const float *__restrict__ theta, float *__restrict__ Q, int64_t n,
-                              int64_t b) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t bb = b * b;
-  if (e >= n * bb) return;
-  int64_t j = e / bb, rc = e % bb, r = rc / b, c = rc % b;
-  const float *t = theta + j * (b * (b - 1) / 2);
-  float v = 0.f;
-  if (r < c) v = t[triu_index(r, c, b)];
-  else if (r > c) v = -t[triu_index(c, r, b)];
-  Q[e] = v;
+// Both kernels walk 32 x 32 tiles (rb <= cb) of the upper triangle and handle the
+// mirrored tile through LDS, so every global access is contiguous along a row.
+__global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
+  __shared__ float t[32][33];
+  const int rb = blockIdx.y, cb = blockIdx.x;
+  if (cb < rb) return;
+  int64_t z = blockIdx.z;
+  int si = 0;
+  if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
+  const float *th = sg.src[si] + z * (b * (b - 1) / 2);
+  float *Q = sg.dst[si] + z * b * b;
+  const int tc = threadIdx.x & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tr = (threadIdx.x >> 5) + 8 * i;
+    const int64_t r = rb * 32 + tr, c = cb * 32 + tc;
+    float v = 0.f;
+    if (r < b && c < b) {
+      if (r < c) v = th[triu_index(r, c, b)];
+      if (r <= c) Q[r * b + c] = v;
+    }
+    t[tr][tc] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tr = (threadIdx.x >> 5) + 8 * i;
+    const int64_t r = cb * 32 + tr, c = rb * 32 + tc;  // mirrored element (r > c)
+    if (r < b && c < b && r > c) Q[r * b + c] = -t[tc][tr];
+  }
+}
+
+int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s) {
+  const int64_t nz = sg.n[0] + sg.n[1];
+  if (nz <= 0) return POETX_OK;
+  const unsigned T = (unsigned)cdiv(b, 32);
+  return launch("unpack_skew", s, [&] { k_unpack_skew<<<dim3(T, T, (unsigned)nz), 256, 0, s>>>(sg, b); });
 }
 
 int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t s) {
-  int64_t tot = n * b * b;
-  if (tot <= 0) return POETX_OK;
-  return launch("unpack_skew", s, [&] { k_unpack_skew<<<(unsigned)cdiv(tot, 256), 256, 0, s>>>(theta, Q, n, b); });
+  SkewSegs sg;
+  sg.src[0] = theta; sg.dst[0] = Q; sg.n[0] = n;
+  return unpack_skew2(sg, b, s);
 }
 
-__global__ void k_pack_skew_grad(const float *__restrict__ M, float *__restrict__ dtheta, int64_t n,
-                                 int64_t b) {
-  int64_t p = b * (b - 1) / 2;
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= n * p) return;
-  int64_t j = e / p, k = e % p;
-  // invert the row-major triangle offset: find r with start(r) <= k < start(r+1)
-  int64_t r = 0, start = 0;
-  while (start + (b - 1 - r) <= k) { start += b - 1 - r; ++r; }
-  int64_t c = r + 1 + (k - start);
-  const float *Mj = M + j * b * b;
-  dtheta[e] = Mj[r * b + c] - Mj[c * b + r];
+__global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b) {
+  __shared__ float up[32][33], lo[32][33];
+  const int rb = blockIdx.y, cb = blockIdx.x;
+  if (cb < rb) return;
+  int64_t z = blockIdx.z;
+  int si = 0;
+  if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
+  const float *M = sg.src[si] + z * b * b;
+  float *dth = sg.dst[si] + z * (b * (b - 1) / 2);
+  const int tc = threadIdx.x & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tr = (threadIdx.x >> 5) + 8 * i;
+    const int64_t r = rb * 32 + tr, c = cb * 32 + tc;
+    up[tr][tc] = (r < b && c < b) ? M[r * b + c] : 0.f;
+    const int64_t r2 = cb * 32 + tr, c2 = rb * 32 + tc;
+    lo[tr][tc] = (r2 < b && c2 < b) ? M[r2 * b + c2] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tr = (threadIdx.x >> 5) + 8 * i;
+    const int64_t r = rb * 32 + tr, c = cb * 32 + tc;
+    if (r < c && c < b) dth[triu_index(r, c, b)] = up[tr][tc] - lo[tc][tr];
+  }
+}
+
+int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s) {
+  const int64_t nz = sg.n[0] + sg.n[1];
+  if (nz <= 0) return POETX_OK;
+  const unsigned T = (unsigned)cdiv(b, 32);
+  return launch("pack_skew_grad", s, [&] { k_pack_skew_grad<<<dim3(T, T, (unsigned)nz), 256, 0, s>>>(sg, b); });
 }
 
 int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s) {
-  int64_t tot = n * (b * (b - 1) / 2);
-  if (tot <= 0) return POETX_OK;
-  return launch("pack_skew_grad", s, [&] { k_pack_skew_grad<<<(unsigned)cdiv(tot, 256), 256, 0, s>>>(M, dtheta, n, b); });
+  SkewSegs sg;
+  sg.src[0] = M; sg.dst[0] = dtheta; sg.n[0] = n;
+  return pack_skew_grad2(sg, b, s);
 }
 
 __global__ void k_lincomb(float *__restrict__ out, int64_t n, int64_t b, float cI, const float *X0,

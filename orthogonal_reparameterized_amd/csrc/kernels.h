@@ -34,7 +34,16 @@ int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esiz
 // out[i] = src[perm[i]] for float32 vectors
 int gather_f32(const float *src, float *out, int64_t n, const int32_t *perm, hipStream_t s);
 
-// Packed skew helpers (Method §4 storage).
+// Packed skew helpers (Method §4 storage), over up to two segments of blocks:
+//   unpack: dst = Q[n][b][b] from src = theta[n][b(b-1)/2]
+//   pack  : dst = dtheta[k(i,j)] = M[i][j] - M[j][i] from src = M[n][b][b]
+struct SkewSegs {
+  const float *src[2] = {nullptr, nullptr};
+  float *dst[2] = {nullptr, nullptr};
+  int64_t n[2] = {0, 0};
+};
+int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s);
+int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s);
 int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t s);
 int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s);
 // out = c0*X0 + c1*X1 + c2*X2 + c3*X3 + cI*I over n blocks of b x b (null X_i skipped)
@@ -72,5 +81,26 @@ struct MfmaDesc {
 };
 bool mfma_supported(const MfmaDesc &d);
 int gemm_mfma(const MfmaDesc &d, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Float32-accurate batched b x b products for the CNP steps (split-bf16 MFMA):
+//   C[z] = alpha * A[z] . B[z] + sum_i ce[i] * E_i[z] + cI * I,   b % 64 == 0
+// over the blocks of up to two segments; C written as float32 (C) and/or bf16 (Cb).
+// ---------------------------------------------------------------------------
+struct CnpMMSeg {
+  const float *A = nullptr, *B = nullptr;
+  float *C = nullptr;
+  bf16_t *Cb = nullptr;
+  const float *E[4] = {nullptr, nullptr, nullptr, nullptr};
+  int64_t nblk = 0;
+};
+struct CnpMMArgs {
+  int b = 0;
+  float alpha = 1.f, cI = 0.f;
+  float ce[4] = {0.f, 0.f, 0.f, 0.f};
+  CnpMMSeg seg[2];
+  const char *name = "cnp_mm";
+};
+int cnp_mm(const CnpMMArgs &a, hipStream_t s);
 
 }  // namespace poetx
