@@ -337,7 +337,7 @@ int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y,
     m.scaleN = scaleN; m.sSNb = b;
     m.name = transposed ? "block_apply_t" : "block_apply";
     m.role = transposed ? MFMA_BLOCK_APPLY_T : MFMA_BLOCK_APPLY;
-    return gemm_mfma(m, s);
+    return gemm_mfma_best(m, s);
   }
   GemmDesc g;
   g.M = p.N; g.N = b; g.K = b; g.batch = nb;
@@ -372,7 +372,7 @@ int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, float *pa
     m.C = parts; m.c_dt = POETX_F32; m.ldc = b; m.sCb = b * b; m.sCsplit = nb * b * b;
     m.name = "block_grad";
     m.role = MFMA_BLOCK_GRAD;
-    return gemm_mfma(m, s);
+    return gemm_mfma_best(m, s);
   }
   GemmDesc g;
   g.M = b; g.N = b; g.K = p.N; g.batch = nb;
@@ -395,7 +395,7 @@ int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, hipStr
     m.scaleN = p.w == POETX_I8 ? L->w_scale : nullptr;
     m.name = "gemm_nt";
     m.role = MFMA_GEMM_NT;
-    return gemm_mfma(m, s);
+    return gemm_mfma_best(m, s);
   }
   GemmDesc g;
   g.M = p.N; g.N = p.dout; g.K = p.din;
@@ -418,7 +418,7 @@ int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, hipS
     m.C = dA; m.c_dt = p.act; m.ldc = p.din;
     m.name = "gemm_nn";
     m.role = MFMA_GEMM_NN;
-    return gemm_mfma(m, s);
+    return gemm_mfma_best(m, s);
   }
   GemmDesc g;
   g.M = p.N; g.N = p.din; g.K = p.dout;

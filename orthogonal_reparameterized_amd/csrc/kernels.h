@@ -80,7 +80,13 @@ struct MfmaDesc {
   const char *name = "mfma_gemm";  // label for the measurement hooks
 };
 bool mfma_supported(const MfmaDesc &d);
-int gemm_mfma(const MfmaDesc &d, hipStream_t s);
+int gemm_mfma(const MfmaDesc &d, hipStream_t s);    // register-staged kernel (any operand dtype)
+bool mfma2_supported(const MfmaDesc &d);
+int gemm_mfma2(const MfmaDesc &d, hipStream_t s);   // direct-to-LDS kernel (bf16 operands)
+// the direct-to-LDS kernel where it applies, else the register-staged one
+inline int gemm_mfma_best(const MfmaDesc &d, hipStream_t s) {
+  return mfma2_supported(d) ? gemm_mfma2(d, s) : gemm_mfma(d, s);
+}
 
 // ---------------------------------------------------------------------------
 // Float32-accurate batched b x b products for the CNP steps (split-bf16 MFMA):
