@@ -22,11 +22,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-namespace {
-
-constexpr int BK = 64;
-constexpr uint32_t RSRC_DW3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-
+// kernel argument block (external linkage: kernel templates are instantiated with it)
 struct G2Args {
   int64_t M, N, K, Kc;
   int splits;
@@ -37,79 +33,125 @@ struct G2Args {
   const float *scaleN; int64_t sSNb;
 };
 
+namespace {
+
+constexpr uint32_t RSRC_DW3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
   uint32_t n = bytes > 0x7fffffff ? 0x7fffffffu : (uint32_t)(bytes < 0 ? 0 : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, (int)RSRC_DW3);
 }
 
-// k-contiguous tile [R][64] bf16 = 128-byte rows; 16-byte chunk c of row r sits at
-// chunk c ^ (r & 7).  One wave instruction fills 8 rows (1 KB).
-template <int R, int NW>
-__device__ inline void load_kc(__amdgpu_buffer_rsrc_t rs, int64_t ld, int64_t row0, int64_t k0,
-                               bf16_t *tile) {
-  constexpr int INSTR = R / 8 / NW;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < INSTR; ++i) {
-    const int grp = w * INSTR + i;
-    const int row = grp * 8 + (l >> 3);
-    const int lchunk = (l & 7) ^ (row & 7);
-    const int64_t off = ((row0 + row) * ld + k0 + lchunk * 8) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + grp * 8 * BK), 16, (int)off, 0, 0, 0);
-  }
+// s_waitcnt with vmcnt = N (expcnt, lgkmcnt left at their maxima); gfx9 encoding.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
 
-// k-major tile [64][C] bf16 = 2C-byte rows; chunk c of row r sits at c ^ ((r & 3) << 1)
-// (32-byte blocks rotate with the row so the 4 rows one ds_read_b64_tr_b16 group reads
-// fall in different banks).  One wave instruction fills 1 KB.
-template <int C, int NW>
-__device__ inline void load_km(__amdgpu_buffer_rsrc_t rs, int64_t ld, int64_t col0, int64_t k0,
-                               bf16_t *tile) {
-  constexpr int CH = C / 8;               // 16-byte chunks per row
-  constexpr int RPI = 64 / CH;            // rows per wave instruction
-  constexpr int INSTR = BK / RPI / NW;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+// k-contiguous tile [R][BKT] bf16 (BKT = 32 or 64 -> 64- or 128-byte rows).  The
+// 16-byte chunk c of row r sits at c ^ kc_key(r), which spreads the rows one
+// 8-lane ds_read_b128 phase touches over all 128 bytes of a bank sweep.  One wave
+// instruction (64 lanes x 16 B) fills 1 KB = 64 / (BKT/8) rows.
+template <int BKT>
+__device__ inline int kc_key(int r) { return BKT == 64 ? (r & 7) : ((r >> 1) & 3); }
+
+template <int R, int NW, int BKT>
+struct LoaderKC {
+  static constexpr int CR = BKT / 8;        // chunks per row
+  static constexpr int RPI = 64 / CR;       // rows per wave instruction
+  static constexpr int INSTR = R / RPI / NW;
+  int voff[INSTR];  // per-lane byte offset of its 16-byte chunk at k0 = 0
+  __device__ void init(int64_t ld, int64_t row0) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < INSTR; ++i) {
-    const int grp = w * INSTR + i;
-    const int row = grp * RPI + l / CH;
-    const int lchunk = (l % CH) ^ ((row & 3) << 1);
-    const int64_t off = ((k0 + row) * ld + col0 + lchunk * 8) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + grp * RPI * C), 16, (int)off, 0, 0, 0);
+    for (int i = 0; i < INSTR; ++i) {
+      const int row = (w * INSTR + i) * RPI + l / CR;
+      const int lchunk = (l % CR) ^ kc_key<BKT>(row);
+      voff[i] = (int)(((row0 + row) * ld + lchunk * 8) * 2);
+    }
   }
-}
+  // k0 is added to the per-lane offset: the raw-buffer range check covers only the
+  // lane offset (not soffset), and rows past the valid extent must read as zero.
+  __device__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t k0, int64_t ld, bf16_t *tile) const {
+    const int w = threadIdx.x >> 6;
+    const int kb = (int)(k0 * 2);
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * INSTR + i) * RPI * BKT), 16,
+                                               voff[i] + kb, 0, 0, 0);
+  }
+};
+
+// k-major tile [BKT][C] bf16 = 2C-byte rows; chunk c of row r sits at c ^ (km_key(r) << 1):
+// 32-byte blocks rotate with row bits {0, 1, 3}, so the 8 rows that two 16-lane groups of
+// one ds_read_b64_tr_b16 touch (k .. k+3 and k+8 .. k+11) land in 8 different 32-byte
+// bank groups.  One wave instruction fills 1 KB.
+__device__ inline int km_key(int r) { return (r & 3) | ((r >> 1) & 4); }
+
+template <int C, int NW, int BKT>
+struct LoaderKM {
+  static constexpr int CH = C / 8;     // 16-byte chunks per row
+  static constexpr int RPI = 64 / CH;  // rows per wave instruction
+  static constexpr int INSTR = BKT / RPI / NW;
+  int voff[INSTR];
+  __device__ void init(int64_t ld, int64_t col0) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int row = (w * INSTR + i) * RPI + l / CH;
+      const int lchunk = (l % CH) ^ (km_key(row) << 1);
+      voff[i] = (int)((row * ld + col0 + lchunk * 8) * 2);
+    }
+  }
+  __device__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t k0, int64_t ld, bf16_t *tile) const {
+    const int w = threadIdx.x >> 6;
+    const int kb = (int)(k0 * ld * 2);
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * INSTR + i) * RPI * C), 16,
+                                               voff[i] + kb, 0, 0, 0);
+  }
+};
 
 // MFMA operand fragment (lane l: 8 consecutive k of row/column l % 16).
+template <int BKT>
 __device__ inline bf16x8 frag_kc(const bf16_t *t, int r0, int ks) {
   const int l = threadIdx.x & 63, row = r0 + (l & 15);
-  const int pchunk = ((ks >> 3) + (l >> 4)) ^ (row & 7);
-  s16x8 v = *(const s16x8 *)(t + row * BK + pchunk * 8);
+  const int pchunk = ((ks >> 3) + (l >> 4)) ^ kc_key<BKT>(row);
+  s16x8 v = *(const s16x8 *)(t + row * BKT + pchunk * 8);
   return __builtin_bit_cast(bf16x8, v);
 }
+// From a k-major tile through ds_read_b64_tr_b16: within each 16-lane group, lane i
+// receives element i%4 of the 8-byte chunk that lane 4e + i/4 addressed (e = 0..3);
+// lane j addressing row kb + j/4, columns c0 + 4(j%4) .. +3 gives lane i the four
+// k values kb .. kb+3 of column c0 + i.
 template <int C>
 __device__ inline bf16x8 frag_km(const bf16_t *t, int c0, int ks) {
   const int l = threadIdx.x & 63, g = l >> 4, j = l & 15;
   const int col = c0 + 4 * (j & 3);
   const int r0 = ks + 8 * g + (j >> 2), r1 = r0 + 4;
-  const int p0 = ((col >> 3) ^ ((r0 & 3) << 1)) * 8 + (col & 7);
-  const int p1 = ((col >> 3) ^ ((r1 & 3) << 1)) * 8 + (col & 7);
+  const int p0 = ((col >> 3) ^ (km_key(r0) << 1)) * 8 + (col & 7);
+  const int p1 = ((col >> 3) ^ (km_key(r1) << 1)) * 8 + (col & 7);
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + r0 * C + p0));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + r1 * C + p1));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
 
+
 }  // namespace
 
-// ROLE separates instantiations per use; WGM x WGN waves, each computing a
-// (BM/WGM) x (BN/WGN) patch.
-template <int ROLE, int BM, int BN, int WGM, int WGN, bool AKM, bool BKM, bool OUTF32>
+// ROLE separates instantiations per use.  WGM x WGN waves, each computing a
+// (BM/WGM) x (BN/WGN) patch; k advances BKT per step through NST LDS stages with
+// NST-1 steps of prefetch in flight.
+template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
+  constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT;
+  constexpr int PF = NST - 1;
   extern __shared__ __align__(16) bf16_t smem[];
-  // stage s: A tile at smem + s*A_ELEMS, B tile at smem + 2*A_ELEMS + s*B_ELEMS
+  // stage s: A tile at smem + s*A_ELEMS, B tile at smem + NST*A_ELEMS + s*B_ELEMS
 
   // ---- tile mapping: batch/split in z; (m, n) from an XCD-aware order of blockIdx.x
   const int64_t z = blockIdx.z, bidx = z / a.splits, kz = z % a.splits;
@@ -141,36 +183,52 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  using LA = typename std::conditional<AKM, LoaderKM<BM, NW, BKT>, LoaderKC<BM, NW, BKT>>::type;
+  using LB = typename std::conditional<BKM, LoaderKM<BN, NW, BKT>, LoaderKC<BN, NW, BKT>>::type;
+  constexpr int LPS = LA::INSTR + LB::INSTR;  // loads per wave per stage
+  LA la;
+  LB lb;
+  la.init(a.lda, m0);
+  lb.init(a.ldb, n0);
   auto issue = [&](int buf, int64_t k0) {
-    bf16_t *ta = smem + buf * A_ELEMS, *tb = smem + 2 * A_ELEMS + buf * B_ELEMS;
-    if constexpr (AKM) load_km<BM, NW>(ra, a.lda, m0, k0, ta);
-    else load_kc<BM, NW>(ra, a.lda, m0, k0, ta);
-    if constexpr (BKM) load_km<BN, NW>(rb, a.ldb, n0, k0, tb);
-    else load_kc<BN, NW>(rb, a.ldb, n0, k0, tb);
+    la.issue(ra, k0, a.lda, smem + buf * A_ELEMS);
+    lb.issue(rb, k0, a.ldb, smem + NST * A_ELEMS + buf * B_ELEMS);
   };
 
-  int cur = 0;
-  if (kbeg < kend) issue(0, kbeg);
-  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage `cur` have landed
-    __syncthreads();                // ... and everyone's; stage cur^1 is free again
-    if (k0 + BK < kend) issue(cur ^ 1, k0 + BK);
-    const bf16_t *ta = smem + cur * A_ELEMS, *tb = smem + 2 * A_ELEMS + cur * B_ELEMS;
+  const int nk = (int)((kend - kbeg + BKT - 1) / BKT);
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 32) {
-      bf16x8 fa[FM], fb[FN];
+  for (int s = 0; s < PF; ++s)
+    if (s < nk) issue(s, kbeg + (int64_t)s * BKT);
+  for (int t = 0; t < nk; ++t) {
+    // stage t has landed for this wave once at most (PF-1) newer stages are outstanding
+    if (t + PF <= nk) wait_vmcnt<(PF - 1) * LPS>();
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // everyone's stage t is in LDS; stage t-1 is no longer read
+    if (t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
+    const int cur = t % NST;
+    const bf16_t *ta = smem + cur * A_ELEMS, *tb = smem + NST * A_ELEMS + cur * B_ELEMS;
+    // all fragments of the step are requested before the first MFMA, so the reads of
+    // the second 32-deep half overlap the MFMAs of the first
+    constexpr int KH = BKT / 32;
+    bf16x8 fa[KH][FM], fb[KH][FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = AKM ? frag_km<BM>(ta, wm + 16 * i, ks) : frag_kc(ta, wm + 16 * i, ks);
+    for (int h = 0; h < KH; ++h) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = BKM ? frag_km<BN>(tb, wn + 16 * j, ks) : frag_kc(tb, wn + 16 * j, ks);
+      for (int i = 0; i < FM; ++i)
+        fa[h][i] = AKM ? frag_km<BM>(ta, wm + 16 * i, 32 * h) : frag_kc<BKT>(ta, wm + 16 * i, 32 * h);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[h][j] = BKM ? frag_km<BN>(tb, wn + 16 * j, 32 * h) : frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
+    }
+#pragma unroll
+    for (int h = 0; h < KH; ++h)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           // operands swapped: lane l then holds C[m = l%16][n = 4*(l/16) + 0..3]
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-    }
-    cur ^= 1;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], acc[i][j], 0, 0, 0);
+
   }
 
   const int l = threadIdx.x & 63;
@@ -184,8 +242,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
       const int64_t n = n0 + wn + 16 * j + 4 * (l >> 4);
       f32x4 v = acc[i][j];
       if (a.scaleN) {
-        float4 s = *(const float4 *)(a.scaleN + bidx * a.sSNb + n);
-        v[0] *= s.x; v[1] *= s.y; v[2] *= s.z; v[3] *= s.w;
+        float4 sc = *(const float4 *)(a.scaleN + bidx * a.sSNb + n);
+        v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
       }
       if constexpr (OUTF32) {
         *(float4 *)(Cb + (m * a.ldc + n) * 4) = make_float4(v[0], v[1], v[2], v[3]);
@@ -199,41 +257,209 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   }
 }
 
-template <int ROLE, int BM, int BN, int WGM, int WGN, bool AKM, bool BKM>
+
+// Ping-pong schedule for the W' products (256 x 256 tile, 8 waves, BK = 64, 2 LDS
+// stages).  The waves form two groups of four, one wave of each group per SIMD.
+// Group 1 runs one phase behind group 0, so in every phase one group issues MFMAs
+// while the other reads its next fragments from LDS; a wave loads all fragments of a
+// k step into registers before its MFMA phase, so an LDS stage is free as soon as
+// both groups have read it.  Group 0 also issues the global->LDS loads of the next
+// stage at the start of its read phase and waits for them before the barrier that
+// ends its MFMA phase (two phases of latency cover).
+//   phase A of step t: group 0 reads stage t (and issues stage t+1); group 1 multiplies step t-1
+//   phase B of step t: group 0 multiplies step t;                     group 1 reads stage t
+template <int ROLE, bool AKM, bool BKM, bool OUTF32>
+__global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
+  constexpr int BM = 256, BN = 256, BKT = 64, WGN = 4;
+  constexpr int WTM = 128, WTN = 64, FM = WTM / 16, FN = WTN / 16;
+  constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT;
+  extern __shared__ __align__(16) bf16_t smem[];
+
+  const int64_t z = blockIdx.z, bidx = z / a.splits, kz = z % a.splits;
+  const int T = a.tiles_m * a.tiles_n;
+  int L = blockIdx.x;
+  if (T % 8 == 0) L = (L % 8) * (T / 8) + L / 8;
+  const int GM = a.tiles_m < 4 ? a.tiles_m : 4;
+  const int grp_size = GM * a.tiles_n;
+  const int grp = L / grp_size, first_m = grp * GM;
+  const int gm = (a.tiles_m - first_m) < GM ? (a.tiles_m - first_m) : GM;
+  const int local = L % grp_size;
+  const int tm = first_m + local % gm, tn = local / gm;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int64_t kbeg = kz * a.Kc;
+  const int64_t kend = (kbeg + a.Kc < a.K) ? kbeg + a.Kc : a.K;
+  const bf16_t *A = a.A + bidx * a.sAb;
+  const bf16_t *B = a.B + bidx * a.sBb;
+  const __amdgpu_buffer_rsrc_t ra = AKM ? make_rsrc(A, kend * a.lda * 2) : make_rsrc(A, a.M * a.lda * 2);
+  const __amdgpu_buffer_rsrc_t rb = BKM ? make_rsrc(B, kend * a.ldb * 2) : make_rsrc(B, a.N * a.ldb * 2);
+
+  const int wave = threadIdx.x >> 6, group = wave >> 2;
+  const int wm = (wave / WGN) * WTM, wn = (wave % WGN) * WTN;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  using LA = typename std::conditional<AKM, LoaderKM<BM, 4, BKT>, LoaderKC<BM, 4, BKT>>::type;
+  using LB = typename std::conditional<BKM, LoaderKM<BN, 4, BKT>, LoaderKC<BN, 4, BKT>>::type;
+  LA la;
+  LB lb;
+  if (group == 0) {
+    la.init(a.lda, m0);
+    lb.init(a.ldb, n0);
+  }
+  auto issue = [&](int buf, int64_t k0) {
+    la.issue(ra, k0, a.lda, smem + buf * A_ELEMS);
+    lb.issue(rb, k0, a.ldb, smem + 2 * A_ELEMS + buf * B_ELEMS);
+  };
+  bf16x8 fa[FM], fb[FN];  // fragments of one 32-deep half step
+  auto read_frags = [&](int buf, int h) {
+    const bf16_t *ta = smem + buf * A_ELEMS, *tb = smem + 2 * A_ELEMS + buf * B_ELEMS;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = AKM ? frag_km<BM>(ta, wm + 16 * i, 32 * h) : frag_kc<BKT>(ta, wm + 16 * i, 32 * h);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = BKM ? frag_km<BN>(tb, wn + 16 * j, 32 * h) : frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = (int)((kend - kbeg + BKT - 1) / BKT);
+  if (group == 0) {
+    if (nk > 0) issue(0, kbeg);
+    if (nk > 1) issue(1, kbeg + BKT);
+    wait_vmcnt<LA::INSTR + LB::INSTR>();  // stage 0 landed (stage 1 may still be in flight)
+    if (nk <= 1) __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // phase A: group 0 reads half h of stage t; group 1 multiplies the half before
+      if (group == 0) read_frags(t & 1, h);
+      else if (t > 0 || h > 0) multiply();
+      __syncthreads();
+      // phase B: group 0 multiplies half h; group 1 reads it
+      if (group == 0) {
+        multiply();
+        if (h == 1) __builtin_amdgcn_s_waitcnt(0);  // stage t+1 has landed
+      } else {
+        read_frags(t & 1, h);
+      }
+      __syncthreads();
+    }
+    // both groups are done with stage t: its buffer takes stage t+2
+    if (group == 0 && t + 2 < nk) issue(t & 1, kbeg + (int64_t)(t + 2) * BKT);
+  }
+  if (group == 1 && nk > 0) multiply();
+
+  const int l = threadIdx.x & 63;
+  char *Cb = (char *)a.C + (bidx * a.sCb + kz * a.sCsplit) * (OUTF32 ? 4 : 2);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + wm + 16 * i + (l & 15);
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + wn + 16 * j + 4 * (l >> 4);
+      f32x4 v = acc[i][j];
+      if (a.scaleN) {
+        float4 sc = *(const float4 *)(a.scaleN + bidx * a.sSNb + n);
+        v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+      }
+      if constexpr (OUTF32) {
+        *(float4 *)(Cb + (m * a.ldc + n) * 4) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        uint2 p;
+        p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        p.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(uint2 *)(Cb + (m * a.ldc + n) * 2) = p;
+      }
+    }
+  }
+}
+
+// explicit instantiations (every configuration the dispatcher below launches)
+#define POETX_G2_INST(R, BMv, BNv, WM, WN, BKv, NS, AK, BKm)                                     \
+  template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, true>(G2Args);       \
+  template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, false>(G2Args);
+POETX_G2_INST(MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false)
+POETX_G2_INST(MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true)
+POETX_G2_INST(MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false)
+POETX_G2_INST(MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true)
+#undef POETX_G2_INST
+template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false>(G2Args);
+template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, true>(G2Args);
+
+template <int ROLE, bool AKM, bool BKM>
+static int run_pp(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
+  const size_t lds = (size_t)2 * 512 * 64 * 2;
+  if (d.M <= 0 || d.N % 256 || d.K % 64) return POETX_ERR_UNSUPPORTED;
+  G2Args a = k;
+  a.tiles_m = (int)cdiv(d.M, 256);
+  a.tiles_n = (int)(d.N / 256);
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)(d.batch * d.splits));
+  if (d.c_dt == POETX_F32) {
+    static bool attr = false;
+    if (!attr) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return POETX_ERR_HIP;
+      attr = true;
+    }
+    return launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, true><<<grid, 512, lds, s>>>(a); });
+  }
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  return launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, false><<<grid, 512, lds, s>>>(a); });
+}
+
+template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32>
+static int run2o(const G2Args &a, const char *name, dim3 grid, size_t lds, hipStream_t s) {
+  constexpr int NT = 64 * WGM * WGN;
+  auto kern = &k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32>;
+  static bool attr = false;  // raise the dynamic-LDS limit once per instantiation
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  return launch(name, s, [&] { k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32><<<grid, NT, lds, s>>>(a); });
+}
+
+template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM>
 static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
-  const size_t lds = (size_t)2 * (BM + BN) * BK * 2;
-  if (d.M <= 0 || d.N % BN) return POETX_ERR_UNSUPPORTED;
+  const size_t lds = (size_t)NST * (BM + BN) * BKT * 2;
+  if (d.M <= 0 || d.N % BN || d.K % BKT && (!AKM || !BKM)) return POETX_ERR_UNSUPPORTED;
   G2Args a = k;
   a.tiles_m = (int)cdiv(d.M, BM);
   a.tiles_n = (int)(d.N / BN);
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)(d.batch * d.splits));
-  constexpr int NT = 64 * WGM * WGN;
-  if (d.c_dt == POETX_F32) {
-    auto kern = k_gemm2<ROLE, BM, BN, WGM, WGN, AKM, BKM, true>;
-    static bool attr = false;  // raise the dynamic-LDS limit once per instantiation
-    if (!attr) {
-      if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return POETX_ERR_HIP;
-      attr = true;
-    }
-    return launch(d.name, s, [&] { kern<<<grid, NT, lds, s>>>(a); });
-  }
-  auto kern = k_gemm2<ROLE, BM, BN, WGM, WGN, AKM, BKM, false>;
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return POETX_ERR_HIP;
-    attr = true;
-  }
-  return launch(d.name, s, [&] { kern<<<grid, NT, lds, s>>>(a); });
+  if (d.c_dt == POETX_F32) return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, true>(a, d.name, grid, lds, s);
+  return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false>(a, d.name, grid, lds, s);
 }
 
 bool mfma2_supported(const MfmaDesc &d) {
   if (d.b_dt != POETX_BF16) return false;  // int8 weights keep the register-staged kernel
   if (d.c_dt != POETX_BF16 && d.c_dt != POETX_F32) return false;
   if (d.splits < 1 || d.batch * d.splits > 65535) return false;
-  if (d.splits > 1 && (d.kchunk <= 0 || d.kchunk % BK || cdiv(d.K, d.kchunk) != d.splits)) return false;
-  if ((!d.a_km || !d.b_km) && d.K % BK) return false;
+  if (d.splits > 1 && (d.kchunk <= 0 || d.kchunk % 64 || cdiv(d.K, d.kchunk) != d.splits)) return false;
+  if ((!d.a_km || !d.b_km) && d.K % 64) return false;
   // 32-bit buffer offsets, with room for the rows a last partial tile addresses
   const int64_t a_ext = ((d.a_km ? d.K : d.M) + 256) * d.lda * 2, b_ext = ((d.b_km ? d.K : d.N) + 256) * d.ldb * 2;
   if (a_ext > 0x7fffffff || b_ext > 0x7fffffff) return false;
@@ -258,19 +484,21 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s) {
   switch (d.role) {
     case MFMA_GEMM_NT:
       if (d.a_km || d.b_km) return POETX_ERR_UNSUPPORTED;
-      return run2<MFMA_GEMM_NT, 256, 256, 2, 4, false, false>(k, d, s);
+      return run2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false>(k, d, s);
     case MFMA_GEMM_NN:
       if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
-      return run2<MFMA_GEMM_NN, 256, 256, 2, 4, false, true>(k, d, s);
+      // the k-major W' operand goes through the transposing LDS reads; the ping-pong
+      // schedule hides their extra latency best (measured against the plain schedule)
+      return run_pp<MFMA_GEMM_NN, false, true>(k, d, s);
     case MFMA_BLOCK_APPLY:
       if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
-      return run2<MFMA_BLOCK_APPLY, 128, 128, 2, 2, false, true>(k, d, s);
+      return run2<MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true>(k, d, s);
     case MFMA_BLOCK_APPLY_T:
       if (d.a_km || d.b_km) return POETX_ERR_UNSUPPORTED;
-      return run2<MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, false, false>(k, d, s);
+      return run2<MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false>(k, d, s);
     case MFMA_BLOCK_GRAD:
       if (!d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
-      return run2<MFMA_BLOCK_GRAD, 128, 128, 2, 2, true, true>(k, d, s);
+      return run2<MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true>(k, d, s);
     default:
       return POETX_ERR_UNSUPPORTED;
   }
