@@ -161,20 +161,23 @@ int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype,
   float *T = (float *)ar.take(blk), *U = (float *)ar.take(blk);
   POETX_TRY(unpack_skew(theta, Q, n, b, s));
   if (cnp_use_mfma(b)) {
+    // S = Q Q and, from the same accumulators, T = 2I + 2Q + S
     CnpMMArgs a;
     a.b = (int)b;
     a.name = "cnp_fwd_mm";
-    a.seg[0].A = Q; a.seg[0].B = Q; a.seg[0].C = S; a.seg[0].nblk = n;
-    POETX_TRY(cnp_mm(a, s));                                                        // S = Q Q
-    POETX_TRY(lincomb(T, n, b, 2.f, Q, 2.f, S, 1.f, nullptr, 0.f, nullptr, 0.f, s)); // T = 2I + 2Q + S
+    a.ce[1][0] = 2.f; a.cI[1] = 2.f;
+    a.seg[0].A = Q; a.seg[0].B = Q; a.seg[0].C = S; a.seg[0].C2 = T; a.seg[0].E[0] = Q; a.seg[0].nblk = n;
+    a.ce[0][0] = 0.f;
+    POETX_TRY(cnp_mm(a, s));
+    // G = I + 2Q + S T
     CnpMMArgs c;
     c.b = (int)b;
     c.name = "cnp_fwd_mm";
-    c.cI = 1.f; c.ce[0] = 2.f;
+    c.cI[0] = 1.f; c.ce[0][0] = 2.f;
     c.seg[0].A = S; c.seg[0].B = T; c.seg[0].E[0] = Q; c.seg[0].nblk = n;
     if (g_dtype == POETX_F32) c.seg[0].C = (float *)g;
     else c.seg[0].Cb = (bf16_t *)g;
-    return cnp_mm(c, s);                                                            // G = I + 2Q + S T
+    return cnp_mm(c, s);
   }
   POETX_TRY(gemm_generic(batched_f32(n, b, Q, Q, S, POETX_F32), s));
   POETX_TRY(lincomb(T, n, b, 2.f, Q, 2.f, S, 1.f, nullptr, 0.f, nullptr, 0.f, s));
@@ -205,8 +208,8 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStre
       CnpMMArgs a;
       a.b = (int)b;
       a.name = "cnp_bwd_mm";
-      a.alpha = alpha;
-      a.ce[0] = c0; a.ce[1] = c1; a.ce[2] = c2; a.ce[3] = c3;
+      a.alpha[0] = alpha;
+      a.ce[0][0] = c0; a.ce[0][1] = c1; a.ce[0][2] = c2; a.ce[0][3] = c3;
       for (int i = 0; i < nside; ++i) {
         fill(a.seg[i], side[i], B[i]);
         a.seg[i].nblk = side[i].n;

@@ -8,10 +8,11 @@
 // product, well inside float32-level accuracy for the CNP outputs.
 //
 // One launch computes, for every block z of up to two segments (the R and the
-// P side of a layer) and every 64 x 64 output tile,
-//     C[z] = alpha * A[z] . B[z] + sum_i ce[i] * E_i[z] + cI * I
-// with A, B, E_i dense row-major float32 [b][b]; C is written as float32
-// and/or bf16.
+// P side of a layer) and every 64 x 64 output tile, up to two outputs
+//     out_o[z] = alpha_o * A[z] . B[z] + sum_i ce_o[i] * E_i[z] + cI_o * I      (o = 0, 1)
+// with A, B, E_i dense row-major float32 [b][b]; out_0 is written as float32 (C)
+// and/or bf16 (Cb), out_1 as float32 (C2).  The k loop runs in 32-deep steps
+// through two LDS stages (small footprint, so several workgroups share a CU).
 #include "kernels.h"
 
 namespace poetx {
@@ -133,25 +134,33 @@ __global__ __launch_bounds__(NTH) void k_cnp_mm(CnpMMArgs a) {
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn + 16 * j + 4 * (l >> 4);
       const int64_t e = off + (int64_t)m * b + n;
-      f32x4 v = acc[i][j] * a.alpha;
+      float4 ex[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (S.E[t]) {
-          float4 x = *(const float4 *)(S.E[t] + e);
-          v[0] += a.ce[t] * x.x; v[1] += a.ce[t] * x.y; v[2] += a.ce[t] * x.z; v[3] += a.ce[t] * x.w;
+      for (int t = 0; t < 4; ++t)
+        ex[t] = S.E[t] ? *(const float4 *)(S.E[t] + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        if (o == 1 && !S.C2) continue;
+        f32x4 v = acc[i][j] * a.alpha[o];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float c = a.ce[o][t];
+          v[0] += c * ex[t].x; v[1] += c * ex[t].y; v[2] += c * ex[t].z; v[3] += c * ex[t].w;
         }
-      }
-      if (a.cI != 0.f) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (m == n + c) v[c] += a.cI;
-      }
-      if (S.C) *(float4 *)(S.C + e) = make_float4(v[0], v[1], v[2], v[3]);
-      if (S.Cb) {
-        uint2 p;
-        p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        p.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *(uint2 *)(S.Cb + e) = p;
+          if (m == n + c) v[c] += a.cI[o];
+        if (o == 1) {
+          *(float4 *)(S.C2 + e) = make_float4(v[0], v[1], v[2], v[3]);
+          continue;
+        }
+        if (S.C) *(float4 *)(S.C + e) = make_float4(v[0], v[1], v[2], v[3]);
+        if (S.Cb) {
+          uint2 p;
+          p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          p.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *(uint2 *)(S.Cb + e) = p;
+        }
       }
     }
   }

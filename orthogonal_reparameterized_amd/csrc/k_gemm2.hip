@@ -207,8 +207,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
     if (t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
     const int cur = t % NST;
     const bf16_t *ta = smem + cur * A_ELEMS, *tb = smem + NST * A_ELEMS + cur * B_ELEMS;
-    // all fragments of the step are requested before the first MFMA, so the reads of
-    // the second 32-deep half overlap the MFMAs of the first
+    // All fragments of the step are requested before the first MFMA (a scheduling
+    // barrier keeps the compiler from sinking the second half's reads into the MFMA
+    // chain), so LDS latency is paid once per step instead of once per fragment pair.
     constexpr int KH = BKT / 32;
     bf16x8 fa[KH][FM], fb[KH][FN];
 #pragma unroll
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
       for (int j = 0; j < FN; ++j)
         fb[h][j] = BKM ? frag_km<BN>(tb, wn + 16 * j, 32 * h) : frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int h = 0; h < KH; ++h)
 #pragma unroll
@@ -228,7 +230,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
         for (int j = 0; j < FN; ++j)
           // operands swapped: lane l then holds C[m = l%16][n = 4*(l/16) + 0..3]
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], acc[i][j], 0, 0, 0);
-
   }
 
   const int l = threadIdx.x & 63;

@@ -89,21 +89,22 @@ inline int gemm_mfma_best(const MfmaDesc &d, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Float32-accurate batched b x b products for the CNP steps (split-bf16 MFMA):
-//   C[z] = alpha * A[z] . B[z] + sum_i ce[i] * E_i[z] + cI * I,   b % 64 == 0
-// over the blocks of up to two segments; C written as float32 (C) and/or bf16 (Cb).
+// Float32-accurate batched b x b products for the CNP steps (split-bf16 MFMA), b % 64 == 0,
+// over the blocks of up to two segments, with up to two outputs:
+//   out_o[z] = alpha[o] * A[z] . B[z] + sum_i ce[o][i] * E_i[z] + cI[o] * I
+// out_0 written as float32 (C) and/or bf16 (Cb); out_1 as float32 (C2, optional).
 // ---------------------------------------------------------------------------
 struct CnpMMSeg {
   const float *A = nullptr, *B = nullptr;
-  float *C = nullptr;
+  float *C = nullptr, *C2 = nullptr;
   bf16_t *Cb = nullptr;
   const float *E[4] = {nullptr, nullptr, nullptr, nullptr};
   int64_t nblk = 0;
 };
 struct CnpMMArgs {
   int b = 0;
-  float alpha = 1.f, cI = 0.f;
-  float ce[4] = {0.f, 0.f, 0.f, 0.f};
+  float alpha[2] = {1.f, 1.f}, cI[2] = {0.f, 0.f};
+  float ce[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   CnpMMSeg seg[2];
   const char *name = "cnp_mm";
 };
