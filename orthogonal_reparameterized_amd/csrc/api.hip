@@ -331,6 +331,9 @@ int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y,
                 const float *scaleN, hipStream_t s) {
   int64_t b = p.b, nb = d / b;
   if (p.N == 0) return POETX_OK;
+  if (p.mfma && block_stream_supported(b, d, p.N))
+    return block_stream((const bf16_t *)X, (const bf16_t *)G, (bf16_t *)Y, p.N, d, b, transposed, scaleN,
+                        transposed ? "block_apply_t" : "block_apply", s);
   if (p.mfma) {
     MfmaDesc m;
     m.M = p.N; m.N = b; m.K = b; m.batch = nb;

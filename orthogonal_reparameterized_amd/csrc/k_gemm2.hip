@@ -48,21 +48,21 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
 
-// k-contiguous tile [R][BKT] bf16 (BKT = 32 or 64 -> 64- or 128-byte rows).  The
+// k-contiguous tile [R][BKT] bf16 (BKT = 32, 64 or more -> 64-, 128-, ...-byte rows).  The
 // 16-byte chunk c of row r sits at c ^ kc_key(r), which spreads the rows one
 // 8-lane ds_read_b128 phase touches over all 128 bytes of a bank sweep.  One wave
 // instruction (64 lanes x 16 B) fills 1 KB = 64 / (BKT/8) rows.
 template <int BKT>
-__device__ inline int kc_key(int r) { return BKT == 64 ? (r & 7) : ((r >> 1) & 3); }
+__device__ inline int kc_key(int r) { return BKT >= 64 ? (r & 7) : ((r >> 1) & 3); }
 
-template <int R, int NW, int BKT>
+template <int R, int NW, int BKT, int WOFF = 0>
 struct LoaderKC {
   static constexpr int CR = BKT / 8;        // chunks per row
   static constexpr int RPI = 64 / CR;       // rows per wave instruction
   static constexpr int INSTR = R / RPI / NW;
   int voff[INSTR];  // per-lane byte offset of its 16-byte chunk at k0 = 0
   __device__ void init(int64_t ld, int64_t row0) {
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int w = (threadIdx.x >> 6) - WOFF, l = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
       const int row = (w * INSTR + i) * RPI + l / CR;
@@ -73,7 +73,7 @@ struct LoaderKC {
   // k0 is added to the per-lane offset: the raw-buffer range check covers only the
   // lane offset (not soffset), and rows past the valid extent must read as zero.
   __device__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t k0, int64_t ld, bf16_t *tile) const {
-    const int w = threadIdx.x >> 6;
+    const int w = (threadIdx.x >> 6) - WOFF;
     const int kb = (int)(k0 * 2);
 #pragma unroll
     for (int i = 0; i < INSTR; ++i)
@@ -87,24 +87,28 @@ struct LoaderKC {
 // one ds_read_b64_tr_b16 touch (k .. k+3 and k+8 .. k+11) land in 8 different 32-byte
 // bank groups.  One wave instruction fills 1 KB.
 __device__ inline int km_key(int r) { return (r & 3) | ((r >> 1) & 4); }
+// chunk XOR for a k-major tile of C columns (C/8 chunks per row; narrow tiles keep
+// only the bits that stay inside the row)
+template <int C>
+__device__ inline int km_xor(int r) { return (km_key(r) << 1) & (C / 8 - 1); }
 
-template <int C, int NW, int BKT>
+template <int C, int NW, int BKT, int WOFF = 0>
 struct LoaderKM {
   static constexpr int CH = C / 8;     // 16-byte chunks per row
   static constexpr int RPI = 64 / CH;  // rows per wave instruction
   static constexpr int INSTR = BKT / RPI / NW;
   int voff[INSTR];
   __device__ void init(int64_t ld, int64_t col0) {
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int w = (threadIdx.x >> 6) - WOFF, l = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
       const int row = (w * INSTR + i) * RPI + l / CH;
-      const int lchunk = (l % CH) ^ (km_key(row) << 1);
+      const int lchunk = (l % CH) ^ km_xor<C>(row);
       voff[i] = (int)((row * ld + col0 + lchunk * 8) * 2);
     }
   }
   __device__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t k0, int64_t ld, bf16_t *tile) const {
-    const int w = threadIdx.x >> 6;
+    const int w = (threadIdx.x >> 6) - WOFF;
     const int kb = (int)(k0 * ld * 2);
 #pragma unroll
     for (int i = 0; i < INSTR; ++i)
@@ -130,8 +134,8 @@ __device__ inline bf16x8 frag_km(const bf16_t *t, int c0, int ks) {
   const int l = threadIdx.x & 63, g = l >> 4, j = l & 15;
   const int col = c0 + 4 * (j & 3);
   const int r0 = ks + 8 * g + (j >> 2), r1 = r0 + 4;
-  const int p0 = ((col >> 3) ^ (km_key(r0) << 1)) * 8 + (col & 7);
-  const int p1 = ((col >> 3) ^ (km_key(r1) << 1)) * 8 + (col & 7);
+  const int p0 = ((col >> 3) ^ km_xor<C>(r0)) * 8 + (col & 7);
+  const int p1 = ((col >> 3) ^ km_xor<C>(r1)) * 8 + (col & 7);
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + r0 * C + p0));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + r1 * C + p1));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -387,6 +391,172 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
       }
     }
   }
+}
+
+
+// Streaming block-diagonal product: Y_j = X_j . G_j (TRANS = false) or X_j . G_j^T
+// (TRANS = true) for every b x b block j, where X_j, Y_j are columns [jb, (j+1)b) of
+// token-major activations.  The op is HBM-bound (about 130 flop per byte at b = 256),
+// so each workgroup keeps one SW-wide slice of G_j resident in LDS and streams
+// T-token tiles of X_j through a 3-stage ring (prefetch distance 2), writing the
+// T x SW output tile straight from the accumulators.  A tile is read by the b/SW
+// slice workgroups of its block; their ids are 8 apart so they share an XCD (and its L2).
+struct BSArgs {
+  int64_t N, d;           // tokens, row stride (elements) of X and Y
+  int nb, P;              // blocks; workgroups per (block, slice)
+  const bf16_t *X; const bf16_t *G; bf16_t *Y;
+  const float *scaleN;    // per output column (length d) or null
+};
+
+template <int B, int SW, int T, bool TRANS>
+__global__ __launch_bounds__(384) void k_block_stream(BSArgs a) {
+  // waves 0-3 multiply and store; waves 4-5 only issue the global->LDS loads, so the
+  // producers' vmcnt waits track loads alone and the consumers' stores never stall
+  // the ring
+  constexpr int NCW = 4, NPW = 2;
+  constexpr int NSL = B / SW, NST = 3;
+  constexpr int WTM = T / 2, WTN = SW / 2, FM = WTM / 16, FN = WTN / 16;
+  constexpr int G_ELEMS = B * SW, A_ELEMS = T * B;
+  extern __shared__ __align__(16) bf16_t smem[];
+  bf16_t *sG = smem;
+
+  // blockIdx.x = (u / 8) * (8 * NSL) + h * 8 + u % 8 with u = j * P + p
+  const int x = blockIdx.x;
+  const int h = (x / 8) % NSL;
+  const int u = (x / (8 * NSL)) * 8 + x % 8;
+  if (u >= a.nb * a.P) return;
+  const int j = u / a.P, p = u % a.P;
+  const int64_t ntile = (a.N + T - 1) / T;
+
+  const int wave = threadIdx.x >> 6;
+  const bool producer = wave >= NCW;
+  const int wm = ((wave & 3) >> 1) * WTM, wn = (wave & 1) * WTN;
+  const int l = threadIdx.x & 63;
+
+  using LG = typename std::conditional<TRANS, LoaderKC<SW, NPW, B, NCW>, LoaderKM<SW, NPW, B, NCW>>::type;
+  using LXT = LoaderKC<T, NPW, B, NCW>;
+  constexpr int LX = LXT::INSTR;
+  LXT lx;
+  const bf16_t *Xj = a.X + (int64_t)j * B;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xj, a.N * a.d * 2);
+  if (producer) {
+    const bf16_t *Gs = TRANS ? a.G + (int64_t)j * B * B + (int64_t)h * SW * B : a.G + (int64_t)j * B * B + h * SW;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gs, (int64_t)B * B * 2);
+    LG lg;
+    lg.init(B, 0);
+    lx.init(a.d, 0);
+    lg.issue(rg, 0, B, sG);
+    if (p < ntile) lx.issue(rx, (int64_t)p * T * a.d, a.d, smem + G_ELEMS);
+    if (p + a.P < ntile) lx.issue(rx, (int64_t)(p + a.P) * T * a.d, a.d, smem + G_ELEMS + A_ELEMS);
+  }
+  int64_t tile = p;
+  for (int it = 0; tile < ntile; ++it, tile += a.P) {
+    if (producer) {
+      if (tile + a.P < ntile) wait_vmcnt<LX>();  // this tile (and G) landed; the next may fly
+      else __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();  // the tile is in LDS; the stage of tile it-1 is no longer read
+    if (producer) {
+      if (tile + 2 * a.P < ntile)
+        lx.issue(rx, (tile + 2 * a.P) * T * a.d, a.d, smem + G_ELEMS + ((it + 2) % NST) * A_ELEMS);
+      continue;
+    }
+    const bf16_t *ta = smem + G_ELEMS + (it % NST) * A_ELEMS;
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < B; k2 += 64) {
+      bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int ks = k2 + 32 * hh;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[hh][i] = frag_kc<B>(ta, wm + 16 * i, ks);
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj)
+          fb[hh][jj] = TRANS ? frag_kc<B>(sG, wn + 16 * jj, ks) : frag_km<SW>(sG, wn + 16 * jj, ks);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[hh][jj], fa[hh][i], acc[i][jj], 0, 0, 0);
+    }
+    // epilogue: lane holds Y[m = l%16][n = 4*(l/16) + 0..3] of each 16 x 16 patch
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = tile * T + wm + 16 * i + (l & 15);
+      if (m >= a.N) continue;
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) {
+        const int64_t n = (int64_t)j * B + h * SW + wn + 16 * jj + 4 * (l >> 4);
+        f32x4 v = acc[i][jj];
+        if (a.scaleN) {
+          float4 sc = *(const float4 *)(a.scaleN + n);
+          v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(uint2 *)(a.Y + m * a.d + n) = pk;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
+}
+
+#define POETX_BS_INST(Bv, SWv, Tv)                                       \
+  template __global__ void k_block_stream<Bv, SWv, Tv, false>(BSArgs); \
+  template __global__ void k_block_stream<Bv, SWv, Tv, true>(BSArgs);
+POETX_BS_INST(128, 128, 64)
+POETX_BS_INST(256, 128, 64)
+POETX_BS_INST(512, 64, 32)
+#undef POETX_BS_INST
+
+template <int B, int SW, int T, bool TRANS>
+static int run_bs(const BSArgs &a, const char *name, hipStream_t s) {
+  const size_t lds = ((size_t)B * SW + 3 * (size_t)T * B) * 2;
+  constexpr int NSL = B / SW;
+  const int64_t units = (int64_t)a.nb * a.P;
+  dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_stream<B, SW, T, TRANS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  return launch(name, s, [&] { k_block_stream<B, SW, T, TRANS><<<grid, 384, lds, s>>>(a); });
+}
+
+bool block_stream_supported(int64_t b, int64_t d, int64_t n_tokens) {
+  if (b != 128 && b != 256 && b != 512) return false;
+  if (d % b) return false;
+  return (n_tokens + 64) * d * 2 < 0x7fffffff;
+}
+
+int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t d, int64_t b,
+                 bool transposed, const float *scaleN, const char *name, hipStream_t s) {
+  if (n_tokens <= 0) return POETX_OK;
+  if (!block_stream_supported(b, d, n_tokens)) return POETX_ERR_UNSUPPORTED;
+  BSArgs a;
+  a.N = n_tokens; a.d = d; a.nb = (int)(d / b);
+  a.X = X; a.G = G; a.Y = Y; a.scaleN = scaleN;
+  const int sw = b == 512 ? 64 : 128, t = b == 512 ? 32 : 64;
+  const int64_t slices = (int64_t)a.nb * (b / sw);
+  const int64_t ntile = (n_tokens + t - 1) / t;
+  int64_t P = (256 + slices - 1) / slices;  // about one workgroup per CU in total
+  if (P > ntile) P = ntile;
+  a.P = (int)(P < 1 ? 1 : P);
+  if (b == 128) return transposed ? run_bs<128, 128, 64, true>(a, name, s) : run_bs<128, 128, 64, false>(a, name, s);
+  if (b == 256) return transposed ? run_bs<256, 128, 64, true>(a, name, s) : run_bs<256, 128, 64, false>(a, name, s);
+  return transposed ? run_bs<512, 64, 32, true>(a, name, s) : run_bs<512, 64, 32, false>(a, name, s);
 }
 
 // explicit instantiations (every configuration the dispatcher below launches)

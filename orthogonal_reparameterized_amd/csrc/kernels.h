@@ -83,6 +83,12 @@ bool mfma_supported(const MfmaDesc &d);
 int gemm_mfma(const MfmaDesc &d, hipStream_t s);    // register-staged kernel (any operand dtype)
 bool mfma2_supported(const MfmaDesc &d);
 int gemm_mfma2(const MfmaDesc &d, hipStream_t s);   // direct-to-LDS kernel (bf16 operands)
+// Streaming block-diagonal product (b in {128, 256, 512}):
+//   Y[:, jb:(j+1)b] = X[:, jb:(j+1)b] . G[j]  (transposed: . G[j]^T), times scaleN[col]
+// X, Y token-major [n_tokens][d] bf16, G [d/b][b][b] bf16.
+bool block_stream_supported(int64_t b, int64_t d, int64_t n_tokens);
+int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t d, int64_t b,
+                 bool transposed, const float *scaleN, const char *name, hipStream_t s);
 // the direct-to-LDS kernel where it applies, else the register-staged one
 inline int gemm_mfma_best(const MfmaDesc &d, hipStream_t s) {
   return mfma2_supported(d) ? gemm_mfma2(d, s) : gemm_mfma(d, s);
