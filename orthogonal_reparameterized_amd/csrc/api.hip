@@ -356,9 +356,11 @@ int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y,
   return gemm_generic(g, s);
 }
 
-// dG[j] = X[:, jb:(j+1)b]^T . Y[:, jb:(j+1)b]  (sum over tokens), as fp32 partials over
-// token chunks of grad_chunk(...) tokens (a multiple of 64), summed later in a fixed order.
-int64_t grad_chunk(const Plan &p, int64_t nb) {
+// dG[j] = X[:, jb:(j+1)b]^T . Y[:, jb:(j+1)b]  (sum over tokens), as fp32 partials that
+// are summed later in a fixed order.  grad_parts() is the number of partials.
+bool grad_streams(const Plan &p, int64_t d) { return p.mfma && p.N > 0 && block_stream_supported(p.b, d, p.N); }
+
+int64_t grad_chunk(const Plan &p, int64_t nb) {  // token chunk of the split-k kernel
   if (!p.mfma || p.N == 0) return p.N > 0 ? p.N : 1;
   int64_t tiles = nb * (p.b / 128) * (p.b / 128);
   int64_t want = cdiv(512, tiles);
@@ -366,10 +368,17 @@ int64_t grad_chunk(const Plan &p, int64_t nb) {
   return kc < 256 ? 256 : kc;
 }
 
-int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, float *parts, int64_t kc,
-               hipStream_t s) {
+int64_t grad_parts(const Plan &p, int64_t nb) {
+  if (p.N == 0) return 1;
+  if (grad_streams(p, nb * p.b)) return block_grad_stream_parts(p.b, nb * p.b, p.N);
+  return cdiv(p.N, grad_chunk(p, nb));
+}
+
+int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, float *parts, hipStream_t s) {
   int64_t b = p.b, nb = d / b;
+  if (grad_streams(p, d)) return block_grad_stream((const bf16_t *)X, (const bf16_t *)Y, parts, p.N, d, b, s);
   if (p.mfma) {
+    const int64_t kc = grad_chunk(p, nb);
     MfmaDesc m;
     m.M = b; m.N = b; m.K = p.N; m.batch = nb;
     m.splits = cdiv(p.N, kc); m.kchunk = kc;
@@ -496,8 +505,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   if (!ws_bytes) return POETX_ERR_INVALID_ARG;
   if (p.mem && saved_b) return POETX_ERR_INVALID_ARG;
   const int64_t b = p.b, bb = b * b;
-  const int64_t kcr = grad_chunk(p, p.nr), kcp = grad_chunk(p, p.np);
-  const int64_t sr = p.N > 0 ? cdiv(p.N, kcr) : 1, sp = p.N > 0 ? cdiv(p.N, kcp) : 1;
+  const int64_t sr = grad_parts(p, p.nr), sp = grad_parts(p, p.np);
   size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
   Arena ar(ws);
   FwdBufs f;
@@ -542,7 +550,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   if (p.N > 0) {
     POETX_TRY(block_apply(p, p.dout, dzg, L->g_p, dbuf, true,
                           p.w == POETX_I8 ? L->w_scale : nullptr, s));
-    POETX_TRY(block_grad(p, p.dout, bt, dzg, part_p, kcp, s));
+    POETX_TRY(block_grad(p, p.dout, bt, dzg, part_p, s));
     POETX_TRY(reduce_parts(part_p, gp, p.np * bb, sp, p.np * bb, s));
     // dA = dB W'
     POETX_TRY(gemm_bwd(p, L, dbuf, da, s));
@@ -550,7 +558,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
     void *dxw = L->perm_in ? dxt : dx;
     POETX_TRY(block_apply(p, p.din, da, L->g_r, dxw, true, nullptr, s));
     if (L->perm_in) POETX_TRY(permute_cols(dxt, dx, p.N, p.din, (int)p.ae, nullptr, L->perm_in, true, s));
-    POETX_TRY(block_grad(p, p.din, xg, da, part_r, kcr, s));
+    POETX_TRY(block_grad(p, p.din, xg, da, part_r, s));
     POETX_TRY(reduce_parts(part_r, gr, p.nr * bb, sr, p.nr * bb, s));
   } else {
     POETX_TRY(lincomb(gr, p.nr, b, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));

@@ -559,6 +559,145 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
   return transposed ? run_bs<512, 64, 32, true>(a, name, s) : run_bs<512, 64, 32, false>(a, name, s);
 }
 
+
+// Streaming block gradient: parts[p][j][r][c] = sum over the token tiles t = p, p+P, ...
+// of Xs_j[t]^T dY_j[t], for every b x b block j (r indexes columns of Xs_j, c of dY_j).
+// Each workgroup owns one 128 x 128 slice (rs, cs) of one block's gradient and keeps it
+// in registers while T-token tiles of both operands stream through a 4-stage LDS ring
+// (producer waves as in k_block_stream).  The P partials per block are summed later in
+// a fixed order.
+struct BGArgs {
+  int64_t N, d;
+  int nb, P;
+  const bf16_t *Xs; const bf16_t *dY; float *parts;  // parts: [P][nb][b][b]
+};
+
+template <int B>
+__global__ __launch_bounds__(384) void k_block_grad_stream(BGArgs a) {
+  constexpr int NCW = 4, NPW = 2, S = 128, T = 64, NST = 4;
+  constexpr int NSL = (B / S) * (B / S);
+  constexpr int WT = S / 2, F = WT / 16;  // 2 x 2 waves of 64 x 64
+  constexpr int TILE = T * S;             // elements per operand tile
+  extern __shared__ __align__(16) bf16_t smem[];
+
+  const int x = blockIdx.x;
+  const int sl = (x / 8) % NSL;
+  const int u = (x / (8 * NSL)) * 8 + x % 8;
+  if (u >= a.nb * a.P) return;
+  const int j = u / a.P, p = u % a.P;
+  const int rs = sl / (B / S), cs = sl % (B / S);
+  const int64_t ntile = (a.N + T - 1) / T;
+
+  const int wave = threadIdx.x >> 6;
+  const bool producer = wave >= NCW;
+  const int wm = ((wave & 3) >> 1) * WT, wn = (wave & 1) * WT;
+  const int l = threadIdx.x & 63;
+
+  using LT = LoaderKM<S, NPW, T, NCW>;
+  constexpr int LPT = 2 * LT::INSTR;  // loads per producer wave per token tile
+  LT la, lb;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.Xs + (int64_t)j * B + rs * S, a.N * a.d * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dY + (int64_t)j * B + cs * S, a.N * a.d * 2);
+  auto issue = [&](int64_t t, int stage) {
+    la.issue(ra, t * T, a.d, smem + (2 * stage) * TILE);
+    lb.issue(rb, t * T, a.d, smem + (2 * stage + 1) * TILE);
+  };
+  if (producer) {
+    la.init(a.d, 0);
+    lb.init(a.d, 0);
+    for (int s = 0; s < NST - 1; ++s)
+      if (p + (int64_t)s * a.P < ntile) issue(p + (int64_t)s * a.P, s);
+  }
+  f32x4 acc[F][F];
+#pragma unroll
+  for (int i = 0; i < F; ++i)
+#pragma unroll
+    for (int jj = 0; jj < F; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int64_t tile = p;
+  for (int it = 0; tile < ntile; ++it, tile += a.P) {
+    if (producer) {
+      if (tile + 2 * a.P < ntile) wait_vmcnt<2 * LPT>();
+      else if (tile + a.P < ntile) wait_vmcnt<LPT>();
+      else __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    if (producer) {
+      if (tile + 3 * a.P < ntile) issue(tile + 3 * a.P, (it + 3) % NST);
+      continue;
+    }
+    const bf16_t *ta = smem + (2 * (it % NST)) * TILE, *tb = ta + TILE;
+    bf16x8 fa[2][F], fb[2][F];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int i = 0; i < F; ++i) fa[hh][i] = frag_km<S>(ta, wm + 16 * i, 32 * hh);
+#pragma unroll
+      for (int jj = 0; jj < F; ++jj) fb[hh][jj] = frag_km<S>(tb, wn + 16 * jj, 32 * hh);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int jj = 0; jj < F; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[hh][jj], fa[hh][i], acc[i][jj], 0, 0, 0);
+  }
+  if (!producer) {
+    float *out = a.parts + ((int64_t)p * a.nb + j) * B * B;
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      const int r = rs * S + wm + 16 * i + (l & 15);
+#pragma unroll
+      for (int jj = 0; jj < F; ++jj) {
+        const int c = cs * S + wn + 16 * jj + 4 * (l >> 4);
+        *(float4 *)(out + (int64_t)r * B + c) = make_float4(acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
+}
+template __global__ void k_block_grad_stream<128>(BGArgs);
+template __global__ void k_block_grad_stream<256>(BGArgs);
+template __global__ void k_block_grad_stream<512>(BGArgs);
+
+template <int B>
+static int run_bg(const BGArgs &a, hipStream_t s) {
+  constexpr int NSL = (B / 128) * (B / 128);
+  const size_t lds = (size_t)4 * 2 * 64 * 128 * 2;
+  const int64_t units = (int64_t)a.nb * a.P;
+  dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_grad_stream<B>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  return launch("block_grad", s, [&] { k_block_grad_stream<B><<<grid, 384, lds, s>>>(a); });
+}
+
+int64_t block_grad_stream_parts(int64_t b, int64_t d, int64_t n_tokens) {
+  const int64_t slices = (d / b) * (b / 128) * (b / 128);
+  int64_t P = (256 + slices - 1) / slices;
+  const int64_t ntile = (n_tokens + 63) / 64;
+  if (P > ntile) P = ntile;
+  return P < 1 ? 1 : P;
+}
+
+int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t d, int64_t b,
+                      hipStream_t s) {
+  if (!block_stream_supported(b, d, n_tokens)) return POETX_ERR_UNSUPPORTED;
+  BGArgs a;
+  a.N = n_tokens; a.d = d; a.nb = (int)(d / b);
+  a.P = (int)block_grad_stream_parts(b, d, n_tokens);
+  a.Xs = Xs; a.dY = dY; a.parts = parts;
+  if (b == 128) return run_bg<128>(a, s);
+  if (b == 256) return run_bg<256>(a, s);
+  return run_bg<512>(a, s);
+}
+
 // explicit instantiations (every configuration the dispatcher below launches)
 #define POETX_G2_INST(R, BMv, BNv, WM, WN, BKv, NS, AK, BKm)                                     \
   template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, true>(G2Args);       \

@@ -89,6 +89,12 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s);   // direct-to-LDS kernel (bf1
 bool block_stream_supported(int64_t b, int64_t d, int64_t n_tokens);
 int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t d, int64_t b,
                  bool transposed, const float *scaleN, const char *name, hipStream_t s);
+// Streaming block gradient (same b and shape limits as block_stream): P partials
+//   parts[p][j] = sum_{t in token tiles p, p+P, ...} Xs_j[t]^T dY_j[t],  parts [P][d/b][b][b] fp32,
+// with P = block_grad_stream_parts(b, d, n_tokens); n_tokens >= 1.
+int64_t block_grad_stream_parts(int64_t b, int64_t d, int64_t n_tokens);
+int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t d, int64_t b,
+                      hipStream_t s);
 // the direct-to-LDS kernel where it applies, else the register-staged one
 inline int gemm_mfma_best(const MfmaDesc &d, hipStream_t s) {
   return mfma2_supported(d) ? gemm_mfma2(d, s) : gemm_mfma(d, s);
