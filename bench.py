@@ -115,7 +115,7 @@ def profile_steps(st, steps):
     return {k: (n / steps, ms / n) for k, (n, ms) in rec.items()}, wall
 
 
-def merge_time_ms(wl, inputs, reps=10):
+def merge_time_ms(wl, inputs, reps=10, with_t=False):
     import torch
     from orthogonal_reparameterized_amd import binding as B
     from orthogonal_reparameterized_amd.step import upload
@@ -124,16 +124,17 @@ def merge_time_ms(wl, inputs, reps=10):
     pin, pout = upload(inputs["perm_in"], "i32"), upload(inputs["perm_out"], "i32")
     out = torch.empty_like(w)
     so = torch.empty_like(s) if s is not None else None
-    B.poetx_merge_perm(w, pout, pin, s, out, so)
+    ot = torch.empty((wl.d_in, wl.d_out), dtype=w.dtype, device=w.device) if with_t else None
+    B.poetx_merge_perm(w, pout, pin, s, out, so, ot)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        B.poetx_merge_perm(w, pout, pin, s, out, so)
+        B.poetx_merge_perm(w, pout, pin, s, out, so, ot)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    nbytes = 2 * w.numel() * w.element_size()
+    nbytes = (4 if with_t else 2) * w.numel() * w.element_size()
     return ms, nbytes / (ms * 1e-3) / 1e9
 
 
@@ -267,6 +268,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mem", action="store_true")
+    ap.add_argument("--no-wt", action="store_true", help="fast variant without the W'^T copy")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", metavar="DB")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DB")
@@ -298,11 +300,14 @@ def main():
     for variant in wl.variants:
         if variant == "mem" and args.no_mem and "fast" in wl.variants:
             continue
-        st = LayerStep(wl, inputs, variant)
+        # the fast variant also keeps W'^T from the merge (one more weight copy, the
+        # backward's product then reads W' k-contiguous); mem stays memory-lean
+        keep_wt = variant == "fast" and wl.w == "bf16" and not args.no_wt
+        st = LayerStep(wl, inputs, variant, transposed_weight=keep_wt)
         ms = time_steps(st, args.steps, args.warmup)
         prof, prof_wall = profile_steps(st, args.steps)
         alg = algorithmic(wl, variant, n)
-        variants[variant] = {"ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+        variants[variant] = {"ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3), "w_merged_t": keep_wt,
                              "layer_roofline_ms": layer_roofline_ms(wl, variant, n),
                              "roofline_frac": layer_roofline_ms(wl, variant, n) / ms,
                              "ms_per_step_with_event_hooks": prof_wall}
@@ -330,6 +335,7 @@ def main():
                 "kernel": DOMINANT, "avg_launch_ms": dom["avg_ms"],
                 "algorithmic_flops_per_launch": flops_launch}
     merge_ms, merge_gbs = merge_time_ms(wl, inputs) if wl.w != "i8" else (None, None)
+    merge_t_ms, merge_t_gbs = merge_time_ms(wl, inputs, with_t=True) if wl.w == "bf16" else (None, None)
     out = {
         "metric": METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -339,7 +345,8 @@ def main():
         "roofline": roof,
         "variants": variants,
         "phases": phases,
-        "merge_per_phase": {"ms": merge_ms, "GB_s": merge_gbs},
+        "merge_per_phase": {"ms": merge_ms, "GB_s": merge_gbs,
+                            "with_transpose_ms": merge_t_ms, "with_transpose_GB_s": merge_t_gbs},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, inputs)

@@ -76,6 +76,9 @@ typedef struct {
   int32_t g_dtype;             /* dtype of g_r / g_p: F32 or BF16 (== act_dtype)     */
   int32_t variant;             /* poetx_variant                                     */
   const void *w_merged;        /* [d_out][d_in] W' from poetx_merge_perm            */
+  const void *w_merged_t;      /* optional [d_in][d_out] copy of W'^T (BF16 only), or
+                                  NULL; when given, the backward's dA = dB.W' reads it
+                                  k-contiguous (faster, one more weight copy)          */
   const float *w_scale;        /* [d_out] per-row scale of an I8 W', else NULL      */
   const int32_t *perm_in;      /* [d_in]  or NULL (identity)                        */
   const int32_t *perm_out;     /* [d_out] or NULL (identity)                        */
@@ -90,6 +93,8 @@ typedef struct {
  *     w_merged[i][k] = w[perm_out[i]][perm_in[k]]
  * and for an I8 weight with per-output-row scales also
  *     w_scale_merged[i] = w_scale[perm_out[i]]   (exact: a row scale moves with its row).
+ * When w_merged_t is not NULL it also receives the transpose w_merged_t[k][i] =
+ * w_merged[i][k] ([d_in][d_out], same dtype; must not alias w or w_merged).
  * w: [d_out][d_in] of w_dtype (F32, BF16 or I8); w_scale: [d_out] (I8 only, else NULL);
  * perm_out: [d_out], perm_in: [d_in] (each may be NULL = identity; entries must form a
  * permutation -- not checked on the device).  Output w_merged has w's dtype and shape.
@@ -98,7 +103,7 @@ typedef struct {
  */
 int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64_t d_out,
                      int64_t d_in, const int32_t *perm_out, const int32_t *perm_in,
-                     void *w_merged, float *w_scale_merged, void *stream);
+                     void *w_merged, float *w_scale_merged, void *w_merged_t, void *stream);
 
 /*
  * poetx_cnp -- Method §4 (Cayley-Neumann parameterization, eq. 9) on nblocks

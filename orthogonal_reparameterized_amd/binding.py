@@ -39,12 +39,12 @@ class PoetxLayerC(ctypes.Structure):
     _fields_ = [
         ("d_in", _i64), ("d_out", _i64), ("b", _i64),
         ("act_dtype", _i32), ("w_dtype", _i32), ("g_dtype", _i32), ("variant", _i32),
-        ("w_merged", _vp), ("w_scale", _vp), ("perm_in", _vp), ("perm_out", _vp),
+        ("w_merged", _vp), ("w_merged_t", _vp), ("w_scale", _vp), ("perm_in", _vp), ("perm_out", _vp),
         ("theta_r", _vp), ("theta_p", _vp), ("g_r", _vp), ("g_p", _vp),
     ]
 
 
-_lib.poetx_merge_perm.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+_lib.poetx_merge_perm.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.poetx_cnp.argtypes = [_i32, _i64, _i64, _vp, _vp, _i32, _vp, _i32, _vp, _vp,
                            ctypes.POINTER(_sz), _vp]
 _lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp,
@@ -128,15 +128,19 @@ def release_workspace():
 
 # --------------------------------------------------------------------------
 def poetx_merge_perm(w: torch.Tensor, perm_out=None, perm_in=None, w_scale=None,
-                     out: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None):
-    """W'[i][k] = W[perm_out[i]][perm_in[k]] (and s'[i] = s[perm_out[i]] for int8)."""
+                     out: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None,
+                     out_t: Optional[torch.Tensor] = None):
+    """W'[i][k] = W[perm_out[i]][perm_in[k]] (and s'[i] = s[perm_out[i]] for int8).
+
+    If out_t is given it also receives W'^T ([d_in][d_out]).
+    """
     d_out, d_in = w.shape
     out = torch.empty_like(w) if out is None else out
     if w.dtype == torch.int8 and out_scale is None:
         out_scale = torch.empty_like(w_scale)
     st = _lib.poetx_merge_perm(_ptr(w), _ptr(w_scale), _dt(w), d_out, d_in, _ptr(perm_out),
                                _ptr(perm_in), _ptr(out), _ptr(out_scale) if w.dtype == torch.int8 else None,
-                               _stream(w.device))
+                               _ptr(out_t), _stream(w.device))
     _check(st, "poetx_merge_perm")
     return out, (out_scale if w.dtype == torch.int8 else None)
 
@@ -178,6 +182,7 @@ class Layer:
     w_scale: Optional[torch.Tensor] = None
     perm_in: Optional[torch.Tensor] = None
     perm_out: Optional[torch.Tensor] = None
+    w_merged_t: Optional[torch.Tensor] = None
 
     @property
     def d_out(self):
@@ -194,7 +199,8 @@ class Layer:
         c.w_dtype = _dt(self.w_merged)
         c.g_dtype = _dt(self.g_r)
         c.variant = self.variant
-        for name in ("w_merged", "w_scale", "perm_in", "perm_out", "theta_r", "theta_p", "g_r", "g_p"):
+        for name in ("w_merged", "w_merged_t", "w_scale", "perm_in", "perm_out", "theta_r", "theta_p",
+                     "g_r", "g_p"):
             p = _ptr(getattr(self, name))
             setattr(c, name, p.value if p is not None else None)
         return c

@@ -102,14 +102,16 @@ extern "C" const char *poetx_version(void) { return "0.1.0"; }
 extern "C" int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype,
                                 int64_t d_out, int64_t d_in, const int32_t *perm_out,
                                 const int32_t *perm_in, void *w_merged, float *w_scale_merged,
-                                void *stream) {
+                                void *w_merged_t, void *stream) {
   if (!w || !w_merged || d_out < 1 || d_in < 1) return POETX_ERR_INVALID_ARG;
   if (w_dtype != POETX_F32 && w_dtype != POETX_BF16 && w_dtype != POETX_I8) return POETX_ERR_INVALID_ARG;
   if (w_dtype == POETX_I8 && (!w_scale || !w_scale_merged)) return POETX_ERR_INVALID_ARG;
   if ((size_t)d_in * dtype_size(w_dtype) > 65536) return POETX_ERR_UNSUPPORTED;
+  if (w_merged_t && (w_merged_t == w || w_merged_t == w_merged)) return POETX_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   POETX_TRY(permute_cols(w, w_merged, d_out, d_in, (int)dtype_size(w_dtype), perm_out, perm_in, false, s));
   if (w_dtype == POETX_I8) POETX_TRY(gather_f32(w_scale, w_scale_merged, d_out, perm_out, s));
+  if (w_merged_t) POETX_TRY(transpose(w_merged, w_merged_t, d_out, d_in, (int)dtype_size(w_dtype), s));
   return POETX_OK;
 }
 
@@ -425,6 +427,17 @@ int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, hipStr
 // dA = dB' . W'  (dB' already carries the int8 row scales)
 int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, hipStream_t s) {
   if (p.N == 0) return POETX_OK;
+  if (p.mfma && L->w_merged_t && p.w == POETX_BF16) {
+    // dA = dB . (W'^T)^T: both operands k-contiguous
+    MfmaDesc m;
+    m.M = p.N; m.N = p.din; m.K = p.dout;
+    m.A = dB; m.a_km = false; m.lda = p.dout;
+    m.B = L->w_merged_t; m.b_km = false; m.b_dt = POETX_BF16; m.ldb = p.dout;
+    m.C = dA; m.c_dt = p.act; m.ldc = p.din;
+    m.name = "gemm_nn";
+    m.role = MFMA_GEMM_NT;
+    return gemm_mfma_best(m, s);
+  }
   if (p.mfma) {
     MfmaDesc m;
     m.M = p.N; m.N = p.din; m.K = p.dout;

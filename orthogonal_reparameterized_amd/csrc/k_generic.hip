@@ -228,6 +228,35 @@ int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esiz
   }
 }
 
+// out[c][r] = in[r][c] for a [rows][cols] matrix, through 64 x 64 LDS tiles.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ in, T *__restrict__ out, int64_t rows,
+                                                   int64_t cols) {
+  __shared__ T t[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) t[i][tx] = in[r * cols + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) out[c * rows + r] = t[tx][i];
+  }
+}
+
+int transpose(const void *in, void *out, int64_t rows, int64_t cols, int esize, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return POETX_OK;
+  if (cdiv(rows, 64) > 65535) return POETX_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 64));
+  switch (esize) {
+    case 4: return launch("transpose", s, [&] { k_transpose<uint32_t><<<grid, 256, 0, s>>>((const uint32_t *)in, (uint32_t *)out, rows, cols); });
+    case 2: return launch("transpose", s, [&] { k_transpose<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols); });
+    default: return launch("transpose", s, [&] { k_transpose<uint8_t><<<grid, 256, 0, s>>>((const uint8_t *)in, (uint8_t *)out, rows, cols); });
+  }
+}
+
 __global__ void k_gather_f32(const float *__restrict__ src, float *__restrict__ out, int64_t n,
                              const int32_t *__restrict__ perm) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

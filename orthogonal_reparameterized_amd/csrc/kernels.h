@@ -31,6 +31,8 @@ int gemm_generic(const GemmDesc &g, hipStream_t s);
 //   scatter: out[r][cperm[i]] = in[r][i]
 int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esize,
                  const int32_t *rperm, const int32_t *cperm, bool scatter, hipStream_t s);
+// out[c][r] = in[r][c] ([rows][cols] -> [cols][rows]) for esize-byte elements
+int transpose(const void *in, void *out, int64_t rows, int64_t cols, int esize, hipStream_t s);
 // out[i] = src[perm[i]] for float32 vectors
 int gather_f32(const float *src, float *out, int64_t n, const int32_t *perm, hipStream_t s);
 

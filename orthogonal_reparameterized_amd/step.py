@@ -26,7 +26,8 @@ def upload(arr, dtype: str, device="cuda"):
 
 
 class LayerStep:
-    def __init__(self, wl, inputs: dict, variant: str = "fast", device="cuda", perms: bool = True):
+    def __init__(self, wl, inputs: dict, variant: str = "fast", device="cuda", perms: bool = True,
+                 transposed_weight: bool = False):
         self.wl = wl
         self.variant = B.POETX_FAST if variant == "fast" else B.POETX_MEM
         act = _TORCH[wl.act]
@@ -41,8 +42,12 @@ class LayerStep:
         else:
             w = upload(inputs["w"], wl.w, dev)
             s = None
-        # phase start: merge the weight-side permutations into W once (Method §2)
-        self.w_merged, self.w_scale = B.poetx_merge_perm(w, self.perm_out, self.perm_in, s)
+        # phase start: merge the weight-side permutations into W once (Method §2); optionally
+        # also keep W'^T so that the backward product reads it k-contiguous
+        self.w_merged_t = (torch.empty((wl.d_in, wl.d_out), dtype=w.dtype, device=dev)
+                           if transposed_weight else None)
+        self.w_merged, self.w_scale = B.poetx_merge_perm(w, self.perm_out, self.perm_in, s,
+                                                         out_t=self.w_merged_t)
         del w
         self.theta_r = upload(inputs["theta_r"], "f32", dev)
         self.theta_p = upload(inputs["theta_p"], "f32", dev)
@@ -58,7 +63,7 @@ class LayerStep:
         self.dtheta_p = torch.empty_like(self.theta_p)
         self.layer = B.Layer(self.w_merged, self.theta_r, self.theta_p, self.g_r, self.g_p, b,
                              act_dtype=act, variant=self.variant, w_scale=self.w_scale,
-                             perm_in=self.perm_in, perm_out=self.perm_out)
+                             perm_in=self.perm_in, perm_out=self.perm_out, w_merged_t=self.w_merged_t)
 
     def cnp(self):
         B.poetx_cnp(B.POETX_CNP_FWD, self.theta_r, self.wl.b, g=self.g_r)

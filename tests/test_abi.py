@@ -117,5 +117,6 @@ def test_validation_codes(B):
     assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 64, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
                            ctypes.byref(small), None) == B.POETX_ERR_WORKSPACE
     # merge
-    assert B.raw.poetx_merge_perm(None, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, None) == B.POETX_ERR_INVALID_ARG
-    assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_I8, 4, 4, None, None, FAKE, None, None) == B.POETX_ERR_INVALID_ARG
+    assert B.raw.poetx_merge_perm(None, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG
+    assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_I8, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG
+    assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, FAKE, None) == B.POETX_ERR_INVALID_ARG

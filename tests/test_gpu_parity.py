@@ -121,16 +121,19 @@ def test_merge_bit_exact(B, dt):
         wm, _ = B.poetx_merge_perm(wt, torch.from_numpy(pout).cuda(), torch.from_numpy(pin).cuda())
         assert np.array_equal(wm.view(torch.int16).cpu().numpy().view(np.uint16), ref)
     else:
+        wt = torch.empty((d_in, d_out), dtype=torch.float32, device="cuda")
         wm, _ = B.poetx_merge_perm(torch.from_numpy(w).cuda(), torch.from_numpy(pout).cuda(),
-                                   torch.from_numpy(pin).cuda())
-        assert np.array_equal(wm.cpu().numpy(), O.merge_perm(w, pout, pin))
+                                   torch.from_numpy(pin).cuda(), out_t=wt)
+        ref = O.merge_perm(w, pout, pin)
+        assert np.array_equal(wm.cpu().numpy(), ref)
+        assert np.array_equal(wt.cpu().numpy(), ref.T)
 
 
 # ----------------------------------------------------------------- layer ----
 
-def _run_step(wl, inp, variant, perms=True):
+def _run_step(wl, inp, variant, perms=True, transposed_weight=False):
     from orthogonal_reparameterized_amd.step import LayerStep
-    st = LayerStep(wl, inp, variant, perms=perms)
+    st = LayerStep(wl, inp, variant, perms=perms, transposed_weight=transposed_weight)
     out = st.step(want_dg=True)
     torch.cuda.synchronize()
     return st, out
@@ -182,6 +185,16 @@ def test_layer_bf16_small(B, n, d_in, d_out, b, perms, variant):
     _compare(st, out, ref, TOL_BF16, f"small n={n} {d_in}->{d_out} b={b} perms={perms} {variant}")
 
 
+@pytest.mark.parametrize("n,d_in,d_out,b", [(257, 512, 768, 256), (130, 1024, 512, 512)])
+def test_layer_bf16_transposed_weight(B, n, d_in, d_out, b):
+    """With W'^T kept from the merge the backward reads it k-contiguous; same results."""
+    wl = WL.Workload(97, "small bf16 wt", n, d_in, d_out, b, "bf16", "bf16", "bf16", 0.01, d_in)
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    st, out = _run_step(wl, inp, "fast", transposed_weight=True)
+    _compare(st, out, ref, TOL_BF16, f"W'^T n={n} {d_in}->{d_out} b={b}")
+
+
 def test_layer_bf16_generic_block(B):
     """b = 48 (not a multiple of 128) goes through the vector-ALU path."""
     wl = WL.Workload(91, "small bf16 b48", 70, 96, 144, 48, "bf16", "bf16", "bf16", 0.02, 96)
@@ -220,11 +233,12 @@ def _full(key):
     return wl, inp, ref
 
 
-@pytest.mark.parametrize("key,variant", [(3, "fast"), (3, "mem"), (4, "fast"), (4, "mem"), (5, "mem")])
-def test_layer_full_size(B, key, variant):
+@pytest.mark.parametrize("key,variant,wt", [(3, "fast", False), (3, "fast", True), (3, "mem", False),
+                                             (4, "fast", True), (4, "mem", False), (5, "mem", False)])
+def test_layer_full_size(B, key, variant, wt):
     wl, inp, ref = _full(key)
-    _say(f"workload {key} {variant} on GPU")
-    st, out = _run_step(wl, inp, variant)
+    _say(f"workload {key} {variant} (W'^T kept: {wt}) on GPU")
+    st, out = _run_step(wl, inp, variant, transposed_weight=wt)
     _compare(st, out, ref, TOL_BF16, f"workload{key} {variant}")
 
 
