@@ -176,9 +176,8 @@ def load_traffic(kernel, workload_key):
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "orthogonal_reparameterized_amd", "csrc", "k_mfma.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if kv.get("k_mfma_sha") != sha or "traffic_bytes_per_launch" not in kv:
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    if kv.get("kernel_source_sha") != sha or "traffic_bytes_per_launch" not in kv:
         return None
     return float(kv["traffic_bytes_per_launch"])
 
@@ -204,10 +203,11 @@ def copy_calibration():
                       "GB_s_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}))
 
 
-KERNEL_SYMBOL = {  # kernel label -> substring of its symbol in traces
-    "gemm_nt": "k_mfma_gemm<0,", "gemm_nn": "k_mfma_gemm<1,", "block_apply": "k_mfma_gemm<2,",
-    "block_apply_t": "k_mfma_gemm<3,", "block_grad": "k_mfma_gemm<4,",
+KERNEL_SYMBOL = {  # kernel label -> substring of its symbol in traces (workload 3 shapes)
+    "gemm_nt": "k_gemm2<0,", "gemm_nn": "k_gemm_pp<1,", "block_apply": "k_block_stream<256,128,64,false>",
+    "block_apply_t": "k_block_stream<256,128,64,true>", "block_grad": "k_block_grad_stream<256>",
 }
+KERNEL_SOURCE = os.path.join(ROOT, "orthogonal_reparameterized_amd", "csrc", "k_gemm2.hip")
 
 
 def summarize_trace(db):
@@ -244,8 +244,7 @@ def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, label=D
     sym = KERNEL_SYMBOL[label]
     nf, f = pick(per_kernel(fetch_db, "FETCH_SIZE"), sym)
     nw, w = pick(per_kernel(write_db, "WRITE_SIZE"), sym)
-    src = os.path.join(ROOT, "orthogonal_reparameterized_amd", "csrc", "k_mfma.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
     print(f"kernel_label = {label}")
     print(f"kernel_symbol_match = {sym}")
     print(f"dispatches_fetch = {nf}")
@@ -257,7 +256,8 @@ def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, label=D
     print(f"fetch_scale = {f_scale:.4f}")
     print(f"write_scale = {w_scale:.4f}")
     print(f"traffic_bytes_per_launch = {(f * f_scale + w * w_scale) * 1024:.0f}")
-    print(f"k_mfma_sha = {sha}")
+    print(f"kernel_source = {os.path.relpath(KERNEL_SOURCE, ROOT)}")
+    print(f"kernel_source_sha = {sha}")
 
 
 def main():
