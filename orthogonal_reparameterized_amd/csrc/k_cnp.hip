@@ -49,6 +49,9 @@ __device__ inline bf16x8 frag_b(const bf16_t *t, int c0, int ks) {
 }
 }  // namespace
 
+// NKS = b / 32 when known at compile time (the k loop is then fully unrolled, so the
+// register ring has static slots); NKS = 0 handles any b % 64 == 0 with no ring.
+template <int NKS>
 __global__ __launch_bounds__(NTH) void k_cnp_mm(CnpMMArgs a) {
   __shared__ __align__(16) bf16_t sAh[2][TM * A_LD], sAl[2][TM * A_LD];
   __shared__ __align__(16) bf16_t sBh[2][TK * B_LD], sBl[2][TK * B_LD];
@@ -62,30 +65,33 @@ __global__ __launch_bounds__(NTH) void k_cnp_mm(CnpMMArgs a) {
   const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TM;
   const int tid = threadIdx.x, wave = tid >> 6, wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
 
-  float4 ra[2], rb[2];
-  auto gload = [&](int k0) {
+  // register ring of RD k-steps in flight: the small per-step MFMA work cannot cover a
+  // global round trip, so loads are issued RD-1 steps ahead of their LDS store
+  constexpr int RD = NKS ? 3 : 1;
+  float4 ra[RD][2], rb[RD][2];
+  auto gload = [&](int slot, int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int q = tid + NTH * i;                 // 512 float4 per operand tile
       int ar = q >> 3, ac = (q & 7) * 4;     // A tile: 64 rows x 32 k
-      ra[i] = *(const float4 *)(A + (int64_t)(m0 + ar) * b + k0 + ac);
+      ra[slot][i] = *(const float4 *)(A + (int64_t)(m0 + ar) * b + k0 + ac);
       int br = q >> 4, bc = (q & 15) * 4;    // B tile: 32 k-rows x 64 columns
-      rb[i] = *(const float4 *)(B + (int64_t)(k0 + br) * b + n0 + bc);
+      rb[slot][i] = *(const float4 *)(B + (int64_t)(k0 + br) * b + n0 + bc);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int slot, int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int q = tid + NTH * i;
       int ar = q >> 3, ac = (q & 7) * 4;
       int br = q >> 4, bc = (q & 15) * 4;
       uint16_t h[4], l[4];
-      split2(ra[i].x, h[0], l[0]); split2(ra[i].y, h[1], l[1]);
-      split2(ra[i].z, h[2], l[2]); split2(ra[i].w, h[3], l[3]);
+      split2(ra[slot][i].x, h[0], l[0]); split2(ra[slot][i].y, h[1], l[1]);
+      split2(ra[slot][i].z, h[2], l[2]); split2(ra[slot][i].w, h[3], l[3]);
       *(uint2 *)(sAh[buf] + ar * A_LD + ac) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
       *(uint2 *)(sAl[buf] + ar * A_LD + ac) = make_uint2(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16);
-      split2(rb[i].x, h[0], l[0]); split2(rb[i].y, h[1], l[1]);
-      split2(rb[i].z, h[2], l[2]); split2(rb[i].w, h[3], l[3]);
+      split2(rb[slot][i].x, h[0], l[0]); split2(rb[slot][i].y, h[1], l[1]);
+      split2(rb[slot][i].z, h[2], l[2]); split2(rb[slot][i].w, h[3], l[3]);
       *(uint2 *)(sBh[buf] + br * B_LD + bc) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
       *(uint2 *)(sBl[buf] + br * B_LD + bc) = make_uint2(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16);
     }
@@ -97,13 +103,16 @@ __global__ __launch_bounds__(NTH) void k_cnp_mm(CnpMMArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore(0);
+  const int nk = NKS ? NKS : b / TK;
+#pragma unroll
+  for (int s = 0; s < RD; ++s)
+    if (s < nk) gload(s, s * TK);
+  lstore(0, 0);
   __syncthreads();
-  int cur = 0;
-  for (int k0 = 0; k0 < b; k0 += TK) {
-    const bool more = k0 + TK < b;
-    if (more) gload(k0 + TK);
+#pragma unroll
+  for (int st = 0; st < (NKS ? NKS : nk); ++st) {
+    const int cur = st & 1;
+    if (st + RD < nk) gload(st % RD, (st + RD) * TK);  // slot st%RD was stored at step st-1
     bf16x8 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -121,9 +130,8 @@ __global__ __launch_bounds__(NTH) void k_cnp_mm(CnpMMArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[j], al[i], acc[i][j], 0, 0, 0);
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[j], ah[i], acc[i][j], 0, 0, 0);
       }
-    if (more) lstore(cur ^ 1);
+    if (st + 1 < nk) lstore((st + 1) % RD, cur ^ 1);
     __syncthreads();
-    cur ^= 1;
   }
 
   const int l = tid & 63;
@@ -166,12 +174,24 @@ __global__ __launch_bounds__(NTH) void k_cnp_mm(CnpMMArgs a) {
   }
 }
 
+template __global__ void k_cnp_mm<0>(CnpMMArgs);
+template __global__ void k_cnp_mm<2>(CnpMMArgs);
+template __global__ void k_cnp_mm<4>(CnpMMArgs);
+template __global__ void k_cnp_mm<8>(CnpMMArgs);
+template __global__ void k_cnp_mm<16>(CnpMMArgs);
+
 int cnp_mm(const CnpMMArgs &a, hipStream_t s) {
   const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
   if (nz <= 0) return POETX_OK;
   if (a.b % TM || nz > 65535) return POETX_ERR_UNSUPPORTED;
   dim3 grid(a.b / TM, a.b / TM, (unsigned)nz);
-  return launch(a.name, s, [&] { k_cnp_mm<<<grid, NTH, 0, s>>>(a); });
+  switch (a.b) {
+    case 64: return launch(a.name, s, [&] { k_cnp_mm<2><<<grid, NTH, 0, s>>>(a); });
+    case 128: return launch(a.name, s, [&] { k_cnp_mm<4><<<grid, NTH, 0, s>>>(a); });
+    case 256: return launch(a.name, s, [&] { k_cnp_mm<8><<<grid, NTH, 0, s>>>(a); });
+    case 512: return launch(a.name, s, [&] { k_cnp_mm<16><<<grid, NTH, 0, s>>>(a); });
+    default: return launch(a.name, s, [&] { k_cnp_mm<0><<<grid, NTH, 0, s>>>(a); });
+  }
 }
 
 }  // namespace poetx
