@@ -260,6 +260,49 @@ def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, label=D
     print(f"kernel_source_sha = {sha}")
 
 
+def cnp_bench(wl, steps, warmup):
+    """Workload 2: CNP forward (G in bf16) and backward on independent blocks."""
+    import torch
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd import workloads as WL
+    theta, dg = WL.make_cnp_inputs(wl.nblocks, wl.b, wl.theta_std, seed=WL.BASE_SEED + wl.key)
+    th = torch.from_numpy(theta).cuda()
+    dgt = torch.from_numpy(dg).cuda()
+    del theta, dg
+    g = torch.empty((wl.nblocks, wl.b, wl.b), dtype=torch.bfloat16, device="cuda")
+    dth = torch.empty_like(th)
+    res = {}
+    for name, fn in (("fwd", lambda: B.poetx_cnp(B.POETX_CNP_FWD, th, wl.b, g=g)),
+                     ("bwd", lambda: B.poetx_cnp(B.POETX_CNP_BWD, th, wl.b, dg=dgt, dtheta=dth))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) * 1e3 / steps
+    b, n = wl.b, wl.nblocks
+    # float32-equivalent flops: forward 2 b^3-products, backward 6 (each 2 b^3)
+    f_fwd, f_bwd = 4.0 * b ** 3 * n, 12.0 * b ** 3 * n
+    ms = res["fwd"] + res["bwd"]
+    out = {
+        "metric": "CNP fwd+bwd blocks/s (4096 x b=256)", "value": n / (ms * 1e-3), "unit": "blocks/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (split-bf16 MFMA)", "data": "synthetic",
+        "config": {"workload": wl.name, "nblocks": n, "b": b},
+        "fwd_ms": res["fwd"], "bwd_ms": res["bwd"],
+        "fwd_tflops_f32_equiv": f_fwd / (res["fwd"] * 1e-3) / 1e12,
+        "bwd_tflops_f32_equiv": f_bwd / (res["bwd"] * 1e-3) / 1e12,
+        # three bf16 MFMA passes per float32-accurate product
+        "roofline": {"bound": "mfma", "achieved": 3 * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": 3 * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "traffic": None, "kernel": "cnp (all launches, bf16 MFMA passes)"},
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +336,9 @@ def main():
     from orthogonal_reparameterized_amd.step import LayerStep
 
     wl = WL.WORKLOADS[args.workload]
+    if wl.nblocks:
+        cnp_bench(wl, args.steps, args.warmup)
+        return
     inputs = WL.make_layer_inputs(wl)
     n = wl.n_tokens
     variants = {}
@@ -334,7 +380,7 @@ def main():
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(DOMINANT, wl.key),
                 "kernel": DOMINANT, "avg_launch_ms": dom["avg_ms"],
                 "algorithmic_flops_per_launch": flops_launch}
-    merge_ms, merge_gbs = merge_time_ms(wl, inputs) if wl.w != "i8" else (None, None)
+    merge_ms, merge_gbs = merge_time_ms(wl, inputs)
     merge_t_ms, merge_t_gbs = merge_time_ms(wl, inputs, with_t=True) if wl.w == "bf16" else (None, None)
     out = {
         "metric": METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -348,7 +394,7 @@ def main():
         "merge_per_phase": {"ms": merge_ms, "GB_s": merge_gbs,
                             "with_transpose_ms": merge_t_ms, "with_transpose_GB_s": merge_t_gbs},
     }
-    if not args.no_cpu:
+    if not args.no_cpu and wl.w != "i8":
         out["cpu_baseline"] = cpu_baseline(wl, inputs)
     print(json.dumps(out))
 
