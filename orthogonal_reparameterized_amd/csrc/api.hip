@@ -125,8 +125,12 @@ extern "C" int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_d
 //   K1 = Gb P, K2 = K1 P, K3 = K2 P,
 //   H2 = (2Gb + K1) + P Gb, H1 = (2Gb + 2K1 + K2) + P H2, Qbar = (2Gb + 2K1 + 2K2 + K3) + P H1,
 // then dtheta[k(i,j)] = Qbar[i][j] - Qbar[j][i].
-// For b % 64 == 0 every product runs on split-bf16 MFMA (k_cnp.hip); other b use
-// the float32 vector-ALU product.
+// For b in {64, 128, 256, 512} both directions run as row-panel chains of products
+// by Q (k_cnp.hip): the forward as G = (((Q + 2I)Q + 2I)Q + 2I)Q + I in one launch,
+// the backward as K_l = -K_{l-1}Q (rows of Gb P^l) in one launch and the same
+// Horner in P, transposed (Qbar^T = R0^T + (R1^T + (R2^T + Gb^T Q)Q)Q), in a second.
+// Other b % 64 == 0 run the products above one launch each on split-bf16 MFMA;
+// the remaining b use the float32 vector-ALU product.
 namespace {
 
 GemmDesc batched_f32(int64_t n, int64_t b, const float *A, const float *B, void *C, int c_dt) {
@@ -159,6 +163,21 @@ int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype,
                  hipStream_t s) {
   Arena ar(ws);
   size_t blk = (size_t)n * b * b * 4;
+  if (cnp_chain_supported(b)) {
+    // Q as bf16 planes, then the whole Horner chain in one launch
+    SkewSegs un;
+    un.src[0] = theta; un.n[0] = n;
+    un.planes[0] = (bf16_t *)ar.take(blk);
+    POETX_TRY(unpack_skew2(un, b, s));
+    CnpChainArgs c;
+    c.b = (int)b;
+    c.mode = CNP_CHAIN_FWD;
+    c.name = "cnp_fwd_chain";
+    c.seg[0].qp = un.planes[0]; c.seg[0].nblk = n;
+    if (g_dtype == POETX_F32) c.seg[0].out = (float *)g;
+    else c.seg[0].outb = (bf16_t *)g;
+    return cnp_chain(c, s);
+  }
   float *Q = (float *)ar.take(blk), *S = (float *)ar.take(blk);
   float *T = (float *)ar.take(blk), *U = (float *)ar.take(blk);
   POETX_TRY(unpack_skew(theta, Q, n, b, s));
@@ -194,7 +213,34 @@ struct CnpBwdSide {
 };
 
 // CNP backward of up to two independent sides sharing b (the R and P sides of a layer).
+int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
+  Arena ar(ws);
+  SkewSegs un, pk;
+  CnpChainArgs ca, cb;
+  ca.b = cb.b = (int)b;
+  ca.mode = CNP_CHAIN_BWDA; ca.name = "cnp_bwd_chain_a";
+  cb.mode = CNP_CHAIN_BWDB; cb.name = "cnp_bwd_chain_b";
+  for (int i = 0; i < nside; ++i) {
+    const size_t blk = (size_t)side[i].n * b * b * 4;
+    un.src[i] = side[i].theta; un.n[i] = side[i].n;
+    un.planes[i] = (bf16_t *)ar.take(blk);
+    CnpChainSeg g;
+    g.qp = un.planes[i]; g.dg = side[i].dg; g.nblk = side[i].n;
+    for (int j = 0; j < 3; ++j) g.r[j] = (float *)ar.take(blk);
+    g.out = (float *)ar.take(blk);
+    ca.seg[i] = g;
+    cb.seg[i] = g;
+    pk.src[i] = g.out; pk.dst[i] = side[i].dtheta; pk.n[i] = side[i].n;
+  }
+  POETX_TRY(unpack_skew2(un, b, s));
+  // first half (rows of Gb P^l) for every block, then the transposed left-Horner half
+  POETX_TRY(cnp_chain(ca, s));
+  POETX_TRY(cnp_chain(cb, s));
+  return pack_skew_grad2(pk, b, s);
+}
+
 int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
+  if (cnp_chain_supported(b)) return cnp_bwd_chain(b, side, nside, ws, s);
   Arena ar(ws);
   struct Bufs { float *Q, *K1, *K2, *K3, *Ha, *Hb; } B[2] = {};
   SkewSegs un;

@@ -21,6 +21,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 namespace {
@@ -56,13 +57,27 @@ __global__ __launch_bounds__(NTH) void k_cnp_mm(CnpMMArgs a) {
   __shared__ __align__(16) bf16_t sAh[2][TM * A_LD], sAl[2][TM * A_LD];
   __shared__ __align__(16) bf16_t sBh[2][TK * B_LD], sBl[2][TK * B_LD];
   const int b = a.b;
-  int64_t z = blockIdx.z;
+  // 1-D grid; workgroup L runs on XCD L % 8.  All tiles of one b x b block go to the
+  // same XCD (block = xcd + 8 * (slot / T)), so each block's operands are fetched
+  // into one L2 only; blocks past the last full group of 8 keep the plain order.
+  const int tpr = b / TM, T = tpr * tpr;
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk, nz8 = nz & ~(int64_t)7;
+  const int64_t L = blockIdx.x;
+  int64_t z, t;
+  if (L < nz8 * T) {
+    const int64_t slot = L >> 3;
+    z = (L & 7) + 8 * (slot / T);
+    t = slot % T;
+  } else {
+    z = L / T;
+    t = L % T;
+  }
   int sg = 0;
   if (z >= a.seg[0].nblk) { z -= a.seg[0].nblk; sg = 1; }
   const CnpMMSeg &S = a.seg[sg];
   const int64_t off = z * (int64_t)b * b;
   const float *A = S.A + off, *B = S.B + off;
-  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TM;
+  const int m0 = (int)(t / tpr) * TM, n0 = (int)(t % tpr) * TM;
   const int tid = threadIdx.x, wave = tid >> 6, wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
 
   // register ring of RD k-steps in flight: the small per-step MFMA work cannot cover a
@@ -183,14 +198,304 @@ template __global__ void k_cnp_mm<16>(CnpMMArgs);
 int cnp_mm(const CnpMMArgs &a, hipStream_t s) {
   const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
   if (nz <= 0) return POETX_OK;
-  if (a.b % TM || nz > 65535) return POETX_ERR_UNSUPPORTED;
-  dim3 grid(a.b / TM, a.b / TM, (unsigned)nz);
+  const int64_t nwg = nz * (a.b / TM) * (a.b / TM);
+  if (a.b % TM || nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
+  dim3 grid((unsigned)nwg);
   switch (a.b) {
     case 64: return launch(a.name, s, [&] { k_cnp_mm<2><<<grid, NTH, 0, s>>>(a); });
     case 128: return launch(a.name, s, [&] { k_cnp_mm<4><<<grid, NTH, 0, s>>>(a); });
     case 256: return launch(a.name, s, [&] { k_cnp_mm<8><<<grid, NTH, 0, s>>>(a); });
     case 512: return launch(a.name, s, [&] { k_cnp_mm<16><<<grid, NTH, 0, s>>>(a); });
     default: return launch(a.name, s, [&] { k_cnp_mm<0><<<grid, NTH, 0, s>>>(a); });
+  }
+}
+
+
+
+// ================================================================ chains ====
+// Every product of the Cayley-Neumann steps can be written as X.Q with the same Q:
+//   forward   G = (((Q + 2I) Q + 2I) Q + 2I) Q + I                 (eq. 9, Horner in Q)
+//   backward  with P = Q^T = -Q, K_l = Gb P^l and R_j = sum_{l <= 3-j} a_{j+l+1} Gb P^l,
+//             Qbar = R0 + P (R1 + P (R2 + P Gb)), so
+//             Qbar^T = R0^T + (R1^T + (R2^T + Gb^T Q) Q) Q.
+// A row panel of X.Q needs only the same rows of X, so one workgroup runs a whole
+// chain on a 32-row panel, which stays in LDS as split planes.  Q never goes
+// through LDS: the unpack stores its bf16 planes in MFMA fragment order (see
+// cnp_frag_off), so each wave streams its own B fragments from L2 straight into
+// registers with 16-byte coalesced loads, several k steps ahead, and the waves
+// only meet at the end of each product, when the panel is replaced.  Only the
+// backward's first half has to finish for every row before the second starts.
+namespace {
+constexpr int RP = 32, CTK = 32, CNTH = 512;
+
+template <int B>
+struct ChainCfg {
+  static constexpr int NK = B / CTK;                  // k steps per product
+  static constexpr int NT = B / 16;                   // 16-column tiles of Q
+  static constexpr int WM = B >= 128 ? 2 : 1;         // 16-row tiles per wave
+  static constexpr int WN = B >= 128 ? B / 128 : 1;   // 16-column tiles per wave
+  // k steps of B fragments in flight per wave: enough bytes in flight to cover the
+  // latency of the first product, whose fragments are not in L2 yet
+  static constexpr int D = B >= 512 ? 2 : (3 * NK < 8 ? 3 * NK : 8);
+  static constexpr int A_LD = B + 8;
+  static constexpr int NP = B / RP;                   // panels per block
+};
+
+__device__ inline bf16x8 frag_a_ld(const bf16_t *t, int ld, int r0, int k0) {
+  int l = threadIdx.x & 63;
+  s16x8 v = *(const s16x8 *)(t + (r0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ inline void put_split4(bf16_t *h, bf16_t *lo, float4 v) {
+  uint16_t a[4], c[4];
+  split2(v.x, a[0], c[0]); split2(v.y, a[1], c[1]); split2(v.z, a[2], c[2]); split2(v.w, a[3], c[3]);
+  *(uint2 *)h = make_uint2(a[0] | (uint32_t)a[1] << 16, a[2] | (uint32_t)a[3] << 16);
+  *(uint2 *)lo = make_uint2(c[0] | (uint32_t)c[1] << 16, c[2] | (uint32_t)c[3] << 16);
+}
+}  // namespace
+
+template <int B, int MODE>
+__global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
+  using C = ChainCfg<B>;
+  extern __shared__ __align__(16) bf16_t smem[];
+  bf16_t *sAh = smem, *sAl = smem + RP * C::A_LD;
+
+  // 1-D grid, all panels of one block on one XCD (workgroup L runs on XCD L % 8)
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk, nz8 = nz & ~(int64_t)7;
+  const int64_t L = blockIdx.x;
+  int64_t z, pnl;
+  if (L < nz8 * C::NP) {
+    const int64_t slot = L >> 3;
+    z = (L & 7) + 8 * (slot / C::NP);
+    pnl = slot % C::NP;
+  } else {
+    z = L / C::NP;
+    pnl = L % C::NP;
+  }
+  int sg = 0;
+  if (z >= a.seg[0].nblk) { z -= a.seg[0].nblk; sg = 1; }
+  const CnpChainSeg &S = a.seg[sg];
+  const int64_t off = z * (int64_t)B * B;
+  const int r0 = (int)pnl * RP;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int mb = B >= 128 ? 0 : 16 * (wave >> 2);
+  const int nb = B >= 128 ? wave * (B / 8) : 16 * (wave & 3);
+
+  // ---- B fragments of Q: chunk (k, t, plane) of 1 KB holds what lane l needs for
+  // k step k and column tile t; this wave reads tiles nb/16 .. nb/16 + WN - 1.
+  const bf16_t *qf = S.qp + 2 * off;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(qf), (short)0, 4 * B * B, 0x00020000);
+  const int voff = l * 16 + (nb / 16) * 2048;
+  u32x4 fb[C::D][C::WN][2];
+  auto fload = [&](int slot, int k) {
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+        fb[slot][j][pl] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff, (k * C::NT + j) * 2048 + pl * 1024, 0));
+  };
+#pragma unroll
+  for (int s = 0; s < C::D; ++s) fload(s, s % C::NK);
+
+  // ---- start panel
+  f32x4 run[C::WM][C::WN];  // BWDA: running 2Gb + 2K1 + ... in accumulator layout
+  if constexpr (MODE == CNP_CHAIN_FWD) {
+    // X = Q[rows] + 2I: rows r0.. are k step pnl of the fragment-ordered planes
+    for (int q = tid; q < C::NT * 2 * 64; q += CNTH) {
+      const int ln = q & 63, pl = (q >> 6) & 1, t = q >> 7;
+      const u32x4 v = *(const u32x4 *)(qf + ((pnl * C::NT + t) * 2 + pl) * 512 + ln * 8);
+      bf16_t *dst = (pl ? sAl : sAh) + (8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e * C::A_LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+    if (tid < RP) sAh[tid * C::A_LD + r0 + tid] = 0x4000;  // bf16(2.0); Q has a zero diagonal
+  } else if constexpr (MODE == CNP_CHAIN_BWDA) {
+    const float *G = S.dg + off;
+    for (int q = tid; q < RP * B / 4; q += CNTH) {
+      const int row = q / (B / 4), c4 = q % (B / 4);
+      const float4 v = *(const float4 *)(G + (int64_t)(r0 + row) * B + c4 * 4);
+      put_split4(sAh + row * C::A_LD + c4 * 4, sAl + row * C::A_LD + c4 * 4, v);
+    }
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j) {
+        const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
+        const float4 v = *(const float4 *)(G + (int64_t)(r0 + m) * B + n);
+        run[i][j] = f32x4{2.f * v.x, 2.f * v.y, 2.f * v.z, 2.f * v.w};
+      }
+  } else {
+    // X = Gb^T[rows]: X[m][k] = Gb[k][r0 + m]
+    const float *G = S.dg + off;
+    for (int q = tid; q < B * RP / 4; q += CNTH) {
+      const int k = q / (RP / 4), c4 = q % (RP / 4);
+      const float4 v = *(const float4 *)(G + (int64_t)k * B + r0 + c4 * 4);
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint16_t h, lo;
+        split2(e[t], h, lo);
+        sAh[(c4 * 4 + t) * C::A_LD + k] = h;
+        sAl[(c4 * 4 + t) * C::A_LD + k] = lo;
+      }
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[C::WM][C::WN];
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int NS = 3 * C::NK;
+  // one k step of product p; st is always a compile-time value, p is one too for
+  // b <= 256 (everything unrolled: every wait on the loads in flight is exact) and a
+  // loop variable for b = 512 (three unrolled products would not fit the registers)
+  auto step = [&](const int st, const int p) {
+    const int g = p * C::NK + st;
+    const int u = C::NK % C::D == 0 ? st % C::D : g % C::D;
+    bf16x8 ah[C::WM], al[C::WM], fbh[C::WN], fbl[C::WN];
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i) {
+      ah[i] = frag_a_ld(sAh, C::A_LD, mb + 16 * i, st * CTK);
+      al[i] = frag_a_ld(sAl, C::A_LD, mb + 16 * i, st * CTK);
+    }
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      fbh[j] = __builtin_bit_cast(bf16x8, fb[u][j][0]);
+      fbl[j] = __builtin_bit_cast(bf16x8, fb[u][j][1]);
+    }
+    // operands swapped: lane l holds C[m = l%16][n = 4*(l/16) + 0..3]; pass-major
+    // order puts the other accumulators between two passes on the same one
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbl[j], ah[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbh[j], al[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbh[j], ah[i], acc[i][j], 0, 0, 0);
+    if (g + C::D < NS) fload(u, (st + C::D) % C::NK);  // refill the slot just consumed
+
+    if (st == C::NK - 1) {
+      // ---- end of product p: every wave is done with the panel before it is replaced
+      if (p < 2) __syncthreads();
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::WN; ++j) {
+          const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
+          const int gm = r0 + m;  // row within the block
+          f32x4 v = acc[i][j];
+          if constexpr (MODE == CNP_CHAIN_FWD) {
+            const float d = p < 2 ? 2.f : 1.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (gm == n + c) v[c] += d;
+            if (p == 2) {
+              const int64_t e = off + (int64_t)gm * B + n;
+              if (S.out) *(float4 *)(S.out + e) = make_float4(v[0], v[1], v[2], v[3]);
+              if (S.outb) {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                *(uint2 *)(S.outb + e) = pk;
+              }
+            }
+          } else if constexpr (MODE == CNP_CHAIN_BWDA) {
+            v = -v;                    // K_{p+1} = -X Q
+            const f32x4 r = run[i][j] + v;
+            run[i][j] += 2.f * v;
+            float *R = S.r[p] + off;   // transposed store: R^T[n + c][gm]
+#pragma unroll
+            for (int c = 0; c < 4; ++c) R[(int64_t)(n + c) * B + gm] = r[c];
+          } else {
+            const float4 e = *(const float4 *)(S.r[p] + off + (int64_t)gm * B + n);
+            v[0] += e.x; v[1] += e.y; v[2] += e.z; v[3] += e.w;
+            if (p == 2) {
+              float *O = S.out + off;  // X^T = Qbar
+#pragma unroll
+              for (int c = 0; c < 4; ++c) O[(int64_t)(n + c) * B + gm] = v[c];
+            }
+          }
+          if (p < 2)
+            put_split4(sAh + m * C::A_LD + n, sAl + m * C::A_LD + n, make_float4(v[0], v[1], v[2], v[3]));
+          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      if (p < 2) __syncthreads();
+    }
+  };
+  if constexpr (B >= 512) {
+    static_assert(C::NK % C::D == 0, "slots must not depend on p");
+#pragma unroll 1
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int st = 0; st < C::NK; ++st) step(st, p);
+  } else {
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int st = 0; st < C::NK; ++st) step(st, p);
+  }
+}
+
+#define POETX_CHAIN_INST(B)                                          \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_FWD>(CnpChainArgs);  \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDA>(CnpChainArgs); \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDB>(CnpChainArgs);
+POETX_CHAIN_INST(64)
+POETX_CHAIN_INST(128)
+POETX_CHAIN_INST(256)
+POETX_CHAIN_INST(512)
+#undef POETX_CHAIN_INST
+
+bool cnp_chain_supported(int64_t b) { return b == 64 || b == 128 || b == 256 || b == 512; }
+
+namespace {
+template <int B>
+int chain_run(const CnpChainArgs &a, hipStream_t s) {
+  using C = ChainCfg<B>;
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
+  const int64_t nwg = nz * C::NP;
+  if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
+  const size_t lds = (size_t)2 * RP * C::A_LD * sizeof(bf16_t);
+  static bool attr[3] = {false, false, false};  // dynamic LDS above 64 KB, set once per kernel
+  auto go = [&](void (*kern)(CnpChainArgs), int mode) -> int {
+    if (!attr[mode]) {
+      if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return POETX_ERR_HIP;
+      attr[mode] = true;
+    }
+    return launch(a.name, s, [&] { kern<<<dim3((unsigned)nwg), CNTH, lds, s>>>(a); });
+  };
+  switch (a.mode) {
+    case CNP_CHAIN_FWD: return go(k_cnp_chain<B, CNP_CHAIN_FWD>, 0);
+    case CNP_CHAIN_BWDA: return go(k_cnp_chain<B, CNP_CHAIN_BWDA>, 1);
+    case CNP_CHAIN_BWDB: return go(k_cnp_chain<B, CNP_CHAIN_BWDB>, 2);
+    default: return POETX_ERR_INVALID_ARG;
+  }
+}
+}  // namespace
+
+int cnp_chain(const CnpChainArgs &a, hipStream_t s) {
+  if (a.seg[0].nblk + a.seg[1].nblk <= 0) return POETX_OK;
+  switch (a.b) {
+    case 64: return chain_run<64>(a, s);
+    case 128: return chain_run<128>(a, s);
+    case 256: return chain_run<256>(a, s);
+    case 512: return chain_run<512>(a, s);
+    default: return POETX_ERR_UNSUPPORTED;
   }
 }
 

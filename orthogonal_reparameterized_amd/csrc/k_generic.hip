@@ -306,11 +306,60 @@ __global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
   }
 }
 
+// Fragment-order planes (b % 32 == 0): workgroup (cb, rb) builds the 32 x 32 tile of
+// Q at rows 32 rb.., columns 32 cb.. from the upper-triangle tile it mirrors (read
+// along theta's rows, transposed through LDS when rb > cb), then writes it as four
+// 1 KB fragment chunks (2 column tiles x 2 planes), 16 bytes per thread.
+__global__ __launch_bounds__(256) void k_unpack_frag(SkewSegs sg, int64_t b) {
+  __shared__ float t[32][33];
+  const int rb = blockIdx.y, cb = blockIdx.x;
+  int64_t z = blockIdx.z;
+  int si = 0;
+  if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
+  const float *th = sg.src[si] + z * (b * (b - 1) / 2);
+  const int ur = rb < cb ? rb : cb, uc = rb < cb ? cb : rb;
+  const int tid = threadIdx.x, tc = tid & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tr = (tid >> 5) + 8 * i;
+    const int64_t r = ur * 32 + tr, c = uc * 32 + tc;
+    t[tr][tc] = r < c ? th[triu_index(r, c, b)] : 0.f;
+  }
+  __syncthreads();
+  const int tt = tid >> 7, pl = (tid >> 6) & 1, ln = tid & 63;
+  const int col = 16 * tt + (ln & 15);
+  uint32_t w[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    uint32_t h2 = 0;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 8 * (ln >> 4) + 2 * e2 + hf;
+      // Q[r][c] = theta(r, c) above the diagonal, -theta(c, r) below, 0 on it
+      float v;
+      if (rb < cb) v = t[row][col];
+      else if (rb > cb) v = -t[col][row];
+      else v = row < col ? t[row][col] : (row > col ? -t[col][row] : 0.f);
+      const bf16_t hi = f32_to_bf16(v);
+      const bf16_t q = pl ? f32_to_bf16(v - bf16_to_f32(hi)) : hi;
+      h2 |= (uint32_t)q << (16 * hf);
+    }
+    w[e2] = h2;
+  }
+  bf16_t *dst = sg.planes[si] + 2 * z * b * b + cnp_frag_off(32 * rb, 32 * cb + 16 * tt, b) + pl * 512 + ln * 8;
+  *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   const int64_t nz = sg.n[0] + sg.n[1];
   if (nz <= 0) return POETX_OK;
   const unsigned T = (unsigned)cdiv(b, 32);
-  return launch("unpack_skew", s, [&] { k_unpack_skew<<<dim3(T, T, (unsigned)nz), 256, 0, s>>>(sg, b); });
+  const dim3 grid(T, T, (unsigned)nz);
+  if (sg.planes[0]) {
+    if (b % 32) return POETX_ERR_UNSUPPORTED;
+    return launch("unpack_skew", s, [&] { k_unpack_frag<<<grid, 256, 0, s>>>(sg, b); });
+  }
+  return launch("unpack_skew", s, [&] { k_unpack_skew<<<grid, 256, 0, s>>>(sg, b); });
 }
 
 int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t s) {

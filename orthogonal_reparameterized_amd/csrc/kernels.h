@@ -39,9 +39,22 @@ int gather_f32(const float *src, float *out, int64_t n, const int32_t *perm, hip
 // Packed skew helpers (Method §4 storage), over up to two segments of blocks:
 //   unpack: dst = Q[n][b][b] from src = theta[n][b(b-1)/2]
 //   pack  : dst = dtheta[k(i,j)] = M[i][j] - M[j][i] from src = M[n][b][b]
+//   unpack with planes[0] set (b % 32 == 0): Q as bf16 planes hi = bf16(Q) and
+//   lo = bf16(Q - hi) in MFMA fragment order (cnp_frag_off), instead of dst
+// Element offset of Q[r][c] (hi plane; the lo plane is 512 further) within one
+// block's 2 b^2 fragment-ordered planes: 1 KB chunks (k step kk = r / 32, column
+// tile t = c / 16, plane), each the B operand of a v_mfma_f32_16x16x32_bf16 for
+// that k step and tile, lane l holding Q[32 kk + 8 (l / 16) + e][16 t + l % 16]
+// as element e = 0..7.
+__host__ __device__ inline int64_t cnp_frag_off(int64_t r, int64_t c, int64_t b) {
+  const int64_t kk = r >> 5, kr = r & 31, t = c >> 4;
+  const int64_t lane = 16 * (kr >> 3) + (c & 15);
+  return (kk * (b >> 4) + t) * 1024 + lane * 8 + (kr & 7);
+}
 struct SkewSegs {
   const float *src[2] = {nullptr, nullptr};
   float *dst[2] = {nullptr, nullptr};
+  bf16_t *planes[2] = {nullptr, nullptr};
   int64_t n[2] = {0, 0};
 };
 int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s);
@@ -123,5 +136,32 @@ struct CnpMMArgs {
   const char *name = "cnp_mm";
 };
 int cnp_mm(const CnpMMArgs &a, hipStream_t s);
+
+// Row-panel chains of products by one b x b matrix Q per block (b in {64, 128, 256,
+// 512}), float32-accurate through split-bf16 MFMA, Q given as its bf16 planes
+// qp[n][2][b][b] (the unpack's planes layout).  One workgroup keeps a 32-row panel X of its block resident and runs
+// X <- X.Q three times; the mode fixes the start panel and what happens between
+// products (all matrices [n][b][b] row-major float32 unless noted):
+//   CNP_CHAIN_FWD : X = Q + 2I; X <- XQ + 2I; X <- XQ + 2I; G = XQ + I   -> g (f32 or bf16)
+//   CNP_CHAIN_BWDA: X = Gb; K_s = -XQ, X <- K_s; writes, transposed, r[0] = (2Gb + K1)^T,
+//                   r[1] = (2Gb + 2K1 + K2)^T, r[2] = (2Gb + 2K1 + 2K2 + K3)^T
+//   CNP_CHAIN_BWDB: X = Gb^T; X <- XQ + r[0]; X <- XQ + r[1]; X <- XQ + r[2]; writes X^T
+//                   (that is Qbar) -> out
+enum { CNP_CHAIN_FWD = 0, CNP_CHAIN_BWDA = 1, CNP_CHAIN_BWDB = 2 };
+struct CnpChainSeg {
+  const bf16_t *qp = nullptr;
+  const float *dg = nullptr;
+  float *r[3] = {nullptr, nullptr, nullptr};
+  float *out = nullptr;
+  bf16_t *outb = nullptr;
+  int64_t nblk = 0;
+};
+struct CnpChainArgs {
+  int b = 0, mode = CNP_CHAIN_FWD;
+  CnpChainSeg seg[2];
+  const char *name = "cnp_chain";
+};
+bool cnp_chain_supported(int64_t b);
+int cnp_chain(const CnpChainArgs &a, hipStream_t s);
 
 }  // namespace poetx

@@ -44,7 +44,14 @@ def _say(*a):
 
 # ------------------------------------------------------------------- CNP ----
 
-@pytest.mark.parametrize("n,b,std", [(8, 32, 0.02), (3, 256, 0.01), (2, 512, 0.01), (5, 48, 0.05)])
+# b = 64..512 run the row-panel chains (n = 11 and 19 also cover the blocks past the
+# last full group of 8 in the workgroup order), b = 192 the per-product MFMA path,
+# b = 32 and 48 the float32 vector-ALU path
+CNP_CASES = [(8, 32, 0.02), (11, 64, 0.03), (19, 128, 0.02), (3, 192, 0.01), (3, 256, 0.01),
+             (2, 512, 0.01)]
+
+
+@pytest.mark.parametrize("n,b,std", CNP_CASES + [(5, 48, 0.05)])
 def test_cnp_forward_f32(B, n, b, std):
     _say(f"cnp fwd f32 n={n} b={b}")
     theta, _ = WL.make_cnp_inputs(n, b, std, seed=100 + b)
@@ -53,7 +60,7 @@ def test_cnp_forward_f32(B, n, b, std):
     assert rel_fro_per_block(to_host_f64(g), ref) <= TOL_CNP_F32
 
 
-@pytest.mark.parametrize("n,b", [(4, 256), (2, 512)])
+@pytest.mark.parametrize("n,b", [(9, 64), (4, 128), (4, 256), (2, 512)])
 def test_cnp_forward_bf16_ulp(B, n, b):
     _say(f"cnp fwd bf16 n={n} b={b}")
     theta, _ = WL.make_cnp_inputs(n, b, 0.01, seed=200 + b)
@@ -72,7 +79,7 @@ def test_cnp_zero_is_identity(B):
         assert torch.equal(g.float().cpu(), torch.eye(b).expand(3, b, b))
 
 
-@pytest.mark.parametrize("n,b,std", [(8, 32, 0.02), (3, 256, 0.01), (2, 512, 0.01)])
+@pytest.mark.parametrize("n,b,std", CNP_CASES)
 def test_cnp_backward_f32(B, n, b, std):
     _say(f"cnp bwd f32 n={n} b={b}")
     theta, dg = WL.make_cnp_inputs(n, b, std, seed=300 + b)
