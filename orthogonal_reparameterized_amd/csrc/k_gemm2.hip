@@ -519,6 +519,157 @@ POETX_BS_INST(256, 128, 64)
 POETX_BS_INST(512, 64, 32)
 #undef POETX_BS_INST
 
+// Register-resident variant for b = 128 and 256: each of the 4 consumer waves keeps
+// its b x (b/4) share of G_j (or G_j^T) as MFMA operand fragments in registers for
+// the whole kernel (b = 256: 128 VGPRs), so one workgroup covers the block's full
+// width -- every token tile of X_j is read once -- and the whole LDS is a 4-stage
+// ring of T-token tiles (more bytes in flight per CU than with G held in LDS).
+// G is staged once through the ring's LDS at the start.  Workgroup u covers block
+// j = u % nb and token tiles p, p + P, ... with p = u / nb, so the blocks of the
+// same token rows run side by side.
+template <int LX, int K>
+__device__ inline void wait_tiles(int later) {  // vmcnt <= later * LX, later clamped to K
+  if constexpr (K == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= K) wait_vmcnt<K * LX>();
+    else wait_tiles<LX, K - 1>(later);
+  }
+}
+
+template <int B, int T, int NST, bool TRANS>
+__global__ __launch_bounds__(384) void k_block_reg(BSArgs a) {
+  constexpr int NCW = 4, NPW = 2;
+  constexpr int NTW = B / 64, NKS = B / 32, FM = T / 16;
+  constexpr int A_ELEMS = T * B;
+  static_assert(NST * A_ELEMS >= B * B, "G is staged in the ring");
+  extern __shared__ __align__(16) bf16_t smem[];
+  const int u = blockIdx.x;
+  if (u >= a.nb * a.P) return;
+  const int p = u / a.nb, j = u % a.nb;
+  const int64_t ntile = (a.N + T - 1) / T;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const bool producer = wave >= NCW;
+  const int n0 = wave * (B / 4);  // a consumer's first output column within the block
+
+  // ---- this wave's columns of the block operand, into registers
+  bf16x8 gf[NTW][NKS];
+  if (!producer) {
+    const bf16_t *Gj = a.G + (int64_t)j * B * B;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gj, (int64_t)B * B * 2);
+    if constexpr (TRANS) {
+      LoaderKC<B, NCW, B, 0> lg;  // rows n, k contiguous: G_j^T fragments via frag_kc
+      lg.init(B, 0);
+      lg.issue(rg, 0, B, smem);
+    } else {
+      LoaderKM<B, NCW, B, 0> lg;  // rows k, n contiguous: G_j fragments via frag_km
+      lg.init(B, 0);
+      lg.issue(rg, 0, B, smem);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  if (!producer) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        gf[t][s] = TRANS ? frag_kc<B>(smem, n0 + 16 * t, 32 * s) : frag_km<B>(smem, n0 + 16 * t, 32 * s);
+  }
+  __syncthreads();  // the ring may now overwrite the staged block
+
+  using LXT = LoaderKC<T, NPW, B, NCW>;
+  constexpr int LX = LXT::INSTR;
+  LXT lx;
+  const bf16_t *Xj = a.X + (int64_t)j * B;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xj, a.N * a.d * 2);
+  if (producer) {
+    lx.init(a.d, 0);
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s) {
+      const int64_t tl = p + (int64_t)s * a.P;
+      if (tl < ntile) lx.issue(rx, tl * T * a.d, a.d, smem + s * A_ELEMS);
+    }
+  }
+  int64_t tile = p;
+  for (int it = 0; tile < ntile; ++it, tile += a.P) {
+    if (producer) {
+      // tiles it .. it + NST - 2 may be in flight (loads complete in order): wait for
+      // tile it only
+      const int64_t later = (ntile - 1 - tile) / a.P;
+      wait_tiles<LX, NST - 2>((int)(later < NST - 2 ? later : NST - 2));
+    }
+    __syncthreads();  // tile it is in LDS; the stage read in iteration it-1 is free
+    if (producer) {
+      const int64_t nx = tile + (int64_t)(NST - 1) * a.P;
+      if (nx < ntile) lx.issue(rx, nx * T * a.d, a.d, smem + ((it + NST - 1) % NST) * A_ELEMS);
+      continue;
+    }
+    const bf16_t *ta = smem + (it % NST) * A_ELEMS;
+    f32x4 acc[FM][NTW];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; s2 += 2) {
+      bf16x8 fa[2][FM];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[h][i] = frag_kc<B>(ta, 16 * i, 32 * (s2 + h));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int t = 0; t < NTW; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[t][s2 + h], fa[h][i], acc[i][t], 0, 0, 0);
+    }
+    // epilogue: lane holds Y[m = l%16][n = 4*(l/16) + 0..3] of each 16 x 16 patch
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = tile * T + 16 * i + (l & 15);
+      if (m >= a.N) continue;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int64_t n = (int64_t)j * B + n0 + 16 * t + 4 * (l >> 4);
+        f32x4 v = acc[i][t];
+        if (a.scaleN) {
+          float4 sc = *(const float4 *)(a.scaleN + n);
+          v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(uint2 *)(a.Y + m * a.d + n) = pk;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
+}
+// b = 256 uses 32-token tiles (the 128 registers of G leave room for 2 x 4 patches of
+// accumulators), b = 128 64-token tiles; both rings hold 128 or 64 KB
+template __global__ void k_block_reg<128, 64, 4, false>(BSArgs);
+template __global__ void k_block_reg<128, 64, 4, true>(BSArgs);
+template __global__ void k_block_reg<256, 32, 8, false>(BSArgs);
+template __global__ void k_block_reg<256, 32, 8, true>(BSArgs);
+
+template <int B, int T, int NST, bool TRANS>
+static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
+  const size_t lds = (size_t)NST * T * B * 2;
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_reg<B, T, NST, TRANS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  const dim3 grid((unsigned)(a.nb * a.P));
+  return launch(name, s, [&] { k_block_reg<B, T, NST, TRANS><<<grid, 384, lds, s>>>(a); });
+}
+
 template <int B, int SW, int T, bool TRANS>
 static int run_bs(const BSArgs &a, const char *name, hipStream_t s) {
   const size_t lds = ((size_t)B * SW + 3 * (size_t)T * B) * 2;
@@ -548,6 +699,16 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
   BSArgs a;
   a.N = n_tokens; a.d = d; a.nb = (int)(d / b);
   a.X = X; a.G = G; a.Y = Y; a.scaleN = scaleN;
+  if (b == 128 || b == 256) {
+    // one workgroup per (token partition, block), about one per CU in total
+    const int tt = b == 256 ? 32 : 64;
+    const int64_t ntile = (n_tokens + tt - 1) / tt;
+    int64_t P = 256 / a.nb;
+    if (P > ntile) P = ntile;
+    a.P = (int)(P < 1 ? 1 : P);
+    if (b == 128) return transposed ? run_br<128, 64, 4, true>(a, name, s) : run_br<128, 64, 4, false>(a, name, s);
+    return transposed ? run_br<256, 32, 8, true>(a, name, s) : run_br<256, 32, 8, false>(a, name, s);
+  }
   const int sw = b == 512 ? 64 : 128, t = b == 512 ? 32 : 64;
   const int64_t slices = (int64_t)a.nb * (b / sw);
   const int64_t ntile = (n_tokens + t - 1) / t;

@@ -49,13 +49,16 @@ class LayerStep:
         self.w_merged, self.w_scale = B.poetx_merge_perm(w, self.perm_out, self.perm_in, s,
                                                          out_t=self.w_merged_t)
         del w
-        self.theta_r = upload(inputs["theta_r"], "f32", dev)
-        self.theta_p = upload(inputs["theta_p"], "f32", dev)
+        # theta_R and theta_P (and G_R, G_P) live in one buffer each, so that the CNP
+        # forward of both sides is a single poetx_cnp call over n_R + n_P blocks
+        self.n_r, self.n_p = wl.d_in // wl.b, wl.d_out // wl.b
+        self.theta = upload(np.concatenate([inputs["theta_r"], inputs["theta_p"]]), "f32", dev)
+        self.theta_r, self.theta_p = self.theta[:self.n_r], self.theta[self.n_r:]
         self.x = upload(inputs["x"], wl.act, dev)
         self.dz = upload(inputs["dz"], wl.act, dev)
         n, b = self.x.shape[0], wl.b
-        self.g_r = torch.empty((wl.d_in // b, b, b), dtype=act, device=dev)
-        self.g_p = torch.empty((wl.d_out // b, b, b), dtype=act, device=dev)
+        self.g = torch.empty((self.n_r + self.n_p, b, b), dtype=act, device=dev)
+        self.g_r, self.g_p = self.g[:self.n_r], self.g[self.n_r:]
         self.z = torch.empty((n, wl.d_out), dtype=act, device=dev)
         self.saved_b = torch.empty((n, wl.d_out), dtype=act, device=dev) if self.variant == B.POETX_FAST else None
         self.dx = torch.empty((n, wl.d_in), dtype=act, device=dev)
@@ -66,8 +69,8 @@ class LayerStep:
                              perm_in=self.perm_in, perm_out=self.perm_out, w_merged_t=self.w_merged_t)
 
     def cnp(self):
-        B.poetx_cnp(B.POETX_CNP_FWD, self.theta_r, self.wl.b, g=self.g_r)
-        B.poetx_cnp(B.POETX_CNP_FWD, self.theta_p, self.wl.b, g=self.g_p)
+        # both sides share b: one call over the n_R + n_P blocks of the shared buffer
+        B.poetx_cnp(B.POETX_CNP_FWD, self.theta, self.wl.b, g=self.g)
 
     def forward(self):
         B.poetx_forward(self.layer, self.x, self.z, self.saved_b)
