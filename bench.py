@@ -12,7 +12,8 @@ timing starts.  Prints ONE JSON line.
 Extra modes used to make the committed profile summaries:
     --copy-calibration   time a plain 1 GiB device copy (the HBM counter calibration)
     --no-cpu             skip the CPU-oracle baseline leg
-    --summarize-trace DB             markdown kernel table from a rocprofv3 --kernel-trace database
+    --summarize-trace DB [JSON]      markdown kernel table from a rocprofv3 --kernel-trace database
+                                     (with the traced run's JSON line: dominant kernel trace vs events)
     --summarize-counters F W CF CW   HBM traffic of the dominant kernel from four rocprofv3 --pmc
                                      databases (FETCH_SIZE, WRITE_SIZE; then the same two counters
                                      taken on --copy-calibration)
@@ -176,8 +177,7 @@ def load_traffic(kernel, workload_key):
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
-    if kv.get("kernel_source_sha") != sha or "traffic_bytes_per_launch" not in kv:
+    if kv.get("kernel_source_sha") != kernel_source_sha() or "traffic_bytes_per_launch" not in kv:
         return None
     return float(kv["traffic_bytes_per_launch"])
 
@@ -204,13 +204,25 @@ def copy_calibration():
 
 
 KERNEL_SYMBOL = {  # kernel label -> substring of its symbol in traces (workload 3 shapes)
-    "gemm_nt": "k_gemm2<0,", "gemm_nn": "k_gemm_pp<1,", "block_apply": "k_block_stream<256,128,64,false>",
-    "block_apply_t": "k_block_stream<256,128,64,true>", "block_grad": "k_block_grad_stream<256>",
+    "gemm_nt": "k_gemm2<0,", "gemm_nn": "k_gemm_pp<1,", "block_apply": "k_block_reg<256,32,8,false>",
+    "block_apply_t": "k_block_reg<256,32,8,true>", "block_grad": "k_block_grad_stream<256>",
 }
-KERNEL_SOURCE = os.path.join(ROOT, "orthogonal_reparameterized_amd", "csrc", "k_gemm2.hip")
+# the dominant kernel's sources: recorded counters stay valid while these are unchanged
+KERNEL_SOURCES = [os.path.join(ROOT, "orthogonal_reparameterized_amd", "csrc", f)
+                  for f in ("k_gemm2.hip", "lds_tiles.h")]
 
 
-def summarize_trace(db):
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def summarize_trace(db, bench_json=None):
+    """Markdown kernel table of a --kernel-trace database; with the JSON line that the
+    traced bench.py run printed, also the dominant kernel's trace average next to the
+    event-timed average that run reported (the last launches are the event-timed ones)."""
     import sqlite3
     con = sqlite3.connect(db)
     rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), "
@@ -221,6 +233,24 @@ def summarize_trace(db):
     for name, n, avg, mn, mx, sm in rows:
         short = name.replace("(poetx::KArgs)", "").replace("poetx::", "")[:90]
         print(f"| `{short}` | {n} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | {100 * sm / tot:.1f}% |")
+    if bench_json:
+        line = [ln for ln in open(bench_json) if ln.startswith("{")][-1]
+        d = json.loads(line)
+        roof = d.get("roofline") or {}
+        ph = d["phases"][d["config"]["variant"]][roof["kernel"]]
+        n_ev = int(round(ph["launches_per_step"] * d["steps"]))
+        if roof["kernel"] == "gemm_nt" and d["variants"][d["config"]["variant"]].get("w_merged_t"):
+            n_ev *= 2  # the backward product runs the same kernel (on W'^T) in the fast variant
+        sym = KERNEL_SYMBOL[roof["kernel"]].replace(" ", "")
+        durs = [r[1] for r in con.execute("select name, duration from kernels order by start")
+                if sym in r[0].replace(" ", "")]
+        last = durs[-n_ev:]
+        print()
+        print(f"Dominant kernel `{roof['kernel']}` (`{sym}`) in this run: trace average over all "
+              f"{len(durs)} launches {sum(durs) / len(durs) / 1e3:.1f} us, over the last {len(last)} "
+              f"(the event-timed ones) {sum(last) / len(last) / 1e3:.1f} us; bench.py's event-timed "
+              f"average {roof['avg_launch_ms'] * 1e3:.1f} us -> {roof['achieved']:.0f} TFLOP/s, "
+              f"frac {roof['frac']:.3f}; step {d['ms_per_step']:.4f} ms, {d['value'] / 1e6:.3f} M tokens/s.")
 
 
 def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, label=DOMINANT):
@@ -244,7 +274,6 @@ def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, label=D
     sym = KERNEL_SYMBOL[label]
     nf, f = pick(per_kernel(fetch_db, "FETCH_SIZE"), sym)
     nw, w = pick(per_kernel(write_db, "WRITE_SIZE"), sym)
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
     print(f"kernel_label = {label}")
     print(f"kernel_symbol_match = {sym}")
     print(f"dispatches_fetch = {nf}")
@@ -256,8 +285,8 @@ def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, label=D
     print(f"fetch_scale = {f_scale:.4f}")
     print(f"write_scale = {w_scale:.4f}")
     print(f"traffic_bytes_per_launch = {(f * f_scale + w * w_scale) * 1024:.0f}")
-    print(f"kernel_source = {os.path.relpath(KERNEL_SOURCE, ROOT)}")
-    print(f"kernel_source_sha = {sha}")
+    print(f"kernel_sources = {' + '.join(os.path.relpath(f, ROOT) for f in KERNEL_SOURCES)}")
+    print(f"kernel_source_sha = {kernel_source_sha()}")
 
 
 def cnp_bench(wl, steps, warmup):
@@ -313,11 +342,11 @@ def main():
     ap.add_argument("--no-mem", action="store_true")
     ap.add_argument("--no-wt", action="store_true", help="fast variant without the W'^T copy")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-trace", metavar="DB")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="DB [BENCH_JSON]")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DB")
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(*args.summarize_trace[:2])
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)

@@ -1,0 +1,463 @@
+// Block-diagonal products on token-major activations (Method §3: one b x b block per
+// group of b features, batched over the blocks): the streaming apply Y_j = X_j G_j or
+// X_j G_j^T and the per-block gradients X_j^T dY_j.  HBM-bound at the layer's shapes.
+#include "lds_tiles.h"
+
+namespace poetx {
+
+// Streaming block-diagonal product: Y_j = X_j . G_j (TRANS = false) or X_j . G_j^T
+// (TRANS = true) for every b x b block j, where X_j, Y_j are columns [jb, (j+1)b) of
+// token-major activations.  The op is HBM-bound (about 130 flop per byte at b = 256),
+// so each workgroup keeps one SW-wide slice of G_j resident in LDS and streams
+// T-token tiles of X_j through a 3-stage ring (prefetch distance 2), writing the
+// T x SW output tile straight from the accumulators.  A tile is read by the b/SW
+// slice workgroups of its block; their ids are 8 apart so they share an XCD (and its L2).
+struct BSArgs {
+  int64_t N, d;           // tokens, row stride (elements) of X and Y
+  int nb, P;              // blocks; workgroups per (block, slice)
+  const bf16_t *X; const bf16_t *G; bf16_t *Y;
+  const float *scaleN;    // per output column (length d) or null
+};
+
+template <int B, int SW, int T, bool TRANS>
+__global__ __launch_bounds__(384) void k_block_stream(BSArgs a) {
+  // waves 0-3 multiply and store; waves 4-5 only issue the global->LDS loads, so the
+  // producers' vmcnt waits track loads alone and the consumers' stores never stall
+  // the ring
+  constexpr int NCW = 4, NPW = 2;
+  constexpr int NSL = B / SW, NST = 3;
+  constexpr int WTM = T / 2, WTN = SW / 2, FM = WTM / 16, FN = WTN / 16;
+  constexpr int G_ELEMS = B * SW, A_ELEMS = T * B;
+  extern __shared__ __align__(16) bf16_t smem[];
+  bf16_t *sG = smem;
+
+  // blockIdx.x = (u / 8) * (8 * NSL) + h * 8 + u % 8 with u = j * P + p
+  const int x = blockIdx.x;
+  const int h = (x / 8) % NSL;
+  const int u = (x / (8 * NSL)) * 8 + x % 8;
+  if (u >= a.nb * a.P) return;
+  const int j = u / a.P, p = u % a.P;
+  const int64_t ntile = (a.N + T - 1) / T;
+
+  const int wave = threadIdx.x >> 6;
+  const bool producer = wave >= NCW;
+  const int wm = ((wave & 3) >> 1) * WTM, wn = (wave & 1) * WTN;
+  const int l = threadIdx.x & 63;
+
+  using LG = typename std::conditional<TRANS, LoaderKC<SW, NPW, B, NCW>, LoaderKM<SW, NPW, B, NCW>>::type;
+  using LXT = LoaderKC<T, NPW, B, NCW>;
+  constexpr int LX = LXT::INSTR;
+  LXT lx;
+  const bf16_t *Xj = a.X + (int64_t)j * B;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xj, a.N * a.d * 2);
+  if (producer) {
+    const bf16_t *Gs = TRANS ? a.G + (int64_t)j * B * B + (int64_t)h * SW * B : a.G + (int64_t)j * B * B + h * SW;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gs, (int64_t)B * B * 2);
+    LG lg;
+    lg.init(B, 0);
+    lx.init(a.d, 0);
+    lg.issue(rg, 0, B, sG);
+    if (p < ntile) lx.issue(rx, (int64_t)p * T * a.d, a.d, smem + G_ELEMS);
+    if (p + a.P < ntile) lx.issue(rx, (int64_t)(p + a.P) * T * a.d, a.d, smem + G_ELEMS + A_ELEMS);
+  }
+  int64_t tile = p;
+  for (int it = 0; tile < ntile; ++it, tile += a.P) {
+    if (producer) {
+      if (tile + a.P < ntile) wait_vmcnt<LX>();  // this tile (and G) landed; the next may fly
+      else __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();  // the tile is in LDS; the stage of tile it-1 is no longer read
+    if (producer) {
+      if (tile + 2 * a.P < ntile)
+        lx.issue(rx, (tile + 2 * a.P) * T * a.d, a.d, smem + G_ELEMS + ((it + 2) % NST) * A_ELEMS);
+      continue;
+    }
+    const bf16_t *ta = smem + G_ELEMS + (it % NST) * A_ELEMS;
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < B; k2 += 64) {
+      bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int ks = k2 + 32 * hh;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[hh][i] = frag_kc<B>(ta, wm + 16 * i, ks);
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj)
+          fb[hh][jj] = TRANS ? frag_kc<B>(sG, wn + 16 * jj, ks) : frag_km<SW>(sG, wn + 16 * jj, ks);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[hh][jj], fa[hh][i], acc[i][jj], 0, 0, 0);
+    }
+    // epilogue: lane holds Y[m = l%16][n = 4*(l/16) + 0..3] of each 16 x 16 patch
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = tile * T + wm + 16 * i + (l & 15);
+      if (m >= a.N) continue;
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj) {
+        const int64_t n = (int64_t)j * B + h * SW + wn + 16 * jj + 4 * (l >> 4);
+        f32x4 v = acc[i][jj];
+        if (a.scaleN) {
+          float4 sc = *(const float4 *)(a.scaleN + n);
+          v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(uint2 *)(a.Y + m * a.d + n) = pk;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
+}
+
+#define POETX_BS_INST(Bv, SWv, Tv)                                       \
+  template __global__ void k_block_stream<Bv, SWv, Tv, false>(BSArgs); \
+  template __global__ void k_block_stream<Bv, SWv, Tv, true>(BSArgs);
+POETX_BS_INST(128, 128, 64)
+POETX_BS_INST(256, 128, 64)
+POETX_BS_INST(512, 64, 32)
+#undef POETX_BS_INST
+
+// Register-resident variant for b = 128 and 256: each of the 4 consumer waves keeps
+// its b x (b/4) share of G_j (or G_j^T) as MFMA operand fragments in registers for
+// the whole kernel (b = 256: 128 VGPRs), so one workgroup covers the block's full
+// width -- every token tile of X_j is read once -- and the whole LDS is a 4-stage
+// ring of T-token tiles (more bytes in flight per CU than with G held in LDS).
+// G is staged once through the ring's LDS at the start.  Workgroup u covers block
+// j = u % nb and token tiles p, p + P, ... with p = u / nb, so the blocks of the
+// same token rows run side by side.
+template <int B, int T, int NST, bool TRANS>
+__global__ __launch_bounds__(384) void k_block_reg(BSArgs a) {
+  constexpr int NCW = 4, NPW = 2;
+  constexpr int NTW = B / 64, NKS = B / 32, FM = T / 16;
+  constexpr int A_ELEMS = T * B;
+  static_assert(NST * A_ELEMS >= B * B, "G is staged in the ring");
+  extern __shared__ __align__(16) bf16_t smem[];
+  const int u = blockIdx.x;
+  if (u >= a.nb * a.P) return;
+  const int p = u / a.nb, j = u % a.nb;
+  const int64_t ntile = (a.N + T - 1) / T;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const bool producer = wave >= NCW;
+  const int n0 = wave * (B / 4);  // a consumer's first output column within the block
+
+  // ---- this wave's columns of the block operand, into registers
+  bf16x8 gf[NTW][NKS];
+  if (!producer) {
+    const bf16_t *Gj = a.G + (int64_t)j * B * B;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gj, (int64_t)B * B * 2);
+    if constexpr (TRANS) {
+      LoaderKC<B, NCW, B, 0> lg;  // rows n, k contiguous: G_j^T fragments via frag_kc
+      lg.init(B, 0);
+      lg.issue(rg, 0, B, smem);
+    } else {
+      LoaderKM<B, NCW, B, 0> lg;  // rows k, n contiguous: G_j fragments via frag_km
+      lg.init(B, 0);
+      lg.issue(rg, 0, B, smem);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  if (!producer) {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+      for (int s = 0; s < NKS; ++s)
+        gf[t][s] = TRANS ? frag_kc<B>(smem, n0 + 16 * t, 32 * s) : frag_km<B>(smem, n0 + 16 * t, 32 * s);
+  }
+  __syncthreads();  // the ring may now overwrite the staged block
+
+  using LXT = LoaderKC<T, NPW, B, NCW>;
+  constexpr int LX = LXT::INSTR;
+  LXT lx;
+  const bf16_t *Xj = a.X + (int64_t)j * B;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xj, a.N * a.d * 2);
+  if (producer) {
+    lx.init(a.d, 0);
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s) {
+      const int64_t tl = p + (int64_t)s * a.P;
+      if (tl < ntile) lx.issue(rx, tl * T * a.d, a.d, smem + s * A_ELEMS);
+    }
+  }
+  int64_t tile = p;
+  for (int it = 0; tile < ntile; ++it, tile += a.P) {
+    if (producer) {
+      // tiles it .. it + NST - 2 may be in flight (loads complete in order): wait for
+      // tile it only
+      const int64_t later = (ntile - 1 - tile) / a.P;
+      wait_tiles<LX, NST - 2>((int)(later < NST - 2 ? later : NST - 2));
+    }
+    __syncthreads();  // tile it is in LDS; the stage read in iteration it-1 is free
+    if (producer) {
+      const int64_t nx = tile + (int64_t)(NST - 1) * a.P;
+      if (nx < ntile) lx.issue(rx, nx * T * a.d, a.d, smem + ((it + NST - 1) % NST) * A_ELEMS);
+      continue;
+    }
+    const bf16_t *ta = smem + (it % NST) * A_ELEMS;
+    f32x4 acc[FM][NTW];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; s2 += 2) {
+      bf16x8 fa[2][FM];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[h][i] = frag_kc<B>(ta, 16 * i, 32 * (s2 + h));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int t = 0; t < NTW; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[t][s2 + h], fa[h][i], acc[i][t], 0, 0, 0);
+    }
+    // epilogue: lane holds Y[m = l%16][n = 4*(l/16) + 0..3] of each 16 x 16 patch
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = tile * T + 16 * i + (l & 15);
+      if (m >= a.N) continue;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int64_t n = (int64_t)j * B + n0 + 16 * t + 4 * (l >> 4);
+        f32x4 v = acc[i][t];
+        if (a.scaleN) {
+          float4 sc = *(const float4 *)(a.scaleN + n);
+          v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(uint2 *)(a.Y + m * a.d + n) = pk;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
+}
+// b = 256 uses 32-token tiles (the 128 registers of G leave room for 2 x 4 patches of
+// accumulators), b = 128 64-token tiles; both rings hold 128 or 64 KB
+template __global__ void k_block_reg<128, 64, 4, false>(BSArgs);
+template __global__ void k_block_reg<128, 64, 4, true>(BSArgs);
+template __global__ void k_block_reg<256, 32, 8, false>(BSArgs);
+template __global__ void k_block_reg<256, 32, 8, true>(BSArgs);
+
+template <int B, int T, int NST, bool TRANS>
+static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
+  const size_t lds = (size_t)NST * T * B * 2;
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_reg<B, T, NST, TRANS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  const dim3 grid((unsigned)(a.nb * a.P));
+  return launch(name, s, [&] { k_block_reg<B, T, NST, TRANS><<<grid, 384, lds, s>>>(a); });
+}
+
+template <int B, int SW, int T, bool TRANS>
+static int run_bs(const BSArgs &a, const char *name, hipStream_t s) {
+  const size_t lds = ((size_t)B * SW + 3 * (size_t)T * B) * 2;
+  constexpr int NSL = B / SW;
+  const int64_t units = (int64_t)a.nb * a.P;
+  dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_stream<B, SW, T, TRANS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  return launch(name, s, [&] { k_block_stream<B, SW, T, TRANS><<<grid, 384, lds, s>>>(a); });
+}
+
+bool block_stream_supported(int64_t b, int64_t d, int64_t n_tokens) {
+  if (b != 128 && b != 256 && b != 512) return false;
+  if (d % b) return false;
+  return (n_tokens + 64) * d * 2 < 0x7fffffff;
+}
+
+int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t d, int64_t b,
+                 bool transposed, const float *scaleN, const char *name, hipStream_t s) {
+  if (n_tokens <= 0) return POETX_OK;
+  if (!block_stream_supported(b, d, n_tokens)) return POETX_ERR_UNSUPPORTED;
+  BSArgs a;
+  a.N = n_tokens; a.d = d; a.nb = (int)(d / b);
+  a.X = X; a.G = G; a.Y = Y; a.scaleN = scaleN;
+  if (b == 128 || b == 256) {
+    // one workgroup per (token partition, block), about one per CU in total
+    const int tt = b == 256 ? 32 : 64;
+    const int64_t ntile = (n_tokens + tt - 1) / tt;
+    int64_t P = 256 / a.nb;
+    if (P > ntile) P = ntile;
+    a.P = (int)(P < 1 ? 1 : P);
+    if (b == 128) return transposed ? run_br<128, 64, 4, true>(a, name, s) : run_br<128, 64, 4, false>(a, name, s);
+    return transposed ? run_br<256, 32, 8, true>(a, name, s) : run_br<256, 32, 8, false>(a, name, s);
+  }
+  const int sw = b == 512 ? 64 : 128, t = b == 512 ? 32 : 64;
+  const int64_t slices = (int64_t)a.nb * (b / sw);
+  const int64_t ntile = (n_tokens + t - 1) / t;
+  int64_t P = (256 + slices - 1) / slices;  // about one workgroup per CU in total
+  if (P > ntile) P = ntile;
+  a.P = (int)(P < 1 ? 1 : P);
+  if (b == 128) return transposed ? run_bs<128, 128, 64, true>(a, name, s) : run_bs<128, 128, 64, false>(a, name, s);
+  if (b == 256) return transposed ? run_bs<256, 128, 64, true>(a, name, s) : run_bs<256, 128, 64, false>(a, name, s);
+  return transposed ? run_bs<512, 64, 32, true>(a, name, s) : run_bs<512, 64, 32, false>(a, name, s);
+}
+
+
+// Streaming block gradient: parts[p][j][r][c] = sum over the token tiles t = p, p+P, ...
+// of Xs_j[t]^T dY_j[t], for every b x b block j (r indexes columns of Xs_j, c of dY_j).
+// Each workgroup owns one 128 x 128 slice (rs, cs) of one block's gradient and keeps it
+// in registers while T-token tiles of both operands stream through a 4-stage LDS ring
+// (producer waves as in k_block_stream).  The P partials per block are summed later in
+// a fixed order.
+struct BGArgs {
+  int64_t N, d;
+  int nb, P;
+  const bf16_t *Xs; const bf16_t *dY; float *parts;  // parts: [P][nb][b][b]
+};
+
+template <int B>
+__global__ __launch_bounds__(384) void k_block_grad_stream(BGArgs a) {
+  constexpr int NCW = 4, NPW = 2, S = 128, T = 64, NST = 4;
+  constexpr int NSL = (B / S) * (B / S);
+  constexpr int WT = S / 2, F = WT / 16;  // 2 x 2 waves of 64 x 64
+  constexpr int TILE = T * S;             // elements per operand tile
+  extern __shared__ __align__(16) bf16_t smem[];
+
+  const int x = blockIdx.x;
+  const int sl = (x / 8) % NSL;
+  const int u = (x / (8 * NSL)) * 8 + x % 8;
+  if (u >= a.nb * a.P) return;
+  const int j = u / a.P, p = u % a.P;
+  const int rs = sl / (B / S), cs = sl % (B / S);
+  const int64_t ntile = (a.N + T - 1) / T;
+
+  const int wave = threadIdx.x >> 6;
+  const bool producer = wave >= NCW;
+  const int wm = ((wave & 3) >> 1) * WT, wn = (wave & 1) * WT;
+  const int l = threadIdx.x & 63;
+
+  using LT = LoaderKM<S, NPW, T, NCW>;
+  constexpr int LPT = 2 * LT::INSTR;  // loads per producer wave per token tile
+  LT la, lb;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.Xs + (int64_t)j * B + rs * S, a.N * a.d * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.dY + (int64_t)j * B + cs * S, a.N * a.d * 2);
+  auto issue = [&](int64_t t, int stage) {
+    la.issue(ra, t * T, a.d, smem + (2 * stage) * TILE);
+    lb.issue(rb, t * T, a.d, smem + (2 * stage + 1) * TILE);
+  };
+  if (producer) {
+    la.init(a.d, 0);
+    lb.init(a.d, 0);
+    for (int s = 0; s < NST - 1; ++s)
+      if (p + (int64_t)s * a.P < ntile) issue(p + (int64_t)s * a.P, s);
+  }
+  f32x4 acc[F][F];
+#pragma unroll
+  for (int i = 0; i < F; ++i)
+#pragma unroll
+    for (int jj = 0; jj < F; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int64_t tile = p;
+  for (int it = 0; tile < ntile; ++it, tile += a.P) {
+    if (producer) {
+      if (tile + 2 * a.P < ntile) wait_vmcnt<2 * LPT>();
+      else if (tile + a.P < ntile) wait_vmcnt<LPT>();
+      else __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    if (producer) {
+      if (tile + 3 * a.P < ntile) issue(tile + 3 * a.P, (it + 3) % NST);
+      continue;
+    }
+    const bf16_t *ta = smem + (2 * (it % NST)) * TILE, *tb = ta + TILE;
+    bf16x8 fa[2][F], fb[2][F];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int i = 0; i < F; ++i) fa[hh][i] = frag_km<S>(ta, wm + 16 * i, 32 * hh);
+#pragma unroll
+      for (int jj = 0; jj < F; ++jj) fb[hh][jj] = frag_km<S>(tb, wn + 16 * jj, 32 * hh);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int jj = 0; jj < F; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[hh][jj], fa[hh][i], acc[i][jj], 0, 0, 0);
+  }
+  if (!producer) {
+    float *out = a.parts + ((int64_t)p * a.nb + j) * B * B;
+#pragma unroll
+    for (int i = 0; i < F; ++i) {
+      const int r = rs * S + wm + 16 * i + (l & 15);
+#pragma unroll
+      for (int jj = 0; jj < F; ++jj) {
+        const int c = cs * S + wn + 16 * jj + 4 * (l >> 4);
+        *(float4 *)(out + (int64_t)r * B + c) = make_float4(acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
+}
+template __global__ void k_block_grad_stream<128>(BGArgs);
+template __global__ void k_block_grad_stream<256>(BGArgs);
+template __global__ void k_block_grad_stream<512>(BGArgs);
+
+template <int B>
+static int run_bg(const BGArgs &a, hipStream_t s) {
+  constexpr int NSL = (B / 128) * (B / 128);
+  const size_t lds = (size_t)4 * 2 * 64 * 128 * 2;
+  const int64_t units = (int64_t)a.nb * a.P;
+  dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_grad_stream<B>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  return launch("block_grad", s, [&] { k_block_grad_stream<B><<<grid, 384, lds, s>>>(a); });
+}
+
+int64_t block_grad_stream_parts(int64_t b, int64_t d, int64_t n_tokens) {
+  const int64_t slices = (d / b) * (b / 128) * (b / 128);
+  int64_t P = (256 + slices - 1) / slices;
+  const int64_t ntile = (n_tokens + 63) / 64;
+  if (P > ntile) P = ntile;
+  return P < 1 ? 1 : P;
+}
+
+int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t d, int64_t b,
+                      hipStream_t s) {
+  if (!block_stream_supported(b, d, n_tokens)) return POETX_ERR_UNSUPPORTED;
+  BGArgs a;
+  a.N = n_tokens; a.d = d; a.nb = (int)(d / b);
+  a.P = (int)block_grad_stream_parts(b, d, n_tokens);
+  a.Xs = Xs; a.dY = dY; a.parts = parts;
+  if (b == 128) return run_bg<128>(a, s);
+  if (b == 256) return run_bg<256>(a, s);
+  return run_bg<512>(a, s);
+}
+
+}  // namespace poetx
