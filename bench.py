@@ -67,11 +67,18 @@ def algorithmic(wl, variant, n):
     add("block_apply_t", 2.0 * n * di * b, 2 * n * di * ae + g_bytes_r)          # dX~
     add("permute_cols", 0, 2 * n * di * ae)                                       # scatter dX
     add("block_grad", 2.0 * n * di * b, 2 * n * di * ae)                          # dG_R
-    # CNP: forward = 2 float32-accurate b^3 products per block (Q.Q, S.T), backward = 6;
-    # bytes are the float32 operands each product reads and writes (A, B, epilogue terms, C).
+    # CNP, both sides (nb blocks): the forward chain G = (((Q+2I)Q+2I)Q+2I)Q + I and each
+    # of the two backward chains run 3 float32-accurate b^3 products (2 b^3 flops each).
+    # Bytes are the method's minimum: theta in and G out (forward), theta and dG in and
+    # dtheta out (backward, split over its two launches); the unpack and pack launches
+    # carry the theta / dtheta side.
     nb = nr + np_
-    add("cnp_fwd_mm", 4.0 * b ** 3 * nb, nb * b * b * (8 + 4 + 12 + ae))
-    add("cnp_bwd_mm", 12.0 * b ** 3 * nb, nb * b * b * 4 * (3 + 3 + 3 + 4 + 6 + 7))
+    p, bb = b * (b - 1) // 2, b * b
+    add("unpack_skew", 0, 2 * nb * 4 * p)
+    add("cnp_fwd_chain", 6.0 * b ** 3 * nb, nb * ae * bb)
+    add("cnp_bwd_chain_a", 6.0 * b ** 3 * nb, nb * 4 * bb)
+    add("cnp_bwd_chain_b", 6.0 * b ** 3 * nb, 0)
+    add("pack_skew_grad", 0, nb * 4 * p)
     return ops
 
 
@@ -80,9 +87,13 @@ def step_flops(wl, variant, n):
 
 
 def layer_roofline_ms(wl, variant, n):
+    """Sum over kernels of max(flops / MFMA peak, bytes / HBM peak).  The CNP products
+    are float32-accurate through three bf16 MFMA passes, so they count 3x against the
+    bf16 peak; everything else runs one bf16 pass per product."""
     t = 0.0
-    for f, y in algorithmic(wl, variant, n).values():
-        t += max(f / (PEAK_BF16_TFLOPS * 1e12), y / (PEAK_HBM_GBS * 1e9))
+    for name, (f, y) in algorithmic(wl, variant, n).items():
+        passes = 3 if name.startswith("cnp_") else 1
+        t += max(passes * f / (PEAK_BF16_TFLOPS * 1e12), y / (PEAK_HBM_GBS * 1e9))
     return t * 1e3
 
 
