@@ -143,7 +143,10 @@ __global__ __launch_bounds__(384) void k_block_reg(BSArgs a) {
   constexpr int NCW = 4, NPW = 2;
   constexpr int NTW = B / 64, NKS = B / 32, FM = T / 16;
   constexpr int A_ELEMS = T * B;
-  static_assert(NST * A_ELEMS >= B * B, "G is staged in the ring");
+  // per consumer wave, its T x (B/4) output tile is restaged in LDS so that the
+  // global stores are 16 bytes per lane along rows (whole 128-byte lines at b = 256)
+  constexpr int OW = B / 4, OCH = OW / 8, O_ELEMS = T * OW;
+  static_assert(NST * A_ELEMS + NCW * O_ELEMS >= B * B, "G is staged in the ring");
   extern __shared__ __align__(16) bf16_t smem[];
   const int u = blockIdx.x;
   if (u >= a.nb * a.P) return;
@@ -212,13 +215,20 @@ __global__ __launch_bounds__(384) void k_block_reg(BSArgs a) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s2 = 0; s2 < NKS; s2 += 2) {
-      bf16x8 fa[2][FM];
+    // A fragments double-buffered per pair of k steps: the next pair's LDS reads are
+    // in flight while this pair's MFMAs issue
+    bf16x8 fa[2][2][FM];
+    auto read_pair = [&](int q, int s2) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[h][i] = frag_kc<B>(ta, 16 * i, 32 * (s2 + h));
+        for (int i = 0; i < FM; ++i) fa[q][h][i] = frag_kc<B>(ta, 16 * i, 32 * (s2 + h));
+    };
+    read_pair(0, 0);
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; s2 += 2) {
+      const int q = (s2 / 2) & 1;
+      if (s2 + 2 < NKS) read_pair(q ^ 1, s2 + 2);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -226,40 +236,50 @@ __global__ __launch_bounds__(384) void k_block_reg(BSArgs a) {
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int t = 0; t < NTW; ++t)
-            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[t][s2 + h], fa[h][i], acc[i][t], 0, 0, 0);
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[t][s2 + h], fa[q][h][i], acc[i][t], 0, 0, 0);
     }
-    // epilogue: lane holds Y[m = l%16][n = 4*(l/16) + 0..3] of each 16 x 16 patch
+    // epilogue: lane holds Y[m = l%16][n = 4*(l/16) + 0..3] of each 16 x 16 patch; the
+    // bf16 tile goes to this wave's staging rows (16-byte chunks XOR-swizzled by row),
+    // then back out 16 bytes per lane, 8 (b = 256) or 4 (b = 128) lanes per row
+    bf16_t *so = smem + NST * A_ELEMS + wave * O_ELEMS;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t m = tile * T + 16 * i + (l & 15);
-      if (m >= a.N) continue;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
-        const int64_t n = (int64_t)j * B + n0 + 16 * t + 4 * (l >> 4);
+        const int row = 16 * i + (l & 15), col = 16 * t + 4 * (l >> 4);
         f32x4 v = acc[i][t];
         if (a.scaleN) {
-          float4 sc = *(const float4 *)(a.scaleN + n);
+          float4 sc = *(const float4 *)(a.scaleN + (int64_t)j * B + n0 + col);
           v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
         }
         uint2 pk;
         pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
         pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *(uint2 *)(a.Y + m * a.d + n) = pk;
+        const int pch = (col >> 3) ^ (row & (OCH - 1));
+        *(uint2 *)(so + row * OW + pch * 8 + (col & 7)) = pk;
       }
+    __builtin_amdgcn_wave_barrier();  // the wave's LDS writes precede its reads (in order)
+#pragma unroll
+    for (int k = 0; k < T * OCH / 64; ++k) {
+      const int q = l + 64 * k, row = q / OCH, c = q % OCH;
+      const int64_t m = tile * T + row;
+      const uint4 v = *(const uint4 *)(so + row * OW + ((c ^ (row & (OCH - 1))) * 8));
+      if (m < a.N) *(uint4 *)(a.Y + m * a.d + (int64_t)j * B + n0 + c * 8) = v;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
 }
 // b = 256 uses 32-token tiles (the 128 registers of G leave room for 2 x 4 patches of
-// accumulators), b = 128 64-token tiles; both rings hold 128 or 64 KB
+// accumulators) and a 7-stage ring, b = 128 64-token tiles and 4 stages; with the
+// output staging that is 128 or 80 KB of LDS
 template __global__ void k_block_reg<128, 64, 4, false>(BSArgs);
 template __global__ void k_block_reg<128, 64, 4, true>(BSArgs);
-template __global__ void k_block_reg<256, 32, 8, false>(BSArgs);
-template __global__ void k_block_reg<256, 32, 8, true>(BSArgs);
+template __global__ void k_block_reg<256, 32, 7, false>(BSArgs);
+template __global__ void k_block_reg<256, 32, 7, true>(BSArgs);
 
 template <int B, int T, int NST, bool TRANS>
 static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
-  const size_t lds = (size_t)NST * T * B * 2;
+  const size_t lds = (size_t)(NST + 1) * T * B * 2;  // ring + 4 output staging tiles
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_reg<B, T, NST, TRANS>),
@@ -308,7 +328,7 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
     if (P > ntile) P = ntile;
     a.P = (int)(P < 1 ? 1 : P);
     if (b == 128) return transposed ? run_br<128, 64, 4, true>(a, name, s) : run_br<128, 64, 4, false>(a, name, s);
-    return transposed ? run_br<256, 32, 8, true>(a, name, s) : run_br<256, 32, 8, false>(a, name, s);
+    return transposed ? run_br<256, 32, 7, true>(a, name, s) : run_br<256, 32, 7, false>(a, name, s);
   }
   const int sw = b == 512 ? 64 : 128, t = b == 512 ? 32 : 64;
   const int64_t slices = (int64_t)a.nb * (b / sw);

@@ -142,44 +142,61 @@ __global__ __launch_bounds__(512) void k_permute_cols_v(const T *__restrict__ in
 #pragma unroll
     for (int e = 0; e < V; ++e) idx[u][e] = ch < nch ? (cperm ? cperm[ch * V + e] : (int)(ch * V + e)) : 0;
   }
-  for (int64_t r0 = (int64_t)blockIdx.x * RB; r0 < rows; r0 += (int64_t)gridDim.x * RB) {
+  // The next RB rows are loaded into registers while the current ones are written,
+  // so every workgroup keeps reads in flight across its whole loop.
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 pre[RB][MAXC];
+  const int64_t stride = (int64_t)gridDim.x * RB;
+  auto load_rows = [&](int64_t r0) {
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      if (r0 + rr >= rows) continue;
+      const int64_t src = (!scatter && rperm) ? rperm[r0 + rr] : r0 + rr;
+#pragma unroll
+      for (int u = 0; u < MAXC; ++u) {
+        const int64_t ch = threadIdx.x + (int64_t)u * blockDim.x;
+        if (ch < nch) pre[rr][u] = *(const u32x4 *)(in + src * cols + ch * V);
+      }
+    }
+  };
+  int64_t r0 = (int64_t)blockIdx.x * RB;
+  if (r0 < rows) load_rows(r0);
+  for (; r0 < rows; r0 += stride) {
     const int nr = (int)(rows - r0 < RB ? rows - r0 : RB);
-    if (!scatter) {
-      for (int rr = 0; rr < nr; ++rr) {
-        const int64_t src = rperm ? rperm[r0 + rr] : r0 + rr;
-        for (int64_t ch = threadIdx.x; ch < nch; ch += blockDim.x)
-          *(uint4 *)(buf + rr * cols + ch * V) = *(const uint4 *)(in + src * cols + ch * V);
-      }
-      __syncthreads();
-      for (int rr = 0; rr < nr; ++rr) {
+    // rows r0 .. r0 + nr into LDS: as read (gather) or scattered by column (scatter)
 #pragma unroll
-        for (int u = 0; u < MAXC; ++u) {
-          const int64_t ch = threadIdx.x + (int64_t)u * blockDim.x;
-          if (ch < nch) {
-            union { uint4 q; T v[V]; } o;
+    for (int rr = 0; rr < RB; ++rr) {
+      if (rr >= nr) continue;
 #pragma unroll
-            for (int e = 0; e < V; ++e) o.v[e] = buf[rr * cols + idx[u][e]];
-            *(uint4 *)(out + (r0 + rr) * cols + ch * V) = o.q;
-          }
+      for (int u = 0; u < MAXC; ++u) {
+        const int64_t ch = threadIdx.x + (int64_t)u * blockDim.x;
+        if (ch >= nch) continue;
+        if (!scatter) {
+          *(u32x4 *)(buf + rr * cols + ch * V) = pre[rr][u];
+        } else {
+          union { u32x4 q; T v[V]; } o;
+          o.q = pre[rr][u];
+#pragma unroll
+          for (int e = 0; e < V; ++e) buf[rr * cols + idx[u][e]] = o.v[e];
         }
       }
-    } else {
-      for (int rr = 0; rr < nr; ++rr) {
+    }
+    __syncthreads();
+    if (r0 + stride < rows) load_rows(r0 + stride);
+    for (int rr = 0; rr < nr; ++rr) {
 #pragma unroll
-        for (int u = 0; u < MAXC; ++u) {
-          const int64_t ch = threadIdx.x + (int64_t)u * blockDim.x;
-          if (ch < nch) {
-            union { uint4 q; T v[V]; } o;
-            o.q = *(const uint4 *)(in + (r0 + rr) * cols + ch * V);
+      for (int u = 0; u < MAXC; ++u) {
+        const int64_t ch = threadIdx.x + (int64_t)u * blockDim.x;
+        if (ch >= nch) continue;
+        union { u32x4 q; T v[V]; } o;
+        if (!scatter) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) buf[rr * cols + idx[u][e]] = o.v[e];
-          }
+          for (int e = 0; e < V; ++e) o.v[e] = buf[rr * cols + idx[u][e]];
+        } else {
+          o.q = *(const u32x4 *)(buf + rr * cols + ch * V);
         }
+        *(u32x4 *)(out + (r0 + rr) * cols + ch * V) = o.q;
       }
-      __syncthreads();
-      for (int rr = 0; rr < nr; ++rr)
-        for (int64_t ch = threadIdx.x; ch < nch; ch += blockDim.x)
-          *(uint4 *)(out + (r0 + rr) * cols + ch * V) = *(const uint4 *)(buf + rr * cols + ch * V);
     }
     __syncthreads();
   }
