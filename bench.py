@@ -97,6 +97,27 @@ def layer_roofline_ms(wl, variant, n):
     return t * 1e3
 
 
+def fold_time_ms(wl, inputs, reps=10):
+    """Phase-end fold (poetx_fold) at the workload's weight shape; None for int8."""
+    if wl.w == "i8":
+        return None
+    import torch
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.step import LayerStep
+    st = LayerStep(wl, dict(inputs, x=inputs["x"][:64], dz=inputs["dz"][:64]), "mem")
+    st.cnp()
+    w_out = torch.empty_like(st.w_merged)
+    B.poetx_fold(st.layer, w_out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        B.poetx_fold(st.layer, w_out)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def time_steps(st, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -432,7 +453,8 @@ def main():
         "variants": variants,
         "phases": phases,
         "merge_per_phase": {"ms": merge_ms, "GB_s": merge_gbs,
-                            "with_transpose_ms": merge_t_ms, "with_transpose_GB_s": merge_t_gbs},
+                            "with_transpose_ms": merge_t_ms, "with_transpose_GB_s": merge_t_gbs,
+                            "fold_ms": fold_time_ms(wl, inputs)},
     }
     if not args.no_cpu and wl.w != "i8":
         out["cpu_baseline"] = cpu_baseline(wl, inputs)

@@ -152,6 +152,23 @@ int poetx_backward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void
                    float *dtheta_p, float *dg_r, float *dg_p, void *ws, size_t *ws_bytes,
                    void *stream);
 
+/*
+ * poetx_fold -- the consolidation step of merge-then-reinitialize (the POET training
+ * recipe's periodic merge, on the "Poet Orthogonal LLM Training" skill page under its
+ * memory optimization; with POET-X's merged permutations, Method §2): the layer's
+ * effective weight in original coordinates,
+ *     w_out[perm_out[i]][perm_in[k]] = (Diag(G_P)^T . W' . Diag(G_R)^T)[i][k],
+ * so that x . w_out^T equals poetx_forward's z for every token row x.  A caller starts
+ * the next phase by zeroing theta (then G = I), drawing new permutations and calling
+ * poetx_merge_perm(w_out, ...).
+ * w_out: [d_out][d_in] of L->w_dtype (F32 or BF16; must not alias L->w_merged).
+ * Uses L->w_merged, g_r, g_p, perm_in, perm_out (theta and variant unused).  With BF16
+ * the two block products round their outputs to bf16 (fp32 accumulation).  Workspace:
+ * query with ws == NULL.  Errors: I8 weight -> POETX_ERR_UNSUPPORTED (a folded weight
+ * would need a requantizer the pages do not give); shapes as poetx_forward.
+ */
+int poetx_fold(const poetx_layer *L /*[host]*/, void *w_out, void *ws, size_t *ws_bytes, void *stream);
+
 /* Human-readable name of a poetx_status code (static string). */
 const char *poetx_status_string(int status);
 

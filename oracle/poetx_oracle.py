@@ -273,6 +273,38 @@ def layer_backward(X, dZ, Wm, G_R, G_P, perm_in=None, perm_out=None):
     return dX, dG_R, dG_P, B
 
 
+# ---------------------------------------------------------------------------
+# Phase-end fold: the consolidation step of merge-then-reinitialize (the POET
+# recipe's periodic merge of the learned transforms into the frozen weight, on the
+# "Poet Orthogonal LLM Training" skill page; with POET-X's merged permutations,
+# Method §2).  The next phase then starts from theta = 0 and new permutations.
+# ---------------------------------------------------------------------------
+
+def _block_diag(G):
+    n, b, _ = G.shape
+    D = np.zeros((n * b, n * b), dtype=np.float64)
+    for j in range(n):
+        D[j * b:(j + 1) * b, j * b:(j + 1) * b] = G[j]
+    return D
+
+
+def fold_weights(Wm, G_R, G_P, perm_in=None, perm_out=None):
+    """The layer's effective weight in original coordinates.
+
+    With M = Diag(G_P)^T . W' . Diag(G_R)^T (dense block-diagonal assembly),
+        W[perm_out[i]][perm_in[k]] = M[i][k],
+    so that X . W^T equals layer_forward(X, W', G_R, G_P, perm_in, perm_out).
+    """
+    Wm = np.asarray(Wm, dtype=np.float64)
+    M = _block_diag(np.asarray(G_P, dtype=np.float64)).T @ Wm @ _block_diag(np.asarray(G_R, dtype=np.float64)).T
+    d_out, d_in = M.shape
+    rows = np.arange(d_out) if perm_out is None else np.asarray(perm_out, dtype=np.int64)
+    cols = np.arange(d_in) if perm_in is None else np.asarray(perm_in, dtype=np.int64)
+    W = np.empty_like(M)
+    W[np.ix_(rows, cols)] = M
+    return W
+
+
 def poetx_step(X, dZ, Wm, theta_R, theta_P, b, perm_in=None, perm_out=None):
     """One full step of the layer: CNP forward, forward, backward, CNP backward.
 

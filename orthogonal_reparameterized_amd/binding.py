@@ -51,16 +51,17 @@ _lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp,
                                ctypes.POINTER(_sz), _vp]
 _lib.poetx_backward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, ctypes.POINTER(_sz), _vp]
+_lib.poetx_fold.argtypes = [ctypes.POINTER(PoetxLayerC), _vp, _vp, ctypes.POINTER(_sz), _vp]
 _lib.poetx_status_string.argtypes = [ctypes.c_int]
 _lib.poetx_status_string.restype = ctypes.c_char_p
 _lib.poetx_version.restype = ctypes.c_char_p
 _lib.poetx_prof_enable.argtypes = [_i32]
 _lib.poetx_prof_read.argtypes = [ctypes.c_char_p, _sz]
-for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward",
+for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold",
            "poetx_prof_enable", "poetx_prof_read"):
     getattr(_lib, _f).restype = ctypes.c_int
 
-EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward",
+EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold",
             "poetx_status_string", "poetx_version", "poetx_prof_enable", "poetx_prof_read")
 
 
@@ -256,6 +257,21 @@ def poetx_backward(layer: Layer, x: torch.Tensor, dz: torch.Tensor,
     if want_dg:
         out.update(dg_r=dg_r, dg_p=dg_p)
     return out
+
+
+def poetx_fold(layer: Layer, w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer's effective weight [d_out][d_in] in original coordinates (see poetx.h)."""
+    L = layer.to_c()
+    dev = layer.w_merged.device
+    if w_out is None:
+        w_out = torch.empty((layer.d_out, layer.d_in), dtype=layer.w_merged.dtype, device=dev)
+    nbytes = _sz(0)
+    _check(_lib.poetx_fold(ctypes.byref(L), None, None, ctypes.byref(nbytes), None), "poetx_fold(size)")
+    ws = _workspace(dev, nbytes.value)
+    nb = _sz(ws.numel())
+    _check(_lib.poetx_fold(ctypes.byref(L), _ptr(w_out), _ptr(ws), ctypes.byref(nb), _stream(dev)),
+           "poetx_fold")
+    return w_out
 
 
 def prof_enable(on: bool = True):

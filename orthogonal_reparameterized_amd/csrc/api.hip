@@ -629,3 +629,44 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   sides[1].n = p.np; sides[1].theta = L->theta_p; sides[1].dg = gp; sides[1].dtheta = dtheta_p;
   return cnp_bwd_impl(b, sides, 2, cws, s);
 }
+
+// ================================================================= fold ====
+// Phase-end fold (the consolidation step of merge-then-reinitialize): the layer's
+// effective weight in original coordinates,
+//   w_out[perm_out[i]][perm_in[k]] = (Diag(G_P)^T . W' . Diag(G_R)^T)[i][k],
+// so that x . w_out^T is poetx_forward's z for every token row x.  The block products
+// reuse the block-diagonal kernels with the rows of W' (then of the transpose) as the
+// token dimension; the final gather uses the inverse permutations.
+extern "C" int poetx_fold(const poetx_layer *L, void *w_out, void *ws, size_t *ws_bytes, void *stream) {
+  Plan p;
+  POETX_TRY(validate(L, 0, p));
+  if (!ws_bytes) return POETX_ERR_INVALID_ARG;
+  if (L->w_dtype == POETX_I8) return POETX_ERR_UNSUPPORTED;  // a folded int8 weight needs a requantizer
+  const size_t es = dtype_size(p.w), wb = (size_t)p.dout * p.din * es;
+  Arena ar(ws);
+  void *m1 = ar.take(wb), *t1 = ar.take(wb), *t2 = ar.take(wb);
+  int32_t *inv_out = L->perm_out ? (int32_t *)ar.take((size_t)p.dout * 4) : nullptr;
+  int32_t *inv_in = L->perm_in ? (int32_t *)ar.take((size_t)p.din * 4) : nullptr;
+  if (!ws) {
+    *ws_bytes = ar.used;
+    return POETX_OK;
+  }
+  if (!L->w_merged || !L->g_r || !L->g_p || !w_out) return POETX_ERR_INVALID_ARG;
+  if (w_out == L->w_merged) return POETX_ERR_INVALID_ARG;
+  if (*ws_bytes < ar.used) return POETX_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  Plan pr = p;
+  pr.N = p.dout;  // rows of W' as tokens over d_in features: M1 = W' . Diag(G_R)^T
+  POETX_TRY(block_apply(pr, p.din, L->w_merged, L->g_r, m1, true, nullptr, s));
+  POETX_TRY(transpose(m1, t1, p.dout, p.din, (int)es, s));
+  Plan pp = p;
+  pp.N = p.din;  // M^T = M1^T . Diag(G_P)
+  POETX_TRY(block_apply(pp, p.dout, t1, L->g_p, t2, false, nullptr, s));
+  const bool perms = L->perm_out || L->perm_in;
+  void *m = perms ? m1 : w_out;
+  POETX_TRY(transpose(t2, m, p.din, p.dout, (int)es, s));
+  if (!perms) return POETX_OK;
+  if (inv_out) POETX_TRY(invert_perm(L->perm_out, inv_out, p.dout, s));
+  if (inv_in) POETX_TRY(invert_perm(L->perm_in, inv_in, p.din, s));
+  return permute_cols(m, w_out, p.dout, p.din, (int)es, inv_out, inv_in, false, s);
+}

@@ -245,6 +245,17 @@ int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esiz
   }
 }
 
+// inv[perm[i]] = i (perm must be a permutation of 0 .. n-1; not checked).
+__global__ void k_invert_perm(const int32_t *__restrict__ perm, int32_t *__restrict__ inv, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) inv[perm[i]] = (int32_t)i;
+}
+
+int invert_perm(const int32_t *perm, int32_t *inv, int64_t n, hipStream_t s) {
+  if (n <= 0) return POETX_OK;
+  return launch("invert_perm", s, [&] { k_invert_perm<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(perm, inv, n); });
+}
+
 // out[c][r] = in[r][c] for a [rows][cols] matrix, through 64 x 64 LDS tiles.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ in, T *__restrict__ out, int64_t rows,

@@ -57,6 +57,8 @@ struct SkewSegs {
   bf16_t *planes[2] = {nullptr, nullptr};
   int64_t n[2] = {0, 0};
 };
+// inv[perm[i]] = i for a permutation of 0 .. n-1
+int invert_perm(const int32_t *perm, int32_t *inv, int64_t n, hipStream_t s);
 int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s);
 int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s);
 int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t s);

@@ -120,3 +120,22 @@ def test_validation_codes(B):
     assert B.raw.poetx_merge_perm(None, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG
     assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_I8, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG
     assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, FAKE, None) == B.POETX_ERR_INVALID_ARG
+
+
+FAKE_OUT = 0x20000  # a second never-dereferenced address (distinct from the layer's W')
+
+
+def fold(B, c, w_out=FAKE_OUT, ws=None, ws_bytes=0):
+    nb = ctypes.c_size_t(ws_bytes)
+    st = B.raw.poetx_fold(ctypes.byref(c), w_out, ws, ctypes.byref(nb), None)
+    return st, nb.value
+
+
+def test_fold_validation(B):
+    st, need = fold(B, layer(B))
+    assert st == B.POETX_OK and need >= 3 * 512 * 768 * 2  # three [d_out][d_in] bf16 buffers
+    assert fold(B, layer(B), ws=FAKE, ws_bytes=need - 1)[0] == B.POETX_ERR_WORKSPACE
+    assert fold(B, layer(B), w_out=None, ws=FAKE, ws_bytes=need)[0] == B.POETX_ERR_INVALID_ARG
+    assert fold(B, layer(B), w_out=FAKE, ws=FAKE, ws_bytes=need)[0] == B.POETX_ERR_INVALID_ARG  # aliases W'
+    assert fold(B, layer(B, w=B.POETX_I8, w_scale=FAKE, variant=B.POETX_MEM))[0] == B.POETX_ERR_UNSUPPORTED
+    assert fold(B, layer(B, b=100))[0] == B.POETX_ERR_SHAPE

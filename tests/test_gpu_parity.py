@@ -230,6 +230,80 @@ def test_int8_fast_rejected(B):
     assert e.value.status == B.POETX_ERR_UNSUPPORTED
 
 
+# ------------------------------------------------------------ phase-end fold ----
+
+FOLD_CASES = [
+    # (d_in, d_out, b, dtype, perms): fp32 vector-ALU path, and the bf16 block kernels
+    (256, 256, 32, "f32", True),
+    (512, 768, 256, "bf16", True),
+    (256, 384, 128, "bf16", False),
+    (1024, 512, 512, "bf16", True),
+]
+
+
+def _fold_layer(wl, inp):
+    from orthogonal_reparameterized_amd.step import LayerStep
+    st = LayerStep(wl, inp, "mem")
+    st.cnp()
+    return st
+
+
+@pytest.mark.parametrize("d_in,d_out,b,dt,perms", FOLD_CASES)
+def test_fold(B, d_in, d_out, b, dt, perms):
+    """poetx_fold against the oracle's fold of the same W', G_R, G_P and permutations."""
+    _say(f"fold {d_in}x{d_out} b={b} {dt} perms={perms}")
+    wl = WL.Workload(95, "fold", 16, d_in, d_out, b, dt, dt, dt, 0.02, d_in, perms=perms)
+    inp = WL.make_layer_inputs(wl)
+    st = _fold_layer(wl, inp)
+    w_eff = B.poetx_fold(st.layer)
+    ref = O.fold_weights(to_host_f64(st.w_merged), to_host_f64(st.g_r), to_host_f64(st.g_p),
+                         inp["perm_in"], inp["perm_out"])
+    tol = TOL_CNP_F32 if dt == "f32" else TOL_BF16
+    assert norm_max_err(to_host_f64(w_eff), ref) <= tol
+
+
+def test_fold_phase_identity(B):
+    """The next phase starts from the folded weight, theta = 0 and new permutations, and
+    computes the same layer: its forward matches the old phase's forward."""
+    wl = WL.Workload(96, "fold phase", 130, 512, 768, 256, "bf16", "bf16", "bf16", 0.02, 512)
+    inp = WL.make_layer_inputs(wl)
+    st = _fold_layer(wl, inp)
+    z_old, _ = B.poetx_forward(st.layer, st.x)
+    w_eff = B.poetx_fold(st.layer)
+    rng = np.random.default_rng(7)
+    pin = torch.from_numpy(rng.permutation(wl.d_in).astype(np.int32)).cuda()
+    pout = torch.from_numpy(rng.permutation(wl.d_out).astype(np.int32)).cuda()
+    w_new, _ = B.poetx_merge_perm(w_eff, pout, pin)
+    th_r, th_p = torch.zeros_like(st.theta_r), torch.zeros_like(st.theta_p)
+    g_r = B.poetx_cnp(B.POETX_CNP_FWD, th_r, wl.b)
+    g_p = B.poetx_cnp(B.POETX_CNP_FWD, th_p, wl.b)
+    layer = B.Layer(w_new, th_r, th_p, g_r, g_p, wl.b, act_dtype=torch.bfloat16, variant=B.POETX_MEM,
+                    perm_in=pin, perm_out=pout)
+    z_new, _ = B.poetx_forward(layer, st.x)
+    assert torch.equal(g_r.float().cpu(), torch.eye(wl.b).expand_as(g_r.float().cpu()))
+    assert norm_max_err(to_host_f64(z_new), to_host_f64(z_old)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("key", [3, 4])
+def test_fold_full_size_sampled(B, key):
+    """Workloads 3 and 4 at full size: sampled (P-block, R-block) pairs of the folded
+    weight against the oracle's fold of that block pair."""
+    wl = WL.WORKLOADS[key]
+    _say(f"fold workload {key}")
+    inp = WL.make_layer_inputs(wl, n_tokens=64)
+    st = _fold_layer(wl, inp)
+    w_eff = to_host_f64(B.poetx_fold(st.layer))
+    wm = to_host_f64(st.w_merged)
+    g_r, g_p = to_host_f64(st.g_r), to_host_f64(st.g_p)
+    pin, pout = np.asarray(inp["perm_in"], np.int64), np.asarray(inp["perm_out"], np.int64)
+    b, n_r, n_p = wl.b, wl.d_in // wl.b, wl.d_out // wl.b
+    for jp, jr in [(0, 0), (n_p - 1, n_r - 1), (n_p // 2, 1), (1, n_r // 2)]:
+        rows, cols = slice(jp * b, (jp + 1) * b), slice(jr * b, (jr + 1) * b)
+        ref = O.fold_weights(wm[rows, cols], g_r[jr:jr + 1], g_p[jp:jp + 1])
+        got = w_eff[np.ix_(pout[rows], pin[cols])]
+        assert norm_max_err(got, ref) <= TOL_BF16, (jp, jr)
+
+
 @functools.lru_cache(maxsize=None)
 def _full(key):
     wl = WL.WORKLOADS[key]

@@ -19,6 +19,8 @@ What pins what:
     closed forms.
   * int8: merge is exact; theta = 0 equals X (diag(s) q)^T.
   * spectrum: singular values of the effective weight match W's to O(|Q|^4).
+  * phase-end fold: X W_eff^T equals the dense unmerged layer; with theta = 0 the
+    fold undoes the merge exactly.
   * a mutation test plants plausible mistakes in a copy of the oracle and
     checks that some pin above fails for each.
 """
@@ -201,6 +203,25 @@ def test_layer_forward_pins():
     _check_layer_forward(O.layer_forward, O.merge_perm, O.cnp_forward)
 
 
+def _check_fold(fold, merge_perm, cnp_forward):
+    rng = np.random.default_rng(21)
+    for perms in (True, False):
+        W, th_r, th_p, X, dZ, pin, pout, b = _small_layer(rng, perms=perms)
+        G_R, G_P = cnp_forward(th_r, b), cnp_forward(th_p, b)
+        Wm = merge_perm(W, pout, pin)
+        Weff = fold(Wm, G_R, G_P, pin, pout)
+        # the folded weight reproduces the dense, unmerged layer (eq. 3 with R and P)
+        np.testing.assert_allclose(X @ Weff.T, dense_reference(W, G_R, G_P, X, pin, pout), rtol=0, atol=1e-12)
+        # theta = 0 (G = I): the fold undoes the merge exactly
+        I_r = np.broadcast_to(np.eye(b), G_R.shape)
+        I_p = np.broadcast_to(np.eye(b), G_P.shape)
+        assert np.array_equal(fold(Wm, I_r, I_p, pin, pout), W)
+
+
+def test_fold_pins():
+    _check_fold(O.fold_weights, O.merge_perm, O.cnp_forward)
+
+
 def test_layer_empty_tokens():
     rng = np.random.default_rng(3)
     W, th_r, th_p, X, dZ, pin, pout, b = _small_layer(rng, n=0)
@@ -344,7 +365,17 @@ def _mutants():
             r["dX"] = r["dX"][:, pin]
         return r
 
+    def fold_untransposed(Wm, G_R, G_P, pin=None, pout=None):
+        return O.fold_weights(Wm, np.swapaxes(G_R, 1, 2), G_P, pin, pout)
+
+    def fold_gathers(Wm, G_R, G_P, pin=None, pout=None):
+        # gathers with the permutations where the fold must scatter
+        W = O.fold_weights(Wm, G_R, G_P, None, None)
+        return W if pin is None else W[np.asarray(pout)][:, np.asarray(pin)]
+
     return [
+        ("fold keeps G_R untransposed", lambda: _check_fold(fold_untransposed, O.merge_perm, O.cnp_forward)),
+        ("fold gathers instead of scattering", lambda: _check_fold(fold_gathers, O.merge_perm, O.cnp_forward)),
         ("fwd drops Q^3", lambda: _check_cnp_forward(fwd_drop_q3)),
         ("fwd sign slip", lambda: _check_cnp_forward(fwd_sign)),
         ("fwd missing factor 2", lambda: _check_cnp_forward(fwd_half)),
