@@ -118,6 +118,25 @@ def fold_time_ms(wl, inputs, reps=10):
     return e0.elapsed_time(e1) / reps
 
 
+def adam_time_ms(wl, reps=20):
+    """poetx_adam_step over the layer's packed theta (both sides), float32 state."""
+    import torch
+    from orthogonal_reparameterized_amd import binding as B
+    n = (wl.d_in // wl.b + wl.d_out // wl.b) * (wl.b * (wl.b - 1) // 2)
+    th = torch.zeros(n, device="cuda")
+    g, m, v = torch.randn(n, device="cuda"), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    B.poetx_adam_step(th, g, m, v, lr=1e-3, step=1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(reps):
+        B.poetx_adam_step(th, g, m, v, lr=1e-3, step=t + 2)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"ms": ms, "params": n, "GB_s": 7 * 4 * n / (ms * 1e-3) / 1e9}
+
+
 def time_steps(st, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -455,6 +474,7 @@ def main():
         "merge_per_phase": {"ms": merge_ms, "GB_s": merge_gbs,
                             "with_transpose_ms": merge_t_ms, "with_transpose_GB_s": merge_t_gbs,
                             "fold_ms": fold_time_ms(wl, inputs)},
+        "optimizer_per_step": adam_time_ms(wl),
     }
     if not args.no_cpu and wl.w != "i8":
         out["cpu_baseline"] = cpu_baseline(wl, inputs)

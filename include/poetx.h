@@ -169,6 +169,22 @@ int poetx_backward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void
  */
 int poetx_fold(const poetx_layer *L /*[host]*/, void *w_out, void *ws, size_t *ws_bytes, void *stream);
 
+/*
+ * poetx_adam_step -- one Adam update of packed theta, fused in a single pass.  The
+ * optimizer state lives on the b(b-1)/2 packed parameters per block, half of a dense
+ * b x b (Method §4); gamma scales the learning rate (the pages set it below 1, to 0.5,
+ * for POET-XQ: practical advice 3).  With g = dtheta from poetx_backward:
+ *     m = beta1 m + (1 - beta1) g,   v = beta2 v + (1 - beta2) g^2,
+ *     theta -= gamma lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * theta, m, v: [n_params] float32, updated in place (m, v start at zero); grad:
+ * [n_params] float32, read-only; all 16-byte aligned.  t = step >= 1.  The pages do not
+ * fix the other hyperparameters: the caller passes them.
+ * Errors: step < 1, beta outside [0, 1), eps <= 0, NULL or misaligned pointers ->
+ * POETX_ERR_INVALID_ARG.
+ */
+int poetx_adam_step(int64_t n_params, float *theta, const float *grad, float *m, float *v, float lr,
+                    float beta1, float beta2, float eps, int64_t step, float gamma, void *stream);
+
 /* Human-readable name of a poetx_status code (static string). */
 const char *poetx_status_string(int status);
 

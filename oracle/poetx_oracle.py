@@ -305,6 +305,23 @@ def fold_weights(Wm, G_R, G_P, perm_in=None, perm_out=None):
     return W
 
 
+# ---------------------------------------------------------------------------
+# Optimizer on packed theta: the state lives on the b(b-1)/2 packed parameters per
+# block (Method §4, which halves optimizer state and gradients); gamma scales the
+# learning rate (practical advice 3, 0.5 for POET-XQ).  Adam as published by Kingma
+# and Ba (2015); the pages fix no other hyperparameter.
+# ---------------------------------------------------------------------------
+
+def adam_step(theta, g, m, v, lr, beta1, beta2, eps, t, gamma=1.0):
+    """One Adam step; returns the new (theta, m, v)."""
+    theta, g = np.asarray(theta, dtype=np.float64), np.asarray(g, dtype=np.float64)
+    m = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * g * g
+    m_hat = m / (1.0 - beta1 ** t)
+    v_hat = v / (1.0 - beta2 ** t)
+    return theta - gamma * lr * m_hat / (np.sqrt(v_hat) + eps), m, v
+
+
 def poetx_step(X, dZ, Wm, theta_R, theta_P, b, perm_in=None, perm_out=None):
     """One full step of the layer: CNP forward, forward, backward, CNP backward.
 

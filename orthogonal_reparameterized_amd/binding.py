@@ -52,16 +52,18 @@ _lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp,
 _lib.poetx_backward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, ctypes.POINTER(_sz), _vp]
 _lib.poetx_fold.argtypes = [ctypes.POINTER(PoetxLayerC), _vp, _vp, ctypes.POINTER(_sz), _vp]
+_lib.poetx_adam_step.argtypes = [_i64, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                 ctypes.c_float, _i64, ctypes.c_float, _vp]
 _lib.poetx_status_string.argtypes = [ctypes.c_int]
 _lib.poetx_status_string.restype = ctypes.c_char_p
 _lib.poetx_version.restype = ctypes.c_char_p
 _lib.poetx_prof_enable.argtypes = [_i32]
 _lib.poetx_prof_read.argtypes = [ctypes.c_char_p, _sz]
-for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold",
+for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold", "poetx_adam_step",
            "poetx_prof_enable", "poetx_prof_read"):
     getattr(_lib, _f).restype = ctypes.c_int
 
-EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold",
+EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold", "poetx_adam_step",
             "poetx_status_string", "poetx_version", "poetx_prof_enable", "poetx_prof_read")
 
 
@@ -272,6 +274,16 @@ def poetx_fold(layer: Layer, w_out: Optional[torch.Tensor] = None) -> torch.Tens
     _check(_lib.poetx_fold(ctypes.byref(L), _ptr(w_out), _ptr(ws), ctypes.byref(nb), _stream(dev)),
            "poetx_fold")
     return w_out
+
+
+def poetx_adam_step(theta: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, *, lr: float,
+                    step: int, betas=(0.9, 0.999), eps: float = 1e-8, gamma: float = 1.0):
+    """In-place Adam update of packed theta (and its state m, v) from grad = dtheta."""
+    for t in (theta, grad, m, v):
+        assert t.dtype == torch.float32 and t.is_contiguous() and t.numel() == theta.numel()
+    _check(_lib.poetx_adam_step(theta.numel(), _ptr(theta), _ptr(grad), _ptr(m), _ptr(v), lr, betas[0],
+                                betas[1], eps, step, gamma, _stream(theta.device)), "poetx_adam_step")
+    return theta
 
 
 def prof_enable(on: bool = True):

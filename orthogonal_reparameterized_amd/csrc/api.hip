@@ -1,5 +1,6 @@
 // libpoetx C ABI: argument validation, workspace carving and kernel sequencing
 // for the POET-X layer (declarations and contracts in include/poetx.h).
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -669,4 +670,20 @@ extern "C" int poetx_fold(const poetx_layer *L, void *w_out, void *ws, size_t *w
   if (inv_out) POETX_TRY(invert_perm(L->perm_out, inv_out, p.dout, s));
   if (inv_in) POETX_TRY(invert_perm(L->perm_in, inv_in, p.din, s));
   return permute_cols(m, w_out, p.dout, p.din, (int)es, inv_out, inv_in, false, s);
+}
+
+// ================================================================ optimizer ====
+extern "C" int poetx_adam_step(int64_t n_params, float *theta, const float *grad, float *m, float *v,
+                               float lr, float beta1, float beta2, float eps, int64_t step, float gamma,
+                               void *stream) {
+  if (n_params < 0 || step < 1) return POETX_ERR_INVALID_ARG;
+  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f)) return POETX_ERR_INVALID_ARG;
+  if (n_params == 0) return POETX_OK;
+  if (!theta || !grad || !m || !v) return POETX_ERR_INVALID_ARG;
+  if (((uintptr_t)theta | (uintptr_t)grad | (uintptr_t)m | (uintptr_t)v) % 16) return POETX_ERR_INVALID_ARG;
+  // bias corrections in double on the host
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step), bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  const float step_size = (float)((double)gamma * (double)lr / bc1);
+  const float rs2 = (float)(1.0 / std::sqrt(bc2));
+  return adam_step(n_params, theta, grad, m, v, step_size, beta1, beta2, rs2, eps, (hipStream_t)stream);
 }

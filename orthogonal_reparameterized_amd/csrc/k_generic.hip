@@ -256,6 +256,41 @@ int invert_perm(const int32_t *perm, int32_t *inv, int64_t n, hipStream_t s) {
   return launch("invert_perm", s, [&] { k_invert_perm<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(perm, inv, n); });
 }
 
+// Adam on packed parameters, one fused pass: m, v, theta updated in place from g.
+//   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;  theta -= step_size * m / (sqrt(v) * rs2 + eps)
+// with step_size = gamma lr / (1 - b1^t) and rs2 = 1 / sqrt(1 - b2^t) from the host.
+__global__ void k_adam(int64_t n, float *__restrict__ theta, const float *__restrict__ g, float *__restrict__ m,
+                       float *__restrict__ v, float step_size, float b1, float b2, float rs2, float eps) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    float4 t = ((float4 *)theta)[i], gg = ((const float4 *)g)[i], mm = ((float4 *)m)[i], vv = ((float4 *)v)[i];
+    float *tp = &t.x, *gp = &gg.x, *mp = &mm.x, *vp = &vv.x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mp[c] = b1 * mp[c] + (1.f - b1) * gp[c];
+      vp[c] = b2 * vp[c] + (1.f - b2) * gp[c] * gp[c];
+      tp[c] -= step_size * mp[c] / (sqrtf(vp[c]) * rs2 + eps);
+    }
+    ((float4 *)theta)[i] = t; ((float4 *)m)[i] = mm; ((float4 *)v)[i] = vv;
+  }
+  // tail (n % 4 elements), handled by the first threads of the grid
+  const int64_t e = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < n) {
+    const float gg = g[e];
+    const float mm = b1 * m[e] + (1.f - b1) * gg, vv = b2 * v[e] + (1.f - b2) * gg * gg;
+    m[e] = mm; v[e] = vv;
+    theta[e] -= step_size * mm / (sqrtf(vv) * rs2 + eps);
+  }
+}
+
+int adam_step(int64_t n, float *theta, const float *g, float *m, float *v, float step_size, float b1, float b2,
+              float rs2, float eps, hipStream_t s) {
+  if (n <= 0) return POETX_OK;
+  const int64_t want = cdiv(n / 4 > 0 ? n / 4 : 1, 256);
+  const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
+  return launch("adam_step", s, [&] { k_adam<<<grid, 256, 0, s>>>(n, theta, g, m, v, step_size, b1, b2, rs2, eps); });
+}
+
 // out[c][r] = in[r][c] for a [rows][cols] matrix, through 64 x 64 LDS tiles.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ in, T *__restrict__ out, int64_t rows,

@@ -57,6 +57,9 @@ struct SkewSegs {
   bf16_t *planes[2] = {nullptr, nullptr};
   int64_t n[2] = {0, 0};
 };
+// fused Adam pass on packed parameters (step_size and rs2 carry the bias corrections)
+int adam_step(int64_t n, float *theta, const float *g, float *m, float *v, float step_size, float b1, float b2,
+              float rs2, float eps, hipStream_t s);
 // inv[perm[i]] = i for a permutation of 0 .. n-1
 int invert_perm(const int32_t *perm, int32_t *inv, int64_t n, hipStream_t s);
 int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s);

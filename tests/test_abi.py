@@ -139,3 +139,13 @@ def test_fold_validation(B):
     assert fold(B, layer(B), w_out=FAKE, ws=FAKE, ws_bytes=need)[0] == B.POETX_ERR_INVALID_ARG  # aliases W'
     assert fold(B, layer(B, w=B.POETX_I8, w_scale=FAKE, variant=B.POETX_MEM))[0] == B.POETX_ERR_UNSUPPORTED
     assert fold(B, layer(B, b=100))[0] == B.POETX_ERR_SHAPE
+
+
+def test_adam_validation(B):
+    f = B.raw.poetx_adam_step
+    assert f(0, None, None, None, None, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_OK  # empty: no-op
+    assert f(8, FAKE, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 0, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(8, FAKE, FAKE, FAKE, FAKE, 1e-3, 1.0, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(8, FAKE, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 0.0, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(8, FAKE, None, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(8, FAKE + 4, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG

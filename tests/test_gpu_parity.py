@@ -304,6 +304,29 @@ def test_fold_full_size_sampled(B, key):
         assert norm_max_err(got, ref) <= TOL_BF16, (jp, jr)
 
 
+# ------------------------------------------------------------ optimizer ----
+
+@pytest.mark.parametrize("n", [4, 1023, 32 * 32640])
+def test_adam_step(B, n):
+    """poetx_adam_step over several steps against the oracle's Adam, float32 state."""
+    rng = np.random.default_rng(41)
+    th = (rng.standard_normal(n) * 0.01).astype(np.float32)
+    th_d = torch.from_numpy(th).cuda()
+    m_d, v_d = torch.zeros_like(th_d), torch.zeros_like(th_d)
+    ref_t, ref_m, ref_v = th.astype(np.float64), np.zeros(n), np.zeros(n)
+    # the kernel takes its hyperparameters as float32: the oracle gets the same values
+    lr, b1, b2, eps, gamma = (float(np.float32(x)) for x in (1e-3, 0.9, 0.999, 1e-8, 0.5))
+    for t in range(1, 4):
+        g = rng.standard_normal(n).astype(np.float32)
+        B.poetx_adam_step(th_d, torch.from_numpy(g).cuda(), m_d, v_d, lr=1e-3, step=t, gamma=0.5)
+        ref_t, ref_m, ref_v = O.adam_step(ref_t, g, ref_m, ref_v, lr, b1, b2, eps, t, gamma)
+    torch.cuda.synchronize()
+    # float32 arithmetic: state to a few ulp; theta moves by ~1e-3 per step
+    np.testing.assert_allclose(m_d.cpu().numpy(), ref_m, rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(v_d.cpu().numpy(), ref_v, rtol=1e-5, atol=1e-9)
+    np.testing.assert_allclose(th_d.cpu().numpy(), ref_t, rtol=1e-5, atol=1e-7)
+
+
 @functools.lru_cache(maxsize=None)
 def _full(key):
     wl = WL.WORKLOADS[key]

@@ -21,6 +21,8 @@ What pins what:
   * spectrum: singular values of the effective weight match W's to O(|Q|^4).
   * phase-end fold: X W_eff^T equals the dense unmerged layer; with theta = 0 the
     fold undoes the merge exactly.
+  * optimizer on packed theta: the closed-form first Adam step and three steps of
+    the library optimizer (torch.optim.Adam).
   * a mutation test plants plausible mistakes in a copy of the oracle and
     checks that some pin above fails for each.
 """
@@ -222,6 +224,30 @@ def test_fold_pins():
     _check_fold(O.fold_weights, O.merge_perm, O.cnp_forward)
 
 
+def _check_adam(adam_step):
+    import torch
+    rng = np.random.default_rng(31)
+    th0 = rng.standard_normal(300) * 0.01
+    g = [rng.standard_normal(300) for _ in range(3)]
+    lr, b1, b2, eps, gamma = 1e-3, 0.9, 0.999, 1e-8, 0.5
+    # closed form of the first step from zero state: theta - gamma lr g / (|g| + eps)
+    th1, m1, v1 = adam_step(th0, g[0], np.zeros(300), np.zeros(300), lr, b1, b2, eps, 1, gamma)
+    np.testing.assert_allclose(th1, th0 - gamma * lr * g[0] / (np.abs(g[0]) + eps), rtol=1e-12, atol=1e-15)
+    # three steps against the library optimizer (torch.optim.Adam, float64, lr = gamma lr)
+    p = torch.nn.Parameter(torch.tensor(th0, dtype=torch.float64))
+    opt = torch.optim.Adam([p], lr=gamma * lr, betas=(b1, b2), eps=eps)
+    th, m, v = th0, np.zeros(300), np.zeros(300)
+    for t in range(1, 4):
+        p.grad = torch.tensor(g[t - 1], dtype=torch.float64)
+        opt.step()
+        th, m, v = adam_step(th, g[t - 1], m, v, lr, b1, b2, eps, t, gamma)
+    np.testing.assert_allclose(th, p.detach().numpy(), rtol=0, atol=1e-15)
+
+
+def test_adam_pins():
+    _check_adam(O.adam_step)
+
+
 def test_layer_empty_tokens():
     rng = np.random.default_rng(3)
     W, th_r, th_p, X, dZ, pin, pout, b = _small_layer(rng, n=0)
@@ -373,7 +399,13 @@ def _mutants():
         W = O.fold_weights(Wm, G_R, G_P, None, None)
         return W if pin is None else W[np.asarray(pout)][:, np.asarray(pin)]
 
+    def adam_no_bias_correction(theta, g, m, v, lr, b1, b2, eps, t, gamma=1.0):
+        m = b1 * np.asarray(m) + (1 - b1) * np.asarray(g)
+        v = b2 * np.asarray(v) + (1 - b2) * np.asarray(g) ** 2
+        return np.asarray(theta) - gamma * lr * m / (np.sqrt(v) + eps), m, v
+
     return [
+        ("adam without bias correction", lambda: _check_adam(adam_no_bias_correction)),
         ("fold keeps G_R untransposed", lambda: _check_fold(fold_untransposed, O.merge_perm, O.cnp_forward)),
         ("fold gathers instead of scattering", lambda: _check_fold(fold_gathers, O.merge_perm, O.cnp_forward)),
         ("fwd drops Q^3", lambda: _check_cnp_forward(fwd_drop_q3)),
