@@ -37,7 +37,10 @@
  *    NULL = the default stream) and never synchronizes.
  *  - Workspace: calls taking (ws, ws_bytes) report the bytes they need when
  *    called with ws == NULL (writing *ws_bytes, launching nothing).  With
- *    ws != NULL, *ws_bytes below the requirement is POETX_ERR_WORKSPACE.
+ *    ws != NULL, *ws_bytes below the requirement is POETX_ERR_WORKSPACE.  The
+ *    requirement can depend on the current device (its compute-unit count sets
+ *    how the W' products split their last round of tiles): query on the device
+ *    the call will run on.
  *  - Errors: arguments are validated on the host before any launch; on a
  *    validation error nothing is launched and outputs are untouched.  A failed
  *    launch returns POETX_ERR_HIP; faults during execution surface at the

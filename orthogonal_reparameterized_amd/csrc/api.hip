@@ -448,7 +448,9 @@ int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, float *pa
 }
 
 // B = A . W'^T (scaled per output row of W' for int8 weights)
-int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, hipStream_t s) {
+// `tail` (may be null): workspace of gemm_tail_ws_bytes for the product's shape.
+int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, void *tail, size_t tail_bytes,
+             hipStream_t s) {
   if (p.N == 0) return POETX_OK;
   if (p.mfma) {
     MfmaDesc m;
@@ -459,6 +461,8 @@ int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, hipStr
     m.scaleN = p.w == POETX_I8 ? L->w_scale : nullptr;
     m.name = "gemm_nt";
     m.role = MFMA_GEMM_NT;
+    m.tail_ws = tail;
+    m.tail_ws_bytes = tail ? tail_bytes : 0;
     return gemm_mfma_best(m, s);
   }
   GemmDesc g;
@@ -472,7 +476,8 @@ int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, hipStr
 }
 
 // dA = dB' . W'  (dB' already carries the int8 row scales)
-int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, hipStream_t s) {
+int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, void *tail, size_t tail_bytes,
+             hipStream_t s) {
   if (p.N == 0) return POETX_OK;
   if (p.mfma && L->w_merged_t && p.w == POETX_BF16) {
     // dA = dB . (W'^T)^T: both operands k-contiguous
@@ -483,6 +488,8 @@ int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, hipS
     m.C = dA; m.c_dt = p.act; m.ldc = p.din;
     m.name = "gemm_nn";
     m.role = MFMA_GEMM_NT;
+    m.tail_ws = tail;
+    m.tail_ws_bytes = tail ? tail_bytes : 0;
     return gemm_mfma_best(m, s);
   }
   if (p.mfma) {
@@ -493,6 +500,8 @@ int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, hipS
     m.C = dA; m.c_dt = p.act; m.ldc = p.din;
     m.name = "gemm_nn";
     m.role = MFMA_GEMM_NN;
+    m.tail_ws = tail;
+    m.tail_ws_bytes = tail ? tail_bytes : 0;
     return gemm_mfma_best(m, s);
   }
   GemmDesc g;
@@ -517,16 +526,21 @@ void carve_fwd(Arena &ar, const Plan &p, const poetx_layer *L, bool want_b, FwdB
   if (L->perm_out) f.zt = ar.take(xout);
 }
 
+// workspace for splitting the leftover tiles of the forward W' product
+size_t tail_fwd_bytes(const Plan &p) { return p.mfma ? gemm_tail_ws_bytes(p.N, p.dout, p.din) : 0; }
+// ... and of the backward one (dA = dB . W', same tiles with or without W'^T)
+size_t tail_bwd_bytes(const Plan &p) { return p.mfma ? gemm_tail_ws_bytes(p.N, p.din, p.dout) : 0; }
+
 // Gather(X) -> Xg ; A = Xg . Diag(G_R) ; B = A . W'^T
-int run_front(const Plan &p, const poetx_layer *L, const void *x, const FwdBufs &f, void *bt,
-              hipStream_t s) {
+int run_front(const Plan &p, const poetx_layer *L, const void *x, const FwdBufs &f, void *bt, void *tail,
+              size_t tail_bytes, hipStream_t s) {
   const void *xg = x;
   if (L->perm_in) {
     POETX_TRY(permute_cols(x, f.xg, p.N, p.din, (int)p.ae, nullptr, L->perm_in, false, s));
     xg = f.xg;
   }
   POETX_TRY(block_apply(p, p.din, xg, L->g_r, f.a, false, nullptr, s));
-  return gemm_fwd(p, L, f.a, bt, s);
+  return gemm_fwd(p, L, f.a, bt, tail, tail_bytes, s);
 }
 
 }  // namespace
@@ -540,6 +554,8 @@ extern "C" int poetx_forward(const poetx_layer *L, int64_t n_tokens, const void 
   Arena ar(ws);
   FwdBufs f;
   carve_fwd(ar, p, L, p.mem, f);
+  const size_t tb = tail_fwd_bytes(p);
+  void *tail = tb ? ar.take(tb) : nullptr;
   if (!ws) {
     *ws_bytes = ar.used;
     return POETX_OK;
@@ -550,7 +566,7 @@ extern "C" int poetx_forward(const poetx_layer *L, int64_t n_tokens, const void 
   if (p.N == 0) return POETX_OK;
   hipStream_t s = (hipStream_t)stream;
   void *bt = p.mem ? f.bt : saved_b;
-  POETX_TRY(run_front(p, L, x, f, bt, s));
+  POETX_TRY(run_front(p, L, x, f, bt, tail, tb, s));
   void *zt = L->perm_out ? f.zt : z;
   POETX_TRY(block_apply(p, p.dout, bt, L->g_p, zt, false, nullptr, s));
   if (L->perm_out) POETX_TRY(permute_cols(zt, z, p.N, p.dout, (int)p.ae, nullptr, L->perm_out, true, s));
@@ -579,6 +595,10 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   float *gr = dg_r ? dg_r : (float *)ar.take((size_t)p.nr * bb * 4);
   float *gp = dg_p ? dg_p : (float *)ar.take((size_t)p.np * bb * 4);
   void *cws = ar.take(cnp_ws_bytes(POETX_CNP_BWD, p.nr, b) + cnp_ws_bytes(POETX_CNP_BWD, p.np, b));
+  // one region serves the recomputed forward product (mem) and the dA product in turn
+  const size_t tfb = p.mem ? tail_fwd_bytes(p) : 0, tbb = tail_bwd_bytes(p);  // 0: not split
+  const size_t tb = tfb > tbb ? tfb : tbb;
+  void *tail = tb ? ar.take(tb) : nullptr;
   if (!ws) {
     *ws_bytes = ar.used;
     return POETX_OK;
@@ -594,7 +614,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   const void *xg = x;
   if (p.N > 0) {
     if (p.mem) {
-      POETX_TRY(run_front(p, L, x, f, f.bt, s));
+      POETX_TRY(run_front(p, L, x, f, f.bt, tail, tb, s));
       bt = f.bt;
     } else if (L->perm_in) {
       POETX_TRY(permute_cols(x, f.xg, p.N, p.din, (int)p.ae, nullptr, L->perm_in, false, s));
@@ -613,7 +633,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
     POETX_TRY(block_grad(p, p.dout, bt, dzg, part_p, s));
     POETX_TRY(reduce_parts(part_p, gp, p.np * bb, sp, p.np * bb, s));
     // dA = dB W'
-    POETX_TRY(gemm_bwd(p, L, dbuf, da, s));
+    POETX_TRY(gemm_bwd(p, L, dbuf, da, tail, tb, s));
     // R side: dX~ = dA Diag(G_R)^T; dG_R = sum_t X~^T dA; dX = Scatter_in(dX~)
     void *dxw = L->perm_in ? dxt : dx;
     POETX_TRY(block_apply(p, p.din, da, L->g_r, dxw, true, nullptr, s));

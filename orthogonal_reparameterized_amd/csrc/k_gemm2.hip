@@ -9,6 +9,11 @@
 // read with ds_read_b128, "k-major" tiles [64 k][cols] with ds_read_b64_tr_b16.
 // Buffer resources clip every operand to its valid rows, so rows past M (token
 // tails) and past the k range of a split read as zero without a branch.
+// int8 weights (BI8) travel to LDS as int8 (half the bytes of a bf16 tile) and are
+// widened to bf16 in registers, exactly, right before the MFMAs; their per-row scale is
+// applied in the epilogue.
+#include <atomic>
+
 #include "lds_tiles.h"
 
 namespace poetx {
@@ -22,41 +27,103 @@ struct G2Args {
   const bf16_t *B; int64_t ldb, sBb;
   void *C; int64_t ldc, sCb, sCsplit;
   const float *scaleN; int64_t sSNb;
+  // Tiles at or past full_tiles (in the order of the m-group map) are each shared by
+  // tail_splits blocks, block p taking k in [p*tail_kc, (p+1)*tail_kc); their fp32
+  // partials go to part[tail tile][p][BM*BN] and are summed by k_tail_reduce.
+  // full_tiles = tiles_m * tiles_n when no tile is split.
+  int full_tiles, tail_splits;
+  int64_t tail_kc;
+  float *part;
 };
+
+namespace {
+
+// The tile a block computes and its k range.  Whole tiles keep the XCD-aware order
+// (consecutive ids land on one XCD); split tiles follow them, their parts adjacent.
+struct TileSel {
+  int L, tail, part;
+  int64_t kbeg, kend;
+};
+__device__ inline TileSel select_tile(const G2Args &a, int64_t kz) {
+  TileSel t;
+  int L = blockIdx.x;
+  if (L >= a.full_tiles) {
+    const int u = L - a.full_tiles;
+    t.tail = u / a.tail_splits;
+    t.part = u % a.tail_splits;
+    t.L = a.full_tiles + t.tail;
+    t.kbeg = (int64_t)t.part * a.tail_kc;
+    t.kend = t.kbeg + a.tail_kc < a.K ? t.kbeg + a.tail_kc : a.K;
+  } else {
+    if (a.full_tiles % 8 == 0) L = (L % 8) * (a.full_tiles / 8) + L / 8;
+    t.L = L;
+    t.tail = -1;
+    t.part = 0;
+    t.kbeg = kz * a.Kc;
+    t.kend = t.kbeg + a.Kc < a.K ? t.kbeg + a.Kc : a.K;
+  }
+  return t;
+}
+
+// (m, n) tile of tile-order index L: groups of 4 m-tiles sweep over n, so the
+// blocks running together share their A and B panels.
+__device__ inline void tile_coords(const G2Args &a, int L, int &tm, int &tn) {
+  const int GM = a.tiles_m < 4 ? a.tiles_m : 4;
+  const int grp_size = GM * a.tiles_n;
+  const int grp = L / grp_size, first_m = grp * GM;
+  const int gm = (a.tiles_m - first_m) < GM ? (a.tiles_m - first_m) : GM;
+  const int local = L % grp_size;
+  tm = first_m + local % gm;
+  tn = local / gm;
+}
+
+// A part of a split tile stores its fp32 accumulators thread-major (whole lines per
+// wave store); k_tail_reduce sums the parts after the product kernel has ended.
+template <int FM, int FN, int NTH>
+__device__ inline void tail_store(const f32x4 (&acc)[FM][FN], const G2Args &a, int tail, int part) {
+  f32x4 *dst = (f32x4 *)a.part + ((int64_t)tail * a.tail_splits + part) * (FM * FN * NTH);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) dst[(i * FN + j) * NTH + threadIdx.x] = acc[i][j];
+}
+
+}  // namespace
 
 
 // ROLE separates instantiations per use.  WGM x WGN waves, each computing a
 // (BM/WGM) x (BN/WGN) patch; k advances BKT per step through NST LDS stages with
 // NST-1 steps of prefetch in flight.
-template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32>
+//
+// With an int8 k-contiguous B (BI8) the 64 k of a step are dealt out in a different
+// order, identically on both operands: lane group g (lanes 16g .. 16g+15) of the h-th
+// MFMA covers k = 16g + 8h + 0..7, so one 16-byte LDS read of a B row (k = 16g .. +15)
+// feeds both MFMAs of the step, and the A reads take bf16 chunk 2g + h.
+template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32,
+          bool BI8 = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
+  static_assert(!BI8 || (!AKM && !BKM && BKT == 64), "int8 B: k-contiguous operands, 64-deep steps");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT;
+  constexpr int EB = BI8 ? 1 : 2;  // bytes per B element
+  constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT * EB / 2;  // in bf16 slots
   constexpr int PF = NST - 1;
   extern __shared__ __align__(16) bf16_t smem[];
   // stage s: A tile at smem + s*A_ELEMS, B tile at smem + NST*A_ELEMS + s*B_ELEMS
 
   // ---- tile mapping: batch/split in z; (m, n) from an XCD-aware order of blockIdx.x
   const int64_t z = blockIdx.z, bidx = z / a.splits, kz = z % a.splits;
-  const int T = a.tiles_m * a.tiles_n;
-  int L = blockIdx.x;
-  if (T % 8 == 0) L = (L % 8) * (T / 8) + L / 8;  // consecutive ids land on one XCD
-  const int GM = a.tiles_m < 4 ? a.tiles_m : 4;   // 4 m-tiles share each sweep over n
-  const int grp_size = GM * a.tiles_n;
-  const int grp = L / grp_size, first_m = grp * GM;
-  const int gm = (a.tiles_m - first_m) < GM ? (a.tiles_m - first_m) : GM;
-  const int local = L % grp_size;
-  const int tm = first_m + local % gm, tn = local / gm;
+  const TileSel sel = select_tile(a, kz);
+  int tm, tn;
+  tile_coords(a, sel.L, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  const int64_t kbeg = kz * a.Kc;
-  const int64_t kend = (kbeg + a.Kc < a.K) ? kbeg + a.Kc : a.K;
+  const int64_t kbeg = sel.kbeg, kend = sel.kend;
   const bf16_t *A = a.A + bidx * a.sAb;
-  const bf16_t *B = a.B + bidx * a.sBb;
+  const bf16_t *B = (const bf16_t *)((const char *)a.B + bidx * a.sBb * EB);
   // valid extents: k-contiguous operands end at their last row, k-major at kend
   const __amdgpu_buffer_rsrc_t ra = AKM ? make_rsrc(A, kend * a.lda * 2) : make_rsrc(A, a.M * a.lda * 2);
-  const __amdgpu_buffer_rsrc_t rb = BKM ? make_rsrc(B, kend * a.ldb * 2) : make_rsrc(B, a.N * a.ldb * 2);
+  const __amdgpu_buffer_rsrc_t rb = BKM ? make_rsrc(B, kend * a.ldb * EB) : make_rsrc(B, a.N * a.ldb * EB);
 
   const int wave = threadIdx.x >> 6;
   const int wm = (wave / WGN) * WTM, wn = (wave % WGN) * WTN;
@@ -67,16 +134,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // an int8 row of BKT bytes loads as a bf16 row of BKT/2 (k and ld halve with it)
+  constexpr int BKB = BI8 ? BKT / 2 : BKT;
+  const int64_t ldb_s = BI8 ? a.ldb / 2 : a.ldb;
   using LA = typename std::conditional<AKM, LoaderKM<BM, NW, BKT>, LoaderKC<BM, NW, BKT>>::type;
-  using LB = typename std::conditional<BKM, LoaderKM<BN, NW, BKT>, LoaderKC<BN, NW, BKT>>::type;
+  using LB = typename std::conditional<BKM, LoaderKM<BN, NW, BKT>, LoaderKC<BN, NW, BKB>>::type;
   constexpr int LPS = LA::INSTR + LB::INSTR;  // loads per wave per stage
   LA la;
   LB lb;
   la.init(a.lda, m0);
-  lb.init(a.ldb, n0);
+  lb.init(ldb_s, n0);
   auto issue = [&](int buf, int64_t k0) {
     la.issue(ra, k0, a.lda, smem + buf * A_ELEMS);
-    lb.issue(rb, k0, a.ldb, smem + NST * A_ELEMS + buf * B_ELEMS);
+    lb.issue(rb, BI8 ? k0 / 2 : k0, ldb_s, smem + NST * A_ELEMS + buf * B_ELEMS);
   };
 
   const int nk = (int)((kend - kbeg + BKT - 1) / BKT);
@@ -91,6 +161,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
     if (t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
     const int cur = t % NST;
     const bf16_t *ta = smem + cur * A_ELEMS, *tb = smem + NST * A_ELEMS + cur * B_ELEMS;
+    if constexpr (BI8) {
+      const int l = threadIdx.x & 63, g = l >> 4;
+      bf16x8 fa[2][FM];
+      u32x4v rq[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm + 16 * i + (l & 15);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          fa[h][i] = __builtin_bit_cast(bf16x8, *(const s16x8 *)(ta + row * BKT + ((2 * g + h) ^ kc_key<BKT>(row)) * 8));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn + 16 * j + (l & 15);
+        rq[j] = *(const u32x4v *)((const char *)tb + row * BKT + ((g ^ kc_key<BKB>(row)) << 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const bf16x8 fb = widen_i8x8(rq[j][2 * h], rq[j][2 * h + 1]);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[h][i], acc[i][j], 0, 0, 0);
+        }
+      continue;
+    }
     // All fragments of the step are requested before the first MFMA (a scheduling
     // barrier keeps the compiler from sinking the second half's reads into the MFMA
     // chain), so LDS latency is paid once per step instead of once per fragment pair.
@@ -116,6 +214,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], acc[i][j], 0, 0, 0);
   }
 
+  if constexpr (BM == 256 && BN == 256) {  // only the W' products split tiles
+    if (sel.tail >= 0) {
+      tail_store<FM, FN, 64 * NW>(acc, a, sel.tail, sel.part);
+      return;
+    }
+  }
   const int l = threadIdx.x & 63;
   char *Cb = (char *)a.C + (bidx * a.sCb + kz * a.sCsplit) * (OUTF32 ? 4 : 2);
 #pragma unroll
@@ -153,31 +257,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
 // ends its MFMA phase (two phases of latency cover).
 //   phase A of step t: group 0 reads stage t (and issues stage t+1); group 1 multiplies step t-1
 //   phase B of step t: group 0 multiplies step t;                     group 1 reads stage t
-template <int ROLE, bool AKM, bool BKM, bool OUTF32>
+// An int8 B (BI8, k-major only) stays int8 in LDS, 256-byte rows, and is read with the
+// 8-bit transposing LDS read, one per fragment.
+template <int ROLE, bool AKM, bool BKM, bool OUTF32, bool BI8 = false>
 __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
+  static_assert(!BI8 || (!AKM && BKM), "int8 B: k-major B, k-contiguous A");
   constexpr int BM = 256, BN = 256, BKT = 64, WGN = 4;
   constexpr int WTM = 128, WTN = 64, FM = WTM / 16, FN = WTN / 16;
-  constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT;
+  constexpr int EB = BI8 ? 1 : 2;
+  constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT * EB / 2;
   extern __shared__ __align__(16) bf16_t smem[];
 
   const int64_t z = blockIdx.z, bidx = z / a.splits, kz = z % a.splits;
-  const int T = a.tiles_m * a.tiles_n;
-  int L = blockIdx.x;
-  if (T % 8 == 0) L = (L % 8) * (T / 8) + L / 8;
-  const int GM = a.tiles_m < 4 ? a.tiles_m : 4;
-  const int grp_size = GM * a.tiles_n;
-  const int grp = L / grp_size, first_m = grp * GM;
-  const int gm = (a.tiles_m - first_m) < GM ? (a.tiles_m - first_m) : GM;
-  const int local = L % grp_size;
-  const int tm = first_m + local % gm, tn = local / gm;
+  const TileSel sel = select_tile(a, kz);
+  int tm, tn;
+  tile_coords(a, sel.L, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  const int64_t kbeg = kz * a.Kc;
-  const int64_t kend = (kbeg + a.Kc < a.K) ? kbeg + a.Kc : a.K;
+  const int64_t kbeg = sel.kbeg, kend = sel.kend;
   const bf16_t *A = a.A + bidx * a.sAb;
-  const bf16_t *B = a.B + bidx * a.sBb;
+  const bf16_t *B = (const bf16_t *)((const char *)a.B + bidx * a.sBb * EB);
   const __amdgpu_buffer_rsrc_t ra = AKM ? make_rsrc(A, kend * a.lda * 2) : make_rsrc(A, a.M * a.lda * 2);
-  const __amdgpu_buffer_rsrc_t rb = BKM ? make_rsrc(B, kend * a.ldb * 2) : make_rsrc(B, a.N * a.ldb * 2);
+  const __amdgpu_buffer_rsrc_t rb = BKM ? make_rsrc(B, kend * a.ldb * EB) : make_rsrc(B, a.N * a.ldb * EB);
 
   const int wave = threadIdx.x >> 6, group = wave >> 2;
   const int wm = (wave / WGN) * WTM, wn = (wave % WGN) * WTN;
@@ -188,17 +289,20 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // an int8 row of 256 bytes loads as a bf16 row of 128 (ld and column offsets halve)
+  constexpr int BNS = BI8 ? BN / 2 : BN;
+  const int64_t ldb_s = BI8 ? a.ldb / 2 : a.ldb;
   using LA = typename std::conditional<AKM, LoaderKM<BM, 4, BKT>, LoaderKC<BM, 4, BKT>>::type;
-  using LB = typename std::conditional<BKM, LoaderKM<BN, 4, BKT>, LoaderKC<BN, 4, BKT>>::type;
+  using LB = typename std::conditional<BKM, LoaderKM<BNS, 4, BKT, 0, BI8>, LoaderKC<BN, 4, BKT>>::type;
   LA la;
   LB lb;
   if (group == 0) {
     la.init(a.lda, m0);
-    lb.init(a.ldb, n0);
+    lb.init(ldb_s, BI8 ? n0 / 2 : n0);
   }
   auto issue = [&](int buf, int64_t k0) {
     la.issue(ra, k0, a.lda, smem + buf * A_ELEMS);
-    lb.issue(rb, k0, a.ldb, smem + 2 * A_ELEMS + buf * B_ELEMS);
+    lb.issue(rb, k0, ldb_s, smem + 2 * A_ELEMS + buf * B_ELEMS);
   };
   bf16x8 fa[FM], fb[FN];  // fragments of one 32-deep half step
   auto read_frags = [&](int buf, int h) {
@@ -207,8 +311,10 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
     for (int i = 0; i < FM; ++i)
       fa[i] = AKM ? frag_km<BM>(ta, wm + 16 * i, 32 * h) : frag_kc<BKT>(ta, wm + 16 * i, 32 * h);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[j] = BKM ? frag_km<BN>(tb, wn + 16 * j, 32 * h) : frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (BI8) fb[j] = frag_km8<BN>(tb, wn + 16 * j, 32 * h);
+      else fb[j] = BKM ? frag_km<BN>(tb, wn + 16 * j, 32 * h) : frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
+    }
   };
   auto multiply = [&]() {
 #pragma unroll
@@ -247,6 +353,10 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
   }
   if (group == 1 && nk > 0) multiply();
 
+  if (sel.tail >= 0) {
+    tail_store<FM, FN, 512>(acc, a, sel.tail, sel.part);
+    return;
+  }
   const int l = threadIdx.x & 63;
   char *Cb = (char *)a.C + (bidx * a.sCb + kz * a.sCsplit) * (OUTF32 ? 4 : 2);
 #pragma unroll
@@ -274,6 +384,43 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
 }
 
 
+// Sum of the parts of each split tile, in part order 0, 1, ... (so the result does not
+// depend on which part finished first), times scaleN, to bf16 C.  The 256 x 256 tiles
+// of both W' kernels share one fragment layout: 8 waves as 2 (m) x 4 (n), 128 x 64 per
+// wave, lane l of fragment (i, j) holding C[16i + l%16][16j + 4(l/16) + 0..3].  Eight
+// blocks per tile, each over an eighth of the fragments.
+__global__ __launch_bounds__(256) void k_tail_reduce(G2Args a) {
+  constexpr int FM = 8, FN = 4, NTH = 512, QP = FM * FN * NTH;  // f32x4 per part
+  constexpr int SL = 8, PER = QP / SL / 256;
+  const int tail = blockIdx.x / SL, sl = blockIdx.x % SL;
+  int tm, tn;
+  tile_coords(a, a.full_tiles + tail, tm, tn);
+  const f32x4 *P = (const f32x4 *)a.part + (int64_t)tail * a.tail_splits * QP;
+  f32x4 v[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) v[e] = P[(sl * PER + e) * 256 + threadIdx.x];
+  for (int p = 1; p < a.tail_splits; ++p)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[e] += P[(int64_t)p * QP + (sl * PER + e) * 256 + threadIdx.x];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int q = (sl * PER + e) * 256 + threadIdx.x;
+    const int fr = q / NTH, src = q % NTH, i = fr / FN, j = fr % FN, wave = src >> 6, l = src & 63;
+    const int64_t m = (int64_t)tm * 256 + (wave / 4) * 128 + 16 * i + (l & 15);
+    const int64_t n = (int64_t)tn * 256 + (wave % 4) * 64 + 16 * j + 4 * (l >> 4);
+    if (m >= a.M) continue;
+    f32x4 w = v[e];
+    if (a.scaleN) {
+      const float4 sc = *(const float4 *)(a.scaleN + n);
+      w[0] *= sc.x; w[1] *= sc.y; w[2] *= sc.z; w[3] *= sc.w;
+    }
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(w[0]) | ((uint32_t)f32_to_bf16(w[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16(w[2]) | ((uint32_t)f32_to_bf16(w[3]) << 16);
+    *(uint2 *)((char *)a.C + (m * a.ldc + n) * 2) = pk;
+  }
+}
+
 // explicit instantiations (every configuration the dispatcher below launches)
 #define POETX_G2_INST(R, BMv, BNv, WM, WN, BKv, NS, AK, BKm)                                     \
   template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, true>(G2Args);       \
@@ -283,17 +430,98 @@ POETX_G2_INST(MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true)
 POETX_G2_INST(MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false)
 POETX_G2_INST(MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true)
 #undef POETX_G2_INST
+template __global__ void k_gemm2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, true>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, true>(G2Args);
+template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false, true>(G2Args);
 
-template <int ROLE, bool AKM, bool BKM>
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+namespace {
+
+// Leftover tiles of a W' product (256 x 256 tiles, one block per CU): when the last
+// round would leave at least half the CUs idle, its tiles are split along k so that
+// about one block per CU runs in that round.  Every part keeps at least 4 k steps.
+struct TailPlan {
+  int64_t full, r, s, kc;
+};
+TailPlan tail_plan(int64_t tiles, int64_t K, int cus) {
+  TailPlan t{tiles, 0, 1, K};
+  if (cus <= 0 || K % 64) return t;
+  const int64_t r = tiles % cus, nk = K / 64;
+  if (r == 0 || 2 * r > cus) return t;
+  int64_t sp = cus / r;
+  if (sp > 8) sp = 8;
+  if (sp > nk / 4) sp = nk / 4;
+  if (sp < 2) return t;
+  const int64_t kc = cdiv(nk, sp) * 64;
+  sp = cdiv(K, kc);
+  if (sp < 2) return t;
+  t.full = tiles - r; t.r = r; t.s = sp; t.kc = kc;
+  return t;
+}
+
+// Fill in the split of the leftover tiles: none without a large enough workspace, for
+// other tile shapes, batches, k splits or fp32 results.
+void plan_tail(G2Args &a, const MfmaDesc &d, int bm, int bn) {
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  a.full_tiles = (int)tiles; a.tail_splits = 1; a.tail_kc = a.K; a.part = nullptr;
+  if (!d.tail_ws || d.batch != 1 || d.splits != 1 || bm != 256 || bn != 256 || d.c_dt != POETX_BF16) return;
+  const TailPlan t = tail_plan(tiles, d.K, device_cus());
+  if (t.r == 0 || (size_t)t.r * t.s * bm * bn * 4 > d.tail_ws_bytes) return;
+  a.full_tiles = (int)t.full; a.tail_splits = (int)t.s; a.tail_kc = t.kc;
+  a.part = (float *)d.tail_ws;
+}
+
+int tail_reduce(const G2Args &a, const MfmaDesc &d, hipStream_t s) {
+  const int r = a.tiles_m * a.tiles_n - a.full_tiles;
+  if (r == 0) return POETX_OK;
+  return launch("gemm_tail_reduce", s, [&] { k_tail_reduce<<<r * 8, 256, 0, s>>>(a); });
+}
+
+}  // namespace
+
+size_t gemm_tail_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N % 256 || K % 64) return 0;
+  const TailPlan t = tail_plan(cdiv(M, 256) * (N / 256), K, device_cus());
+  return (size_t)t.r * t.s * 256 * 256 * 4;
+}
+
+template <int ROLE, bool AKM, bool BKM, bool BI8 = false>
 static int run_pp(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
-  const size_t lds = (size_t)2 * 512 * 64 * 2;
+  const size_t lds = (size_t)2 * 64 * (256 * 2 + 256 * (BI8 ? 1 : 2));
   if (d.M <= 0 || d.N % 256 || d.K % 64) return POETX_ERR_UNSUPPORTED;
   G2Args a = k;
   a.tiles_m = (int)cdiv(d.M, 256);
   a.tiles_n = (int)(d.N / 256);
-  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)(d.batch * d.splits));
+  plan_tail(a, d, 256, 256);
+  dim3 grid((unsigned)(a.full_tiles + (a.tiles_m * a.tiles_n - a.full_tiles) * a.tail_splits), 1,
+            (unsigned)(d.batch * d.splits));
+  if constexpr (BI8) {  // int8 W' products write bf16 gradients only
+    if (d.c_dt != POETX_BF16) return POETX_ERR_UNSUPPORTED;
+    static bool attr = false;
+    if (!attr) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, false, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return POETX_ERR_HIP;
+      attr = true;
+    }
+    POETX_TRY(launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, false, true><<<grid, 512, lds, s>>>(a); }));
+    return tail_reduce(a, d, s);
+  }
   if (d.c_dt == POETX_F32) {
     static bool attr = false;
     if (!attr) {
@@ -311,13 +539,15 @@ static int run_pp(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
       return POETX_ERR_HIP;
     attr = true;
   }
-  return launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, false><<<grid, 512, lds, s>>>(a); });
+  POETX_TRY(launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, false><<<grid, 512, lds, s>>>(a); }));
+  return tail_reduce(a, d, s);
 }
 
-template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32>
+template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32,
+          bool BI8 = false>
 static int run2o(const G2Args &a, const char *name, dim3 grid, size_t lds, hipStream_t s) {
   constexpr int NT = 64 * WGM * WGN;
-  auto kern = &k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32>;
+  auto kern = &k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8>;
   static bool attr = false;  // raise the dynamic-LDS limit once per instantiation
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -325,23 +555,37 @@ static int run2o(const G2Args &a, const char *name, dim3 grid, size_t lds, hipSt
       return POETX_ERR_HIP;
     attr = true;
   }
-  return launch(name, s, [&] { k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32><<<grid, NT, lds, s>>>(a); });
+  return launch(name, s, [&] { k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8><<<grid, NT, lds, s>>>(a); });
 }
 
-template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM>
+template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool BI8 = false>
 static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
-  const size_t lds = (size_t)NST * (BM + BN) * BKT * 2;
+  const size_t lds = (size_t)NST * (BM * 2 + BN * (BI8 ? 1 : 2)) * BKT;
   if (d.M <= 0 || d.N % BN || d.K % BKT && (!AKM || !BKM)) return POETX_ERR_UNSUPPORTED;
   G2Args a = k;
   a.tiles_m = (int)cdiv(d.M, BM);
   a.tiles_n = (int)(d.N / BN);
-  dim3 grid((unsigned)(a.tiles_m * a.tiles_n), 1, (unsigned)(d.batch * d.splits));
+  plan_tail(a, d, BM, BN);
+  dim3 grid((unsigned)(a.full_tiles + (a.tiles_m * a.tiles_n - a.full_tiles) * a.tail_splits), 1,
+            (unsigned)(d.batch * d.splits));
+  if constexpr (BI8) {  // int8 W' products write bf16 activations only
+    if (d.c_dt != POETX_BF16) return POETX_ERR_UNSUPPORTED;
+    POETX_TRY((run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false, true>(a, d.name, grid, lds, s)));
+    return tail_reduce(a, d, s);
+  }
   if (d.c_dt == POETX_F32) return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, true>(a, d.name, grid, lds, s);
-  return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false>(a, d.name, grid, lds, s);
+  POETX_TRY((run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false>(a, d.name, grid, lds, s)));
+  return tail_reduce(a, d, s);
 }
 
 bool mfma2_supported(const MfmaDesc &d) {
-  if (d.b_dt != POETX_BF16) return false;  // int8 weights keep the register-staged kernel
+  if (d.b_dt == POETX_I8) {
+    // int8 W' in the two W' products only (16-byte aligned rows), bf16 results
+    if (d.role != MFMA_GEMM_NT && d.role != MFMA_GEMM_NN) return false;
+    if (d.c_dt != POETX_BF16 || d.ldb % 16 || d.batch != 1 || d.splits != 1) return false;
+  } else if (d.b_dt != POETX_BF16) {
+    return false;
+  }
   if (d.c_dt != POETX_BF16 && d.c_dt != POETX_F32) return false;
   if (d.splits < 1 || d.batch * d.splits > 65535) return false;
   if (d.splits > 1 && (d.kchunk <= 0 || d.kchunk % 64 || cdiv(d.K, d.kchunk) != d.splits)) return false;
@@ -367,14 +611,17 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s) {
   k.C = d.C; k.ldc = d.ldc; k.sCb = d.sCb; k.sCsplit = d.sCsplit;
   k.scaleN = d.scaleN; k.sSNb = d.sSNb;
   k.tiles_m = k.tiles_n = 0;
+  const bool i8 = d.b_dt == POETX_I8;
   switch (d.role) {
     case MFMA_GEMM_NT:
       if (d.a_km || d.b_km) return POETX_ERR_UNSUPPORTED;
+      if (i8) return run2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, true>(k, d, s);
       return run2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false>(k, d, s);
     case MFMA_GEMM_NN:
       if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
       // the k-major W' operand goes through the transposing LDS reads; the ping-pong
       // schedule hides their extra latency best (measured against the plain schedule)
+      if (i8) return run_pp<MFMA_GEMM_NN, false, true, true>(k, d, s);
       return run_pp<MFMA_GEMM_NN, false, true>(k, d, s);
     case MFMA_BLOCK_APPLY:
       if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;

@@ -98,10 +98,16 @@ struct MfmaDesc {
   const float *scaleN = nullptr;
   int64_t sSNb = 0;  // batch stride of scaleN
   const char *name = "mfma_gemm";  // label for the measurement hooks
+  // Workspace of gemm_tail_ws_bytes(M, N, K) bytes for the W' products (batch 1, no
+  // split): lets the last round's leftover tiles be split along k.  Optional.
+  void *tail_ws = nullptr;
+  size_t tail_ws_bytes = 0;
 };
 bool mfma_supported(const MfmaDesc &d);
 int gemm_mfma(const MfmaDesc &d, hipStream_t s);    // register-staged kernel (any operand dtype)
 bool mfma2_supported(const MfmaDesc &d);
+size_t gemm_tail_ws_bytes(int64_t M, int64_t N, int64_t K);  // 0: no tile would be split
+int device_cus();  // compute units of the current device, 0 if unknown
 int gemm_mfma2(const MfmaDesc &d, hipStream_t s);   // direct-to-LDS kernel (bf16 operands)
 // Streaming block-diagonal product (b in {128, 256, 512}):
 //   Y[:, jb:(j+1)b] = X[:, jb:(j+1)b] . G[j]  (transposed: . G[j]^T), times scaleN[col]

@@ -13,7 +13,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
 namespace {
@@ -74,8 +77,14 @@ __device__ inline int km_key(int r) { return (r & 3) | ((r >> 1) & 4); }
 // only the bits that stay inside the row)
 template <int C>
 __device__ inline int km_xor(int r) { return (km_key(r) << 1) & (C / 8 - 1); }
+// int8 k-major tiles are read 8 consecutive rows at a time (ds_read_b64_tr_b8), one
+// 16-byte chunk per row: rotating the chunk by the row's low three bits puts those 8
+// chunks on 8 different 16-byte bank groups.
+template <int C, bool I8>
+__device__ inline int km_xor_sel(int r) { return I8 ? (r & 7) : km_xor<C>(r); }
 
-template <int C, int NW, int BKT, int WOFF = 0>
+// I8: the tile holds int8 rows of 2C bytes, loaded as if they were C bf16 values.
+template <int C, int NW, int BKT, int WOFF = 0, bool I8 = false>
 struct LoaderKM {
   static constexpr int CH = C / 8;     // 16-byte chunks per row
   static constexpr int RPI = 64 / CH;  // rows per wave instruction
@@ -86,7 +95,7 @@ struct LoaderKM {
 #pragma unroll
     for (int i = 0; i < INSTR; ++i) {
       const int row = (w * INSTR + i) * RPI + l / CH;
-      const int lchunk = (l % CH) ^ km_xor<C>(row);
+      const int lchunk = (l % CH) ^ km_xor_sel<C, I8>(row);
       voff[i] = (int)((row * ld + col0 + lchunk * 8) * 2);
     }
   }
@@ -123,6 +132,35 @@ __device__ inline bf16x8 frag_km(const bf16_t *t, int c0, int ks) {
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(t + r1 * C + p1));
   s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight signed bytes (|q| <= 127) widened to bf16; every such integer is exact in bf16,
+// so the float's upper half is the bf16 value.
+__device__ inline bf16x8 widen_i8x8(uint32_t lo, uint32_t hi) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t src = e < 2 ? lo : hi;
+    const int sh = (e & 1) * 16;
+    const float x0 = (float)(int)(int8_t)(src >> sh), x1 = (float)(int)(int8_t)(src >> (sh + 8));
+    w[e] = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+  }
+  const u32x4v v = {w[0], w[1], w[2], w[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// MFMA operand fragment from a k-major int8 tile of CB-byte rows (chunks rotated by
+// km_xor_sel<., true>), through ds_read_b64_tr_b8: within each 16-lane group, lane i
+// receives byte i%8 of the 8-byte pieces that lanes 2e + i/8 addressed (e = 0..7); lane
+// j addressing row kb + j/2, columns c0 + 8(j%2) .. +7 therefore gives lane i the eight
+// k values kb .. kb+7 of column c0 + i.  c0 is a multiple of 16.
+template <int CB>
+__device__ inline bf16x8 frag_km8(const bf16_t *t, int c0, int ks) {
+  const int l = threadIdx.x & 63, g = l >> 4, j = l & 15;
+  const int r = ks + 8 * g + (j >> 1);
+  const int p = (((c0 >> 4) ^ (r & 7)) << 4) + 8 * (j & 1);
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)((const char *)t + r * CB + p));
+  return widen_i8x8((uint32_t)v[0], (uint32_t)v[1]);
 }
 
 template <int LX, int K>
