@@ -24,6 +24,10 @@ Conventions (readings of the page where it is silent or ambiguous):
     Z[t][perm_out[i]] = Z~[t][i]; a missing (None) permutation is the identity.
   * packed skew storage: theta[k] is Q[i][j] (i < j) with k running row-major
     over the strict upper triangle, Q[j][i] = -theta[k].
+  * a side of width d with block size b has ceil(d/b) diagonal blocks: floor(d/b)
+    of size b, then one of size d - b*floor(d/b) when that is not zero (Method
+    §3).  Block sets are sequences of square arrays (an array [n][b][b] when all
+    sizes agree); a flat theta holds the blocks' packed vectors one after another.
 
 Parity status: every function here is pinned by tests/test_oracle.py against
 closed forms, library routines, an independent dense assembly and finite
@@ -46,6 +50,10 @@ __all__ = [
     "merge_perm",
     "merge_perm_int8",
     "dequantize_rows",
+    "block_sizes",
+    "split_packed",
+    "cnp_forward_blocks",
+    "cnp_backward_blocks",
     "layer_forward",
     "layer_backward",
     "poetx_step",
@@ -149,6 +157,41 @@ def cnp_backward(theta: np.ndarray, dG: np.ndarray, b: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Blocks of unequal size: the ceil(d/b) blocks of Method §3, the last one holding
+# the d - b*floor(d/b) remaining coordinates.
+# ---------------------------------------------------------------------------
+
+def block_sizes(d: int, b: int):
+    """Sizes of the diagonal blocks of a side of width d with block size b."""
+    full, last = divmod(int(d), int(b))
+    return [int(b)] * full + ([last] if last else [])
+
+
+def split_packed(theta, sizes):
+    """The per-block packed vectors of a flat theta (blocks one after another)."""
+    theta = np.asarray(theta, dtype=np.float64)
+    out, o = [], 0
+    for s in sizes:
+        p = packed_size(s)
+        out.append(theta[o:o + p])
+        o += p
+    assert o == theta.shape[0], "flat theta length does not match the block sizes"
+    return out
+
+
+def cnp_forward_blocks(theta, sizes):
+    """G of every block (eq. 9 per block, each at its own size), from a flat theta."""
+    return [cnp_forward(t[None], s)[0] for t, s in zip(split_packed(theta, sizes), sizes)]
+
+
+def cnp_backward_blocks(theta, dG, sizes):
+    """Flat dL/dtheta from the blocks' dL/dG (the adjoint of eq. 9 per block)."""
+    parts = [cnp_backward(t[None], np.asarray(g, dtype=np.float64)[None], s)[0]
+             for t, g, s in zip(split_packed(theta, sizes), dG, sizes)]
+    return np.concatenate(parts) if parts else np.zeros(0)
+
+
+# ---------------------------------------------------------------------------
 # Permutation merge (Method §2: W is fixed during the inner phase, so the two
 # weight-side permutations are folded into it once: W' = Psi_out W Psi_in^T).
 # ---------------------------------------------------------------------------
@@ -194,31 +237,50 @@ def _scatter_cols(M, perm):
     return out
 
 
+def _blocks(G):
+    """A block set as a list of float64 square arrays."""
+    return [np.asarray(g, dtype=np.float64) for g in G]
+
+
+def _stack_if_uniform(blocks):
+    """An array [n][b][b] when all blocks share one size, else the list itself."""
+    if len({g.shape[0] for g in blocks}) <= 1 and blocks:
+        return np.stack(blocks)
+    return blocks
+
+
 def _block_right(M, G):
-    """Row-wise block-diagonal product: out[:, jb:(j+1)b] = M[:, jb:(j+1)b] @ G[j]."""
-    n, b, _ = G.shape
-    out = np.empty((M.shape[0], n * b), dtype=np.float64)
-    for j in range(n):
-        out[:, j * b:(j + 1) * b] = M[:, j * b:(j + 1) * b] @ G[j]
+    """Row-wise block-diagonal product: the columns of block j (offset o, size s) are
+    out[:, o:o+s] = M[:, o:o+s] @ G[j]."""
+    G = _blocks(G)
+    out = np.empty((M.shape[0], sum(g.shape[0] for g in G)), dtype=np.float64)
+    o = 0
+    for g in G:
+        s = g.shape[0]
+        out[:, o:o + s] = M[:, o:o + s] @ g
+        o += s
     return out
 
 
 def _block_right_t(M, G):
-    """out[:, jb:(j+1)b] = M[:, jb:(j+1)b] @ G[j]^T (adjoint of _block_right in M)."""
-    n, b, _ = G.shape
-    out = np.empty((M.shape[0], n * b), dtype=np.float64)
-    for j in range(n):
-        out[:, j * b:(j + 1) * b] = M[:, j * b:(j + 1) * b] @ G[j].T
+    """out[:, o:o+s] = M[:, o:o+s] @ G[j]^T (adjoint of _block_right in M)."""
+    G = _blocks(G)
+    out = np.empty((M.shape[0], sum(g.shape[0] for g in G)), dtype=np.float64)
+    o = 0
+    for g in G:
+        s = g.shape[0]
+        out[:, o:o + s] = M[:, o:o + s] @ g.T
+        o += s
     return out
 
 
-def _block_grad(L, R, b):
-    """dG[j] = L[:, jb:(j+1)b]^T @ R[:, jb:(j+1)b] (sum over tokens)."""
-    n = L.shape[1] // b
-    out = np.empty((n, b, b), dtype=np.float64)
-    for j in range(n):
-        out[j] = L[:, j * b:(j + 1) * b].T @ R[:, j * b:(j + 1) * b]
-    return out
+def _block_grad(L, R, sizes):
+    """dG[j] = L[:, o:o+s]^T @ R[:, o:o+s] over the blocks' column ranges (sum over tokens)."""
+    out, o = [], 0
+    for s in sizes:
+        out.append(L[:, o:o + s].T @ R[:, o:o + s])
+        o += s
+    return _stack_if_uniform(out)
 
 
 def layer_forward(X, Wm, G_R, G_P, perm_in=None, perm_out=None, keep=False):
@@ -235,9 +297,9 @@ def layer_forward(X, Wm, G_R, G_P, perm_in=None, perm_out=None, keep=False):
     X = np.asarray(X, dtype=np.float64)
     Wm = np.asarray(Wm, dtype=np.float64)
     Xt = _gather_cols(X, perm_in)
-    A = _block_right(Xt, np.asarray(G_R, dtype=np.float64))
+    A = _block_right(Xt, G_R)
     B = A @ Wm.T
-    Zt = _block_right(B, np.asarray(G_P, dtype=np.float64))
+    Zt = _block_right(B, G_P)
     Z = _scatter_cols(Zt, perm_out)
     if keep:
         return Z, dict(Xt=Xt, A=A, B=B, Zt=Zt)
@@ -257,18 +319,16 @@ def layer_backward(X, dZ, Wm, G_R, G_P, perm_in=None, perm_out=None):
     X = np.asarray(X, dtype=np.float64)
     dZ = np.asarray(dZ, dtype=np.float64)
     Wm = np.asarray(Wm, dtype=np.float64)
-    G_R = np.asarray(G_R, dtype=np.float64)
-    G_P = np.asarray(G_P, dtype=np.float64)
-    b = G_R.shape[-1]
+    G_R, G_P = _blocks(G_R), _blocks(G_P)
     Xt = _gather_cols(X, perm_in)
     A = _block_right(Xt, G_R)
     B = A @ Wm.T
     dZt = _gather_cols(dZ, perm_out)
     dB = _block_right_t(dZt, G_P)
-    dG_P = _block_grad(B, dZt, b)
+    dG_P = _block_grad(B, dZt, [g.shape[0] for g in G_P])
     dA = dB @ Wm
     dXt = _block_right_t(dA, G_R)
-    dG_R = _block_grad(Xt, dA, b)
+    dG_R = _block_grad(Xt, dA, [g.shape[0] for g in G_R])
     dX = _scatter_cols(dXt, perm_in)
     return dX, dG_R, dG_P, B
 
@@ -281,10 +341,14 @@ def layer_backward(X, dZ, Wm, G_R, G_P, perm_in=None, perm_out=None):
 # ---------------------------------------------------------------------------
 
 def _block_diag(G):
-    n, b, _ = G.shape
-    D = np.zeros((n * b, n * b), dtype=np.float64)
-    for j in range(n):
-        D[j * b:(j + 1) * b, j * b:(j + 1) * b] = G[j]
+    G = _blocks(G)
+    d = sum(g.shape[0] for g in G)
+    D = np.zeros((d, d), dtype=np.float64)
+    o = 0
+    for g in G:
+        s = g.shape[0]
+        D[o:o + s, o:o + s] = g
+        o += s
     return D
 
 
@@ -296,7 +360,7 @@ def fold_weights(Wm, G_R, G_P, perm_in=None, perm_out=None):
     so that X . W^T equals layer_forward(X, W', G_R, G_P, perm_in, perm_out).
     """
     Wm = np.asarray(Wm, dtype=np.float64)
-    M = _block_diag(np.asarray(G_P, dtype=np.float64)).T @ Wm @ _block_diag(np.asarray(G_R, dtype=np.float64)).T
+    M = _block_diag(G_P).T @ Wm @ _block_diag(G_R).T
     d_out, d_in = M.shape
     rows = np.arange(d_out) if perm_out is None else np.asarray(perm_out, dtype=np.int64)
     cols = np.arange(d_in) if perm_in is None else np.asarray(perm_in, dtype=np.int64)
@@ -325,14 +389,28 @@ def adam_step(theta, g, m, v, lr, beta1, beta2, eps, t, gamma=1.0):
 def poetx_step(X, dZ, Wm, theta_R, theta_P, b, perm_in=None, perm_out=None):
     """One full step of the layer: CNP forward, forward, backward, CNP backward.
 
+    theta_* are [n][p] when b divides the side's width; a flat theta (one
+    dimension) holds the ceil(d/b) blocks of block_sizes(d, b), the last one
+    possibly smaller, and its gradient comes back flat too.
     Returns a dict with G_R, G_P, Z, dX, dG_R, dG_P, dtheta_R, dtheta_P, B.
     """
-    G_R = cnp_forward(theta_R, b)
-    G_P = cnp_forward(theta_P, b)
+    d_out, d_in = np.shape(Wm)
+
+    def fwd(theta, d):
+        if np.ndim(theta) == 1:
+            return cnp_forward_blocks(theta, block_sizes(d, b))
+        return cnp_forward(theta, b)
+
+    def bwd(theta, dG, d):
+        if np.ndim(theta) == 1:
+            return cnp_backward_blocks(theta, dG, block_sizes(d, b))
+        return cnp_backward(theta, dG, b)
+
+    G_R, G_P = fwd(theta_R, d_in), fwd(theta_P, d_out)
     Z = layer_forward(X, Wm, G_R, G_P, perm_in, perm_out)
     dX, dG_R, dG_P, B = layer_backward(X, dZ, Wm, G_R, G_P, perm_in, perm_out)
     return dict(
         G_R=G_R, G_P=G_P, Z=Z, dX=dX, dG_R=dG_R, dG_P=dG_P, B=B,
-        dtheta_R=cnp_backward(theta_R, dG_R, b),
-        dtheta_P=cnp_backward(theta_P, dG_P, b),
+        dtheta_R=bwd(theta_R, dG_R, d_in),
+        dtheta_P=bwd(theta_P, dG_P, d_out),
     )

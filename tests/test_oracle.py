@@ -23,6 +23,10 @@ What pins what:
     fold undoes the merge exactly.
   * optimizer on packed theta: the closed-form first Adam step and three steps of
     the library optimizer (torch.optim.Adam).
+  * blocks of unequal size (ceil(d/b) blocks, the last one smaller): the dense
+    unmerged layer built with the library's block_diag from blocks that the test
+    slices out of the flat theta itself; central differences on theta and X;
+    divisible widths reduce exactly to the [n][p] layout.
   * a mutation test plants plausible mistakes in a copy of the oracle and
     checks that some pin above fails for each.
 """
@@ -218,6 +222,12 @@ def _check_fold(fold, merge_perm, cnp_forward):
         I_r = np.broadcast_to(np.eye(b), G_R.shape)
         I_p = np.broadcast_to(np.eye(b), G_P.shape)
         assert np.array_equal(fold(Wm, I_r, I_p, pin, pout), W)
+    # blocks of unequal size (ceil(d/b) blocks, the last one smaller)
+    for d_in, d_out, b in RAGGED:
+        W, th_r, th_p, X, dZ, pin, pout = _ragged_layer(rng, d_in, d_out, b)
+        G_R, G_P = _blocks_from_flat(th_r, d_in, b), _blocks_from_flat(th_p, d_out, b)
+        Weff = fold(merge_perm(W, pout, pin), G_R, G_P, pin, pout)
+        np.testing.assert_allclose(X @ Weff.T, dense_reference(W, G_R, G_P, X, pin, pout), rtol=0, atol=1e-12)
 
 
 def test_fold_pins():
@@ -294,6 +304,72 @@ def _check_layer_backward(poetx_step, merge_perm):
 
 def test_layer_backward_pins():
     _check_layer_backward(O.poetx_step, O.merge_perm)
+
+
+# ------------------------------------------------------------ ragged blocks ----
+
+def _blocks_from_flat(theta, d, b):
+    """Test-side reading of the flat layout: floor(d/b) packed vectors of size
+    b(b-1)/2, then the last block's, each turned into G by cnp_forward."""
+    full, last = divmod(d, b)
+    p = b * (b - 1) // 2
+    Gs = list(O.cnp_forward(theta[:full * p].reshape(full, p), b)) if full else []
+    if last:
+        Gs.append(O.cnp_forward(theta[full * p:][None], last)[0])
+    return Gs
+
+
+RAGGED = [(10, 7, 4), (9, 12, 4), (5, 6, 8)]  # last blocks 2 | 3, 1 | none, whole side < b
+
+
+def _ragged_layer(rng, d_in, d_out, b, n=3, std=0.15):
+    W = rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)
+    pr = sum(s * (s - 1) // 2 for s in O.block_sizes(d_in, b))
+    pp = sum(s * (s - 1) // 2 for s in O.block_sizes(d_out, b))
+    th_r = rng.standard_normal(pr) * std
+    th_p = rng.standard_normal(pp) * std
+    X = rng.standard_normal((n, d_in))
+    dZ = rng.standard_normal((n, d_out))
+    return W, th_r, th_p, X, dZ, rng.permutation(d_in), rng.permutation(d_out)
+
+
+def _check_ragged(poetx_step):
+    assert O.block_sizes(10, 4) == [4, 4, 2] and O.block_sizes(7, 4) == [4, 3]
+    assert O.block_sizes(8, 4) == [4, 4] and O.block_sizes(9, 4) == [4, 4, 1] and O.block_sizes(3, 4) == [3]
+    rng = np.random.default_rng(41)
+    for d_in, d_out, b in RAGGED:
+        W, th_r, th_p, X, dZ, pin, pout = _ragged_layer(rng, d_in, d_out, b)
+        Wm = O.merge_perm(W, pout, pin)
+        r = poetx_step(X, dZ, Wm, th_r, th_p, b, pin, pout)
+        G_R, G_P = _blocks_from_flat(th_r, d_in, b), _blocks_from_flat(th_p, d_out, b)
+        np.testing.assert_allclose(r["Z"], dense_reference(W, G_R, G_P, X, pin, pout), rtol=0, atol=1e-13)
+
+        def loss(tr, tp, x):
+            Z = dense_reference(W, _blocks_from_flat(tr, d_in, b), _blocks_from_flat(tp, d_out, b), x, pin, pout)
+            return np.sum(Z * dZ)
+
+        h = 1e-6
+        for slot, key in ((0, "dtheta_R"), (1, "dtheta_P"), (2, "dX")):
+            base = [th_r, th_p, X]
+            fd = np.zeros_like(base[slot])
+            for idx in np.ndindex(fd.shape):
+                ap, am = [a.copy() for a in base], [a.copy() for a in base]
+                ap[slot][idx] += h
+                am[slot][idx] -= h
+                fd[idx] = (loss(*ap) - loss(*am)) / (2 * h)
+            np.testing.assert_allclose(r[key], fd, rtol=0, atol=2e-8, err_msg=f"{key} at {(d_in, d_out, b)}")
+    # divisible widths: the flat layout is the [n][p] layout, block after block
+    W, th_r, th_p, X, dZ, pin, pout = _ragged_layer(rng, 8, 12, 4)
+    Wm = O.merge_perm(W, pout, pin)
+    rf = poetx_step(X, dZ, Wm, th_r, th_p, 4, pin, pout)
+    ru = O.poetx_step(X, dZ, Wm, th_r.reshape(2, 6), th_p.reshape(3, 6), 4, pin, pout)
+    assert np.array_equal(rf["Z"], ru["Z"]) and np.array_equal(rf["dX"], ru["dX"])
+    assert np.array_equal(rf["dtheta_R"], ru["dtheta_R"].ravel())
+    assert np.array_equal(rf["dtheta_P"], ru["dtheta_P"].ravel())
+
+
+def test_ragged_blocks_pins():
+    _check_ragged(O.poetx_step)
 
 
 # -------------------------------------------------------------------- int8 ----
@@ -404,7 +480,25 @@ def _mutants():
         v = b2 * np.asarray(v) + (1 - b2) * np.asarray(g) ** 2
         return np.asarray(theta) - gamma * lr * m / (np.sqrt(v) + eps), m, v
 
+    def step_ragged_tail_ignored(X, dZ, Wm, tr, tp, b, pin=None, pout=None):
+        # the smaller last input block stays the identity (its parameters unused)
+        d_in = np.shape(Wm)[1]
+        full = d_in // b
+        tr = np.array(tr, dtype=np.float64)
+        if d_in % b:
+            tr[full * (b * (b - 1) // 2):] = 0.0
+        return O.poetx_step(X, dZ, Wm, tr, tp, b, pin, pout)
+
+    def step_ragged_tail_grad_dropped(X, dZ, Wm, tr, tp, b, pin=None, pout=None):
+        r = O.poetx_step(X, dZ, Wm, tr, tp, b, pin, pout)
+        d_out = np.shape(Wm)[0]
+        if d_out % b:
+            r["dtheta_P"][(d_out // b) * (b * (b - 1) // 2):] = 0.0
+        return r
+
     return [
+        ("ragged last block ignored", lambda: _check_ragged(step_ragged_tail_ignored)),
+        ("ragged last block gradient dropped", lambda: _check_ragged(step_ragged_tail_grad_dropped)),
         ("adam without bias correction", lambda: _check_adam(adam_no_bias_correction)),
         ("fold keeps G_R untransposed", lambda: _check_fold(fold_untransposed, O.merge_perm, O.cnp_forward)),
         ("fold gathers instead of scattering", lambda: _check_fold(fold_gathers, O.merge_perm, O.cnp_forward)),
