@@ -45,8 +45,14 @@
  *    validation error nothing is launched and outputs are untouched.  A failed
  *    launch returns POETX_ERR_HIP; faults during execution surface at the
  *    caller's next synchronization.  poetx_status_string() names a code.
- *  - Supported block sizes: b in {2..512} with b | d_in and b | d_out and
- *    b % 16 == 0 for bf16 layers; any b >= 2 dividing the widths for fp32.
+ *  - Block sizes: 2 <= b <= 1024.  A side of width d has ceil(d/b) diagonal
+ *    blocks (Method §3): d/b full b x b blocks, then, when b does not divide d, one
+ *    last block of size d % b.  A side's theta holds the blocks' packed vectors one
+ *    after another ([d/b][b(b-1)/2], then (d%b)(d%b-1)/2 values) and its G the
+ *    blocks one after another ([d/b][b][b], then [d%b][d%b]).  A block of size 1 has
+ *    no parameters and G = [1].  The MFMA kernels serve bf16 layers with b, d_in
+ *    and d_out multiples of 128 (a last block of such a layer too); every other
+ *    shape runs on the float32 vector-ALU product.
  */
 #ifndef POETX_H
 #define POETX_H
@@ -85,10 +91,12 @@ typedef struct {
   const float *w_scale;        /* [d_out] per-row scale of an I8 W', else NULL      */
   const int32_t *perm_in;      /* [d_in]  or NULL (identity)                        */
   const int32_t *perm_out;     /* [d_out] or NULL (identity)                        */
-  const float *theta_r;        /* [n_R][b(b-1)/2] packed Q of G_R                   */
-  const float *theta_p;        /* [n_P][b(b-1)/2] packed Q of G_P                   */
-  const void *g_r;             /* [n_R][b][b] from poetx_cnp(FWD, theta_r)          */
-  const void *g_p;             /* [n_P][b][b] from poetx_cnp(FWD, theta_p)          */
+  const float *theta_r;        /* [n_R][b(b-1)/2] packed Q of G_R (n_R = d_in/b; with
+                                  a last block of size d_in % b, its packed vector
+                                  follows)                                           */
+  const float *theta_p;        /* [n_P][b(b-1)/2] packed Q of G_P, likewise         */
+  const void *g_r;             /* [n_R][b][b] (then the last block) from poetx_cnp  */
+  const void *g_p;             /* [n_P][b][b] (then the last block) from poetx_cnp  */
 } poetx_layer;
 
 /*
@@ -118,8 +126,14 @@ int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64
  *     ([n][b][b], dg_dtype F32), the exact adjoint of eq. 9 (the page leaves
  *     its eq. 10 unprinted); g unused.
  * Products are evaluated to float32 accuracy (split-bf16 MFMA passes), whatever
- * g_dtype is.  Workspace: query with ws == NULL.
- * Errors: b < 2 or b > 512 -> POETX_ERR_SHAPE; NULL theta / output -> INVALID_ARG.
+ * g_dtype is.  Workspace: query with ws == NULL.  A layer whose b does not divide a
+ * width calls this once for the side's full blocks and once for its last block (at
+ * that block's size).  theta, dtheta, g and dg need only be aligned to their element
+ * size (a last block sits at an offset of whole blocks); g and dg that are not
+ * 16-byte aligned take the float32 vector-ALU path.  b == 1: G = [1] per block,
+ * no parameters (theta and dtheta may be NULL).
+ * Errors: b < 1 or b > 1024 -> POETX_ERR_SHAPE; NULL theta (b > 1) / output ->
+ * INVALID_ARG.
  */
 int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *theta, void *g,
               int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta, void *ws,
@@ -145,9 +159,9 @@ int poetx_forward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void 
  *     dA  = dB . W';          dX~ = dA . Diag(G_R)^T;  dG_R[j] = sum_t X~_j^T dA_j
  *     dx  = Scatter_in(dX~);  dtheta_* = CNP backward of dG_*.
  * saved_b: FAST -> the B written by poetx_forward; MEM -> NULL (recomputed).
- * dx [N][d_in] act dtype; dtheta_r [n_R][p], dtheta_p [n_P][p] float32 (overwritten,
- * sums over all N tokens).  dg_r [n_R][b][b], dg_p [n_P][b][b] float32 are optional
- * outputs of the block gradients (NULL = not written).  Reductions over tokens run
+ * dx [N][d_in] act dtype; dtheta_r, dtheta_p float32 in theta's layout (overwritten,
+ * sums over all N tokens).  dg_r, dg_p float32 in G's layout ([n][b][b], then the last
+ * block) are optional outputs of the block gradients (NULL = not written).  Reductions over tokens run
  * in a fixed order: results are bitwise reproducible run to run.
  */
 int poetx_backward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void *x,

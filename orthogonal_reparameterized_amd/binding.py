@@ -95,15 +95,15 @@ def _dt(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
-def _ptr(t: Optional[torch.Tensor]):
+def _ptr(t: Optional[torch.Tensor], align: int = 16):
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("tensor must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
-    if t.data_ptr() % 16:
-        raise ValueError("tensor must be 16-byte aligned")
+    if t.data_ptr() % align:
+        raise ValueError(f"tensor must be {align}-byte aligned")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -165,7 +165,11 @@ def poetx_cnp(direction: int, theta: torch.Tensor, b: int, *, g: Optional[torch.
                           ctypes.byref(nbytes), None), "poetx_cnp(size)")
     ws = _workspace(dev, nbytes.value)
     nb = _sz(ws.numel())
-    st = _lib.poetx_cnp(direction, n, b, _ptr(theta), _ptr(g), gdt, _ptr(dg), dgdt, _ptr(dtheta),
+    # poetx_cnp takes element-aligned theta, G and dG (a smaller last block of a side
+    # sits at an offset of whole blocks, which need not be a multiple of 16 bytes)
+    def ep(t):
+        return None if t is None else _ptr(t, t.element_size())
+    st = _lib.poetx_cnp(direction, n, b, ep(theta), ep(g), gdt, ep(dg), dgdt, ep(dtheta),
                         _ptr(ws), ctypes.byref(nb), _stream(dev))
     _check(st, "poetx_cnp")
     return g if direction == POETX_CNP_FWD else dtheta
@@ -244,8 +248,13 @@ def poetx_backward(layer: Layer, x: torch.Tensor, dz: torch.Tensor,
     dg_r = dg_p = None
     if want_dg:
         b = layer.b
-        dg_r = torch.empty((layer.d_in // b, b, b), dtype=torch.float32, device=dev)
-        dg_p = torch.empty((layer.d_out // b, b, b), dtype=torch.float32, device=dev)
+        if layer.d_in % b or layer.d_out % b:  # flat: full blocks, then the smaller last block
+            dg_r = torch.empty((layer.d_in // b) * b * b + (layer.d_in % b) ** 2, dtype=torch.float32, device=dev)
+            dg_p = torch.empty((layer.d_out // b) * b * b + (layer.d_out % b) ** 2, dtype=torch.float32,
+                               device=dev)
+        else:
+            dg_r = torch.empty((layer.d_in // b, b, b), dtype=torch.float32, device=dev)
+            dg_p = torch.empty((layer.d_out // b, b, b), dtype=torch.float32, device=dev)
     nbytes = _sz(0)
     _check(_lib.poetx_backward(ctypes.byref(L), n, None, None, None, None, None, None, _ptr(dg_r),
                                _ptr(dg_p), None, ctypes.byref(nbytes), None), "poetx_backward(size)")

@@ -160,11 +160,16 @@ size_t cnp_ws_bytes(int dir, int64_t n, int64_t b) {
   return ar.used;
 }
 
+bool al16(const void *q) { return ((uintptr_t)q & 15) == 0; }
+
 int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype, void *ws,
                  hipStream_t s) {
   Arena ar(ws);
   size_t blk = (size_t)n * b * b * 4;
-  if (cnp_chain_supported(b)) {
+  // the chain and MFMA paths store G with 8- and 16-byte stores; a G that is only
+  // element-aligned takes the vector-ALU path
+  const bool vec = al16(g);
+  if (vec && cnp_chain_supported(b)) {
     // Q as bf16 planes, then the whole Horner chain in one launch
     SkewSegs un;
     un.src[0] = theta; un.n[0] = n;
@@ -182,7 +187,7 @@ int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype,
   float *Q = (float *)ar.take(blk), *S = (float *)ar.take(blk);
   float *T = (float *)ar.take(blk), *U = (float *)ar.take(blk);
   POETX_TRY(unpack_skew(theta, Q, n, b, s));
-  if (cnp_use_mfma(b)) {
+  if (vec && cnp_use_mfma(b)) {
     // S = Q Q and, from the same accumulators, T = 2I + 2Q + S
     CnpMMArgs a;
     a.b = (int)b;
@@ -241,7 +246,11 @@ int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStr
 }
 
 int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
-  if (cnp_chain_supported(b)) return cnp_bwd_chain(b, side, nside, ws, s);
+  // the chain and MFMA paths read dG with vector loads: an only element-aligned dG
+  // takes the vector-ALU path
+  bool vec = true;
+  for (int i = 0; i < nside; ++i) vec = vec && al16(side[i].dg);
+  if (vec && cnp_chain_supported(b)) return cnp_bwd_chain(b, side, nside, ws, s);
   Arena ar(ws);
   struct Bufs { float *Q, *K1, *K2, *K3, *Ha, *Hb; } B[2] = {};
   SkewSegs un;
@@ -252,7 +261,7 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStre
     un.src[i] = side[i].theta; un.dst[i] = B[i].Q; un.n[i] = side[i].n;
   }
   POETX_TRY(unpack_skew2(un, b, s));
-  if (cnp_use_mfma(b)) {
+  if (vec && cnp_use_mfma(b)) {
     auto run = [&](auto fill, float alpha, float c0, float c1, float c2, float c3) {
       CnpMMArgs a;
       a.b = (int)b;
@@ -310,7 +319,7 @@ extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *t
                          void *ws, size_t *ws_bytes, void *stream) {
   if (dir != POETX_CNP_FWD && dir != POETX_CNP_BWD) return POETX_ERR_INVALID_ARG;
   if (nblocks < 0 || !ws_bytes) return POETX_ERR_INVALID_ARG;
-  if (b < 2 || b > 512) return POETX_ERR_SHAPE;
+  if (b < 1 || b > 1024) return POETX_ERR_SHAPE;
   if (dir == POETX_CNP_FWD) {
     if (g_dtype != POETX_F32 && g_dtype != POETX_BF16) return POETX_ERR_INVALID_ARG;
   } else {
@@ -321,12 +330,16 @@ extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *t
     *ws_bytes = need;
     return POETX_OK;
   }
-  if (!theta) return POETX_ERR_INVALID_ARG;
+  // (blocks of size 1 have no parameters: theta and dtheta may then be NULL)
+  if (!theta && b > 1) return POETX_ERR_INVALID_ARG;
   if (dir == POETX_CNP_FWD && !g) return POETX_ERR_INVALID_ARG;
-  if (dir == POETX_CNP_BWD && (!dg || !dtheta)) return POETX_ERR_INVALID_ARG;
+  if (dir == POETX_CNP_BWD && (!dg || (!dtheta && b > 1))) return POETX_ERR_INVALID_ARG;
   if (*ws_bytes < need) return POETX_ERR_WORKSPACE;
   if (nblocks == 0) return POETX_OK;
   hipStream_t s = (hipStream_t)stream;
+  if (b == 1) {  // no parameters: G = [1], nothing to differentiate
+    return dir == POETX_CNP_FWD ? fill_one(g, nblocks, g_dtype, s) : POETX_OK;
+  }
   if (dir == POETX_CNP_FWD) return cnp_fwd_impl(nblocks, b, theta, g, g_dtype, ws, s);
   CnpBwdSide sd;
   sd.n = nblocks; sd.theta = theta; sd.dg = (const float *)dg; sd.dtheta = dtheta;
@@ -336,8 +349,11 @@ extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *t
 // ================================================================== layer ====
 namespace {
 
+// A side of width d has ceil(d/b) diagonal blocks (Method §3): d/b full b x b blocks
+// (nr, np) and, when b does not divide d, a last block of size d % b (lr, lp; 0 when
+// there is none).  theta and G of a side hold the full blocks, then the last one.
 struct Plan {
-  int64_t N, din, dout, b, nr, np;
+  int64_t N, din, dout, b, nr, np, lr, lp;
   int act, w, gdt;
   bool mem, mfma;
   size_t ae;  // activation element size
@@ -346,8 +362,7 @@ struct Plan {
 int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
   if (!L || n_tokens < 0) return POETX_ERR_INVALID_ARG;
   if (L->d_in < 1 || L->d_out < 1) return POETX_ERR_INVALID_ARG;
-  if (L->b < 2 || L->b > 512) return POETX_ERR_SHAPE;
-  if (L->d_in % L->b || L->d_out % L->b) return POETX_ERR_SHAPE;
+  if (L->b < 2 || L->b > 1024) return POETX_ERR_SHAPE;
   if (L->act_dtype != POETX_F32 && L->act_dtype != POETX_BF16) return POETX_ERR_INVALID_ARG;
   if (L->w_dtype != POETX_F32 && L->w_dtype != POETX_BF16 && L->w_dtype != POETX_I8) return POETX_ERR_INVALID_ARG;
   if (L->g_dtype != L->act_dtype) return POETX_ERR_UNSUPPORTED;
@@ -362,6 +377,7 @@ int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
     return POETX_ERR_UNSUPPORTED;
   p.N = n_tokens; p.din = L->d_in; p.dout = L->d_out; p.b = L->b;
   p.nr = L->d_in / L->b; p.np = L->d_out / L->b;
+  p.lr = L->d_in % L->b; p.lp = L->d_out % L->b;
   p.act = L->act_dtype; p.w = L->w_dtype; p.gdt = L->g_dtype;
   p.mem = L->variant == POETX_MEM;
   p.ae = dtype_size(p.act);
@@ -375,76 +391,138 @@ int check_layer_ptrs(const poetx_layer *L) {
   return POETX_OK;
 }
 
-// Y[:, jb:(j+1)b] = X[:, jb:(j+1)b] . G[j]  (transposed: . G[j]^T), for all blocks j.
-int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y, bool transposed,
-                const float *scaleN, hipStream_t s) {
-  int64_t b = p.b, nb = d / b;
-  if (p.N == 0) return POETX_OK;
-  if (p.mfma && block_stream_supported(b, d, p.N))
-    return block_stream((const bf16_t *)X, (const bf16_t *)G, (bf16_t *)Y, p.N, d, b, transposed, scaleN,
+// Y[:, o:o+bs] = X[:, o:o+bs] . G[j]  (transposed: . G[j]^T) for nb blocks of size bs
+// at column offsets o = j*bs; X, Y have row stride ld, G is [nb][bs][bs].
+int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *X, const void *G, void *Y,
+                 bool transposed, const float *scaleN, hipStream_t s) {
+  if (p.N == 0 || nb == 0) return POETX_OK;
+  const bool mfma = p.mfma && bs % 128 == 0;
+  if (mfma && block_stream_supported(bs, ld, nb, p.N))
+    return block_stream((const bf16_t *)X, (const bf16_t *)G, (bf16_t *)Y, p.N, ld, nb, bs, transposed, scaleN,
                         transposed ? "block_apply_t" : "block_apply", s);
-  if (p.mfma) {
+  if (mfma) {
     MfmaDesc m;
-    m.M = p.N; m.N = b; m.K = b; m.batch = nb;
-    m.A = X; m.a_km = false; m.lda = d; m.sAb = b;
-    m.B = G; m.b_km = !transposed; m.b_dt = POETX_BF16; m.ldb = b; m.sBb = b * b;
-    m.C = Y; m.c_dt = p.act; m.ldc = d; m.sCb = b;
-    m.scaleN = scaleN; m.sSNb = b;
+    m.M = p.N; m.N = bs; m.K = bs; m.batch = nb;
+    m.A = X; m.a_km = false; m.lda = ld; m.sAb = bs;
+    m.B = G; m.b_km = !transposed; m.b_dt = POETX_BF16; m.ldb = bs; m.sBb = bs * bs;
+    m.C = Y; m.c_dt = p.act; m.ldc = ld; m.sCb = bs;
+    m.scaleN = scaleN; m.sSNb = bs;
     m.name = transposed ? "block_apply_t" : "block_apply";
     m.role = transposed ? MFMA_BLOCK_APPLY_T : MFMA_BLOCK_APPLY;
     return gemm_mfma_best(m, s);
   }
   GemmDesc g;
-  g.M = p.N; g.N = b; g.K = b; g.batch = nb;
-  g.A = X; g.a_dt = p.act; g.sAb = b; g.sAm = d; g.sAk = 1;
-  g.B = G; g.b_dt = p.gdt; g.sBb = b * b;
-  if (transposed) { g.sBk = 1; g.sBn = b; } else { g.sBk = b; g.sBn = 1; }
-  g.C = Y; g.c_dt = p.act; g.sCb = b; g.sCm = d; g.sCn = 1;
-  g.scaleN = scaleN; g.sSNb = b;
+  g.M = p.N; g.N = bs; g.K = bs; g.batch = nb;
+  g.A = X; g.a_dt = p.act; g.sAb = bs; g.sAm = ld; g.sAk = 1;
+  g.B = G; g.b_dt = p.gdt; g.sBb = bs * bs;
+  if (transposed) { g.sBk = 1; g.sBn = bs; } else { g.sBk = bs; g.sBn = 1; }
+  g.C = Y; g.c_dt = p.act; g.sCb = bs; g.sCm = ld; g.sCn = 1;
+  g.scaleN = scaleN; g.sSNb = bs;
   g.name = transposed ? "block_apply_t_generic" : "block_apply_generic";
   return gemm_generic(g, s);
 }
 
-// dG[j] = X[:, jb:(j+1)b]^T . Y[:, jb:(j+1)b]  (sum over tokens), as fp32 partials that
-// are summed later in a fixed order.  grad_parts() is the number of partials.
-bool grad_streams(const Plan &p, int64_t d) { return p.mfma && p.N > 0 && block_stream_supported(p.b, d, p.N); }
+// Offsets of a side's last block: its first column and its G.
+const void *col_off(const Plan &p, const void *X, int64_t c) { return (const char *)X + c * p.ae; }
+void *col_off(const Plan &p, void *X, int64_t c) { return (char *)X + c * p.ae; }
+const void *g_last(const Plan &p, const void *G, int64_t nb) {
+  return (const char *)G + nb * p.b * p.b * dtype_size(p.gdt);
+}
 
-int64_t grad_chunk(const Plan &p, int64_t nb) {  // token chunk of the split-k kernel
-  if (!p.mfma || p.N == 0) return p.N > 0 ? p.N : 1;
-  int64_t tiles = nb * (p.b / 128) * (p.b / 128);
+// Y = X . Diag(G) (transposed: . Diag(G)^T) over all ceil(d/b) blocks of a side.
+int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y, bool transposed,
+                const float *scaleN, hipStream_t s) {
+  const int64_t b = p.b, nb = d / b, bl = d % b;
+  POETX_TRY(apply_blocks(p, d, nb, b, X, G, Y, transposed, scaleN, s));
+  if (bl == 0) return POETX_OK;
+  const int64_t c = nb * b;
+  return apply_blocks(p, d, 1, bl, col_off(p, X, c), g_last(p, G, nb), col_off(p, Y, c), transposed,
+                      scaleN ? scaleN + c : nullptr, s);
+}
+
+// dG[j] = X[:, o:o+bs]^T . Y[:, o:o+bs] (sum over tokens) for nb blocks of size bs, as
+// fp32 partials [P][nb][bs][bs] that are summed later in a fixed order;
+// grad_parts() is P.
+bool grad_streams(const Plan &p, int64_t ld, int64_t nb, int64_t bs) {
+  return p.mfma && bs % 128 == 0 && p.N > 0 && block_stream_supported(bs, ld, nb, p.N);
+}
+
+int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of the split-k kernel
+  if (p.N == 0) return 1;
+  if (!p.mfma) return p.N;
+  if (bs % 128) return p.N < 1024 ? p.N : 1024;  // vector-ALU product, one launch per chunk group
+  int64_t tiles = nb * (bs / 128) * (bs / 128);
   int64_t want = cdiv(512, tiles);
   int64_t kc = cdiv(cdiv(p.N, want), 64) * 64;
   return kc < 256 ? 256 : kc;
 }
 
-int64_t grad_parts(const Plan &p, int64_t nb) {
-  if (p.N == 0) return 1;
-  if (grad_streams(p, nb * p.b)) return block_grad_stream_parts(p.b, nb * p.b, p.N);
-  return cdiv(p.N, grad_chunk(p, nb));
+int64_t grad_parts(const Plan &p, int64_t ld, int64_t nb, int64_t bs) {
+  if (p.N == 0 || nb == 0) return 1;
+  if (grad_streams(p, ld, nb, bs)) return block_grad_stream_parts(bs, nb, p.N);
+  return cdiv(p.N, grad_chunk(p, nb, bs));
 }
 
-int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, float *parts, hipStream_t s) {
-  int64_t b = p.b, nb = d / b;
-  if (grad_streams(p, d)) return block_grad_stream((const bf16_t *)X, (const bf16_t *)Y, parts, p.N, d, b, s);
-  if (p.mfma) {
-    const int64_t kc = grad_chunk(p, nb);
+int grad_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *X, const void *Y, float *parts,
+                hipStream_t s) {
+  if (nb == 0) return POETX_OK;
+  if (grad_streams(p, ld, nb, bs))
+    return block_grad_stream((const bf16_t *)X, (const bf16_t *)Y, parts, p.N, ld, nb, bs, s);
+  if (p.mfma && bs % 128 == 0) {
+    const int64_t kc = grad_chunk(p, nb, bs);
     MfmaDesc m;
-    m.M = b; m.N = b; m.K = p.N; m.batch = nb;
+    m.M = bs; m.N = bs; m.K = p.N; m.batch = nb;
     m.splits = cdiv(p.N, kc); m.kchunk = kc;
-    m.A = X; m.a_km = true; m.lda = d; m.sAb = b;
-    m.B = Y; m.b_km = true; m.b_dt = POETX_BF16; m.ldb = d; m.sBb = b;
-    m.C = parts; m.c_dt = POETX_F32; m.ldc = b; m.sCb = b * b; m.sCsplit = nb * b * b;
+    m.A = X; m.a_km = true; m.lda = ld; m.sAb = bs;
+    m.B = Y; m.b_km = true; m.b_dt = POETX_BF16; m.ldb = ld; m.sBb = bs;
+    m.C = parts; m.c_dt = POETX_F32; m.ldc = bs; m.sCb = bs * bs; m.sCsplit = nb * bs * bs;
     m.name = "block_grad";
     m.role = MFMA_BLOCK_GRAD;
     return gemm_mfma_best(m, s);
   }
-  GemmDesc g;
-  g.M = b; g.N = b; g.K = p.N; g.batch = nb;
-  g.A = X; g.a_dt = p.act; g.sAb = b; g.sAm = 1; g.sAk = d;
-  g.B = Y; g.b_dt = p.act; g.sBb = b; g.sBk = d; g.sBn = 1;
-  g.C = parts; g.c_dt = POETX_F32; g.sCb = b * b; g.sCm = b; g.sCn = 1;
-  g.name = "block_grad_generic";
-  return gemm_generic(g, s);
+  // vector-ALU product, one launch per token chunk (a batch over the blocks) into
+  // partial c of [P][nb][bs][bs]
+  const int64_t kc = grad_chunk(p, nb, bs);
+  for (int64_t c = 0, t0 = 0; t0 < p.N; ++c, t0 += kc) {
+    GemmDesc g;
+    g.M = bs; g.N = bs; g.K = p.N - t0 < kc ? p.N - t0 : kc; g.batch = nb;
+    g.A = col_off(p, X, t0 * ld); g.a_dt = p.act; g.sAb = bs; g.sAm = 1; g.sAk = ld;
+    g.B = col_off(p, Y, t0 * ld); g.b_dt = p.act; g.sBb = bs; g.sBk = ld; g.sBn = 1;
+    g.C = parts + c * nb * bs * bs; g.c_dt = POETX_F32; g.sCb = bs * bs; g.sCm = bs; g.sCn = 1;
+    g.name = "block_grad_generic";
+    POETX_TRY(gemm_generic(g, s));
+  }
+  return POETX_OK;
+}
+
+// Partials of the block gradients of a side: full blocks and the last block apart.
+struct GradParts {
+  int64_t P = 1, Pl = 1;           // partial counts
+  float *full = nullptr, *last = nullptr;
+};
+
+void carve_grad_parts(Arena &ar, const Plan &p, int64_t d, GradParts &g) {
+  const int64_t b = p.b, nb = d / b, bl = d % b;
+  g.P = grad_parts(p, d, nb, b);
+  g.full = (float *)ar.take((size_t)g.P * nb * b * b * 4);
+  g.Pl = bl ? grad_parts(p, d, 1, bl) : 1;
+  g.last = bl ? (float *)ar.take((size_t)g.Pl * bl * bl * 4) : nullptr;
+}
+
+// dG of every block of a side into dg ([nb][b][b] then [bl][bl]), via the partials.
+int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, const GradParts &gp, float *dg,
+               hipStream_t s) {
+  const int64_t b = p.b, nb = d / b, bl = d % b;
+  if (nb) {
+    POETX_TRY(grad_blocks(p, d, nb, b, X, Y, gp.full, s));
+    POETX_TRY(reduce_parts(gp.full, dg, nb * b * b, gp.P, nb * b * b, s));
+  }
+  if (bl) {
+    const int64_t c = nb * b;
+    POETX_TRY(grad_blocks(p, d, 1, bl, col_off(p, X, c), col_off(p, Y, c), gp.last, s));
+    POETX_TRY(reduce_parts(gp.last, dg + nb * b * b, bl * bl, gp.Pl, bl * bl, s));
+  }
+  return POETX_OK;
 }
 
 // B = A . W'^T (scaled per output row of W' for int8 weights)
@@ -581,7 +659,6 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   if (!ws_bytes) return POETX_ERR_INVALID_ARG;
   if (p.mem && saved_b) return POETX_ERR_INVALID_ARG;
   const int64_t b = p.b, bb = b * b;
-  const int64_t sr = grad_parts(p, p.nr), sp = grad_parts(p, p.np);
   size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
   Arena ar(ws);
   FwdBufs f;
@@ -590,11 +667,16 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   void *dbuf = ar.take(xout);
   void *da = ar.take(xin);
   void *dxt = L->perm_in ? ar.take(xin) : nullptr;
-  float *part_r = (float *)ar.take((size_t)sr * p.nr * bb * 4);
-  float *part_p = (float *)ar.take((size_t)sp * p.np * bb * 4);
-  float *gr = dg_r ? dg_r : (float *)ar.take((size_t)p.nr * bb * 4);
-  float *gp = dg_p ? dg_p : (float *)ar.take((size_t)p.np * bb * 4);
-  void *cws = ar.take(cnp_ws_bytes(POETX_CNP_BWD, p.nr, b) + cnp_ws_bytes(POETX_CNP_BWD, p.np, b));
+  GradParts part_r, part_p;
+  carve_grad_parts(ar, p, p.din, part_r);
+  carve_grad_parts(ar, p, p.dout, part_p);
+  float *gr = dg_r ? dg_r : (float *)ar.take((size_t)(p.nr * bb + p.lr * p.lr) * 4);
+  float *gp = dg_p ? dg_p : (float *)ar.take((size_t)(p.np * bb + p.lp * p.lp) * 4);
+  // the full blocks of both sides in one CNP backward, then the last blocks; the calls
+  // run one after the other and share one workspace region
+  const size_t cw_full = cnp_ws_bytes(POETX_CNP_BWD, p.nr, b) + cnp_ws_bytes(POETX_CNP_BWD, p.np, b);
+  const size_t cw_last = cnp_ws_bytes(POETX_CNP_BWD, p.lr > 1, p.lr) + cnp_ws_bytes(POETX_CNP_BWD, p.lp > 1, p.lp);
+  void *cws = ar.take(cw_full > cw_last ? cw_full : cw_last);
   // one region serves the recomputed forward product (mem) and the dA product in turn
   const size_t tfb = p.mem ? tail_fwd_bytes(p) : 0, tbb = tail_bwd_bytes(p);  // 0: not split
   const size_t tb = tfb > tbb ? tfb : tbb;
@@ -630,25 +712,38 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   if (p.N > 0) {
     POETX_TRY(block_apply(p, p.dout, dzg, L->g_p, dbuf, true,
                           p.w == POETX_I8 ? L->w_scale : nullptr, s));
-    POETX_TRY(block_grad(p, p.dout, bt, dzg, part_p, s));
-    POETX_TRY(reduce_parts(part_p, gp, p.np * bb, sp, p.np * bb, s));
+    POETX_TRY(block_grad(p, p.dout, bt, dzg, part_p, gp, s));
     // dA = dB W'
     POETX_TRY(gemm_bwd(p, L, dbuf, da, tail, tb, s));
     // R side: dX~ = dA Diag(G_R)^T; dG_R = sum_t X~^T dA; dX = Scatter_in(dX~)
     void *dxw = L->perm_in ? dxt : dx;
     POETX_TRY(block_apply(p, p.din, da, L->g_r, dxw, true, nullptr, s));
     if (L->perm_in) POETX_TRY(permute_cols(dxt, dx, p.N, p.din, (int)p.ae, nullptr, L->perm_in, true, s));
-    POETX_TRY(block_grad(p, p.din, xg, da, part_r, s));
-    POETX_TRY(reduce_parts(part_r, gr, p.nr * bb, sr, p.nr * bb, s));
+    POETX_TRY(block_grad(p, p.din, xg, da, part_r, gr, s));
   } else {
     POETX_TRY(lincomb(gr, p.nr, b, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
     POETX_TRY(lincomb(gp, p.np, b, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
+    if (p.lr) POETX_TRY(lincomb(gr + p.nr * bb, 1, p.lr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
+    if (p.lp) POETX_TRY(lincomb(gp + p.np * bb, 1, p.lp, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, nullptr, 0.f, s));
   }
-  // CNP backward on both sides (Method §4)
+  // CNP backward (Method §4): the full blocks of both sides together, then each side's
+  // last block at its own size (a block of size 1 has no parameters)
+  const int64_t pb = b * (b - 1) / 2;
   CnpBwdSide sides[2];
-  sides[0].n = p.nr; sides[0].theta = L->theta_r; sides[0].dg = gr; sides[0].dtheta = dtheta_r;
-  sides[1].n = p.np; sides[1].theta = L->theta_p; sides[1].dg = gp; sides[1].dtheta = dtheta_p;
-  return cnp_bwd_impl(b, sides, 2, cws, s);
+  int ns = 0;
+  if (p.nr) { sides[ns].n = p.nr; sides[ns].theta = L->theta_r; sides[ns].dg = gr; sides[ns].dtheta = dtheta_r; ++ns; }
+  if (p.np) { sides[ns].n = p.np; sides[ns].theta = L->theta_p; sides[ns].dg = gp; sides[ns].dtheta = dtheta_p; ++ns; }
+  if (ns) POETX_TRY(cnp_bwd_impl(b, sides, ns, cws, s));
+  CnpBwdSide lr, lp;
+  lr.n = 1; lr.theta = L->theta_r + p.nr * pb; lr.dg = gr + p.nr * bb; lr.dtheta = dtheta_r + p.nr * pb;
+  lp.n = 1; lp.theta = L->theta_p + p.np * pb; lp.dg = gp + p.np * bb; lp.dtheta = dtheta_p + p.np * pb;
+  if (p.lr > 1 && p.lr == p.lp) {
+    const CnpBwdSide both[2] = {lr, lp};
+    return cnp_bwd_impl(p.lr, both, 2, cws, s);
+  }
+  if (p.lr > 1) POETX_TRY(cnp_bwd_impl(p.lr, &lr, 1, cws, s));
+  if (p.lp > 1) POETX_TRY(cnp_bwd_impl(p.lp, &lp, 1, cws, s));
+  return POETX_OK;
 }
 
 // ================================================================= fold ====

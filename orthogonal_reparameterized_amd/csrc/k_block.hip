@@ -307,18 +307,18 @@ static int run_bs(const BSArgs &a, const char *name, hipStream_t s) {
   return launch(name, s, [&] { k_block_stream<B, SW, T, TRANS><<<grid, 384, lds, s>>>(a); });
 }
 
-bool block_stream_supported(int64_t b, int64_t d, int64_t n_tokens) {
+bool block_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens) {
   if (b != 128 && b != 256 && b != 512) return false;
-  if (d % b) return false;
-  return (n_tokens + 64) * d * 2 < 0x7fffffff;
+  if (nb < 1 || nb * b > ld || ld % 8) return false;
+  return (n_tokens + 64) * ld * 2 < 0x7fffffff;
 }
 
-int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t d, int64_t b,
-                 bool transposed, const float *scaleN, const char *name, hipStream_t s) {
+int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t ld, int64_t nb,
+                 int64_t b, bool transposed, const float *scaleN, const char *name, hipStream_t s) {
   if (n_tokens <= 0) return POETX_OK;
-  if (!block_stream_supported(b, d, n_tokens)) return POETX_ERR_UNSUPPORTED;
+  if (!block_stream_supported(b, ld, nb, n_tokens)) return POETX_ERR_UNSUPPORTED;
   BSArgs a;
-  a.N = n_tokens; a.d = d; a.nb = (int)(d / b);
+  a.N = n_tokens; a.d = ld; a.nb = (int)nb;
   a.X = X; a.G = G; a.Y = Y; a.scaleN = scaleN;
   if (b == 128 || b == 256) {
     // one workgroup per (token partition, block), about one per CU in total
@@ -460,20 +460,20 @@ static int run_bg(const BGArgs &a, hipStream_t s) {
   return launch("block_grad", s, [&] { k_block_grad_stream<B><<<grid, 384, lds, s>>>(a); });
 }
 
-int64_t block_grad_stream_parts(int64_t b, int64_t d, int64_t n_tokens) {
-  const int64_t slices = (d / b) * (b / 128) * (b / 128);
+int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens) {
+  const int64_t slices = nb * (b / 128) * (b / 128);
   int64_t P = (256 + slices - 1) / slices;
   const int64_t ntile = (n_tokens + 63) / 64;
   if (P > ntile) P = ntile;
   return P < 1 ? 1 : P;
 }
 
-int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t d, int64_t b,
-                      hipStream_t s) {
-  if (!block_stream_supported(b, d, n_tokens)) return POETX_ERR_UNSUPPORTED;
+int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t ld, int64_t nb,
+                      int64_t b, hipStream_t s) {
+  if (!block_stream_supported(b, ld, nb, n_tokens)) return POETX_ERR_UNSUPPORTED;
   BGArgs a;
-  a.N = n_tokens; a.d = d; a.nb = (int)(d / b);
-  a.P = (int)block_grad_stream_parts(b, d, n_tokens);
+  a.N = n_tokens; a.d = ld; a.nb = (int)nb;
+  a.P = (int)block_grad_stream_parts(b, nb, n_tokens);
   a.Xs = Xs; a.dY = dY; a.parts = parts;
   if (b == 128) return run_bg<128>(a, s);
   if (b == 256) return run_bg<256>(a, s);

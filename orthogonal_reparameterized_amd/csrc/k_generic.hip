@@ -512,4 +512,19 @@ int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int6
   });
 }
 
+// n elements set to 1 (float32 or bf16): the G of n blocks of size 1.
+__global__ void k_fill_one(void *out, int64_t n, int bf) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (bf) ((bf16_t *)out)[i] = (bf16_t)0x3F80;
+  else ((float *)out)[i] = 1.f;
+}
+
+int fill_one(void *out, int64_t n, int dt, hipStream_t s) {
+  if (n <= 0) return POETX_OK;
+  return launch("fill_one", s, [&] {
+    k_fill_one<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(out, n, dt == POETX_BF16 ? 1 : 0);
+  });
+}
+
 }  // namespace poetx

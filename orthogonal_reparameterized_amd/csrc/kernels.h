@@ -71,6 +71,7 @@ int lincomb(float *out, int64_t n, int64_t b, float cI, const float *X0, float c
             const float *X1, float c1, const float *X2, float c2, const float *X3, float c3,
             hipStream_t s);
 // out[e] = sum_{p < parts} in[p * stride + e], in a fixed order (deterministic)
+int fill_one(void *out, int64_t n, int dt, hipStream_t s);  // n values 1 (F32 or BF16)
 int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int64_t stride,
                  hipStream_t s);
 
@@ -109,18 +110,19 @@ bool mfma2_supported(const MfmaDesc &d);
 size_t gemm_tail_ws_bytes(int64_t M, int64_t N, int64_t K);  // 0: no tile would be split
 int device_cus();  // compute units of the current device, 0 if unknown
 int gemm_mfma2(const MfmaDesc &d, hipStream_t s);   // direct-to-LDS kernel (bf16 operands)
-// Streaming block-diagonal product (b in {128, 256, 512}):
-//   Y[:, jb:(j+1)b] = X[:, jb:(j+1)b] . G[j]  (transposed: . G[j]^T), times scaleN[col]
-// X, Y token-major [n_tokens][d] bf16, G [d/b][b][b] bf16.
-bool block_stream_supported(int64_t b, int64_t d, int64_t n_tokens);
-int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t d, int64_t b,
-                 bool transposed, const float *scaleN, const char *name, hipStream_t s);
+// Streaming block-diagonal product over the first nb blocks (b in {128, 256, 512}):
+//   Y[:, jb:(j+1)b] = X[:, jb:(j+1)b] . G[j]  (transposed: . G[j]^T), times scaleN[col],
+// j < nb.  X, Y token-major with row stride ld (>= nb*b, a multiple of 8) bf16,
+// G [nb][b][b] bf16.
+bool block_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens);
+int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t ld, int64_t nb,
+                 int64_t b, bool transposed, const float *scaleN, const char *name, hipStream_t s);
 // Streaming block gradient (same b and shape limits as block_stream): P partials
-//   parts[p][j] = sum_{t in token tiles p, p+P, ...} Xs_j[t]^T dY_j[t],  parts [P][d/b][b][b] fp32,
-// with P = block_grad_stream_parts(b, d, n_tokens); n_tokens >= 1.
-int64_t block_grad_stream_parts(int64_t b, int64_t d, int64_t n_tokens);
-int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t d, int64_t b,
-                      hipStream_t s);
+//   parts[p][j] = sum_{t in token tiles p, p+P, ...} Xs_j[t]^T dY_j[t],  parts [P][nb][b][b] fp32,
+// with P = block_grad_stream_parts(b, nb, n_tokens); n_tokens >= 1.
+int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens);
+int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t ld, int64_t nb,
+                      int64_t b, hipStream_t s);
 // the direct-to-LDS kernel where it applies, else the register-staged one
 inline int gemm_mfma_best(const MfmaDesc &d, hipStream_t s) {
   return mfma2_supported(d) ? gemm_mfma2(d, s) : gemm_mfma(d, s);

@@ -50,15 +50,28 @@ class LayerStep:
                                                          out_t=self.w_merged_t)
         del w
         # theta_R and theta_P (and G_R, G_P) live in one buffer each, so that the CNP
-        # forward of both sides is a single poetx_cnp call over n_R + n_P blocks
+        # forward of both sides is a single poetx_cnp call over n_R + n_P blocks.  With a
+        # smaller last block on a side (b not dividing its width) the side's theta and G
+        # are flat: full blocks first, then the last block.
         self.n_r, self.n_p = wl.d_in // wl.b, wl.d_out // wl.b
-        self.theta = upload(np.concatenate([inputs["theta_r"], inputs["theta_p"]]), "f32", dev)
-        self.theta_r, self.theta_p = self.theta[:self.n_r], self.theta[self.n_r:]
+        self.l_r, self.l_p = wl.d_in % wl.b, wl.d_out % wl.b
+        self.ragged = bool(self.l_r or self.l_p)
         self.x = upload(inputs["x"], wl.act, dev)
         self.dz = upload(inputs["dz"], wl.act, dev)
         n, b = self.x.shape[0], wl.b
-        self.g = torch.empty((self.n_r + self.n_p, b, b), dtype=act, device=dev)
-        self.g_r, self.g_p = self.g[:self.n_r], self.g[self.n_r:]
+        if not self.ragged:
+            self.theta = upload(np.concatenate([inputs["theta_r"], inputs["theta_p"]]), "f32", dev)
+            self.theta_r, self.theta_p = self.theta[:self.n_r], self.theta[self.n_r:]
+            self.g = torch.empty((self.n_r + self.n_p, b, b), dtype=act, device=dev)
+            self.g_r, self.g_p = self.g[:self.n_r], self.g[self.n_r:]
+        else:
+            # one allocation per side, so that each side's buffer starts 16-byte aligned
+            self.theta = None
+            self.theta_r = upload(np.ravel(inputs["theta_r"]), "f32", dev)
+            self.theta_p = upload(np.ravel(inputs["theta_p"]), "f32", dev)
+            self.g = None
+            self.g_r = torch.empty(self.n_r * b * b + self.l_r ** 2, dtype=act, device=dev)
+            self.g_p = torch.empty(self.n_p * b * b + self.l_p ** 2, dtype=act, device=dev)
         self.z = torch.empty((n, wl.d_out), dtype=act, device=dev)
         self.saved_b = torch.empty((n, wl.d_out), dtype=act, device=dev) if self.variant == B.POETX_FAST else None
         self.dx = torch.empty((n, wl.d_in), dtype=act, device=dev)
@@ -69,8 +82,19 @@ class LayerStep:
                              perm_in=self.perm_in, perm_out=self.perm_out, w_merged_t=self.w_merged_t)
 
     def cnp(self):
-        # both sides share b: one call over the n_R + n_P blocks of the shared buffer
-        B.poetx_cnp(B.POETX_CNP_FWD, self.theta, self.wl.b, g=self.g)
+        b = self.wl.b
+        if not self.ragged:
+            # both sides share b: one call over the n_R + n_P blocks of the shared buffer
+            B.poetx_cnp(B.POETX_CNP_FWD, self.theta, b, g=self.g)
+            return
+        p = b * (b - 1) // 2
+        for theta, g, n, last in ((self.theta_r, self.g_r, self.n_r, self.l_r),
+                                  (self.theta_p, self.g_p, self.n_p, self.l_p)):
+            if n:
+                B.poetx_cnp(B.POETX_CNP_FWD, theta[:n * p].view(n, p), b, g=g[:n * b * b].view(n, b, b))
+            if last:
+                B.poetx_cnp(B.POETX_CNP_FWD, theta[n * p:].view(1, last * (last - 1) // 2), last,
+                            g=g[n * b * b:].view(1, last, last))
 
     def forward(self):
         B.poetx_forward(self.layer, self.x, self.z, self.saved_b)

@@ -44,7 +44,7 @@ class Workload:
     perms: bool = True
 
     @property
-    def n_r(self):
+    def n_r(self):  # full b x b blocks of the input side
         return self.d_in // self.b
 
     @property
@@ -52,8 +52,24 @@ class Workload:
         return self.d_out // self.b
 
     @property
+    def l_r(self):  # size of the input side's last, smaller block (0: none)
+        return self.d_in % self.b
+
+    @property
+    def l_p(self):
+        return self.d_out % self.b
+
+    @property
+    def ragged(self):
+        return bool(self.l_r or self.l_p)
+
+    @property
     def p(self):
         return self.b * (self.b - 1) // 2
+
+    def theta_len(self, side: str) -> int:
+        n, last = (self.n_r, self.l_r) if side == "r" else (self.n_p, self.l_p)
+        return n * self.p + last * (last - 1) // 2
 
 
 WORKLOADS = {
@@ -143,8 +159,12 @@ def make_layer_inputs(wl: Workload, n_tokens: int | None = None, seed: int | Non
     else:
         out["w"] = store(w64, wl.w)
     del w64
-    out["theta_r"] = (g_tr.standard_normal((wl.n_r, wl.p)) * wl.theta_std * theta_scale).astype(np.float32)
-    out["theta_p"] = (g_tp.standard_normal((wl.n_p, wl.p)) * wl.theta_std * theta_scale).astype(np.float32)
+    # [n][p] when b divides both widths; otherwise flat, the blocks' packed vectors one
+    # after another (the last block of a side is the smaller one)
+    shp_r = (wl.n_r, wl.p) if not wl.ragged else (wl.theta_len("r"),)
+    shp_p = (wl.n_p, wl.p) if not wl.ragged else (wl.theta_len("p"),)
+    out["theta_r"] = (g_tr.standard_normal(shp_r) * wl.theta_std * theta_scale).astype(np.float32)
+    out["theta_p"] = (g_tp.standard_normal(shp_p) * wl.theta_std * theta_scale).astype(np.float32)
     out["x"] = store(g_x.standard_normal((n, wl.d_in)), wl.act)
     out["dz"] = store(g_dz.standard_normal((n, wl.d_out)), wl.act)
     return out

@@ -25,6 +25,23 @@ def to_host_f64(t):
     return t.cpu().numpy().astype(np.float64)
 
 
+def flat(x):
+    """Blocks of unequal size (a list) or any array, as one flat float64 vector."""
+    if isinstance(x, (list, tuple)):
+        return np.concatenate([np.ravel(np.asarray(a, dtype=np.float64)) for a in x]) if x else np.zeros(0)
+    return np.ravel(np.asarray(x, dtype=np.float64))
+
+
+def split_g(g_flat, d, b):
+    """A side's flat G (full b x b blocks, then the last block of size d % b) as a list."""
+    g_flat = np.ravel(g_flat)
+    full, last = divmod(d, b)
+    out = [g_flat[j * b * b:(j + 1) * b * b].reshape(b, b) for j in range(full)]
+    if last:
+        out.append(g_flat[full * b * b:].reshape(last, last))
+    return out
+
+
 def norm_max_err(got, ref):
     """||got - ref||_inf / ||ref||_inf."""
     den = np.max(np.abs(ref))

@@ -84,9 +84,12 @@ def test_workspace_queries(B):
 def test_validation_codes(B):
     ok = layer(B)
     # shape errors
-    assert fwd(B, layer(B, b=100))[0] == B.POETX_ERR_SHAPE          # 100 does not divide 512
     assert fwd(B, layer(B, b=1))[0] == B.POETX_ERR_SHAPE
-    assert fwd(B, layer(B, b=1024, d_in=2048, d_out=2048))[0] == B.POETX_ERR_SHAPE
+    assert fwd(B, layer(B, b=2048, d_in=4096, d_out=4096))[0] == B.POETX_ERR_SHAPE  # above 1024
+    # ceil(d/b) blocks: b need not divide the widths (512 = 5 * 100 + 12); b = 1024 is supported
+    assert fwd(B, layer(B, b=100))[0] == B.POETX_OK
+    assert bwd(B, layer(B, b=100))[0] == B.POETX_OK
+    assert fwd(B, layer(B, b=1024, d_in=2048, d_out=2048))[0] == B.POETX_OK
     # invalid arguments
     assert fwd(B, layer(B, act=7))[0] == B.POETX_ERR_INVALID_ARG
     assert fwd(B, layer(B, variant=5))[0] == B.POETX_ERR_INVALID_ARG
@@ -107,8 +110,12 @@ def test_validation_codes(B):
     assert bwd(B, ok, ws=FAKE, ws_bytes=need - 1)[0] == B.POETX_ERR_WORKSPACE
     # CNP
     nb = ctypes.c_size_t(1 << 40)
-    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 1, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
-                           ctypes.byref(nb), None) == B.POETX_ERR_SHAPE
+    for bad_b in (0, 2048):
+        assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, bad_b, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+                               ctypes.byref(nb), None) == B.POETX_ERR_SHAPE
+    q = ctypes.c_size_t(0)  # blocks of size 1 (no parameters) are accepted
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 1, None, None, B.POETX_BF16, None, 0, None, None,
+                           ctypes.byref(q), None) == B.POETX_OK
     assert B.raw.poetx_cnp(9, 4, 64, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
                            ctypes.byref(nb), None) == B.POETX_ERR_INVALID_ARG
     assert B.raw.poetx_cnp(B.POETX_CNP_BWD, 4, 64, FAKE, None, 0, None, B.POETX_F32, FAKE, FAKE,
@@ -138,7 +145,8 @@ def test_fold_validation(B):
     assert fold(B, layer(B), w_out=None, ws=FAKE, ws_bytes=need)[0] == B.POETX_ERR_INVALID_ARG
     assert fold(B, layer(B), w_out=FAKE, ws=FAKE, ws_bytes=need)[0] == B.POETX_ERR_INVALID_ARG  # aliases W'
     assert fold(B, layer(B, w=B.POETX_I8, w_scale=FAKE, variant=B.POETX_MEM))[0] == B.POETX_ERR_UNSUPPORTED
-    assert fold(B, layer(B, b=100))[0] == B.POETX_ERR_SHAPE
+    assert fold(B, layer(B, b=2048, d_in=4096, d_out=4096))[0] == B.POETX_ERR_SHAPE
+    assert fold(B, layer(B, b=100))[0] == B.POETX_OK  # a smaller last block on each side
 
 
 def test_adam_validation(B):

@@ -22,8 +22,8 @@ torch = pytest.importorskip("torch")
 
 from oracle import poetx_oracle as O  # noqa: E402
 from orthogonal_reparameterized_amd import workloads as WL  # noqa: E402
-from tests.helpers import (bf16_ulp, norm_max_err, oracle_layer, rel_fro,  # noqa: E402
-                           rel_fro_per_block, to_host_f64)
+from tests.helpers import (bf16_ulp, flat, norm_max_err, oracle_layer, rel_fro,  # noqa: E402
+                           rel_fro_per_block, split_g, to_host_f64)
 
 TOL_BF16 = 2e-2
 TOL_F32_LAYER = 1e-4
@@ -48,7 +48,7 @@ def _say(*a):
 # last full group of 8 in the workgroup order), b = 192 the per-product MFMA path,
 # b = 32 and 48 the float32 vector-ALU path
 CNP_CASES = [(8, 32, 0.02), (11, 64, 0.03), (19, 128, 0.02), (3, 192, 0.01), (3, 256, 0.01),
-             (2, 512, 0.01)]
+             (2, 512, 0.01), (2, 1024, 0.005)]
 
 
 @pytest.mark.parametrize("n,b,std", CNP_CASES + [(5, 48, 0.05)])
@@ -69,6 +69,16 @@ def test_cnp_forward_bf16_ulp(B, n, b):
     got = to_host_f64(g)
     bound = np.maximum(bf16_ulp(ref), 2.0 ** -20)
     assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_cnp_size_one_blocks(B):
+    """Blocks of size 1 have no parameters: G = [1] in either dtype, no gradient entries."""
+    th = torch.zeros((5, 0), device="cuda")
+    for dt in (torch.float32, torch.bfloat16):
+        g = B.poetx_cnp(B.POETX_CNP_FWD, th, 1, g_dtype=dt)
+        assert torch.equal(g.float().cpu(), torch.ones(5, 1, 1))
+    d = B.poetx_cnp(B.POETX_CNP_BWD, th, 1, dg=torch.ones((5, 1, 1), device="cuda"))
+    assert d.shape == (5, 0)
 
 
 def test_cnp_zero_is_identity(B):
@@ -147,17 +157,20 @@ def _run_step(wl, inp, variant, perms=True, transposed_weight=False):
 
 
 def _compare(st, out, ref, tol, label):
+    # blocks of unequal size come back from the oracle as lists: compare flattened
+    def e(got, key):
+        return norm_max_err(flat(to_host_f64(got)), flat(ref[key]))
     errs = {
-        "G_R": norm_max_err(to_host_f64(st.g_r), ref["G_R"]),
-        "G_P": norm_max_err(to_host_f64(st.g_p), ref["G_P"]),
-        "Z": norm_max_err(to_host_f64(st.z), ref["Z"]),
-        "dX": norm_max_err(to_host_f64(out["dx"]), ref["dX"]),
-        "dG_R": norm_max_err(to_host_f64(out["dg_r"]), ref["dG_R"]),
-        "dG_P": norm_max_err(to_host_f64(out["dg_p"]), ref["dG_P"]),
-        "dtheta_R": norm_max_err(to_host_f64(out["dtheta_r"]), ref["dtheta_R"]),
-        "dtheta_P": norm_max_err(to_host_f64(out["dtheta_p"]), ref["dtheta_P"]),
+        "G_R": e(st.g_r, "G_R"),
+        "G_P": e(st.g_p, "G_P"),
+        "Z": e(st.z, "Z"),
+        "dX": e(out["dx"], "dX"),
+        "dG_R": e(out["dg_r"], "dG_R"),
+        "dG_P": e(out["dg_p"], "dG_P"),
+        "dtheta_R": e(out["dtheta_r"], "dtheta_R"),
+        "dtheta_P": e(out["dtheta_p"], "dtheta_P"),
     }
-    fro = {k: rel_fro(to_host_f64(v), ref[r]) for k, v, r in
+    fro = {k: rel_fro(flat(to_host_f64(v)), flat(ref[r])) for k, v, r in
            (("Z", st.z, "Z"), ("dX", out["dx"], "dX"), ("dtheta_R", out["dtheta_r"], "dtheta_R"))}
     _say(f"{label}: normalized max errors {errs} rel-fro {fro}")
     for k, e in errs.items():
@@ -211,6 +224,39 @@ def test_layer_bf16_generic_block(B):
     _compare(st, out, ref, TOL_BF16, "b=48 generic")
 
 
+RAGGED = [
+    # (n_tokens, d_in, d_out, b, dtype): ceil(d/b) blocks, the last one smaller
+    (257, 640, 896, 256, "bf16"),   # last blocks 128 | 128 on the MFMA kernels
+    (100, 384, 640, 512, "bf16"),   # input side narrower than b (one block of 384)
+    (70, 576, 320, 256, "bf16"),    # 128 does not divide d_in: vector-ALU path, last blocks 64
+    (64, 200, 150, 32, "f32"),      # last blocks 8 | 22
+    (33, 97, 70, 32, "f32"),        # a last block of size 1 (no parameters) | 6
+]
+
+
+@pytest.mark.parametrize("n,d_in,d_out,b,dt", RAGGED)
+@pytest.mark.parametrize("variant", ["fast", "mem"])
+def test_layer_ragged_blocks(B, n, d_in, d_out, b, dt, variant):
+    wl = WL.Workload(96, "ragged", n, d_in, d_out, b, dt, dt, dt, 0.02, d_in)
+    assert wl.ragged
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    _say(f"ragged n={n} {d_in}->{d_out} b={b} {dt} {variant}")
+    st, out = _run_step(wl, inp, variant)
+    _compare(st, out, ref, TOL_BF16 if dt == "bf16" else TOL_F32_LAYER, f"ragged {d_in}->{d_out} b={b} {variant}")
+
+
+@pytest.mark.parametrize("variant", ["fast", "mem"])
+def test_layer_b1024(B, variant):
+    """b = 1024: CNP on the per-product MFMA path, block products on the MFMA engines."""
+    wl = WL.Workload(98, "b1024", 130, 2048, 1024, 1024, "bf16", "bf16", "bf16", 0.005, 2048)
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    _say(f"b=1024 {variant}")
+    st, out = _run_step(wl, inp, variant)
+    _compare(st, out, ref, TOL_BF16, f"b=1024 {variant}")
+
+
 def test_layer_int8_small(B):
     wl = WL.Workload(92, "small int8", 200, 512, 768, 256, "bf16", "i8", "bf16", 0.01, 512, variants=("mem",))
     inp = WL.make_layer_inputs(wl)
@@ -238,6 +284,8 @@ FOLD_CASES = [
     (512, 768, 256, "bf16", True),
     (256, 384, 128, "bf16", False),
     (1024, 512, 512, "bf16", True),
+    (640, 896, 256, "bf16", True),   # a smaller last block on each side
+    (200, 150, 32, "f32", True),
 ]
 
 
@@ -256,8 +304,8 @@ def test_fold(B, d_in, d_out, b, dt, perms):
     inp = WL.make_layer_inputs(wl)
     st = _fold_layer(wl, inp)
     w_eff = B.poetx_fold(st.layer)
-    ref = O.fold_weights(to_host_f64(st.w_merged), to_host_f64(st.g_r), to_host_f64(st.g_p),
-                         inp["perm_in"], inp["perm_out"])
+    ref = O.fold_weights(to_host_f64(st.w_merged), split_g(to_host_f64(st.g_r), d_in, b),
+                         split_g(to_host_f64(st.g_p), d_out, b), inp["perm_in"], inp["perm_out"])
     tol = TOL_CNP_F32 if dt == "f32" else TOL_BF16
     assert norm_max_err(to_host_f64(w_eff), ref) <= tol
 
