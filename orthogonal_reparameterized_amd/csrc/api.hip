@@ -554,15 +554,29 @@ int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, void *
 }
 
 // dA = dB' . W'  (dB' already carries the int8 row scales)
+// Without a kept W'^T, the backward product still runs on the k-contiguous NT kernel when
+// that kernel tiles the shape: W' is transposed into the workspace first (one pass over
+// the weight, much less than what reading W' n-major costs the product).
+bool bwd_transposes_w(const Plan &p, const poetx_layer *L) {
+  return p.mfma && p.N > 0 && !L->w_merged_t && (p.w == POETX_BF16 || p.w == POETX_I8) && p.din % 256 == 0 &&
+         p.dout % 64 == 0;
+}
+
+// `wt`: workspace for W'^T when bwd_transposes_w, else null.
 int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, void *tail, size_t tail_bytes,
-             hipStream_t s) {
+             void *wt, hipStream_t s) {
   if (p.N == 0) return POETX_OK;
-  if (p.mfma && L->w_merged_t && p.w == POETX_BF16) {
+  const void *w_t = p.w == POETX_BF16 ? L->w_merged_t : nullptr;
+  if (p.mfma && !w_t && wt) {
+    POETX_TRY(transpose(L->w_merged, wt, p.dout, p.din, (int)dtype_size(p.w), s));
+    w_t = wt;
+  }
+  if (p.mfma && w_t) {
     // dA = dB . (W'^T)^T: both operands k-contiguous
     MfmaDesc m;
     m.M = p.N; m.N = p.din; m.K = p.dout;
     m.A = dB; m.a_km = false; m.lda = p.dout;
-    m.B = L->w_merged_t; m.b_km = false; m.b_dt = POETX_BF16; m.ldb = p.dout;
+    m.B = w_t; m.b_km = false; m.b_dt = p.w; m.ldb = p.dout;
     m.C = dA; m.c_dt = p.act; m.ldc = p.din;
     m.name = "gemm_nn";
     m.role = MFMA_GEMM_NT;
@@ -681,6 +695,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   const size_t tfb = p.mem ? tail_fwd_bytes(p) : 0, tbb = tail_bwd_bytes(p);  // 0: not split
   const size_t tb = tfb > tbb ? tfb : tbb;
   void *tail = tb ? ar.take(tb) : nullptr;
+  void *wt = bwd_transposes_w(p, L) ? ar.take((size_t)p.din * p.dout * dtype_size(p.w)) : nullptr;
   if (!ws) {
     *ws_bytes = ar.used;
     return POETX_OK;
@@ -714,7 +729,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
                           p.w == POETX_I8 ? L->w_scale : nullptr, s));
     POETX_TRY(block_grad(p, p.dout, bt, dzg, part_p, gp, s));
     // dA = dB W'
-    POETX_TRY(gemm_bwd(p, L, dbuf, da, tail, tb, s));
+    POETX_TRY(gemm_bwd(p, L, dbuf, da, tail, tb, wt, s));
     // R side: dX~ = dA Diag(G_R)^T; dG_R = sum_t X~^T dA; dX = Scatter_in(dX~)
     void *dxw = L->perm_in ? dxt : dx;
     POETX_TRY(block_apply(p, p.din, da, L->g_r, dxw, true, nullptr, s));

@@ -309,8 +309,45 @@ __global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ in, T *
   }
 }
 
+// The same with 16-byte global accesses: a tile of TR x TR elements (128-byte tile rows:
+// 64 x 64 for 2-byte, 128 x 128 for 1-byte elements) is read along its rows in 16-byte
+// chunks into a padded LDS tile, and written along its columns in 16-byte chunks, each
+// gathered from V = 16 / sizeof(T) consecutive tile rows.  Needs rows and cols to be
+// multiples of V (whole chunks) and 16-byte aligned buffers.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose_v(const T *__restrict__ in, T *__restrict__ out, int64_t rows,
+                                                     int64_t cols) {
+  constexpr int V = 16 / sizeof(T), TR = 128 / sizeof(T), LD = TR + V;
+  __shared__ __align__(16) T t[TR][LD];
+  const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * TR;
+  for (int q = threadIdx.x; q < TR * 8; q += 256) {
+    const int row = q >> 3, ch = q & 7;
+    const int64_t r = r0 + row, c = c0 + ch * V;
+    if (r < rows && c < cols) *(uint4 *)&t[row][ch * V] = *(const uint4 *)(in + r * cols + c);
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < TR * 8; q += 256) {
+    const int cc = q >> 3, rr = q & 7;
+    const int64_t c = c0 + cc, r = r0 + rr * V;
+    if (c < cols && r < rows) {
+      union { uint4 v; T e[V]; } u;
+#pragma unroll
+      for (int j = 0; j < V; ++j) u.e[j] = t[rr * V + j][cc];
+      *(uint4 *)(out + c * rows + r) = u.v;
+    }
+  }
+}
+
 int transpose(const void *in, void *out, int64_t rows, int64_t cols, int esize, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return POETX_OK;
+  const int64_t V = 16 / esize, TR = 128 / esize;
+  if (esize <= 2 && rows % V == 0 && cols % V == 0 && (((uintptr_t)in | (uintptr_t)out) & 15) == 0 &&
+      cdiv(rows, TR) <= 65535) {
+    dim3 grid((unsigned)cdiv(cols, TR), (unsigned)cdiv(rows, TR));
+    if (esize == 2)
+      return launch("transpose", s, [&] { k_transpose_v<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols); });
+    return launch("transpose", s, [&] { k_transpose_v<uint8_t><<<grid, 256, 0, s>>>((const uint8_t *)in, (uint8_t *)out, rows, cols); });
+  }
   if (cdiv(rows, 64) > 65535) return POETX_ERR_UNSUPPORTED;
   dim3 grid((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 64));
   switch (esize) {

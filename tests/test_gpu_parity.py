@@ -129,14 +129,24 @@ def test_merge_bit_exact(B, dt):
                                     torch.from_numpy(pin).cuda(), torch.from_numpy(s).cuda())
         qr, sr = O.merge_perm_int8(w, s, pout, pin)
         assert np.array_equal(wm.cpu().numpy(), qr) and np.array_equal(sm.cpu().numpy(), sr)
+        # the 1-byte transpose (the backward's W'^T of an int8 layer): 16-byte chunk path, and
+        # a width that is not a multiple of 16 (element path)
+        for rows, cols in ((384, 640), (40, 72)):
+            q = rng.integers(-127, 128, size=(rows, cols)).astype(np.int8)
+            q_t = torch.empty((cols, rows), dtype=torch.int8, device="cuda")
+            B.poetx_merge_perm(torch.from_numpy(q).cuda(), None, None,
+                               torch.ones(rows, dtype=torch.float32, device="cuda"), out_t=q_t)
+            assert np.array_equal(q_t.cpu().numpy(), q.T)
         return
     w = rng.standard_normal((d_out, d_in)).astype(np.float32)
     if dt == "bf16":
         bits = WL.f32_to_bf16_bits(w)
         wt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
         ref = O.merge_perm(bits, pout, pin)
-        wm, _ = B.poetx_merge_perm(wt, torch.from_numpy(pout).cuda(), torch.from_numpy(pin).cuda())
+        w_t = torch.empty((d_in, d_out), dtype=torch.bfloat16, device="cuda")
+        wm, _ = B.poetx_merge_perm(wt, torch.from_numpy(pout).cuda(), torch.from_numpy(pin).cuda(), out_t=w_t)
         assert np.array_equal(wm.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+        assert np.array_equal(w_t.view(torch.int16).cpu().numpy().view(np.uint16), ref.T)
     else:
         wt = torch.empty((d_in, d_out), dtype=torch.float32, device="cuda")
         wm, _ = B.poetx_merge_perm(torch.from_numpy(w).cuda(), torch.from_numpy(pout).cuda(),
