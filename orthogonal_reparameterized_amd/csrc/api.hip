@@ -397,6 +397,20 @@ int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *
                  bool transposed, const float *scaleN, hipStream_t s) {
   if (p.N == 0 || nb == 0) return POETX_OK;
   const bool mfma = p.mfma && bs % 128 == 0;
+  if (mfma && bs == 512) {
+    // At b = 512 each block product is a K = N = 512 GEMM: the 256 x 256 W' kernels,
+    // batched over blocks, read X twice (two column tiles) where a block kernel with a
+    // G slice in LDS reads it once per slice
+    MfmaDesc m;
+    m.M = p.N; m.N = bs; m.K = bs; m.batch = nb;
+    m.A = X; m.a_km = false; m.lda = ld; m.sAb = bs;
+    m.B = G; m.b_km = !transposed; m.b_dt = POETX_BF16; m.ldb = bs; m.sBb = bs * bs;
+    m.C = Y; m.c_dt = p.act; m.ldc = ld; m.sCb = bs;
+    m.scaleN = scaleN; m.sSNb = bs;
+    m.name = transposed ? "block_apply_t" : "block_apply";
+    m.role = transposed ? MFMA_GEMM_NT : MFMA_GEMM_NN;
+    if (mfma2_supported(m)) return gemm_mfma2(m, s);
+  }
   if (mfma && block_stream_supported(bs, ld, nb, p.N))
     return block_stream((const bf16_t *)X, (const bf16_t *)G, (bf16_t *)Y, p.N, ld, nb, bs, transposed, scaleN,
                         transposed ? "block_apply_t" : "block_apply", s);
