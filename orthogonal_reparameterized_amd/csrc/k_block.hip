@@ -461,8 +461,11 @@ static int run_bg(const BGArgs &a, hipStream_t s) {
 }
 
 int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens) {
+  // about one workgroup per CU in a single round: rounding the partition count up would
+  // start a second, mostly idle round
   const int64_t slices = nb * (b / 128) * (b / 128);
-  int64_t P = (256 + slices - 1) / slices;
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  int64_t P = cus / slices;
   const int64_t ntile = (n_tokens + 63) / 64;
   if (P > ntile) P = ntile;
   return P < 1 ? 1 : P;
