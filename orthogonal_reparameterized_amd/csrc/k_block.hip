@@ -130,22 +130,25 @@ POETX_BS_INST(256, 128, 64)
 POETX_BS_INST(512, 64, 32)
 #undef POETX_BS_INST
 
-// Register-resident variant for b = 128 and 256: each of the 4 consumer waves keeps
-// its b x (b/4) share of G_j (or G_j^T) as MFMA operand fragments in registers for
-// the whole kernel (b = 256: 128 VGPRs), so one workgroup covers the block's full
-// width -- every token tile of X_j is read once -- and the whole LDS is a 4-stage
-// ring of T-token tiles (more bytes in flight per CU than with G held in LDS).
+// Register-resident variant for b = 128 and 256: each of the NCW consumer waves keeps
+// its b x (b/NCW) share of G_j (or G_j^T) as MFMA operand fragments in registers for
+// the whole kernel, so one workgroup covers the block's full width -- every token tile
+// of X_j is read once -- and the whole LDS is a ring of T-token tiles (more bytes in
+// flight per CU than with G held in LDS).  At b = 256 the 8 consumers (64 VGPRs of G
+// each) put two MFMA-issuing waves on every SIMD: a lone wave issues MFMAs at about
+// two thirds of the SIMD's rate (measured on bare MFMAs), and with 4 consumers the
+// kernel was bound by exactly that.
 // G is staged once through the ring's LDS at the start.  Workgroup u covers block
 // j = u % nb and token tiles p, p + P, ... with p = u / nb, so the blocks of the
 // same token rows run side by side.
-template <int B, int T, int NST, bool TRANS>
-__global__ __launch_bounds__(384) void k_block_reg(BSArgs a) {
-  constexpr int NCW = 4, NPW = 2;
-  constexpr int NTW = B / 64, NKS = B / 32, FM = T / 16;
+template <int B, int T, int NST, bool TRANS, int NCW = 4>
+__global__ __launch_bounds__(64 * (NCW + 2)) void k_block_reg(BSArgs a) {
+  constexpr int NPW = 2;
+  constexpr int NTW = B / (16 * NCW), NKS = B / 32, FM = T / 16;
   constexpr int A_ELEMS = T * B;
-  // per consumer wave, its T x (B/4) output tile is restaged in LDS so that the
-  // global stores are 16 bytes per lane along rows (whole 128-byte lines at b = 256)
-  constexpr int OW = B / 4, OCH = OW / 8, O_ELEMS = T * OW;
+  // per consumer wave, its T x (B/NCW) output tile is restaged in LDS so that the
+  // global stores are 16 bytes per lane along rows
+  constexpr int OW = B / NCW, OCH = OW / 8, O_ELEMS = T * OW;
   static_assert(NST * A_ELEMS + NCW * O_ELEMS >= B * B, "G is staged in the ring");
   extern __shared__ __align__(16) bf16_t smem[];
   const int u = blockIdx.x;
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(384) void k_block_reg(BSArgs a) {
   const int64_t ntile = (a.N + T - 1) / T;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
   const bool producer = wave >= NCW;
-  const int n0 = wave * (B / 4);  // a consumer's first output column within the block
+  const int n0 = wave * (B / NCW);  // a consumer's first output column within the block
 
   // ---- this wave's columns of the block operand, into registers
   bf16x8 gf[NTW][NKS];
@@ -276,19 +279,21 @@ template __global__ void k_block_reg<128, 64, 4, false>(BSArgs);
 template __global__ void k_block_reg<128, 64, 4, true>(BSArgs);
 template __global__ void k_block_reg<256, 32, 7, false>(BSArgs);
 template __global__ void k_block_reg<256, 32, 7, true>(BSArgs);
+template __global__ void k_block_reg<256, 32, 7, false, 8>(BSArgs);
+template __global__ void k_block_reg<256, 32, 7, true, 8>(BSArgs);
 
-template <int B, int T, int NST, bool TRANS>
+template <int B, int T, int NST, bool TRANS, int NCW = 4>
 static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
-  const size_t lds = (size_t)(NST + 1) * T * B * 2;  // ring + 4 output staging tiles
+  const size_t lds = (size_t)(NST + 1) * T * B * 2;  // ring + NCW output staging tiles
   static bool attr = false;
   if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_reg<B, T, NST, TRANS>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_reg<B, T, NST, TRANS, NCW>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return POETX_ERR_HIP;
     attr = true;
   }
   const dim3 grid((unsigned)(a.nb * a.P));
-  return launch(name, s, [&] { k_block_reg<B, T, NST, TRANS><<<grid, 384, lds, s>>>(a); });
+  return launch(name, s, [&] { k_block_reg<B, T, NST, TRANS, NCW><<<grid, 64 * (NCW + 2), lds, s>>>(a); });
 }
 
 template <int B, int SW, int T, bool TRANS>
@@ -328,7 +333,7 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
     if (P > ntile) P = ntile;
     a.P = (int)(P < 1 ? 1 : P);
     if (b == 128) return transposed ? run_br<128, 64, 4, true>(a, name, s) : run_br<128, 64, 4, false>(a, name, s);
-    return transposed ? run_br<256, 32, 7, true>(a, name, s) : run_br<256, 32, 7, false>(a, name, s);
+    return transposed ? run_br<256, 32, 7, true, 8>(a, name, s) : run_br<256, 32, 7, false, 8>(a, name, s);
   }
   const int sw = b == 512 ? 64 : 128, t = b == 512 ? 32 : 64;
   const int64_t slices = (int64_t)a.nb * (b / sw);
