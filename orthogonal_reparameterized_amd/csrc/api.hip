@@ -399,8 +399,8 @@ int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *
   const bool mfma = p.mfma && bs % 128 == 0;
   if (mfma && bs == 512) {
     // At b = 512 each block product is a K = N = 512 GEMM: the 256 x 256 W' kernels,
-    // batched over blocks, read X twice (two column tiles) where a block kernel with a
-    // G slice in LDS reads it once per slice
+    // batched over blocks, read X twice (two column tiles); a block kernel with a
+    // 64-column G slice in LDS read it once per slice and was L2-bound
     MfmaDesc m;
     m.M = p.N; m.N = bs; m.K = bs; m.batch = nb;
     m.A = X; m.a_km = false; m.lda = ld; m.sAb = bs;
@@ -458,7 +458,7 @@ int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y,
 // fp32 partials [P][nb][bs][bs] that are summed later in a fixed order;
 // grad_parts() is P.
 bool grad_streams(const Plan &p, int64_t ld, int64_t nb, int64_t bs) {
-  return p.mfma && bs % 128 == 0 && p.N > 0 && block_stream_supported(bs, ld, nb, p.N);
+  return p.mfma && bs % 128 == 0 && p.N > 0 && block_grad_stream_supported(bs, ld, nb, p.N);
 }
 
 int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of the split-k kernel

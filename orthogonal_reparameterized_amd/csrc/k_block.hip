@@ -5,13 +5,9 @@
 
 namespace poetx {
 
-// Streaming block-diagonal product: Y_j = X_j . G_j (TRANS = false) or X_j . G_j^T
+// Block-diagonal product arguments: Y_j = X_j . G_j (TRANS = false) or X_j . G_j^T
 // (TRANS = true) for every b x b block j, where X_j, Y_j are columns [jb, (j+1)b) of
-// token-major activations.  The op is HBM-bound (about 130 flop per byte at b = 256),
-// so each workgroup keeps one SW-wide slice of G_j resident in LDS and streams
-// T-token tiles of X_j through a 3-stage ring (prefetch distance 2), writing the
-// T x SW output tile straight from the accumulators.  A tile is read by the b/SW
-// slice workgroups of its block; their ids are 8 apart so they share an XCD (and its L2).
+// token-major activations.
 struct BSArgs {
   int64_t N, d;           // tokens, row stride (elements) of X and Y
   int nb, P;              // blocks; workgroups per (block, slice)
@@ -19,116 +15,6 @@ struct BSArgs {
   const float *scaleN;    // per output column (length d) or null
 };
 
-template <int B, int SW, int T, bool TRANS>
-__global__ __launch_bounds__(384) void k_block_stream(BSArgs a) {
-  // waves 0-3 multiply and store; waves 4-5 only issue the global->LDS loads, so the
-  // producers' vmcnt waits track loads alone and the consumers' stores never stall
-  // the ring
-  constexpr int NCW = 4, NPW = 2;
-  constexpr int NSL = B / SW, NST = 3;
-  constexpr int WTM = T / 2, WTN = SW / 2, FM = WTM / 16, FN = WTN / 16;
-  constexpr int G_ELEMS = B * SW, A_ELEMS = T * B;
-  extern __shared__ __align__(16) bf16_t smem[];
-  bf16_t *sG = smem;
-
-  // blockIdx.x = (u / 8) * (8 * NSL) + h * 8 + u % 8 with u = j * P + p
-  const int x = blockIdx.x;
-  const int h = (x / 8) % NSL;
-  const int u = (x / (8 * NSL)) * 8 + x % 8;
-  if (u >= a.nb * a.P) return;
-  const int j = u / a.P, p = u % a.P;
-  const int64_t ntile = (a.N + T - 1) / T;
-
-  const int wave = threadIdx.x >> 6;
-  const bool producer = wave >= NCW;
-  const int wm = ((wave & 3) >> 1) * WTM, wn = (wave & 1) * WTN;
-  const int l = threadIdx.x & 63;
-
-  using LG = typename std::conditional<TRANS, LoaderKC<SW, NPW, B, NCW>, LoaderKM<SW, NPW, B, NCW>>::type;
-  using LXT = LoaderKC<T, NPW, B, NCW>;
-  constexpr int LX = LXT::INSTR;
-  LXT lx;
-  const bf16_t *Xj = a.X + (int64_t)j * B;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xj, a.N * a.d * 2);
-  if (producer) {
-    const bf16_t *Gs = TRANS ? a.G + (int64_t)j * B * B + (int64_t)h * SW * B : a.G + (int64_t)j * B * B + h * SW;
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gs, (int64_t)B * B * 2);
-    LG lg;
-    lg.init(B, 0);
-    lx.init(a.d, 0);
-    lg.issue(rg, 0, B, sG);
-    if (p < ntile) lx.issue(rx, (int64_t)p * T * a.d, a.d, smem + G_ELEMS);
-    if (p + a.P < ntile) lx.issue(rx, (int64_t)(p + a.P) * T * a.d, a.d, smem + G_ELEMS + A_ELEMS);
-  }
-  int64_t tile = p;
-  for (int it = 0; tile < ntile; ++it, tile += a.P) {
-    if (producer) {
-      if (tile + a.P < ntile) wait_vmcnt<LX>();  // this tile (and G) landed; the next may fly
-      else __builtin_amdgcn_s_waitcnt(0);
-    }
-    __syncthreads();  // the tile is in LDS; the stage of tile it-1 is no longer read
-    if (producer) {
-      if (tile + 2 * a.P < ntile)
-        lx.issue(rx, (tile + 2 * a.P) * T * a.d, a.d, smem + G_ELEMS + ((it + 2) % NST) * A_ELEMS);
-      continue;
-    }
-    const bf16_t *ta = smem + G_ELEMS + (it % NST) * A_ELEMS;
-    f32x4 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int jj = 0; jj < FN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k2 = 0; k2 < B; k2 += 64) {
-      bf16x8 fa[2][FM], fb[2][FN];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int ks = k2 + 32 * hh;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[hh][i] = frag_kc<B>(ta, wm + 16 * i, ks);
-#pragma unroll
-        for (int jj = 0; jj < FN; ++jj)
-          fb[hh][jj] = TRANS ? frag_kc<B>(sG, wn + 16 * jj, ks) : frag_km<SW>(sG, wn + 16 * jj, ks);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int jj = 0; jj < FN; ++jj)
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[hh][jj], fa[hh][i], acc[i][jj], 0, 0, 0);
-    }
-    // epilogue: lane holds Y[m = l%16][n = 4*(l/16) + 0..3] of each 16 x 16 patch
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t m = tile * T + wm + 16 * i + (l & 15);
-      if (m >= a.N) continue;
-#pragma unroll
-      for (int jj = 0; jj < FN; ++jj) {
-        const int64_t n = (int64_t)j * B + h * SW + wn + 16 * jj + 4 * (l >> 4);
-        f32x4 v = acc[i][jj];
-        if (a.scaleN) {
-          float4 sc = *(const float4 *)(a.scaleN + n);
-          v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
-        }
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *(uint2 *)(a.Y + m * a.d + n) = pk;
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
-}
-
-#define POETX_BS_INST(Bv, SWv, Tv)                                       \
-  template __global__ void k_block_stream<Bv, SWv, Tv, false>(BSArgs); \
-  template __global__ void k_block_stream<Bv, SWv, Tv, true>(BSArgs);
-POETX_BS_INST(128, 128, 64)
-POETX_BS_INST(256, 128, 64)
-POETX_BS_INST(512, 64, 32)
-#undef POETX_BS_INST
 
 // Register-resident variant for b = 128 and 256: each of the NCW consumer waves keeps
 // its b x (b/NCW) share of G_j (or G_j^T) as MFMA operand fragments in registers for
@@ -272,13 +158,11 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void k_block_reg(BSArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
 }
-// b = 256 uses 32-token tiles (the 128 registers of G leave room for 2 x 4 patches of
-// accumulators) and a 7-stage ring, b = 128 64-token tiles and 4 stages; with the
-// output staging that is 128 or 80 KB of LDS
+// b = 256 uses 8 consumers (64 registers of G each, 2 x 2 accumulator patches), 32-token
+// tiles and a 7-stage ring; b = 128 4 consumers, 64-token tiles and 4 stages.  With the
+// output staging that is 128 or 80 KB of LDS.
 template __global__ void k_block_reg<128, 64, 4, false>(BSArgs);
 template __global__ void k_block_reg<128, 64, 4, true>(BSArgs);
-template __global__ void k_block_reg<256, 32, 7, false>(BSArgs);
-template __global__ void k_block_reg<256, 32, 7, true>(BSArgs);
 template __global__ void k_block_reg<256, 32, 7, false, 8>(BSArgs);
 template __global__ void k_block_reg<256, 32, 7, true, 8>(BSArgs);
 
@@ -296,24 +180,8 @@ static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
   return launch(name, s, [&] { k_block_reg<B, T, NST, TRANS, NCW><<<grid, 64 * (NCW + 2), lds, s>>>(a); });
 }
 
-template <int B, int SW, int T, bool TRANS>
-static int run_bs(const BSArgs &a, const char *name, hipStream_t s) {
-  const size_t lds = ((size_t)B * SW + 3 * (size_t)T * B) * 2;
-  constexpr int NSL = B / SW;
-  const int64_t units = (int64_t)a.nb * a.P;
-  dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_stream<B, SW, T, TRANS>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return POETX_ERR_HIP;
-    attr = true;
-  }
-  return launch(name, s, [&] { k_block_stream<B, SW, T, TRANS><<<grid, 384, lds, s>>>(a); });
-}
-
 bool block_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens) {
-  if (b != 128 && b != 256 && b != 512) return false;
+  if (b != 128 && b != 256) return false;
   if (nb < 1 || nb * b > ld || ld % 8) return false;
   return (n_tokens + 64) * ld * 2 < 0x7fffffff;
 }
@@ -325,25 +193,18 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
   BSArgs a;
   a.N = n_tokens; a.d = ld; a.nb = (int)nb;
   a.X = X; a.G = G; a.Y = Y; a.scaleN = scaleN;
+  const int cus = device_cus() > 0 ? device_cus() : 256;
   if (b == 128 || b == 256) {
     // one workgroup per (token partition, block), about one per CU in total
     const int tt = b == 256 ? 32 : 64;
     const int64_t ntile = (n_tokens + tt - 1) / tt;
-    int64_t P = 256 / a.nb;
+    int64_t P = cus / a.nb;
     if (P > ntile) P = ntile;
     a.P = (int)(P < 1 ? 1 : P);
     if (b == 128) return transposed ? run_br<128, 64, 4, true>(a, name, s) : run_br<128, 64, 4, false>(a, name, s);
     return transposed ? run_br<256, 32, 7, true, 8>(a, name, s) : run_br<256, 32, 7, false, 8>(a, name, s);
   }
-  const int sw = b == 512 ? 64 : 128, t = b == 512 ? 32 : 64;
-  const int64_t slices = (int64_t)a.nb * (b / sw);
-  const int64_t ntile = (n_tokens + t - 1) / t;
-  int64_t P = (256 + slices - 1) / slices;  // about one workgroup per CU in total
-  if (P > ntile) P = ntile;
-  a.P = (int)(P < 1 ? 1 : P);
-  if (b == 128) return transposed ? run_bs<128, 128, 64, true>(a, name, s) : run_bs<128, 128, 64, false>(a, name, s);
-  if (b == 256) return transposed ? run_bs<256, 128, 64, true>(a, name, s) : run_bs<256, 128, 64, false>(a, name, s);
-  return transposed ? run_bs<512, 64, 32, true>(a, name, s) : run_bs<512, 64, 32, false>(a, name, s);
+  return POETX_ERR_UNSUPPORTED;
 }
 
 
@@ -351,7 +212,7 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
 // of Xs_j[t]^T dY_j[t], for every b x b block j (r indexes columns of Xs_j, c of dY_j).
 // Each workgroup owns one 128 x 128 slice (rs, cs) of one block's gradient and keeps it
 // in registers while T-token tiles of both operands stream through a 4-stage LDS ring
-// (producer waves as in k_block_stream).  The P partials per block are summed later in
+// (two producer waves that only issue the global->LDS loads).  The P partials per block are summed later in
 // a fixed order.
 struct BGArgs {
   int64_t N, d;
@@ -465,6 +326,12 @@ static int run_bg(const BGArgs &a, hipStream_t s) {
   return launch("block_grad", s, [&] { k_block_grad_stream<B><<<grid, 384, lds, s>>>(a); });
 }
 
+bool block_grad_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens) {
+  if (b != 128 && b != 256 && b != 512) return false;
+  if (nb < 1 || nb * b > ld || ld % 8) return false;
+  return (n_tokens + 64) * ld * 2 < 0x7fffffff;
+}
+
 int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens) {
   // about one workgroup per CU in a single round: rounding the partition count up would
   // start a second, mostly idle round
@@ -478,7 +345,7 @@ int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens) {
 
 int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t ld, int64_t nb,
                       int64_t b, hipStream_t s) {
-  if (!block_stream_supported(b, ld, nb, n_tokens)) return POETX_ERR_UNSUPPORTED;
+  if (!block_grad_stream_supported(b, ld, nb, n_tokens)) return POETX_ERR_UNSUPPORTED;
   BGArgs a;
   a.N = n_tokens; a.d = ld; a.nb = (int)nb;
   a.P = (int)block_grad_stream_parts(b, nb, n_tokens);
