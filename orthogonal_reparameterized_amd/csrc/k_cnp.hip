@@ -226,17 +226,22 @@ int cnp_mm(const CnpMMArgs &a, hipStream_t s) {
 // only meet at the end of each product, when the panel is replaced.  Only the
 // backward's first half has to finish for every row before the second starts.
 namespace {
-constexpr int RP = 32, CTK = 32, CNTH = 512;
+constexpr int CTK = 32, CNTH = 512;
 
-template <int B>
+// RP: rows per panel (one workgroup).  32 fills the GPU from few blocks; 64 halves the
+// streaming of Q (every panel workgroup streams all of Q once per product) when there
+// are blocks enough for 4 workgroups per CU (b = 128 and 256).
+template <int B, int RP>
 struct ChainCfg {
+  static_assert(RP == 32 || (RP == 64 && B >= 128 && B <= 256), "panel height");
   static constexpr int NK = B / CTK;                  // k steps per product
   static constexpr int NT = B / 16;                   // 16-column tiles of Q
-  static constexpr int WM = B >= 128 ? 2 : 1;         // 16-row tiles per wave
+  static constexpr int WM = B >= 128 ? RP / 16 : 1;   // 16-row tiles per wave
   static constexpr int WN = B >= 128 ? B / 128 : 1;   // 16-column tiles per wave
   // k steps of B fragments in flight per wave: enough bytes in flight to cover the
-  // latency of the first product, whose fragments are not in L2 yet
-  static constexpr int D = B >= 512 ? 2 : (3 * NK < 8 ? 3 * NK : 8);
+  // latency of the first product, whose fragments are not in L2 yet (a 64-row panel
+  // spends twice the MFMAs on each fragment)
+  static constexpr int D = B >= 512 ? 2 : RP == 64 ? 4 : (3 * NK < 8 ? 3 * NK : 8);
   static constexpr int A_LD = B + 8;
   static constexpr int NP = B / RP;                   // panels per block
 };
@@ -254,9 +259,9 @@ __device__ inline void put_split4(bf16_t *h, bf16_t *lo, float4 v) {
 }
 }  // namespace
 
-template <int B, int MODE>
+template <int B, int MODE, int RP>
 __global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
-  using C = ChainCfg<B>;
+  using C = ChainCfg<B, RP>;
   extern __shared__ __align__(16) bf16_t smem[];
   bf16_t *sAh = smem, *sAl = smem + RP * C::A_LD;
 
@@ -302,11 +307,11 @@ __global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
   // ---- start panel
   f32x4 run[C::WM][C::WN];  // BWDA: running 2Gb + 2K1 + ... in accumulator layout
   if constexpr (MODE == CNP_CHAIN_FWD) {
-    // X = Q[rows] + 2I: rows r0.. are k step pnl of the fragment-ordered planes
-    for (int q = tid; q < C::NT * 2 * 64; q += CNTH) {
-      const int ln = q & 63, pl = (q >> 6) & 1, t = q >> 7;
-      const u32x4 v = *(const u32x4 *)(qf + ((pnl * C::NT + t) * 2 + pl) * 512 + ln * 8);
-      bf16_t *dst = (pl ? sAl : sAh) + (8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
+    // X = Q[rows] + 2I: rows r0.. are k steps pnl * RP/32 .. of the fragment-ordered planes
+    for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += CNTH) {
+      const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
+      const u32x4 v = *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8);
+      bf16_t *dst = (pl ? sAl : sAh) + (32 * ks + 8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst[e * C::A_LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
     }
@@ -450,22 +455,24 @@ __global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
   }
 }
 
-#define POETX_CHAIN_INST(B)                                          \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_FWD>(CnpChainArgs);  \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDA>(CnpChainArgs); \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDB>(CnpChainArgs);
-POETX_CHAIN_INST(64)
-POETX_CHAIN_INST(128)
-POETX_CHAIN_INST(256)
-POETX_CHAIN_INST(512)
+#define POETX_CHAIN_INST(B, R)                                              \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_FWD, R>(CnpChainArgs);  \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDA, R>(CnpChainArgs); \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDB, R>(CnpChainArgs);
+POETX_CHAIN_INST(64, 32)
+POETX_CHAIN_INST(128, 32)
+POETX_CHAIN_INST(256, 32)
+POETX_CHAIN_INST(512, 32)
+POETX_CHAIN_INST(128, 64)
+POETX_CHAIN_INST(256, 64)
 #undef POETX_CHAIN_INST
 
 bool cnp_chain_supported(int64_t b) { return b == 64 || b == 128 || b == 256 || b == 512; }
 
 namespace {
-template <int B>
+template <int B, int RP>
 int chain_run(const CnpChainArgs &a, hipStream_t s) {
-  using C = ChainCfg<B>;
+  using C = ChainCfg<B, RP>;
   const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
   const int64_t nwg = nz * C::NP;
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
@@ -480,21 +487,25 @@ int chain_run(const CnpChainArgs &a, hipStream_t s) {
     return launch(a.name, s, [&] { kern<<<dim3((unsigned)nwg), CNTH, lds, s>>>(a); });
   };
   switch (a.mode) {
-    case CNP_CHAIN_FWD: return go(k_cnp_chain<B, CNP_CHAIN_FWD>, 0);
-    case CNP_CHAIN_BWDA: return go(k_cnp_chain<B, CNP_CHAIN_BWDA>, 1);
-    case CNP_CHAIN_BWDB: return go(k_cnp_chain<B, CNP_CHAIN_BWDB>, 2);
+    case CNP_CHAIN_FWD: return go(k_cnp_chain<B, CNP_CHAIN_FWD, RP>, 0);
+    case CNP_CHAIN_BWDA: return go(k_cnp_chain<B, CNP_CHAIN_BWDA, RP>, 1);
+    case CNP_CHAIN_BWDB: return go(k_cnp_chain<B, CNP_CHAIN_BWDB, RP>, 2);
     default: return POETX_ERR_INVALID_ARG;
   }
 }
 }  // namespace
 
 int cnp_chain(const CnpChainArgs &a, hipStream_t s) {
-  if (a.seg[0].nblk + a.seg[1].nblk <= 0) return POETX_OK;
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
+  if (nz <= 0) return POETX_OK;
+  // 64-row panels once they still give 4 workgroups per CU
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const bool tall = nz * (a.b / 64) >= 4 * (int64_t)cus;
   switch (a.b) {
-    case 64: return chain_run<64>(a, s);
-    case 128: return chain_run<128>(a, s);
-    case 256: return chain_run<256>(a, s);
-    case 512: return chain_run<512>(a, s);
+    case 64: return chain_run<64, 32>(a, s);
+    case 128: return tall ? chain_run<128, 64>(a, s) : chain_run<128, 32>(a, s);
+    case 256: return tall ? chain_run<256, 64>(a, s) : chain_run<256, 32>(a, s);
+    case 512: return chain_run<512, 32>(a, s);
     default: return POETX_ERR_UNSUPPORTED;
   }
 }

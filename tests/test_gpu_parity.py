@@ -48,7 +48,10 @@ def _say(*a):
 # last full group of 8 in the workgroup order), b = 192 the per-product MFMA path,
 # b = 32 and 48 the float32 vector-ALU path
 CNP_CASES = [(8, 32, 0.02), (11, 64, 0.03), (19, 128, 0.02), (3, 192, 0.01), (3, 256, 0.01),
-             (2, 512, 0.01), (2, 1024, 0.005)]
+             (2, 512, 0.01), (2, 1024, 0.005),
+             # enough blocks for the 64-row panels (4 workgroups per CU): 517 = 8 * 64 + 5
+             # also leaves blocks past the last full group of 8
+             (517, 128, 0.02), (256, 256, 0.01)]
 
 
 @pytest.mark.parametrize("n,b,std", CNP_CASES + [(5, 48, 0.05)])
