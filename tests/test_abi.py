@@ -90,6 +90,11 @@ def test_validation_codes(B):
     assert fwd(B, layer(B, b=100))[0] == B.POETX_OK
     assert bwd(B, layer(B, b=100))[0] == B.POETX_OK
     assert fwd(B, layer(B, b=1024, d_in=2048, d_out=2048))[0] == B.POETX_OK
+    # widest rows: 64 KB of activations per token (32768 bf16), one step past that is refused
+    assert fwd(B, layer(B, d_in=32768, d_out=256))[0] == B.POETX_OK
+    assert fwd(B, layer(B, d_in=256, d_out=32768))[0] == B.POETX_OK
+    assert fwd(B, layer(B, d_in=32768 + 256, d_out=256))[0] == B.POETX_ERR_UNSUPPORTED
+    assert bwd(B, layer(B, d_in=256, d_out=32768 + 256))[0] == B.POETX_ERR_UNSUPPORTED
     # invalid arguments
     assert fwd(B, layer(B, act=7))[0] == B.POETX_ERR_INVALID_ARG
     assert fwd(B, layer(B, variant=5))[0] == B.POETX_ERR_INVALID_ARG
@@ -127,6 +132,9 @@ def test_validation_codes(B):
     assert B.raw.poetx_merge_perm(None, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG
     assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_I8, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG
     assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, FAKE, None) == B.POETX_ERR_INVALID_ARG
+    # rows of W past 64 KB are refused before any launch
+    assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_BF16, 4, 32768 + 8, None, None, FAKE, None, None,
+                                  None) == B.POETX_ERR_UNSUPPORTED
 
 
 FAKE_OUT = 0x20000  # a second never-dereferenced address (distinct from the layer's W')

@@ -259,6 +259,19 @@ def test_layer_ragged_blocks(B, n, d_in, d_out, b, dt, variant):
     _compare(st, out, ref, TOL_BF16 if dt == "bf16" else TOL_F32_LAYER, f"ragged {d_in}->{d_out} b={b} {variant}")
 
 
+@pytest.mark.parametrize("d_in,d_out", [(32768, 256), (256, 32768)])
+def test_layer_widest_rows(B, d_in, d_out):
+    """64 KB activation rows (the widest the library takes), a few tokens: the element-wise
+    permutation path, a W' product of one tile split along k, 128-block CNP calls."""
+    wl = WL.Workload(99, "widest", 3, d_in, d_out, 256, "bf16", "bf16", "bf16", 0.01, d_in)
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    _say(f"widest rows {d_in}->{d_out}")
+    for variant in ("fast", "mem"):
+        st, out = _run_step(wl, inp, variant)
+        _compare(st, out, ref, TOL_BF16, f"widest {d_in}->{d_out} {variant}")
+
+
 @pytest.mark.parametrize("variant", ["fast", "mem"])
 def test_layer_b1024(B, variant):
     """b = 1024: CNP on the per-product MFMA path, block products on the MFMA engines."""
