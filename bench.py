@@ -256,7 +256,7 @@ def copy_calibration():
 
 KERNEL_SYMBOL = {  # kernel label -> substring of its symbol in traces (workload 3 shapes)
     "gemm_nt": "k_gemm2<0,", "gemm_nn": "k_gemm_pp<1,", "block_apply": "k_block_reg<256,32,7,false,8>",
-    "block_apply_t": "k_block_reg<256,32,7,true,8>", "block_grad": "k_block_grad_stream<256>",
+    "block_apply_t": "k_block_reg<256,32,7,true,8>", "block_grad": "k_block_grad_stream<256,4,64,2>",
 }
 # the dominant kernel's sources: recorded counters stay valid while these are unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "orthogonal_reparameterized_amd", "csrc", f)

@@ -220,9 +220,9 @@ struct BGArgs {
   const bf16_t *Xs; const bf16_t *dY; float *parts;  // parts: [P][nb][b][b]
 };
 
-template <int B>
-__global__ __launch_bounds__(384) void k_block_grad_stream(BGArgs a) {
-  constexpr int NCW = 4, NPW = 2, S = 128, T = 64, NST = 4;
+template <int B, int NST, int T, int NPW>
+__global__ __launch_bounds__(64 * (4 + NPW)) void k_block_grad_stream(BGArgs a) {
+  constexpr int NCW = 4, S = 128, KH = T / 32;
   constexpr int NSL = (B / S) * (B / S);
   constexpr int WT = S / 2, F = WT / 16;  // 2 x 2 waves of 64 x 64
   constexpr int TILE = T * S;             // elements per operand tile
@@ -253,6 +253,7 @@ __global__ __launch_bounds__(384) void k_block_grad_stream(BGArgs a) {
   if (producer) {
     la.init(a.d, 0);
     lb.init(a.d, 0);
+#pragma unroll
     for (int s = 0; s < NST - 1; ++s)
       if (p + (int64_t)s * a.P < ntile) issue(p + (int64_t)s * a.P, s);
   }
@@ -265,32 +266,33 @@ __global__ __launch_bounds__(384) void k_block_grad_stream(BGArgs a) {
   int64_t tile = p;
   for (int it = 0; tile < ntile; ++it, tile += a.P) {
     if (producer) {
-      if (tile + 2 * a.P < ntile) wait_vmcnt<2 * LPT>();
-      else if (tile + a.P < ntile) wait_vmcnt<LPT>();
-      else __builtin_amdgcn_s_waitcnt(0);
+      // tiles it .. it + NST - 2 may be in flight (loads complete in order): wait for
+      // tile it only
+      const int64_t later = (ntile - 1 - tile) / a.P;
+      wait_tiles<LPT, NST - 2>((int)(later < NST - 2 ? later : NST - 2));
     }
     __syncthreads();
     if (producer) {
-      if (tile + 3 * a.P < ntile) issue(tile + 3 * a.P, (it + 3) % NST);
+      const int64_t nx = tile + (int64_t)(NST - 1) * a.P;
+      if (nx < ntile) issue(nx, (it + NST - 1) % NST);
       continue;
     }
     const bf16_t *ta = smem + (2 * (it % NST)) * TILE, *tb = ta + TILE;
-    bf16x8 fa[2][F], fb[2][F];
+    // per 32-token half: its fragments, then its MFMAs (the compiler overlaps the second
+    // half's LDS reads with the first half's MFMAs)
+    bf16x8 fa[KH][F], fb[KH][F];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < KH; ++hh) {
 #pragma unroll
       for (int i = 0; i < F; ++i) fa[hh][i] = frag_km<S>(ta, wm + 16 * i, 32 * hh);
 #pragma unroll
       for (int jj = 0; jj < F; ++jj) fb[hh][jj] = frag_km<S>(tb, wn + 16 * jj, 32 * hh);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int i = 0; i < F; ++i)
 #pragma unroll
         for (int jj = 0; jj < F; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[hh][jj], fa[hh][i], acc[i][jj], 0, 0, 0);
+    }
   }
   if (!producer) {
     float *out = a.parts + ((int64_t)p * a.nb + j) * B * B;
@@ -306,24 +308,26 @@ __global__ __launch_bounds__(384) void k_block_grad_stream(BGArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
 }
-template __global__ void k_block_grad_stream<128>(BGArgs);
-template __global__ void k_block_grad_stream<256>(BGArgs);
-template __global__ void k_block_grad_stream<512>(BGArgs);
+// ring of BG_NST stages of two BG_T-token operand tiles, BG_NPW producer waves
+constexpr int BG_NST = 4, BG_T = 64, BG_NPW = 2;
+template __global__ void k_block_grad_stream<128, BG_NST, BG_T, BG_NPW>(BGArgs);
+template __global__ void k_block_grad_stream<256, BG_NST, BG_T, BG_NPW>(BGArgs);
+template __global__ void k_block_grad_stream<512, BG_NST, BG_T, BG_NPW>(BGArgs);
 
 template <int B>
 static int run_bg(const BGArgs &a, hipStream_t s) {
   constexpr int NSL = (B / 128) * (B / 128);
-  const size_t lds = (size_t)4 * 2 * 64 * 128 * 2;
+  const size_t lds = (size_t)BG_NST * 2 * BG_T * 128 * 2;
   const int64_t units = (int64_t)a.nb * a.P;
   dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
   static bool attr = false;
   if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_grad_stream<B>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_grad_stream<B, BG_NST, BG_T, BG_NPW>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return POETX_ERR_HIP;
     attr = true;
   }
-  return launch("block_grad", s, [&] { k_block_grad_stream<B><<<grid, 384, lds, s>>>(a); });
+  return launch("block_grad", s, [&] { k_block_grad_stream<B, BG_NST, BG_T, BG_NPW><<<grid, 64 * (4 + BG_NPW), lds, s>>>(a); });
 }
 
 bool block_grad_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens) {
@@ -338,7 +342,7 @@ int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens) {
   const int64_t slices = nb * (b / 128) * (b / 128);
   const int cus = device_cus() > 0 ? device_cus() : 256;
   int64_t P = cus / slices;
-  const int64_t ntile = (n_tokens + 63) / 64;
+  const int64_t ntile = (n_tokens + BG_T - 1) / BG_T;
   if (P > ntile) P = ntile;
   return P < 1 ? 1 : P;
 }
