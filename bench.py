@@ -56,8 +56,7 @@ def algorithmic(wl, variant, n):
         add("permute_cols", 0, 2 * n * di * ae)
         add("block_apply", 2.0 * n * di * b, 2 * n * di * ae + g_bytes_r)
         add("gemm_nt", 2.0 * n * di * do, n * di * ae + do * di * we + n * do * ae)
-    if not mem:
-        add("permute_cols", 0, 2 * n * di * ae)          # backward re-gathers X for dG_R
+    # fast keeps the forward's X~ for dG_R (the gather above writes it): no second gather
     add("block_apply", 2.0 * n * do * b, 2 * n * do * ae + g_bytes_p)            # Z~ = B G_P
     add("permute_cols", 0, 2 * n * do * ae)                                       # scatter Z
     add("permute_cols", 0, 2 * n * do * ae)                                       # gather dZ
@@ -434,6 +433,7 @@ def main():
         prof, prof_wall = profile_steps(st, args.steps)
         alg = algorithmic(wl, variant, n)
         variants[variant] = {"ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3), "w_merged_t": keep_wt,
+                             "kept_x": st.saved_x is not None,
                              "layer_roofline_ms": layer_roofline_ms(wl, variant, n),
                              "roofline_frac": layer_roofline_ms(wl, variant, n) / ms,
                              "ms_per_step_with_event_hooks": prof_wall}

@@ -145,12 +145,17 @@ int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *theta, void 
  * L->g_r, L->g_p must hold poetx_cnp(FWD) of L->theta_r, L->theta_p.
  * saved_b: FAST variant -> output B = A.W'^T [N][d_out] in act dtype, kept for
  * the backward (Method §5, POET-X_fast); MEM variant -> must be NULL (B is
- * recomputed in the backward, POET-X_mem).  n_tokens == 0 is a no-op.
+ * recomputed in the backward, POET-X_mem).
+ * saved_x: FAST variant, optional -> output X~ = Gather_in(x) [N][d_in] in act dtype,
+ * kept so that the backward need not gather x again (one more activation copy for one
+ * less pass over x; the pages keep only B).  NULL -> not kept.  Not written when
+ * perm_in is NULL (then X~ = x).  MEM variant -> must be NULL.  n_tokens == 0 is a
+ * no-op.
  * Errors: I8 weight with FAST -> POETX_ERR_UNSUPPORTED (Method §6: POET-XQ
  * builds on the recomputing variant); shape errors -> POETX_ERR_SHAPE.
  */
 int poetx_forward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void *x, void *z,
-                  void *saved_b, void *ws, size_t *ws_bytes, void *stream);
+                  void *saved_b, void *saved_x, void *ws, size_t *ws_bytes, void *stream);
 
 /*
  * poetx_backward -- chain rule through poetx_forward (Method §1: W gets no
@@ -159,15 +164,17 @@ int poetx_forward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void 
  *     dA  = dB . W';          dX~ = dA . Diag(G_R)^T;  dG_R[j] = sum_t X~_j^T dA_j
  *     dx  = Scatter_in(dX~);  dtheta_* = CNP backward of dG_*.
  * saved_b: FAST -> the B written by poetx_forward; MEM -> NULL (recomputed).
+ * saved_x: FAST -> the X~ written by poetx_forward into its saved_x, or NULL (X~ is then
+ * gathered from x again); MEM -> NULL.  Pass the same saved_x to the workspace query.
  * dx [N][d_in] act dtype; dtheta_r, dtheta_p float32 in theta's layout (overwritten,
  * sums over all N tokens).  dg_r, dg_p float32 in G's layout ([n][b][b], then the last
  * block) are optional outputs of the block gradients (NULL = not written).  Reductions over tokens run
  * in a fixed order: results are bitwise reproducible run to run.
  */
 int poetx_backward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void *x,
-                   const void *dz, const void *saved_b, void *dx, float *dtheta_r,
-                   float *dtheta_p, float *dg_r, float *dg_p, void *ws, size_t *ws_bytes,
-                   void *stream);
+                   const void *dz, const void *saved_b, const void *saved_x, void *dx,
+                   float *dtheta_r, float *dtheta_p, float *dg_r, float *dg_p, void *ws,
+                   size_t *ws_bytes, void *stream);
 
 /*
  * poetx_fold -- the consolidation step of merge-then-reinitialize (the POET training

@@ -47,10 +47,10 @@ class PoetxLayerC(ctypes.Structure):
 _lib.poetx_merge_perm.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.poetx_cnp.argtypes = [_i32, _i64, _i64, _vp, _vp, _i32, _vp, _i32, _vp, _vp,
                            ctypes.POINTER(_sz), _vp]
-_lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp,
+_lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp,
                                ctypes.POINTER(_sz), _vp]
 _lib.poetx_backward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp, _vp,
-                                _vp, _vp, _vp, ctypes.POINTER(_sz), _vp]
+                                _vp, _vp, _vp, _vp, ctypes.POINTER(_sz), _vp]
 _lib.poetx_fold.argtypes = [ctypes.POINTER(PoetxLayerC), _vp, _vp, ctypes.POINTER(_sz), _vp]
 _lib.poetx_adam_step.argtypes = [_i64, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                  ctypes.c_float, _i64, ctypes.c_float, _vp]
@@ -214,8 +214,9 @@ class Layer:
 
 
 def poetx_forward(layer: Layer, x: torch.Tensor, z: Optional[torch.Tensor] = None,
-                  saved_b: Optional[torch.Tensor] = None):
-    """Returns (z, saved_b); saved_b is None for the mem variant."""
+                  saved_b: Optional[torch.Tensor] = None, saved_x: Optional[torch.Tensor] = None):
+    """Returns (z, saved_b); saved_b is None for the mem variant.  saved_x (fast variant,
+    optional, [N][d_in]) receives the gathered input for poetx_backward."""
     L = layer.to_c()
     n = x.shape[0]
     dev = x.device
@@ -225,20 +226,21 @@ def poetx_forward(layer: Layer, x: torch.Tensor, z: Optional[torch.Tensor] = Non
     if layer.variant == POETX_MEM:
         saved_b = None
     nbytes = _sz(0)
-    _check(_lib.poetx_forward(ctypes.byref(L), n, None, None, None, None, ctypes.byref(nbytes), None),
-           "poetx_forward(size)")
+    _check(_lib.poetx_forward(ctypes.byref(L), n, None, None, None, _ptr(saved_x), None, ctypes.byref(nbytes),
+                              None), "poetx_forward(size)")
     ws = _workspace(dev, nbytes.value)
     nb = _sz(ws.numel())
-    st = _lib.poetx_forward(ctypes.byref(L), n, _ptr(x), _ptr(z), _ptr(saved_b), _ptr(ws),
+    st = _lib.poetx_forward(ctypes.byref(L), n, _ptr(x), _ptr(z), _ptr(saved_b), _ptr(saved_x), _ptr(ws),
                             ctypes.byref(nb), _stream(dev))
     _check(st, "poetx_forward")
     return z, saved_b
 
 
 def poetx_backward(layer: Layer, x: torch.Tensor, dz: torch.Tensor,
-                   saved_b: Optional[torch.Tensor] = None, *, dx=None, dtheta_r=None, dtheta_p=None,
-                   want_dg: bool = False):
-    """Returns dict(dx, dtheta_r, dtheta_p[, dg_r, dg_p])."""
+                   saved_b: Optional[torch.Tensor] = None, *, saved_x=None, dx=None, dtheta_r=None,
+                   dtheta_p=None, want_dg: bool = False):
+    """Returns dict(dx, dtheta_r, dtheta_p[, dg_r, dg_p]).  saved_x: what poetx_forward wrote
+    into its saved_x, or None."""
     L = layer.to_c()
     n = x.shape[0]
     dev = x.device
@@ -256,11 +258,11 @@ def poetx_backward(layer: Layer, x: torch.Tensor, dz: torch.Tensor,
             dg_r = torch.empty((layer.d_in // b, b, b), dtype=torch.float32, device=dev)
             dg_p = torch.empty((layer.d_out // b, b, b), dtype=torch.float32, device=dev)
     nbytes = _sz(0)
-    _check(_lib.poetx_backward(ctypes.byref(L), n, None, None, None, None, None, None, _ptr(dg_r),
-                               _ptr(dg_p), None, ctypes.byref(nbytes), None), "poetx_backward(size)")
+    _check(_lib.poetx_backward(ctypes.byref(L), n, None, None, None, _ptr(saved_x), None, None, None,
+                               _ptr(dg_r), _ptr(dg_p), None, ctypes.byref(nbytes), None), "poetx_backward(size)")
     ws = _workspace(dev, nbytes.value)
     nb = _sz(ws.numel())
-    st = _lib.poetx_backward(ctypes.byref(L), n, _ptr(x), _ptr(dz), _ptr(saved_b), _ptr(dx),
+    st = _lib.poetx_backward(ctypes.byref(L), n, _ptr(x), _ptr(dz), _ptr(saved_b), _ptr(saved_x), _ptr(dx),
                              _ptr(dtheta_r), _ptr(dtheta_p), _ptr(dg_r), _ptr(dg_p), _ptr(ws),
                              ctypes.byref(nb), _stream(dev))
     _check(st, "poetx_backward")

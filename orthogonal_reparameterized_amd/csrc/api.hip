@@ -623,10 +623,11 @@ struct FwdBufs {
   void *xg = nullptr, *a = nullptr, *bt = nullptr, *zt = nullptr;
 };
 
-// Carve forward intermediates.  `want_b` asks for B in the workspace.
-void carve_fwd(Arena &ar, const Plan &p, const poetx_layer *L, bool want_b, FwdBufs &f) {
+// Carve forward intermediates.  `want_b` asks for B in the workspace; `saved_x` (the
+// caller's buffer for X~, or null) replaces the workspace copy of X~.
+void carve_fwd(Arena &ar, const Plan &p, const poetx_layer *L, bool want_b, void *saved_x, FwdBufs &f) {
   size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
-  if (L->perm_in) f.xg = ar.take(xin);
+  if (L->perm_in) f.xg = saved_x ? saved_x : ar.take(xin);
   f.a = ar.take(xin);
   if (want_b) f.bt = ar.take(xout);
   if (L->perm_out) f.zt = ar.take(xout);
@@ -652,14 +653,14 @@ int run_front(const Plan &p, const poetx_layer *L, const void *x, const FwdBufs 
 }  // namespace
 
 extern "C" int poetx_forward(const poetx_layer *L, int64_t n_tokens, const void *x, void *z,
-                             void *saved_b, void *ws, size_t *ws_bytes, void *stream) {
+                             void *saved_b, void *saved_x, void *ws, size_t *ws_bytes, void *stream) {
   Plan p;
   POETX_TRY(validate(L, n_tokens, p));
   if (!ws_bytes) return POETX_ERR_INVALID_ARG;
-  if (p.mem && saved_b) return POETX_ERR_INVALID_ARG;
+  if (p.mem && (saved_b || saved_x)) return POETX_ERR_INVALID_ARG;
   Arena ar(ws);
   FwdBufs f;
-  carve_fwd(ar, p, L, p.mem, f);
+  carve_fwd(ar, p, L, p.mem, L->perm_in ? saved_x : nullptr, f);
   const size_t tb = tail_fwd_bytes(p);
   void *tail = tb ? ar.take(tb) : nullptr;
   if (!ws) {
@@ -680,17 +681,20 @@ extern "C" int poetx_forward(const poetx_layer *L, int64_t n_tokens, const void 
 }
 
 extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void *x, const void *dz,
-                              const void *saved_b, void *dx, float *dtheta_r, float *dtheta_p,
-                              float *dg_r, float *dg_p, void *ws, size_t *ws_bytes, void *stream) {
+                              const void *saved_b, const void *saved_x, void *dx, float *dtheta_r,
+                              float *dtheta_p, float *dg_r, float *dg_p, void *ws, size_t *ws_bytes,
+                              void *stream) {
   Plan p;
   POETX_TRY(validate(L, n_tokens, p));
   if (!ws_bytes) return POETX_ERR_INVALID_ARG;
-  if (p.mem && saved_b) return POETX_ERR_INVALID_ARG;
+  if (p.mem && (saved_b || saved_x)) return POETX_ERR_INVALID_ARG;
+  // X~ kept by the forward (fast variant with an input permutation), else gathered here
+  const void *kept_xg = L->perm_in ? saved_x : nullptr;
   const int64_t b = p.b, bb = b * b;
   size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
   Arena ar(ws);
   FwdBufs f;
-  carve_fwd(ar, p, L, p.mem, f);
+  carve_fwd(ar, p, L, p.mem, const_cast<void *>(kept_xg), f);
   void *dzt = L->perm_out ? ar.take(xout) : nullptr;
   void *dbuf = ar.take(xout);
   void *da = ar.take(xin);
@@ -727,7 +731,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
     if (p.mem) {
       POETX_TRY(run_front(p, L, x, f, f.bt, tail, tb, s));
       bt = f.bt;
-    } else if (L->perm_in) {
+    } else if (L->perm_in && !kept_xg) {
       POETX_TRY(permute_cols(x, f.xg, p.N, p.din, (int)p.ae, nullptr, L->perm_in, false, s));
     }
     if (L->perm_in) xg = f.xg;

@@ -27,7 +27,7 @@ def upload(arr, dtype: str, device="cuda"):
 
 class LayerStep:
     def __init__(self, wl, inputs: dict, variant: str = "fast", device="cuda", perms: bool = True,
-                 transposed_weight: bool = False):
+                 transposed_weight: bool = False, keep_x: bool = True):
         self.wl = wl
         self.variant = B.POETX_FAST if variant == "fast" else B.POETX_MEM
         act = _TORCH[wl.act]
@@ -74,6 +74,9 @@ class LayerStep:
             self.g_p = torch.empty(self.n_p * b * b + self.l_p ** 2, dtype=act, device=dev)
         self.z = torch.empty((n, wl.d_out), dtype=act, device=dev)
         self.saved_b = torch.empty((n, wl.d_out), dtype=act, device=dev) if self.variant == B.POETX_FAST else None
+        # fast: also keep the gathered input X~ for the backward (no second gather of x)
+        self.saved_x = (torch.empty((n, wl.d_in), dtype=act, device=dev)
+                        if self.variant == B.POETX_FAST and keep_x and self.perm_in is not None else None)
         self.dx = torch.empty((n, wl.d_in), dtype=act, device=dev)
         self.dtheta_r = torch.empty_like(self.theta_r)
         self.dtheta_p = torch.empty_like(self.theta_p)
@@ -97,10 +100,10 @@ class LayerStep:
                             g=g[n * b * b:].view(1, last, last))
 
     def forward(self):
-        B.poetx_forward(self.layer, self.x, self.z, self.saved_b)
+        B.poetx_forward(self.layer, self.x, self.z, self.saved_b, self.saved_x)
 
     def backward(self, want_dg=False):
-        return B.poetx_backward(self.layer, self.x, self.dz, self.saved_b, dx=self.dx,
+        return B.poetx_backward(self.layer, self.x, self.dz, self.saved_b, saved_x=self.saved_x, dx=self.dx,
                                 dtheta_r=self.dtheta_r, dtheta_p=self.dtheta_p, want_dg=want_dg)
 
     def step(self, want_dg=False):

@@ -52,18 +52,20 @@ def layer(B, **kw):
     for f in ("w_merged", "theta_r", "theta_p", "g_r", "g_p"):
         setattr(c, f, kw.get(f, FAKE))
     c.w_scale = kw.get("w_scale", None)
+    c.perm_in = kw.get("perm_in", None)
+    c.perm_out = kw.get("perm_out", None)
     return c
 
 
-def fwd(B, c, n=64, ws=None, ws_bytes=0, x=FAKE, z=FAKE, saved=FAKE):
+def fwd(B, c, n=64, ws=None, ws_bytes=0, x=FAKE, z=FAKE, saved=FAKE, saved_x=None):
     nb = ctypes.c_size_t(ws_bytes)
-    st = B.raw.poetx_forward(ctypes.byref(c), n, x, z, saved, ws, ctypes.byref(nb), None)
+    st = B.raw.poetx_forward(ctypes.byref(c), n, x, z, saved, saved_x, ws, ctypes.byref(nb), None)
     return st, nb.value
 
 
-def bwd(B, c, n=64, ws=None, ws_bytes=0, saved=FAKE, dtr=FAKE, dtp=FAKE):
+def bwd(B, c, n=64, ws=None, ws_bytes=0, saved=FAKE, dtr=FAKE, dtp=FAKE, saved_x=None):
     nb = ctypes.c_size_t(ws_bytes)
-    st = B.raw.poetx_backward(ctypes.byref(c), n, FAKE, FAKE, saved, FAKE, dtr, dtp, None, None, ws,
+    st = B.raw.poetx_backward(ctypes.byref(c), n, FAKE, FAKE, saved, saved_x, FAKE, dtr, dtp, None, None, ws,
                               ctypes.byref(nb), None)
     return st, nb.value
 
@@ -75,6 +77,16 @@ def test_workspace_queries(B):
     assert st == B.POETX_OK and need_mem > need_fast  # mem keeps B in the workspace
     st, need_b = bwd(B, layer(B))
     assert st == B.POETX_OK and need_b > 0
+    # a kept X~ (fast, with an input permutation) replaces the workspace copy: N x d_in bf16 less
+    perm = layer(B, perm_in=FAKE)
+    st, ws_gather = fwd(B, perm)
+    st2, ws_kept = fwd(B, perm, saved_x=FAKE)
+    assert st == st2 == B.POETX_OK and ws_gather - ws_kept == 64 * 512 * 2
+    st, ws_gather = bwd(B, perm)
+    st2, ws_kept = bwd(B, perm, saved_x=FAKE)
+    assert st == st2 == B.POETX_OK and ws_gather - ws_kept == 64 * 512 * 2
+    # without an input permutation there is nothing to keep
+    assert fwd(B, layer(B), saved_x=FAKE)[1] == need_fast
     nb = ctypes.c_size_t(0)
     assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 16, 256, None, None, B.POETX_BF16, None, B.POETX_F32, None,
                            None, ctypes.byref(nb), None) == B.POETX_OK
@@ -103,6 +115,9 @@ def test_validation_codes(B):
     assert fwd(B, ok, ws=FAKE, ws_bytes=1 << 40, x=None)[0] == B.POETX_ERR_INVALID_ARG
     assert fwd(B, ok, ws=FAKE, ws_bytes=1 << 40, saved=None)[0] == B.POETX_ERR_INVALID_ARG
     assert fwd(B, layer(B, variant=B.POETX_MEM))[0] == B.POETX_ERR_INVALID_ARG  # mem with saved_b
+    mem = layer(B, variant=B.POETX_MEM, perm_in=FAKE)
+    assert fwd(B, mem, saved=None, saved_x=FAKE)[0] == B.POETX_ERR_INVALID_ARG  # mem keeps nothing
+    assert bwd(B, mem, saved=None, saved_x=FAKE)[0] == B.POETX_ERR_INVALID_ARG
     assert bwd(B, ok, ws=FAKE, ws_bytes=1 << 40, dtr=None)[0] == B.POETX_ERR_INVALID_ARG
     # unsupported combinations: int8 weight with the fast variant (POET-XQ needs recompute)
     assert fwd(B, layer(B, w=B.POETX_I8, w_scale=FAKE))[0] == B.POETX_ERR_UNSUPPORTED

@@ -161,9 +161,9 @@ def test_merge_bit_exact(B, dt):
 
 # ----------------------------------------------------------------- layer ----
 
-def _run_step(wl, inp, variant, perms=True, transposed_weight=False):
+def _run_step(wl, inp, variant, perms=True, transposed_weight=False, keep_x=True):
     from orthogonal_reparameterized_amd.step import LayerStep
-    st = LayerStep(wl, inp, variant, perms=perms, transposed_weight=transposed_weight)
+    st = LayerStep(wl, inp, variant, perms=perms, transposed_weight=transposed_weight, keep_x=keep_x)
     out = st.step(want_dg=True)
     torch.cuda.synchronize()
     return st, out
@@ -197,6 +197,24 @@ def test_layer_workload1_f32(B, variant):
     ref = oracle_layer(inp, wl)
     st, out = _run_step(wl, inp, variant)
     _compare(st, out, ref, TOL_F32_LAYER, f"workload1 {variant}")
+
+
+@pytest.mark.parametrize("n,d_in,d_out,b", [(257, 512, 768, 256), (8192, 4096, 4096, 256)])
+def test_layer_kept_x_matches_regather(B, n, d_in, d_out, b):
+    """The fast variant's kept X~ (saved_x) must give bit-identical results to gathering x
+    again in the backward: the same kernels read the same values."""
+    wl = WL.Workload(91, "kept x", n, d_in, d_out, b, "bf16", "bf16", "bf16", 0.01, d_in)
+    inp = WL.make_layer_inputs(wl)
+    st0, out0 = _run_step(wl, inp, "fast", keep_x=False)
+    st1, out1 = _run_step(wl, inp, "fast", keep_x=True)
+    assert st0.saved_x is None and st1.saved_x is not None
+    # the kept copy is the gathered input itself
+    xg = st1.x[:, st1.perm_in.long()]
+    assert torch.equal(st1.saved_x, xg)
+    assert torch.equal(st0.z, st1.z)
+    for k in ("dx", "dtheta_r", "dtheta_p", "dg_r", "dg_p"):
+        assert torch.equal(out0[k], out1[k]), k
+    _say(f"kept x {n}x{d_in}->{d_out}: identical to the re-gather")
 
 
 SMALL_BF16 = [
