@@ -85,7 +85,21 @@ static int gemm_generic_b(const GemmDesc &g, hipStream_t s) {
 
 int gemm_generic(const GemmDesc &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return POETX_OK;
-  if (g.batch > 65535 || cdiv(g.M, 64) > 65535) return POETX_ERR_UNSUPPORTED;
+  if (cdiv(g.M, 64) > 65535) return POETX_ERR_UNSUPPORTED;
+  if (g.batch > 65535) {
+    // the batch runs along the grid's z (at most 65535): launch it in chunks
+    for (int64_t z0 = 0; z0 < g.batch; z0 += 65535) {
+      GemmDesc c = g;
+      c.batch = g.batch - z0 < 65535 ? g.batch - z0 : 65535;
+      c.A = (const char *)g.A + z0 * g.sAb * (int64_t)dtype_size(g.a_dt);
+      c.B = (const char *)g.B + z0 * g.sBb * (int64_t)dtype_size(g.b_dt);
+      c.C = (char *)g.C + z0 * g.sCb * (int64_t)dtype_size(g.c_dt);
+      if (g.D) c.D = g.D + z0 * g.sDb;
+      if (g.scaleN) c.scaleN = g.scaleN + z0 * g.sSNb;
+      POETX_TRY(gemm_generic(c, s));
+    }
+    return POETX_OK;
+  }
   switch (g.a_dt) {
     case POETX_F32: return gemm_generic_b<float>(g, s);
     case POETX_BF16: return gemm_generic_b<bf16_t>(g, s);
@@ -377,13 +391,21 @@ __device__ inline int64_t triu_index(int64_t r, int64_t c, int64_t b) {
   return r * b - r * (r + 1) / 2 + (c - r - 1);
 }
 
+// Tile (rb, cb), rb <= cb, of the upper triangle from the linear index of the upper tiles
+// of a T x T tile grid (row-major over rb, then cb = rb .. T-1).
+__device__ inline void upper_tile(int idx, int T, int &rb, int &cb) {
+  rb = 0;
+  while (idx >= T - rb) { idx -= T - rb; ++rb; }
+  cb = rb + idx;
+}
+
 // Both kernels walk 32 x 32 tiles (rb <= cb) of the upper triangle and handle the
 // mirrored tile through LDS, so every global access is contiguous along a row.
 __global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
   __shared__ float t[32][33];
-  const int rb = blockIdx.y, cb = blockIdx.x;
-  if (cb < rb) return;
-  int64_t z = blockIdx.z;
+  int rb, cb;
+  upper_tile((int)blockIdx.y, (int)((b + 31) / 32), rb, cb);
+  int64_t z = blockIdx.x;
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
   const float *th = sg.src[si] + z * (b * (b - 1) / 2);
@@ -409,55 +431,62 @@ __global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
   }
 }
 
-// Fragment-order planes (b % 32 == 0): workgroup (cb, rb) builds the 32 x 32 tile of
-// Q at rows 32 rb.., columns 32 cb.. from the upper-triangle tile it mirrors (read
-// along theta's rows, transposed through LDS when rb > cb), then writes it as four
-// 1 KB fragment chunks (2 column tiles x 2 planes), 16 bytes per thread.
+// Fragment-order planes (b % 32 == 0): workgroup (u, z) reads the upper-triangle tile
+// (rb, cb), rb <= cb, of theta along its rows into LDS, then writes the 32 x 32 tile of Q
+// at rows 32 rb.., columns 32 cb.. and, off the diagonal, its mirror at (cb, rb) (the
+// negated transpose), each as four 1 KB fragment chunks (2 column tiles x 2 planes), 16
+// bytes per thread.
 __global__ __launch_bounds__(256) void k_unpack_frag(SkewSegs sg, int64_t b) {
   __shared__ float t[32][33];
-  const int rb = blockIdx.y, cb = blockIdx.x;
-  int64_t z = blockIdx.z;
+  int rb, cb;
+  upper_tile((int)blockIdx.y, (int)((b + 31) / 32), rb, cb);
+  int64_t z = blockIdx.x;
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
   const float *th = sg.src[si] + z * (b * (b - 1) / 2);
-  const int ur = rb < cb ? rb : cb, uc = rb < cb ? cb : rb;
   const int tid = threadIdx.x, tc = tid & 31;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tr = (tid >> 5) + 8 * i;
-    const int64_t r = ur * 32 + tr, c = uc * 32 + tc;
+    const int64_t r = rb * 32 + tr, c = cb * 32 + tc;
     t[tr][tc] = r < c ? th[triu_index(r, c, b)] : 0.f;
   }
   __syncthreads();
   const int tt = tid >> 7, pl = (tid >> 6) & 1, ln = tid & 63;
   const int col = 16 * tt + (ln & 15);
-  uint32_t w[4];
+  bf16_t *base = sg.planes[si] + 2 * z * b * b + pl * 512 + ln * 8;
+  // mir = 0: the tile at (rb, cb); mir = 1: its mirror at (cb, rb)
+  for (int mir = 0; mir < (rb < cb ? 2 : 1); ++mir) {
+    uint32_t w[4];
 #pragma unroll
-  for (int e2 = 0; e2 < 4; ++e2) {
-    uint32_t h2 = 0;
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t h2 = 0;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int row = 8 * (ln >> 4) + 2 * e2 + hf;
-      // Q[r][c] = theta(r, c) above the diagonal, -theta(c, r) below, 0 on it
-      float v;
-      if (rb < cb) v = t[row][col];
-      else if (rb > cb) v = -t[col][row];
-      else v = row < col ? t[row][col] : (row > col ? -t[col][row] : 0.f);
-      const bf16_t hi = f32_to_bf16(v);
-      const bf16_t q = pl ? f32_to_bf16(v - bf16_to_f32(hi)) : hi;
-      h2 |= (uint32_t)q << (16 * hf);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = 8 * (ln >> 4) + 2 * e2 + hf;
+        // Q[r][c] = theta(r, c) above the diagonal, -theta(c, r) below, 0 on it
+        float v;
+        if (mir) v = -t[col][row];
+        else if (rb < cb) v = t[row][col];
+        else v = row < col ? t[row][col] : (row > col ? -t[col][row] : 0.f);
+        const bf16_t hi = f32_to_bf16(v);
+        const bf16_t q = pl ? f32_to_bf16(v - bf16_to_f32(hi)) : hi;
+        h2 |= (uint32_t)q << (16 * hf);
+      }
+      w[e2] = h2;
     }
-    w[e2] = h2;
+    const int r0 = 32 * (mir ? cb : rb), c0 = 32 * (mir ? rb : cb);
+    *(uint4 *)(base + cnp_frag_off(r0, c0 + 16 * tt, b)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  bf16_t *dst = sg.planes[si] + 2 * z * b * b + cnp_frag_off(32 * rb, 32 * cb + 16 * tt, b) + pl * 512 + ln * 8;
-  *(uint4 *)dst = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   const int64_t nz = sg.n[0] + sg.n[1];
   if (nz <= 0) return POETX_OK;
+  // blocks along x (no 65535 limit), the upper 32 x 32 tiles of a block along y
+  if (nz > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
   const unsigned T = (unsigned)cdiv(b, 32);
-  const dim3 grid(T, T, (unsigned)nz);
+  const dim3 grid((unsigned)nz, T * (T + 1) / 2);
   if (sg.planes[0]) {
     if (b % 32) return POETX_ERR_UNSUPPORTED;
     return launch("unpack_skew", s, [&] { k_unpack_frag<<<grid, 256, 0, s>>>(sg, b); });
@@ -473,9 +502,9 @@ int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t 
 
 __global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b) {
   __shared__ float up[32][33], lo[32][33];
-  const int rb = blockIdx.y, cb = blockIdx.x;
-  if (cb < rb) return;
-  int64_t z = blockIdx.z;
+  int rb, cb;
+  upper_tile((int)blockIdx.y, (int)((b + 31) / 32), rb, cb);
+  int64_t z = blockIdx.x;
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
   const float *M = sg.src[si] + z * b * b;
@@ -501,8 +530,9 @@ __global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b) 
 int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   const int64_t nz = sg.n[0] + sg.n[1];
   if (nz <= 0) return POETX_OK;
+  if (nz > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
   const unsigned T = (unsigned)cdiv(b, 32);
-  return launch("pack_skew_grad", s, [&] { k_pack_skew_grad<<<dim3(T, T, (unsigned)nz), 256, 0, s>>>(sg, b); });
+  return launch("pack_skew_grad", s, [&] { k_pack_skew_grad<<<dim3((unsigned)nz, T * (T + 1) / 2), 256, 0, s>>>(sg, b); });
 }
 
 int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s) {
@@ -544,9 +574,34 @@ __global__ void k_reduce_parts(const float *__restrict__ in, float *__restrict__
   out[e] = acc;
 }
 
+// Same sums, 4 elements per thread, the loads of four partials in flight at a time; the
+// additions keep the order p = 0, 1, ... of the scalar kernel.
+__global__ void k_reduce_parts4(const float4 *__restrict__ in, float4 *__restrict__ out, int64_t n4,
+                                int64_t parts, int64_t stride4) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n4) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](const float4 v) { acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w; };
+  int64_t p = 0;
+  for (; p + 4 <= parts; p += 4) {
+    const float4 v0 = in[p * stride4 + e], v1 = in[(p + 1) * stride4 + e];
+    const float4 v2 = in[(p + 2) * stride4 + e], v3 = in[(p + 3) * stride4 + e];
+    add(v0); add(v1); add(v2); add(v3);
+  }
+  for (; p < parts; ++p) add(in[p * stride4 + e]);
+  out[e] = acc;
+}
+
 int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int64_t stride,
                  hipStream_t s) {
   if (elems <= 0) return POETX_OK;
+  if (elems % 4 == 0 && stride % 4 == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0) {
+    const int64_t n4 = elems / 4;
+    return launch("reduce_parts", s, [&] {
+      k_reduce_parts4<<<(unsigned)cdiv(n4, 256), 256, 0, s>>>((const float4 *)in, (float4 *)out, n4, parts,
+                                                              stride / 4);
+    });
+  }
   return launch("reduce_parts", s, [&] {
     k_reduce_parts<<<(unsigned)cdiv(elems, 256), 256, 0, s>>>(in, out, elems, parts, stride);
   });

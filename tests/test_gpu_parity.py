@@ -118,6 +118,25 @@ def test_cnp_workload2_sampled(B):
     assert rel_fro_per_block(to_host_f64(d[torch.from_numpy(idx).cuda()]), ref_d) <= TOL_CNP_F32
 
 
+@pytest.mark.parametrize("b", [2, 32, 64])
+def test_cnp_many_blocks(B, b):
+    """More blocks than a grid's y or z dimension holds (65535): the vector-ALU path (b = 2,
+    32) and the chains (b = 64), forward and backward, on sampled blocks either side of it."""
+    n = 66000
+    _say(f"cnp many blocks n={n} b={b}")
+    theta, dg = WL.make_cnp_inputs(n, b, 0.02, seed=400 + b)
+    th_d = torch.from_numpy(theta).cuda()
+    g = B.poetx_cnp(B.POETX_CNP_FWD, th_d, b, g_dtype=torch.float32)
+    d = B.poetx_cnp(B.POETX_CNP_BWD, th_d, b, dg=torch.from_numpy(dg).cuda())
+    torch.cuda.synchronize()
+    idx = np.array([0, 1, 65534, 65535, 65536, n - 1])
+    sel = torch.from_numpy(idx).cuda()
+    ref_g = O.cnp_forward(theta[idx].astype(np.float64), b)
+    assert rel_fro_per_block(to_host_f64(g[sel]), ref_g) <= TOL_CNP_F32
+    ref_d = O.cnp_backward(theta[idx].astype(np.float64), dg[idx].astype(np.float64), b)
+    assert rel_fro_per_block(to_host_f64(d[sel]), ref_d) <= TOL_CNP_F32
+
+
 # ----------------------------------------------------------------- merge ----
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "i8"])
