@@ -463,11 +463,20 @@ bool grad_streams(const Plan &p, int64_t ld, int64_t nb, int64_t bs) {
 
 int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of the split-k kernel
   if (p.N == 0) return 1;
-  if (!p.mfma) return p.N;
-  if (bs % 128) return p.N < 1024 ? p.N : 1024;  // vector-ALU product, one launch per chunk group
+  if (!p.mfma || bs % 128) {
+    // vector-ALU product, one launch per chunk: chunks of 1024 tokens keep each float32
+    // accumulation short (a sum over millions of tokens in one chain loses digits), with
+    // at most 4096 partials and 256 MB of them
+    const int64_t part_bytes = nb * bs * bs * 4;
+    int64_t pmax = ((int64_t)256 << 20) / (part_bytes > 0 ? part_bytes : 1);
+    pmax = pmax < 1 ? 1 : pmax > 4096 ? 4096 : pmax;
+    const int64_t kc = cdiv(p.N, pmax);
+    return p.N <= 1024 ? p.N : kc > 1024 ? kc : 1024;
+  }
   int64_t tiles = nb * (bs / 128) * (bs / 128);
   int64_t want = cdiv(512, tiles);
   int64_t kc = cdiv(cdiv(p.N, want), 64) * 64;
+  if (kc > kMaxChain) kc = kMaxChain;  // keep each float32 accumulation chain bounded
   return kc < 256 ? 256 : kc;
 }
 

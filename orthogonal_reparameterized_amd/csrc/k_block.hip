@@ -342,6 +342,9 @@ int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens) {
   const int64_t slices = nb * (b / 128) * (b / 128);
   const int cus = device_cus() > 0 ? device_cus() : 256;
   int64_t P = cus / slices;
+  // more partitions past kMaxChain tokens each: a float32 accumulation over millions of
+  // tokens in one chain loses digits
+  if (P < cdiv(n_tokens, kMaxChain)) P = cdiv(n_tokens, kMaxChain);
   const int64_t ntile = (n_tokens + BG_T - 1) / BG_T;
   if (P > ntile) P = ntile;
   return P < 1 ? 1 : P;

@@ -85,7 +85,19 @@ static int gemm_generic_b(const GemmDesc &g, hipStream_t s) {
 
 int gemm_generic(const GemmDesc &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return POETX_OK;
-  if (cdiv(g.M, 64) > 65535) return POETX_ERR_UNSUPPORTED;
+  if (cdiv(g.N, 64) > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
+  constexpr int64_t MCH = 65535 * 64;  // rows per launch: 64-row tiles along the grid's y
+  if (g.M > MCH) {
+    for (int64_t m0 = 0; m0 < g.M; m0 += MCH) {
+      GemmDesc c = g;
+      c.M = g.M - m0 < MCH ? g.M - m0 : MCH;
+      c.A = (const char *)g.A + m0 * g.sAm * (int64_t)dtype_size(g.a_dt);
+      c.C = (char *)g.C + m0 * g.sCm * (int64_t)dtype_size(g.c_dt);
+      if (g.D) c.D = g.D + m0 * g.sDm;
+      POETX_TRY(gemm_generic(c, s));
+    }
+    return POETX_OK;
+  }
   if (g.batch > 65535) {
     // the batch runs along the grid's z (at most 65535): launch it in chunks
     for (int64_t z0 = 0; z0 < g.batch; z0 += 65535) {

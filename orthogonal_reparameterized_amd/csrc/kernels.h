@@ -122,6 +122,9 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
 // with P = block_grad_stream_parts(b, nb, n_tokens); n_tokens >= 1.
 bool block_grad_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens);
 int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens);
+// most tokens one float32 accumulator of a block gradient sums before its partial is
+// written (the partials are then summed in a fixed order)
+constexpr int64_t kMaxChain = 65536;
 int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t n_tokens, int64_t ld, int64_t nb,
                       int64_t b, hipStream_t s);
 // the direct-to-LDS kernel where it applies, else the register-staged one

@@ -236,6 +236,63 @@ def test_layer_kept_x_matches_regather(B, n, d_in, d_out, b):
     _say(f"kept x {n}x{d_in}->{d_out}: identical to the re-gather")
 
 
+def test_layer_f32_over_four_million_tokens(B):
+    """fp32 layer (float32 vector-ALU products) past 65535 x 64 = 4194240 tokens, the rows one
+    launch of those products covers: 61 oracle tokens tiled 68760 times.  Z and dX repeat the
+    oracle's per-token values; dG and dtheta are 68760 times the oracle's (sums over tokens).
+    Tolerance for the sums, relative to their largest magnitude: 1024-token chunks summed in
+    float32, then 4096 partials summed in order, (1024 + 4096 / 2) x 2^-24 = 1.8e-4; the
+    test allows 3e-4 (measured about 1e-5)."""
+    n0, k = 61, 68760
+    wl = WL.Workload(92, "tiled f32", n0, 64, 64, 32, "f32", "f32", "f32", 0.02, 64)
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    big = dict(inp, x=np.tile(inp["x"], (k, 1)), dz=np.tile(inp["dz"], (k, 1)))
+    _say(f"tiled f32 layer: {n0 * k} tokens")
+    for variant in ("fast", "mem"):
+        st, out = _run_step(wl, big, variant)
+        z = st.z.view(k, n0, wl.d_out).double()
+        dx = out["dx"].view(k, n0, wl.d_in).double()
+        for name, got, r in (("Z", z, ref["Z"]), ("dX", dx, ref["dX"])):
+            rt = torch.from_numpy(np.asarray(r, dtype=np.float64)).cuda()
+            err = ((got - rt).abs().max() / rt.abs().max()).item()
+            assert err <= TOL_F32_LAYER, f"{variant} {name}: {err}"
+        errs, scale = {}, {}
+        for key, rkey in (("dtheta_r", "dtheta_R"), ("dtheta_p", "dtheta_P"), ("dg_r", "dG_R"), ("dg_p", "dG_P")):
+            got, want = flat(to_host_f64(out[key])), k * flat(ref[rkey])
+            errs[key] = float(np.max(np.abs(got - want)))
+            scale[key] = float(np.max(np.abs(want)))
+        _say(f"tiled f32 layer {variant}: max abs errors {errs} max abs values {scale}")
+        for key in errs:
+            assert errs[key] <= 3e-4 * scale[key], f"{variant} {key}: {errs[key] / scale[key]}"
+        _say(f"tiled f32 layer {variant}: ok")
+        del st, out
+        torch.cuda.empty_cache()
+
+
+def test_layer_bf16_long_token_sums(B):
+    """bf16 layer at 4096 -> 4096, b = 256, 268800 tokens (64 oracle tokens tiled 4200 times):
+    past 4 partitions x 65536 tokens, so the streaming block gradient splits its token sums
+    into more partials.  Z and dX repeat the oracle's per-token values; dG and dtheta are
+    4200 times the oracle's, within the bf16 layer bar."""
+    n0, k = 64, 4200
+    wl = WL.Workload(93, "tiled bf16", n0, 4096, 4096, 256, "bf16", "bf16", "bf16", 0.01, 4096)
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    big = dict(inp, x=np.tile(inp["x"], (k, 1)), dz=np.tile(inp["dz"], (k, 1)))
+    _say(f"tiled bf16 layer: {n0 * k} tokens")
+    st, out = _run_step(wl, big, "fast")
+    for name, got, r in (("Z", st.z, ref["Z"]), ("dX", out["dx"], ref["dX"])):
+        g = got.view(k, n0, -1).float()
+        rt = torch.from_numpy(np.asarray(r, dtype=np.float32)).cuda()
+        err = ((g - rt).abs().max() / rt.abs().max()).item()
+        assert err <= TOL_BF16, f"{name}: {err}"
+    for key, rkey in (("dtheta_r", "dtheta_R"), ("dtheta_p", "dtheta_P"), ("dg_r", "dG_R"), ("dg_p", "dG_P")):
+        err = norm_max_err(flat(to_host_f64(out[key])), k * flat(ref[rkey]))
+        assert err <= TOL_BF16, f"{key}: {err}"
+    _say("tiled bf16 layer: ok")
+
+
 SMALL_BF16 = [
     # (n_tokens, d_in, d_out, b, perms) -- several 128-wide tiles and ragged token tails
     (257, 512, 768, 256, True),
