@@ -411,13 +411,31 @@ __device__ inline void upper_tile(int idx, int T, int &rb, int &cb) {
   cb = rb + idx;
 }
 
+// Block z and upper tile (rb, cb) of 1-D workgroup L over nz blocks of T x T tiles.  All
+// tiles of one block run on one XCD (workgroup L runs on XCD L % 8): neighbouring tiles
+// share the cache lines at their edges (a row of packed theta runs across them), which
+// then meet in one L2 instead of being written back in parts by several.
+__device__ inline void block_tile(int64_t L, int64_t nz, int T, int64_t &z, int &rb, int &cb) {
+  const int64_t NT = (int64_t)T * (T + 1) / 2, nz8 = nz & ~(int64_t)7;
+  int64_t idx;
+  if (L < nz8 * NT) {
+    const int64_t slot = L >> 3;
+    z = (L & 7) + 8 * (slot / NT);
+    idx = slot % NT;
+  } else {
+    z = L / NT;
+    idx = L % NT;
+  }
+  upper_tile((int)idx, T, rb, cb);
+}
+
 // Both kernels walk 32 x 32 tiles (rb <= cb) of the upper triangle and handle the
 // mirrored tile through LDS, so every global access is contiguous along a row.
 __global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
   __shared__ float t[32][33];
   int rb, cb;
-  upper_tile((int)blockIdx.y, (int)((b + 31) / 32), rb, cb);
-  int64_t z = blockIdx.x;
+  int64_t z;
+  block_tile(blockIdx.x, sg.n[0] + sg.n[1], (int)((b + 31) / 32), z, rb, cb);
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
   const float *th = sg.src[si] + z * (b * (b - 1) / 2);
@@ -451,8 +469,8 @@ __global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
 __global__ __launch_bounds__(256) void k_unpack_frag(SkewSegs sg, int64_t b) {
   __shared__ float t[32][33];
   int rb, cb;
-  upper_tile((int)blockIdx.y, (int)((b + 31) / 32), rb, cb);
-  int64_t z = blockIdx.x;
+  int64_t z;
+  block_tile(blockIdx.x, sg.n[0] + sg.n[1], (int)((b + 31) / 32), z, rb, cb);
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
   const float *th = sg.src[si] + z * (b * (b - 1) / 2);
@@ -495,10 +513,10 @@ __global__ __launch_bounds__(256) void k_unpack_frag(SkewSegs sg, int64_t b) {
 int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   const int64_t nz = sg.n[0] + sg.n[1];
   if (nz <= 0) return POETX_OK;
-  // blocks along x (no 65535 limit), the upper 32 x 32 tiles of a block along y
-  if (nz > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
-  const unsigned T = (unsigned)cdiv(b, 32);
-  const dim3 grid((unsigned)nz, T * (T + 1) / 2);
+  // one workgroup per upper 32 x 32 tile of every block, 1-D (see block_tile)
+  const int64_t T = cdiv(b, 32), nwg = nz * (T * (T + 1) / 2);
+  if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)nwg);
   if (sg.planes[0]) {
     if (b % 32) return POETX_ERR_UNSUPPORTED;
     return launch("unpack_skew", s, [&] { k_unpack_frag<<<grid, 256, 0, s>>>(sg, b); });
@@ -515,8 +533,8 @@ int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t 
 __global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b) {
   __shared__ float up[32][33], lo[32][33];
   int rb, cb;
-  upper_tile((int)blockIdx.y, (int)((b + 31) / 32), rb, cb);
-  int64_t z = blockIdx.x;
+  int64_t z;
+  block_tile(blockIdx.x, sg.n[0] + sg.n[1], (int)((b + 31) / 32), z, rb, cb);
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
   const float *M = sg.src[si] + z * b * b;
@@ -542,9 +560,9 @@ __global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b) 
 int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   const int64_t nz = sg.n[0] + sg.n[1];
   if (nz <= 0) return POETX_OK;
-  if (nz > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
-  const unsigned T = (unsigned)cdiv(b, 32);
-  return launch("pack_skew_grad", s, [&] { k_pack_skew_grad<<<dim3((unsigned)nz, T * (T + 1) / 2), 256, 0, s>>>(sg, b); });
+  const int64_t T = cdiv(b, 32), nwg = nz * (T * (T + 1) / 2);
+  if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
+  return launch("pack_skew_grad", s, [&] { k_pack_skew_grad<<<dim3((unsigned)nwg), 256, 0, s>>>(sg, b); });
 }
 
 int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s) {
