@@ -66,8 +66,9 @@ def algorithmic(wl, variant, n):
     add("block_apply_t", 2.0 * n * di * b, 2 * n * di * ae + g_bytes_r)          # dX~
     add("permute_cols", 0, 2 * n * di * ae)                                       # scatter dX
     add("block_grad", 2.0 * n * di * b, 2 * n * di * ae)                          # dG_R
-    # CNP, both sides (nb blocks): the forward chain G = (((Q+2I)Q+2I)Q+2I)Q + I and each
-    # of the two backward chains run 3 float32-accurate b^3 products (2 b^3 flops each).
+    # CNP, both sides (nb blocks): the forward chain G = (((Q+2I)Q+2I)Q+2I)Q + I runs 3
+    # float32-accurate b^3 products (2 b^3 flops each); the backward 8 in one fused launch
+    # when the blocks fill the GPU, else 3 + 3 in two chain launches.
     # Bytes are the method's minimum: theta in and G out (forward), theta and dG in and
     # dtheta out (backward, split over its two launches); the unpack and pack launches
     # carry the theta / dtheta side.
@@ -75,8 +76,11 @@ def algorithmic(wl, variant, n):
     p, bb = b * (b - 1) // 2, b * b
     add("unpack_skew", 0, 2 * nb * 4 * p)
     add("cnp_fwd_chain", 6.0 * b ** 3 * nb, nb * ae * bb)
-    add("cnp_bwd_chain_a", 6.0 * b ** 3 * nb, nb * 4 * bb)
-    add("cnp_bwd_chain_b", 6.0 * b ** 3 * nb, 0)
+    if nb * (b // 64) >= 4 * 256:
+        add("cnp_bwd_fused", 16.0 * b ** 3 * nb, nb * 4 * bb)   # 8 products in one launch
+    else:
+        add("cnp_bwd_chain_a", 6.0 * b ** 3 * nb, nb * 4 * bb)  # few blocks: two launches
+        add("cnp_bwd_chain_b", 6.0 * b ** 3 * nb, 0)
     add("pack_skew_grad", 0, nb * 4 * p)
     return ops
 

@@ -218,7 +218,29 @@ struct CnpBwdSide {
   float *dtheta = nullptr;
 };
 
-// CNP backward of up to two independent sides sharing b (the R and P sides of a layer).
+// CNP backward of up to two independent sides sharing b (the R and P sides of a layer):
+// unpack Q, then the whole adjoint in one fused launch, then pack dtheta.
+int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
+  Arena ar(ws);
+  SkewSegs un, pk;
+  CnpChainArgs c;
+  c.b = (int)b;
+  c.name = "cnp_bwd_fused";
+  for (int i = 0; i < nside; ++i) {
+    const size_t blk = (size_t)side[i].n * b * b * 4;
+    un.src[i] = side[i].theta; un.n[i] = side[i].n;
+    un.planes[i] = (bf16_t *)ar.take(blk);
+    c.seg[i].qp = un.planes[i]; c.seg[i].dg = side[i].dg; c.seg[i].nblk = side[i].n;
+    c.seg[i].out = (float *)ar.take(blk);
+    pk.src[i] = c.seg[i].out; pk.dst[i] = side[i].dtheta; pk.n[i] = side[i].n;
+  }
+  POETX_TRY(unpack_skew2(un, b, s));
+  POETX_TRY(cnp_bwd_fused(c, s));
+  return pack_skew_grad2(pk, b, s);
+}
+
+// The same in two chain launches (b = 512, and few blocks), with the three R_j^T through
+// memory.
 int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
   Arena ar(ws);
   SkewSegs un, pk;
@@ -250,6 +272,9 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStre
   // takes the vector-ALU path
   bool vec = true;
   for (int i = 0; i < nside; ++i) vec = vec && al16(side[i].dg);
+  int64_t nz = 0;
+  for (int i = 0; i < nside; ++i) nz += side[i].n;
+  if (vec && cnp_bwd_fused_supported(b, nz)) return cnp_bwd_fused_path(b, side, nside, ws, s);
   if (vec && cnp_chain_supported(b)) return cnp_bwd_chain(b, side, nside, ws, s);
   Arena ar(ws);
   struct Bufs { float *Q, *K1, *K2, *K3, *Ha, *Hb; } B[2] = {};

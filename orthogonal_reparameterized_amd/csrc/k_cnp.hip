@@ -467,7 +467,215 @@ POETX_CHAIN_INST(128, 64)
 POETX_CHAIN_INST(256, 64)
 #undef POETX_CHAIN_INST
 
+// ========================================================== fused backward ====
+// The adjoint of eq. 9 regrouped so that one workgroup finishes a row panel C of Qbar^T
+// alone.  With U_j = Q^j[C,:] (U_0 = I[C,:]) and W_0 = Gb^T[C,:]:
+//     W_j = W_{j-1} Q + U_j Gb^T   (j = 1, 2, 3),    Qbar^T[C,:] = W_3 + 2 (W_0 + W_1 + W_2)
+// (expanding gives sum_{i+j<=3} c_{i+j+1} U_j Gb^T Q^i, the adjoint of I + sum_k c_k Q^k with
+// c = 2, 2, 2, 1).  Phase j makes W_j and, for j < 3, U_{j+1} = U_j Q: the W and U panels
+// stay in LDS as split planes, both B operands (Q from the fragment-ordered planes, Gb^T
+// read as rows of Gb and split in registers) stream once per phase, and nothing between
+// the phases goes through memory.  Eight products, against six in the two chain launches
+// whose three intermediates R_j^T make a round trip through HBM.
+template <int B, int RP>
+struct FusedCfg {
+  static_assert(RP == 32 || RP == 64, "panel height");
+  static constexpr int NK = B / CTK;
+  static constexpr int NT = B / 16;
+  static constexpr int WM = B >= 128 ? RP / 16 : 1;
+  static constexpr int WN = B >= 128 ? B / 128 : 1;
+  static constexpr int D = RP == 64 ? 2 : 3;  // k steps of both B operands in flight
+  static constexpr int A_LD = B + 8;
+  static constexpr int NP = B / RP;
+};
+
+template <int B, int RP>
+__global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
+  using C = FusedCfg<B, RP>;
+  extern __shared__ __align__(16) bf16_t smem[];
+  bf16_t *sWh = smem, *sWl = smem + RP * C::A_LD;
+  bf16_t *sUh = smem + 2 * RP * C::A_LD, *sUl = smem + 3 * RP * C::A_LD;
+
+  // 1-D grid, all panels of one block on one XCD (workgroup L runs on XCD L % 8)
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk, nz8 = nz & ~(int64_t)7;
+  const int64_t L = blockIdx.x;
+  int64_t z, pnl;
+  if (L < nz8 * C::NP) {
+    const int64_t slot = L >> 3;
+    z = (L & 7) + 8 * (slot / C::NP);
+    pnl = slot % C::NP;
+  } else {
+    z = L / C::NP;
+    pnl = L % C::NP;
+  }
+  int sg = 0;
+  if (z >= a.seg[0].nblk) { z -= a.seg[0].nblk; sg = 1; }
+  const CnpChainSeg &S = a.seg[sg];
+  const int64_t off = z * (int64_t)B * B;
+  const int r0 = (int)pnl * RP;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int mb = B >= 128 ? 0 : 16 * (wave >> 2);
+  const int nb = B >= 128 ? wave * (B / 8) : 16 * (wave & 3);
+
+  // ---- B operands.  Q: chunk (k, t, plane) of 1 KB holds what lane l needs for k step k
+  // and column tile t.  Gb^T: lane l needs Gb[16 t + l%16][32 k + 8 (l/16) + 0..7], 32
+  // contiguous bytes of a row of Gb.
+  const bf16_t *qf = S.qp + 2 * off;
+  const float *G = S.dg + off;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(qf), (short)0, 4 * B * B, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(G), (short)0, 4 * B * B, 0x00020000);
+  const int voff = l * 16 + (nb / 16) * 2048;
+  const int goff = ((nb + (l & 15)) * B + 8 * (l >> 4)) * 4;
+  u32x4 fq[C::D][C::WN][2], fg[C::D][C::WN][2];
+  auto fload = [&](int slot, int k) {
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+        fq[slot][j][pl] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff, (k * C::NT + j) * 2048 + pl * 1024, 0));
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        fg[slot][j][h] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, goff, (16 * j * B + k * CTK) * 4 + 16 * h, 0));
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < C::D; ++s) fload(s, s % C::NK);
+
+  // ---- start panels: U_1 = Q[rows] (k steps pnl * RP/32 .. of the planes), W_0 = Gb^T[rows]
+  for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += CNTH) {
+    const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
+    const u32x4 v = *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8);
+    bf16_t *dst = (pl ? sUl : sUh) + (32 * ks + 8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e * C::A_LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
+  }
+  for (int q = tid; q < B * RP / 4; q += CNTH) {  // W_0[m][k] = Gb[k][r0 + m]
+    const int k = q / (RP / 4), c4 = q % (RP / 4);
+    const float4 v = *(const float4 *)(G + (int64_t)k * B + r0 + c4 * 4);
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint16_t h, lo;
+      split2(e[t], h, lo);
+      sWh[(c4 * 4 + t) * C::A_LD + k] = h;
+      sWl[(c4 * 4 + t) * C::A_LD + k] = lo;
+    }
+  }
+  // running 2 (W_0 + W_1 + ...) in accumulator layout, starting at 2 W_0
+  f32x4 run[C::WM][C::WN];
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) run[i][j][c] = 2.f * G[(int64_t)(n + c) * B + r0 + m];
+    }
+  __syncthreads();
+
+  f32x4 accW[C::WM][C::WN], accU[C::WM][C::WN];
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) accW[i][j] = accU[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int NS = 3 * C::NK;
+  auto step = [&](const int st, const int p) {
+    const int g = p * C::NK + st;
+    const int u = C::NK % C::D == 0 ? st % C::D : g % C::D;
+    bf16x8 qh[C::WN], ql[C::WN], gh[C::WN], gl[C::WN];
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      qh[j] = __builtin_bit_cast(bf16x8, fq[u][j][0]);
+      ql[j] = __builtin_bit_cast(bf16x8, fq[u][j][1]);
+      // whole vectors are reinterpreted, then indexed: a bit cast of one element of a
+      // vector (bit_cast(float, v[i])) reads element 0 whatever i is with this compiler
+      const f32x4 g0 = __builtin_bit_cast(f32x4, fg[u][j][0]), g1 = __builtin_bit_cast(f32x4, fg[u][j][1]);
+      uint16_t h[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split2(e < 4 ? g0[e & 3] : g1[e & 3], h[e], lo[e]);
+      s16x8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { hv[e] = (short)h[e]; lv[e] = (short)lo[e]; }
+      gh[j] = __builtin_bit_cast(bf16x8, hv);
+      gl[j] = __builtin_bit_cast(bf16x8, lv);
+    }
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i) {
+      const bf16x8 wh = frag_a_ld(sWh, C::A_LD, mb + 16 * i, st * CTK);
+      const bf16x8 wl = frag_a_ld(sWl, C::A_LD, mb + 16 * i, st * CTK);
+      const bf16x8 uh = frag_a_ld(sUh, C::A_LD, mb + 16 * i, st * CTK);
+      const bf16x8 ul = frag_a_ld(sUl, C::A_LD, mb + 16 * i, st * CTK);
+      // operands swapped: lane l holds C[m = l%16][n = 4*(l/16) + 0..3]
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j) {
+        f32x4 w = accW[i][j];
+        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j], wh, w, 0, 0, 0);
+        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gl[j], uh, w, 0, 0, 0);
+        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], wl, w, 0, 0, 0);
+        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gh[j], ul, w, 0, 0, 0);
+        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], wh, w, 0, 0, 0);
+        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gh[j], uh, w, 0, 0, 0);
+        accW[i][j] = w;
+        if (p < 2) {
+          f32x4 v = accU[i][j];
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j], uh, v, 0, 0, 0);
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], ul, v, 0, 0, 0);
+          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], uh, v, 0, 0, 0);
+          accU[i][j] = v;
+        }
+      }
+    }
+    if (g + C::D < NS) fload(u, (st + C::D) % C::NK);  // refill the slot just consumed
+
+    if (st == C::NK - 1) {
+      // ---- end of phase p: every wave is done with both panels before they are replaced
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::WN; ++j) {
+          const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
+          const f32x4 w = accW[i][j];
+          if (p < 2) {
+            run[i][j] += 2.f * w;
+            const f32x4 v = accU[i][j];
+            put_split4(sWh + m * C::A_LD + n, sWl + m * C::A_LD + n, make_float4(w[0], w[1], w[2], w[3]));
+            put_split4(sUh + m * C::A_LD + n, sUl + m * C::A_LD + n, make_float4(v[0], v[1], v[2], v[3]));
+          } else {
+            const f32x4 o = w + run[i][j];
+            float *O = S.out + off;  // Qbar^T[r0 + m][n + c] = Qbar[n + c][r0 + m]
+#pragma unroll
+            for (int c = 0; c < 4; ++c) O[(int64_t)(n + c) * B + r0 + m] = o[c];
+          }
+          accW[i][j] = accU[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      if (p < 2) __syncthreads();
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int st = 0; st < C::NK; ++st) step(st, p);
+}
+template __global__ void k_cnp_bwd_fused<64, 32>(CnpChainArgs);
+template __global__ void k_cnp_bwd_fused<128, 64>(CnpChainArgs);
+template __global__ void k_cnp_bwd_fused<256, 64>(CnpChainArgs);
+
 bool cnp_chain_supported(int64_t b) { return b == 64 || b == 128 || b == 256 || b == 512; }
+// The fused backward takes over once the blocks give 4 workgroups of 64-row panels per CU
+// (32-row at b = 64): below that its three phases in one workgroup are a longer chain of
+// dependent products than the two launches' three each (measured: 45 against 41 us at
+// 32 blocks of 256; 3.3 against 4.1 ms at 4096).
+bool cnp_bwd_fused_supported(int64_t b, int64_t nz) {
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  if (b == 64) return nz >= 4 * (int64_t)cus;
+  return (b == 128 || b == 256) && nz * (b / 64) >= 4 * (int64_t)cus;
+}
 
 namespace {
 template <int B, int RP>
@@ -494,6 +702,36 @@ int chain_run(const CnpChainArgs &a, hipStream_t s) {
   }
 }
 }  // namespace
+
+namespace {
+template <int B, int RP>
+int fused_run(const CnpChainArgs &a, hipStream_t s) {
+  using C = FusedCfg<B, RP>;
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
+  const int64_t nwg = nz * C::NP;
+  if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
+  const size_t lds = (size_t)4 * RP * C::A_LD * sizeof(bf16_t);
+  static bool attr = false;  // dynamic LDS above 64 KB, set once
+  if (!attr) {
+    if (hipFuncSetAttribute((const void *)k_cnp_bwd_fused<B, RP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+      return POETX_ERR_HIP;
+    attr = true;
+  }
+  return launch(a.name, s, [&] { k_cnp_bwd_fused<B, RP><<<dim3((unsigned)nwg), CNTH, lds, s>>>(a); });
+}
+}  // namespace
+
+int cnp_bwd_fused(const CnpChainArgs &a, hipStream_t s) {
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
+  if (nz <= 0) return POETX_OK;
+  switch (a.b) {
+    case 64: return fused_run<64, 32>(a, s);
+    case 128: return fused_run<128, 64>(a, s);
+    case 256: return fused_run<256, 64>(a, s);
+    default: return POETX_ERR_UNSUPPORTED;
+  }
+}
 
 int cnp_chain(const CnpChainArgs &a, hipStream_t s) {
   const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;

@@ -180,5 +180,10 @@ struct CnpChainArgs {
 };
 bool cnp_chain_supported(int64_t b);
 int cnp_chain(const CnpChainArgs &a, hipStream_t s);
+// The whole CNP backward of every block in one launch (mode unused): reads qp (Q's
+// planes) and dg, writes Qbar (fp32 [b][b]) to out; r unused.  b in {64, 128, 256}, and
+// taken for nz blocks in all (both segments) when cnp_bwd_fused_supported(b, nz).
+bool cnp_bwd_fused_supported(int64_t b, int64_t nz);
+int cnp_bwd_fused(const CnpChainArgs &a, hipStream_t s);
 
 }  // namespace poetx
