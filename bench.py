@@ -291,6 +291,12 @@ def summarize_trace(db, bench_json=None):
         line = [ln for ln in open(bench_json) if ln.startswith("{")][-1]
         d = json.loads(line)
         roof = d.get("roofline") or {}
+        if "phases" not in d:  # the CNP microbenchmark: no per-label phases
+            print()
+            print(f"bench.py in this run: forward {d['fwd_ms']:.3f} ms, backward {d['bwd_ms']:.3f} ms per call "
+                  f"over {d['config']['nblocks']} blocks of b = {d['config']['b']}: "
+                  f"{d['value'] / 1e3:.0f} K blocks/s.")
+            return
         ph = d["phases"][d["config"]["variant"]][roof["kernel"]]
         n_ev = int(round(ph["launches_per_step"] * d["steps"]))
         if roof["kernel"] == "gemm_nt" and d["variants"][d["config"]["variant"]].get("w_merged_t"):
