@@ -118,6 +118,42 @@ def test_cnp_workload2_sampled(B):
     assert rel_fro_per_block(to_host_f64(d[torch.from_numpy(idx).cuda()]), ref_d) <= TOL_CNP_F32
 
 
+def test_layer_fused_cnp_backward_two_sides(B):
+    """A layer wide enough (32768 -> 32768, b = 256: 128 + 128 blocks) that its CNP backward
+    runs the fused kernel over both sides in one launch.  The layer's dtheta on sampled
+    blocks of each side against the oracle's CNP backward of the dG the layer itself
+    reports; W, x and dz are drawn on the GPU (their values do not enter the check)."""
+    torch.manual_seed(11)
+    d, b, n = 32768, 256, 64
+    nb = d // b
+    p = b * (b - 1) // 2
+    rng = np.random.default_rng(12)
+    th_r = (rng.standard_normal((nb, p)) * 0.01).astype(np.float32)
+    th_p = (rng.standard_normal((nb, p)) * 0.01).astype(np.float32)
+    tr, tp = torch.from_numpy(th_r).cuda(), torch.from_numpy(th_p).cuda()
+    w = (torch.randn(d, d, device="cuda", dtype=torch.bfloat16) * d ** -0.5)
+    g_r = B.poetx_cnp(B.POETX_CNP_FWD, tr, b, g_dtype=torch.bfloat16)
+    g_p = B.poetx_cnp(B.POETX_CNP_FWD, tp, b, g_dtype=torch.bfloat16)
+    L = B.Layer(w, tr, tp, g_r, g_p, b, act_dtype=torch.bfloat16, variant=B.POETX_FAST)
+    x = torch.randn(n, d, device="cuda", dtype=torch.bfloat16)
+    dz = torch.randn(n, d, device="cuda", dtype=torch.bfloat16)
+    _say("fused cnp backward, two sides: layer 32768 -> 32768")
+    _, sb = B.poetx_forward(L, x)
+    torch.cuda.synchronize()
+    B.prof_read()
+    B.prof_enable(True)
+    out = B.poetx_backward(L, x, dz, sb, want_dg=True)
+    torch.cuda.synchronize()
+    B.prof_enable(False)
+    assert "cnp_bwd_fused" in B.prof_read()  # the launch this test is for
+    idx = np.array([0, 1, 77, nb - 1])
+    for th, key_g, key_t in ((th_r, "dg_r", "dtheta_r"), (th_p, "dg_p", "dtheta_p")):
+        dg = out[key_g][torch.from_numpy(idx).cuda()].double().cpu().numpy()
+        ref = O.cnp_backward(th[idx].astype(np.float64), dg, b)
+        got = out[key_t][torch.from_numpy(idx).cuda()].double().cpu().numpy()
+        assert rel_fro_per_block(got, ref) <= TOL_CNP_F32, key_t
+
+
 @pytest.mark.parametrize("b", [2, 32, 64])
 def test_cnp_many_blocks(B, b):
     """More blocks than a grid's y or z dimension holds (65535): the vector-ALU path (b = 2,
