@@ -210,15 +210,21 @@ def cpu_baseline(wl, inputs, target_s=15.0):
         O.poetx_step(x, dz, wm, tr, tp, wl.b, inputs["perm_in"], inputs["perm_out"])
         return time.perf_counter() - t0
 
-    n = 256
+    n = min(256, wl.n_tokens)
     t = run(n)
     while t < target_s / 4 and n < wl.n_tokens:
         n = min(wl.n_tokens, n * 4)
         t = run(n)
+    reps = 1
+    while t < 1.0:  # a workload that takes the oracle well under a second: repeat whole steps
+        reps *= 2
+        t = sum(run(n) for _ in range(reps))
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    return {"value": n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {wl.n_tokens} tokens of the workload, one full oracle step "
-                      f"(CNP fwd, layer fwd, layer bwd, CNP bwd) in float64 NumPy, {t:.1f} s"}
+    what = (f"first {n} of {wl.n_tokens} tokens of the workload" if n < wl.n_tokens
+            else f"all {n} tokens of the workload")
+    steps = "one full oracle step" if reps == 1 else f"{reps} full oracle steps"
+    return {"value": reps * n / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}, {steps} (CNP fwd, layer fwd, layer bwd, CNP bwd) in float64 NumPy, {t:.1f} s"}
 
 
 def load_traffic(kernel, workload_key):
