@@ -482,8 +482,11 @@ int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y,
 // dG[j] = X[:, o:o+bs]^T . Y[:, o:o+bs] (sum over tokens) for nb blocks of size bs, as
 // fp32 partials [P][nb][bs][bs] that are summed later in a fixed order;
 // grad_parts() is P.
+// The streaming kernel owns 128 x 128 slices of a block's gradient: at b = 512 sixteen of
+// them, so every operand slice is read by four workgroups; there the MFMA engine's 256 x 256
+// tiles (two readers per slice) split over tokens take over.
 bool grad_streams(const Plan &p, int64_t ld, int64_t nb, int64_t bs) {
-  return p.mfma && bs % 128 == 0 && p.N > 0 && block_grad_stream_supported(bs, ld, nb, p.N);
+  return p.mfma && bs % 128 == 0 && bs < 512 && p.N > 0 && block_grad_stream_supported(bs, ld, nb, p.N);
 }
 
 int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of the split-k kernel
@@ -498,8 +501,12 @@ int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of t
     const int64_t kc = cdiv(p.N, pmax);
     return p.N <= 1024 ? p.N : kc > 1024 ? kc : 1024;
   }
-  int64_t tiles = nb * (bs / 128) * (bs / 128);
-  int64_t want = cdiv(512, tiles);
+  // about one round of workgroups: 256 x 256 tiles where b allows (fp32 partials of a
+  // whole b x b per split, so no more splits than the CUs need)
+  const int64_t t = bs % 256 == 0 ? 256 : 128;
+  const int64_t tiles = nb * (bs / t) * (bs / t);
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const int64_t want = t == 256 ? (cus / tiles > 1 ? cus / tiles : 1) : cdiv(512, tiles);
   int64_t kc = cdiv(cdiv(p.N, want), 64) * 64;
   if (kc > kMaxChain) kc = kMaxChain;  // keep each float32 accumulation chain bounded
   return kc < 256 ? 256 : kc;

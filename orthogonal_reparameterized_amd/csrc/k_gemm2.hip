@@ -429,6 +429,7 @@ POETX_G2_INST(MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false)
 POETX_G2_INST(MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true)
 POETX_G2_INST(MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false)
 POETX_G2_INST(MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true)
+POETX_G2_INST(MFMA_BLOCK_GRAD, 256, 256, 2, 4, 64, 2, true, true)
 #undef POETX_G2_INST
 template __global__ void k_gemm2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, true>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false>(G2Args);
@@ -631,6 +632,8 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s) {
       return run2<MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false>(k, d, s);
     case MFMA_BLOCK_GRAD:
       if (!d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
+      // blocks of a multiple of 256: 256 x 256 tiles, each operand slice read by two of them
+      if (d.M % 256 == 0 && d.N % 256 == 0) return run2<MFMA_BLOCK_GRAD, 256, 256, 2, 4, 64, 2, true, true>(k, d, s);
       return run2<MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true>(k, d, s);
     default:
       return POETX_ERR_UNSUPPORTED;
