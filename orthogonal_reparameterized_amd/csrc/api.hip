@@ -418,22 +418,25 @@ int check_layer_ptrs(const poetx_layer *L) {
 
 // Y[:, o:o+bs] = X[:, o:o+bs] . G[j]  (transposed: . G[j]^T) for nb blocks of size bs
 // at column offsets o = j*bs; X, Y have row stride ld, G is [nb][bs][bs].
+// Gt: optional copy of the blocks' transposes (b = 512): the plain product then runs on the
+// k-contiguous NT kernel too.
 int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *X, const void *G, void *Y,
-                 bool transposed, const float *scaleN, hipStream_t s) {
+                 bool transposed, const float *scaleN, hipStream_t s, const void *Gt = nullptr) {
   if (p.N == 0 || nb == 0) return POETX_OK;
   const bool mfma = p.mfma && bs % 128 == 0;
   if (mfma && bs == 512) {
     // At b = 512 each block product is a K = N = 512 GEMM: the 256 x 256 W' kernels,
     // batched over blocks, read X twice (two column tiles); a block kernel with a
     // 64-column G slice in LDS read it once per slice and was L2-bound
+    const bool kc = transposed || Gt;  // B k-contiguous: G^T of the blocks, or G itself for the transposed product
     MfmaDesc m;
     m.M = p.N; m.N = bs; m.K = bs; m.batch = nb;
     m.A = X; m.a_km = false; m.lda = ld; m.sAb = bs;
-    m.B = G; m.b_km = !transposed; m.b_dt = POETX_BF16; m.ldb = bs; m.sBb = bs * bs;
+    m.B = transposed ? G : (Gt ? Gt : G); m.b_km = !kc; m.b_dt = POETX_BF16; m.ldb = bs; m.sBb = bs * bs;
     m.C = Y; m.c_dt = p.act; m.ldc = ld; m.sCb = bs;
     m.scaleN = scaleN; m.sSNb = bs;
     m.name = transposed ? "block_apply_t" : "block_apply";
-    m.role = transposed ? MFMA_GEMM_NT : MFMA_GEMM_NN;
+    m.role = kc ? MFMA_GEMM_NT : MFMA_GEMM_NN;
     if (mfma2_supported(m)) return gemm_mfma2(m, s);
   }
   if (mfma && block_stream_supported(bs, ld, nb, p.N))
@@ -468,11 +471,12 @@ const void *g_last(const Plan &p, const void *G, int64_t nb) {
   return (const char *)G + nb * p.b * p.b * dtype_size(p.gdt);
 }
 
-// Y = X . Diag(G) (transposed: . Diag(G)^T) over all ceil(d/b) blocks of a side.
+// Y = X . Diag(G) (transposed: . Diag(G)^T) over all ceil(d/b) blocks of a side.  Gt, if
+// given, holds the full blocks' transposes (see apply_blocks).
 int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y, bool transposed,
-                const float *scaleN, hipStream_t s) {
+                const float *scaleN, hipStream_t s, const void *Gt = nullptr) {
   const int64_t b = p.b, nb = d / b, bl = d % b;
-  POETX_TRY(apply_blocks(p, d, nb, b, X, G, Y, transposed, scaleN, s));
+  POETX_TRY(apply_blocks(p, d, nb, b, X, G, Y, transposed, scaleN, s, Gt));
   if (bl == 0) return POETX_OK;
   const int64_t c = nb * b;
   return apply_blocks(p, d, 1, bl, col_off(p, X, c), g_last(p, G, nb), col_off(p, Y, c), transposed,
@@ -662,12 +666,33 @@ int gemm_bwd(const Plan &p, const poetx_layer *L, const void *dB, void *dA, void
 
 struct FwdBufs {
   void *xg = nullptr, *a = nullptr, *bt = nullptr, *zt = nullptr;
+  void *gt_r = nullptr, *gt_p = nullptr;  // transposed G blocks for the plain b = 512 products
 };
+
+// b = 512 on the MFMA kernels: the plain block products read G^T k-contiguous
+bool wants_gt(const Plan &p) { return p.mfma && p.b == 512 && p.gdt == POETX_BF16; }
+
+// G^T of a side's nb full blocks into gt; *out = gt, or null where there is no buffer or G
+// is not 16-byte aligned (the product then reads G n-major).
+int transposed_g(const Plan &p, const void *g, void *gt, int64_t nb, hipStream_t s, const void **out) {
+  *out = nullptr;
+  if (!gt || nb == 0) return POETX_OK;
+  const int st = transpose_batched(g, gt, nb, p.b, p.b, s);
+  if (st == POETX_ERR_UNSUPPORTED) return POETX_OK;
+  if (st == POETX_OK) *out = gt;
+  return st;
+}
 
 // Carve forward intermediates.  `want_b` asks for B in the workspace; `saved_x` (the
 // caller's buffer for X~, or null) replaces the workspace copy of X~.
-void carve_fwd(Arena &ar, const Plan &p, const poetx_layer *L, bool want_b, void *saved_x, FwdBufs &f) {
+// fwd: the forward (both plain products), else the backward (the R side's, recomputed by mem).
+void carve_fwd(Arena &ar, const Plan &p, const poetx_layer *L, bool want_b, void *saved_x, FwdBufs &f,
+               bool fwd = true) {
   size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
+  if (wants_gt(p) && p.N > 0) {
+    if (p.nr && (fwd || p.mem)) f.gt_r = ar.take((size_t)p.nr * p.b * p.b * 2);
+    if (p.np && fwd) f.gt_p = ar.take((size_t)p.np * p.b * p.b * 2);
+  }
   if (L->perm_in) f.xg = saved_x ? saved_x : ar.take(xin);
   f.a = ar.take(xin);
   if (want_b) f.bt = ar.take(xout);
@@ -687,7 +712,9 @@ int run_front(const Plan &p, const poetx_layer *L, const void *x, const FwdBufs 
     POETX_TRY(permute_cols(x, f.xg, p.N, p.din, (int)p.ae, nullptr, L->perm_in, false, s));
     xg = f.xg;
   }
-  POETX_TRY(block_apply(p, p.din, xg, L->g_r, f.a, false, nullptr, s));
+  const void *gtr;
+  POETX_TRY(transposed_g(p, L->g_r, f.gt_r, p.nr, s, &gtr));
+  POETX_TRY(block_apply(p, p.din, xg, L->g_r, f.a, false, nullptr, s, gtr));
   return gemm_fwd(p, L, f.a, bt, tail, tail_bytes, s);
 }
 
@@ -716,7 +743,9 @@ extern "C" int poetx_forward(const poetx_layer *L, int64_t n_tokens, const void 
   void *bt = p.mem ? f.bt : saved_b;
   POETX_TRY(run_front(p, L, x, f, bt, tail, tb, s));
   void *zt = L->perm_out ? f.zt : z;
-  POETX_TRY(block_apply(p, p.dout, bt, L->g_p, zt, false, nullptr, s));
+  const void *gtp;
+  POETX_TRY(transposed_g(p, L->g_p, f.gt_p, p.np, s, &gtp));
+  POETX_TRY(block_apply(p, p.dout, bt, L->g_p, zt, false, nullptr, s, gtp));
   if (L->perm_out) POETX_TRY(permute_cols(zt, z, p.N, p.dout, (int)p.ae, nullptr, L->perm_out, true, s));
   return POETX_OK;
 }
@@ -735,7 +764,7 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
   Arena ar(ws);
   FwdBufs f;
-  carve_fwd(ar, p, L, p.mem, const_cast<void *>(kept_xg), f);
+  carve_fwd(ar, p, L, p.mem, const_cast<void *>(kept_xg), f, false);
   void *dzt = L->perm_out ? ar.take(xout) : nullptr;
   void *dbuf = ar.take(xout);
   void *da = ar.take(xin);

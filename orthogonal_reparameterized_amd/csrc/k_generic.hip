@@ -349,6 +349,8 @@ __global__ __launch_bounds__(256) void k_transpose_v(const T *__restrict__ in, T
   constexpr int V = 16 / sizeof(T), TR = 128 / sizeof(T), LD = TR + V;
   __shared__ __align__(16) T t[TR][LD];
   const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * TR;
+  in += (int64_t)blockIdx.z * rows * cols;  // matrix z of a batch (z = 0 for one matrix)
+  out += (int64_t)blockIdx.z * rows * cols;
   for (int q = threadIdx.x; q < TR * 8; q += 256) {
     const int row = q >> 3, ch = q & 7;
     const int64_t r = r0 + row, c = c0 + ch * V;
@@ -384,6 +386,17 @@ int transpose(const void *in, void *out, int64_t rows, int64_t cols, int esize, 
     case 2: return launch("transpose", s, [&] { k_transpose<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols); });
     default: return launch("transpose", s, [&] { k_transpose<uint8_t><<<grid, 256, 0, s>>>((const uint8_t *)in, (uint8_t *)out, rows, cols); });
   }
+}
+
+int transpose_batched(const void *in, void *out, int64_t batch, int64_t rows, int64_t cols, hipStream_t s) {
+  if (batch <= 0 || rows <= 0 || cols <= 0) return POETX_OK;
+  const int64_t V = 8, TR = 64;  // bf16
+  if (rows % V || cols % V || (((uintptr_t)in | (uintptr_t)out) & 15) || batch > 65535 || cdiv(rows, TR) > 65535)
+    return POETX_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)cdiv(cols, TR), (unsigned)cdiv(rows, TR), (unsigned)batch);
+  return launch("transpose", s, [&] {
+    k_transpose_v<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols);
+  });
 }
 
 __global__ void k_gather_f32(const float *__restrict__ src, float *__restrict__ out, int64_t n,

@@ -33,6 +33,9 @@ int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esiz
                  const int32_t *rperm, const int32_t *cperm, bool scatter, hipStream_t s);
 // out[c][r] = in[r][c] ([rows][cols] -> [cols][rows]) for esize-byte elements
 int transpose(const void *in, void *out, int64_t rows, int64_t cols, int esize, hipStream_t s);
+// the same for each of batch contiguous bf16 matrices (rows, cols multiples of 8, 16-byte
+// aligned pointers)
+int transpose_batched(const void *in, void *out, int64_t batch, int64_t rows, int64_t cols, hipStream_t s);
 // out[i] = src[perm[i]] for float32 vectors
 int gather_f32(const float *src, float *out, int64_t n, const int32_t *perm, hipStream_t s);
 
