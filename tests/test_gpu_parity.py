@@ -550,6 +550,20 @@ def test_layer_full_size(B, key, variant, wt):
     _compare(st, out, ref, TOL_BF16, f"workload{key} {variant}")
 
 
+@pytest.mark.parametrize("b", [256, 512])
+def test_layer_many_tiles_ragged(B, b):
+    """12289 tokens at 2048 -> 2048: 49 row tiles of 256, the last one holding a single
+    token.  The W' products take 392 whole tiles in two rounds (the leftover round is too
+    full to split along k) and, at b = 512, the batched block products 4 x 49 x 2 tiles."""
+    wl = WL.Workload(98, "many tiles ragged", 12289, 2048, 2048, b, "bf16", "bf16", "bf16", 0.01, 2048)
+    inp = WL.make_layer_inputs(wl)
+    ref = oracle_layer(inp, wl)
+    for variant in ("fast", "mem"):
+        st, out = _run_step(wl, inp, variant)
+        _compare(st, out, ref, TOL_BF16, f"many tiles ragged b={b} {variant}")
+        del st, out
+
+
 def test_fast_mem_identical_and_deterministic(B):
     wl = WL.Workload(94, "det", 300, 512, 512, 256, "bf16", "bf16", "bf16", 0.01, 512)
     inp = WL.make_layer_inputs(wl)
