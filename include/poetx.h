@@ -67,7 +67,7 @@ extern "C" {
 typedef enum {
   POETX_OK = 0,
   POETX_ERR_INVALID_ARG = -1, /* NULL where a buffer is required, bad enum, n < 0 */
-  POETX_ERR_SHAPE = -2,       /* b does not divide a width, b out of range       */
+  POETX_ERR_SHAPE = -2,       /* block size b out of range                       */
   POETX_ERR_UNSUPPORTED = -3, /* a combination the library does not implement    */
   POETX_ERR_WORKSPACE = -4,   /* *ws_bytes smaller than required                 */
   POETX_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed      */
