@@ -200,7 +200,11 @@ def cpu_baseline(wl, inputs, target_s=15.0):
 
     from oracle import poetx_oracle as O
     from orthogonal_reparameterized_amd import workloads as WL
-    wm = O.merge_perm(WL.to_f64(inputs["w"], wl.w), inputs["perm_out"], inputs["perm_in"])
+    if wl.w == "i8":  # the oracle's W' is the merged int8 weight times its merged row scales
+        qm, sm = O.merge_perm_int8(inputs["w_q"], inputs["w_s"], inputs["perm_out"], inputs["perm_in"])
+        wm = O.dequantize_rows(qm, sm)
+    else:
+        wm = O.merge_perm(WL.to_f64(inputs["w"], wl.w), inputs["perm_out"], inputs["perm_in"])
     tr, tp = inputs["theta_r"].astype(np.float64), inputs["theta_p"].astype(np.float64)
 
     def run(n):
@@ -492,7 +496,7 @@ def main():
                             "fold_ms": fold_time_ms(wl, inputs)},
         "optimizer_per_step": adam_time_ms(wl),
     }
-    if not args.no_cpu and wl.w != "i8":
+    if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, inputs)
     print(json.dumps(out))
 
