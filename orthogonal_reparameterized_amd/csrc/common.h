@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 
@@ -32,6 +33,20 @@ inline int launch(const char *name, hipStream_t s, F &&f) {
   hipError_t e = hipGetLastError();
   if (prof_on()) prof_end(s);
   return e == hipSuccess ? POETX_OK : POETX_ERR_HIP;
+}
+
+// Raises kernel `fn`'s dynamic-LDS limit to `bytes` on the current device, once per
+// device: `done` is that kernel's record, one bit per device id (ids past 63 set the
+// attribute on every call).  Two threads may both set it; the call is idempotent.
+inline int lds_limit(const void *fn, size_t bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return POETX_ERR_HIP;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return POETX_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+    return POETX_ERR_HIP;
+  if (bit) done.fetch_or(bit, std::memory_order_release);
+  return POETX_OK;
 }
 
 // ------------------------------------------------------------- bf16 bits ----

@@ -169,13 +169,8 @@ template __global__ void k_block_reg<256, 32, 7, true, 8>(BSArgs);
 template <int B, int T, int NST, bool TRANS, int NCW = 4>
 static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
   const size_t lds = (size_t)(NST + 1) * T * B * 2;  // ring + NCW output staging tiles
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_reg<B, T, NST, TRANS, NCW>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return POETX_ERR_HIP;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};
+  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_block_reg<B, T, NST, TRANS, NCW>), lds, attr));
   const dim3 grid((unsigned)(a.nb * a.P));
   return launch(name, s, [&] { k_block_reg<B, T, NST, TRANS, NCW><<<grid, 64 * (NCW + 2), lds, s>>>(a); });
 }
@@ -320,13 +315,8 @@ static int run_bg(const BGArgs &a, hipStream_t s) {
   const size_t lds = (size_t)BG_NST * 2 * BG_T * 128 * 2;
   const int64_t units = (int64_t)a.nb * a.P;
   dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_block_grad_stream<B, BG_NST, BG_T, BG_NPW>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return POETX_ERR_HIP;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};
+  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_block_grad_stream<B, BG_NST, BG_T, BG_NPW>), lds, attr));
   return launch("block_grad", s, [&] { k_block_grad_stream<B, BG_NST, BG_T, BG_NPW><<<grid, 64 * (4 + BG_NPW), lds, s>>>(a); });
 }
 

@@ -685,13 +685,9 @@ int chain_run(const CnpChainArgs &a, hipStream_t s) {
   const int64_t nwg = nz * C::NP;
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
   const size_t lds = (size_t)2 * RP * C::A_LD * sizeof(bf16_t);
-  static bool attr[3] = {false, false, false};  // dynamic LDS above 64 KB, set once per kernel
+  static std::atomic<uint64_t> attr[3];  // dynamic LDS above 64 KB, per kernel and device
   auto go = [&](void (*kern)(CnpChainArgs), int mode) -> int {
-    if (!attr[mode]) {
-      if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return POETX_ERR_HIP;
-      attr[mode] = true;
-    }
+    POETX_TRY(lds_limit((const void *)kern, lds, attr[mode]));
     return launch(a.name, s, [&] { kern<<<dim3((unsigned)nwg), CNTH, lds, s>>>(a); });
   };
   switch (a.mode) {
@@ -711,13 +707,8 @@ int fused_run(const CnpChainArgs &a, hipStream_t s) {
   const int64_t nwg = nz * C::NP;
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
   const size_t lds = (size_t)4 * RP * C::A_LD * sizeof(bf16_t);
-  static bool attr = false;  // dynamic LDS above 64 KB, set once
-  if (!attr) {
-    if (hipFuncSetAttribute((const void *)k_cnp_bwd_fused<B, RP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
-      return POETX_ERR_HIP;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};  // dynamic LDS above 64 KB, per device
+  POETX_TRY(lds_limit((const void *)k_cnp_bwd_fused<B, RP>, lds, attr));
   return launch(a.name, s, [&] { k_cnp_bwd_fused<B, RP><<<dim3((unsigned)nwg), CNTH, lds, s>>>(a); });
 }
 }  // namespace

@@ -513,33 +513,18 @@ static int run_pp(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
             (unsigned)(d.batch * d.splits));
   if constexpr (BI8) {  // int8 W' products write bf16 gradients only
     if (d.c_dt != POETX_BF16) return POETX_ERR_UNSUPPORTED;
-    static bool attr = false;
-    if (!attr) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, false, true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return POETX_ERR_HIP;
-      attr = true;
-    }
+    static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
+    POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, false, true>), lds, attr));
     POETX_TRY(launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, false, true><<<grid, 512, lds, s>>>(a); }));
     return tail_reduce(a, d, s);
   }
   if (d.c_dt == POETX_F32) {
-    static bool attr = false;
-    if (!attr) {
-      if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return POETX_ERR_HIP;
-      attr = true;
-    }
+    static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
+    POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, true>), lds, attr));
     return launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, true><<<grid, 512, lds, s>>>(a); });
   }
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return POETX_ERR_HIP;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
+  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, false>), lds, attr));
   POETX_TRY(launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, false><<<grid, 512, lds, s>>>(a); }));
   return tail_reduce(a, d, s);
 }
@@ -549,13 +534,8 @@ template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM
 static int run2o(const G2Args &a, const char *name, dim3 grid, size_t lds, hipStream_t s) {
   constexpr int NT = 64 * WGM * WGN;
   auto kern = &k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8>;
-  static bool attr = false;  // raise the dynamic-LDS limit once per instantiation
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
-      return POETX_ERR_HIP;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
+  POETX_TRY(lds_limit(reinterpret_cast<const void *>(kern), lds, attr));
   return launch(name, s, [&] { k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8><<<grid, NT, lds, s>>>(a); });
 }
 
