@@ -38,7 +38,8 @@ DOMINANT = "gemm_nt"
 
 
 def algorithmic(wl, variant, n):
-    """Per-step algorithmic flops and HBM bytes of each kernel label."""
+    """Per-step algorithmic flops and HBM bytes of each kernel label: the minimum each kernel
+    must compute and move (its operands read once, its results written once)."""
     di, do, b = wl.d_in, wl.d_out, wl.b
     nr, np_ = di // b, do // b
     ae = 2 if wl.act == "bf16" else 4
@@ -422,7 +423,7 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the layer would shard by tokens with an all-reduce of dtheta).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

@@ -1,6 +1,6 @@
 """Plain fp64 CPU oracle for the POET-X linear layer (forward, backward, CNP, merge).
 
-TEST INFRASTRUCTURE ONLY.  This module is the checker that the HIP path is
+TEST INFRASTRUCTURE ONLY.  This module is the oracle that the HIP path is
 compared against.  Only the test-suite, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it.  The product path (the
 ``orthogonal_reparameterized_amd`` package and its C-ABI library) never imports,

@@ -1,6 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
 
-Tolerances (derived in the design doc):
+Tolerances (from the arithmetic: float32 products accumulate to about 1e-6 relative, and one
+bf16 rounding of an operand or result costs up to 2^-9 = 2e-3 relative, a few of them per step):
   * float32 CNP outputs (G in fp32, dtheta from an identical dG): max over blocks
     of the relative Frobenius error <= 1e-5.
   * bf16 G: every element within one bf16 ulp of the oracle's value (absolute
