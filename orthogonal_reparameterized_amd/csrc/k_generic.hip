@@ -340,32 +340,48 @@ __global__ __launch_bounds__(256) void k_transpose(const T *__restrict__ in, T *
 
 // The same with 16-byte global accesses: a tile of TR x TR elements (128-byte tile rows:
 // 64 x 64 for 2-byte, 128 x 128 for 1-byte elements) is read along its rows in 16-byte
-// chunks into a padded LDS tile, and written along its columns in 16-byte chunks, each
-// gathered from V = 16 / sizeof(T) consecutive tile rows.  Needs rows and cols to be
-// multiples of V (whole chunks) and 16-byte aligned buffers.
+// chunks into LDS, and written along its columns in 16-byte chunks, each gathered from
+// V = 16 / sizeof(T) consecutive tile rows.  A thread reads those V rows a 4-byte word at a
+// time (P = 4 / sizeof(T) columns per word) and writes P output chunks, so the LDS is read
+// with one instruction per word instead of one per element.  The 16-byte chunk c of tile
+// row r sits at chunk c ^ ((r / V) % 8), which puts the eight row groups a wave reads at
+// once on different banks.  Needs rows and cols to be multiples of V (whole chunks) and
+// 16-byte aligned buffers.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose_v(const T *__restrict__ in, T *__restrict__ out, int64_t rows,
                                                      int64_t cols) {
-  constexpr int V = 16 / sizeof(T), TR = 128 / sizeof(T), LD = TR + V;
-  __shared__ __align__(16) T t[TR][LD];
+  constexpr int V = 16 / sizeof(T), TR = 128 / sizeof(T), P = 4 / sizeof(T);
+  __shared__ __align__(16) uint32_t t[TR * 32];  // TR rows of 128 bytes
   const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * TR;
   in += (int64_t)blockIdx.z * rows * cols;  // matrix z of a batch (z = 0 for one matrix)
   out += (int64_t)blockIdx.z * rows * cols;
   for (int q = threadIdx.x; q < TR * 8; q += 256) {
     const int row = q >> 3, ch = q & 7;
     const int64_t r = r0 + row, c = c0 + ch * V;
-    if (r < rows && c < cols) *(uint4 *)&t[row][ch * V] = *(const uint4 *)(in + r * cols + c);
+    if (r < rows && c < cols)
+      *(uint4 *)&t[row * 32 + ((ch ^ ((row / V) & 7)) << 2)] = *(const uint4 *)(in + r * cols + c);
   }
   __syncthreads();
-  for (int q = threadIdx.x; q < TR * 8; q += 256) {
-    const int cc = q >> 3, rr = q & 7;
-    const int64_t c = c0 + cc, r = r0 + rr * V;
-    if (c < cols && r < rows) {
-      union { uint4 v; T e[V]; } u;
+  const int rr = threadIdx.x & 7, cg = threadIdx.x >> 3;  // rows rr*V .., columns cg*P ..
+  const int64_t r = r0 + rr * V;
+  if (r >= rows) return;
+  uint32_t w[V];
 #pragma unroll
-      for (int j = 0; j < V; ++j) u.e[j] = t[rr * V + j][cc];
-      *(uint4 *)(out + c * rows + r) = u.v;
+  for (int j = 0; j < V; ++j) w[j] = t[(rr * V + j) * 32 + ((((cg >> 2) ^ rr) & 7) << 2) + (cg & 3)];
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    const int64_t c = c0 + cg * P + e;
+    if (c >= cols) break;
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int k = 0; k < P; ++k)  // element e of the words of rows 4i/P*... in order
+        x |= ((w[i * P + k] >> (8 * sizeof(T) * e)) & ((1u << (8 * sizeof(T))) - 1)) << (8 * sizeof(T) * k);
+      u[i] = x;
     }
+    *(uint4 *)(out + c * rows + r) = make_uint4(u[0], u[1], u[2], u[3]);
   }
 }
 
