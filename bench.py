@@ -9,14 +9,30 @@ The permutation merge runs once per inner phase, before the timed region, and
 is timed separately.  Inputs are seeded synthetic data resident in HBM before
 timing starts.  Prints ONE JSON line.
 
+Timing: W untimed warm-up steps, then exactly K steps between two device
+synchronizations.  Inside that timed region the dominant kernel's launches (the W'
+product) carry a start and a stop event bound to their own dispatch (the library's
+per-thread recorder, hipExtLaunchKernel, events without a system-scope fence), and
+one event marks each step boundary: `roofline` and the per-step median/min/max come
+from the timed steps themselves.  The same K steps then run once unrecorded (the
+cost of the recording) and once with every launch recorded (`phases`, the per-kernel
+table: a recorded dispatch waits a few us on its events, so that pass's step time is
+longer, while the kernels' own durations match an unrecorded kernel trace).
+
+Besides the head workload (default 3) the default run also measures the other
+workloads of the build: 4 (fast, mem), 5 (mem) and 2 (CNP blocks/s); the head
+workload is also run with NULL activation permutations and as the pages' own fast
+variant (which keeps only B).  --only-head skips all of that (profiling runs).
+
 Extra modes used to make the committed profile summaries:
     --copy-calibration   time a plain 1 GiB device copy (the HBM counter calibration)
     --no-cpu             skip the CPU-oracle baseline leg
     --summarize-trace DB [JSON]      markdown kernel table from a rocprofv3 --kernel-trace database
                                      (with the traced run's JSON line: dominant kernel trace vs events)
-    --summarize-counters F W CF CW   HBM traffic of the dominant kernel from four rocprofv3 --pmc
-                                     databases (FETCH_SIZE, WRITE_SIZE; then the same two counters
-                                     taken on --copy-calibration)
+    --summarize-counters F W CF CW [JSON]  HBM traffic per kernel from four rocprofv3 --pmc databases
+                                     (FETCH_SIZE, WRITE_SIZE; then the same two counters taken on
+                                     --copy-calibration); with the run's JSON line, traffic / algorithmic
+    --summarize-pmc DB [DB ...]      per-kernel averages of any counters in --pmc databases
 """
 
 from __future__ import annotations
@@ -25,6 +41,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -37,7 +54,8 @@ PEAK_HBM_GBS = 8000.0
 DOMINANT = "gemm_nt"
 
 
-def algorithmic(wl, variant, n):
+# ------------------------------------------------------------------ work model ----
+def algorithmic(wl, variant, n, perms=True, keep_x=True):
     """Per-step algorithmic flops and HBM bytes of each kernel label: the minimum each kernel
     must compute and move (its operands read once, its results written once)."""
     di, do, b = wl.d_in, wl.d_out, wl.b
@@ -54,121 +72,197 @@ def algorithmic(wl, variant, n):
     g_bytes_r, g_bytes_p = nr * b * b * ae, np_ * b * b * ae
     fronts = 2 if mem else 1  # mem recomputes gather, R-side apply and the forward GEMM
     for _ in range(fronts):
-        add("permute_cols", 0, 2 * n * di * ae)
+        if perms:
+            add("permute_cols", 0, 2 * n * di * ae)                               # gather X
         add("block_apply", 2.0 * n * di * b, 2 * n * di * ae + g_bytes_r)
         add("gemm_nt", 2.0 * n * di * do, n * di * ae + do * di * we + n * do * ae)
-    # fast keeps the forward's X~ for dG_R (the gather above writes it): no second gather
+    if perms and not mem and not keep_x:
+        add("permute_cols", 0, 2 * n * di * ae)                                   # gather X again
     add("block_apply", 2.0 * n * do * b, 2 * n * do * ae + g_bytes_p)            # Z~ = B G_P
-    add("permute_cols", 0, 2 * n * do * ae)                                       # scatter Z
-    add("permute_cols", 0, 2 * n * do * ae)                                       # gather dZ
+    if perms:
+        add("permute_cols", 0, 2 * n * do * ae)                                   # scatter Z
+        add("permute_cols", 0, 2 * n * do * ae)                                   # gather dZ
     add("block_apply_t", 2.0 * n * do * b, 2 * n * do * ae + g_bytes_p)          # dB
     add("block_grad", 2.0 * n * do * b, 2 * n * do * ae)                          # dG_P
     add("gemm_nn", 2.0 * n * di * do, n * do * ae + do * di * we + n * di * ae)   # dA
     add("block_apply_t", 2.0 * n * di * b, 2 * n * di * ae + g_bytes_r)          # dX~
-    add("permute_cols", 0, 2 * n * di * ae)                                       # scatter dX
+    if perms:
+        add("permute_cols", 0, 2 * n * di * ae)                                   # scatter dX
     add("block_grad", 2.0 * n * di * b, 2 * n * di * ae)                          # dG_R
-    # CNP, both sides (nb blocks): the forward chain G = (((Q+2I)Q+2I)Q+2I)Q + I runs 3
-    # float32-accurate b^3 products (2 b^3 flops each); the backward 8 in one fused launch
-    # when the blocks fill the GPU, else 3 + 3 in two chain launches.
-    # Bytes are the method's minimum: theta in and G out (forward), theta and dG in and
-    # dtheta out (backward, split over its two launches); the unpack and pack launches
-    # carry the theta / dtheta side.
+    # CNP, both sides (nb blocks), at the method's own product count (forward 2 b^3-products
+    # by Horner, backward 6; 2 b^3 flops each) and its minimum bytes: theta in and G out
+    # (forward), theta and dG in and dtheta out (backward).
     nb = nr + np_
     p, bb = b * (b - 1) // 2, b * b
-    add("unpack_skew", 0, 2 * nb * 4 * p)
-    add("cnp_fwd_chain", 6.0 * b ** 3 * nb, nb * ae * bb)
-    if nb * (b // 64) >= 4 * 256:
-        add("cnp_bwd_fused", 16.0 * b ** 3 * nb, nb * 4 * bb)   # 8 products in one launch
-    else:
-        add("cnp_bwd_chain_a", 6.0 * b ** 3 * nb, nb * 4 * bb)  # few blocks: two launches
-        add("cnp_bwd_chain_b", 6.0 * b ** 3 * nb, 0)
-    add("pack_skew_grad", 0, nb * 4 * p)
+    add("cnp_fwd", 4.0 * b ** 3 * nb, nb * 4 * p + nb * ae * bb)
+    add("cnp_bwd", 12.0 * b ** 3 * nb, nb * 4 * (bb + 2 * p))
     return ops
+
+
+# kernel labels of the library -> the algorithmic group they carry
+LABEL_GROUP = {"unpack_skew": "cnp_fwd", "cnp_fwd_chain": "cnp_fwd", "cnp_fwd_mm": "cnp_fwd",
+               "cnp_bwd_fused": "cnp_bwd", "cnp_bwd_chain_a": "cnp_bwd", "cnp_bwd_chain_b": "cnp_bwd",
+               "cnp_bwd_mm": "cnp_bwd", "pack_skew_grad": "cnp_bwd", "reduce_parts": "block_grad",
+               "gemm_tail_reduce": None, "transpose": None}
+
+
+def survey_floor_ms(wl, variant, n):
+    """The step's roofline floor with the activation permutations fused into the block
+    products: sum over the method's steps of max(flops / 2.5 PF/s, bytes / 8 TB/s), every
+    product counted once in bf16, the CNP at its method flops (Horner 2 + 6 products)."""
+    di, do, b = wl.d_in, wl.d_out, wl.b
+    ae = 2 if wl.act == "bf16" else 4
+    we = {"bf16": 2, "f32": 4, "i8": 1}[wl.w]
+    nr, np_ = di // b, do // b
+    nb, p, bb = nr + np_, b * (b - 1) // 2, b * b
+    gr, gp = nr * bb * ae, np_ * bb * ae
+    gemm = (2.0 * n * di * do, n * di * ae + di * do * we + n * do * ae)
+    phases = [
+        (4.0 * b ** 3 * nb, nb * 4 * p + nb * ae * bb),                      # S1 CNP forward
+        (2.0 * n * di * b, 2 * n * di * ae + gr),                            # S2+S3 gather + apply R
+        gemm,                                                                # S4
+        (2.0 * n * do * b, 2 * n * do * ae + gp),                            # S5 apply P + scatter
+        (4.0 * n * do * b, 3 * n * do * ae + gp + np_ * bb * 4),             # S7 P side
+        gemm,                                                                # S8
+        (4.0 * n * di * b, 3 * n * di * ae + gr + nr * bb * 4),              # S9 R side
+        (12.0 * b ** 3 * nb, nb * 4 * (bb + 2 * p)),                         # S10 CNP backward
+    ]
+    if variant == "mem":
+        phases += [(2.0 * n * di * b, 2 * n * di * ae + gr), gemm]          # S6 recompute
+    t = sum(max(f / (PEAK_BF16_TFLOPS * 1e12), y / (PEAK_HBM_GBS * 1e9)) for f, y in phases)
+    return t * 1e3
+
+
+def unfused_floor_ms(wl, variant, n, perms=True, keep_x=True):
+    """The same floor for the kernels as built: each permutation a separate pass over its
+    activation (bytes per label from algorithmic())."""
+    t = 0.0
+    for f, y in algorithmic(wl, variant, n, perms, keep_x).values():
+        t += max(f / (PEAK_BF16_TFLOPS * 1e12), y / (PEAK_HBM_GBS * 1e9))
+    return t * 1e3
 
 
 def step_flops(wl, variant, n):
     return sum(f for f, _ in algorithmic(wl, variant, n).values())
 
 
-def layer_roofline_ms(wl, variant, n):
-    """Sum over kernels of max(flops / MFMA peak, bytes / HBM peak).  The CNP products
-    are float32-accurate through three bf16 MFMA passes, so they count 3x against the
-    bf16 peak; everything else runs one bf16 pass per product."""
-    t = 0.0
-    for name, (f, y) in algorithmic(wl, variant, n).items():
-        passes = 3 if name.startswith("cnp_") else 1
-        t += max(passes * f / (PEAK_BF16_TFLOPS * 1e12), y / (PEAK_HBM_GBS * 1e9))
-    return t * 1e3
+# ------------------------------------------------------------------ timing ----
+def _sync():
+    import torch
+    torch.cuda.synchronize()
 
 
-def fold_time_ms(wl, inputs, reps=10):
-    """Phase-end fold (poetx_fold) at the workload's weight shape; None for int8."""
-    if wl.w == "i8":
-        return None
+def time_steps(st, steps, warmup, record, only=None):
+    """K steps between two synchronizations, an event at each step boundary; with
+    `record`, the launches labelled `only` (every launch when None) carry dispatch-bound
+    start/stop events."""
+    import torch
+    from orthogonal_reparameterized_amd import binding as B
+    for _ in range(warmup):
+        st.step()
+    _sync()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    if record:
+        B.prof_read()  # clear
+        B.prof_only(only)
+        B.prof_enable(True)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i].record()
+        st.step()
+    ev[steps].record()
+    _sync()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    rec = None
+    if record:
+        B.prof_enable(False)
+        B.prof_only(None)
+        rec = B.prof_read()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return wall, per, rec
+
+
+def phase_table(rec, alg, steps):
+    out = {}
+    for name, (cnt, tot, mn, mx) in sorted(rec.items()):
+        e = {"launches_per_step": cnt / steps, "avg_ms": tot / cnt, "min_ms": mn, "max_ms": mx,
+             "ms_per_step": tot / steps}
+        grp = LABEL_GROUP.get(name, name)
+        if grp in alg and grp == name:
+            f, y = alg[name]
+            per = cnt / steps
+            e["tflops"] = f / per / (e["avg_ms"] * 1e-3) / 1e12
+            e["gbs"] = y / per / (e["avg_ms"] * 1e-3) / 1e9
+            e["frac_mfma"] = e["tflops"] / PEAK_BF16_TFLOPS
+            e["frac_hbm"] = e["gbs"] / PEAK_HBM_GBS
+        out[name] = e
+    # CNP groups: several launches carry one method step
+    for grp in ("cnp_fwd", "cnp_bwd"):
+        ms = sum(e["ms_per_step"] for k, e in out.items() if LABEL_GROUP.get(k) == grp)
+        if ms > 0 and grp in alg:
+            f, y = alg[grp]
+            out[grp + " (all launches)"] = {
+                "ms_per_step": ms, "tflops": f / (ms * 1e-3) / 1e12, "gbs": y / (ms * 1e-3) / 1e9,
+                "frac_mfma": f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "frac_hbm": y / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    return out
+
+
+def flush_cache(buf):
+    """Write 1 GiB: evicts the 256 MB Infinity Cache and the L2s."""
+    buf.fill_(1)
+
+
+def run_variant(wl, inputs, variant, steps, warmup, *, keep_wt, keep_x=True, perms=True, cold_steps=0):
     import torch
     from orthogonal_reparameterized_amd import binding as B
     from orthogonal_reparameterized_amd.step import LayerStep
-    st = LayerStep(wl, dict(inputs, x=inputs["x"][:64], dz=inputs["dz"][:64]), "mem")
-    st.cnp()
-    w_out = torch.empty_like(st.w_merged)
-    B.poetx_fold(st.layer, w_out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        B.poetx_fold(st.layer, w_out)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
-
-
-def adam_time_ms(wl, reps=20):
-    """poetx_adam_step over the layer's packed theta (both sides), float32 state."""
-    import torch
-    from orthogonal_reparameterized_amd import binding as B
-    n = (wl.d_in // wl.b + wl.d_out // wl.b) * (wl.b * (wl.b - 1) // 2)
-    th = torch.zeros(n, device="cuda")
-    g, m, v = torch.randn(n, device="cuda"), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
-    B.poetx_adam_step(th, g, m, v, lr=1e-3, step=1)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for t in range(reps):
-        B.poetx_adam_step(th, g, m, v, lr=1e-3, step=t + 2)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    return {"ms": ms, "params": n, "GB_s": 7 * 4 * n / (ms * 1e-3) / 1e9}
-
-
-def time_steps(st, steps, warmup):
-    import torch
-    for _ in range(warmup):
-        st.step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        st.step()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
-
-
-def profile_steps(st, steps):
-    """Per-kernel-label launch counts and average durations (HIP events on the
-    library's launch stream, recorded around each launch)."""
-    import torch
-    from orthogonal_reparameterized_amd import binding as B
-    B.prof_read()  # clear
-    B.prof_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        st.step()
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    B.prof_enable(False)
-    rec = B.prof_read()
-    return {k: (n / steps, ms / n) for k, (n, ms) in rec.items()}, wall
+    st = LayerStep(wl, inputs, variant, transposed_weight=keep_wt, keep_x=keep_x, perms=perms)
+    n = wl.n_tokens
+    # the timed steps: only the dominant kernel's launches carry events (a recorded dispatch
+    # waits a few us on its events' bookkeeping), then the same steps unrecorded, then once
+    # more with every launch recorded for the per-kernel table
+    wall, per, rec_dom = time_steps(st, steps, warmup, record=True, only=DOMINANT)
+    wall_off, per_off, _ = time_steps(st, steps, 1, record=False)
+    wall_all, _, rec = time_steps(st, steps, 1, record=True)
+    alg = algorithmic(wl, variant, n, perms, keep_x and st.saved_x is not None)
+    floor_fused = survey_floor_ms(wl, variant, n)
+    floor_unfused = unfused_floor_ms(wl, variant, n, perms, keep_x and st.saved_x is not None)
+    v = {"ms_per_step": wall, "tokens_per_s": n / (wall * 1e-3),
+         "step_ms": {"median": statistics.median(per), "min": min(per), "max": max(per),
+                     "mean": sum(per) / len(per)},
+         "ms_per_step_unrecorded": wall_off,
+         "step_ms_unrecorded": {"median": statistics.median(per_off), "min": min(per_off),
+                                "max": max(per_off)},
+         "ms_per_step_all_recorded": wall_all,
+         "w_merged_t": keep_wt, "kept_x": st.saved_x is not None, "activation_permutations": perms,
+         "floor_fused_ms": floor_fused, "frac_of_fused_floor": floor_fused / wall,
+         "floor_unfused_ms": floor_unfused, "frac_of_unfused_floor": floor_unfused / wall}
+    phases = phase_table(rec, alg, steps)
+    if rec_dom and DOMINANT in rec_dom:
+        # the dominant kernel as timed inside the timed steps themselves
+        phases[DOMINANT + " (timed steps)"] = phase_table({DOMINANT: rec_dom[DOMINANT]}, alg, steps)[DOMINANT]
+    cold = None
+    if cold_steps:
+        # per-phase HBM figures with nothing left in the caches from the previous step
+        fl = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        B.prof_read()
+        acc = {}
+        for _ in range(cold_steps):
+            flush_cache(fl)
+            _sync()
+            B.prof_enable(True)
+            st.step()
+            _sync()
+            B.prof_enable(False)
+            for k, (c, t, mn, mx) in B.prof_read().items():
+                a = acc.setdefault(k, [0, 0.0, mn, mx])
+                a[0] += c; a[1] += t; a[2] = min(a[2], mn); a[3] = max(a[3], mx)
+        cold = phase_table({k: tuple(a) for k, a in acc.items()}, alg, cold_steps)
+        del fl
+    del st
+    torch.cuda.empty_cache()
+    return v, phases, cold
 
 
 def merge_time_ms(wl, inputs, reps=10, with_t=False):
@@ -182,16 +276,100 @@ def merge_time_ms(wl, inputs, reps=10, with_t=False):
     so = torch.empty_like(s) if s is not None else None
     ot = torch.empty((wl.d_in, wl.d_out), dtype=w.dtype, device=w.device) if with_t else None
     B.poetx_merge_perm(w, pout, pin, s, out, so, ot)
-    torch.cuda.synchronize()
+    _sync()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
         B.poetx_merge_perm(w, pout, pin, s, out, so, ot)
     e1.record()
-    torch.cuda.synchronize()
+    _sync()
     ms = e0.elapsed_time(e1) / reps
     nbytes = (4 if with_t else 2) * w.numel() * w.element_size()
     return ms, nbytes / (ms * 1e-3) / 1e9
+
+
+def fold_time_ms(wl, inputs, reps=10):
+    """Phase-end fold (poetx_fold) at the workload's weight shape; None for int8."""
+    if wl.w == "i8":
+        return None
+    import torch
+    from orthogonal_reparameterized_amd import binding as B
+    from orthogonal_reparameterized_amd.step import LayerStep
+    st = LayerStep(wl, dict(inputs, x=inputs["x"][:64], dz=inputs["dz"][:64]), "mem")
+    st.cnp()
+    w_out = torch.empty_like(st.w_merged)
+    B.poetx_fold(st.layer, w_out)
+    _sync()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        B.poetx_fold(st.layer, w_out)
+    e1.record()
+    _sync()
+    return e0.elapsed_time(e1) / reps
+
+
+def adam_time_ms(wl, reps=20):
+    """poetx_adam_step over the layer's packed theta (both sides), float32 state."""
+    import torch
+    from orthogonal_reparameterized_amd import binding as B
+    n = (wl.d_in // wl.b + wl.d_out // wl.b) * (wl.b * (wl.b - 1) // 2)
+    th = torch.zeros(n, device="cuda")
+    g, m, v = torch.randn(n, device="cuda"), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    B.poetx_adam_step(th, g, m, v, lr=1e-3, step=1)
+    _sync()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(reps):
+        B.poetx_adam_step(th, g, m, v, lr=1e-3, step=t + 2)
+    e1.record()
+    _sync()
+    ms = e0.elapsed_time(e1) / reps
+    return {"ms": ms, "params": n, "GB_s": 7 * 4 * n / (ms * 1e-3) / 1e9}
+
+
+def measured_peaks(wl):
+    """What this GPU sustains on a plain 1 GiB device copy and on the vendor library's
+    GEMM (torch.matmul, hipBLASLt) at the W' product's shape."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    _sync()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    _sync()
+    copy_gbs = 2 * n / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del a, b
+    m, k, nn = wl.n_tokens, wl.d_in, wl.d_out
+    x = torch.randn(m, k, device="cuda").to(torch.bfloat16)
+    w = torch.randn(nn, k, device="cuda").to(torch.bfloat16)
+    wt = w.t()
+    y = torch.empty(m, nn, dtype=torch.bfloat16, device="cuda")
+    for _ in range(10):
+        torch.matmul(x, wt, out=y)
+    _sync()
+    ms = None
+    for _ in range(5):  # the best of five batches of 20 (the library's clocks settle)
+        e0.record()
+        for _ in range(20):
+            torch.matmul(x, wt, out=y)
+        e1.record()
+        _sync()
+        t = e0.elapsed_time(e1) / 20
+        ms = t if ms is None else min(ms, t)
+    del x, w, wt, y
+    torch.cuda.empty_cache()
+    return {"copy_GB_s": copy_gbs, "library_gemm_TF_s": 2.0 * m * k * nn / (ms * 1e-3) / 1e12,
+            "library_gemm_ms": ms, "library_gemm_shape": [m, nn, k],
+            "how": "torch copy_ of 1 GiB (read + write bytes / time); torch.matmul bf16 (hipBLASLt) "
+                   "X[N][d_in] @ W^T[d_in][d_out], best of 5 batches of 20 launches"}
 
 
 def cpu_baseline(wl, inputs, target_s=15.0):
@@ -232,42 +410,31 @@ def cpu_baseline(wl, inputs, target_s=15.0):
             "sample": f"{what}, {steps} (CNP fwd, layer fwd, layer bwd, CNP bwd) in float64 NumPy, {t:.1f} s"}
 
 
-def load_traffic(kernel, workload_key):
-    """HBM bytes per launch from the committed counter summary, if it matches this source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_workload{workload_key}_counters.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.strip().split("=", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_sha() or "traffic_bytes_per_launch" not in kv:
-        return None
-    return float(kv["traffic_bytes_per_launch"])
-
-
 def copy_calibration():
     import torch
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     a.fill_(1)
     b = torch.empty_like(a)
-    torch.cuda.synchronize()
+    _sync()
     for _ in range(3):
         b.copy_(a)
-    torch.cuda.synchronize()
+    _sync()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(10):
         b.copy_(a)
     e1.record()
-    torch.cuda.synchronize()
+    _sync()
     ms = e0.elapsed_time(e1) / 10
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
                       "GB_s_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}))
 
 
+# ------------------------------------------------------------ profile summaries ----
+KERNEL_SYMBOL_CANDIDATES = {  # kernel label -> substrings of the symbols that may carry it
+    "gemm_nt": ("k_gemm4<", "k_gemm2<0,"),
+}
 KERNEL_SYMBOL = {  # kernel label -> substring of its symbol in traces (workload 3 shapes)
     "gemm_nt": "k_gemm2<0,", "gemm_nn": "k_gemm_pp<1,", "block_apply": "k_block_reg<256,32,7,false,8>",
     "block_apply_t": "k_block_reg<256,32,7,true,8>", "block_grad": "k_block_grad_stream<256,4,64,2>",
@@ -284,10 +451,29 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
+def load_traffic(kernel, workload_key):
+    """HBM bytes per launch from the committed counter summary, if it matches this source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_workload{workload_key}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def _short(name):
+    return name.replace("(poetx::KArgs)", "").replace("poetx::", "").replace("void ", "")[:95]
+
+
 def summarize_trace(db, bench_json=None):
     """Markdown kernel table of a --kernel-trace database; with the JSON line that the
     traced bench.py run printed, also the dominant kernel's trace average next to the
-    event-timed average that run reported (the last launches are the event-timed ones)."""
+    recorder's average from the same timed steps."""
     import sqlite3
     con = sqlite3.connect(db)
     rows = con.execute("select name, count(*), avg(duration), min(duration), max(duration), "
@@ -296,70 +482,100 @@ def summarize_trace(db, bench_json=None):
     print("| kernel | calls | avg us | min us | max us | share |")
     print("|---|---:|---:|---:|---:|---:|")
     for name, n, avg, mn, mx, sm in rows:
-        short = name.replace("(poetx::KArgs)", "").replace("poetx::", "")[:90]
-        print(f"| `{short}` | {n} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | {100 * sm / tot:.1f}% |")
-    if bench_json:
-        line = [ln for ln in open(bench_json) if ln.startswith("{")][-1]
-        d = json.loads(line)
-        roof = d.get("roofline") or {}
-        if "phases" not in d:  # the CNP microbenchmark: no per-label phases
-            print()
-            print(f"bench.py in this run: forward {d['fwd_ms']:.3f} ms, backward {d['bwd_ms']:.3f} ms per call "
-                  f"over {d['config']['nblocks']} blocks of b = {d['config']['b']}: "
-                  f"{d['value'] / 1e3:.0f} K blocks/s.")
-            return
-        ph = d["phases"][d["config"]["variant"]][roof["kernel"]]
-        n_ev = int(round(ph["launches_per_step"] * d["steps"]))
-        if roof["kernel"] == "gemm_nt" and d["variants"][d["config"]["variant"]].get("w_merged_t"):
-            n_ev *= 2  # the backward product runs the same kernel (on W'^T) in the fast variant
-        sym = KERNEL_SYMBOL[roof["kernel"]].replace(" ", "")
-        durs = [r[1] for r in con.execute("select name, duration from kernels order by start")
-                if sym in r[0].replace(" ", "")]
-        last = durs[-n_ev:]
+        print(f"| `{_short(name)}` | {n} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | {100 * sm / tot:.1f}% |")
+    if not bench_json:
+        return
+    line = [ln for ln in open(bench_json) if ln.startswith("{")][-1]
+    d = json.loads(line)
+    if "phases" not in d:  # the CNP microbenchmark
         print()
-        print(f"Dominant kernel `{roof['kernel']}` (`{sym}`) in this run: trace average over all "
-              f"{len(durs)} launches {sum(durs) / len(durs) / 1e3:.1f} us, over the last {len(last)} "
-              f"(the event-timed ones) {sum(last) / len(last) / 1e3:.1f} us; bench.py's event-timed "
-              f"average {roof['avg_launch_ms'] * 1e3:.1f} us -> {roof['achieved']:.0f} TFLOP/s, "
-              f"frac {roof['frac']:.3f}; step {d['ms_per_step']:.4f} ms, {d['value'] / 1e6:.3f} M tokens/s.")
+        print(f"bench.py in this run: forward {d['fwd_ms']:.3f} ms, backward {d['bwd_ms']:.3f} ms per call "
+              f"over {d['config']['nblocks']} blocks of b = {d['config']['b']}: "
+              f"{d['value'] / 1e3:.0f} K blocks/s.")
+        return
+    roof = d["roofline"]
+    names = [r[0].replace(" ", "") for r in rows]
+    sym = next(sm for sm in KERNEL_SYMBOL_CANDIDATES[roof["kernel"]] if any(sm in nm for nm in names))
+    durs = [r[1] for r in con.execute("select name, duration from kernels order by start")
+            if sym in r[0].replace(" ", "")]
+    # the traced run (--only-head, one variant): W warm-up steps, K timed steps (this kernel
+    # recorded), 1 + K unrecorded, 1 + K all recorded, then 5 cold-cache steps
+    k, w = d["steps"], d["warmup"]
+    per = len(durs) / (w + 3 * k + 2 + 5)
+    c = int(round(per))
+    timed = durs[w * c:(w + k) * c]
+    unrec = durs[(w + k + 1) * c:(w + 2 * k + 1) * c]
+    allrec = durs[(w + 2 * k + 2) * c:(w + 3 * k + 2) * c]
+
+    def avg(v):
+        return sum(v) / len(v) / 1e3 if v else float("nan")
+    print()
+    print(f"Dominant kernel `{roof['kernel']}` (`{sym}`, {c} launch(es) per step): trace average over the "
+          f"timed steps' launches {avg(timed):.1f} us, over the unrecorded steps' {avg(unrec):.1f} us, over "
+          f"the all-recorded steps' {avg(allrec):.1f} us; bench.py's event-timed average over its "
+          f"{roof['launches']} launches in the timed steps {roof['avg_launch_ms'] * 1e3:.1f} us -> "
+          f"{roof['achieved']:.0f} TFLOP/s, frac {roof['frac']:.3f}.  Step {d['ms_per_step']:.4f} ms "
+          f"(median {d['step_ms']['median']:.4f}), {d['value'] / 1e6:.3f} M tokens/s; unrecorded "
+          f"{d['variants'][d['config']['variant']]['ms_per_step_unrecorded']:.4f} ms.")
 
 
-def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, label=DOMINANT):
+def _pmc_rows(db, counter=None):
     import sqlite3
+    con = sqlite3.connect(db)
+    q = "select kernel_name, counter_name, count(*), avg(value) from counters_collection"
+    if counter:
+        return con.execute(q + " where counter_name = ? group by kernel_name, counter_name", (counter,)).fetchall()
+    return con.execute(q + " group by kernel_name, counter_name").fetchall()
 
-    def per_kernel(db, counter):
-        con = sqlite3.connect(db)
-        return con.execute("select kernel_name, count(*), avg(value) from counters_collection "
-                           "where counter_name = ? group by kernel_name", (counter,)).fetchall()
 
+def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, bench_json=None):
+    """HBM bytes per dispatch of every kernel in the run, scaled by what the same counters
+    read on a 1 GiB copy; with the run's JSON line, next to the algorithmic bytes."""
     def pick(rows, match):
-        for name, n, v in rows:
+        for name, _, n, v in rows:
             if match in name.replace(" ", ""):
                 return n, v
         raise SystemExit(f"no kernel matching {match}")
 
     copy_kib = float(1 << 30) / 1024
-    _, cf = pick(per_kernel(copy_fetch_db, "FETCH_SIZE"), "copyBuffer")
-    _, cw = pick(per_kernel(copy_write_db, "WRITE_SIZE"), "copyBuffer")
+    _, cf = pick(_pmc_rows(copy_fetch_db, "FETCH_SIZE"), "copyBuffer")
+    _, cw = pick(_pmc_rows(copy_write_db, "WRITE_SIZE"), "copyBuffer")
     f_scale, w_scale = copy_kib / cf, copy_kib / cw
-    sym = KERNEL_SYMBOL[label]
-    nf, f = pick(per_kernel(fetch_db, "FETCH_SIZE"), sym)
-    nw, w = pick(per_kernel(write_db, "WRITE_SIZE"), sym)
-    print(f"kernel_label = {label}")
-    print(f"kernel_symbol_match = {sym}")
-    print(f"dispatches_fetch = {nf}")
-    print(f"dispatches_write = {nw}")
-    print(f"fetch_kib_per_dispatch_raw = {f:.1f}")
-    print(f"write_kib_per_dispatch_raw = {w:.1f}")
+    fetch = {r[0]: (r[2], r[3]) for r in _pmc_rows(fetch_db, "FETCH_SIZE")}
+    write = {r[0]: (r[2], r[3]) for r in _pmc_rows(write_db, "WRITE_SIZE")}
     print(f"copy_fetch_kib_raw = {cf:.1f}  (1 GiB copy reads {copy_kib:.0f} KiB)")
     print(f"copy_write_kib_raw = {cw:.1f}  (1 GiB copy writes {copy_kib:.0f} KiB)")
     print(f"fetch_scale = {f_scale:.4f}")
     print(f"write_scale = {w_scale:.4f}")
+    print()
+    print("| kernel | dispatches | fetch MB | write MB | traffic MB per dispatch |")
+    print("|---|---:|---:|---:|---:|")
+    for name in sorted(fetch, key=lambda k: -fetch[k][1]):
+        nf, f = fetch[name]
+        _, w = write.get(name, (0, 0.0))
+        tr = (f * f_scale + w * w_scale) * 1024
+        print(f"| `{_short(name)}` | {nf} | {f * f_scale * 1024 / 1e6:.1f} | {w * w_scale * 1024 / 1e6:.1f} | "
+              f"{tr / 1e6:.1f} |")
+    sym = KERNEL_SYMBOL[DOMINANT]
+    _, f = pick(_pmc_rows(fetch_db, "FETCH_SIZE"), sym)
+    _, w = pick(_pmc_rows(write_db, "WRITE_SIZE"), sym)
+    print()
+    print(f"kernel_label = {DOMINANT}")
+    print(f"kernel_symbol_match = {sym}")
     print(f"traffic_bytes_per_launch = {(f * f_scale + w * w_scale) * 1024:.0f}")
     print(f"kernel_sources = {' + '.join(os.path.relpath(f, ROOT) for f in KERNEL_SOURCES)}")
     print(f"kernel_source_sha = {kernel_source_sha()}")
 
 
+def summarize_pmc(*dbs):
+    print("| kernel | counter | dispatches | average per dispatch |")
+    print("|---|---|---:|---:|")
+    for db in dbs:
+        for name, ctr, n, v in sorted(_pmc_rows(db), key=lambda r: (r[0], r[1])):
+            print(f"| `{_short(name)}` | {ctr} | {n} | {v:.4g} |")
+
+
+# ---------------------------------------------------------------- workloads ----
 def cnp_bench(wl, steps, warmup):
     """Workload 2: CNP forward (G in bf16) and backward on independent blocks."""
     import torch
@@ -371,36 +587,54 @@ def cnp_bench(wl, steps, warmup):
     del theta, dg
     g = torch.empty((wl.nblocks, wl.b, wl.b), dtype=torch.bfloat16, device="cuda")
     dth = torch.empty_like(th)
-    res = {}
+    res, per = {}, {}
     for name, fn in (("fwd", lambda: B.poetx_cnp(B.POETX_CNP_FWD, th, wl.b, g=g)),
                      ("bwd", lambda: B.poetx_cnp(B.POETX_CNP_BWD, th, wl.b, dg=dgt, dtheta=dth))):
         for _ in range(warmup):
             fn()
-        torch.cuda.synchronize()
+        _sync()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        for _ in range(steps):
+        for i in range(steps):
+            ev[i].record()
             fn()
-        torch.cuda.synchronize()
+        ev[steps].record()
+        _sync()
         res[name] = (time.perf_counter() - t0) * 1e3 / steps
+        per[name] = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     b, n = wl.b, wl.nblocks
-    # float32-equivalent flops: forward 2 b^3-products, backward 6 (each 2 b^3)
+    # method flops: forward 2 b^3-products (Horner), backward 6 (each 2 b^3)
     f_fwd, f_bwd = 4.0 * b ** 3 * n, 12.0 * b ** 3 * n
+    p = b * (b - 1) // 2
+    y_fwd, y_bwd = n * (4 * p + 2 * b * b), n * (4 * b * b + 8 * p)
     ms = res["fwd"] + res["bwd"]
-    out = {
+    del th, dgt, g, dth
+    torch.cuda.empty_cache()
+    return {
         "metric": "CNP fwd+bwd blocks/s (4096 x b=256)", "value": n / (ms * 1e-3), "unit": "blocks/s",
-        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (split-bf16 MFMA)", "data": "synthetic",
+        "ms_per_step": ms, "fwd_ms": res["fwd"], "bwd_ms": res["bwd"],
+        "fwd_ms_median": statistics.median(per["fwd"]), "bwd_ms_median": statistics.median(per["bwd"]),
         "config": {"workload": wl.name, "nblocks": n, "b": b},
-        "fwd_ms": res["fwd"], "bwd_ms": res["bwd"],
-        "fwd_tflops_f32_equiv": f_fwd / (res["fwd"] * 1e-3) / 1e12,
-        "bwd_tflops_f32_equiv": f_bwd / (res["bwd"] * 1e-3) / 1e12,
-        # three bf16 MFMA passes per float32-accurate product
-        "roofline": {"bound": "mfma", "achieved": 3 * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": 3 * (f_fwd + f_bwd) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                     "traffic": None, "kernel": "cnp (all launches, bf16 MFMA passes)"},
+        "fwd_frac_mfma_method_flops": f_fwd / (res["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "bwd_frac_mfma_method_flops": f_bwd / (res["bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "fwd_frac_hbm": y_fwd / (res["fwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "bwd_frac_hbm": y_bwd / (res["bwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "floor_ms_single_pass": (max(f_fwd / 2.5e15, y_fwd / 8e12) + max(f_bwd / 2.5e15, y_bwd / 8e12)) * 1e3,
     }
-    print(json.dumps(out))
+
+
+def layer_summary(wl, steps, warmup):
+    """One layer workload's variants, for the lines beside the head workload."""
+    from orthogonal_reparameterized_amd import workloads as WL
+    inputs = WL.make_layer_inputs(wl)
+    out = {"config": {"workload": wl.name, "n_tokens": wl.n_tokens, "d_in": wl.d_in, "d_out": wl.d_out,
+                      "b": wl.b, "weight": wl.w}}
+    for variant in wl.variants:
+        keep_wt = variant == "fast" and wl.w == "bf16"
+        v, ph, _ = run_variant(wl, inputs, variant, steps, warmup, keep_wt=keep_wt)
+        v["dominant"] = {k: ph[k] for k in ("gemm_nt", "gemm_nn") if k in ph}
+        out[variant] = v
+    return out
 
 
 def main():
@@ -411,16 +645,22 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mem", action="store_true")
+    ap.add_argument("--only-head", action="store_true",
+                    help="only the head workload's headline variant (and mem unless --no-mem)")
     ap.add_argument("--no-wt", action="store_true", help="fast variant without the W'^T copy")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", nargs="+", metavar="DB [BENCH_JSON]")
-    ap.add_argument("--summarize-counters", nargs=4, metavar="DB")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DB")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DB")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace[:2])
         return
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters[:5])
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -430,49 +670,43 @@ def main():
         copy_calibration()
         return
 
-    import torch
-
     from orthogonal_reparameterized_amd import workloads as WL
-    from orthogonal_reparameterized_amd.step import LayerStep
 
     wl = WL.WORKLOADS[args.workload]
     if wl.nblocks:
-        cnp_bench(wl, args.steps, args.warmup)
+        r = cnp_bench(wl, args.steps, args.warmup)
+        r.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                  "scaling": "weak", "vs_baseline": None, "dtype": "f32 (split-bf16 MFMA)", "data": "synthetic"})
+        print(json.dumps(r))
         return
     inputs = WL.make_layer_inputs(wl)
     n = wl.n_tokens
-    variants = {}
-    phases = {}
+    variants, phases = {}, {}
+    head = "fast" if "fast" in wl.variants else "mem"
+    cold = None
     for variant in wl.variants:
         if variant == "mem" and args.no_mem and "fast" in wl.variants:
             continue
-        # the fast variant also keeps W'^T from the merge (one more weight copy, the
-        # backward's product then reads W' k-contiguous); mem stays memory-lean
+        # the headline fast variant also keeps W'^T from the merge (one more weight copy; the
+        # backward's product then reads W' k-contiguous) and the gathered input X~
         keep_wt = variant == "fast" and wl.w == "bf16" and not args.no_wt
-        st = LayerStep(wl, inputs, variant, transposed_weight=keep_wt)
-        ms = time_steps(st, args.steps, args.warmup)
-        prof, prof_wall = profile_steps(st, args.steps)
-        alg = algorithmic(wl, variant, n)
-        variants[variant] = {"ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3), "w_merged_t": keep_wt,
-                             "kept_x": st.saved_x is not None,
-                             "layer_roofline_ms": layer_roofline_ms(wl, variant, n),
-                             "roofline_frac": layer_roofline_ms(wl, variant, n) / ms,
-                             "ms_per_step_with_event_hooks": prof_wall}
-        ph = {}
-        for name, (launches, avg_ms) in sorted(prof.items()):
-            ph[name] = {"launches_per_step": launches, "avg_ms": avg_ms}
-            if name in alg:
-                f, y = alg[name]
-                per = launches if launches else 1
-                ph[name]["tflops"] = f / per / (avg_ms * 1e-3) / 1e12
-                ph[name]["gbs"] = y / per / (avg_ms * 1e-3) / 1e9
-        phases[variant] = ph
-        del st
-        torch.cuda.empty_cache()
+        v, ph, c = run_variant(wl, inputs, variant, args.steps, args.warmup, keep_wt=keep_wt,
+                               cold_steps=5 if variant == head else 0)
+        variants[variant], phases[variant] = v, ph
+        if variant == head:
+            cold = c
+    if not args.only_head and "fast" in wl.variants:
+        # the pages' own fast variant keeps only B; and the literal chain without the two
+        # activation permutations
+        v, ph, _ = run_variant(wl, inputs, "fast", args.steps, args.warmup, keep_wt=False, keep_x=False)
+        variants["fast_pages"], phases["fast_pages"] = v, ph
+        v, ph, _ = run_variant(wl, inputs, "fast", args.steps, args.warmup,
+                               keep_wt=wl.w == "bf16" and not args.no_wt, perms=False)
+        variants["fast_null_perm"], phases["fast_null_perm"] = v, ph
 
-    head = "fast" if "fast" in variants else "mem"
     ms = variants[head]["ms_per_step"]
-    dom = phases[head].get(DOMINANT)
+    dom = phases[head].get(DOMINANT + " (timed steps)")
+    peaks = measured_peaks(wl)
     roof = None
     if dom:
         flops_launch = 2.0 * n * wl.d_in * wl.d_out
@@ -480,7 +714,15 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(DOMINANT, wl.key),
                 "kernel": DOMINANT, "avg_launch_ms": dom["avg_ms"],
-                "algorithmic_flops_per_launch": flops_launch}
+                "launches": int(round(dom["launches_per_step"] * args.steps)),
+                "algorithmic_flops_per_launch": flops_launch,
+                "measured_peak": peaks["library_gemm_TF_s"],
+                "frac_of_measured_peak": achieved / peaks["library_gemm_TF_s"],
+                "timing": "dispatch-bound start/stop events on this kernel's launches inside the timed steps"}
+    for ph in list(phases.values()) + ([cold] if cold else []):
+        for e in ph.values():
+            if "gbs" in e:
+                e["frac_hbm_measured_copy"] = e["gbs"] / peaks["copy_GB_s"]
     merge_ms, merge_gbs = merge_time_ms(wl, inputs)
     merge_t_ms, merge_t_gbs = merge_time_ms(wl, inputs, with_t=True) if wl.w == "bf16" else (None, None)
     out = {
@@ -490,15 +732,26 @@ def main():
         "config": {"workload": wl.name, "n_tokens": n, "d_in": wl.d_in, "d_out": wl.d_out, "b": wl.b,
                    "variant": head, "activation_permutations": wl.perms, "weight": wl.w},
         "roofline": roof,
+        "step_ms": variants[head]["step_ms"],
         "variants": variants,
         "phases": phases,
+        "phases_cold_cache": cold,
+        "measured_peaks": peaks,
         "merge_per_phase": {"ms": merge_ms, "GB_s": merge_gbs,
                             "with_transpose_ms": merge_t_ms, "with_transpose_GB_s": merge_t_gbs,
                             "fold_ms": fold_time_ms(wl, inputs)},
         "optimizer_per_step": adam_time_ms(wl),
     }
+    del inputs
+    if not args.only_head:
+        others = {}
+        for key in (4, 5, 6):
+            if key != args.workload:
+                others[str(key)] = layer_summary(WL.WORKLOADS[key], max(5, args.steps // 2), 3)
+        others["2"] = cnp_bench(WL.WORKLOADS[2], max(5, args.steps // 2), 2)
+        out["other_workloads"] = others
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(wl, inputs)
+        out["cpu_baseline"] = cpu_baseline(wl, WL.make_layer_inputs(wl))
     print(json.dumps(out))
 
 

@@ -85,8 +85,9 @@ typedef struct {
   int32_t g_dtype;             /* dtype of g_r / g_p: F32 or BF16 (== act_dtype)     */
   int32_t variant;             /* poetx_variant                                     */
   const void *w_merged;        /* [d_out][d_in] W' from poetx_merge_perm            */
-  const void *w_merged_t;      /* optional [d_in][d_out] copy of W'^T (BF16 only), or
-                                  NULL; when given, the backward's dA = dB.W' reads it
+  const void *w_merged_t;      /* optional [d_in][d_out] copy of W'^T (BF16 only: set
+                                  with an I8 W' it is POETX_ERR_INVALID_ARG), or NULL;
+                                  when given, the backward's dA = dB.W' reads it
                                   k-contiguous (faster, one more weight copy)          */
   const float *w_scale;        /* [d_out] per-row scale of an I8 W', else NULL      */
   const int32_t *perm_in;      /* [d_in]  or NULL (identity)                        */
@@ -216,15 +217,24 @@ const char *poetx_status_string(int status);
 const char *poetx_version(void);
 
 /*
- * Measurement hooks (not part of the layer's math).  poetx_prof_enable(1)
- * makes every later kernel launch of the library record a pair of HIP events
- * on its stream; poetx_prof_read() synchronizes those events and writes one
- * line per kernel name, "name launches total_ms\n", into buf (truncated to
- * len bytes, NUL-terminated), then clears the record.  poetx_prof_enable(0)
- * stops recording.  Host-side state shared by all callers; not thread-safe.
- * Returns POETX_OK or POETX_ERR_HIP.
+ * Measurement hooks (not part of the layer's math).  poetx_prof_enable(1) turns on the
+ * CALLING THREAD's recorder: every later kernel launch that this thread makes through
+ * the library carries a start and a stop event bound to the dispatch itself
+ * (hipExtLaunchKernel), so a recorded duration is that kernel's own execution time and
+ * no marker packet is placed between kernels (the events carry no system-scope fence, so
+ * recording leaves the caches alone).  poetx_prof_read() synchronizes this
+ * thread's recorded events and writes one line per kernel label,
+ * "label launches total_ms min_ms max_ms\n", into buf (truncated to len bytes,
+ * NUL-terminated), then clears this thread's record.  poetx_prof_enable(0) stops
+ * recording.  poetx_prof_only(label) limits this thread's recording to the launches with
+ * that label (NULL or "" = every launch): each recorded dispatch still waits on its
+ * events' bookkeeping (a few us of idle GPU before it), so a timing of one kernel inside
+ * a longer sequence records that kernel alone.  The recorder is thread-local: calls from
+ * different threads neither see nor disturb each other's records.  Returns POETX_OK or
+ * POETX_ERR_HIP.
  */
 int poetx_prof_enable(int32_t on);
+int poetx_prof_only(const char *label);
 int poetx_prof_read(char *buf, size_t len);
 
 #ifdef __cplusplus

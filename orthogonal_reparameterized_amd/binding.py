@@ -59,12 +59,13 @@ _lib.poetx_status_string.restype = ctypes.c_char_p
 _lib.poetx_version.restype = ctypes.c_char_p
 _lib.poetx_prof_enable.argtypes = [_i32]
 _lib.poetx_prof_read.argtypes = [ctypes.c_char_p, _sz]
+_lib.poetx_prof_only.argtypes = [ctypes.c_char_p]
 for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold", "poetx_adam_step",
-           "poetx_prof_enable", "poetx_prof_read"):
+           "poetx_prof_enable", "poetx_prof_only", "poetx_prof_read"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold", "poetx_adam_step",
-            "poetx_status_string", "poetx_version", "poetx_prof_enable", "poetx_prof_read")
+            "poetx_status_string", "poetx_version", "poetx_prof_enable", "poetx_prof_only", "poetx_prof_read")
 
 
 class PoetxError(RuntimeError):
@@ -111,16 +112,20 @@ def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-# A per-device scratch tensor, grown on demand and reused between calls on the
-# same stream (stream order makes reuse safe).
+# Scratch tensors keyed by (device, stream): each is allocated while its stream is the
+# current one and only ever used by calls on that stream, so the caching allocator's
+# stream ordering makes both the reuse between calls and the release of an outgrown
+# buffer safe.  Layers driven on different streams get different workspaces.
 _ws_cache: dict = {}
 
 
 def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
-    key = (dev.index if dev.index is not None else torch.cuda.current_device())
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
     t = _ws_cache.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        with torch.cuda.device(idx):
+            t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=f"cuda:{idx}")
         _ws_cache[key] = t
     return t
 
@@ -301,14 +306,20 @@ def prof_enable(on: bool = True):
     _check(_lib.poetx_prof_enable(1 if on else 0), "poetx_prof_enable")
 
 
+def prof_only(label: Optional[str] = None):
+    """Record only the launches labelled `label` (None: every launch)."""
+    _check(_lib.poetx_prof_only(label.encode() if label else None), "poetx_prof_only")
+
+
 def prof_read() -> dict:
-    """{kernel name: (launches, total_ms)} since the last read."""
+    """{kernel label: (launches, total_ms, min_ms, max_ms)} recorded by this thread since
+    the last read."""
     buf = ctypes.create_string_buffer(1 << 16)
     _check(_lib.poetx_prof_read(buf, len(buf)), "poetx_prof_read")
     out = {}
     for line in buf.value.decode().splitlines():
-        name, n, ms = line.split()
-        out[name] = (int(n), float(ms))
+        name, n, ms, mn, mx = line.split()
+        out[name] = (int(n), float(ms), float(mn), float(mx))
     return out
 
 

@@ -11,70 +11,85 @@
 using namespace poetx;
 
 // ============================================================ measurement ====
+// Per-thread recorder of kernel durations (poetx_prof_enable / poetx_prof_read): each
+// launch made by this thread while it is on carries a start and a stop event bound to
+// the dispatch (launch_k in common.h).  Nothing here is shared between threads.
 namespace poetx {
 namespace {
 struct ProfRec {
   const char *name;
   hipEvent_t a, b;
 };
-bool g_prof = false;
-std::vector<ProfRec> g_recs;
-std::vector<hipEvent_t> g_pool;
-const char *g_pending = nullptr;
-hipEvent_t g_pending_ev = nullptr;
-
-hipEvent_t pool_get() {
-  if (!g_pool.empty()) {
-    hipEvent_t e = g_pool.back();
-    g_pool.pop_back();
-    return e;
+struct Recorder {
+  bool on = false;
+  std::string only;  // record only launches with this label ("" = every launch)
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;  // events are reused, never destroyed (the runtime may be
+                                 // gone by the time a thread's storage is torn down)
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    // timing-only events: without the system-scope fence an event would write back and
+    // invalidate the caches around every recorded dispatch (idle gaps of several us between
+    // kernels, and kernels that start on cold caches)
+    hipEvent_t e = nullptr;
+    return hipEventCreateWithFlags(&e, hipEventDisableSystemFence) == hipSuccess ? e : nullptr;
   }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
+};
+thread_local Recorder t_rec;
 }  // namespace
 
-bool prof_on() { return g_prof; }
-void prof_begin(const char *name, hipStream_t s) {
-  g_pending = name;
-  g_pending_ev = pool_get();
-  if (g_pending_ev) hipEventRecord(g_pending_ev, s);
+bool prof_on() { return t_rec.on; }
+bool prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop) {
+  if (!t_rec.only.empty() && t_rec.only != name) return false;
+  *start = t_rec.get();
+  *stop = t_rec.get();
+  if (*start && *stop) return true;
+  if (*start) t_rec.pool.push_back(*start);
+  if (*stop) t_rec.pool.push_back(*stop);
+  *start = *stop = nullptr;
+  return false;
 }
-void prof_end(hipStream_t s) {
-  hipEvent_t e = pool_get();
-  if (!g_pending_ev || !e) return;
-  hipEventRecord(e, s);
-  g_recs.push_back({g_pending, g_pending_ev, e});
-  g_pending_ev = nullptr;
-}
+void prof_commit(const char *name, hipEvent_t start, hipEvent_t stop) { t_rec.recs.push_back({name, start, stop}); }
 }  // namespace poetx
 
 extern "C" int poetx_prof_enable(int32_t on) {
-  g_prof = on != 0;
+  t_rec.on = on != 0;
+  return POETX_OK;
+}
+
+extern "C" int poetx_prof_only(const char *label) {
+  t_rec.only = label ? label : "";
   return POETX_OK;
 }
 
 extern "C" int poetx_prof_read(char *buf, size_t len) {
-  struct Acc { std::string name; long n; double ms; };
+  struct Acc { std::string name; long n; double ms, mn, mx; };
   std::vector<Acc> acc;
   int st = POETX_OK;
-  for (auto &r : g_recs) {
+  for (auto &r : t_rec.recs) {
     float ms = 0.f;
     if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
       st = POETX_ERR_HIP;
     bool found = false;
     for (auto &a : acc)
-      if (a.name == r.name) { a.n++; a.ms += ms; found = true; break; }
-    if (!found) acc.push_back({r.name, 1, (double)ms});
-    g_pool.push_back(r.a);
-    g_pool.push_back(r.b);
+      if (a.name == r.name) {
+        a.n++; a.ms += ms; a.mn = ms < a.mn ? ms : a.mn; a.mx = ms > a.mx ? ms : a.mx;
+        found = true;
+        break;
+      }
+    if (!found) acc.push_back({r.name, 1, (double)ms, (double)ms, (double)ms});
+    t_rec.pool.push_back(r.a);
+    t_rec.pool.push_back(r.b);
   }
-  g_recs.clear();
+  t_rec.recs.clear();
   std::string out;
   char line[256];
   for (auto &a : acc) {
-    snprintf(line, sizeof line, "%s %ld %.6f\n", a.name.c_str(), a.n, a.ms);
+    snprintf(line, sizeof line, "%s %ld %.6f %.6f %.6f\n", a.name.c_str(), a.n, a.ms, a.mn, a.mx);
     out += line;
   }
   if (buf && len) {
@@ -384,6 +399,11 @@ struct Plan {
   size_t ae;  // activation element size
 };
 
+// Block products and gradients of blocks of size bs run on MFMA for bf16 activations when
+// bs is 64 or a multiple of 128 (the streaming kernels, or the batched MFMA engines for
+// other multiples of 128); every other size on the float32 vector-ALU product.
+bool blk_mfma(const Plan &p, int64_t bs) { return p.act == POETX_BF16 && (bs == 64 || bs % 128 == 0); }
+
 int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
   if (!L || n_tokens < 0) return POETX_ERR_INVALID_ARG;
   if (L->d_in < 1 || L->d_out < 1) return POETX_ERR_INVALID_ARG;
@@ -395,6 +415,8 @@ int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
   if (L->w_dtype == POETX_I8) {
     if (L->act_dtype != POETX_BF16) return POETX_ERR_UNSUPPORTED;
     if (L->variant == POETX_FAST) return POETX_ERR_UNSUPPORTED;
+    // a kept W'^T is a BF16-only option: the int8 backward transposes W' itself
+    if (L->w_merged_t) return POETX_ERR_INVALID_ARG;
   } else if (L->w_dtype != L->act_dtype) {
     return POETX_ERR_UNSUPPORTED;
   }
@@ -406,7 +428,9 @@ int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
   p.act = L->act_dtype; p.w = L->w_dtype; p.gdt = L->g_dtype;
   p.mem = L->variant == POETX_MEM;
   p.ae = dtype_size(p.act);
-  p.mfma = p.act == POETX_BF16 && p.b % 128 == 0 && p.din % 128 == 0 && p.dout % 128 == 0;
+  // the W' products run on MFMA whenever both widths tile by 128, whatever b is; each
+  // block product picks its own kernel by its block size (blk_mfma)
+  p.mfma = p.act == POETX_BF16 && p.din % 128 == 0 && p.dout % 128 == 0;
   return POETX_OK;
 }
 
@@ -423,7 +447,7 @@ int check_layer_ptrs(const poetx_layer *L) {
 int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *X, const void *G, void *Y,
                  bool transposed, const float *scaleN, hipStream_t s, const void *Gt = nullptr) {
   if (p.N == 0 || nb == 0) return POETX_OK;
-  const bool mfma = p.mfma && bs % 128 == 0;
+  const bool mfma = blk_mfma(p, bs);
   if (mfma && bs == 512) {
     // At b = 512 each block product is a K = N = 512 GEMM: the 256 x 256 W' kernels,
     // batched over blocks, read X twice (two column tiles); a block kernel with a
@@ -442,7 +466,7 @@ int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *
   if (mfma && block_stream_supported(bs, ld, nb, p.N))
     return block_stream((const bf16_t *)X, (const bf16_t *)G, (bf16_t *)Y, p.N, ld, nb, bs, transposed, scaleN,
                         transposed ? "block_apply_t" : "block_apply", s);
-  if (mfma) {
+  if (mfma && bs % 128 == 0) {
     MfmaDesc m;
     m.M = p.N; m.N = bs; m.K = bs; m.batch = nb;
     m.A = X; m.a_km = false; m.lda = ld; m.sAb = bs;
@@ -490,12 +514,16 @@ int block_apply(const Plan &p, int64_t d, const void *X, const void *G, void *Y,
 // them, so every operand slice is read by four workgroups; there the MFMA engine's 256 x 256
 // tiles (two readers per slice) split over tokens take over.
 bool grad_streams(const Plan &p, int64_t ld, int64_t nb, int64_t bs) {
-  return p.mfma && bs % 128 == 0 && bs < 512 && p.N > 0 && block_grad_stream_supported(bs, ld, nb, p.N);
+  return blk_mfma(p, bs) && bs < 512 && p.N > 0 && block_grad_stream_supported(bs, ld, nb, p.N);
 }
+
+// the batched MFMA engine (256 x 256 or 128 x 128 tiles split over tokens) takes the
+// gradients of blocks of a multiple of 128 that the streaming kernel does not
+bool grad_engine(const Plan &p, int64_t bs) { return blk_mfma(p, bs) && bs % 128 == 0; }
 
 int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of the split-k kernel
   if (p.N == 0) return 1;
-  if (!p.mfma || bs % 128) {
+  if (!grad_engine(p, bs)) {
     // vector-ALU product, one launch per chunk: chunks of 1024 tokens keep each float32
     // accumulation short (a sum over millions of tokens in one chain loses digits), with
     // at most 4096 partials and 256 MB of them
@@ -527,7 +555,7 @@ int grad_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *X
   if (nb == 0) return POETX_OK;
   if (grad_streams(p, ld, nb, bs))
     return block_grad_stream((const bf16_t *)X, (const bf16_t *)Y, parts, p.N, ld, nb, bs, s);
-  if (p.mfma && bs % 128 == 0) {
+  if (grad_engine(p, bs)) {
     const int64_t kc = grad_chunk(p, nb, bs);
     MfmaDesc m;
     m.M = bs; m.N = bs; m.K = p.N; m.batch = nb;

@@ -2,6 +2,7 @@
 // workspace carving.  Not part of the public ABI (see include/poetx.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -19,19 +20,25 @@ namespace poetx {
     if (_st != POETX_OK) return _st;     \
   } while (0)
 
-// Launch bookkeeping: every kernel launch goes through begin_launch / end_launch,
-// which check for launch errors and, when measurement is on, bracket the launch
-// with HIP events (see poetx_prof_enable).
-void prof_begin(const char *name, hipStream_t s);
-void prof_end(hipStream_t s);
+// Launch bookkeeping: every kernel launch goes through launch_k, which checks for
+// launch errors and, while the calling thread's measurement recorder is on (see
+// poetx_prof_enable), attaches a start and a stop event to the dispatch itself
+// (hipExtLaunchKernel), so the recorded time is the kernel's own execution with no
+// marker packets between kernels.  The recorder is per thread: no state is shared
+// between callers.
 bool prof_on();
+// a pair from this thread's pool when a launch labelled `name` is to be recorded
+bool prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop);
+void prof_commit(const char *name, hipEvent_t start, hipEvent_t stop);
 
-template <typename F>
-inline int launch(const char *name, hipStream_t s, F &&f) {
-  if (prof_on()) prof_begin(name, s);
-  f();
-  hipError_t e = hipGetLastError();
-  if (prof_on()) prof_end(s);
+template <typename... KP, typename... Args>
+inline int launch_k(const char *name, hipStream_t s, void (*kern)(KP...), dim3 grid, dim3 block, size_t lds,
+                    Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool rec = prof_on() && prof_events(name, &e0, &e1);
+  hipExtLaunchKernelGGL(kern, grid, block, (std::uint32_t)lds, s, e0, e1, 0, args...);
+  const hipError_t e = hipGetLastError();
+  if (rec) prof_commit(name, e0, e1);
   return e == hipSuccess ? POETX_OK : POETX_ERR_HIP;
 }
 

@@ -159,8 +159,10 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void k_block_reg(BSArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
 }
 // b = 256 uses 8 consumers (64 registers of G each, 2 x 2 accumulator patches), 32-token
-// tiles and a 7-stage ring; b = 128 4 consumers, 64-token tiles and 4 stages.  With the
-// output staging that is 128 or 80 KB of LDS.
+// tiles and a 7-stage ring; b = 128 and 64 4 consumers, 64-token tiles and 4 stages.  With
+// the output staging that is 128, 80 or 40 KB of LDS.
+template __global__ void k_block_reg<64, 64, 4, false>(BSArgs);
+template __global__ void k_block_reg<64, 64, 4, true>(BSArgs);
 template __global__ void k_block_reg<128, 64, 4, false>(BSArgs);
 template __global__ void k_block_reg<128, 64, 4, true>(BSArgs);
 template __global__ void k_block_reg<256, 32, 7, false, 8>(BSArgs);
@@ -172,11 +174,11 @@ static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
   static std::atomic<uint64_t> attr{0};
   POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_block_reg<B, T, NST, TRANS, NCW>), lds, attr));
   const dim3 grid((unsigned)(a.nb * a.P));
-  return launch(name, s, [&] { k_block_reg<B, T, NST, TRANS, NCW><<<grid, 64 * (NCW + 2), lds, s>>>(a); });
+  return launch_k(name, s, k_block_reg<B, T, NST, TRANS, NCW>, grid, 64 * (NCW + 2), lds, a);
 }
 
 bool block_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens) {
-  if (b != 128 && b != 256) return false;
+  if (b != 64 && b != 128 && b != 256) return false;
   if (nb < 1 || nb * b > ld || ld % 8) return false;
   return (n_tokens + 64) * ld * 2 < 0x7fffffff;
 }
@@ -189,13 +191,14 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
   a.N = n_tokens; a.d = ld; a.nb = (int)nb;
   a.X = X; a.G = G; a.Y = Y; a.scaleN = scaleN;
   const int cus = device_cus() > 0 ? device_cus() : 256;
-  if (b == 128 || b == 256) {
+  if (b == 64 || b == 128 || b == 256) {
     // one workgroup per (token partition, block), about one per CU in total
     const int tt = b == 256 ? 32 : 64;
     const int64_t ntile = (n_tokens + tt - 1) / tt;
     int64_t P = cus / a.nb;
     if (P > ntile) P = ntile;
     a.P = (int)(P < 1 ? 1 : P);
+    if (b == 64) return transposed ? run_br<64, 64, 4, true>(a, name, s) : run_br<64, 64, 4, false>(a, name, s);
     if (b == 128) return transposed ? run_br<128, 64, 4, true>(a, name, s) : run_br<128, 64, 4, false>(a, name, s);
     return transposed ? run_br<256, 32, 7, true, 8>(a, name, s) : run_br<256, 32, 7, false, 8>(a, name, s);
   }
@@ -205,8 +208,8 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
 
 // Streaming block gradient: parts[p][j][r][c] = sum over the token tiles t = p, p+P, ...
 // of Xs_j[t]^T dY_j[t], for every b x b block j (r indexes columns of Xs_j, c of dY_j).
-// Each workgroup owns one 128 x 128 slice (rs, cs) of one block's gradient and keeps it
-// in registers while T-token tiles of both operands stream through a 4-stage LDS ring
+// Each workgroup owns one S x S slice (rs, cs) of one block's gradient, S = min(b, 128),
+// and keeps it in registers while T-token tiles of both operands stream through a 4-stage LDS ring
 // (two producer waves that only issue the global->LDS loads).  The P partials per block are summed later in
 // a fixed order.
 struct BGArgs {
@@ -217,7 +220,7 @@ struct BGArgs {
 
 template <int B, int NST, int T, int NPW>
 __global__ __launch_bounds__(64 * (4 + NPW)) void k_block_grad_stream(BGArgs a) {
-  constexpr int NCW = 4, S = 128, KH = T / 32;
+  constexpr int NCW = 4, S = B < 128 ? B : 128, KH = T / 32;
   constexpr int NSL = (B / S) * (B / S);
   constexpr int WT = S / 2, F = WT / 16;  // 2 x 2 waves of 64 x 64
   constexpr int TILE = T * S;             // elements per operand tile
@@ -305,23 +308,24 @@ __global__ __launch_bounds__(64 * (4 + NPW)) void k_block_grad_stream(BGArgs a) 
 }
 // ring of BG_NST stages of two BG_T-token operand tiles, BG_NPW producer waves
 constexpr int BG_NST = 4, BG_T = 64, BG_NPW = 2;
+template __global__ void k_block_grad_stream<64, BG_NST, BG_T, BG_NPW>(BGArgs);
 template __global__ void k_block_grad_stream<128, BG_NST, BG_T, BG_NPW>(BGArgs);
 template __global__ void k_block_grad_stream<256, BG_NST, BG_T, BG_NPW>(BGArgs);
 template __global__ void k_block_grad_stream<512, BG_NST, BG_T, BG_NPW>(BGArgs);
 
 template <int B>
 static int run_bg(const BGArgs &a, hipStream_t s) {
-  constexpr int NSL = (B / 128) * (B / 128);
-  const size_t lds = (size_t)BG_NST * 2 * BG_T * 128 * 2;
+  constexpr int S = B < 128 ? B : 128, NSL = (B / S) * (B / S);
+  const size_t lds = (size_t)BG_NST * 2 * BG_T * S * 2;
   const int64_t units = (int64_t)a.nb * a.P;
   dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
   static std::atomic<uint64_t> attr{0};
   POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_block_grad_stream<B, BG_NST, BG_T, BG_NPW>), lds, attr));
-  return launch("block_grad", s, [&] { k_block_grad_stream<B, BG_NST, BG_T, BG_NPW><<<grid, 64 * (4 + BG_NPW), lds, s>>>(a); });
+  return launch_k("block_grad", s, k_block_grad_stream<B, BG_NST, BG_T, BG_NPW>, grid, 64 * (4 + BG_NPW), lds, a);
 }
 
 bool block_grad_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens) {
-  if (b != 128 && b != 256 && b != 512) return false;
+  if (b != 64 && b != 128 && b != 256 && b != 512) return false;
   if (nb < 1 || nb * b > ld || ld % 8) return false;
   return (n_tokens + 64) * ld * 2 < 0x7fffffff;
 }
@@ -329,7 +333,7 @@ bool block_grad_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_to
 int64_t block_grad_stream_parts(int64_t b, int64_t nb, int64_t n_tokens) {
   // about one workgroup per CU in a single round: rounding the partition count up would
   // start a second, mostly idle round
-  const int64_t slices = nb * (b / 128) * (b / 128);
+  const int64_t sl = b < 128 ? b : 128, slices = nb * (b / sl) * (b / sl);
   const int cus = device_cus() > 0 ? device_cus() : 256;
   int64_t P = cus / slices;
   // more partitions past kMaxChain tokens each: a float32 accumulation over millions of
@@ -347,6 +351,7 @@ int block_grad_stream(const bf16_t *Xs, const bf16_t *dY, float *parts, int64_t 
   a.N = n_tokens; a.d = ld; a.nb = (int)nb;
   a.P = (int)block_grad_stream_parts(b, nb, n_tokens);
   a.Xs = Xs; a.dY = dY; a.parts = parts;
+  if (b == 64) return run_bg<64>(a, s);
   if (b == 128) return run_bg<128>(a, s);
   if (b == 256) return run_bg<256>(a, s);
   return run_bg<512>(a, s);

@@ -202,11 +202,11 @@ int cnp_mm(const CnpMMArgs &a, hipStream_t s) {
   if (a.b % TM || nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
   dim3 grid((unsigned)nwg);
   switch (a.b) {
-    case 64: return launch(a.name, s, [&] { k_cnp_mm<2><<<grid, NTH, 0, s>>>(a); });
-    case 128: return launch(a.name, s, [&] { k_cnp_mm<4><<<grid, NTH, 0, s>>>(a); });
-    case 256: return launch(a.name, s, [&] { k_cnp_mm<8><<<grid, NTH, 0, s>>>(a); });
-    case 512: return launch(a.name, s, [&] { k_cnp_mm<16><<<grid, NTH, 0, s>>>(a); });
-    default: return launch(a.name, s, [&] { k_cnp_mm<0><<<grid, NTH, 0, s>>>(a); });
+    case 64: return launch_k(a.name, s, k_cnp_mm<2>, grid, NTH, 0, a);
+    case 128: return launch_k(a.name, s, k_cnp_mm<4>, grid, NTH, 0, a);
+    case 256: return launch_k(a.name, s, k_cnp_mm<8>, grid, NTH, 0, a);
+    case 512: return launch_k(a.name, s, k_cnp_mm<16>, grid, NTH, 0, a);
+    default: return launch_k(a.name, s, k_cnp_mm<0>, grid, NTH, 0, a);
   }
 }
 
@@ -688,7 +688,7 @@ int chain_run(const CnpChainArgs &a, hipStream_t s) {
   static std::atomic<uint64_t> attr[3];  // dynamic LDS above 64 KB, per kernel and device
   auto go = [&](void (*kern)(CnpChainArgs), int mode) -> int {
     POETX_TRY(lds_limit((const void *)kern, lds, attr[mode]));
-    return launch(a.name, s, [&] { kern<<<dim3((unsigned)nwg), CNTH, lds, s>>>(a); });
+    return launch_k(a.name, s, kern, dim3((unsigned)nwg), CNTH, lds, a);
   };
   switch (a.mode) {
     case CNP_CHAIN_FWD: return go(k_cnp_chain<B, CNP_CHAIN_FWD, RP>, 0);
@@ -709,7 +709,7 @@ int fused_run(const CnpChainArgs &a, hipStream_t s) {
   const size_t lds = (size_t)4 * RP * C::A_LD * sizeof(bf16_t);
   static std::atomic<uint64_t> attr{0};  // dynamic LDS above 64 KB, per device
   POETX_TRY(lds_limit((const void *)k_cnp_bwd_fused<B, RP>, lds, attr));
-  return launch(a.name, s, [&] { k_cnp_bwd_fused<B, RP><<<dim3((unsigned)nwg), CNTH, lds, s>>>(a); });
+  return launch_k(a.name, s, k_cnp_bwd_fused<B, RP>, dim3((unsigned)nwg), CNTH, lds, a);
 }
 }  // namespace
 

@@ -384,6 +384,134 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
 }
 
 
+// Four-wave form of the W' product B = A . W'^T (both operands k-contiguous, bf16), one
+// wave per SIMD: 256 x 256 tiles, 2 x 2 waves of 128 x 128, v_mfma_f32_32x32x16_bf16
+// (a lone wave keeps that shape's pipe fuller than the 16 x 16 x 32 shape's) with the
+// 256 accumulators of a wave in AGPRs.  Per 64-deep k step a wave reads 32 fragments
+// (16 KB of A, 16 KB of B) for 64 MFMAs: two thirds of the LDS reads per flop of the
+// eight-wave 128 x 64 wave tiles.  The step's barrier sits after the reads of its last
+// 16-deep substep have returned and before that substep's MFMAs: those MFMAs then cover
+// both the barrier and the LDS latency of the next step's first fragments, and the
+// stage they came from is free for the loads two steps ahead.
+template <bool OUTF32>
+__global__ __launch_bounds__(256, 1) void k_gemm4(G2Args a) {
+  constexpr int BM = 256, BN = 256, BKT = 64, NST = 2, NSUB = BKT / 16;
+  constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT;
+  constexpr int FM = 4, FN = 4;  // 32 x 32 tiles per wave
+  extern __shared__ __align__(16) bf16_t smem[];
+
+  const TileSel sel = select_tile(a, 0);
+  int tm, tn;
+  tile_coords(a, sel.L, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t kbeg = sel.kbeg, kend = sel.kend;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.M * a.lda * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B, a.N * a.ldb * 2);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  using LA = LoaderKC<BM, 4, BKT>;
+  using LB = LoaderKC<BN, 4, BKT>;
+  constexpr int LPS = LA::INSTR + LB::INSTR;
+  LA la;
+  LB lb;
+  la.init(a.lda, m0);
+  lb.init(a.ldb, n0);
+  auto issue = [&](int buf, int64_t k0) {
+    la.issue(ra, k0, a.lda, smem + buf * A_ELEMS);
+    lb.issue(rb, k0, a.ldb, smem + NST * A_ELEMS + buf * B_ELEMS);
+  };
+  // fragment of a 32 x 16 operand slice: lane l holds row r0 + l % 32, k = ks + 8 (l / 32) .. +7
+  auto frag = [&](const bf16_t *t, int r0, int ks) {
+    const int row = r0 + (l & 31);
+    const int pchunk = ((ks >> 3) + (l >> 5)) ^ kc_key<BKT>(row);
+    return __builtin_bit_cast(bf16x8, *(const s16x8 *)(t + row * BKT + pchunk * 8));
+  };
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read = [&](int q, int buf, int s) {
+    const bf16_t *ta = smem + buf * A_ELEMS, *tb = smem + NST * A_ELEMS + buf * B_ELEMS;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[q][i] = frag(ta, wm + 32 * i, 16 * s);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[q][j] = frag(tb, wn + 32 * j, 16 * s);
+  };
+  auto mma = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        // operands swapped: lane l holds C[m = l % 32][n = 8 (e / 4) + 4 (l / 32) + e % 4]
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q][j], fa[q][i], acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = (int)((kend - kbeg + BKT - 1) / BKT);
+  if (nk > 0) issue(0, kbeg);
+  if (nk > 1) issue(1, kbeg + BKT);
+  if (nk > 1) wait_vmcnt<LPS>();
+  else __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // stage 0 in LDS for every wave
+  if (nk > 0) read(0, 0, 0);
+  for (int t = 0; t < nk; ++t) {
+    const int cur = t & 1;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const int q = s & 1;
+      if (s + 1 < NSUB) {
+        read(q ^ 1, cur, s + 1);
+        mma(q);
+      } else {
+        // the last substep's fragments are in registers: stage t is no longer read by
+        // this wave, and stage t+1 has landed for it
+        if (t + 1 < nk) {
+          if (t + 2 < nk) wait_vmcnt<0>();
+          else __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+        if (t + 2 < nk) issue(cur, kbeg + (int64_t)(t + 2) * BKT);
+        if (t + 1 < nk) read(q ^ 1, cur ^ 1, 0);
+        mma(q);
+      }
+    }
+  }
+
+  char *Cb = (char *)a.C;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + wm + 32 * i + (l & 31);
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0 + wn + 32 * j + 8 * g + 4 * (l >> 5);
+        f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        if (a.scaleN) {
+          float4 sc = *(const float4 *)(a.scaleN + n);
+          v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+        }
+        if constexpr (OUTF32) {
+          *(float4 *)(Cb + (m * a.ldc + n) * 4) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          uint2 p;
+          p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          p.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *(uint2 *)(Cb + (m * a.ldc + n) * 2) = p;
+        }
+      }
+  }
+}
+
+
 // Sum of the parts of each split tile, in part order 0, 1, ... (so the result does not
 // depend on which part finished first), times scaleN, to bf16 C.  The 256 x 256 tiles
 // of both W' kernels share one fragment layout: 8 waves as 2 (m) x 4 (n), 128 x 64 per
@@ -421,6 +549,13 @@ __global__ __launch_bounds__(256) void k_tail_reduce(G2Args a) {
   }
 }
 
+// The four-wave form passes the parity tests but measured slower than the eight-wave
+// kernel at workload 3 (248-254 against 215 us per W' product on one box); it stays off.
+#ifndef POETX_GEMM4
+#define POETX_GEMM4 0
+#endif
+constexpr bool kUseGemm4 = POETX_GEMM4 != 0;
+
 // explicit instantiations (every configuration the dispatcher below launches)
 #define POETX_G2_INST(R, BMv, BNv, WM, WN, BKv, NS, AK, BKm)                                     \
   template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, true>(G2Args);       \
@@ -432,6 +567,8 @@ POETX_G2_INST(MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true)
 POETX_G2_INST(MFMA_BLOCK_GRAD, 256, 256, 2, 4, 64, 2, true, true)
 #undef POETX_G2_INST
 template __global__ void k_gemm2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, true>(G2Args);
+template __global__ void k_gemm4<false>(G2Args);
+template __global__ void k_gemm4<true>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, true>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false, true>(G2Args);
@@ -490,7 +627,7 @@ void plan_tail(G2Args &a, const MfmaDesc &d, int bm, int bn) {
 int tail_reduce(const G2Args &a, const MfmaDesc &d, hipStream_t s) {
   const int r = a.tiles_m * a.tiles_n - a.full_tiles;
   if (r == 0) return POETX_OK;
-  return launch("gemm_tail_reduce", s, [&] { k_tail_reduce<<<r * 8, 256, 0, s>>>(a); });
+  return launch_k("gemm_tail_reduce", s, k_tail_reduce, r * 8, 256, 0, a);
 }
 
 }  // namespace
@@ -515,17 +652,17 @@ static int run_pp(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
     if (d.c_dt != POETX_BF16) return POETX_ERR_UNSUPPORTED;
     static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
     POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, false, true>), lds, attr));
-    POETX_TRY(launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, false, true><<<grid, 512, lds, s>>>(a); }));
+    POETX_TRY(launch_k(d.name, s, k_gemm_pp<ROLE, AKM, BKM, false, true>, grid, 512, lds, a));
     return tail_reduce(a, d, s);
   }
   if (d.c_dt == POETX_F32) {
     static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
     POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, true>), lds, attr));
-    return launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, true><<<grid, 512, lds, s>>>(a); });
+    return launch_k(d.name, s, k_gemm_pp<ROLE, AKM, BKM, true>, grid, 512, lds, a);
   }
   static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
   POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm_pp<ROLE, AKM, BKM, false>), lds, attr));
-  POETX_TRY(launch(d.name, s, [&] { k_gemm_pp<ROLE, AKM, BKM, false><<<grid, 512, lds, s>>>(a); }));
+  POETX_TRY(launch_k(d.name, s, k_gemm_pp<ROLE, AKM, BKM, false>, grid, 512, lds, a));
   return tail_reduce(a, d, s);
 }
 
@@ -536,7 +673,7 @@ static int run2o(const G2Args &a, const char *name, dim3 grid, size_t lds, hipSt
   auto kern = &k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8>;
   static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
   POETX_TRY(lds_limit(reinterpret_cast<const void *>(kern), lds, attr));
-  return launch(name, s, [&] { k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8><<<grid, NT, lds, s>>>(a); });
+  return launch_k(name, s, k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8>, grid, NT, lds, a);
 }
 
 template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool BI8 = false>
@@ -557,6 +694,28 @@ static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
   if (d.c_dt == POETX_F32) return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, true>(a, d.name, grid, lds, s);
   POETX_TRY((run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false>(a, d.name, grid, lds, s)));
   return tail_reduce(a, d, s);
+}
+
+// The four-wave W' product: whole tiles only (a plan that splits leftover tiles along k
+// takes the eight-wave kernel, whose partial layout the reduce kernel reads).
+static int run4(const G2Args &k, const MfmaDesc &d, hipStream_t s, bool *done) {
+  *done = false;
+  const size_t lds = (size_t)2 * (256 + 256) * 64 * 2;
+  G2Args a = k;
+  a.tiles_m = (int)cdiv(d.M, 256);
+  a.tiles_n = (int)(d.N / 256);
+  plan_tail(a, d, 256, 256);
+  if (a.full_tiles != a.tiles_m * a.tiles_n) return POETX_OK;
+  *done = true;
+  const dim3 grid((unsigned)a.full_tiles);
+  if (d.c_dt == POETX_F32) {
+    static std::atomic<uint64_t> attr{0};
+    POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm4<true>), lds, attr));
+    return launch_k(d.name, s, k_gemm4<true>, grid, 256, lds, a);
+  }
+  static std::atomic<uint64_t> attr{0};
+  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm4<false>), lds, attr));
+  return launch_k(d.name, s, k_gemm4<false>, grid, 256, lds, a);
 }
 
 bool mfma2_supported(const MfmaDesc &d) {
@@ -597,6 +756,11 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s) {
     case MFMA_GEMM_NT:
       if (d.a_km || d.b_km) return POETX_ERR_UNSUPPORTED;
       if (i8) return run2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, true>(k, d, s);
+      if (d.batch == 1 && d.splits == 1 && kUseGemm4) {
+        bool done = false;
+        POETX_TRY(run4(k, d, s, &done));
+        if (done) return POETX_OK;
+      }
       return run2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false>(k, d, s);
     case MFMA_GEMM_NN:
       if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;

@@ -70,8 +70,8 @@ template <typename TA, typename TB>
 static int gemm_generic_c(const GemmDesc &g, hipStream_t s) {
   dim3 grid((unsigned)cdiv(g.N, 64), (unsigned)cdiv(g.M, 64), (unsigned)g.batch);
   if (g.c_dt == POETX_F32)
-    return launch(g.name, s, [&] { k_gemm_generic<TA, TB, float><<<grid, 256, 0, s>>>(g); });
-  return launch(g.name, s, [&] { k_gemm_generic<TA, TB, bf16_t><<<grid, 256, 0, s>>>(g); });
+    return launch_k(g.name, s, k_gemm_generic<TA, TB, float>, grid, 256, 0, g);
+  return launch_k(g.name, s, k_gemm_generic<TA, TB, bf16_t>, grid, 256, 0, g);
 }
 
 template <typename TA>
@@ -236,9 +236,7 @@ static int permute_v(const void *in, void *out, int64_t rows, int64_t cols, cons
                      const int32_t *cperm, int sc, hipStream_t s) {
   const size_t row_bytes = (size_t)cols * sizeof(T);
   const unsigned grid = (unsigned)(cdiv(rows, 2) < 512 ? cdiv(rows, 2) : 512);
-  return launch("permute_cols", s, [&] {
-    k_permute_cols_v<T, 2><<<grid, 512, row_bytes * 2, s>>>((const T *)in, (T *)out, rows, cols, rperm, cperm, sc);
-  });
+  return launch_k("permute_cols", s, k_permute_cols_v<T, 2>, grid, 512, row_bytes * 2, (const T *)in, (T *)out, rows, cols, rperm, cperm, sc);
 }
 
 int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esize,
@@ -260,17 +258,11 @@ int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esiz
   unsigned grid = (unsigned)(rows < 4096 ? rows : 4096);
   switch (esize) {
     case 4:
-      return launch("permute_cols", s, [&] {
-        k_permute_cols<uint32_t><<<grid, 256, lds, s>>>((const uint32_t *)in, (uint32_t *)out, rows, cols, rperm, cperm, sc);
-      });
+      return launch_k("permute_cols", s, k_permute_cols<uint32_t>, grid, 256, lds, (const uint32_t *)in, (uint32_t *)out, rows, cols, rperm, cperm, sc);
     case 2:
-      return launch("permute_cols", s, [&] {
-        k_permute_cols<uint16_t><<<grid, 256, lds, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols, rperm, cperm, sc);
-      });
+      return launch_k("permute_cols", s, k_permute_cols<uint16_t>, grid, 256, lds, (const uint16_t *)in, (uint16_t *)out, rows, cols, rperm, cperm, sc);
     default:
-      return launch("permute_cols", s, [&] {
-        k_permute_cols<uint8_t><<<grid, 256, lds, s>>>((const uint8_t *)in, (uint8_t *)out, rows, cols, rperm, cperm, sc);
-      });
+      return launch_k("permute_cols", s, k_permute_cols<uint8_t>, grid, 256, lds, (const uint8_t *)in, (uint8_t *)out, rows, cols, rperm, cperm, sc);
   }
 }
 
@@ -282,7 +274,7 @@ __global__ void k_invert_perm(const int32_t *__restrict__ perm, int32_t *__restr
 
 int invert_perm(const int32_t *perm, int32_t *inv, int64_t n, hipStream_t s) {
   if (n <= 0) return POETX_OK;
-  return launch("invert_perm", s, [&] { k_invert_perm<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(perm, inv, n); });
+  return launch_k("invert_perm", s, k_invert_perm, (unsigned)cdiv(n, 256), 256, 0, perm, inv, n);
 }
 
 // Adam on packed parameters, one fused pass: m, v, theta updated in place from g.
@@ -317,7 +309,7 @@ int adam_step(int64_t n, float *theta, const float *g, float *m, float *v, float
   if (n <= 0) return POETX_OK;
   const int64_t want = cdiv(n / 4 > 0 ? n / 4 : 1, 256);
   const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
-  return launch("adam_step", s, [&] { k_adam<<<grid, 256, 0, s>>>(n, theta, g, m, v, step_size, b1, b2, rs2, eps); });
+  return launch_k("adam_step", s, k_adam, grid, 256, 0, n, theta, g, m, v, step_size, b1, b2, rs2, eps);
 }
 
 // out[c][r] = in[r][c] for a [rows][cols] matrix, through 64 x 64 LDS tiles.
@@ -392,15 +384,15 @@ int transpose(const void *in, void *out, int64_t rows, int64_t cols, int esize, 
       cdiv(rows, TR) <= 65535) {
     dim3 grid((unsigned)cdiv(cols, TR), (unsigned)cdiv(rows, TR));
     if (esize == 2)
-      return launch("transpose", s, [&] { k_transpose_v<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols); });
-    return launch("transpose", s, [&] { k_transpose_v<uint8_t><<<grid, 256, 0, s>>>((const uint8_t *)in, (uint8_t *)out, rows, cols); });
+      return launch_k("transpose", s, k_transpose_v<uint16_t>, grid, 256, 0, (const uint16_t *)in, (uint16_t *)out, rows, cols);
+    return launch_k("transpose", s, k_transpose_v<uint8_t>, grid, 256, 0, (const uint8_t *)in, (uint8_t *)out, rows, cols);
   }
   if (cdiv(rows, 64) > 65535) return POETX_ERR_UNSUPPORTED;
   dim3 grid((unsigned)cdiv(cols, 64), (unsigned)cdiv(rows, 64));
   switch (esize) {
-    case 4: return launch("transpose", s, [&] { k_transpose<uint32_t><<<grid, 256, 0, s>>>((const uint32_t *)in, (uint32_t *)out, rows, cols); });
-    case 2: return launch("transpose", s, [&] { k_transpose<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols); });
-    default: return launch("transpose", s, [&] { k_transpose<uint8_t><<<grid, 256, 0, s>>>((const uint8_t *)in, (uint8_t *)out, rows, cols); });
+    case 4: return launch_k("transpose", s, k_transpose<uint32_t>, grid, 256, 0, (const uint32_t *)in, (uint32_t *)out, rows, cols);
+    case 2: return launch_k("transpose", s, k_transpose<uint16_t>, grid, 256, 0, (const uint16_t *)in, (uint16_t *)out, rows, cols);
+    default: return launch_k("transpose", s, k_transpose<uint8_t>, grid, 256, 0, (const uint8_t *)in, (uint8_t *)out, rows, cols);
   }
 }
 
@@ -410,9 +402,7 @@ int transpose_batched(const void *in, void *out, int64_t batch, int64_t rows, in
   if (rows % V || cols % V || (((uintptr_t)in | (uintptr_t)out) & 15) || batch > 65535 || cdiv(rows, TR) > 65535)
     return POETX_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)cdiv(cols, TR), (unsigned)cdiv(rows, TR), (unsigned)batch);
-  return launch("transpose", s, [&] {
-    k_transpose_v<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)in, (uint16_t *)out, rows, cols);
-  });
+  return launch_k("transpose", s, k_transpose_v<uint16_t>, grid, 256, 0, (const uint16_t *)in, (uint16_t *)out, rows, cols);
 }
 
 __global__ void k_gather_f32(const float *__restrict__ src, float *__restrict__ out, int64_t n,
@@ -423,7 +413,7 @@ __global__ void k_gather_f32(const float *__restrict__ src, float *__restrict__ 
 
 int gather_f32(const float *src, float *out, int64_t n, const int32_t *perm, hipStream_t s) {
   if (n <= 0) return POETX_OK;
-  return launch("gather_f32", s, [&] { k_gather_f32<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(src, out, n, perm); });
+  return launch_k("gather_f32", s, k_gather_f32, (unsigned)cdiv(n, 256), 256, 0, src, out, n, perm);
 }
 
 // ============================================================= packed skew ====
@@ -548,9 +538,9 @@ int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   const dim3 grid((unsigned)nwg);
   if (sg.planes[0]) {
     if (b % 32) return POETX_ERR_UNSUPPORTED;
-    return launch("unpack_skew", s, [&] { k_unpack_frag<<<grid, 256, 0, s>>>(sg, b); });
+    return launch_k("unpack_skew", s, k_unpack_frag, grid, 256, 0, sg, b);
   }
-  return launch("unpack_skew", s, [&] { k_unpack_skew<<<grid, 256, 0, s>>>(sg, b); });
+  return launch_k("unpack_skew", s, k_unpack_skew, grid, 256, 0, sg, b);
 }
 
 int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t s) {
@@ -591,7 +581,7 @@ int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   if (nz <= 0) return POETX_OK;
   const int64_t T = cdiv(b, 32), nwg = nz * (T * (T + 1) / 2);
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
-  return launch("pack_skew_grad", s, [&] { k_pack_skew_grad<<<dim3((unsigned)nwg), 256, 0, s>>>(sg, b); });
+  return launch_k("pack_skew_grad", s, k_pack_skew_grad, dim3((unsigned)nwg), 256, 0, sg, b);
 }
 
 int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s) {
@@ -619,9 +609,7 @@ int lincomb(float *out, int64_t n, int64_t b, float cI, const float *X0, float c
             float c1, const float *X2, float c2, const float *X3, float c3, hipStream_t s) {
   int64_t tot = n * b * b;
   if (tot <= 0) return POETX_OK;
-  return launch("lincomb", s, [&] {
-    k_lincomb<<<(unsigned)cdiv(tot, 256), 256, 0, s>>>(out, n, b, cI, X0, c0, X1, c1, X2, c2, X3, c3);
-  });
+  return launch_k("lincomb", s, k_lincomb, (unsigned)cdiv(tot, 256), 256, 0, out, n, b, cI, X0, c0, X1, c1, X2, c2, X3, c3);
 }
 
 __global__ void k_reduce_parts(const float *__restrict__ in, float *__restrict__ out, int64_t elems,
@@ -656,14 +644,9 @@ int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int6
   if (elems <= 0) return POETX_OK;
   if (elems % 4 == 0 && stride % 4 == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0) {
     const int64_t n4 = elems / 4;
-    return launch("reduce_parts", s, [&] {
-      k_reduce_parts4<<<(unsigned)cdiv(n4, 256), 256, 0, s>>>((const float4 *)in, (float4 *)out, n4, parts,
-                                                              stride / 4);
-    });
+    return launch_k("reduce_parts", s, k_reduce_parts4, (unsigned)cdiv(n4, 256), 256, 0, (const float4 *)in, (float4 *)out, n4, parts, stride / 4);
   }
-  return launch("reduce_parts", s, [&] {
-    k_reduce_parts<<<(unsigned)cdiv(elems, 256), 256, 0, s>>>(in, out, elems, parts, stride);
-  });
+  return launch_k("reduce_parts", s, k_reduce_parts, (unsigned)cdiv(elems, 256), 256, 0, in, out, elems, parts, stride);
 }
 
 // n elements set to 1 (float32 or bf16): the G of n blocks of size 1.
@@ -676,9 +659,7 @@ __global__ void k_fill_one(void *out, int64_t n, int bf) {
 
 int fill_one(void *out, int64_t n, int dt, hipStream_t s) {
   if (n <= 0) return POETX_OK;
-  return launch("fill_one", s, [&] {
-    k_fill_one<<<(unsigned)cdiv(n, 256), 256, 0, s>>>(out, n, dt == POETX_BF16 ? 1 : 0);
-  });
+  return launch_k("fill_one", s, k_fill_one, (unsigned)cdiv(n, 256), 256, 0, out, n, dt == POETX_BF16 ? 1 : 0);
 }
 
 }  // namespace poetx

@@ -260,8 +260,8 @@ bool mfma_supported(const MfmaDesc &d) {
 template <int ROLE, bool AKM, bool BKM, bool BI8>
 static int run_c(const KArgs &k, const MfmaDesc &d, dim3 grid, hipStream_t s) {
   if (d.c_dt == POETX_F32)
-    return launch(d.name, s, [&] { k_mfma_gemm<ROLE, AKM, BKM, BI8, true><<<grid, NT, 0, s>>>(k); });
-  return launch(d.name, s, [&] { k_mfma_gemm<ROLE, AKM, BKM, BI8, false><<<grid, NT, 0, s>>>(k); });
+    return launch_k(d.name, s, k_mfma_gemm<ROLE, AKM, BKM, BI8, true>, grid, NT, 0, k);
+  return launch_k(d.name, s, k_mfma_gemm<ROLE, AKM, BKM, BI8, false>, grid, NT, 0, k);
 }
 
 int gemm_mfma(const MfmaDesc &d, hipStream_t s) {

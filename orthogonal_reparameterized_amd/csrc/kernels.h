@@ -113,14 +113,14 @@ bool mfma2_supported(const MfmaDesc &d);
 size_t gemm_tail_ws_bytes(int64_t M, int64_t N, int64_t K);  // 0: no tile would be split
 int device_cus();  // compute units of the current device, 0 if unknown
 int gemm_mfma2(const MfmaDesc &d, hipStream_t s);   // direct-to-LDS kernel (bf16 operands)
-// Streaming block-diagonal product over the first nb blocks (b in {128, 256}; G in registers):
+// Streaming block-diagonal product over the first nb blocks (b in {64, 128, 256}; G in registers):
 //   Y[:, jb:(j+1)b] = X[:, jb:(j+1)b] . G[j]  (transposed: . G[j]^T), times scaleN[col],
 // j < nb.  X, Y token-major with row stride ld (>= nb*b, a multiple of 8) bf16,
 // G [nb][b][b] bf16.
 bool block_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens);
 int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, int64_t ld, int64_t nb,
                  int64_t b, bool transposed, const float *scaleN, const char *name, hipStream_t s);
-// Streaming block gradient (b in {128, 256, 512}, shape limits as block_stream): P partials
+// Streaming block gradient (b in {64, 128, 256, 512}, shape limits as block_stream): P partials
 //   parts[p][j] = sum_{t in token tiles p, p+P, ...} Xs_j[t]^T dY_j[t],  parts [P][nb][b][b] fp32,
 // with P = block_grad_stream_parts(b, nb, n_tokens); n_tokens >= 1.
 bool block_grad_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens);

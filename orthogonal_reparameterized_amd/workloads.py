@@ -15,6 +15,7 @@ quantized training at 13B-like shapes; the shapes below stand in for those):
   4  Llama-8B-like MLP up-projection: N=8192, 4096 -> 14336, b=512 (bf16)
   5  POET-XQ 13B-like MLP: N=4096, 5120 -> 13824, b=256, int8 weight with
      per-output-row fp32 scales (mem variant only)
+  6  workload 3 at block size b=64
 """
 
 from __future__ import annotations
@@ -83,6 +84,9 @@ WORKLOADS = {
                 "bf16", 0.01, 4096),
     5: Workload(5, "xq-mlp 5120->13824 b=256 N=4096 int8", 4096, 5120, 13824, 256, "bf16", "i8",
                 "bf16", 0.01, 5120, variants=("mem",)),
+    # workload 3's shapes at the smaller block size b = 64 (64 + 64 blocks)
+    6: Workload(6, "attn-proj 4096->4096 b=64 N=8192", 8192, 4096, 4096, 64, "bf16", "bf16",
+                "bf16", 0.01, 4096),
 }
 
 

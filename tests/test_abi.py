@@ -180,3 +180,73 @@ def test_adam_validation(B):
     assert f(8, FAKE, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 0.0, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
     assert f(8, FAKE, None, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
     assert f(8, FAKE + 4, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
+
+
+def _c_params(name):
+    """Parameter type strings of `name` as declared in poetx.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    body = m.group(1).strip()
+    if body in ("", "void"):
+        return []
+    return [" ".join(p.split()) for p in body.split(",")]
+
+
+def _ctype_of(decl):
+    """ctypes class a binding must use for one C parameter declaration."""
+    d = decl.replace("const ", "")
+    if "size_t *" in d or "size_t*" in d:
+        return "size_t_ptr"
+    if "poetx_layer *" in d:
+        return "layer_ptr"
+    if "char *" in d:
+        return (ctypes.c_char_p, ctypes.c_void_p)
+    if "*" in d:
+        return ctypes.c_void_p
+    base = d.split()[0]
+    return {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int32, "int": ctypes.c_int,
+            "float": ctypes.c_float, "size_t": ctypes.c_size_t}[base]
+
+
+def test_header_signatures_match_binding(B):
+    """Every entry point's parameter list in poetx.h (count and types) is what the binding
+    declares, and the poetx_layer struct has the binding's field order and types."""
+    for name in declared_functions():
+        want = [_ctype_of(p) for p in _c_params(name)]
+        got = list(getattr(B.raw, name).argtypes or [])
+        assert len(got) == len(want), (name, len(got), len(want))
+        for w, g in zip(want, got):
+            if w == "size_t_ptr":
+                assert g is ctypes.POINTER(ctypes.c_size_t), name
+            elif w == "layer_ptr":
+                assert g is ctypes.POINTER(B.PoetxLayerC), name
+            elif w is ctypes.c_int:
+                assert g in (ctypes.c_int, ctypes.c_int32), name
+            elif isinstance(w, tuple):
+                assert g in w, (name, w, g)
+            else:
+                assert g is w, (name, w, g)
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} poetx_layer;", text, flags=re.S).group(1)
+    fields = []
+    for decl in body.split(";"):
+        decl = " ".join(decl.split())
+        if not decl:
+            continue
+        typ = "ptr" if "*" in decl else decl.split()[0]
+        for nm in decl.replace("*", " ").split()[1 if typ != "ptr" else 0:]:
+            nm = nm.strip(",")
+            if nm and nm not in ("const", "void", "float", "int32_t", "int64_t"):
+                fields.append((nm, typ))
+    cmap = {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int32, "ptr": ctypes.c_void_p}
+    assert [(n, cmap[t]) for n, t in fields] == list(B.PoetxLayerC._fields_)
+
+
+def test_int8_with_transposed_weight_refused(B):
+    """A kept W'^T is a BF16-only option: an I8 layer that sets it is refused on the host."""
+    c = layer(B, w=B.POETX_I8, w_scale=FAKE, variant=B.POETX_MEM)
+    assert fwd(B, c, saved=None)[0] == B.POETX_OK
+    c.w_merged_t = FAKE_OUT
+    assert fwd(B, c, saved=None)[0] == B.POETX_ERR_INVALID_ARG
+    assert bwd(B, c, saved=None)[0] == B.POETX_ERR_INVALID_ARG

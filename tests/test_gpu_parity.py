@@ -336,6 +336,10 @@ SMALL_BF16 = [
     (130, 1024, 512, 512, True),
     (64, 256, 256, 128, False),
     (1, 384, 256, 128, True),
+    # b = 64: streaming block kernels at 64 columns, W' products on MFMA (or, at 576, not)
+    (257, 512, 768, 64, True),
+    (130, 576, 320, 64, True),
+    (33, 256, 256, 64, False),
 ]
 
 
@@ -372,7 +376,8 @@ RAGGED = [
     # (n_tokens, d_in, d_out, b, dtype): ceil(d/b) blocks, the last one smaller
     (257, 640, 896, 256, "bf16"),   # last blocks 128 | 128 on the MFMA kernels
     (100, 384, 640, 512, "bf16"),   # input side narrower than b (one block of 384)
-    (70, 576, 320, 256, "bf16"),    # 128 does not divide d_in: vector-ALU path, last blocks 64
+    (70, 576, 320, 256, "bf16"),    # 128 does not divide d_in: vector-ALU W' products; the
+                                    # 256-blocks and the last blocks of 64 on the MFMA block kernels
     (64, 200, 150, 32, "f32"),      # last blocks 8 | 22
     (33, 97, 70, 32, "f32"),        # a last block of size 1 (no parameters) | 6
 ]
@@ -543,7 +548,8 @@ def _full(key):
 
 
 @pytest.mark.parametrize("key,variant,wt", [(3, "fast", False), (3, "fast", True), (3, "mem", False),
-                                             (4, "fast", True), (4, "mem", False), (5, "mem", False)])
+                                             (4, "fast", True), (4, "mem", False), (5, "mem", False),
+                                             (6, "fast", True), (6, "mem", False)])
 def test_layer_full_size(B, key, variant, wt):
     wl, inp, ref = _full(key)
     _say(f"workload {key} {variant} (W'^T kept: {wt}) on GPU")
