@@ -9,7 +9,8 @@ The permutation merge runs once per inner phase, before the timed region, and
 is timed separately.  Inputs are seeded synthetic data resident in HBM before
 timing starts.  Prints ONE JSON line.
 
-Timing: W untimed warm-up steps, then exactly K steps between two device
+Timing: about 0.3 s of untimed steps bring the GPU from idle to its steady clocks (see
+settle()), then W untimed warm-up steps, then exactly K steps between two device
 synchronizations.  Inside that timed region the dominant kernel's launches (the W'
 product) carry a start and a stop event bound to their own dispatch (the library's
 per-thread recorder, hipExtLaunchKernel, events without a system-scope fence), and
@@ -152,6 +153,20 @@ def _sync():
     torch.cuda.synchronize()
 
 
+SETTLE_S = 0.3
+
+
+def settle(st, seconds=SETTLE_S):
+    """Untimed steps for `seconds` of wall time, ahead of the warm-up steps: an idle GPU
+    comes back at low clocks and takes tens of ms of load to reach its steady ones (a
+    kernel trace of the first steps after idle shows every kernel 5-8% slower)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            st.step()
+        _sync()
+
+
 def time_steps(st, steps, warmup, record, only=None):
     """K steps between two synchronizations, an event at each step boundary; with
     `record`, the launches labelled `only` (every launch when None) carry dispatch-bound
@@ -222,6 +237,7 @@ def run_variant(wl, inputs, variant, steps, warmup, *, keep_wt, keep_x=True, per
     # the timed steps: only the dominant kernel's launches carry events (a recorded dispatch
     # waits a few us on its events' bookkeeping), then the same steps unrecorded, then once
     # more with every launch recorded for the per-kernel table
+    settle(st)
     wall, per, rec_dom = time_steps(st, steps, warmup, record=True, only=DOMINANT)
     wall_off, per_off, _ = time_steps(st, steps, 1, record=False)
     wall_all, _, rec = time_steps(st, steps, 1, record=True)
@@ -498,14 +514,17 @@ def summarize_trace(db, bench_json=None):
     sym = next(sm for sm in KERNEL_SYMBOL_CANDIDATES[roof["kernel"]] if any(sm in nm for nm in names))
     durs = [r[1] for r in con.execute("select name, duration from kernels order by start")
             if sym in r[0].replace(" ", "")]
-    # the traced run (--only-head, one variant): W warm-up steps, K timed steps (this kernel
-    # recorded), 1 + K unrecorded, 1 + K all recorded, then 5 cold-cache steps
+    # the traced run (--only-head, one variant): settle steps, W warm-up steps, K timed steps
+    # (this kernel recorded), 1 + K unrecorded, 1 + K all recorded, then 5 cold-cache steps;
+    # the windows are counted back from the end
     k, w = d["steps"], d["warmup"]
-    per = len(durs) / (w + 3 * k + 2 + 5)
-    c = int(round(per))
-    timed = durs[w * c:(w + k) * c]
-    unrec = durs[(w + k + 1) * c:(w + 2 * k + 1) * c]
-    allrec = durs[(w + 2 * k + 2) * c:(w + 3 * k + 2) * c]
+    c = int(round(d["phases"][d["config"]["variant"]]["gemm_nt"]["launches_per_step"]))
+    if d["variants"][d["config"]["variant"]].get("w_merged_t"):
+        c *= 2  # the backward product runs the same kernel on W'^T
+    end = len(durs) - 5 * c
+    allrec = durs[end - k * c:end]
+    unrec = durs[end - (2 * k + 1) * c:end - (k + 1) * c]
+    timed = durs[end - (3 * k + 2) * c:end - (2 * k + 2) * c]
 
     def avg(v):
         return sum(v) / len(v) / 1e3 if v else float("nan")
@@ -590,6 +609,10 @@ def cnp_bench(wl, steps, warmup):
     res, per = {}, {}
     for name, fn in (("fwd", lambda: B.poetx_cnp(B.POETX_CNP_FWD, th, wl.b, g=g)),
                      ("bwd", lambda: B.poetx_cnp(B.POETX_CNP_BWD, th, wl.b, dg=dgt, dtheta=dth))):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < SETTLE_S:
+            fn()
+            _sync()
         for _ in range(warmup):
             fn()
         _sync()

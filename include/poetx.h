@@ -92,12 +92,15 @@ typedef struct {
   const float *w_scale;        /* [d_out] per-row scale of an I8 W', else NULL      */
   const int32_t *perm_in;      /* [d_in]  or NULL (identity)                        */
   const int32_t *perm_out;     /* [d_out] or NULL (identity)                        */
-  const float *theta_r;        /* [n_R][b(b-1)/2] packed Q of G_R (n_R = d_in/b; with
+  const void *theta_r;         /* [n_R][b(b-1)/2] packed Q of G_R (n_R = d_in/b; with
                                   a last block of size d_in % b, its packed vector
-                                  follows)                                           */
-  const float *theta_p;        /* [n_P][b(b-1)/2] packed Q of G_P, likewise         */
+                                  follows), in theta_dtype                           */
+  const void *theta_p;         /* [n_P][b(b-1)/2] packed Q of G_P, likewise         */
   const void *g_r;             /* [n_R][b][b] (then the last block) from poetx_cnp  */
   const void *g_p;             /* [n_P][b][b] (then the last block) from poetx_cnp  */
+  int32_t theta_dtype;         /* F32 (0, the default) or BF16: storage of theta; the
+                                  CNP widens it exactly and computes in float32, and
+                                  dtheta stays float32                               */
 } poetx_layer;
 
 /*
@@ -120,8 +123,9 @@ int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64
 /*
  * poetx_cnp -- Method §4 (Cayley-Neumann parameterization, eq. 9) on nblocks
  * independent b x b blocks.
+ *   theta: packed [n][b(b-1)/2] in theta_dtype (F32, or BF16 storage widened exactly).
  *   dir == POETX_CNP_FWD: g[n][b][b] = I + 2(Q + Q^2 + Q^2.Q) + Q^2.Q^2 from packed
- *     theta[n][b(b-1)/2]; g in g_dtype (F32 or BF16, rounded to nearest even).
+ *     theta; g in g_dtype (F32 or BF16, rounded to nearest even).
  *     dg, dtheta unused (may be NULL).
  *   dir == POETX_CNP_BWD: dtheta[n][b(b-1)/2] = dL/dtheta given dg = dL/dG
  *     ([n][b][b], dg_dtype F32), the exact adjoint of eq. 9 (the page leaves
@@ -133,11 +137,13 @@ int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64
  * size (a last block sits at an offset of whole blocks); g and dg that are not
  * 16-byte aligned take the float32 vector-ALU path.  b == 1: G = [1] per block,
  * no parameters (theta and dtheta may be NULL).
- * Errors: b < 1 or b > 1024 -> POETX_ERR_SHAPE; NULL theta (b > 1) / output ->
- * INVALID_ARG.
+ * The pages load Q and Q^2 in their fused kernel; this library recomputes every power of Q
+ * from theta inside its kernels (no saved Q^2 argument; the results are the same).
+ * Errors: b < 1 or b > 1024 -> POETX_ERR_SHAPE; NULL theta (b > 1) / output, theta_dtype
+ * other than F32 or BF16 -> INVALID_ARG.
  */
-int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *theta, void *g,
-              int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta, void *ws,
+int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const void *theta, int32_t theta_dtype,
+              void *g, int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta, void *ws,
               size_t *ws_bytes, void *stream);
 
 /*
@@ -178,6 +184,35 @@ int poetx_backward(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void
                    size_t *ws_bytes, void *stream);
 
 /*
+ * poetx_backward_adam -- poetx_backward with one Adam step of both sides' packed theta
+ * fused into the CNP backward's last pass (the pass that forms dtheta from dL/dQ), so the
+ * gradient goes straight into the update instead of through a separate optimizer pass
+ * over dtheta.  The optimizer state lives on the b(b-1)/2 packed parameters per block
+ * (Method §4); gamma scales the learning rate (practical advice 3: 0.5 for POET-XQ).  The
+ * update is poetx_adam_step's, element by element (float32 arithmetic; a BF16 theta is
+ * rounded to nearest even after it).
+ * opt [host]: hyperparameters and the device buffers, in theta's layout: m_r, v_r, m_p,
+ * v_p float32 state, updated in place (zero before step 1); theta_r_out, theta_p_out
+ * receive the updated theta in L->theta_dtype and may be L->theta_r / L->theta_p
+ * themselves (an in-place update: every element is read and written by one thread).
+ * dtheta_r, dtheta_p: also written when not NULL.  Other arguments and the workspace as
+ * poetx_backward (the block gradients dg_* are not offered).
+ * Errors: as poetx_backward; NULL opt or state/theta buffers, step < 1, beta outside
+ * [0, 1), eps <= 0 -> POETX_ERR_INVALID_ARG.
+ */
+typedef struct {
+  float lr, beta1, beta2, eps, gamma;
+  int64_t step;                  /* t >= 1 (bias corrections 1 - beta^t)             */
+  float *m_r, *v_r, *m_p, *v_p;  /* Adam state of theta_r, theta_p                    */
+  void *theta_r_out, *theta_p_out;
+} poetx_adam;
+
+int poetx_backward_adam(const poetx_layer *L /*[host]*/, int64_t n_tokens, const void *x,
+                        const void *dz, const void *saved_b, const void *saved_x, void *dx,
+                        float *dtheta_r, float *dtheta_p, const poetx_adam *opt /*[host]*/,
+                        void *ws, size_t *ws_bytes, void *stream);
+
+/*
  * poetx_fold -- the consolidation step of merge-then-reinitialize (the POET training
  * recipe's periodic merge, on the "Poet Orthogonal LLM Training" skill page under its
  * memory optimization; with POET-X's merged permutations, Method §2): the layer's
@@ -201,14 +236,16 @@ int poetx_fold(const poetx_layer *L /*[host]*/, void *w_out, void *ws, size_t *w
  * for POET-XQ: practical advice 3).  With g = dtheta from poetx_backward:
  *     m = beta1 m + (1 - beta1) g,   v = beta2 v + (1 - beta2) g^2,
  *     theta -= gamma lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
- * theta, m, v: [n_params] float32, updated in place (m, v start at zero); grad:
- * [n_params] float32, read-only; all 16-byte aligned.  t = step >= 1.  The pages do not
- * fix the other hyperparameters: the caller passes them.
- * Errors: step < 1, beta outside [0, 1), eps <= 0, NULL or misaligned pointers ->
- * POETX_ERR_INVALID_ARG.
+ * theta: [n_params] in theta_dtype (F32, or BF16: widened, updated in float32, rounded to
+ * nearest even), updated in place; m, v: [n_params] float32, updated in place (m, v start
+ * at zero); grad: [n_params] float32, read-only; all 16-byte aligned.  t = step >= 1.  The
+ * pages do not fix the other hyperparameters: the caller passes them.
+ * Errors: step < 1, beta outside [0, 1), eps <= 0, theta_dtype other than F32 or BF16,
+ * NULL or misaligned pointers -> POETX_ERR_INVALID_ARG.
  */
-int poetx_adam_step(int64_t n_params, float *theta, const float *grad, float *m, float *v, float lr,
-                    float beta1, float beta2, float eps, int64_t step, float gamma, void *stream);
+int poetx_adam_step(int64_t n_params, void *theta, int32_t theta_dtype, const float *grad, float *m,
+                    float *v, float lr, float beta1, float beta2, float eps, int64_t step, float gamma,
+                    void *stream);
 
 /* Human-readable name of a poetx_status code (static string). */
 const char *poetx_status_string(int status);

@@ -40,19 +40,29 @@ class PoetxLayerC(ctypes.Structure):
         ("d_in", _i64), ("d_out", _i64), ("b", _i64),
         ("act_dtype", _i32), ("w_dtype", _i32), ("g_dtype", _i32), ("variant", _i32),
         ("w_merged", _vp), ("w_merged_t", _vp), ("w_scale", _vp), ("perm_in", _vp), ("perm_out", _vp),
-        ("theta_r", _vp), ("theta_p", _vp), ("g_r", _vp), ("g_p", _vp),
+        ("theta_r", _vp), ("theta_p", _vp), ("g_r", _vp), ("g_p", _vp), ("theta_dtype", _i32),
+    ]
+
+
+class PoetxAdamC(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+        ("gamma", ctypes.c_float), ("step", _i64),
+        ("m_r", _vp), ("v_r", _vp), ("m_p", _vp), ("v_p", _vp), ("theta_r_out", _vp), ("theta_p_out", _vp),
     ]
 
 
 _lib.poetx_merge_perm.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
-_lib.poetx_cnp.argtypes = [_i32, _i64, _i64, _vp, _vp, _i32, _vp, _i32, _vp, _vp,
+_lib.poetx_cnp.argtypes = [_i32, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp,
                            ctypes.POINTER(_sz), _vp]
 _lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp,
                                ctypes.POINTER(_sz), _vp]
 _lib.poetx_backward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, ctypes.POINTER(_sz), _vp]
+_lib.poetx_backward_adam.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.POINTER(PoetxAdamC), _vp, ctypes.POINTER(_sz), _vp]
 _lib.poetx_fold.argtypes = [ctypes.POINTER(PoetxLayerC), _vp, _vp, ctypes.POINTER(_sz), _vp]
-_lib.poetx_adam_step.argtypes = [_i64, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+_lib.poetx_adam_step.argtypes = [_i64, _vp, _i32, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                  ctypes.c_float, _i64, ctypes.c_float, _vp]
 _lib.poetx_status_string.argtypes = [ctypes.c_int]
 _lib.poetx_status_string.restype = ctypes.c_char_p
@@ -60,11 +70,13 @@ _lib.poetx_version.restype = ctypes.c_char_p
 _lib.poetx_prof_enable.argtypes = [_i32]
 _lib.poetx_prof_read.argtypes = [ctypes.c_char_p, _sz]
 _lib.poetx_prof_only.argtypes = [ctypes.c_char_p]
-for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold", "poetx_adam_step",
+for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_backward_adam", "poetx_fold",
+           "poetx_adam_step",
            "poetx_prof_enable", "poetx_prof_only", "poetx_prof_read"):
     getattr(_lib, _f).restype = ctypes.c_int
 
-EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_fold", "poetx_adam_step",
+EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_backward_adam", "poetx_fold",
+            "poetx_adam_step",
             "poetx_status_string", "poetx_version", "poetx_prof_enable", "poetx_prof_only", "poetx_prof_read")
 
 
@@ -163,10 +175,11 @@ def poetx_cnp(direction: int, theta: torch.Tensor, b: int, *, g: Optional[torch.
         g = torch.empty((n, b, b), dtype=g_dtype, device=dev) if g is None else g
         gdt, dgdt = _dt(g), POETX_F32
     else:
-        dtheta = torch.empty_like(theta) if dtheta is None else dtheta
+        dtheta = torch.empty(theta.shape, dtype=torch.float32, device=dev) if dtheta is None else dtheta
         gdt, dgdt = POETX_F32, _dt(dg)
+    tdt = _dt(theta)
     nbytes = _sz(0)
-    _check(_lib.poetx_cnp(direction, n, b, None, None, gdt, None, dgdt, None, None,
+    _check(_lib.poetx_cnp(direction, n, b, None, tdt, None, gdt, None, dgdt, None, None,
                           ctypes.byref(nbytes), None), "poetx_cnp(size)")
     ws = _workspace(dev, nbytes.value)
     nb = _sz(ws.numel())
@@ -174,7 +187,7 @@ def poetx_cnp(direction: int, theta: torch.Tensor, b: int, *, g: Optional[torch.
     # sits at an offset of whole blocks, which need not be a multiple of 16 bytes)
     def ep(t):
         return None if t is None else _ptr(t, t.element_size())
-    st = _lib.poetx_cnp(direction, n, b, ep(theta), ep(g), gdt, ep(dg), dgdt, ep(dtheta),
+    st = _lib.poetx_cnp(direction, n, b, ep(theta), tdt, ep(g), gdt, ep(dg), dgdt, ep(dtheta),
                         _ptr(ws), ctypes.byref(nb), _stream(dev))
     _check(st, "poetx_cnp")
     return g if direction == POETX_CNP_FWD else dtheta
@@ -211,6 +224,7 @@ class Layer:
         c.w_dtype = _dt(self.w_merged)
         c.g_dtype = _dt(self.g_r)
         c.variant = self.variant
+        c.theta_dtype = _dt(self.theta_r)
         for name in ("w_merged", "w_merged_t", "w_scale", "perm_in", "perm_out", "theta_r", "theta_p",
                      "g_r", "g_p"):
             p = _ptr(getattr(self, name))
@@ -250,8 +264,8 @@ def poetx_backward(layer: Layer, x: torch.Tensor, dz: torch.Tensor,
     n = x.shape[0]
     dev = x.device
     dx = torch.empty((n, layer.d_in), dtype=layer.act_dtype, device=dev) if dx is None else dx
-    dtheta_r = torch.empty_like(layer.theta_r) if dtheta_r is None else dtheta_r
-    dtheta_p = torch.empty_like(layer.theta_p) if dtheta_p is None else dtheta_p
+    dtheta_r = torch.empty(layer.theta_r.shape, dtype=torch.float32, device=dev) if dtheta_r is None else dtheta_r
+    dtheta_p = torch.empty(layer.theta_p.shape, dtype=torch.float32, device=dev) if dtheta_p is None else dtheta_p
     dg_r = dg_p = None
     if want_dg:
         b = layer.b
@@ -294,12 +308,61 @@ def poetx_fold(layer: Layer, w_out: Optional[torch.Tensor] = None) -> torch.Tens
 
 def poetx_adam_step(theta: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, *, lr: float,
                     step: int, betas=(0.9, 0.999), eps: float = 1e-8, gamma: float = 1.0):
-    """In-place Adam update of packed theta (and its state m, v) from grad = dtheta."""
-    for t in (theta, grad, m, v):
+    """In-place Adam update of packed theta (float32 or bf16) and its float32 state m, v
+    from grad = dtheta."""
+    for t in (grad, m, v):
         assert t.dtype == torch.float32 and t.is_contiguous() and t.numel() == theta.numel()
-    _check(_lib.poetx_adam_step(theta.numel(), _ptr(theta), _ptr(grad), _ptr(m), _ptr(v), lr, betas[0],
-                                betas[1], eps, step, gamma, _stream(theta.device)), "poetx_adam_step")
+    assert theta.is_contiguous()
+    _check(_lib.poetx_adam_step(theta.numel(), _ptr(theta), _dt(theta), _ptr(grad), _ptr(m), _ptr(v), lr,
+                                betas[0], betas[1], eps, step, gamma, _stream(theta.device)), "poetx_adam_step")
     return theta
+
+
+@dataclass
+class AdamState:
+    """Adam state of a layer's two packed thetas (float32, theta's layout) and its step."""
+    m_r: torch.Tensor
+    v_r: torch.Tensor
+    m_p: torch.Tensor
+    v_p: torch.Tensor
+    step: int = 0
+
+    @staticmethod
+    def zeros_like(layer: "Layer") -> "AdamState":
+        z = [torch.zeros(t.shape, dtype=torch.float32, device=t.device)
+             for t in (layer.theta_r, layer.theta_r, layer.theta_p, layer.theta_p)]
+        return AdamState(*z)
+
+
+def poetx_backward_adam(layer: Layer, x: torch.Tensor, dz: torch.Tensor, state: AdamState,
+                        saved_b: Optional[torch.Tensor] = None, *, lr: float, betas=(0.9, 0.999),
+                        eps: float = 1e-8, gamma: float = 1.0, saved_x=None, dx=None, dtheta_r=None,
+                        dtheta_p=None):
+    """The backward with one Adam step of layer.theta_r / layer.theta_p (in place) fused into
+    the CNP backward's last pass; state.step advances by one.  Returns dict(dx[, dtheta_*])."""
+    L = layer.to_c()
+    n = x.shape[0]
+    dev = x.device
+    dx = torch.empty((n, layer.d_in), dtype=layer.act_dtype, device=dev) if dx is None else dx
+    state.step += 1
+    opt = PoetxAdamC()
+    opt.lr, opt.beta1, opt.beta2, opt.eps, opt.gamma, opt.step = lr, betas[0], betas[1], eps, gamma, state.step
+    for name in ("m_r", "v_r", "m_p", "v_p"):
+        setattr(opt, name, _ptr(getattr(state, name)).value)
+    opt.theta_r_out, opt.theta_p_out = _ptr(layer.theta_r).value, _ptr(layer.theta_p).value
+    nbytes = _sz(0)
+    _check(_lib.poetx_backward_adam(ctypes.byref(L), n, None, None, None, _ptr(saved_x), None, None, None,
+                                    ctypes.byref(opt), None, ctypes.byref(nbytes), None), "poetx_backward_adam(size)")
+    ws = _workspace(dev, nbytes.value)
+    nb = _sz(ws.numel())
+    st = _lib.poetx_backward_adam(ctypes.byref(L), n, _ptr(x), _ptr(dz), _ptr(saved_b), _ptr(saved_x), _ptr(dx),
+                                  _ptr(dtheta_r), _ptr(dtheta_p), ctypes.byref(opt), _ptr(ws), ctypes.byref(nb),
+                                  _stream(dev))
+    _check(st, "poetx_backward_adam")
+    out = dict(dx=dx)
+    if dtheta_r is not None:
+        out.update(dtheta_r=dtheta_r, dtheta_p=dtheta_p)
+    return out
 
 
 def prof_enable(on: bool = True):

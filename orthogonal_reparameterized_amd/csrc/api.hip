@@ -177,7 +177,7 @@ size_t cnp_ws_bytes(int dir, int64_t n, int64_t b) {
 
 bool al16(const void *q) { return ((uintptr_t)q & 15) == 0; }
 
-int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype, void *ws,
+int cnp_fwd_impl(int64_t n, int64_t b, const void *theta, int theta_bf16, void *g, int g_dtype, void *ws,
                  hipStream_t s) {
   Arena ar(ws);
   size_t blk = (size_t)n * b * b * 4;
@@ -187,7 +187,7 @@ int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype,
   if (vec && cnp_chain_supported(b)) {
     // Q as bf16 planes, then the whole Horner chain in one launch
     SkewSegs un;
-    un.src[0] = theta; un.n[0] = n;
+    un.src[0] = theta; un.n[0] = n; un.src_bf16 = theta_bf16;
     un.planes[0] = (bf16_t *)ar.take(blk);
     POETX_TRY(unpack_skew2(un, b, s));
     CnpChainArgs c;
@@ -201,7 +201,11 @@ int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype,
   }
   float *Q = (float *)ar.take(blk), *S = (float *)ar.take(blk);
   float *T = (float *)ar.take(blk), *U = (float *)ar.take(blk);
-  POETX_TRY(unpack_skew(theta, Q, n, b, s));
+  {
+    SkewSegs un;
+    un.src[0] = theta; un.dst[0] = Q; un.n[0] = n; un.src_bf16 = theta_bf16;
+    POETX_TRY(unpack_skew2(un, b, s));
+  }
   if (vec && cnp_use_mfma(b)) {
     // S = Q Q and, from the same accumulators, T = 2I + 2Q + S
     CnpMMArgs a;
@@ -227,17 +231,39 @@ int cnp_fwd_impl(int64_t n, int64_t b, const float *theta, void *g, int g_dtype,
   return gemm_generic(with_terms(batched_f32(n, b, S, T, g, g_dtype), U, 1.f, 1.f), s);
 }
 
+// One side's blocks for the CNP backward.  With an Adam epilogue (adam_step or the
+// layer's fused update), dtheta may be null: the update then consumes the gradient in the
+// pack pass without storing it.
 struct CnpBwdSide {
   int64_t n = 0;
-  const float *theta = nullptr, *dg = nullptr;
+  const void *theta = nullptr;
+  const float *dg = nullptr;
   float *dtheta = nullptr;
+  // fused Adam: new theta, state
+  void *theta_out = nullptr;
+  float *m = nullptr, *v = nullptr;
 };
+
+// the packs of up to two sides, with the Adam epilogue when `h` is given
+int pack_sides(SkewSegs &pk, const CnpBwdSide *side, int nside, int64_t b, int theta_bf16, const AdamEpi *h,
+               hipStream_t s) {
+  if (!h) return pack_skew_grad2(pk, b, s);
+  AdamEpi ad = *h;
+  ad.theta_bf16 = theta_bf16;
+  for (int i = 0; i < nside; ++i) {
+    ad.theta_in[i] = side[i].theta; ad.theta_out[i] = side[i].theta_out;
+    ad.m[i] = side[i].m; ad.v[i] = side[i].v;
+  }
+  return pack_skew_grad2(pk, b, s, &ad);
+}
 
 // CNP backward of up to two independent sides sharing b (the R and P sides of a layer):
 // unpack Q, then the whole adjoint in one fused launch, then pack dtheta.
-int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
+int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h,
+                       void *ws, hipStream_t s) {
   Arena ar(ws);
   SkewSegs un, pk;
+  un.src_bf16 = theta_bf16;
   CnpChainArgs c;
   c.b = (int)b;
   c.name = "cnp_bwd_fused";
@@ -251,14 +277,16 @@ int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, void *ws, h
   }
   POETX_TRY(unpack_skew2(un, b, s));
   POETX_TRY(cnp_bwd_fused(c, s));
-  return pack_skew_grad2(pk, b, s);
+  return pack_sides(pk, side, nside, b, theta_bf16, h, s);
 }
 
 // The same in two chain launches (b = 512, and few blocks), with the three R_j^T through
 // memory.
-int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
+int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h, void *ws,
+                  hipStream_t s) {
   Arena ar(ws);
   SkewSegs un, pk;
+  un.src_bf16 = theta_bf16;
   CnpChainArgs ca, cb;
   ca.b = cb.b = (int)b;
   ca.mode = CNP_CHAIN_BWDA; ca.name = "cnp_bwd_chain_a";
@@ -279,21 +307,23 @@ int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStr
   // first half (rows of Gb P^l) for every block, then the transposed left-Horner half
   POETX_TRY(cnp_chain(ca, s));
   POETX_TRY(cnp_chain(cb, s));
-  return pack_skew_grad2(pk, b, s);
+  return pack_sides(pk, side, nside, b, theta_bf16, h, s);
 }
 
-int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStream_t s) {
+int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h, void *ws,
+                 hipStream_t s) {
   // the chain and MFMA paths read dG with vector loads: an only element-aligned dG
   // takes the vector-ALU path
   bool vec = true;
   for (int i = 0; i < nside; ++i) vec = vec && al16(side[i].dg);
   int64_t nz = 0;
   for (int i = 0; i < nside; ++i) nz += side[i].n;
-  if (vec && cnp_bwd_fused_supported(b, nz)) return cnp_bwd_fused_path(b, side, nside, ws, s);
-  if (vec && cnp_chain_supported(b)) return cnp_bwd_chain(b, side, nside, ws, s);
+  if (vec && cnp_bwd_fused_supported(b, nz)) return cnp_bwd_fused_path(b, side, nside, theta_bf16, h, ws, s);
+  if (vec && cnp_chain_supported(b)) return cnp_bwd_chain(b, side, nside, theta_bf16, h, ws, s);
   Arena ar(ws);
   struct Bufs { float *Q, *K1, *K2, *K3, *Ha, *Hb; } B[2] = {};
   SkewSegs un;
+  un.src_bf16 = theta_bf16;
   for (int i = 0; i < nside; ++i) {
     size_t blk = (size_t)side[i].n * b * b * 4;
     B[i] = {(float *)ar.take(blk), (float *)ar.take(blk), (float *)ar.take(blk),
@@ -330,7 +360,7 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStre
       -1.f, 2.f, 2.f, 2.f, 1.f));
     SkewSegs pk;
     for (int i = 0; i < nside; ++i) { pk.src[i] = B[i].Ha; pk.dst[i] = side[i].dtheta; pk.n[i] = side[i].n; }
-    return pack_skew_grad2(pk, b, s);
+    return pack_sides(pk, side, nside, b, theta_bf16, h, s);
   }
   for (int i = 0; i < nside; ++i) {
     const int64_t n = side[i].n;
@@ -347,17 +377,20 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, void *ws, hipStre
     // R0 = 2Gb + 2K1 + 2K2 + K3 = R1 + K2 + K3 (u.K1 now holds R1)
     POETX_TRY(lincomb(u.K2, n, b, 0.f, u.K1, 1.f, u.K2, 1.f, u.K3, 1.f, nullptr, 0.f, s));
     POETX_TRY(gemm_generic(with_terms(batched_f32(n, b, u.Q, u.Hb, u.Ha, POETX_F32), u.K2, 1.f, -1.f), s));
-    POETX_TRY(pack_skew_grad(u.Ha, side[i].dtheta, n, b, s));
+    SkewSegs pk;
+    pk.src[0] = u.Ha; pk.dst[0] = side[i].dtheta; pk.n[0] = n;
+    POETX_TRY(pack_sides(pk, side + i, 1, b, theta_bf16, h, s));
   }
   return POETX_OK;
 }
 
 }  // namespace
 
-extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *theta, void *g,
-                         int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta,
+extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const void *theta, int32_t theta_dtype,
+                         void *g, int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta,
                          void *ws, size_t *ws_bytes, void *stream) {
   if (dir != POETX_CNP_FWD && dir != POETX_CNP_BWD) return POETX_ERR_INVALID_ARG;
+  if (theta_dtype != POETX_F32 && theta_dtype != POETX_BF16) return POETX_ERR_INVALID_ARG;
   if (nblocks < 0 || !ws_bytes) return POETX_ERR_INVALID_ARG;
   if (b < 1 || b > 1024) return POETX_ERR_SHAPE;
   if (dir == POETX_CNP_FWD) {
@@ -380,10 +413,11 @@ extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const float *t
   if (b == 1) {  // no parameters: G = [1], nothing to differentiate
     return dir == POETX_CNP_FWD ? fill_one(g, nblocks, g_dtype, s) : POETX_OK;
   }
-  if (dir == POETX_CNP_FWD) return cnp_fwd_impl(nblocks, b, theta, g, g_dtype, ws, s);
+  const int tb = theta_dtype == POETX_BF16;
+  if (dir == POETX_CNP_FWD) return cnp_fwd_impl(nblocks, b, theta, tb, g, g_dtype, ws, s);
   CnpBwdSide sd;
   sd.n = nblocks; sd.theta = theta; sd.dg = (const float *)dg; sd.dtheta = dtheta;
-  return cnp_bwd_impl(b, &sd, 1, ws, s);
+  return cnp_bwd_impl(b, &sd, 1, tb, nullptr, ws, s);
 }
 
 // ================================================================== layer ====
@@ -412,6 +446,7 @@ int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
   if (L->w_dtype != POETX_F32 && L->w_dtype != POETX_BF16 && L->w_dtype != POETX_I8) return POETX_ERR_INVALID_ARG;
   if (L->g_dtype != L->act_dtype) return POETX_ERR_UNSUPPORTED;
   if (L->variant != POETX_FAST && L->variant != POETX_MEM) return POETX_ERR_INVALID_ARG;
+  if (L->theta_dtype != POETX_F32 && L->theta_dtype != POETX_BF16) return POETX_ERR_INVALID_ARG;
   if (L->w_dtype == POETX_I8) {
     if (L->act_dtype != POETX_BF16) return POETX_ERR_UNSUPPORTED;
     if (L->variant == POETX_FAST) return POETX_ERR_UNSUPPORTED;
@@ -778,10 +813,28 @@ extern "C" int poetx_forward(const poetx_layer *L, int64_t n_tokens, const void 
   return POETX_OK;
 }
 
-extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void *x, const void *dz,
-                              const void *saved_b, const void *saved_x, void *dx, float *dtheta_r,
-                              float *dtheta_p, float *dg_r, float *dg_p, void *ws, size_t *ws_bytes,
-                              void *stream) {
+namespace {
+
+// Bias corrections of Adam step t in double on the host; the kernels take the step size
+// and 1 / sqrt(1 - beta2^t).
+AdamEpi adam_hyper(float lr, float beta1, float beta2, float eps, int64_t step, float gamma) {
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step), bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  AdamEpi h;
+  h.step_size = (float)((double)gamma * (double)lr / bc1);
+  h.rs2 = (float)(1.0 / std::sqrt(bc2));
+  h.b1 = beta1; h.b2 = beta2; h.eps = eps;
+  return h;
+}
+
+bool adam_args_ok(float beta1, float beta2, float eps, int64_t step) {
+  return step >= 1 && beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps > 0.f;
+}
+
+// The backward; with `opt`, the Adam update of both sides' theta fused into the pack of
+// dtheta (dtheta_r / dtheta_p may then be null).
+int backward_impl(const poetx_layer *L, int64_t n_tokens, const void *x, const void *dz, const void *saved_b,
+                  const void *saved_x, void *dx, float *dtheta_r, float *dtheta_p, float *dg_r, float *dg_p,
+                  const poetx_adam *opt, void *ws, size_t *ws_bytes, void *stream) {
   Plan p;
   POETX_TRY(validate(L, n_tokens, p));
   if (!ws_bytes) return POETX_ERR_INVALID_ARG;
@@ -817,7 +870,17 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
     return POETX_OK;
   }
   POETX_TRY(check_layer_ptrs(L));
-  if (!dtheta_r || !dtheta_p) return POETX_ERR_INVALID_ARG;
+  if (!opt && (!dtheta_r || !dtheta_p)) return POETX_ERR_INVALID_ARG;
+  AdamEpi hyper;
+  if (opt) {
+    if (!adam_args_ok(opt->beta1, opt->beta2, opt->eps, opt->step)) return POETX_ERR_INVALID_ARG;
+    if (!opt->theta_r_out || !opt->theta_p_out || !opt->m_r || !opt->v_r || !opt->m_p || !opt->v_p)
+      return POETX_ERR_INVALID_ARG;
+    hyper = adam_hyper(opt->lr, opt->beta1, opt->beta2, opt->eps, opt->step, opt->gamma);
+  }
+  const AdamEpi *h = opt ? &hyper : nullptr;
+  const int th_bf = L->theta_dtype == POETX_BF16;
+  const size_t te = th_bf ? 2 : 4;
   if (p.N > 0 && (!x || !dz || !dx || (!p.mem && !saved_b))) return POETX_ERR_INVALID_ARG;
   if (*ws_bytes < ar.used) return POETX_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -860,22 +923,57 @@ extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void
   // CNP backward (Method §4): the full blocks of both sides together, then each side's
   // last block at its own size (a block of size 1 has no parameters)
   const int64_t pb = b * (b - 1) / 2;
+  // a side's blocks from packed offset `off` (elements) on: theta, dtheta, new theta, state
+  auto side_at = [&](bool rside, int64_t n, int64_t off, const float *dg) {
+    CnpBwdSide sd;
+    sd.n = n;
+    sd.theta = (const char *)(rside ? L->theta_r : L->theta_p) + off * te;
+    sd.dg = dg;
+    float *dth = rside ? dtheta_r : dtheta_p;
+    sd.dtheta = dth ? dth + off : nullptr;
+    if (opt) {
+      sd.theta_out = (char *)(rside ? opt->theta_r_out : opt->theta_p_out) + off * te;
+      sd.m = (rside ? opt->m_r : opt->m_p) + off;
+      sd.v = (rside ? opt->v_r : opt->v_p) + off;
+    }
+    return sd;
+  };
   CnpBwdSide sides[2];
   int ns = 0;
-  if (p.nr) { sides[ns].n = p.nr; sides[ns].theta = L->theta_r; sides[ns].dg = gr; sides[ns].dtheta = dtheta_r; ++ns; }
-  if (p.np) { sides[ns].n = p.np; sides[ns].theta = L->theta_p; sides[ns].dg = gp; sides[ns].dtheta = dtheta_p; ++ns; }
-  if (ns) POETX_TRY(cnp_bwd_impl(b, sides, ns, cws, s));
-  CnpBwdSide lr, lp;
-  lr.n = 1; lr.theta = L->theta_r + p.nr * pb; lr.dg = gr + p.nr * bb; lr.dtheta = dtheta_r + p.nr * pb;
-  lp.n = 1; lp.theta = L->theta_p + p.np * pb; lp.dg = gp + p.np * bb; lp.dtheta = dtheta_p + p.np * pb;
+  if (p.nr) sides[ns++] = side_at(true, p.nr, 0, gr);
+  if (p.np) sides[ns++] = side_at(false, p.np, 0, gp);
+  if (ns) POETX_TRY(cnp_bwd_impl(b, sides, ns, th_bf, h, cws, s));
+  const CnpBwdSide lr = side_at(true, 1, p.nr * pb, gr + p.nr * bb);
+  const CnpBwdSide lp = side_at(false, 1, p.np * pb, gp + p.np * bb);
   if (p.lr > 1 && p.lr == p.lp) {
     const CnpBwdSide both[2] = {lr, lp};
-    return cnp_bwd_impl(p.lr, both, 2, cws, s);
+    return cnp_bwd_impl(p.lr, both, 2, th_bf, h, cws, s);
   }
-  if (p.lr > 1) POETX_TRY(cnp_bwd_impl(p.lr, &lr, 1, cws, s));
-  if (p.lp > 1) POETX_TRY(cnp_bwd_impl(p.lp, &lp, 1, cws, s));
+  if (p.lr > 1) POETX_TRY(cnp_bwd_impl(p.lr, &lr, 1, th_bf, h, cws, s));
+  if (p.lp > 1) POETX_TRY(cnp_bwd_impl(p.lp, &lp, 1, th_bf, h, cws, s));
   return POETX_OK;
 }
+
+}  // namespace
+
+extern "C" int poetx_backward(const poetx_layer *L, int64_t n_tokens, const void *x, const void *dz,
+                              const void *saved_b, const void *saved_x, void *dx, float *dtheta_r,
+                              float *dtheta_p, float *dg_r, float *dg_p, void *ws, size_t *ws_bytes,
+                              void *stream) {
+  return backward_impl(L, n_tokens, x, dz, saved_b, saved_x, dx, dtheta_r, dtheta_p, dg_r, dg_p, nullptr, ws,
+                       ws_bytes, stream);
+}
+
+extern "C" int poetx_backward_adam(const poetx_layer *L, int64_t n_tokens, const void *x, const void *dz,
+                                   const void *saved_b, const void *saved_x, void *dx, float *dtheta_r,
+                                   float *dtheta_p, const poetx_adam *opt, void *ws, size_t *ws_bytes,
+                                   void *stream) {
+  if (!opt) return POETX_ERR_INVALID_ARG;
+  return backward_impl(L, n_tokens, x, dz, saved_b, saved_x, dx, dtheta_r, dtheta_p, nullptr, nullptr, opt, ws,
+                       ws_bytes, stream);
+}
+
+
 
 // ================================================================= fold ====
 // Phase-end fold (the consolidation step of merge-then-reinitialize): the layer's
@@ -919,17 +1017,14 @@ extern "C" int poetx_fold(const poetx_layer *L, void *w_out, void *ws, size_t *w
 }
 
 // ================================================================ optimizer ====
-extern "C" int poetx_adam_step(int64_t n_params, float *theta, const float *grad, float *m, float *v,
-                               float lr, float beta1, float beta2, float eps, int64_t step, float gamma,
+extern "C" int poetx_adam_step(int64_t n_params, void *theta, int32_t theta_dtype, const float *grad, float *m,
+                               float *v, float lr, float beta1, float beta2, float eps, int64_t step, float gamma,
                                void *stream) {
-  if (n_params < 0 || step < 1) return POETX_ERR_INVALID_ARG;
-  if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f)) return POETX_ERR_INVALID_ARG;
+  if (n_params < 0 || !adam_args_ok(beta1, beta2, eps, step)) return POETX_ERR_INVALID_ARG;
+  if (theta_dtype != POETX_F32 && theta_dtype != POETX_BF16) return POETX_ERR_INVALID_ARG;
   if (n_params == 0) return POETX_OK;
   if (!theta || !grad || !m || !v) return POETX_ERR_INVALID_ARG;
   if (((uintptr_t)theta | (uintptr_t)grad | (uintptr_t)m | (uintptr_t)v) % 16) return POETX_ERR_INVALID_ARG;
-  // bias corrections in double on the host
-  const double bc1 = 1.0 - std::pow((double)beta1, (double)step), bc2 = 1.0 - std::pow((double)beta2, (double)step);
-  const float step_size = (float)((double)gamma * (double)lr / bc1);
-  const float rs2 = (float)(1.0 / std::sqrt(bc2));
-  return adam_step(n_params, theta, grad, m, v, step_size, beta1, beta2, rs2, eps, (hipStream_t)stream);
+  return adam_step(n_params, theta, theta_dtype, grad, m, v, adam_hyper(lr, beta1, beta2, eps, step, gamma),
+                   (hipStream_t)stream);
 }

@@ -279,37 +279,58 @@ int invert_perm(const int32_t *perm, int32_t *inv, int64_t n, hipStream_t s) {
 
 // Adam on packed parameters, one fused pass: m, v, theta updated in place from g.
 //   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;  theta -= step_size * m / (sqrt(v) * rs2 + eps)
-// with step_size = gamma lr / (1 - b1^t) and rs2 = 1 / sqrt(1 - b2^t) from the host.
-__global__ void k_adam(int64_t n, float *__restrict__ theta, const float *__restrict__ g, float *__restrict__ m,
-                       float *__restrict__ v, float step_size, float b1, float b2, float rs2, float eps) {
+// with step_size = gamma lr / (1 - b1^t) and rs2 = 1 / sqrt(1 - b2^t) from the host.  A bf16
+// theta is widened, updated in float32 and rounded back to nearest even.
+__device__ inline float adam_update(float th, float gg, float &mm, float &vv, const AdamEpi &h) {
+  mm = h.b1 * mm + (1.f - h.b1) * gg;
+  vv = h.b2 * vv + (1.f - h.b2) * gg * gg;
+  return th - h.step_size * mm / (sqrtf(vv) * h.rs2 + h.eps);
+}
+
+template <typename T>
+__global__ void k_adam(int64_t n, T *__restrict__ theta, const float *__restrict__ g, float *__restrict__ m,
+                       float *__restrict__ v, AdamEpi h) {
   const int64_t n4 = n / 4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    float4 t = ((float4 *)theta)[i], gg = ((const float4 *)g)[i], mm = ((float4 *)m)[i], vv = ((float4 *)v)[i];
-    float *tp = &t.x, *gp = &gg.x, *mp = &mm.x, *vp = &vv.x;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      mp[c] = b1 * mp[c] + (1.f - b1) * gp[c];
-      vp[c] = b2 * vp[c] + (1.f - b2) * gp[c] * gp[c];
-      tp[c] -= step_size * mp[c] / (sqrtf(vp[c]) * rs2 + eps);
+    float tp[4];
+    if constexpr (sizeof(T) == 4) {
+      const float4 t = ((const float4 *)theta)[i];
+      tp[0] = t.x; tp[1] = t.y; tp[2] = t.z; tp[3] = t.w;
+    } else {
+      const uint2 t = ((const uint2 *)theta)[i];
+      tp[0] = bf16_to_f32((bf16_t)t.x); tp[1] = bf16_to_f32((bf16_t)(t.x >> 16));
+      tp[2] = bf16_to_f32((bf16_t)t.y); tp[3] = bf16_to_f32((bf16_t)(t.y >> 16));
     }
-    ((float4 *)theta)[i] = t; ((float4 *)m)[i] = mm; ((float4 *)v)[i] = vv;
+    float4 gg = ((const float4 *)g)[i], mm = ((float4 *)m)[i], vv = ((float4 *)v)[i];
+    float *gp = &gg.x, *mp = &mm.x, *vp = &vv.x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) tp[c] = adam_update(tp[c], gp[c], mp[c], vp[c], h);
+    if constexpr (sizeof(T) == 4) {
+      ((float4 *)theta)[i] = make_float4(tp[0], tp[1], tp[2], tp[3]);
+    } else {
+      ((uint2 *)theta)[i] = make_uint2((uint32_t)f32_to_bf16(tp[0]) | ((uint32_t)f32_to_bf16(tp[1]) << 16),
+                                       (uint32_t)f32_to_bf16(tp[2]) | ((uint32_t)f32_to_bf16(tp[3]) << 16));
+    }
+    ((float4 *)m)[i] = mm; ((float4 *)v)[i] = vv;
   }
   // tail (n % 4 elements), handled by the first threads of the grid
   const int64_t e = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e < n) {
-    const float gg = g[e];
-    const float mm = b1 * m[e] + (1.f - b1) * gg, vv = b2 * v[e] + (1.f - b2) * gg * gg;
+    float mm = m[e], vv = v[e];
+    const float t = adam_update(ld_f(theta + e), g[e], mm, vv, h);
     m[e] = mm; v[e] = vv;
-    theta[e] -= step_size * mm / (sqrtf(vv) * rs2 + eps);
+    st_f(theta + e, t);
   }
 }
 
-int adam_step(int64_t n, float *theta, const float *g, float *m, float *v, float step_size, float b1, float b2,
-              float rs2, float eps, hipStream_t s) {
+int adam_step(int64_t n, void *theta, int theta_dt, const float *g, float *m, float *v, const AdamEpi &h,
+              hipStream_t s) {
   if (n <= 0) return POETX_OK;
   const int64_t want = cdiv(n / 4 > 0 ? n / 4 : 1, 256);
   const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
-  return launch_k("adam_step", s, k_adam, grid, 256, 0, n, theta, g, m, v, step_size, b1, b2, rs2, eps);
+  if (theta_dt == POETX_BF16)
+    return launch_k("adam_step", s, k_adam<bf16_t>, grid, 256, 0, n, (bf16_t *)theta, g, m, v, h);
+  return launch_k("adam_step", s, k_adam<float>, grid, 256, 0, n, (float *)theta, g, m, v, h);
 }
 
 // out[c][r] = in[r][c] for a [rows][cols] matrix, through 64 x 64 LDS tiles.
@@ -448,6 +469,11 @@ __device__ inline void block_tile(int64_t L, int64_t nz, int T, int64_t &z, int 
   upper_tile((int)idx, T, rb, cb);
 }
 
+// Packed parameter e of segment si: float32, or bf16 widened exactly.
+__device__ inline float ld_theta(const SkewSegs &sg, int si, int64_t e) {
+  return sg.src_bf16 ? bf16_to_f32(((const bf16_t *)sg.src[si])[e]) : ((const float *)sg.src[si])[e];
+}
+
 // Both kernels walk 32 x 32 tiles (rb <= cb) of the upper triangle and handle the
 // mirrored tile through LDS, so every global access is contiguous along a row.
 __global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
@@ -457,7 +483,7 @@ __global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
   block_tile(blockIdx.x, sg.n[0] + sg.n[1], (int)((b + 31) / 32), z, rb, cb);
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
-  const float *th = sg.src[si] + z * (b * (b - 1) / 2);
+  const int64_t th0 = z * (b * (b - 1) / 2);
   float *Q = sg.dst[si] + z * b * b;
   const int tc = threadIdx.x & 31;
 #pragma unroll
@@ -466,7 +492,7 @@ __global__ __launch_bounds__(256) void k_unpack_skew(SkewSegs sg, int64_t b) {
     const int64_t r = rb * 32 + tr, c = cb * 32 + tc;
     float v = 0.f;
     if (r < b && c < b) {
-      if (r < c) v = th[triu_index(r, c, b)];
+      if (r < c) v = ld_theta(sg, si, th0 + triu_index(r, c, b));
       if (r <= c) Q[r * b + c] = v;
     }
     t[tr][tc] = v;
@@ -492,13 +518,13 @@ __global__ __launch_bounds__(256) void k_unpack_frag(SkewSegs sg, int64_t b) {
   block_tile(blockIdx.x, sg.n[0] + sg.n[1], (int)((b + 31) / 32), z, rb, cb);
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
-  const float *th = sg.src[si] + z * (b * (b - 1) / 2);
+  const int64_t th0 = z * (b * (b - 1) / 2);
   const int tid = threadIdx.x, tc = tid & 31;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tr = (tid >> 5) + 8 * i;
     const int64_t r = rb * 32 + tr, c = cb * 32 + tc;
-    t[tr][tc] = r < c ? th[triu_index(r, c, b)] : 0.f;
+    t[tr][tc] = r < c ? ld_theta(sg, si, th0 + triu_index(r, c, b)) : 0.f;
   }
   __syncthreads();
   const int tt = tid >> 7, pl = (tid >> 6) & 1, ln = tid & 63;
@@ -549,15 +575,21 @@ int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t 
   return unpack_skew2(sg, b, s);
 }
 
-__global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b) {
+// dtheta[k(r, c)] = M[r][c] - M[c][r]; with ADAM the same pass applies the Adam update to
+// theta (read from ad.theta_in, written to ad.theta_out, which may be the same buffer:
+// each element is read and written by one thread) and to its state m, v, and writes
+// dtheta only where sg.dst is set.
+template <bool ADAM>
+__global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b, AdamEpi ad) {
   __shared__ float up[32][33], lo[32][33];
   int rb, cb;
   int64_t z;
   block_tile(blockIdx.x, sg.n[0] + sg.n[1], (int)((b + 31) / 32), z, rb, cb);
   int si = 0;
   if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
-  const float *M = sg.src[si] + z * b * b;
-  float *dth = sg.dst[si] + z * (b * (b - 1) / 2);
+  const float *M = (const float *)sg.src[si] + z * b * b;
+  const int64_t th0 = z * (b * (b - 1) / 2);
+  float *dth = sg.dst[si] ? sg.dst[si] + th0 : nullptr;
   const int tc = threadIdx.x & 31;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -572,16 +604,31 @@ __global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b) 
   for (int i = 0; i < 4; ++i) {
     const int tr = (threadIdx.x >> 5) + 8 * i;
     const int64_t r = rb * 32 + tr, c = cb * 32 + tc;
-    if (r < c && c < b) dth[triu_index(r, c, b)] = up[tr][tc] - lo[tc][tr];
+    if (r < c && c < b) {
+      const int64_t k = triu_index(r, c, b);
+      const float g = up[tr][tc] - lo[tc][tr];
+      if (!ADAM || dth) dth[k] = g;
+      if constexpr (ADAM) {
+        const int64_t e = th0 + k;
+        float mm = ad.m[si][e], vv = ad.v[si][e];
+        const float th = ad.theta_bf16 ? bf16_to_f32(((const bf16_t *)ad.theta_in[si])[e])
+                                       : ((const float *)ad.theta_in[si])[e];
+        const float t = adam_update(th, g, mm, vv, ad);
+        ad.m[si][e] = mm; ad.v[si][e] = vv;
+        if (ad.theta_bf16) ((bf16_t *)ad.theta_out[si])[e] = f32_to_bf16(t);
+        else ((float *)ad.theta_out[si])[e] = t;
+      }
+    }
   }
 }
 
-int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s) {
+int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s, const AdamEpi *ad) {
   const int64_t nz = sg.n[0] + sg.n[1];
   if (nz <= 0) return POETX_OK;
   const int64_t T = cdiv(b, 32), nwg = nz * (T * (T + 1) / 2);
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
-  return launch_k("pack_skew_grad", s, k_pack_skew_grad, dim3((unsigned)nwg), 256, 0, sg, b);
+  if (ad) return launch_k("pack_skew_grad_adam", s, k_pack_skew_grad<true>, dim3((unsigned)nwg), 256, 0, sg, b, *ad);
+  return launch_k("pack_skew_grad", s, k_pack_skew_grad<false>, dim3((unsigned)nwg), 256, 0, sg, b, AdamEpi());
 }
 
 int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s) {

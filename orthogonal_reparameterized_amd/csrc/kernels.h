@@ -54,19 +54,31 @@ __host__ __device__ inline int64_t cnp_frag_off(int64_t r, int64_t c, int64_t b)
   const int64_t lane = 16 * (kr >> 3) + (c & 15);
   return (kk * (b >> 4) + t) * 1024 + lane * 8 + (kr & 7);
 }
+// src: theta (unpack; float32, or bf16 when src_bf16) or M (pack; float32).
 struct SkewSegs {
-  const float *src[2] = {nullptr, nullptr};
+  const void *src[2] = {nullptr, nullptr};
   float *dst[2] = {nullptr, nullptr};
   bf16_t *planes[2] = {nullptr, nullptr};
   int64_t n[2] = {0, 0};
+  int src_bf16 = 0;
 };
-// fused Adam pass on packed parameters (step_size and rs2 carry the bias corrections)
-int adam_step(int64_t n, float *theta, const float *g, float *m, float *v, float step_size, float b1, float b2,
-              float rs2, float eps, hipStream_t s);
+// Adam hyperparameters (step_size and rs2 carry the bias corrections) and, for the update
+// fused into the pack of dtheta, the parameter and state buffers of up to two segments.
+struct AdamEpi {
+  const void *theta_in[2] = {nullptr, nullptr};
+  void *theta_out[2] = {nullptr, nullptr};
+  float *m[2] = {nullptr, nullptr}, *v[2] = {nullptr, nullptr};
+  int theta_bf16 = 0;
+  float step_size = 0.f, b1 = 0.f, b2 = 0.f, rs2 = 1.f, eps = 1.f;
+};
+// fused Adam pass on packed parameters (theta float32 or bf16)
+int adam_step(int64_t n, void *theta, int theta_dt, const float *g, float *m, float *v, const AdamEpi &h,
+              hipStream_t s);
 // inv[perm[i]] = i for a permutation of 0 .. n-1
 int invert_perm(const int32_t *perm, int32_t *inv, int64_t n, hipStream_t s);
 int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s);
-int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s);
+// with ad: the Adam update of theta fused into the same pass (dtheta written where sg.dst is set)
+int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s, const AdamEpi *ad = nullptr);
 int unpack_skew(const float *theta, float *Q, int64_t n, int64_t b, hipStream_t s);
 int pack_skew_grad(const float *M, float *dtheta, int64_t n, int64_t b, hipStream_t s);
 // out = c0*X0 + c1*X1 + c2*X2 + c3*X3 + cI*I over n blocks of b x b (null X_i skipped)

@@ -27,7 +27,9 @@ def upload(arr, dtype: str, device="cuda"):
 
 class LayerStep:
     def __init__(self, wl, inputs: dict, variant: str = "fast", device="cuda", perms: bool = True,
-                 transposed_weight: bool = False, keep_x: bool = True):
+                 transposed_weight: bool = False, keep_x: bool = True, theta_dtype: str = "f32"):
+        """theta_dtype "bf16": inputs["theta_r"], inputs["theta_p"] hold bf16 bit patterns and
+        theta is stored in bf16 (dtheta and the optimizer state stay float32)."""
         self.wl = wl
         self.variant = B.POETX_FAST if variant == "fast" else B.POETX_MEM
         act = _TORCH[wl.act]
@@ -60,15 +62,15 @@ class LayerStep:
         self.dz = upload(inputs["dz"], wl.act, dev)
         n, b = self.x.shape[0], wl.b
         if not self.ragged:
-            self.theta = upload(np.concatenate([inputs["theta_r"], inputs["theta_p"]]), "f32", dev)
+            self.theta = upload(np.concatenate([inputs["theta_r"], inputs["theta_p"]]), theta_dtype, dev)
             self.theta_r, self.theta_p = self.theta[:self.n_r], self.theta[self.n_r:]
             self.g = torch.empty((self.n_r + self.n_p, b, b), dtype=act, device=dev)
             self.g_r, self.g_p = self.g[:self.n_r], self.g[self.n_r:]
         else:
             # one allocation per side, so that each side's buffer starts 16-byte aligned
             self.theta = None
-            self.theta_r = upload(np.ravel(inputs["theta_r"]), "f32", dev)
-            self.theta_p = upload(np.ravel(inputs["theta_p"]), "f32", dev)
+            self.theta_r = upload(np.ravel(inputs["theta_r"]), theta_dtype, dev)
+            self.theta_p = upload(np.ravel(inputs["theta_p"]), theta_dtype, dev)
             self.g = None
             self.g_r = torch.empty(self.n_r * b * b + self.l_r ** 2, dtype=act, device=dev)
             self.g_p = torch.empty(self.n_p * b * b + self.l_p ** 2, dtype=act, device=dev)
@@ -78,8 +80,9 @@ class LayerStep:
         self.saved_x = (torch.empty((n, wl.d_in), dtype=act, device=dev)
                         if self.variant == B.POETX_FAST and keep_x and self.perm_in is not None else None)
         self.dx = torch.empty((n, wl.d_in), dtype=act, device=dev)
-        self.dtheta_r = torch.empty_like(self.theta_r)
-        self.dtheta_p = torch.empty_like(self.theta_p)
+        self.dtheta_r = torch.empty(self.theta_r.shape, dtype=torch.float32, device=dev)
+        self.dtheta_p = torch.empty(self.theta_p.shape, dtype=torch.float32, device=dev)
+        self.adam = None  # Adam state of the fused update (step_adam)
         self.layer = B.Layer(self.w_merged, self.theta_r, self.theta_p, self.g_r, self.g_p, b,
                              act_dtype=act, variant=self.variant, w_scale=self.w_scale,
                              perm_in=self.perm_in, perm_out=self.perm_out, w_merged_t=self.w_merged_t)
@@ -110,3 +113,15 @@ class LayerStep:
         self.cnp()
         self.forward()
         return self.backward(want_dg)
+
+    def step_adam(self, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, gamma=1.0, keep_dtheta=False):
+        """A training step with the Adam update of theta fused into the backward's CNP pass
+        (theta updated in place; dtheta also written when keep_dtheta)."""
+        if self.adam is None:
+            self.adam = B.AdamState.zeros_like(self.layer)
+        self.cnp()
+        self.forward()
+        return B.poetx_backward_adam(self.layer, self.x, self.dz, self.adam, self.saved_b, lr=lr, betas=betas,
+                                     eps=eps, gamma=gamma, saved_x=self.saved_x, dx=self.dx,
+                                     dtheta_r=self.dtheta_r if keep_dtheta else None,
+                                     dtheta_p=self.dtheta_p if keep_dtheta else None)

@@ -88,7 +88,7 @@ def test_workspace_queries(B):
     # without an input permutation there is nothing to keep
     assert fwd(B, layer(B), saved_x=FAKE)[1] == need_fast
     nb = ctypes.c_size_t(0)
-    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 16, 256, None, None, B.POETX_BF16, None, B.POETX_F32, None,
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 16, 256, None, B.POETX_F32, None, B.POETX_BF16, None, B.POETX_F32, None,
                            None, ctypes.byref(nb), None) == B.POETX_OK
     assert nb.value >= 16 * 256 * 256 * 4
 
@@ -131,17 +131,17 @@ def test_validation_codes(B):
     # CNP
     nb = ctypes.c_size_t(1 << 40)
     for bad_b in (0, 2048):
-        assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, bad_b, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+        assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, bad_b, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, 0, None, FAKE,
                                ctypes.byref(nb), None) == B.POETX_ERR_SHAPE
     q = ctypes.c_size_t(0)  # blocks of size 1 (no parameters) are accepted
-    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 1, None, None, B.POETX_BF16, None, 0, None, None,
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 1, None, B.POETX_F32, None, B.POETX_BF16, None, 0, None, None,
                            ctypes.byref(q), None) == B.POETX_OK
-    assert B.raw.poetx_cnp(9, 4, 64, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+    assert B.raw.poetx_cnp(9, 4, 64, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, 0, None, FAKE,
                            ctypes.byref(nb), None) == B.POETX_ERR_INVALID_ARG
-    assert B.raw.poetx_cnp(B.POETX_CNP_BWD, 4, 64, FAKE, None, 0, None, B.POETX_F32, FAKE, FAKE,
+    assert B.raw.poetx_cnp(B.POETX_CNP_BWD, 4, 64, FAKE, B.POETX_F32, None, 0, None, B.POETX_F32, FAKE, FAKE,
                            ctypes.byref(nb), None) == B.POETX_ERR_INVALID_ARG   # dg missing
     small = ctypes.c_size_t(16)
-    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 64, FAKE, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 64, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, 0, None, FAKE,
                            ctypes.byref(small), None) == B.POETX_ERR_WORKSPACE
     # merge
     assert B.raw.poetx_merge_perm(None, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG
@@ -174,12 +174,12 @@ def test_fold_validation(B):
 
 def test_adam_validation(B):
     f = B.raw.poetx_adam_step
-    assert f(0, None, None, None, None, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_OK  # empty: no-op
-    assert f(8, FAKE, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 0, 1.0, None) == B.POETX_ERR_INVALID_ARG
-    assert f(8, FAKE, FAKE, FAKE, FAKE, 1e-3, 1.0, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
-    assert f(8, FAKE, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 0.0, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
-    assert f(8, FAKE, None, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
-    assert f(8, FAKE + 4, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(0, None, B.POETX_F32, None, None, None, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_OK  # empty: no-op
+    assert f(8, FAKE, B.POETX_F32, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 0, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(8, FAKE, B.POETX_F32, FAKE, FAKE, FAKE, 1e-3, 1.0, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(8, FAKE, B.POETX_F32, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 0.0, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(8, FAKE, B.POETX_F32, None, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
+    assert f(8, FAKE + 4, B.POETX_F32, FAKE, FAKE, FAKE, 1e-3, 0.9, 0.999, 1e-8, 1, 1.0, None) == B.POETX_ERR_INVALID_ARG
 
 
 def _c_params(name):
@@ -200,6 +200,8 @@ def _ctype_of(decl):
         return "size_t_ptr"
     if "poetx_layer *" in d:
         return "layer_ptr"
+    if "poetx_adam *" in d:
+        return "adam_ptr"
     if "char *" in d:
         return (ctypes.c_char_p, ctypes.c_void_p)
     if "*" in d:
@@ -221,6 +223,8 @@ def test_header_signatures_match_binding(B):
                 assert g is ctypes.POINTER(ctypes.c_size_t), name
             elif w == "layer_ptr":
                 assert g is ctypes.POINTER(B.PoetxLayerC), name
+            elif w == "adam_ptr":
+                assert g is ctypes.POINTER(B.PoetxAdamC), name
             elif w is ctypes.c_int:
                 assert g in (ctypes.c_int, ctypes.c_int32), name
             elif isinstance(w, tuple):
@@ -239,8 +243,20 @@ def test_header_signatures_match_binding(B):
             nm = nm.strip(",")
             if nm and nm not in ("const", "void", "float", "int32_t", "int64_t"):
                 fields.append((nm, typ))
-    cmap = {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int32, "ptr": ctypes.c_void_p}
+    cmap = {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int32, "ptr": ctypes.c_void_p, "float": ctypes.c_float}
     assert [(n, cmap[t]) for n, t in fields] == list(B.PoetxLayerC._fields_)
+    body = re.search(r"typedef struct \{([^{}]*)\} poetx_adam;", text).group(1)
+    fields = []
+    for decl in body.split(";"):
+        decl = " ".join(decl.split())
+        if not decl:
+            continue
+        typ = "ptr" if "*" in decl else decl.split()[0]
+        for nm in decl.replace("*", " ").split()[1:]:
+            nm = nm.strip(",")
+            if nm:
+                fields.append((nm, typ))
+    assert [(n, cmap[t]) for n, t in fields] == list(B.PoetxAdamC._fields_)
 
 
 def test_int8_with_transposed_weight_refused(B):
@@ -250,3 +266,36 @@ def test_int8_with_transposed_weight_refused(B):
     c.w_merged_t = FAKE_OUT
     assert fwd(B, c, saved=None)[0] == B.POETX_ERR_INVALID_ARG
     assert bwd(B, c, saved=None)[0] == B.POETX_ERR_INVALID_ARG
+
+
+def test_backward_adam_validation(B):
+    """poetx_backward_adam: same workspace as poetx_backward; optimizer arguments checked on the
+    host (NULL opt or buffers, step < 1, beta outside [0, 1), eps <= 0)."""
+    c = layer(B)
+    st, need = bwd(B, c)
+    nb = ctypes.c_size_t(0)
+    o = B.PoetxAdamC()
+    o.lr, o.beta1, o.beta2, o.eps, o.gamma, o.step = 1e-3, 0.9, 0.999, 1e-8, 1.0, 1
+    o.m_r = o.v_r = o.m_p = o.v_p = FAKE
+    o.theta_r_out = o.theta_p_out = FAKE
+
+    def call(opt, ws=None, ws_bytes=0, dtr=None, dtp=None):
+        nb = ctypes.c_size_t(ws_bytes)
+        st = B.raw.poetx_backward_adam(ctypes.byref(c), 64, FAKE, FAKE, FAKE, None, FAKE, dtr, dtp,
+                                       ctypes.byref(opt) if opt is not None else None, ws, ctypes.byref(nb), None)
+        return st, nb.value
+    st, need_a = call(o)
+    assert st == B.POETX_OK and need_a == need
+    assert call(None)[0] == B.POETX_ERR_INVALID_ARG
+    assert call(o, ws=FAKE, ws_bytes=need - 1)[0] == B.POETX_ERR_WORKSPACE
+    for field, bad in (("step", 0), ("beta1", 1.0), ("beta2", -0.1), ("eps", 0.0), ("m_p", None),
+                       ("theta_r_out", None)):
+        o2 = B.PoetxAdamC.from_buffer_copy(o)
+        setattr(o2, field, bad)
+        assert call(o2, ws=FAKE, ws_bytes=need)[0] == B.POETX_ERR_INVALID_ARG, field
+    # theta dtype of the layer: F32 or BF16
+    bad = layer(B)
+    bad.theta_dtype = 7
+    assert fwd(B, bad)[0] == B.POETX_ERR_INVALID_ARG
+    bad.theta_dtype = B.POETX_BF16
+    assert fwd(B, bad)[0] == B.POETX_OK

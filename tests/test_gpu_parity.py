@@ -52,7 +52,10 @@ CNP_CASES = [(8, 32, 0.02), (11, 64, 0.03), (19, 128, 0.02), (3, 192, 0.01), (3,
              (2, 512, 0.01), (2, 1024, 0.005),
              # enough blocks for the 64-row panels (4 workgroups per CU): 517 = 8 * 64 + 5
              # also leaves blocks past the last full group of 8
-             (517, 128, 0.02), (256, 256, 0.01)]
+             (517, 128, 0.02), (256, 256, 0.01),
+             # enough blocks for the 128-row forward panels (b = 256) and the 64-row b = 512
+             # forward and second backward chains
+             (600, 256, 0.01), (40, 512, 0.01)]
 
 
 @pytest.mark.parametrize("n,b,std", CNP_CASES + [(5, 48, 0.05)])
