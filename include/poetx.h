@@ -103,6 +103,9 @@ typedef struct {
                                   dtheta stays float32                               */
 } poetx_layer;
 
+/* Size of the static device workspace of poetx_cnp_noalloc, per GPU (64 MiB). */
+#define POETX_NOALLOC_SCRATCH_BYTES (64u << 20)
+
 /*
  * poetx_merge_perm -- Method §2 (permutation merge, once per inner phase):
  *     w_merged[i][k] = w[perm_out[i]][perm_in[k]]
@@ -145,6 +148,23 @@ int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64
 int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const void *theta, int32_t theta_dtype,
               void *g, int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta, void *ws,
               size_t *ws_bytes, void *stream);
+
+/*
+ * poetx_cnp_noalloc -- for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): poetx_cnp, same arguments
+ * and results, with its workspace in a static device array of POETX_NOALLOC_SCRATCH_BYTES
+ * per GPU, set up on the first call on each device and held until the process ends.  It
+ * calls no hipMalloc / hipFree.  Every call on a GPU uses that GPU's one array: calls
+ * that overlap on one GPU (two streams, or two threads) race and must not be made; calls
+ * in one stream's order are fine.  The CNP writes every workspace byte it reads, so the
+ * contents a previous call left behind do not matter.
+ * Errors: as poetx_cnp; a call whose workspace (the poetx_cnp query) exceeds
+ * POETX_NOALLOC_SCRATCH_BYTES -> POETX_ERR_WORKSPACE, before any launch (for b = 256 that
+ * is more than 64 forward or 42 backward blocks).
+ */
+int poetx_cnp_noalloc(int32_t dir, int64_t nblocks, int64_t b, const void *theta, int32_t theta_dtype,
+                      void *g, int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta,
+                      void *stream);
 
 /*
  * poetx_forward -- Method §1 eq. 3 with §2 and §3 (batched block-diagonal

@@ -59,6 +59,7 @@ _lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp,
                                ctypes.POINTER(_sz), _vp]
 _lib.poetx_backward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _vp, _vp, _vp, ctypes.POINTER(_sz), _vp]
+_lib.poetx_cnp_noalloc.argtypes = [_i32, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp]
 _lib.poetx_backward_adam.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.POINTER(PoetxAdamC), _vp, ctypes.POINTER(_sz), _vp]
 _lib.poetx_fold.argtypes = [ctypes.POINTER(PoetxLayerC), _vp, _vp, ctypes.POINTER(_sz), _vp]
@@ -70,12 +71,12 @@ _lib.poetx_version.restype = ctypes.c_char_p
 _lib.poetx_prof_enable.argtypes = [_i32]
 _lib.poetx_prof_read.argtypes = [ctypes.c_char_p, _sz]
 _lib.poetx_prof_only.argtypes = [ctypes.c_char_p]
-for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_backward_adam", "poetx_fold",
+for _f in ("poetx_merge_perm", "poetx_cnp", "poetx_cnp_noalloc", "poetx_forward", "poetx_backward", "poetx_backward_adam", "poetx_fold",
            "poetx_adam_step",
            "poetx_prof_enable", "poetx_prof_only", "poetx_prof_read"):
     getattr(_lib, _f).restype = ctypes.c_int
 
-EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_forward", "poetx_backward", "poetx_backward_adam", "poetx_fold",
+EXPORTED = ("poetx_merge_perm", "poetx_cnp", "poetx_cnp_noalloc", "poetx_forward", "poetx_backward", "poetx_backward_adam", "poetx_fold",
             "poetx_adam_step",
             "poetx_status_string", "poetx_version", "poetx_prof_enable", "poetx_prof_only", "poetx_prof_read")
 
