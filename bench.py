@@ -156,10 +156,11 @@ def _sync():
 SETTLE_S = 0.3
 
 
-def settle(st, seconds=SETTLE_S):
+def settle(st, seconds=None):
     """Untimed steps for `seconds` of wall time, ahead of the warm-up steps: an idle GPU
     comes back at low clocks and takes tens of ms of load to reach its steady ones (a
     kernel trace of the first steps after idle shows every kernel 5-8% slower)."""
+    seconds = SETTLE_S if seconds is None else seconds
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(8):
@@ -587,11 +588,30 @@ def summarize_counters(fetch_db, write_db, copy_fetch_db, copy_write_db, bench_j
 
 
 def summarize_pmc(*dbs):
+    """Per-kernel averages of the counters in --pmc databases; where a kernel has
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE, its MFMA-busy fraction (busy cycles summed
+    over the SIMDs / (GPU-active cycles per XCD x SIMDs)), and with SQ_INSTS_VALU_MFMA_MOPS_BF16 its
+    bf16 MFMA flops per dispatch (MOPS x 512)."""
+    import torch
+    simds = 4 * (torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256)
+    per = {}
     print("| kernel | counter | dispatches | average per dispatch |")
     print("|---|---|---:|---:|")
     for db in dbs:
         for name, ctr, n, v in sorted(_pmc_rows(db), key=lambda r: (r[0], r[1])):
             print(f"| `{_short(name)}` | {ctr} | {n} | {v:.4g} |")
+            per.setdefault(name, {})[ctr] = v
+    rows = [(k, d) for k, d in per.items() if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d]
+    if rows:
+        # GRBM_GUI_ACTIVE comes summed over the 8 XCDs (about 8 x the kernel's shader clocks)
+        print()
+        print(f"| kernel | MFMA busy (of {simds} SIMDs x active cycles) | bf16 MFMA GFLOP per dispatch |")
+        print("|---|---:|---:|")
+        for k, d in sorted(rows, key=lambda r: -r[1]["SQ_VALU_MFMA_BUSY_CYCLES"]):
+            busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / 8 * simds)
+            fl = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+            print(f"| `{_short(k)}` | {busy:.3f} | {fl * 512 / 1e9:.1f} |" if fl is not None else
+                  f"| `{_short(k)}` | {busy:.3f} | - |")
 
 
 # ---------------------------------------------------------------- workloads ----
@@ -661,6 +681,7 @@ def layer_summary(wl, steps, warmup):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -671,11 +692,16 @@ def main():
     ap.add_argument("--only-head", action="store_true",
                     help="only the head workload's headline variant (and mem unless --no-mem)")
     ap.add_argument("--no-wt", action="store_true", help="fast variant without the W'^T copy")
+    ap.add_argument("--steps-only", action="store_true",
+                    help="profiling runs: only the layer steps (no cold-cache pass, peaks, merge, fold, Adam)")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="untimed steps before the warm-up (seconds; 0 for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", nargs="+", metavar="DB [BENCH_JSON]")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DB")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB")
     args = ap.parse_args()
+    SETTLE_S = args.settle_s
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace[:2])
         return
@@ -714,7 +740,7 @@ def main():
         # backward's product then reads W' k-contiguous) and the gathered input X~
         keep_wt = variant == "fast" and wl.w == "bf16" and not args.no_wt
         v, ph, c = run_variant(wl, inputs, variant, args.steps, args.warmup, keep_wt=keep_wt,
-                               cold_steps=5 if variant == head else 0)
+                               cold_steps=5 if variant == head and not args.steps_only else 0)
         variants[variant], phases[variant] = v, ph
         if variant == head:
             cold = c
@@ -729,6 +755,13 @@ def main():
 
     ms = variants[head]["ms_per_step"]
     dom = phases[head].get(DOMINANT + " (timed steps)")
+    if args.steps_only:
+        print(json.dumps({"metric": METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                          "step_ms": variants[head]["step_ms"], "variants": variants, "phases": phases,
+                          "config": {"workload": wl.name, "variant": head},
+                          "roofline": {"kernel": DOMINANT, "avg_launch_ms": dom["avg_ms"] if dom else None}}))
+        return
     peaks = measured_peaks(wl)
     roof = None
     if dom:

@@ -36,11 +36,21 @@ __device__ inline void wait_vmcnt() {
 }
 
 // k-contiguous tile [R][BKT] bf16 (BKT = 32, 64 or more -> 64-, 128-, ...-byte rows).  The
-// 16-byte chunk c of row r sits at c ^ kc_key(r), which spreads the rows one
-// 8-lane ds_read_b128 phase touches over all 128 bytes of a bank sweep.  One wave
-// instruction (64 lanes x 16 B) fills 1 KB = 64 / (BKT/8) rows.
+// 16-byte chunk c of row r sits at c ^ kc_key(r).  The LDS serves a ds_read_b128 sixteen
+// lanes at a time from 64 four-byte banks (256 bytes); a fragment read puts 16 consecutive
+// rows in those lanes, one chunk each, so the key spreads them over all sixteen 16-byte
+// bank groups: rows of 128 bytes share a 256-byte window in pairs and are keyed by their
+// row index halved, rows of 64 bytes in fours (index quartered), rows of 256 bytes and
+// more one to a window (keyed by the row index itself).  Measured with fragment-shaped
+// reads: keyed for 32 banks instead (r & 7), 16-row reads lost 5% and 32-row reads 28%
+// of the LDS rate.  One wave instruction (64 lanes x 16 B) fills 1 KB = 64 / (BKT/8) rows.
+#ifndef POETX_KC_KEY32
+template <int BKT>
+__device__ inline int kc_key(int r) { return BKT >= 128 ? (r & 15) : BKT == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+#else
 template <int BKT>
 __device__ inline int kc_key(int r) { return BKT >= 64 ? (r & 7) : ((r >> 1) & 3); }
+#endif
 
 template <int R, int NW, int BKT, int WOFF = 0>
 struct LoaderKC {
