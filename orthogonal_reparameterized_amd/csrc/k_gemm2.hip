@@ -16,6 +16,13 @@
 
 #include "lds_tiles.h"
 
+// Two-stage NT loop that frees a stage with a second barrier once it has been read and
+// issues the loads two k steps ahead there (off: 236 against 218 us per W' product at
+// workload 3 on one box).
+#ifndef POETX_NT_EARLY
+#define POETX_NT_EARLY 0
+#endif
+
 namespace poetx {
 
 // kernel argument block (external linkage: kernel templates are instantiated with it)
@@ -150,15 +157,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   };
 
   const int nk = (int)((kend - kbeg + BKT - 1) / BKT);
+  // EARLY (two stages): a step reads all its fragments first, so its stage is free once every
+  // wave has read it: a second barrier there lets the loads two steps ahead go out a step
+  // sooner than the load of the next stage at the top of the step would
+  constexpr bool EARLY = POETX_NT_EARLY && !BI8 && NST == 2 && ROLE == MFMA_GEMM_NT;
+  if constexpr (EARLY) {
+    if (nk > 0) issue(0, kbeg);
+    if (nk > 1) issue(1, kbeg + BKT);
+  } else {
 #pragma unroll
-  for (int s = 0; s < PF; ++s)
-    if (s < nk) issue(s, kbeg + (int64_t)s * BKT);
+    for (int s = 0; s < PF; ++s)
+      if (s < nk) issue(s, kbeg + (int64_t)s * BKT);
+  }
   for (int t = 0; t < nk; ++t) {
-    // stage t has landed for this wave once at most (PF-1) newer stages are outstanding
-    if (t + PF <= nk) wait_vmcnt<(PF - 1) * LPS>();
-    else __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // everyone's stage t is in LDS; stage t-1 is no longer read
-    if (t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
+    if constexpr (EARLY) {
+      // stage t landed; stage t+1 (issued a step ago) may still be in flight
+      if (t + 1 < nk) wait_vmcnt<LPS>();
+      else __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    } else {
+      // stage t has landed for this wave once at most (PF-1) newer stages are outstanding
+      if (t + PF <= nk) wait_vmcnt<(PF - 1) * LPS>();
+      else __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // everyone's stage t is in LDS; stage t-1 is no longer read
+      if (t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
+    }
     const int cur = t % NST;
     const bf16_t *ta = smem + cur * A_ELEMS, *tb = smem + NST * A_ELEMS + cur * B_ELEMS;
     if constexpr (BI8) {
@@ -204,6 +227,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
         fb[h][j] = BKM ? frag_km<BN>(tb, wn + 16 * j, 32 * h) : frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (EARLY) {
+      __syncthreads();  // every wave's reads of stage t have returned: its buffer takes stage t+2
+      if (t + 2 < nk) issue(cur, kbeg + (int64_t)(t + 2) * BKT);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int h = 0; h < KH; ++h)
 #pragma unroll
@@ -384,20 +412,26 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
 }
 
 
-// Four-wave form of the W' product B = A . W'^T (both operands k-contiguous, bf16), one
-// wave per SIMD: 256 x 256 tiles, 2 x 2 waves of 128 x 128, v_mfma_f32_32x32x16_bf16
-// (a lone wave keeps that shape's pipe fuller than the 16 x 16 x 32 shape's) with the
-// 256 accumulators of a wave in AGPRs.  Per 64-deep k step a wave reads 32 fragments
-// (16 KB of A, 16 KB of B) for 64 MFMAs: two thirds of the LDS reads per flop of the
-// eight-wave 128 x 64 wave tiles.  The step's barrier sits after the reads of its last
-// 16-deep substep have returned and before that substep's MFMAs: those MFMAs then cover
-// both the barrier and the LDS latency of the next step's first fragments, and the
-// stage they came from is free for the loads two steps ahead.
-template <bool OUTF32>
-__global__ __launch_bounds__(256, 1) void k_gemm4(G2Args a) {
-  constexpr int BM = 256, BN = 256, BKT = 64, NST = 2, NSUB = BKT / 16;
+// The W' product B = A . W'^T (both operands k-contiguous, bf16) on v_mfma_f32_32x32x16_bf16,
+// 256 x 256 tiles over WGM x WGN waves (2 x 2: one wave per SIMD, 128 x 128 each, the
+// accumulators in AGPRs).  A 128 x 128 wave patch reads (128 + 128) x 16 x 2 bytes of LDS
+// per 16 MFMAs: a third less LDS traffic per flop than eight 128 x 64 patches, which keeps
+// the LDS below the MFMA rate.  With one wave per SIMD nothing else hides a wave's global
+// loads, so the k range goes through NST stages of BKT (32: four or five 32 KB stages), the
+// loads of a stage issued NST - 1 stages before its first read.
+// The schedule is fixed by hand (a scheduling fence after every group): each 16-deep
+// substep's MFMAs are dealt out one by one, and after each comes one fragment read of the
+// next substep (in the order its MFMAs consume them) and, in a stage's last substep, one of
+// the loads NST stages ahead.  The stage's barrier sits after the reads of its last substep
+// have returned and before that substep's MFMAs: they then cover both the barrier and the
+// LDS latency of the next stage's first fragments, and the stage just read is free for the
+// loads.
+template <int WGM, int WGN, int BKT, int NST>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm4(G2Args a) {
+  constexpr int BM = 256, BN = 256, NSUB = BKT / 16, NW = WGM * WGN;
+  static_assert(NSUB % 2 == 0 && NST >= 2, "fragment buffers alternate by substep");
   constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT;
-  constexpr int FM = 4, FN = 4;  // 32 x 32 tiles per wave
+  constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;  // 32 x 32 tiles per wave
   extern __shared__ __align__(16) bf16_t smem[];
 
   const TileSel sel = select_tile(a, 0);
@@ -410,7 +444,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm4(G2Args a) {
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (wave / WGN) * WTM, wn = (wave % WGN) * WTN;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -420,8 +454,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm4(G2Args a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  using LA = LoaderKC<BM, 4, BKT>;
-  using LB = LoaderKC<BN, 4, BKT>;
+  using LA = LoaderKC<BM, NW, BKT>;
+  using LB = LoaderKC<BN, NW, BKT>;
   constexpr int LPS = LA::INSTR + LB::INSTR;
   LA la;
   LB lb;
@@ -445,45 +479,59 @@ __global__ __launch_bounds__(256, 1) void k_gemm4(G2Args a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[q][j] = frag(tb, wn + 32 * j, 16 * s);
   };
-  auto mma = [&](int q) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        // operands swapped: lane l holds C[m = l % 32][n = 8 (e / 4) + 4 (l / 32) + e % 4]
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q][j], fa[q][i], acc[i][j], 0, 0, 0);
+  // the g-th fragment read of a substep, in the order the MFMAs (row tile i major) use
+  // them: A0, B0 .. B(FN-1), A1 .. A(FM-1)
+  auto read1 = [&](int q, int buf, int s, int g) {
+    const bf16_t *ta = smem + buf * A_ELEMS, *tb = smem + NST * A_ELEMS + buf * B_ELEMS;
+    if (g == 0) fa[q][0] = frag(ta, wm, 16 * s);
+    else if (g <= FN) fb[q][g - 1] = frag(tb, wn + 32 * (g - 1), 16 * s);
+    else fa[q][g - FN] = frag(ta, wm + 32 * (g - FN), 16 * s);
   };
+  auto mma1 = [&](int q, int i, int j) {
+    // operands swapped: lane l holds C[m = l % 32][n = 8 (e / 4) + 4 (l / 32) + e % 4]
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q][j], fa[q][i], acc[i][j], 0, 0, 0);
+  };
+  constexpr int NM = FM * FN, NR = FM + FN, NL = LA::INSTR;  // LB::INSTR == LA::INSTR
+  static_assert(NR <= NM && NL <= NM && LB::INSTR == NL, "one read and one load pair per MFMA at most");
 
   const int nk = (int)((kend - kbeg + BKT - 1) / BKT);
-  if (nk > 0) issue(0, kbeg);
-  if (nk > 1) issue(1, kbeg + BKT);
-  if (nk > 1) wait_vmcnt<LPS>();
-  else __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // stage 0 in LDS for every wave
+  // every buffer takes a stage up front; stage t+NST goes into stage t's buffer once it is read
+#pragma unroll
+  for (int t = 0; t < NST; ++t)
+    if (t < nk) issue(t, kbeg + (int64_t)t * BKT);
+  // stage 0 in LDS for every wave: the stages after it (at most NST - 1) may still be in flight
+  wait_tiles<LPS, NST - 1>(nk - 1);
+  __syncthreads();
   if (nk > 0) read(0, 0, 0);
+  int cur = 0;  // t % NST
   for (int t = 0; t < nk; ++t) {
-    const int cur = t & 1;
+    const int nxt = cur + 1 == NST ? 0 : cur + 1;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const int q = s & 1;
-      if (s + 1 < NSUB) {
-        read(q ^ 1, cur, s + 1);
-        mma(q);
-      } else {
-        // the last substep's fragments are in registers: stage t is no longer read by
-        // this wave, and stage t+1 has landed for it
-        if (t + 1 < nk) {
-          if (t + 2 < nk) wait_vmcnt<0>();
-          else __builtin_amdgcn_s_waitcnt(0);
-        }
+      const bool last = s + 1 == NSUB;
+      if (last && t + 1 < nk) {
+        // the last substep's fragments are in registers: stage t is no longer read by this
+        // wave, and stage t+1 has landed for it once the stages issued after it (up to
+        // t+NST-1, those that exist) are all that is in flight
+        wait_tiles<LPS, NST - 2>(nk - 2 - t);
         __syncthreads();
-        if (t + 2 < nk) issue(cur, kbeg + (int64_t)(t + 2) * BKT);
-        if (t + 1 < nk) read(q ^ 1, cur ^ 1, 0);
-        mma(q);
+      }
+      const bool rd = !last || t + 1 < nk, ld = last && t + NST < nk;
+      const int64_t kl = kbeg + (int64_t)(t + NST) * BKT;
+#pragma unroll
+      for (int g = 0; g < NM; ++g) {
+        mma1(q, g / FN, g % FN);
+        if (rd && g < NR) read1(q ^ 1, last ? nxt : cur, last ? 0 : s + 1, g);
+        if (ld && g < NL) {
+          la.issue_one(ra, kl, smem + cur * A_ELEMS, g);
+          lb.issue_one(rb, kl, smem + NST * A_ELEMS + cur * B_ELEMS, g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    cur = nxt;
   }
-
   char *Cb = (char *)a.C;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -499,14 +547,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm4(G2Args a) {
           float4 sc = *(const float4 *)(a.scaleN + n);
           v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
         }
-        if constexpr (OUTF32) {
-          *(float4 *)(Cb + (m * a.ldc + n) * 4) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-          uint2 p;
-          p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-          p.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-          *(uint2 *)(Cb + (m * a.ldc + n) * 2) = p;
-        }
+        uint2 p;
+        p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        p.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(uint2 *)(Cb + (m * a.ldc + n) * 2) = p;
       }
   }
 }
@@ -550,25 +594,37 @@ __global__ __launch_bounds__(256) void k_tail_reduce(G2Args a) {
 }
 
 // The four-wave form passes the parity tests but measured slower than the eight-wave
-// kernel at workload 3 (248-254 against 215 us per W' product on one box); it stays off.
+// kernel at workload 3: 248-254 against 215 us per W' product with two 64-deep stages,
+// 260 (four 32-deep stages) and 262 us (five) against 214 us on another box; it stays off.
 #ifndef POETX_GEMM4
 #define POETX_GEMM4 0
 #endif
 constexpr bool kUseGemm4 = POETX_GEMM4 != 0;
+#ifndef POETX_G4_WGM
+#define POETX_G4_WGM 2
+#define POETX_G4_WGN 2
+#endif
+#ifndef POETX_G4_BK
+#define POETX_G4_BK 32
+#define POETX_G4_NST 4
+#endif
+#ifndef POETX_NT_BK
+#define POETX_NT_BK 64
+#define POETX_NT_NST 2
+#endif
 
 // explicit instantiations (every configuration the dispatcher below launches)
 #define POETX_G2_INST(R, BMv, BNv, WM, WN, BKv, NS, AK, BKm)                                     \
   template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, true>(G2Args);       \
   template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, false>(G2Args);
-POETX_G2_INST(MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false)
+POETX_G2_INST(MFMA_GEMM_NT, 256, 256, 2, 4, POETX_NT_BK, POETX_NT_NST, false, false)
 POETX_G2_INST(MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true)
 POETX_G2_INST(MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false)
 POETX_G2_INST(MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true)
 POETX_G2_INST(MFMA_BLOCK_GRAD, 256, 256, 2, 4, 64, 2, true, true)
 #undef POETX_G2_INST
 template __global__ void k_gemm2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, true>(G2Args);
-template __global__ void k_gemm4<false>(G2Args);
-template __global__ void k_gemm4<true>(G2Args);
+template __global__ void k_gemm4<POETX_G4_WGM, POETX_G4_WGN, POETX_G4_BK, POETX_G4_NST>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, true>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false, true>(G2Args);
@@ -699,8 +755,10 @@ static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
 // The four-wave W' product: whole tiles only (a plan that splits leftover tiles along k
 // takes the eight-wave kernel, whose partial layout the reduce kernel reads).
 static int run4(const G2Args &k, const MfmaDesc &d, hipStream_t s, bool *done) {
+  constexpr int WGM = POETX_G4_WGM, WGN = POETX_G4_WGN, BKT = POETX_G4_BK, NST = POETX_G4_NST;
   *done = false;
-  const size_t lds = (size_t)2 * (256 + 256) * 64 * 2;
+  if (d.K % BKT || d.c_dt != POETX_BF16) return POETX_OK;
+  const size_t lds = (size_t)NST * (256 + 256) * BKT * 2;
   G2Args a = k;
   a.tiles_m = (int)cdiv(d.M, 256);
   a.tiles_n = (int)(d.N / 256);
@@ -708,14 +766,9 @@ static int run4(const G2Args &k, const MfmaDesc &d, hipStream_t s, bool *done) {
   if (a.full_tiles != a.tiles_m * a.tiles_n) return POETX_OK;
   *done = true;
   const dim3 grid((unsigned)a.full_tiles);
-  if (d.c_dt == POETX_F32) {
-    static std::atomic<uint64_t> attr{0};
-    POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm4<true>), lds, attr));
-    return launch_k(d.name, s, k_gemm4<true>, grid, 256, lds, a);
-  }
   static std::atomic<uint64_t> attr{0};
-  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm4<false>), lds, attr));
-  return launch_k(d.name, s, k_gemm4<false>, grid, 256, lds, a);
+  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_gemm4<WGM, WGN, BKT, NST>), lds, attr));
+  return launch_k(d.name, s, k_gemm4<WGM, WGN, BKT, NST>, grid, 64 * WGM * WGN, lds, a);
 }
 
 bool mfma2_supported(const MfmaDesc &d) {
@@ -761,7 +814,7 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s) {
         POETX_TRY(run4(k, d, s, &done));
         if (done) return POETX_OK;
       }
-      return run2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false>(k, d, s);
+      return run2<MFMA_GEMM_NT, 256, 256, 2, 4, POETX_NT_BK, POETX_NT_NST, false, false>(k, d, s);
     case MFMA_GEMM_NN:
       if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
       // the k-major W' operand goes through the transposing LDS reads; the ping-pong

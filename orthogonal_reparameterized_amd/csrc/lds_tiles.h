@@ -77,6 +77,12 @@ struct LoaderKC {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * INSTR + i) * RPI * BKT), 16,
                                                voff[i] + kb, 0, 0, 0);
   }
+  // the i-th of the INSTR loads alone (a wave index the compiler knows to be uniform)
+  __device__ void issue_one(__amdgpu_buffer_rsrc_t rs, int64_t k0, bf16_t *tile, int i) const {
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) - WOFF;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(tile + (w * INSTR + i) * RPI * BKT), 16,
+                                             voff[i] + (int)(k0 * 2), 0, 0, 0);
+  }
 };
 
 // k-major tile [BKT][C] bf16 = 2C-byte rows; chunk c of row r sits at c ^ (km_key(r) << 1):
