@@ -503,21 +503,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm4(G2Args a) {
   wait_tiles<LPS, NST - 1>(nk - 1);
   __syncthreads();
   if (nk > 0) read(0, 0, 0);
+  // One stage: RD (a next stage exists: read its first fragments, after the stage barrier)
+  // and LD (the stage NST ahead exists: load it) are compile-time flags, so the steady
+  // state runs without a branch between its MFMAs; the last NST stages run the other forms.
   int cur = 0;  // t % NST
-  for (int t = 0; t < nk; ++t) {
+  auto stage = [&](int t, auto rd_c, auto ld_c) {
+    constexpr bool RD = decltype(rd_c)::value, LD = decltype(ld_c)::value;
     const int nxt = cur + 1 == NST ? 0 : cur + 1;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const int q = s & 1;
       const bool last = s + 1 == NSUB;
-      if (last && t + 1 < nk) {
+      if (last && RD) {
         // the last substep's fragments are in registers: stage t is no longer read by this
         // wave, and stage t+1 has landed for it once the stages issued after it (up to
         // t+NST-1, those that exist) are all that is in flight
-        wait_tiles<LPS, NST - 2>(nk - 2 - t);
+        if (LD) wait_vmcnt<(NST - 2) * LPS>();
+        else wait_tiles<LPS, NST - 2>(nk - 2 - t);
         __syncthreads();
       }
-      const bool rd = !last || t + 1 < nk, ld = last && t + NST < nk;
+      const bool rd = !last || RD, ld = last && LD;
       const int64_t kl = kbeg + (int64_t)(t + NST) * BKT;
 #pragma unroll
       for (int g = 0; g < NM; ++g) {
@@ -531,7 +536,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm4(G2Args a) {
       }
     }
     cur = nxt;
-  }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int t = 0;
+  for (; t < nk - NST; ++t) stage(t, T_{}, T_{});
+  for (; t < nk - 1; ++t) stage(t, T_{}, F_{});
+  if (t < nk) stage(t, F_{}, F_{});
   char *Cb = (char *)a.C;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -594,8 +605,10 @@ __global__ __launch_bounds__(256) void k_tail_reduce(G2Args a) {
 }
 
 // The four-wave form passes the parity tests but measured slower than the eight-wave
-// kernel at workload 3: 248-254 against 215 us per W' product with two 64-deep stages,
-// 260 (four 32-deep stages) and 262 us (five) against 214 us on another box; it stays off.
+// kernel at workload 3, per W' product on one box each: 248-254 against 215 us (two 64-deep
+// stages, a branch around every guarded read and load); 260 (four 32-deep stages) and 262
+// (five) against 214 us; with the branch-free steady state, 238 (two 64-deep stages), 250
+// (four 32-deep) and 253 us (three) against 214 us.  It stays off.
 #ifndef POETX_GEMM4
 #define POETX_GEMM4 0
 #endif
@@ -605,8 +618,8 @@ constexpr bool kUseGemm4 = POETX_GEMM4 != 0;
 #define POETX_G4_WGN 2
 #endif
 #ifndef POETX_G4_BK
-#define POETX_G4_BK 32
-#define POETX_G4_NST 4
+#define POETX_G4_BK 64
+#define POETX_G4_NST 2
 #endif
 #ifndef POETX_NT_BK
 #define POETX_NT_BK 64
