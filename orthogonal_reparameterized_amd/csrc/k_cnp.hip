@@ -231,17 +231,26 @@ constexpr int CTK = 32, CNTH = 512;
 // RP: rows per panel (one workgroup).  32 fills the GPU from few blocks; 64 halves the
 // streaming of Q (every panel workgroup streams all of Q once per product) when there
 // are blocks enough for 4 workgroups per CU (b = 128 and 256).
-template <int B, int RP>
+// NW: waves per workgroup.  16 waves split a 128-row panel into two 64-row halves, wave w
+// and w + 8 taking the same columns: their streams of Q fragments are the same, so the
+// second read of each can hit the CU's vector L1 and the panel asks L2 for half the bytes
+// of two 64-row workgroups (same waves per SIMD, one workgroup per CU).  Measured slower
+// at 4096 blocks of 256 (forward 1.75 against 1.64 ms), so it is off (POETX_CHAIN16).
+template <int B, int RP, int NW = 8>
 struct ChainCfg {
-  static_assert(RP == 32 || (RP == 64 && B >= 128 && B <= 256), "panel height");
+  static_assert(RP == 32 || (RP == 64 && B >= 128 && B <= 256) || (RP == 128 && NW == 16 && B >= 128 && B <= 256),
+                "panel height");
+  static_assert(NW == 8 || RP == 128, "16 waves only for 128-row panels");
+  static constexpr int NTH = 64 * NW;
+  static constexpr int RW = RP / (NW / 8);            // rows of one wave's patch
   static constexpr int NK = B / CTK;                  // k steps per product
   static constexpr int NT = B / 16;                   // 16-column tiles of Q
-  static constexpr int WM = B >= 128 ? RP / 16 : 1;   // 16-row tiles per wave
+  static constexpr int WM = B >= 128 ? RW / 16 : 1;   // 16-row tiles per wave
   static constexpr int WN = B >= 128 ? B / 128 : 1;   // 16-column tiles per wave
   // k steps of B fragments in flight per wave: enough bytes in flight to cover the
   // latency of the first product, whose fragments are not in L2 yet (a 64-row panel
   // spends twice the MFMAs on each fragment)
-  static constexpr int D = B >= 512 ? 2 : RP == 64 ? 4 : (3 * NK < 8 ? 3 * NK : 8);
+  static constexpr int D = B >= 512 ? 2 : RW == 64 ? 4 : (3 * NK < 8 ? 3 * NK : 8);
   static constexpr int A_LD = B + 8;
   static constexpr int NP = B / RP;                   // panels per block
 };
@@ -259,9 +268,9 @@ __device__ inline void put_split4(bf16_t *h, bf16_t *lo, float4 v) {
 }
 }  // namespace
 
-template <int B, int MODE, int RP>
-__global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
-  using C = ChainCfg<B, RP>;
+template <int B, int MODE, int RP, int NW>
+__global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
+  using C = ChainCfg<B, RP, NW>;
   extern __shared__ __align__(16) bf16_t smem[];
   bf16_t *sAh = smem, *sAl = smem + RP * C::A_LD;
 
@@ -283,8 +292,8 @@ __global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
   const int64_t off = z * (int64_t)B * B;
   const int r0 = (int)pnl * RP;
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  const int mb = B >= 128 ? 0 : 16 * (wave >> 2);
-  const int nb = B >= 128 ? wave * (B / 8) : 16 * (wave & 3);
+  const int mb = B >= 128 ? C::RW * (wave >> 3) : 16 * (wave >> 2);
+  const int nb = B >= 128 ? (wave & 7) * (B / 8) : 16 * (wave & 3);
 
   // ---- B fragments of Q: chunk (k, t, plane) of 1 KB holds what lane l needs for
   // k step k and column tile t; this wave reads tiles nb/16 .. nb/16 + WN - 1.
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
   f32x4 run[C::WM][C::WN];  // BWDA: running 2Gb + 2K1 + ... in accumulator layout
   if constexpr (MODE == CNP_CHAIN_FWD) {
     // X = Q[rows] + 2I: rows r0.. are k steps pnl * RP/32 .. of the fragment-ordered planes
-    for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += CNTH) {
+    for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += C::NTH) {
       const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
       const u32x4 v = *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8);
       bf16_t *dst = (pl ? sAl : sAh) + (32 * ks + 8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
@@ -319,7 +328,7 @@ __global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
     if (tid < RP) sAh[tid * C::A_LD + r0 + tid] = 0x4000;  // bf16(2.0); Q has a zero diagonal
   } else if constexpr (MODE == CNP_CHAIN_BWDA) {
     const float *G = S.dg + off;
-    for (int q = tid; q < RP * B / 4; q += CNTH) {
+    for (int q = tid; q < RP * B / 4; q += C::NTH) {
       const int row = q / (B / 4), c4 = q % (B / 4);
       const float4 v = *(const float4 *)(G + (int64_t)(r0 + row) * B + c4 * 4);
       put_split4(sAh + row * C::A_LD + c4 * 4, sAl + row * C::A_LD + c4 * 4, v);
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
   } else {
     // X = Gb^T[rows]: X[m][k] = Gb[k][r0 + m]
     const float *G = S.dg + off;
-    for (int q = tid; q < B * RP / 4; q += CNTH) {
+    for (int q = tid; q < B * RP / 4; q += C::NTH) {
       const int k = q / (RP / 4), c4 = q % (RP / 4);
       const float4 v = *(const float4 *)(G + (int64_t)k * B + r0 + c4 * 4);
       const float e[4] = {v.x, v.y, v.z, v.w};
@@ -455,16 +464,18 @@ __global__ __launch_bounds__(CNTH) void k_cnp_chain(CnpChainArgs a) {
   }
 }
 
-#define POETX_CHAIN_INST(B, R)                                              \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_FWD, R>(CnpChainArgs);  \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDA, R>(CnpChainArgs); \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDB, R>(CnpChainArgs);
-POETX_CHAIN_INST(64, 32)
-POETX_CHAIN_INST(128, 32)
-POETX_CHAIN_INST(256, 32)
-POETX_CHAIN_INST(512, 32)
-POETX_CHAIN_INST(128, 64)
-POETX_CHAIN_INST(256, 64)
+#define POETX_CHAIN_INST(B, R, W)                                              \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_FWD, R, W>(CnpChainArgs);  \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDA, R, W>(CnpChainArgs); \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDB, R, W>(CnpChainArgs);
+POETX_CHAIN_INST(64, 32, 8)
+POETX_CHAIN_INST(128, 32, 8)
+POETX_CHAIN_INST(256, 32, 8)
+POETX_CHAIN_INST(512, 32, 8)
+POETX_CHAIN_INST(128, 64, 8)
+POETX_CHAIN_INST(256, 64, 8)
+POETX_CHAIN_INST(128, 128, 16)
+POETX_CHAIN_INST(256, 128, 16)
 #undef POETX_CHAIN_INST
 
 // ========================================================== fused backward ====
@@ -678,9 +689,9 @@ bool cnp_bwd_fused_supported(int64_t b, int64_t nz) {
 }
 
 namespace {
-template <int B, int RP>
+template <int B, int RP, int NW = 8>
 int chain_run(const CnpChainArgs &a, hipStream_t s) {
-  using C = ChainCfg<B, RP>;
+  using C = ChainCfg<B, RP, NW>;
   const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
   const int64_t nwg = nz * C::NP;
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
@@ -688,12 +699,12 @@ int chain_run(const CnpChainArgs &a, hipStream_t s) {
   static std::atomic<uint64_t> attr[3];  // dynamic LDS above 64 KB, per kernel and device
   auto go = [&](void (*kern)(CnpChainArgs), int mode) -> int {
     POETX_TRY(lds_limit((const void *)kern, lds, attr[mode]));
-    return launch_k(a.name, s, kern, dim3((unsigned)nwg), CNTH, lds, a);
+    return launch_k(a.name, s, kern, dim3((unsigned)nwg), C::NTH, lds, a);
   };
   switch (a.mode) {
-    case CNP_CHAIN_FWD: return go(k_cnp_chain<B, CNP_CHAIN_FWD, RP>, 0);
-    case CNP_CHAIN_BWDA: return go(k_cnp_chain<B, CNP_CHAIN_BWDA, RP>, 1);
-    case CNP_CHAIN_BWDB: return go(k_cnp_chain<B, CNP_CHAIN_BWDB, RP>, 2);
+    case CNP_CHAIN_FWD: return go(k_cnp_chain<B, CNP_CHAIN_FWD, RP, NW>, 0);
+    case CNP_CHAIN_BWDA: return go(k_cnp_chain<B, CNP_CHAIN_BWDA, RP, NW>, 1);
+    case CNP_CHAIN_BWDB: return go(k_cnp_chain<B, CNP_CHAIN_BWDB, RP, NW>, 2);
     default: return POETX_ERR_INVALID_ARG;
   }
 }
@@ -730,10 +741,15 @@ int cnp_chain(const CnpChainArgs &a, hipStream_t s) {
   // 64-row panels once they still give 4 workgroups per CU
   const int cus = device_cus() > 0 ? device_cus() : 256;
   const bool tall = nz * (a.b / 64) >= 4 * (int64_t)cus;
+#ifndef POETX_CHAIN16
+#define POETX_CHAIN16 0
+#endif
+  // 128-row panels of 16 waves once they still give 2 workgroups per CU
+  const bool tall2 = POETX_CHAIN16 && nz * (a.b / 128) >= 2 * (int64_t)cus;
   switch (a.b) {
     case 64: return chain_run<64, 32>(a, s);
-    case 128: return tall ? chain_run<128, 64>(a, s) : chain_run<128, 32>(a, s);
-    case 256: return tall ? chain_run<256, 64>(a, s) : chain_run<256, 32>(a, s);
+    case 128: return tall2 ? chain_run<128, 128, 16>(a, s) : tall ? chain_run<128, 64>(a, s) : chain_run<128, 32>(a, s);
+    case 256: return tall2 ? chain_run<256, 128, 16>(a, s) : tall ? chain_run<256, 64>(a, s) : chain_run<256, 32>(a, s);
     case 512: return chain_run<512, 32>(a, s);
     default: return POETX_ERR_UNSUPPORTED;
   }

@@ -555,6 +555,91 @@ __global__ __launch_bounds__(256) void k_unpack_frag(SkewSegs sg, int64_t b) {
   }
 }
 
+// Row-strip form of the fragment-order unpack (b % 32 == 0): workgroup (z, kk) owns the 32
+// rows 32 kk .. 32 kk + 31 of the upper triangle, whose packed parameters are one contiguous
+// run of theta.  It reads that run once, coalesced, into LDS (row pitch SP floats), then
+// writes every 1 KB fragment chunk those parameters determine: the chunks of the strip's
+// own rows right of its diagonal tile (and the diagonal tile itself), and the mirrored
+// chunks below it (rows 32 kk' > 32 kk, column tiles 2 kk and 2 kk + 1), one chunk per wave
+// at a time, both planes at once, 16 bytes per lane and plane.
+// A lane's chunk values are a column of the strip (rows 8 g .. 8 g + 7 at one column) for
+// the chunks of its own rows, and a row (8 consecutive columns) for the mirrored ones; the
+// pitch puts the four row groups g of a column read on four disjoint sets of 16 banks.
+constexpr int SP = 258;
+__global__ __launch_bounds__(512) void k_unpack_frag_strip(SkewSegs sg, int64_t b) {
+  extern __shared__ float strip[];  // [32][SP]: strip[rl][c] = theta(32 kk + rl, c), c > row
+  const int64_t NS = b / 32;
+  const int64_t L = blockIdx.x;
+  int64_t z = L / NS;
+  const int kk = (int)(L % NS);
+  int si = 0;
+  if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
+  const int64_t th0 = z * (b * (b - 1) / 2);
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  // ---- load: row rl of the strip is the run theta(r, r+1 .. b-1), r = 32 kk + rl; all of a
+  // lane's loads (b <= 256: at most 4 per row) are in flight before the first store
+  float val[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = 32 * kk + wave + 8 * i;
+    const int64_t base = th0 + triu_index(r, r + 1, b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = r + 1 + l + 64 * j;
+      val[i][j] = c < b ? ld_theta(sg, si, base + (c - r - 1)) : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = wave + 8 * i, r = 32 * kk + rl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = r + 1 + l + 64 * j;
+      if (c < b) strip[rl * SP + c] = val[i][j];
+    }
+  }
+  __syncthreads();
+  const int NT = (int)(b / 16), NK = (int)NS;
+  const int n_up = NT - 2 * kk, n_mir = 2 * (NK - kk - 1);
+  const int g = l >> 4, c16 = l & 15;
+  bf16_t *planes = sg.planes[si] + 2 * z * b * b;
+  for (int ci = wave; ci < n_up + n_mir; ci += 8) {
+    int r0, c0;
+    float v[8];
+    if (ci < n_up) {
+      // chunk (kk, t) of the strip's own rows: Q[32 kk + 8 g + e][16 t + c16]
+      const int t = 2 * kk + ci;
+      r0 = 32 * kk; c0 = 16 * t;
+      const int c = c0 + c16;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int rl = 8 * g + e, r = r0 + rl;
+        v[e] = c > r ? strip[rl * SP + c] : (c < r ? -strip[(c - r0) * SP + r] : 0.f);
+      }
+    } else {
+      // mirrored chunk (kk', t), t = 2 kk + (j & 1): Q[32 kk' + 8 g + e][16 t + c16]
+      //   = -theta(16 t + c16, 32 kk' + 8 g + e)
+      const int j = ci - n_up, kp = kk + 1 + (j >> 1), t = 2 * kk + (j & 1);
+      r0 = 32 * kp; c0 = 16 * t;
+      const float *src = strip + (c0 + c16 - 32 * kk) * SP + r0 + 8 * g;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = -src[e];
+    }
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint16_t h0, l0, h1, l1;
+      h0 = f32_to_bf16(v[2 * e2]); l0 = f32_to_bf16(v[2 * e2] - bf16_to_f32(h0));
+      h1 = f32_to_bf16(v[2 * e2 + 1]); l1 = f32_to_bf16(v[2 * e2 + 1] - bf16_to_f32(h1));
+      wh[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      wl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    bf16_t *dst = planes + cnp_frag_off(r0, c0, b) + l * 8;
+    *(uint4 *)dst = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    *(uint4 *)(dst + 512) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+  }
+}
+
 int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   const int64_t nz = sg.n[0] + sg.n[1];
   if (nz <= 0) return POETX_OK;
@@ -564,6 +649,12 @@ int unpack_skew2(const SkewSegs &sg, int64_t b, hipStream_t s) {
   const dim3 grid((unsigned)nwg);
   if (sg.planes[0]) {
     if (b % 32) return POETX_ERR_UNSUPPORTED;
+#ifndef POETX_UNPACK_TILES
+    if (b <= SP) {
+      const size_t lds = (size_t)32 * SP * sizeof(float);
+      return launch_k("unpack_skew", s, k_unpack_frag_strip, dim3((unsigned)(nz * (b / 32))), 512, lds, sg, b);
+    }
+#endif
     return launch_k("unpack_skew", s, k_unpack_frag, grid, 256, 0, sg, b);
   }
   return launch_k("unpack_skew", s, k_unpack_skew, grid, 256, 0, sg, b);
@@ -622,11 +713,93 @@ __global__ __launch_bounds__(256) void k_pack_skew_grad(SkewSegs sg, int64_t b, 
   }
 }
 
+// Row-strip form of the pack (b <= 256): workgroup (z, kk) writes the packed run of rows
+// 32 kk .. 32 kk + 31, one contiguous stretch of dtheta (and of theta, m, v with ADAM).  It
+// loads the strip's rows of M right of its diagonal (256-byte row segments) and the
+// mirrored columns below it (128-byte row segments) into LDS with every load of a lane in
+// flight at once, then writes each output row segment with consecutive lanes.
+constexpr int PK_AP = 257;  // A[32][PK_AP]: A[rl][c - r0] = M[r0 + rl][c]
+template <bool ADAM>
+__global__ __launch_bounds__(512) void k_pack_skew_strip(SkewSegs sg, int64_t b, AdamEpi ad) {
+  extern __shared__ float pk_lds[];
+  float *A = pk_lds, *Bt = pk_lds + 32 * PK_AP;  // Bt[cl][33]: Bt[cl][rl] = M[r0 + cl][r0 + rl]
+  const int64_t NS = (b + 31) / 32;
+  const int64_t L = blockIdx.x;
+  int64_t z = L / NS;
+  const int kk = (int)(L % NS);
+  int si = 0;
+  if (z >= sg.n[0]) { z -= sg.n[0]; si = 1; }
+  const float *M = (const float *)sg.src[si] + z * b * b;
+  const int64_t th0 = z * (b * (b - 1) / 2);
+  float *dth = sg.dst[si] ? sg.dst[si] + th0 : nullptr;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int r0 = 32 * kk, w = (int)b - r0;  // columns r0 .. b-1 of the strip
+  float va[4][4], vb[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + wave + 8 * i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cl = l + 64 * j;
+      va[i][j] = (r < b && cl < w) ? M[(int64_t)r * b + r0 + cl] : 0.f;
+    }
+  }
+  const int rl2 = tid & 31;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int cl = (tid >> 5) + 16 * i;
+    vb[i] = (cl < w && r0 + rl2 < b) ? M[(int64_t)(r0 + cl) * b + r0 + rl2] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) A[(wave + 8 * i) * PK_AP + l + 64 * j] = va[i][j];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) Bt[((tid >> 5) + 16 * i) * 33 + rl2] = vb[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = wave + 8 * i, r = r0 + rl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cl = l + 64 * j, c = r0 + cl;
+      if (c > r && c < b) {
+        const int64_t k = triu_index(r, c, b);
+        const float gr = A[rl * PK_AP + cl] - Bt[cl * 33 + rl];
+        if (!ADAM || dth) dth[k] = gr;
+        if constexpr (ADAM) {
+          const int64_t e = th0 + k;
+          float mm = ad.m[si][e], vv = ad.v[si][e];
+          const float th = ad.theta_bf16 ? bf16_to_f32(((const bf16_t *)ad.theta_in[si])[e])
+                                         : ((const float *)ad.theta_in[si])[e];
+          const float t = adam_update(th, gr, mm, vv, ad);
+          ad.m[si][e] = mm; ad.v[si][e] = vv;
+          if (ad.theta_bf16) ((bf16_t *)ad.theta_out[si])[e] = f32_to_bf16(t);
+          else ((float *)ad.theta_out[si])[e] = t;
+        }
+      }
+    }
+  }
+}
+
 int pack_skew_grad2(const SkewSegs &sg, int64_t b, hipStream_t s, const AdamEpi *ad) {
   const int64_t nz = sg.n[0] + sg.n[1];
   if (nz <= 0) return POETX_OK;
   const int64_t T = cdiv(b, 32), nwg = nz * (T * (T + 1) / 2);
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
+#ifndef POETX_PACK_TILES
+  if (b <= 256) {
+    const dim3 gs((unsigned)(nz * cdiv(b, 32)));
+    const size_t lds = (size_t)(32 * PK_AP + 256 * 33) * sizeof(float);
+    static std::atomic<uint64_t> attr[2];  // dynamic LDS above 64 KB, per kernel and device
+    if (ad) {
+      POETX_TRY(lds_limit((const void *)k_pack_skew_strip<true>, lds, attr[1]));
+      return launch_k("pack_skew_grad_adam", s, k_pack_skew_strip<true>, gs, 512, lds, sg, b, *ad);
+    }
+    POETX_TRY(lds_limit((const void *)k_pack_skew_strip<false>, lds, attr[0]));
+    return launch_k("pack_skew_grad", s, k_pack_skew_strip<false>, gs, 512, lds, sg, b, AdamEpi());
+  }
+#endif
   if (ad) return launch_k("pack_skew_grad_adam", s, k_pack_skew_grad<true>, dim3((unsigned)nwg), 256, 0, sg, b, *ad);
   return launch_k("pack_skew_grad", s, k_pack_skew_grad<false>, dim3((unsigned)nwg), 256, 0, sg, b, AdamEpi());
 }
