@@ -16,6 +16,11 @@
 
 #include "lds_tiles.h"
 
+// bf16 256 x 256 tiles leave through LDS (off: straight from the accumulators)
+#ifndef POETX_EPI_LDS
+#define POETX_EPI_LDS 1
+#endif
+
 // Two-stage NT loop that frees a stage with a second barrier once it has been read and
 // issues the loads two k steps ahead there (off: 236 against 218 us per W' product at
 // workload 3 on one box).
@@ -250,6 +255,43 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   }
   const int l = threadIdx.x & 63;
   char *Cb = (char *)a.C + (bidx * a.sCb + kz * a.sCsplit) * (OUTF32 ? 4 : 2);
+  if constexpr (!OUTF32 && BM == 256 && BN == 256 && POETX_EPI_LDS) {
+    // bf16 tile through LDS: an accumulator's lanes hold 16 rows x 32 bytes, which as
+    // global stores are 16 partial cache lines per instruction; staged, every store
+    // instruction writes two whole 512-byte rows.  Rows are EPI_LD bytes apart (16 over a
+    // row) so the 16 rows of one accumulator write fall on different banks.
+    constexpr int EPI_LD = BN * 2 + 16;
+    if ((((uintptr_t)Cb | (uintptr_t)(n0 * 2)) & 15) == 0 && (a.ldc & 7) == 0) {
+      char *st = (char *)smem;
+      __syncthreads();  // every wave is done with the last stage
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = wm + 16 * i + (l & 15);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = wn + 16 * j + 4 * (l >> 4);
+          f32x4 v = acc[i][j];
+          if (a.scaleN) {
+            float4 sc = *(const float4 *)(a.scaleN + bidx * a.sSNb + n0 + n);
+            v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+          }
+          uint2 p;
+          p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          p.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *(uint2 *)(st + m * EPI_LD + n * 2) = p;
+        }
+      }
+      __syncthreads();
+      constexpr int NTH = 64 * NW, RPP = NTH / 32;  // rows per pass: 32 lanes x 16 bytes a row
+      const int ch = threadIdx.x & 31;
+#pragma unroll
+      for (int r = threadIdx.x >> 5; r < BM; r += RPP) {
+        const int64_t m = m0 + r;
+        if (m < a.M) *(uint4 *)(Cb + (m * a.ldc + n0 + ch * 8) * 2) = *(const uint4 *)(st + r * EPI_LD + ch * 16);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int64_t m = m0 + wm + 16 * i + (l & 15);
@@ -290,7 +332,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
 template <int ROLE, bool AKM, bool BKM, bool OUTF32, bool BI8 = false>
 __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
   static_assert(!BI8 || (!AKM && BKM), "int8 B: k-major B, k-contiguous A");
-  constexpr int BM = 256, BN = 256, BKT = 64, WGN = 4;
+  constexpr int BM = 256, BN = 256, BKT = 64, WGN = 4, NW = 8;
   constexpr int WTM = 128, WTN = 64, FM = WTM / 16, FN = WTN / 16;
   constexpr int EB = BI8 ? 1 : 2;
   constexpr int A_ELEMS = BM * BKT, B_ELEMS = BN * BKT * EB / 2;
@@ -387,6 +429,43 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
   }
   const int l = threadIdx.x & 63;
   char *Cb = (char *)a.C + (bidx * a.sCb + kz * a.sCsplit) * (OUTF32 ? 4 : 2);
+  if constexpr (!OUTF32 && BM == 256 && BN == 256 && POETX_EPI_LDS) {
+    // bf16 tile through LDS: an accumulator's lanes hold 16 rows x 32 bytes, which as
+    // global stores are 16 partial cache lines per instruction; staged, every store
+    // instruction writes two whole 512-byte rows.  Rows are EPI_LD bytes apart (16 over a
+    // row) so the 16 rows of one accumulator write fall on different banks.
+    constexpr int EPI_LD = BN * 2 + 16;
+    if ((((uintptr_t)Cb | (uintptr_t)(n0 * 2)) & 15) == 0 && (a.ldc & 7) == 0) {
+      char *st = (char *)smem;
+      __syncthreads();  // every wave is done with the last stage
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = wm + 16 * i + (l & 15);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = wn + 16 * j + 4 * (l >> 4);
+          f32x4 v = acc[i][j];
+          if (a.scaleN) {
+            float4 sc = *(const float4 *)(a.scaleN + bidx * a.sSNb + n0 + n);
+            v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+          }
+          uint2 p;
+          p.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          p.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *(uint2 *)(st + m * EPI_LD + n * 2) = p;
+        }
+      }
+      __syncthreads();
+      constexpr int NTH = 64 * NW, RPP = NTH / 32;  // rows per pass: 32 lanes x 16 bytes a row
+      const int ch = threadIdx.x & 31;
+#pragma unroll
+      for (int r = threadIdx.x >> 5; r < BM; r += RPP) {
+        const int64_t m = m0 + r;
+        if (m < a.M) *(uint4 *)(Cb + (m * a.ldc + n0 + ch * 8) * 2) = *(const uint4 *)(st + r * EPI_LD + ch * 16);
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int64_t m = m0 + wm + 16 * i + (l & 15);
@@ -625,12 +704,20 @@ constexpr bool kUseGemm4 = POETX_GEMM4 != 0;
 #define POETX_NT_BK 64
 #define POETX_NT_NST 2
 #endif
+// batched NT products (the b = 512 block products: K = 512, eight 64-deep steps per tile)
+#ifndef POETX_BNT_BK
+#define POETX_BNT_BK 64
+#define POETX_BNT_NST 2
+#endif
 
 // explicit instantiations (every configuration the dispatcher below launches)
 #define POETX_G2_INST(R, BMv, BNv, WM, WN, BKv, NS, AK, BKm)                                     \
   template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, true>(G2Args);       \
   template __global__ void k_gemm2<R, BMv, BNv, WM, WN, BKv, NS, AK, BKm, false>(G2Args);
 POETX_G2_INST(MFMA_GEMM_NT, 256, 256, 2, 4, POETX_NT_BK, POETX_NT_NST, false, false)
+#if POETX_BNT_BK != POETX_NT_BK || POETX_BNT_NST != POETX_NT_NST
+POETX_G2_INST(MFMA_GEMM_NT, 256, 256, 2, 4, POETX_BNT_BK, POETX_BNT_NST, false, false)
+#endif
 POETX_G2_INST(MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true)
 POETX_G2_INST(MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false)
 POETX_G2_INST(MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true)
@@ -709,7 +796,8 @@ size_t gemm_tail_ws_bytes(int64_t M, int64_t N, int64_t K) {
 
 template <int ROLE, bool AKM, bool BKM, bool BI8 = false>
 static int run_pp(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
-  const size_t lds = (size_t)2 * 64 * (256 * 2 + 256 * (BI8 ? 1 : 2));
+  size_t lds = (size_t)2 * 64 * (256 * 2 + 256 * (BI8 ? 1 : 2));
+  if (POETX_EPI_LDS && lds < (size_t)256 * (256 * 2 + 16)) lds = (size_t)256 * (256 * 2 + 16);  // staged epilogue
   if (d.M <= 0 || d.N % 256 || d.K % 64) return POETX_ERR_UNSUPPORTED;
   G2Args a = k;
   a.tiles_m = (int)cdiv(d.M, 256);
@@ -747,7 +835,9 @@ static int run2o(const G2Args &a, const char *name, dim3 grid, size_t lds, hipSt
 
 template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool BI8 = false>
 static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
-  const size_t lds = (size_t)NST * (BM * 2 + BN * (BI8 ? 1 : 2)) * BKT;
+  size_t lds = (size_t)NST * (BM * 2 + BN * (BI8 ? 1 : 2)) * BKT;
+  if (BM == 256 && BN == 256 && POETX_EPI_LDS && lds < (size_t)BM * (BN * 2 + 16))
+    lds = (size_t)BM * (BN * 2 + 16);  // the staged bf16 epilogue tile
   if (d.M <= 0 || d.N % BN || d.K % BKT && (!AKM || !BKM)) return POETX_ERR_UNSUPPORTED;
   G2Args a = k;
   a.tiles_m = (int)cdiv(d.M, BM);
@@ -827,6 +917,7 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s) {
         POETX_TRY(run4(k, d, s, &done));
         if (done) return POETX_OK;
       }
+      if (d.batch > 1) return run2<MFMA_GEMM_NT, 256, 256, 2, 4, POETX_BNT_BK, POETX_BNT_NST, false, false>(k, d, s);
       return run2<MFMA_GEMM_NT, 256, 256, 2, 4, POETX_NT_BK, POETX_NT_NST, false, false>(k, d, s);
     case MFMA_GEMM_NN:
       if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
