@@ -677,7 +677,13 @@ template __global__ void k_cnp_bwd_fused<64, 32>(CnpChainArgs);
 template __global__ void k_cnp_bwd_fused<128, 64>(CnpChainArgs);
 template __global__ void k_cnp_bwd_fused<256, 64>(CnpChainArgs);
 
-bool cnp_chain_supported(int64_t b) { return b == 64 || b == 128 || b == 256 || b == 512; }
+// b = 512 on the row-panel chains; off, it takes the per-product launches (k_cnp_mm, two
+// forward, six backward): measured slower at workload 4 (115 against 104 us forward, 345
+// against 277 us backward)
+#ifndef POETX_CHAIN512
+#define POETX_CHAIN512 1
+#endif
+bool cnp_chain_supported(int64_t b) { return b == 64 || b == 128 || b == 256 || (POETX_CHAIN512 && b == 512); }
 // The fused backward takes over once the blocks give 4 workgroups of 64-row panels per CU
 // (32-row at b = 64): below that its three phases in one workgroup are a longer chain of
 // dependent products than the two launches' three each (measured: 45 against 41 us at
