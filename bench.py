@@ -500,6 +500,19 @@ def summarize_trace(db, bench_json=None):
     print("|---|---:|---:|---:|---:|---:|")
     for name, n, avg, mn, mx, sm in rows:
         print(f"| `{_short(name)}` | {n} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | {100 * sm / tot:.1f}% |")
+    # a symbol that runs several shapes (the 256 x 256 kernel: W' products, batched block
+    # products at b = 512) gets its launches split by grid (workgroups x batch)
+    shapes = con.execute("select name, grid_x / workgroup_x, grid_z, count(*), avg(duration), min(duration), "
+                         "max(duration) from kernels group by name, grid_x / workgroup_x, grid_z "
+                         "order by name, grid_z, grid_x / workgroup_x").fetchall()
+    multi = {r[0] for r in shapes if sum(1 for q in shapes if q[0] == r[0]) > 1}
+    if multi:
+        print()
+        print("| kernel | workgroups x batch | launches | avg us | min us | max us |")
+        print("|---|---|---:|---:|---:|---:|")
+        for name, gx, gz, n, avg, mn, mx in shapes:
+            if name in multi:
+                print(f"| `{_short(name)}` | {gx} x {gz} | {n} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} |")
     if not bench_json:
         return
     line = [ln for ln in open(bench_json) if ln.startswith("{")][-1]
@@ -513,7 +526,8 @@ def summarize_trace(db, bench_json=None):
     roof = d["roofline"]
     names = [r[0].replace(" ", "") for r in rows]
     sym = next(sm for sm in KERNEL_SYMBOL_CANDIDATES[roof["kernel"]] if any(sm in nm for nm in names))
-    durs = [r[1] for r in con.execute("select name, duration from kernels order by start")
+    # unbatched launches only (batched ones of the same symbol are block products)
+    durs = [r[1] for r in con.execute("select name, duration from kernels where grid_z = 1 order by start")
             if sym in r[0].replace(" ", "")]
     # the traced run (--only-head, one variant): settle steps, W warm-up steps, K timed steps
     # (this kernel recorded), 1 + K unrecorded, 1 + K all recorded, then 5 cold-cache steps;
