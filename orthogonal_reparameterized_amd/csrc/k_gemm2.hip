@@ -16,6 +16,12 @@
 
 #include "lds_tiles.h"
 
+// fragment read distance (substeps) of the four-wave W' kernel: 1, 2 and 3 measured alike
+// (237-238 us per W' product at workload 3), so LDS latency is not what holds it back
+#ifndef POETX_G4_RD
+#define POETX_G4_RD 1
+#endif
+
 // bf16 256 x 256 tiles leave through LDS (off: straight from the accumulators)
 #ifndef POETX_EPI_LDS
 #define POETX_EPI_LDS 1
@@ -550,7 +556,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm4(G2Args a) {
     const int pchunk = ((ks >> 3) + (l >> 5)) ^ kc_key<BKT>(row);
     return __builtin_bit_cast(bf16x8, *(const s16x8 *)(t + row * BKT + pchunk * 8));
   };
-  bf16x8 fa[2][FM], fb[2][FN];
+  // fragments are read RDI substeps ahead of their MFMAs, into NSL register slots
+  constexpr int RDI = POETX_G4_RD, NSL = RDI == 1 ? 2 : NSUB;
+  static_assert(RDI >= 1 && RDI < NSUB, "read distance within a stage");
+  bf16x8 fa[NSL][FM], fb[NSL][FN];
   auto read = [&](int q, int buf, int s) {
     const bf16_t *ta = smem + buf * A_ELEMS, *tb = smem + NST * A_ELEMS + buf * B_ELEMS;
 #pragma unroll
@@ -581,7 +590,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm4(G2Args a) {
   // stage 0 in LDS for every wave: the stages after it (at most NST - 1) may still be in flight
   wait_tiles<LPS, NST - 1>(nk - 1);
   __syncthreads();
-  if (nk > 0) read(0, 0, 0);
+  if (nk > 0) {
+#pragma unroll
+    for (int r = 0; r < RDI; ++r) read(r % NSL, 0, r);
+  }
   // One stage: RD (a next stage exists: read its first fragments, after the stage barrier)
   // and LD (the stage NST ahead exists: load it) are compile-time flags, so the steady
   // state runs without a branch between its MFMAs; the last NST stages run the other forms.
@@ -591,22 +603,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm4(G2Args a) {
     const int nxt = cur + 1 == NST ? 0 : cur + 1;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      const int q = s & 1;
-      const bool last = s + 1 == NSUB;
-      if (last && RD) {
-        // the last substep's fragments are in registers: stage t is no longer read by this
-        // wave, and stage t+1 has landed for it once the stages issued after it (up to
-        // t+NST-1, those that exist) are all that is in flight
+      const int q = s % NSL, rs = s + RDI;  // rs: the substep whose fragments are read now
+      const bool nx = rs >= NSUB;           // ... from stage t+1
+      if (rs == NSUB && RD) {
+        // every fragment of stage t is in registers or on its way (the barrier waits for
+        // them): stage t is no longer read by this wave, and stage t+1 has landed for it once
+        // the stages issued after it (up to t+NST-1, those that exist) are all in flight
         if (LD) wait_vmcnt<(NST - 2) * LPS>();
         else wait_tiles<LPS, NST - 2>(nk - 2 - t);
         __syncthreads();
       }
-      const bool rd = !last || RD, ld = last && LD;
+      const bool rd = !nx || RD, ld = rs == NSUB && LD;
       const int64_t kl = kbeg + (int64_t)(t + NST) * BKT;
 #pragma unroll
       for (int g = 0; g < NM; ++g) {
         mma1(q, g / FN, g % FN);
-        if (rd && g < NR) read1(q ^ 1, last ? nxt : cur, last ? 0 : s + 1, g);
+        if (rd && g < NR) read1(rs % NSL, nx ? nxt : cur, rs % NSUB, g);
         if (ld && g < NL) {
           la.issue_one(ra, kl, smem + cur * A_ELEMS, g);
           lb.issue_one(rb, kl, smem + NST * A_ELEMS + cur * B_ELEMS, g);
