@@ -640,9 +640,10 @@ def cnp_bench(wl, steps, warmup):
     del theta, dg
     g = torch.empty((wl.nblocks, wl.b, wl.b), dtype=torch.bfloat16, device="cuda")
     dth = torch.empty_like(th)
+    q = B.qsave_like(th, wl.b)  # the forward keeps Q's planes; the backward reads them
     res, per = {}, {}
-    for name, fn in (("fwd", lambda: B.poetx_cnp(B.POETX_CNP_FWD, th, wl.b, g=g)),
-                     ("bwd", lambda: B.poetx_cnp(B.POETX_CNP_BWD, th, wl.b, dg=dgt, dtheta=dth))):
+    for name, fn in (("fwd", lambda: B.poetx_cnp(B.POETX_CNP_FWD, th, wl.b, g=g, qsave=q)),
+                     ("bwd", lambda: B.poetx_cnp(B.POETX_CNP_BWD, th, wl.b, dg=dgt, dtheta=dth, qsave=q))):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < SETTLE_S:
             fn()
@@ -665,10 +666,11 @@ def cnp_bench(wl, steps, warmup):
     p = b * (b - 1) // 2
     y_fwd, y_bwd = n * (4 * p + 2 * b * b), n * (4 * b * b + 8 * p)
     ms = res["fwd"] + res["bwd"]
-    del th, dgt, g, dth
+    del th, dgt, g, dth, q
     torch.cuda.empty_cache()
     return {
         "metric": "CNP fwd+bwd blocks/s (4096 x b=256)", "value": n / (ms * 1e-3), "unit": "blocks/s",
+        "saved_q": True,
         "ms_per_step": ms, "fwd_ms": res["fwd"], "bwd_ms": res["bwd"],
         "fwd_ms_median": statistics.median(per["fwd"]), "bwd_ms_median": statistics.median(per["bwd"]),
         "config": {"workload": wl.name, "nblocks": n, "b": b},

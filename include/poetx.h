@@ -101,6 +101,13 @@ typedef struct {
   int32_t theta_dtype;         /* F32 (0, the default) or BF16: storage of theta; the
                                   CNP widens it exactly and computes in float32, and
                                   dtheta stays float32                               */
+  const void *q_r;             /* optional: the qsave buffer that poetx_cnp(FWD) filled
+                                  for the n_R full blocks of G_R from this theta_r, or
+                                  NULL; the backward's CNP then reads Q from it instead
+                                  of unpacking theta_r again (b in {64, 128, 256,
+                                  512}; ignored otherwise; results are the same).  16-byte
+                                  aligned, n_R * b * b * 4 bytes.                   */
+  const void *q_p;             /* the same for the n_P full blocks of G_P           */
 } poetx_layer;
 
 /* Size of the static device workspace of poetx_cnp_noalloc, per GPU (64 MiB). */
@@ -140,19 +147,25 @@ int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64
  * size (a last block sits at an offset of whole blocks); g and dg that are not
  * 16-byte aligned take the float32 vector-ALU path.  b == 1: G = [1] per block,
  * no parameters (theta and dtheta may be NULL).
- * The pages load Q and Q^2 in their fused kernel; this library recomputes every power of Q
- * from theta inside its kernels (no saved Q^2 argument; the results are the same).
+ * qsave (nullable; used for b in {64, 128, 256, 512}, ignored otherwise): the saved
+ * operand of the pages' fused kernel, which loads Q and Q^2 on chip.  Here it holds Q
+ * itself, as the split-bf16 planes
+ * in MFMA fragment order that the CNP kernels read (an internal layout, n * b * b * 4
+ * bytes, 16-byte aligned); every higher power is recomputed inside the kernels.  FWD
+ * writes it; BWD with qsave reads Q from it instead of unpacking theta again, and theta
+ * must then be the theta of the FWD call that wrote it.  Results are the same with or
+ * without it.
  * Errors: b < 1 or b > 1024 -> POETX_ERR_SHAPE; NULL theta (b > 1) / output, theta_dtype
- * other than F32 or BF16 -> INVALID_ARG.
+ * other than F32 or BF16, qsave not 16-byte aligned -> INVALID_ARG.
  */
 int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const void *theta, int32_t theta_dtype,
-              void *g, int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta, void *ws,
-              size_t *ws_bytes, void *stream);
+              void *g, int32_t g_dtype, void *qsave, const void *dg, int32_t dg_dtype, float *dtheta,
+              void *ws, size_t *ws_bytes, void *stream);
 
 /*
  * poetx_cnp_noalloc -- for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): poetx_cnp, same arguments
- * and results, with its workspace in a static device array of POETX_NOALLOC_SCRATCH_BYTES
+ * (no qsave: Q is unpacked from theta in both directions) and results, with its workspace in a static device array of POETX_NOALLOC_SCRATCH_BYTES
  * per GPU, set up on the first call on each device and held until the process ends.  It
  * calls no hipMalloc / hipFree.  Every call on a GPU uses that GPU's one array: calls
  * that overlap on one GPU (two streams, or two threads) race and must not be made; calls

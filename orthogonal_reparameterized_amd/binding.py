@@ -41,6 +41,7 @@ class PoetxLayerC(ctypes.Structure):
         ("act_dtype", _i32), ("w_dtype", _i32), ("g_dtype", _i32), ("variant", _i32),
         ("w_merged", _vp), ("w_merged_t", _vp), ("w_scale", _vp), ("perm_in", _vp), ("perm_out", _vp),
         ("theta_r", _vp), ("theta_p", _vp), ("g_r", _vp), ("g_p", _vp), ("theta_dtype", _i32),
+        ("q_r", _vp), ("q_p", _vp),
     ]
 
 
@@ -53,7 +54,7 @@ class PoetxAdamC(ctypes.Structure):
 
 
 _lib.poetx_merge_perm.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
-_lib.poetx_cnp.argtypes = [_i32, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp,
+_lib.poetx_cnp.argtypes = [_i32, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
                            ctypes.POINTER(_sz), _vp]
 _lib.poetx_forward.argtypes = [ctypes.POINTER(PoetxLayerC), _i64, _vp, _vp, _vp, _vp, _vp,
                                ctypes.POINTER(_sz), _vp]
@@ -166,10 +167,16 @@ def poetx_merge_perm(w: torch.Tensor, perm_out=None, perm_in=None, w_scale=None,
     return out, (out_scale if w.dtype == torch.int8 else None)
 
 
+def qsave_like(theta: torch.Tensor, b: int) -> torch.Tensor:
+    """A buffer for poetx_cnp's qsave (n * b * b * 4 bytes, 16-byte aligned)."""
+    return torch.empty((theta.shape[0], b, b), dtype=torch.float32, device=theta.device)
+
+
 def poetx_cnp(direction: int, theta: torch.Tensor, b: int, *, g: Optional[torch.Tensor] = None,
               g_dtype: torch.dtype = torch.bfloat16, dg: Optional[torch.Tensor] = None,
-              dtheta: Optional[torch.Tensor] = None):
-    """FWD: returns G [n][b][b] in g_dtype; BWD: returns dtheta [n][b(b-1)/2] from dg."""
+              dtheta: Optional[torch.Tensor] = None, qsave: Optional[torch.Tensor] = None):
+    """FWD: returns G [n][b][b] in g_dtype; BWD: returns dtheta [n][b(b-1)/2] from dg.
+    qsave (optional, from qsave_like): FWD fills it, BWD on the same theta reads Q from it."""
     n = theta.shape[0]
     dev = theta.device
     if direction == POETX_CNP_FWD:
@@ -180,7 +187,7 @@ def poetx_cnp(direction: int, theta: torch.Tensor, b: int, *, g: Optional[torch.
         gdt, dgdt = POETX_F32, _dt(dg)
     tdt = _dt(theta)
     nbytes = _sz(0)
-    _check(_lib.poetx_cnp(direction, n, b, None, tdt, None, gdt, None, dgdt, None, None,
+    _check(_lib.poetx_cnp(direction, n, b, None, tdt, None, gdt, None, None, dgdt, None, None,
                           ctypes.byref(nbytes), None), "poetx_cnp(size)")
     ws = _workspace(dev, nbytes.value)
     nb = _sz(ws.numel())
@@ -188,7 +195,7 @@ def poetx_cnp(direction: int, theta: torch.Tensor, b: int, *, g: Optional[torch.
     # sits at an offset of whole blocks, which need not be a multiple of 16 bytes)
     def ep(t):
         return None if t is None else _ptr(t, t.element_size())
-    st = _lib.poetx_cnp(direction, n, b, ep(theta), tdt, ep(g), gdt, ep(dg), dgdt, ep(dtheta),
+    st = _lib.poetx_cnp(direction, n, b, ep(theta), tdt, ep(g), gdt, _ptr(qsave), ep(dg), dgdt, ep(dtheta),
                         _ptr(ws), ctypes.byref(nb), _stream(dev))
     _check(st, "poetx_cnp")
     return g if direction == POETX_CNP_FWD else dtheta
@@ -209,6 +216,8 @@ class Layer:
     perm_in: Optional[torch.Tensor] = None
     perm_out: Optional[torch.Tensor] = None
     w_merged_t: Optional[torch.Tensor] = None
+    q_r: Optional[torch.Tensor] = None    # qsave buffers the CNP forward filled (full blocks)
+    q_p: Optional[torch.Tensor] = None
 
     @property
     def d_out(self):
@@ -227,7 +236,7 @@ class Layer:
         c.variant = self.variant
         c.theta_dtype = _dt(self.theta_r)
         for name in ("w_merged", "w_merged_t", "w_scale", "perm_in", "perm_out", "theta_r", "theta_p",
-                     "g_r", "g_p"):
+                     "g_r", "g_p", "q_r", "q_p"):
             p = _ptr(getattr(self, name))
             setattr(c, name, p.value if p is not None else None)
         return c

@@ -177,18 +177,20 @@ size_t cnp_ws_bytes(int dir, int64_t n, int64_t b) {
 
 bool al16(const void *q) { return ((uintptr_t)q & 15) == 0; }
 
-int cnp_fwd_impl(int64_t n, int64_t b, const void *theta, int theta_bf16, void *g, int g_dtype, void *ws,
-                 hipStream_t s) {
+// qsave (optional, chain block sizes): receives Q's fragment-ordered planes for a later backward.
+int cnp_fwd_impl(int64_t n, int64_t b, const void *theta, int theta_bf16, void *g, int g_dtype, void *qsave,
+                 void *ws, hipStream_t s) {
   Arena ar(ws);
   size_t blk = (size_t)n * b * b * 4;
   // the chain and MFMA paths store G with 8- and 16-byte stores; a G that is only
   // element-aligned takes the vector-ALU path
   const bool vec = al16(g);
   if (vec && cnp_chain_supported(b)) {
-    // Q as bf16 planes, then the whole Horner chain in one launch
+    // Q as bf16 planes (straight into qsave when given), then the whole Horner chain in
+    // one launch
     SkewSegs un;
     un.src[0] = theta; un.n[0] = n; un.src_bf16 = theta_bf16;
-    un.planes[0] = (bf16_t *)ar.take(blk);
+    un.planes[0] = qsave ? (bf16_t *)qsave : (bf16_t *)ar.take(blk);
     POETX_TRY(unpack_skew2(un, b, s));
     CnpChainArgs c;
     c.b = (int)b;
@@ -198,6 +200,12 @@ int cnp_fwd_impl(int64_t n, int64_t b, const void *theta, int theta_bf16, void *
     if (g_dtype == POETX_F32) c.seg[0].out = (float *)g;
     else c.seg[0].outb = (bf16_t *)g;
     return cnp_chain(c, s);
+  }
+  if (qsave) {  // the planes a later backward's chains read, in their own pass here
+    SkewSegs un;
+    un.src[0] = theta; un.n[0] = n; un.src_bf16 = theta_bf16;
+    un.planes[0] = (bf16_t *)qsave;
+    POETX_TRY(unpack_skew2(un, b, s));
   }
   float *Q = (float *)ar.take(blk), *S = (float *)ar.take(blk);
   float *T = (float *)ar.take(blk), *U = (float *)ar.take(blk);
@@ -237,6 +245,7 @@ int cnp_fwd_impl(int64_t n, int64_t b, const void *theta, int theta_bf16, void *
 struct CnpBwdSide {
   int64_t n = 0;
   const void *theta = nullptr;
+  const void *qsave = nullptr;  // Q's planes from the forward (chain paths), or null: unpack theta
   const float *dg = nullptr;
   float *dtheta = nullptr;
   // fused Adam: new theta, state
@@ -269,8 +278,9 @@ int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, int theta_b
   c.name = "cnp_bwd_fused";
   for (int i = 0; i < nside; ++i) {
     const size_t blk = (size_t)side[i].n * b * b * 4;
-    un.src[i] = side[i].theta; un.n[i] = side[i].n;
-    un.planes[i] = (bf16_t *)ar.take(blk);
+    // a side with saved planes is not unpacked again (its segment is left empty)
+    un.src[i] = side[i].theta; un.n[i] = side[i].qsave ? 0 : side[i].n;
+    un.planes[i] = side[i].qsave ? (bf16_t *)side[i].qsave : (bf16_t *)ar.take(blk);
     c.seg[i].qp = un.planes[i]; c.seg[i].dg = side[i].dg; c.seg[i].nblk = side[i].n;
     c.seg[i].out = (float *)ar.take(blk);
     pk.src[i] = c.seg[i].out; pk.dst[i] = side[i].dtheta; pk.n[i] = side[i].n;
@@ -293,8 +303,8 @@ int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, 
   cb.mode = CNP_CHAIN_BWDB; cb.name = "cnp_bwd_chain_b";
   for (int i = 0; i < nside; ++i) {
     const size_t blk = (size_t)side[i].n * b * b * 4;
-    un.src[i] = side[i].theta; un.n[i] = side[i].n;
-    un.planes[i] = (bf16_t *)ar.take(blk);
+    un.src[i] = side[i].theta; un.n[i] = side[i].qsave ? 0 : side[i].n;
+    un.planes[i] = side[i].qsave ? (bf16_t *)side[i].qsave : (bf16_t *)ar.take(blk);
     CnpChainSeg g;
     g.qp = un.planes[i]; g.dg = side[i].dg; g.nblk = side[i].n;
     for (int j = 0; j < 3; ++j) g.r[j] = (float *)ar.take(blk);
@@ -387,8 +397,8 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, c
 }  // namespace
 
 extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const void *theta, int32_t theta_dtype,
-                         void *g, int32_t g_dtype, const void *dg, int32_t dg_dtype, float *dtheta,
-                         void *ws, size_t *ws_bytes, void *stream) {
+                         void *g, int32_t g_dtype, void *qsave, const void *dg, int32_t dg_dtype,
+                         float *dtheta, void *ws, size_t *ws_bytes, void *stream) {
   if (dir != POETX_CNP_FWD && dir != POETX_CNP_BWD) return POETX_ERR_INVALID_ARG;
   if (theta_dtype != POETX_F32 && theta_dtype != POETX_BF16) return POETX_ERR_INVALID_ARG;
   if (nblocks < 0 || !ws_bytes) return POETX_ERR_INVALID_ARG;
@@ -408,15 +418,17 @@ extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const void *th
   if (dir == POETX_CNP_FWD && !g) return POETX_ERR_INVALID_ARG;
   if (dir == POETX_CNP_BWD && (!dg || (!dtheta && b > 1))) return POETX_ERR_INVALID_ARG;
   if (*ws_bytes < need) return POETX_ERR_WORKSPACE;
+  if (qsave && !al16(qsave)) return POETX_ERR_INVALID_ARG;
   if (nblocks == 0) return POETX_OK;
   hipStream_t s = (hipStream_t)stream;
   if (b == 1) {  // no parameters: G = [1], nothing to differentiate
     return dir == POETX_CNP_FWD ? fill_one(g, nblocks, g_dtype, s) : POETX_OK;
   }
   const int tb = theta_dtype == POETX_BF16;
-  if (dir == POETX_CNP_FWD) return cnp_fwd_impl(nblocks, b, theta, tb, g, g_dtype, ws, s);
+  if (!cnp_chain_supported(b)) qsave = nullptr;  // only the chain paths read the planes
+  if (dir == POETX_CNP_FWD) return cnp_fwd_impl(nblocks, b, theta, tb, g, g_dtype, qsave, ws, s);
   CnpBwdSide sd;
-  sd.n = nblocks; sd.theta = theta; sd.dg = (const float *)dg; sd.dtheta = dtheta;
+  sd.n = nblocks; sd.theta = theta; sd.dg = (const float *)dg; sd.dtheta = dtheta; sd.qsave = qsave;
   return cnp_bwd_impl(b, &sd, 1, tb, nullptr, ws, s);
 }
 
@@ -940,8 +952,15 @@ int backward_impl(const poetx_layer *L, int64_t n_tokens, const void *x, const v
   };
   CnpBwdSide sides[2];
   int ns = 0;
-  if (p.nr) sides[ns++] = side_at(true, p.nr, 0, gr);
-  if (p.np) sides[ns++] = side_at(false, p.np, 0, gp);
+  const bool qok = cnp_chain_supported(b);  // saved planes (full blocks only): chain paths
+  if (p.nr) {
+    sides[ns] = side_at(true, p.nr, 0, gr);
+    sides[ns++].qsave = qok ? L->q_r : nullptr;
+  }
+  if (p.np) {
+    sides[ns] = side_at(false, p.np, 0, gp);
+    sides[ns++].qsave = qok ? L->q_p : nullptr;
+  }
   if (ns) POETX_TRY(cnp_bwd_impl(b, sides, ns, th_bf, h, cws, s));
   const CnpBwdSide lr = side_at(true, 1, p.nr * pb, gr + p.nr * bb);
   const CnpBwdSide lp = side_at(false, 1, p.np * pb, gp + p.np * bb);

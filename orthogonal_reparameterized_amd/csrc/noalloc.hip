@@ -39,11 +39,11 @@ extern "C" int poetx_cnp_noalloc(int32_t dir, int64_t nblocks, int64_t b, const 
   using namespace poetx;
   // the requirement first (validates the arguments the query looks at; launches nothing)
   size_t need = 0;
-  POETX_TRY(poetx_cnp(dir, nblocks, b, nullptr, theta_dtype, nullptr, g_dtype, nullptr, dg_dtype, nullptr, nullptr,
-                      &need, nullptr));
+  POETX_TRY(poetx_cnp(dir, nblocks, b, nullptr, theta_dtype, nullptr, g_dtype, nullptr, nullptr, dg_dtype, nullptr,
+                      nullptr, &need, nullptr));
   if (need > (size_t)POETX_NOALLOC_SCRATCH_BYTES) return POETX_ERR_WORKSPACE;
   void *ws = nullptr;
   POETX_TRY(scratch_ptr(&ws));
   size_t avail = (size_t)POETX_NOALLOC_SCRATCH_BYTES;
-  return poetx_cnp(dir, nblocks, b, theta, theta_dtype, g, g_dtype, dg, dg_dtype, dtheta, ws, &avail, stream);
+  return poetx_cnp(dir, nblocks, b, theta, theta_dtype, g, g_dtype, nullptr, dg, dg_dtype, dtheta, ws, &avail, stream);
 }

@@ -27,9 +27,11 @@ def upload(arr, dtype: str, device="cuda"):
 
 class LayerStep:
     def __init__(self, wl, inputs: dict, variant: str = "fast", device="cuda", perms: bool = True,
-                 transposed_weight: bool = False, keep_x: bool = True, theta_dtype: str = "f32"):
+                 transposed_weight: bool = False, keep_x: bool = True, theta_dtype: str = "f32",
+                 save_q: bool = True):
         """theta_dtype "bf16": inputs["theta_r"], inputs["theta_p"] hold bf16 bit patterns and
-        theta is stored in bf16 (dtheta and the optimizer state stay float32)."""
+        theta is stored in bf16 (dtheta and the optimizer state stay float32).  save_q: the CNP
+        forward keeps Q's planes of the full blocks (poetx_cnp's qsave) for the backward."""
         self.wl = wl
         self.variant = B.POETX_FAST if variant == "fast" else B.POETX_MEM
         act = _TORCH[wl.act]
@@ -66,6 +68,8 @@ class LayerStep:
             self.theta_r, self.theta_p = self.theta[:self.n_r], self.theta[self.n_r:]
             self.g = torch.empty((self.n_r + self.n_p, b, b), dtype=act, device=dev)
             self.g_r, self.g_p = self.g[:self.n_r], self.g[self.n_r:]
+            self.q = B.qsave_like(self.theta, b) if save_q else None
+            self.q_r, self.q_p = (self.q[:self.n_r], self.q[self.n_r:]) if save_q else (None, None)
         else:
             # one allocation per side, so that each side's buffer starts 16-byte aligned
             self.theta = None
@@ -74,6 +78,9 @@ class LayerStep:
             self.g = None
             self.g_r = torch.empty(self.n_r * b * b + self.l_r ** 2, dtype=act, device=dev)
             self.g_p = torch.empty(self.n_p * b * b + self.l_p ** 2, dtype=act, device=dev)
+            self.q = None
+            self.q_r = torch.empty((self.n_r, b, b), dtype=torch.float32, device=dev) if save_q and self.n_r else None
+            self.q_p = torch.empty((self.n_p, b, b), dtype=torch.float32, device=dev) if save_q and self.n_p else None
         self.z = torch.empty((n, wl.d_out), dtype=act, device=dev)
         self.saved_b = torch.empty((n, wl.d_out), dtype=act, device=dev) if self.variant == B.POETX_FAST else None
         # fast: also keep the gathered input X~ for the backward (no second gather of x)
@@ -85,19 +92,20 @@ class LayerStep:
         self.adam = None  # Adam state of the fused update (step_adam)
         self.layer = B.Layer(self.w_merged, self.theta_r, self.theta_p, self.g_r, self.g_p, b,
                              act_dtype=act, variant=self.variant, w_scale=self.w_scale,
-                             perm_in=self.perm_in, perm_out=self.perm_out, w_merged_t=self.w_merged_t)
+                             perm_in=self.perm_in, perm_out=self.perm_out, w_merged_t=self.w_merged_t,
+                             q_r=self.q_r, q_p=self.q_p)
 
     def cnp(self):
         b = self.wl.b
         if not self.ragged:
             # both sides share b: one call over the n_R + n_P blocks of the shared buffer
-            B.poetx_cnp(B.POETX_CNP_FWD, self.theta, b, g=self.g)
+            B.poetx_cnp(B.POETX_CNP_FWD, self.theta, b, g=self.g, qsave=self.q)
             return
         p = b * (b - 1) // 2
-        for theta, g, n, last in ((self.theta_r, self.g_r, self.n_r, self.l_r),
-                                  (self.theta_p, self.g_p, self.n_p, self.l_p)):
+        for theta, g, n, last, q in ((self.theta_r, self.g_r, self.n_r, self.l_r, self.q_r),
+                                     (self.theta_p, self.g_p, self.n_p, self.l_p, self.q_p)):
             if n:
-                B.poetx_cnp(B.POETX_CNP_FWD, theta[:n * p].view(n, p), b, g=g[:n * b * b].view(n, b, b))
+                B.poetx_cnp(B.POETX_CNP_FWD, theta[:n * p].view(n, p), b, g=g[:n * b * b].view(n, b, b), qsave=q)
             if last:
                 B.poetx_cnp(B.POETX_CNP_FWD, theta[n * p:].view(1, last * (last - 1) // 2), last,
                             g=g[n * b * b:].view(1, last, last))

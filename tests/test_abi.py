@@ -88,8 +88,8 @@ def test_workspace_queries(B):
     # without an input permutation there is nothing to keep
     assert fwd(B, layer(B), saved_x=FAKE)[1] == need_fast
     nb = ctypes.c_size_t(0)
-    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 16, 256, None, B.POETX_F32, None, B.POETX_BF16, None, B.POETX_F32, None,
-                           None, ctypes.byref(nb), None) == B.POETX_OK
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 16, 256, None, B.POETX_F32, None, B.POETX_BF16, None, None, B.POETX_F32,
+                           None, None, ctypes.byref(nb), None) == B.POETX_OK
     assert nb.value >= 16 * 256 * 256 * 4
 
 
@@ -131,18 +131,21 @@ def test_validation_codes(B):
     # CNP
     nb = ctypes.c_size_t(1 << 40)
     for bad_b in (0, 2048):
-        assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, bad_b, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+        assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, bad_b, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, None, 0, None, FAKE,
                                ctypes.byref(nb), None) == B.POETX_ERR_SHAPE
     q = ctypes.c_size_t(0)  # blocks of size 1 (no parameters) are accepted
-    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 1, None, B.POETX_F32, None, B.POETX_BF16, None, 0, None, None,
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 1, None, B.POETX_F32, None, B.POETX_BF16, None, None, 0, None, None,
                            ctypes.byref(q), None) == B.POETX_OK
-    assert B.raw.poetx_cnp(9, 4, 64, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+    assert B.raw.poetx_cnp(9, 4, 64, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, None, 0, None, FAKE,
                            ctypes.byref(nb), None) == B.POETX_ERR_INVALID_ARG
-    assert B.raw.poetx_cnp(B.POETX_CNP_BWD, 4, 64, FAKE, B.POETX_F32, None, 0, None, B.POETX_F32, FAKE, FAKE,
+    assert B.raw.poetx_cnp(B.POETX_CNP_BWD, 4, 64, FAKE, B.POETX_F32, None, 0, None, None, B.POETX_F32, FAKE, FAKE,
                            ctypes.byref(nb), None) == B.POETX_ERR_INVALID_ARG   # dg missing
     small = ctypes.c_size_t(16)
-    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 64, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, 0, None, FAKE,
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 64, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, None, None, 0, None, FAKE,
                            ctypes.byref(small), None) == B.POETX_ERR_WORKSPACE
+    # a saved-Q buffer must be 16-byte aligned
+    assert B.raw.poetx_cnp(B.POETX_CNP_FWD, 4, 64, FAKE, B.POETX_F32, FAKE, B.POETX_BF16, FAKE + 8, None, 0, None,
+                           FAKE, ctypes.byref(nb), None) == B.POETX_ERR_INVALID_ARG
     # merge
     assert B.raw.poetx_merge_perm(None, None, B.POETX_BF16, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG
     assert B.raw.poetx_merge_perm(FAKE, None, B.POETX_I8, 4, 4, None, None, FAKE, None, None, None) == B.POETX_ERR_INVALID_ARG

@@ -158,6 +158,52 @@ def test_layer_fused_cnp_backward_two_sides(B):
         assert rel_fro_per_block(got, ref) <= TOL_CNP_F32, key_t
 
 
+@pytest.mark.parametrize("n,b", [(40, 256), (600, 256), (70, 64), (24, 512), (3, 96), (5, 48)])
+def test_cnp_saved_q_is_transparent(B, n, b):
+    """poetx_cnp's qsave (Q's planes kept by the forward, read by the backward instead of
+    unpacking theta again) changes nothing: G and dtheta are bitwise those of calls without
+    it, on the chain paths (40 blocks of 256: two backward launches; 600: the fused
+    backward; b = 64, 512), and where qsave is ignored (b = 96 and 48, which take the
+    per-product and the vector-ALU paths)."""
+    _say(f"cnp saved Q n={n} b={b}")
+    theta, dg = WL.make_cnp_inputs(n, b, 0.01, seed=900 + b)
+    th = torch.from_numpy(theta).cuda()
+    dgt = torch.from_numpy(dg).cuda()
+    q = B.qsave_like(th, b)
+    g0 = B.poetx_cnp(B.POETX_CNP_FWD, th, b, g_dtype=torch.bfloat16)
+    g1 = B.poetx_cnp(B.POETX_CNP_FWD, th, b, g_dtype=torch.bfloat16, qsave=q)
+    d0 = B.poetx_cnp(B.POETX_CNP_BWD, th, b, dg=dgt)
+    d1 = B.poetx_cnp(B.POETX_CNP_BWD, th, b, dg=dgt, qsave=q)
+    torch.cuda.synchronize()
+    assert torch.equal(g0.view(torch.int16), g1.view(torch.int16))
+    assert torch.equal(d0.view(torch.int32), d1.view(torch.int32))
+    # and the backward with qsave matches the oracle
+    idx = np.array([0, n - 1])
+    ref = O.cnp_backward(theta[idx].astype(np.float64), dg[idx].astype(np.float64), b)
+    assert rel_fro_per_block(to_host_f64(d1[torch.from_numpy(idx).cuda()]), ref) <= TOL_CNP_F32
+
+
+def test_layer_saved_q_is_transparent(B):
+    """A layer step whose CNP forward keeps Q's planes for the backward (the layer's q_r /
+    q_p) gives bitwise the results of one that unpacks theta again, fast and mem."""
+    from orthogonal_reparameterized_amd.step import LayerStep
+    wl = WL.Workload(89, "saved q", 300, 512, 768, 256, "bf16", "bf16", "bf16", 0.01, 512)
+    inp = WL.make_layer_inputs(wl)
+    for variant in ("fast", "mem"):
+        outs = []
+        for save_q in (False, True):
+            st = LayerStep(wl, inp, variant, save_q=save_q)
+            out = st.step(want_dg=True)
+            torch.cuda.synchronize()
+            outs.append({"z": st.z.clone(), "dx": out["dx"].clone(), "dtheta_r": out["dtheta_r"].clone(),
+                         "dtheta_p": out["dtheta_p"].clone()})
+        _say(f"layer saved Q {variant}")
+        for k in outs[0]:
+            a, c = outs[0][k], outs[1][k]
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               c.view(torch.int16) if c.dtype == torch.bfloat16 else c.view(torch.int32)), (variant, k)
+
+
 @pytest.mark.parametrize("b", [2, 32, 64])
 def test_cnp_many_blocks(B, b):
     """More blocks than a grid's y or z dimension holds (65535): the vector-ALU path (b = 2,
