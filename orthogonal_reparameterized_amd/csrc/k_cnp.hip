@@ -231,6 +231,13 @@ constexpr int CTK = 32, CNTH = 512;
 // RP: rows per panel (one workgroup).  32 fills the GPU from few blocks; 64 halves the
 // streaming of Q (every panel workgroup streams all of Q once per product) when there
 // are blocks enough for 4 workgroups per CU (b = 128 and 256).
+// b = 512 panel height: 32 (two workgroups per CU) or 64 (one; half the Q streamed per row,
+// but 288 workgroups for workload 4's 36 blocks and spills in the backward's first half:
+// 122 / 165 / 157 against 102 / 158 / 132 us for the three chains)
+#ifndef POETX_CHAIN512_RP
+#define POETX_CHAIN512_RP 32
+#endif
+
 // NW: waves per workgroup.  16 waves split a 128-row panel into two 64-row halves, wave w
 // and w + 8 taking the same columns: their streams of Q fragments are the same, so the
 // second read of each can hit the CU's vector L1 and the panel asks L2 for half the bytes
@@ -238,7 +245,7 @@ constexpr int CTK = 32, CNTH = 512;
 // at 4096 blocks of 256 (forward 1.75 against 1.64 ms), so it is off (POETX_CHAIN16).
 template <int B, int RP, int NW = 8>
 struct ChainCfg {
-  static_assert(RP == 32 || (RP == 64 && B >= 128 && B <= 256) || (RP == 128 && NW == 16 && B >= 128 && B <= 256),
+  static_assert(RP == 32 || (RP == 64 && B >= 128) || (RP == 128 && NW == 16 && B >= 128 && B <= 256),
                 "panel height");
   static_assert(NW == 8 || RP == 128, "16 waves only for 128-row panels");
   static constexpr int NTH = 64 * NW;
@@ -474,6 +481,9 @@ POETX_CHAIN_INST(256, 32, 8)
 POETX_CHAIN_INST(512, 32, 8)
 POETX_CHAIN_INST(128, 64, 8)
 POETX_CHAIN_INST(256, 64, 8)
+#if POETX_CHAIN512_RP == 64
+POETX_CHAIN_INST(512, 64, 8)
+#endif
 POETX_CHAIN_INST(128, 128, 16)
 POETX_CHAIN_INST(256, 128, 16)
 #undef POETX_CHAIN_INST
@@ -756,7 +766,7 @@ int cnp_chain(const CnpChainArgs &a, hipStream_t s) {
     case 64: return chain_run<64, 32>(a, s);
     case 128: return tall2 ? chain_run<128, 128, 16>(a, s) : tall ? chain_run<128, 64>(a, s) : chain_run<128, 32>(a, s);
     case 256: return tall2 ? chain_run<256, 128, 16>(a, s) : tall ? chain_run<256, 64>(a, s) : chain_run<256, 32>(a, s);
-    case 512: return chain_run<512, 32>(a, s);
+    case 512: return POETX_CHAIN512_RP == 64 ? chain_run<512, 64>(a, s) : chain_run<512, 32>(a, s);
     default: return POETX_ERR_UNSUPPORTED;
   }
 }
