@@ -629,13 +629,16 @@ def summarize_pmc(*dbs):
 
 
 # ---------------------------------------------------------------- workloads ----
-def cnp_bench(wl, steps, warmup):
-    """Workload 2: CNP forward (G in bf16) and backward on independent blocks."""
+def cnp_bench(wl, steps, warmup, theta_bf16=False):
+    """Workload 2: CNP forward (G in bf16) and backward on independent blocks; theta_bf16:
+    the same draws stored as bf16 (then Q is exact in bf16 and the kernels skip its lo part)."""
     import torch
     from orthogonal_reparameterized_amd import binding as B
     from orthogonal_reparameterized_amd import workloads as WL
     theta, dg = WL.make_cnp_inputs(wl.nblocks, wl.b, wl.theta_std, seed=WL.BASE_SEED + wl.key)
     th = torch.from_numpy(theta).cuda()
+    if theta_bf16:
+        th = th.to(torch.bfloat16)
     dgt = torch.from_numpy(dg).cuda()
     del theta, dg
     g = torch.empty((wl.nblocks, wl.b, wl.b), dtype=torch.bfloat16, device="cuda")
@@ -670,7 +673,7 @@ def cnp_bench(wl, steps, warmup):
     torch.cuda.empty_cache()
     return {
         "metric": "CNP fwd+bwd blocks/s (4096 x b=256)", "value": n / (ms * 1e-3), "unit": "blocks/s",
-        "saved_q": True,
+        "saved_q": True, "theta_dtype": "bf16" if theta_bf16 else "f32",
         "ms_per_step": ms, "fwd_ms": res["fwd"], "bwd_ms": res["bwd"],
         "fwd_ms_median": statistics.median(per["fwd"]), "bwd_ms_median": statistics.median(per["bwd"]),
         "config": {"workload": wl.name, "nblocks": n, "b": b},
@@ -713,6 +716,7 @@ def main():
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="untimed steps before the warm-up (seconds; 0 for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--theta-bf16", action="store_true", help="workload 2 with theta stored in bf16")
     ap.add_argument("--summarize-trace", nargs="+", metavar="DB [BENCH_JSON]")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DB")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB")
@@ -739,7 +743,7 @@ def main():
 
     wl = WL.WORKLOADS[args.workload]
     if wl.nblocks:
-        r = cnp_bench(wl, args.steps, args.warmup)
+        r = cnp_bench(wl, args.steps, args.warmup, theta_bf16=args.theta_bf16)
         r.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
                   "scaling": "weak", "vs_baseline": None, "dtype": "f32 (split-bf16 MFMA)", "data": "synthetic"})
         print(json.dumps(r))
@@ -821,6 +825,7 @@ def main():
             if key != args.workload:
                 others[str(key)] = layer_summary(WL.WORKLOADS[key], max(5, args.steps // 2), 3)
         others["2"] = cnp_bench(WL.WORKLOADS[2], max(5, args.steps // 2), 2)
+        others["2_bf16_theta"] = cnp_bench(WL.WORKLOADS[2], max(5, args.steps // 2), 2, theta_bf16=True)
         out["other_workloads"] = others
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, WL.make_layer_inputs(wl))

@@ -195,6 +195,7 @@ int cnp_fwd_impl(int64_t n, int64_t b, const void *theta, int theta_bf16, void *
     CnpChainArgs c;
     c.b = (int)b;
     c.mode = CNP_CHAIN_FWD;
+    c.qlo = !theta_bf16;
     c.name = "cnp_fwd_chain";
     c.seg[0].qp = un.planes[0]; c.seg[0].nblk = n;
     if (g_dtype == POETX_F32) c.seg[0].out = (float *)g;
@@ -275,6 +276,7 @@ int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, int theta_b
   un.src_bf16 = theta_bf16;
   CnpChainArgs c;
   c.b = (int)b;
+  c.qlo = !theta_bf16;
   c.name = "cnp_bwd_fused";
   for (int i = 0; i < nside; ++i) {
     const size_t blk = (size_t)side[i].n * b * b * 4;
@@ -299,6 +301,7 @@ int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, 
   un.src_bf16 = theta_bf16;
   CnpChainArgs ca, cb;
   ca.b = cb.b = (int)b;
+  ca.qlo = cb.qlo = !theta_bf16;
   ca.mode = CNP_CHAIN_BWDA; ca.name = "cnp_bwd_chain_a";
   cb.mode = CNP_CHAIN_BWDB; cb.name = "cnp_bwd_chain_b";
   for (int i = 0; i < nside; ++i) {

@@ -275,9 +275,13 @@ __device__ inline void put_split4(bf16_t *h, bf16_t *lo, float4 v) {
 }
 }  // namespace
 
-template <int B, int MODE, int RP, int NW>
+// QL: Q's planes carry a lo part.  With bf16 theta, Q is exact in bf16 (lo = 0): the lo
+// plane is neither written nor read and the pass with Q_lo is dropped, which changes nothing
+// but the work (two MFMA passes per product instead of three, half the Q bytes).
+template <int B, int MODE, int RP, int NW, bool QL>
 __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
   using C = ChainCfg<B, RP, NW>;
+  constexpr int NPL = QL ? 2 : 1;  // Q planes streamed
   extern __shared__ __align__(16) bf16_t smem[];
   bf16_t *sAh = smem, *sAl = smem + RP * C::A_LD;
 
@@ -308,12 +312,12 @@ __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
   const __amdgpu_buffer_rsrc_t rq =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(qf), (short)0, 4 * B * B, 0x00020000);
   const int voff = l * 16 + (nb / 16) * 2048;
-  u32x4 fb[C::D][C::WN][2];
+  u32x4 fb[C::D][C::WN][NPL];
   auto fload = [&](int slot, int k) {
 #pragma unroll
     for (int j = 0; j < C::WN; ++j)
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
+      for (int pl = 0; pl < NPL; ++pl)
         fb[slot][j][pl] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff, (k * C::NT + j) * 2048 + pl * 1024, 0));
   };
@@ -326,7 +330,8 @@ __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
     // X = Q[rows] + 2I: rows r0.. are k steps pnl * RP/32 .. of the fragment-ordered planes
     for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += C::NTH) {
       const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
-      const u32x4 v = *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8);
+      const u32x4 v = (QL || !pl) ? *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8)
+                                  : u32x4{0u, 0u, 0u, 0u};
       bf16_t *dst = (pl ? sAl : sAh) + (32 * ks + 8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst[e * C::A_LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
@@ -388,15 +393,17 @@ __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
 #pragma unroll
     for (int j = 0; j < C::WN; ++j) {
       fbh[j] = __builtin_bit_cast(bf16x8, fb[u][j][0]);
-      fbl[j] = __builtin_bit_cast(bf16x8, fb[u][j][1]);
+      if constexpr (QL) fbl[j] = __builtin_bit_cast(bf16x8, fb[u][j][NPL - 1]);
     }
     // operands swapped: lane l holds C[m = l%16][n = 4*(l/16) + 0..3]; pass-major
     // order puts the other accumulators between two passes on the same one
+    if constexpr (QL) {
 #pragma unroll
-    for (int i = 0; i < C::WM; ++i)
+      for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::WN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbl[j], ah[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < C::WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbl[j], ah[i], acc[i][j], 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < C::WM; ++i)
 #pragma unroll
@@ -471,10 +478,11 @@ __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
   }
 }
 
-#define POETX_CHAIN_INST(B, R, W)                                              \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_FWD, R, W>(CnpChainArgs);  \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDA, R, W>(CnpChainArgs); \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDB, R, W>(CnpChainArgs);
+#define POETX_CHAIN_INST2(B, R, W, QL)                                             \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_FWD, R, W, QL>(CnpChainArgs);  \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDA, R, W, QL>(CnpChainArgs); \
+  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDB, R, W, QL>(CnpChainArgs);
+#define POETX_CHAIN_INST(B, R, W) POETX_CHAIN_INST2(B, R, W, true) POETX_CHAIN_INST2(B, R, W, false)
 POETX_CHAIN_INST(64, 32, 8)
 POETX_CHAIN_INST(128, 32, 8)
 POETX_CHAIN_INST(256, 32, 8)
@@ -487,6 +495,7 @@ POETX_CHAIN_INST(512, 64, 8)
 POETX_CHAIN_INST(128, 128, 16)
 POETX_CHAIN_INST(256, 128, 16)
 #undef POETX_CHAIN_INST
+#undef POETX_CHAIN_INST2
 
 // ========================================================== fused backward ====
 // The adjoint of eq. 9 regrouped so that one workgroup finishes a row panel C of Qbar^T
@@ -510,9 +519,10 @@ struct FusedCfg {
   static constexpr int NP = B / RP;
 };
 
-template <int B, int RP>
+template <int B, int RP, bool QL>
 __global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
   using C = FusedCfg<B, RP>;
+  constexpr int NPL = QL ? 2 : 1;  // Q planes streamed (see k_cnp_chain)
   extern __shared__ __align__(16) bf16_t smem[];
   bf16_t *sWh = smem, *sWl = smem + RP * C::A_LD;
   bf16_t *sUh = smem + 2 * RP * C::A_LD, *sUl = smem + 3 * RP * C::A_LD;
@@ -549,12 +559,12 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(G), (short)0, 4 * B * B, 0x00020000);
   const int voff = l * 16 + (nb / 16) * 2048;
   const int goff = ((nb + (l & 15)) * B + 8 * (l >> 4)) * 4;
-  u32x4 fq[C::D][C::WN][2], fg[C::D][C::WN][2];
+  u32x4 fq[C::D][C::WN][NPL], fg[C::D][C::WN][2];
   auto fload = [&](int slot, int k) {
 #pragma unroll
     for (int j = 0; j < C::WN; ++j) {
 #pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
+      for (int pl = 0; pl < NPL; ++pl)
         fq[slot][j][pl] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff, (k * C::NT + j) * 2048 + pl * 1024, 0));
 #pragma unroll
@@ -569,7 +579,8 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
   // ---- start panels: U_1 = Q[rows] (k steps pnl * RP/32 .. of the planes), W_0 = Gb^T[rows]
   for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += CNTH) {
     const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
-    const u32x4 v = *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8);
+    const u32x4 v = (QL || !pl) ? *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8)
+                                : u32x4{0u, 0u, 0u, 0u};
     bf16_t *dst = (pl ? sUl : sUh) + (32 * ks + 8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e * C::A_LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
@@ -612,7 +623,7 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
 #pragma unroll
     for (int j = 0; j < C::WN; ++j) {
       qh[j] = __builtin_bit_cast(bf16x8, fq[u][j][0]);
-      ql[j] = __builtin_bit_cast(bf16x8, fq[u][j][1]);
+      if constexpr (QL) ql[j] = __builtin_bit_cast(bf16x8, fq[u][j][NPL - 1]);
       // whole vectors are reinterpreted, then indexed: a bit cast of one element of a
       // vector (bit_cast(float, v[i])) reads element 0 whatever i is with this compiler
       const f32x4 g0 = __builtin_bit_cast(f32x4, fg[u][j][0]), g1 = __builtin_bit_cast(f32x4, fg[u][j][1]);
@@ -635,7 +646,7 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
 #pragma unroll
       for (int j = 0; j < C::WN; ++j) {
         f32x4 w = accW[i][j];
-        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j], wh, w, 0, 0, 0);
+        if constexpr (QL) w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j], wh, w, 0, 0, 0);
         w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gl[j], uh, w, 0, 0, 0);
         w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], wl, w, 0, 0, 0);
         w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gh[j], ul, w, 0, 0, 0);
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
         accW[i][j] = w;
         if (p < 2) {
           f32x4 v = accU[i][j];
-          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j], uh, v, 0, 0, 0);
+          if constexpr (QL) v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j], uh, v, 0, 0, 0);
           v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], ul, v, 0, 0, 0);
           v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], uh, v, 0, 0, 0);
           accU[i][j] = v;
@@ -683,9 +694,12 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
 #pragma unroll
     for (int st = 0; st < C::NK; ++st) step(st, p);
 }
-template __global__ void k_cnp_bwd_fused<64, 32>(CnpChainArgs);
-template __global__ void k_cnp_bwd_fused<128, 64>(CnpChainArgs);
-template __global__ void k_cnp_bwd_fused<256, 64>(CnpChainArgs);
+template __global__ void k_cnp_bwd_fused<64, 32, true>(CnpChainArgs);
+template __global__ void k_cnp_bwd_fused<128, 64, true>(CnpChainArgs);
+template __global__ void k_cnp_bwd_fused<256, 64, true>(CnpChainArgs);
+template __global__ void k_cnp_bwd_fused<64, 32, false>(CnpChainArgs);
+template __global__ void k_cnp_bwd_fused<128, 64, false>(CnpChainArgs);
+template __global__ void k_cnp_bwd_fused<256, 64, false>(CnpChainArgs);
 
 // b = 512 on the row-panel chains; off, it takes the per-product launches (k_cnp_mm, two
 // forward, six backward): measured slower at workload 4 (115 against 104 us forward, 345
@@ -712,15 +726,19 @@ int chain_run(const CnpChainArgs &a, hipStream_t s) {
   const int64_t nwg = nz * C::NP;
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
   const size_t lds = (size_t)2 * RP * C::A_LD * sizeof(bf16_t);
-  static std::atomic<uint64_t> attr[3];  // dynamic LDS above 64 KB, per kernel and device
-  auto go = [&](void (*kern)(CnpChainArgs), int mode) -> int {
-    POETX_TRY(lds_limit((const void *)kern, lds, attr[mode]));
+  static std::atomic<uint64_t> attr[6];  // dynamic LDS above 64 KB, per kernel and device
+  auto go = [&](void (*kern)(CnpChainArgs), int id) -> int {
+    POETX_TRY(lds_limit((const void *)kern, lds, attr[id]));
     return launch_k(a.name, s, kern, dim3((unsigned)nwg), C::NTH, lds, a);
   };
+  const bool ql = a.qlo != 0;
   switch (a.mode) {
-    case CNP_CHAIN_FWD: return go(k_cnp_chain<B, CNP_CHAIN_FWD, RP, NW>, 0);
-    case CNP_CHAIN_BWDA: return go(k_cnp_chain<B, CNP_CHAIN_BWDA, RP, NW>, 1);
-    case CNP_CHAIN_BWDB: return go(k_cnp_chain<B, CNP_CHAIN_BWDB, RP, NW>, 2);
+    case CNP_CHAIN_FWD:
+      return ql ? go(k_cnp_chain<B, CNP_CHAIN_FWD, RP, NW, true>, 0) : go(k_cnp_chain<B, CNP_CHAIN_FWD, RP, NW, false>, 3);
+    case CNP_CHAIN_BWDA:
+      return ql ? go(k_cnp_chain<B, CNP_CHAIN_BWDA, RP, NW, true>, 1) : go(k_cnp_chain<B, CNP_CHAIN_BWDA, RP, NW, false>, 4);
+    case CNP_CHAIN_BWDB:
+      return ql ? go(k_cnp_chain<B, CNP_CHAIN_BWDB, RP, NW, true>, 2) : go(k_cnp_chain<B, CNP_CHAIN_BWDB, RP, NW, false>, 5);
     default: return POETX_ERR_INVALID_ARG;
   }
 }
@@ -734,9 +752,13 @@ int fused_run(const CnpChainArgs &a, hipStream_t s) {
   const int64_t nwg = nz * C::NP;
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
   const size_t lds = (size_t)4 * RP * C::A_LD * sizeof(bf16_t);
-  static std::atomic<uint64_t> attr{0};  // dynamic LDS above 64 KB, per device
-  POETX_TRY(lds_limit((const void *)k_cnp_bwd_fused<B, RP>, lds, attr));
-  return launch_k(a.name, s, k_cnp_bwd_fused<B, RP>, dim3((unsigned)nwg), CNTH, lds, a);
+  static std::atomic<uint64_t> attr[2];  // dynamic LDS above 64 KB, per kernel and device
+  if (a.qlo) {
+    POETX_TRY(lds_limit((const void *)k_cnp_bwd_fused<B, RP, true>, lds, attr[0]));
+    return launch_k(a.name, s, k_cnp_bwd_fused<B, RP, true>, dim3((unsigned)nwg), CNTH, lds, a);
+  }
+  POETX_TRY(lds_limit((const void *)k_cnp_bwd_fused<B, RP, false>, lds, attr[1]));
+  return launch_k(a.name, s, k_cnp_bwd_fused<B, RP, false>, dim3((unsigned)nwg), CNTH, lds, a);
 }
 }  // namespace
 

@@ -528,6 +528,7 @@ __global__ __launch_bounds__(256) void k_unpack_frag(SkewSegs sg, int64_t b) {
   }
   __syncthreads();
   const int tt = tid >> 7, pl = (tid >> 6) & 1, ln = tid & 63;
+  if (pl && sg.src_bf16) return;  // bf16 theta: the lo plane is all zero and never read
   const int col = 16 * tt + (ln & 15);
   bf16_t *base = sg.planes[si] + 2 * z * b * b + pl * 512 + ln * 8;
   // mir = 0: the tile at (rb, cb); mir = 1: its mirror at (cb, rb)
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(512) void k_unpack_frag_strip(SkewSegs sg, int64_t 
     }
     bf16_t *dst = planes + cnp_frag_off(r0, c0, b) + l * 8;
     *(uint4 *)dst = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    *(uint4 *)(dst + 512) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    if (!sg.src_bf16) *(uint4 *)(dst + 512) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
   }
 }
 

@@ -60,7 +60,7 @@ struct SkewSegs {
   float *dst[2] = {nullptr, nullptr};
   bf16_t *planes[2] = {nullptr, nullptr};
   int64_t n[2] = {0, 0};
-  int src_bf16 = 0;
+  int src_bf16 = 0;  // theta in bf16: Q is exact in bf16, and the planes' lo part (all zero) is not written
 };
 // Adam hyperparameters (step_size and rs2 carry the bias corrections) and, for the update
 // fused into the pack of dtheta, the parameter and state buffers of up to two segments.
@@ -190,6 +190,7 @@ struct CnpChainSeg {
 };
 struct CnpChainArgs {
   int b = 0, mode = CNP_CHAIN_FWD;
+  int qlo = 1;  // 0: Q's planes have no lo part (bf16 theta: Q is exact in bf16)
   CnpChainSeg seg[2];
   const char *name = "cnp_chain";
 };

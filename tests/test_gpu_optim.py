@@ -74,6 +74,31 @@ def test_cnp_bf16_theta(B, n, b):
     assert rel_fro_per_block(to_host_f64(d), ref_d) <= TOL_CNP_F32
 
 
+@pytest.mark.parametrize("n,b", [(600, 256), (1100, 64), (40, 128)])
+def test_cnp_bf16_theta_many_blocks(B, n, b):
+    """bf16 theta where the backward runs the fused kernel (600 blocks of 256, 1100 of 64) and
+    the 64-row chains' neighbour (40 blocks of 128: two chain launches).  With bf16 theta the
+    kernels drop Q's lo plane and its MFMA pass (Q is exact in bf16); sampled blocks against
+    the oracle, and the saved-Q backward bitwise equal to the one that unpacks theta."""
+    theta, dg = WL.make_cnp_inputs(n, b, 0.02, seed=700 + b)
+    bits = WL.f32_to_bf16_bits(theta)
+    exact = WL.bf16_bits_to_f32(bits).astype(np.float64)
+    th = _bf16_dev(bits)
+    dgt = torch.from_numpy(dg).cuda()
+    q = B.qsave_like(th, b)
+    g32 = B.poetx_cnp(B.POETX_CNP_FWD, th, b, g_dtype=torch.float32, qsave=q)
+    d0 = B.poetx_cnp(B.POETX_CNP_BWD, th, b, dg=dgt)
+    d1 = B.poetx_cnp(B.POETX_CNP_BWD, th, b, dg=dgt, qsave=q)
+    torch.cuda.synchronize()
+    _say(f"cnp bf16 theta n={n} b={b}")
+    assert torch.equal(d0.view(torch.int32), d1.view(torch.int32))
+    idx = np.array([0, 1, n // 2, n - 1])
+    sel = torch.from_numpy(idx).cuda()
+    assert rel_fro_per_block(to_host_f64(g32[sel]), O.cnp_forward(exact[idx], b)) <= TOL_CNP_F32
+    ref_d = O.cnp_backward(exact[idx], dg[idx].astype(np.float64), b)
+    assert rel_fro_per_block(to_host_f64(d1[sel]), ref_d) <= TOL_CNP_F32
+
+
 LAYERS = [
     # (n_tokens, d_in, d_out, b): the chains and the MFMA block kernels; smaller last blocks
     (257, 512, 768, 256),
