@@ -642,7 +642,7 @@ def cnp_bench(wl, steps, warmup, theta_bf16=False):
     dgt = torch.from_numpy(dg).cuda()
     del theta, dg
     g = torch.empty((wl.nblocks, wl.b, wl.b), dtype=torch.bfloat16, device="cuda")
-    dth = torch.empty_like(th)
+    dth = torch.empty(th.shape, dtype=torch.float32, device="cuda")  # dtheta is float32 whatever theta is
     q = B.qsave_like(th, wl.b)  # the forward keeps Q's planes; the backward reads them
     res, per = {}, {}
     for name, fn in (("fwd", lambda: B.poetx_cnp(B.POETX_CNP_FWD, th, wl.b, g=g, qsave=q)),

@@ -167,6 +167,19 @@ def poetx_merge_perm(w: torch.Tensor, perm_out=None, perm_in=None, w_scale=None,
     return out, (out_scale if w.dtype == torch.int8 else None)
 
 
+def _need(t: Optional[torch.Tensor], name: str, numel: int, dtypes) -> None:
+    """A buffer the library reads or writes through a raw pointer: contiguous, of one of the
+    expected dtypes and with exactly the elements the call touches."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def qsave_like(theta: torch.Tensor, b: int) -> torch.Tensor:
     """A buffer for poetx_cnp's qsave (n * b * b * 4 bytes, 16-byte aligned)."""
     return torch.empty((theta.shape[0], b, b), dtype=torch.float32, device=theta.device)
@@ -179,12 +192,20 @@ def poetx_cnp(direction: int, theta: torch.Tensor, b: int, *, g: Optional[torch.
     qsave (optional, from qsave_like): FWD fills it, BWD on the same theta reads Q from it."""
     n = theta.shape[0]
     dev = theta.device
+    p = b * (b - 1) // 2
+    # the library writes through raw pointers: every buffer's dtype and size is checked here
+    _need(theta, "theta", n * p, (torch.float32, torch.bfloat16))
     if direction == POETX_CNP_FWD:
         g = torch.empty((n, b, b), dtype=g_dtype, device=dev) if g is None else g
+        _need(g, "g", n * b * b, (torch.float32, torch.bfloat16))
         gdt, dgdt = _dt(g), POETX_F32
     else:
         dtheta = torch.empty(theta.shape, dtype=torch.float32, device=dev) if dtheta is None else dtheta
+        _need(dg, "dg", n * b * b, (torch.float32,))
+        _need(dtheta, "dtheta", n * p, (torch.float32,))
         gdt, dgdt = POETX_F32, _dt(dg)
+    if qsave is not None:
+        _need(qsave, "qsave", n * b * b, (torch.float32,))
     tdt = _dt(theta)
     nbytes = _sz(0)
     _check(_lib.poetx_cnp(direction, n, b, None, tdt, None, gdt, None, None, dgdt, None, None,
@@ -235,6 +256,9 @@ class Layer:
         c.g_dtype = _dt(self.g_r)
         c.variant = self.variant
         c.theta_dtype = _dt(self.theta_r)
+        for q, d in ((self.q_r, self.d_in), (self.q_p, self.d_out)):
+            if q is not None:
+                _need(q, "q_r / q_p", (d // self.b) * self.b * self.b, (torch.float32,))
         for name in ("w_merged", "w_merged_t", "w_scale", "perm_in", "perm_out", "theta_r", "theta_p",
                      "g_r", "g_p", "q_r", "q_p"):
             p = _ptr(getattr(self, name))
@@ -276,6 +300,9 @@ def poetx_backward(layer: Layer, x: torch.Tensor, dz: torch.Tensor,
     dx = torch.empty((n, layer.d_in), dtype=layer.act_dtype, device=dev) if dx is None else dx
     dtheta_r = torch.empty(layer.theta_r.shape, dtype=torch.float32, device=dev) if dtheta_r is None else dtheta_r
     dtheta_p = torch.empty(layer.theta_p.shape, dtype=torch.float32, device=dev) if dtheta_p is None else dtheta_p
+    _need(dx, "dx", n * layer.d_in, (layer.act_dtype,))
+    _need(dtheta_r, "dtheta_r", layer.theta_r.numel(), (torch.float32,))
+    _need(dtheta_p, "dtheta_p", layer.theta_p.numel(), (torch.float32,))
     dg_r = dg_p = None
     if want_dg:
         b = layer.b
@@ -320,9 +347,9 @@ def poetx_adam_step(theta: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v:
                     step: int, betas=(0.9, 0.999), eps: float = 1e-8, gamma: float = 1.0):
     """In-place Adam update of packed theta (float32 or bf16) and its float32 state m, v
     from grad = dtheta."""
-    for t in (grad, m, v):
-        assert t.dtype == torch.float32 and t.is_contiguous() and t.numel() == theta.numel()
-    assert theta.is_contiguous()
+    _need(theta, "theta", theta.numel(), (torch.float32, torch.bfloat16))
+    for t, nm in ((grad, "grad"), (m, "m"), (v, "v")):
+        _need(t, nm, theta.numel(), (torch.float32,))
     _check(_lib.poetx_adam_step(theta.numel(), _ptr(theta), _dt(theta), _ptr(grad), _ptr(m), _ptr(v), lr,
                                 betas[0], betas[1], eps, step, gamma, _stream(theta.device)), "poetx_adam_step")
     return theta
@@ -354,6 +381,13 @@ def poetx_backward_adam(layer: Layer, x: torch.Tensor, dz: torch.Tensor, state: 
     n = x.shape[0]
     dev = x.device
     dx = torch.empty((n, layer.d_in), dtype=layer.act_dtype, device=dev) if dx is None else dx
+    _need(dx, "dx", n * layer.d_in, (layer.act_dtype,))
+    for t, th, nm in ((state.m_r, layer.theta_r, "m_r"), (state.v_r, layer.theta_r, "v_r"),
+                      (state.m_p, layer.theta_p, "m_p"), (state.v_p, layer.theta_p, "v_p")):
+        _need(t, nm, th.numel(), (torch.float32,))
+    for t, th, nm in ((dtheta_r, layer.theta_r, "dtheta_r"), (dtheta_p, layer.theta_p, "dtheta_p")):
+        if t is not None:
+            _need(t, nm, th.numel(), (torch.float32,))
     state.step += 1
     opt = PoetxAdamC()
     opt.lr, opt.beta1, opt.beta2, opt.eps, opt.gamma, opt.step = lr, betas[0], betas[1], eps, gamma, state.step

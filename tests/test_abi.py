@@ -302,3 +302,25 @@ def test_backward_adam_validation(B):
     assert fwd(B, bad)[0] == B.POETX_ERR_INVALID_ARG
     bad.theta_dtype = B.POETX_BF16
     assert fwd(B, bad)[0] == B.POETX_OK
+
+
+def test_binding_rejects_mismatched_buffers(B):
+    """The binding checks every buffer the library reads or writes through a raw pointer
+    (dtype, element count, contiguity) before any device call: a bf16 dtheta for the
+    float32 gradient, a short G or a short saved-Q buffer raise ValueError."""
+    import torch
+    b, n = 64, 3
+    p = b * (b - 1) // 2
+    th32 = torch.zeros(n, p)
+    th16 = th32.to(torch.bfloat16)
+    dg = torch.zeros(n, b, b)
+    with pytest.raises(ValueError):
+        B.poetx_cnp(B.POETX_CNP_BWD, th16, b, dg=dg, dtheta=torch.empty_like(th16))
+    with pytest.raises(ValueError):
+        B.poetx_cnp(B.POETX_CNP_FWD, th32, b, g=torch.empty(n, b, b - 1))
+    with pytest.raises(ValueError):
+        B.poetx_cnp(B.POETX_CNP_FWD, th32, b, qsave=torch.empty(n - 1, b, b))
+    with pytest.raises(ValueError):
+        B.poetx_cnp(B.POETX_CNP_BWD, th32, b, dg=dg.to(torch.bfloat16))
+    with pytest.raises(ValueError):
+        B.poetx_cnp(B.POETX_CNP_FWD, th32[:, :p - 1], b)
