@@ -268,16 +268,17 @@ int pack_sides(SkewSegs &pk, const CnpBwdSide *side, int nside, int64_t b, int t
 }
 
 // CNP backward of up to two independent sides sharing b (the R and P sides of a layer):
-// unpack Q, then the whole adjoint in one fused launch, then pack dtheta.
+// unpack Q, then the whole adjoint in one launch (five products, or the fused eight),
+// then pack dtheta.
 int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h,
-                       void *ws, hipStream_t s) {
+                       void *ws, hipStream_t s, bool five) {
   Arena ar(ws);
   SkewSegs un, pk;
   un.src_bf16 = theta_bf16;
   CnpChainArgs c;
   c.b = (int)b;
   c.qlo = !theta_bf16;
-  c.name = "cnp_bwd_fused";
+  c.name = five ? "cnp_bwd5" : "cnp_bwd_fused";
   for (int i = 0; i < nside; ++i) {
     const size_t blk = (size_t)side[i].n * b * b * 4;
     // a side with saved planes is not unpacked again (its segment is left empty)
@@ -288,7 +289,7 @@ int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, int theta_b
     pk.src[i] = c.seg[i].out; pk.dst[i] = side[i].dtheta; pk.n[i] = side[i].n;
   }
   POETX_TRY(unpack_skew2(un, b, s));
-  POETX_TRY(cnp_bwd_fused(c, s));
+  POETX_TRY(five ? cnp_bwd5(c, s) : cnp_bwd_fused(c, s));
   return pack_sides(pk, side, nside, b, theta_bf16, h, s);
 }
 
@@ -331,7 +332,8 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, c
   for (int i = 0; i < nside; ++i) vec = vec && al16(side[i].dg);
   int64_t nz = 0;
   for (int i = 0; i < nside; ++i) nz += side[i].n;
-  if (vec && cnp_bwd_fused_supported(b, nz)) return cnp_bwd_fused_path(b, side, nside, theta_bf16, h, ws, s);
+  if (vec && cnp_bwd5_supported(b)) return cnp_bwd_fused_path(b, side, nside, theta_bf16, h, ws, s, true);
+  if (vec && cnp_bwd_fused_supported(b, nz)) return cnp_bwd_fused_path(b, side, nside, theta_bf16, h, ws, s, false);
   if (vec && cnp_chain_supported(b)) return cnp_bwd_chain(b, side, nside, theta_bf16, h, ws, s);
   Arena ar(ws);
   struct Bufs { float *Q, *K1, *K2, *K3, *Ha, *Hb; } B[2] = {};

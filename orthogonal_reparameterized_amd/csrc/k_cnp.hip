@@ -33,6 +33,28 @@ __device__ inline void split2(float x, uint16_t &hi, uint16_t &lo) {
   hi = f32_to_bf16(x);
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
+// The same split of two floats at once, packed (element 0 in the low half): gfx950's
+// v_cvt_pk_bf16_f32 rounds to nearest even like f32_to_bf16 (checked over every finite
+// float), in one instruction per pair where the integer rounding takes three per value.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+#ifndef POETX_CVT_PK
+#define POETX_CVT_PK 1
+#endif
+__device__ inline void split_pk(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  if constexpr (POETX_CVT_PK) {
+    const f32x2 v = {x0, x1};
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    const f32x2 r = {x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u)};
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+  } else {
+    uint16_t h0, l0, h1, l1;
+    split2(x0, h0, l0);
+    split2(x1, h1, l1);
+    hi = h0 | (uint32_t)h1 << 16;
+    lo = l0 | (uint32_t)l1 << 16;
+  }
+}
 
 __device__ inline bf16x8 frag_a(const bf16_t *t, int r0, int ks) {
   int l = threadIdx.x & 63;
@@ -268,10 +290,11 @@ __device__ inline bf16x8 frag_a_ld(const bf16_t *t, int ld, int r0, int k0) {
   return __builtin_bit_cast(bf16x8, v);
 }
 __device__ inline void put_split4(bf16_t *h, bf16_t *lo, float4 v) {
-  uint16_t a[4], c[4];
-  split2(v.x, a[0], c[0]); split2(v.y, a[1], c[1]); split2(v.z, a[2], c[2]); split2(v.w, a[3], c[3]);
-  *(uint2 *)h = make_uint2(a[0] | (uint32_t)a[1] << 16, a[2] | (uint32_t)a[3] << 16);
-  *(uint2 *)lo = make_uint2(c[0] | (uint32_t)c[1] << 16, c[2] | (uint32_t)c[3] << 16);
+  uint32_t a0, a1, c0, c1;
+  split_pk(v.x, v.y, a0, c0);
+  split_pk(v.z, v.w, a1, c1);
+  *(uint2 *)h = make_uint2(a0, a1);
+  *(uint2 *)lo = make_uint2(c0, c1);
 }
 }  // namespace
 
@@ -627,12 +650,14 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
       // whole vectors are reinterpreted, then indexed: a bit cast of one element of a
       // vector (bit_cast(float, v[i])) reads element 0 whatever i is with this compiler
       const f32x4 g0 = __builtin_bit_cast(f32x4, fg[u][j][0]), g1 = __builtin_bit_cast(f32x4, fg[u][j][1]);
-      uint16_t h[8], lo[8];
+      u32x4 hv, lv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) split2(e < 4 ? g0[e & 3] : g1[e & 3], h[e], lo[e]);
-      s16x8 hv, lv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { hv[e] = (short)h[e]; lv[e] = (short)lo[e]; }
+      for (int e = 0; e < 4; ++e) {
+        uint32_t h, lo;
+        split_pk(e < 2 ? g0[2 * e] : g1[2 * e - 4], e < 2 ? g0[2 * e + 1] : g1[2 * e - 3], h, lo);
+        hv[e] = h;
+        lv[e] = lo;
+      }
       gh[j] = __builtin_bit_cast(bf16x8, hv);
       gl[j] = __builtin_bit_cast(bf16x8, lv);
     }
@@ -700,6 +725,334 @@ template __global__ void k_cnp_bwd_fused<256, 64, true>(CnpChainArgs);
 template __global__ void k_cnp_bwd_fused<64, 32, false>(CnpChainArgs);
 template __global__ void k_cnp_bwd_fused<128, 64, false>(CnpChainArgs);
 template __global__ void k_cnp_bwd_fused<256, 64, false>(CnpChainArgs);
+
+// ===================================================== five-product backward ====
+// dtheta reads only the skew part D = Qbar - Qbar^T of the adjoint of eq. 9.  The adjoint
+// is sum_k c_k sum_{i+j=k-1} Q^i A_k Q^j with A_k = Gb - Gb^T (k odd) or -(Gb + Gb^T)
+// (k even), and the terms Q^i A_k Q^j and Q^j A_k Q^i are minus each other's transposes,
+// so D = E - E^T where E keeps one term of each such pair (and half of each Q^i A Q^i):
+//     E = K - 2HQ + 2KQ^2 - HQ^3 + QKQ - QHQ^2,   K = Gb - Gb^T,  H = Gb + Gb^T.
+// Grouped by Horner,
+//     J = 2K - HQ - QH,   F = -2H + QK + JQ,   E = K + FQ,
+// every product of which a row panel C computes from rows C alone:
+//   1a  Q[C] H and Q[C] K  (A: Q[C] in LDS; B: H and K, whose fragments are eight
+//                           consecutive elements of a row of Gb and of a column of Gb)
+//   1b  H[C] Q             (A: H[C] in LDS; B: Q's fragment-ordered planes)
+//   2   J[C] Q             (J[C] replaces Q[C] in LDS)
+//   3   F[C] Q             (F[C] replaces H[C]); E[C] = K[C] + F[C] Q is stored row-major.
+// The pack reads E as it reads Qbar (dtheta_rc = E_rc - E_cr).  Five products in four
+// passes over k against the eight of k_cnp_bwd_fused: 15 MFMAs per 16 x 16 tile and k step
+// instead of 24 (10 instead of 19 when Q is exact in bf16).
+#ifndef POETX_BWD5_DG
+#define POETX_BWD5_DG 2
+#endif
+#ifndef POETX_BWD5_DQ
+#define POETX_BWD5_DQ 4
+#endif
+template <int B, int RP>
+struct Bwd5Cfg {
+  static_assert(RP == 32 || (RP == 64 && B >= 128 && B <= 256), "panel height");
+  static constexpr int NK = B / CTK;
+  static constexpr int NT = B / 16;
+  static constexpr int WM = B >= 128 ? RP / 16 : 1;
+  static constexpr int WN = B >= 128 ? B / 128 : 1;
+  static constexpr int DG = B >= 512 ? 1 : POETX_BWD5_DG;  // k steps of Gb in flight (1a)
+  static constexpr int DQ = B >= 512 ? 2 : (3 * NK < POETX_BWD5_DQ ? 3 * NK : POETX_BWD5_DQ);  // of Q
+  static constexpr int A_LD = B + 8;
+  static constexpr int NP = B / RP;
+  static constexpr int MR = RP * B / CNTH;  // prologue: rows of H[C] per thread, one column each
+  static_assert(CNTH % B == 0 && MR % 4 == 0, "prologue layout");
+};
+
+template <int B, int RP, bool QL>
+__global__ __launch_bounds__(CNTH) void k_cnp_bwd5(CnpChainArgs a) {
+  using C = Bwd5Cfg<B, RP>;
+  constexpr int NPL = QL ? 2 : 1;  // Q planes streamed (see k_cnp_chain)
+  constexpr int NK = C::NK, WM = C::WM, WN = C::WN, DQ = C::DQ, DG = C::DG, LD = C::A_LD;
+  extern __shared__ __align__(16) bf16_t smem[];
+  // slot A: Q[C], then J[C]; slot B: H[C], then F[C] (hi and lo planes, RP rows each)
+  bf16_t *sAh = smem, *sAl = smem + RP * LD;
+  bf16_t *sBh = smem + 2 * RP * LD, *sBl = smem + 3 * RP * LD;
+
+  // 1-D grid, all panels of one block on one XCD (workgroup L runs on XCD L % 8)
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk, nz8 = nz & ~(int64_t)7;
+  const int64_t L = blockIdx.x;
+  int64_t z, pnl;
+  if (L < nz8 * C::NP) {
+    const int64_t slot = L >> 3;
+    z = (L & 7) + 8 * (slot / C::NP);
+    pnl = slot % C::NP;
+  } else {
+    z = L / C::NP;
+    pnl = L % C::NP;
+  }
+  int sg = 0;
+  if (z >= a.seg[0].nblk) { z -= a.seg[0].nblk; sg = 1; }
+  const CnpChainSeg &S = a.seg[sg];
+  const int64_t off = z * (int64_t)B * B;
+  const int r0 = (int)pnl * RP;
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+  const int mb = B >= 128 ? 0 : 16 * (wave >> 2);
+  const int nb = B >= 128 ? wave * (B / 8) : 16 * (wave & 3);
+
+  const bf16_t *qf = S.qp + 2 * off;
+  const float *G = S.dg + off;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(qf), (short)0, 4 * B * B, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(G), (short)0, 4 * B * B, 0x00020000);
+
+  // ---- 1a operands: for k step kk and column tile j (n = nb + 16 j + l%16, k = 32 kk +
+  // 8 (l/16) + e) lane l needs Gb[n][k] (32 contiguous bytes of row n) and Gb[k][n] (eight
+  // rows, one element each; sixteen lanes read 64 contiguous bytes of each row)
+  u32x4 grw[DG][WN][2];
+  float gcl[DG][WN][8];
+  const int goff = ((nb + (l & 15)) * B + 8 * (l >> 4)) * 4;
+  const int coff = (8 * (l >> 4) * B + nb + (l & 15)) * 4;
+  auto gload = [&](int slot, int kk) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        grw[slot][j][h] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, goff, (16 * j * B + kk * CTK) * 4 + 16 * h, 0));
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        gcl[slot][j][e] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rg, coff, ((kk * CTK + e) * B + 16 * j) * 4, 0));
+    }
+  };
+  // ---- 1b, 2, 3 operand: Q's planes, chunk (k, t, plane) of 1 KB per k step and column tile
+  u32x4 fq[DQ][WN][NPL];
+  const int voff = l * 16 + (nb / 16) * 2048;
+  auto qload = [&](int slot, int k) {
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl)
+        fq[slot][j][pl] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff, (k * C::NT + j) * 2048 + pl * 1024, 0));
+  };
+#pragma unroll
+  for (int s = 0; s < DG; ++s) gload(s, s);
+
+  // ---- start panels: Q[C] (k steps pnl * RP/32 .. of the planes) into slot A, H[C] into slot B
+  for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += CNTH) {
+    const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
+    const u32x4 v = (QL || !pl) ? *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8)
+                                : u32x4{0u, 0u, 0u, 0u};
+    bf16_t *dst = (pl ? sAl : sAh) + (32 * ks + 8 * (ln >> 4)) * LD + 16 * t + (ln & 15);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e * LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
+  }
+  {
+    // thread: column kc of H[C], rows m0 .. m0 + MR - 1: H[m][kc] = Gb[r0 + m][kc] + Gb[kc][r0 + m]
+    const int kc = tid % B, m0 = (tid / B) * C::MR;
+    float tcol[C::MR];
+#pragma unroll
+    for (int c = 0; c < C::MR / 4; ++c) {
+      const float4 v = *(const float4 *)(G + (int64_t)kc * B + r0 + m0 + 4 * c);
+      tcol[4 * c] = v.x; tcol[4 * c + 1] = v.y; tcol[4 * c + 2] = v.z; tcol[4 * c + 3] = v.w;
+    }
+#pragma unroll
+    for (int mm = 0; mm < C::MR; ++mm) {
+      const int m = m0 + mm;
+      uint16_t h, lo;
+      split2(G[(int64_t)(r0 + m) * B + kc] + tcol[mm], h, lo);
+      sBh[m * LD + kc] = h;
+      sBl[m * LD + kc] = lo;
+    }
+  }
+  __syncthreads();
+
+  // H[C] and K[C] at the accumulator positions of patch (i, j): rows r0 + m, columns n .. n+3
+  auto hk_at = [&](int i, int j, f32x4 &hv, f32x4 &kv) {
+    const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
+    const float4 rw = *(const float4 *)(G + (int64_t)(r0 + m) * B + n);
+    const float rr[4] = {rw.x, rw.y, rw.z, rw.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float cl = G[(int64_t)(n + c) * B + r0 + m];
+      hv[c] = rr[c] + cl;
+      kv[c] = rr[c] - cl;
+    }
+  };
+
+  // the terms of J and F that are not products start in the accumulators of 1a:
+  // accQH = -2K + Q[C]H (so that J = -(HQ + accQH)), accQK = -2H + Q[C]K = F - JQ
+  f32x4 accQH[WM][WN], accQK[WM][WN], acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      f32x4 hv, kv;
+      hk_at(i, j, hv, kv);
+      accQH[i][j] = -2.f * kv;
+      accQK[i][j] = -2.f * hv;
+      acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // ---- 1a: Q[C] H and Q[C] K; the first DQ k steps of Q go out over the last steps
+  constexpr int QS0 = NK >= DQ ? NK - DQ : 0;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const int u = kk % DG;
+    bf16x8 hh[WN], hl[WN], kh[WN], kl[WN];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      // whole vectors are reinterpreted, then indexed (see k_cnp_bwd_fused)
+      const f32x4 g0 = __builtin_bit_cast(f32x4, grw[u][j][0]), g1 = __builtin_bit_cast(f32x4, grw[u][j][1]);
+      u32x4 vh, vl, wh, wl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r0v = e < 2 ? g0[2 * e] : g1[2 * e - 4], r1v = e < 2 ? g0[2 * e + 1] : g1[2 * e - 3];
+        const float c0v = gcl[u][j][2 * e], c1v = gcl[u][j][2 * e + 1];
+        uint32_t a0, a1, b0, b1;
+        split_pk(c0v + r0v, c1v + r1v, a0, a1);  // H[k][n] = Gb[k][n] + Gb[n][k]
+        split_pk(c0v - r0v, c1v - r1v, b0, b1);  // K[k][n] = Gb[k][n] - Gb[n][k]
+        vh[e] = a0; vl[e] = a1; wh[e] = b0; wl[e] = b1;
+      }
+      hh[j] = __builtin_bit_cast(bf16x8, vh); hl[j] = __builtin_bit_cast(bf16x8, vl);
+      kh[j] = __builtin_bit_cast(bf16x8, wh); kl[j] = __builtin_bit_cast(bf16x8, wl);
+    }
+    bf16x8 qh[WM], ql[WM];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      qh[i] = frag_a_ld(sAh, LD, mb + 16 * i, kk * CTK);
+      if constexpr (QL) ql[i] = frag_a_ld(sAl, LD, mb + 16 * i, kk * CTK);
+    }
+    if (kk + DG < NK) gload(u, kk + DG);
+#pragma unroll
+    for (int s = 0; s < DQ; ++s)
+      if (NK >= DQ ? kk == QS0 + s : kk == 0) qload(s, s % NK);
+    // operands swapped: lane l holds C[m = l%16][n = 4*(l/16) + 0..3]
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        accQH[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hl[j], qh[i], accQH[i][j], 0, 0, 0);
+        accQK[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl[j], qh[i], accQK[i][j], 0, 0, 0);
+      }
+    if constexpr (QL) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          accQH[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hh[j], ql[i], accQH[i][j], 0, 0, 0);
+          accQK[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[j], ql[i], accQK[i][j], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        accQH[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hh[j], qh[i], accQH[i][j], 0, 0, 0);
+        accQK[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[j], qh[i], accQK[i][j], 0, 0, 0);
+      }
+  }
+
+  // ---- 1b, 2, 3: X Q for X = H[C], J[C], F[C], one k step at a time
+  constexpr int NS = 3 * NK;
+  auto qstep = [&](const int st, const int p) {
+    const int g = p * NK + st;
+    const int u = NK % DQ == 0 ? st % DQ : g % DQ;
+    const bf16_t *xh = p == 1 ? sAh : sBh, *xl = p == 1 ? sAl : sBl;
+    bf16x8 ah[WM], al[WM], fbh[WN], fbl[WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      ah[i] = frag_a_ld(xh, LD, mb + 16 * i, st * CTK);
+      al[i] = frag_a_ld(xl, LD, mb + 16 * i, st * CTK);
+    }
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      fbh[j] = __builtin_bit_cast(bf16x8, fq[u][j][0]);
+      if constexpr (QL) fbl[j] = __builtin_bit_cast(bf16x8, fq[u][j][NPL - 1]);
+    }
+    if constexpr (QL) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbl[j], ah[i], acc[i][j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbh[j], al[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fbh[j], ah[i], acc[i][j], 0, 0, 0);
+    if (g + DQ < NS) qload(u, (st + DQ) % NK);  // refill the slot just consumed
+
+    if (st == NK - 1) {
+      if (p == 0) {
+        // J = 2K - HQ - QH into slot A (every wave is past 1a, the last reader of Q[C])
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
+            const f32x4 jv = -(acc[i][j] + accQH[i][j]);
+            put_split4(sAh + m * LD + n, sAl + m * LD + n, make_float4(jv[0], jv[1], jv[2], jv[3]));
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        __syncthreads();
+      } else if (p == 1) {
+        // F = -2H + QK + JQ into slot B (H[C] was last read in 1b, before the barrier above);
+        // the last product accumulates onto K[C]
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
+            const f32x4 fv = accQK[i][j] + acc[i][j];
+            put_split4(sBh + m * LD + n, sBl + m * LD + n, make_float4(fv[0], fv[1], fv[2], fv[3]));
+            f32x4 hv, kv;
+            hk_at(i, j, hv, kv);
+            acc[i][j] = kv;
+          }
+        __syncthreads();
+      } else {
+        // E = K + FQ, row-major
+        float *O = S.out + off;
+#pragma unroll
+        for (int i = 0; i < WM; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
+            const f32x4 ev = acc[i][j];
+            *(float4 *)(O + (int64_t)(r0 + m) * B + n) = make_float4(ev[0], ev[1], ev[2], ev[3]);
+          }
+      }
+    }
+  };
+  if constexpr (B >= 512) {
+    static_assert(NK % DQ == 0, "slots must not depend on p");
+#pragma unroll 1
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int st = 0; st < NK; ++st) qstep(st, p);
+  } else {
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int st = 0; st < NK; ++st) qstep(st, p);
+  }
+}
+#define POETX_BWD5_INST(B, R)                                              \
+  template __global__ void k_cnp_bwd5<B, R, true>(CnpChainArgs);           \
+  template __global__ void k_cnp_bwd5<B, R, false>(CnpChainArgs);
+POETX_BWD5_INST(64, 32)
+POETX_BWD5_INST(128, 32)
+POETX_BWD5_INST(128, 64)
+POETX_BWD5_INST(256, 32)
+POETX_BWD5_INST(256, 64)
+POETX_BWD5_INST(512, 32)
+#undef POETX_BWD5_INST
 
 // b = 512 on the row-panel chains; off, it takes the per-product launches (k_cnp_mm, two
 // forward, six backward): measured slower at workload 4 (115 against 104 us forward, 345
@@ -769,6 +1122,46 @@ int cnp_bwd_fused(const CnpChainArgs &a, hipStream_t s) {
     case 64: return fused_run<64, 32>(a, s);
     case 128: return fused_run<128, 64>(a, s);
     case 256: return fused_run<256, 64>(a, s);
+    default: return POETX_ERR_UNSUPPORTED;
+  }
+}
+
+// The five-product backward (k_cnp_bwd5) for every b of the chains; off, the fused
+// eight-product kernel or the two chain launches take the backward.
+#ifndef POETX_BWD5
+#define POETX_BWD5 1
+#endif
+bool cnp_bwd5_supported(int64_t b) { return POETX_BWD5 && (b == 64 || b == 128 || b == 256 || b == 512); }
+
+namespace {
+template <int B, int RP>
+int bwd5_run(const CnpChainArgs &a, hipStream_t s) {
+  using C = Bwd5Cfg<B, RP>;
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
+  const int64_t nwg = nz * C::NP;
+  if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
+  const size_t lds = (size_t)4 * RP * C::A_LD * sizeof(bf16_t);
+  static std::atomic<uint64_t> attr[2];  // dynamic LDS above 64 KB, per kernel and device
+  if (a.qlo) {
+    POETX_TRY(lds_limit((const void *)k_cnp_bwd5<B, RP, true>, lds, attr[0]));
+    return launch_k(a.name, s, k_cnp_bwd5<B, RP, true>, dim3((unsigned)nwg), CNTH, lds, a);
+  }
+  POETX_TRY(lds_limit((const void *)k_cnp_bwd5<B, RP, false>, lds, attr[1]));
+  return launch_k(a.name, s, k_cnp_bwd5<B, RP, false>, dim3((unsigned)nwg), CNTH, lds, a);
+}
+}  // namespace
+
+int cnp_bwd5(const CnpChainArgs &a, hipStream_t s) {
+  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
+  if (nz <= 0) return POETX_OK;
+  // 64-row panels (half the streaming of Q per row) once they still give 4 workgroups per CU
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const bool tall = nz * (a.b / 64) >= 4 * (int64_t)cus;
+  switch (a.b) {
+    case 64: return bwd5_run<64, 32>(a, s);
+    case 128: return tall ? bwd5_run<128, 64>(a, s) : bwd5_run<128, 32>(a, s);
+    case 256: return tall ? bwd5_run<256, 64>(a, s) : bwd5_run<256, 32>(a, s);
+    case 512: return bwd5_run<512, 32>(a, s);
     default: return POETX_ERR_UNSUPPORTED;
   }
 }

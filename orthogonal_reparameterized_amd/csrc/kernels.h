@@ -201,5 +201,10 @@ int cnp_chain(const CnpChainArgs &a, hipStream_t s);
 // taken for nz blocks in all (both segments) when cnp_bwd_fused_supported(b, nz).
 bool cnp_bwd_fused_supported(int64_t b, int64_t nz);
 int cnp_bwd_fused(const CnpChainArgs &a, hipStream_t s);
+// The CNP backward in five products (mode and r unused): reads qp and dg, writes to out a
+// matrix E with E - E^T = Qbar - Qbar^T (all that dtheta needs), fp32 [b][b] row-major.
+// b in {64, 128, 256, 512}.
+bool cnp_bwd5_supported(int64_t b);
+int cnp_bwd5(const CnpChainArgs &a, hipStream_t s);
 
 }  // namespace poetx

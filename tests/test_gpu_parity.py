@@ -124,7 +124,8 @@ def test_cnp_workload2_sampled(B):
 
 def test_layer_fused_cnp_backward_two_sides(B):
     """A layer wide enough (32768 -> 32768, b = 256: 128 + 128 blocks) that its CNP backward
-    runs the fused kernel over both sides in one launch.  The layer's dtheta on sampled
+    runs one launch over both sides (the five-product kernel; the fused eight-product one
+    when that is switched off).  The layer's dtheta on sampled
     blocks of each side against the oracle's CNP backward of the dG the layer itself
     reports; W, x and dz are drawn on the GPU (their values do not enter the check)."""
     torch.manual_seed(11)
@@ -149,7 +150,8 @@ def test_layer_fused_cnp_backward_two_sides(B):
     out = B.poetx_backward(L, x, dz, sb, want_dg=True)
     torch.cuda.synchronize()
     B.prof_enable(False)
-    assert "cnp_bwd_fused" in B.prof_read()  # the launch this test is for
+    rec = B.prof_read()
+    assert "cnp_bwd5" in rec or "cnp_bwd_fused" in rec  # the one-launch backward this test is for
     idx = np.array([0, 1, 77, nb - 1])
     for th, key_g, key_t in ((th_r, "dg_r", "dtheta_r"), (th_p, "dg_p", "dtheta_p")):
         dg = out[key_g][torch.from_numpy(idx).cuda()].double().cpu().numpy()
