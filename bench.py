@@ -102,7 +102,7 @@ def algorithmic(wl, variant, n, perms=True, keep_x=True):
 
 # kernel labels of the library -> the algorithmic group they carry
 LABEL_GROUP = {"unpack_skew": "cnp_fwd", "cnp_fwd_chain": "cnp_fwd", "cnp_fwd_mm": "cnp_fwd",
-               "cnp_bwd5": "cnp_bwd", "cnp_bwd_fused": "cnp_bwd", "cnp_bwd_chain_a": "cnp_bwd", "cnp_bwd_chain_b": "cnp_bwd",
+               "cnp_bwd5": "cnp_bwd",
                "cnp_bwd_mm": "cnp_bwd", "pack_skew_grad": "cnp_bwd", "reduce_parts": "block_grad",
                "gemm_tail_reduce": None, "transpose": None}
 

@@ -142,11 +142,10 @@ extern "C" int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_d
 //   H2 = (2Gb + K1) + P Gb, H1 = (2Gb + 2K1 + K2) + P H2, Qbar = (2Gb + 2K1 + 2K2 + K3) + P H1,
 // then dtheta[k(i,j)] = Qbar[i][j] - Qbar[j][i].
 // For b in {64, 128, 256, 512} both directions run as row-panel chains of products
-// by Q (k_cnp.hip): the forward as G = (((Q + 2I)Q + 2I)Q + 2I)Q + I in one launch,
-// the backward as K_l = -K_{l-1}Q (rows of Gb P^l) in one launch and the same
-// Horner in P, transposed (Qbar^T = R0^T + (R1^T + (R2^T + Gb^T Q)Q)Q), in a second.
-// Other b % 64 == 0 run the products above one launch each on split-bf16 MFMA;
-// the remaining b use the float32 vector-ALU product.
+// (k_cnp.hip): the forward as G = (((Q + 2I)Q + 2I)Q + 2I)Q + I in one launch, the
+// backward in one launch of five products that yield E with E - E^T = Qbar - Qbar^T
+// (dtheta reads nothing else).  Other b % 64 == 0 run the products above one launch
+// each on split-bf16 MFMA; the remaining b use the float32 vector-ALU product.
 namespace {
 
 GemmDesc batched_f32(int64_t n, int64_t b, const float *A, const float *B, void *C, int c_dt) {
@@ -194,7 +193,6 @@ int cnp_fwd_impl(int64_t n, int64_t b, const void *theta, int theta_bf16, void *
     POETX_TRY(unpack_skew2(un, b, s));
     CnpChainArgs c;
     c.b = (int)b;
-    c.mode = CNP_CHAIN_FWD;
     c.qlo = !theta_bf16;
     c.name = "cnp_fwd_chain";
     c.seg[0].qp = un.planes[0]; c.seg[0].nblk = n;
@@ -268,17 +266,17 @@ int pack_sides(SkewSegs &pk, const CnpBwdSide *side, int nside, int64_t b, int t
 }
 
 // CNP backward of up to two independent sides sharing b (the R and P sides of a layer):
-// unpack Q, then the whole adjoint in one launch (five products, or the fused eight),
-// then pack dtheta.
-int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h,
-                       void *ws, hipStream_t s, bool five) {
+// unpack Q (unless the forward kept its planes), then the five products of every block in
+// one launch, then pack dtheta.
+int cnp_bwd5_path(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h, void *ws,
+                  hipStream_t s) {
   Arena ar(ws);
   SkewSegs un, pk;
   un.src_bf16 = theta_bf16;
   CnpChainArgs c;
   c.b = (int)b;
   c.qlo = !theta_bf16;
-  c.name = five ? "cnp_bwd5" : "cnp_bwd_fused";
+  c.name = "cnp_bwd5";
   for (int i = 0; i < nside; ++i) {
     const size_t blk = (size_t)side[i].n * b * b * 4;
     // a side with saved planes is not unpacked again (its segment is left empty)
@@ -289,38 +287,7 @@ int cnp_bwd_fused_path(int64_t b, const CnpBwdSide *side, int nside, int theta_b
     pk.src[i] = c.seg[i].out; pk.dst[i] = side[i].dtheta; pk.n[i] = side[i].n;
   }
   POETX_TRY(unpack_skew2(un, b, s));
-  POETX_TRY(five ? cnp_bwd5(c, s) : cnp_bwd_fused(c, s));
-  return pack_sides(pk, side, nside, b, theta_bf16, h, s);
-}
-
-// The same in two chain launches (b = 512, and few blocks), with the three R_j^T through
-// memory.
-int cnp_bwd_chain(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h, void *ws,
-                  hipStream_t s) {
-  Arena ar(ws);
-  SkewSegs un, pk;
-  un.src_bf16 = theta_bf16;
-  CnpChainArgs ca, cb;
-  ca.b = cb.b = (int)b;
-  ca.qlo = cb.qlo = !theta_bf16;
-  ca.mode = CNP_CHAIN_BWDA; ca.name = "cnp_bwd_chain_a";
-  cb.mode = CNP_CHAIN_BWDB; cb.name = "cnp_bwd_chain_b";
-  for (int i = 0; i < nside; ++i) {
-    const size_t blk = (size_t)side[i].n * b * b * 4;
-    un.src[i] = side[i].theta; un.n[i] = side[i].qsave ? 0 : side[i].n;
-    un.planes[i] = side[i].qsave ? (bf16_t *)side[i].qsave : (bf16_t *)ar.take(blk);
-    CnpChainSeg g;
-    g.qp = un.planes[i]; g.dg = side[i].dg; g.nblk = side[i].n;
-    for (int j = 0; j < 3; ++j) g.r[j] = (float *)ar.take(blk);
-    g.out = (float *)ar.take(blk);
-    ca.seg[i] = g;
-    cb.seg[i] = g;
-    pk.src[i] = g.out; pk.dst[i] = side[i].dtheta; pk.n[i] = side[i].n;
-  }
-  POETX_TRY(unpack_skew2(un, b, s));
-  // first half (rows of Gb P^l) for every block, then the transposed left-Horner half
-  POETX_TRY(cnp_chain(ca, s));
-  POETX_TRY(cnp_chain(cb, s));
+  POETX_TRY(cnp_bwd5(c, s));
   return pack_sides(pk, side, nside, b, theta_bf16, h, s);
 }
 
@@ -330,11 +297,7 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, c
   // takes the vector-ALU path
   bool vec = true;
   for (int i = 0; i < nside; ++i) vec = vec && al16(side[i].dg);
-  int64_t nz = 0;
-  for (int i = 0; i < nside; ++i) nz += side[i].n;
-  if (vec && cnp_bwd5_supported(b)) return cnp_bwd_fused_path(b, side, nside, theta_bf16, h, ws, s, true);
-  if (vec && cnp_bwd_fused_supported(b, nz)) return cnp_bwd_fused_path(b, side, nside, theta_bf16, h, ws, s, false);
-  if (vec && cnp_chain_supported(b)) return cnp_bwd_chain(b, side, nside, theta_bf16, h, ws, s);
+  if (vec && cnp_bwd5_supported(b)) return cnp_bwd5_path(b, side, nside, theta_bf16, h, ws, s);
   Arena ar(ws);
   struct Bufs { float *Q, *K1, *K2, *K3, *Ha, *Hb; } B[2] = {};
   SkewSegs un;
@@ -430,7 +393,7 @@ extern "C" int poetx_cnp(int32_t dir, int64_t nblocks, int64_t b, const void *th
     return dir == POETX_CNP_FWD ? fill_one(g, nblocks, g_dtype, s) : POETX_OK;
   }
   const int tb = theta_dtype == POETX_BF16;
-  if (!cnp_chain_supported(b)) qsave = nullptr;  // only the chain paths read the planes
+  if (!cnp_bwd5_supported(b)) qsave = nullptr;  // only the five-product backward reads the planes
   if (dir == POETX_CNP_FWD) return cnp_fwd_impl(nblocks, b, theta, tb, g, g_dtype, qsave, ws, s);
   CnpBwdSide sd;
   sd.n = nblocks; sd.theta = theta; sd.dg = (const float *)dg; sd.dtheta = dtheta; sd.qsave = qsave;
@@ -957,7 +920,7 @@ int backward_impl(const poetx_layer *L, int64_t n_tokens, const void *x, const v
   };
   CnpBwdSide sides[2];
   int ns = 0;
-  const bool qok = cnp_chain_supported(b);  // saved planes (full blocks only): chain paths
+  const bool qok = cnp_bwd5_supported(b);  // saved planes (full blocks only): five-product backward
   if (p.nr) {
     sides[ns] = side_at(true, p.nr, 0, gr);
     sides[ns++].qsave = qok ? L->q_r : nullptr;

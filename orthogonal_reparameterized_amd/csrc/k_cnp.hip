@@ -235,18 +235,15 @@ int cnp_mm(const CnpMMArgs &a, hipStream_t s) {
 
 
 // ================================================================ chains ====
-// Every product of the Cayley-Neumann steps can be written as X.Q with the same Q:
-//   forward   G = (((Q + 2I) Q + 2I) Q + 2I) Q + I                 (eq. 9, Horner in Q)
-//   backward  with P = Q^T = -Q, K_l = Gb P^l and R_j = sum_{l <= 3-j} a_{j+l+1} Gb P^l,
-//             Qbar = R0 + P (R1 + P (R2 + P Gb)), so
-//             Qbar^T = R0^T + (R1^T + (R2^T + Gb^T Q) Q) Q.
-// A row panel of X.Q needs only the same rows of X, so one workgroup runs a whole
-// chain on a 32-row panel, which stays in LDS as split planes.  Q never goes
-// through LDS: the unpack stores its bf16 planes in MFMA fragment order (see
-// cnp_frag_off), so each wave streams its own B fragments from L2 straight into
-// registers with 16-byte coalesced loads, several k steps ahead, and the waves
-// only meet at the end of each product, when the panel is replaced.  Only the
-// backward's first half has to finish for every row before the second starts.
+// The forward is a chain of products by the same Q,
+//   G = (((Q + 2I) Q + 2I) Q + 2I) Q + I                 (eq. 9, Horner in Q),
+// and a row panel of X.Q needs only the same rows of X, so one workgroup runs the whole
+// chain on a panel of rows, which stays in LDS as split planes.  Q never goes through LDS:
+// the unpack stores its bf16 planes in MFMA fragment order (see cnp_frag_off), so each
+// wave streams its own B fragments from L2 straight into registers with 16-byte
+// coalesced loads, several k steps ahead, and the waves only meet at the end of each
+// product, when the panel is replaced.  The backward (k_cnp_bwd5 below) is built the same
+// way.
 namespace {
 constexpr int CTK = 32, CNTH = 512;
 
@@ -301,7 +298,7 @@ __device__ inline void put_split4(bf16_t *h, bf16_t *lo, float4 v) {
 // QL: Q's planes carry a lo part.  With bf16 theta, Q is exact in bf16 (lo = 0): the lo
 // plane is neither written nor read and the pass with Q_lo is dropped, which changes nothing
 // but the work (two MFMA passes per product instead of three, half the Q bytes).
-template <int B, int MODE, int RP, int NW, bool QL>
+template <int B, int RP, int NW, bool QL>
 __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
   using C = ChainCfg<B, RP, NW>;
   constexpr int NPL = QL ? 2 : 1;  // Q planes streamed
@@ -348,50 +345,17 @@ __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
   for (int s = 0; s < C::D; ++s) fload(s, s % C::NK);
 
   // ---- start panel
-  f32x4 run[C::WM][C::WN];  // BWDA: running 2Gb + 2K1 + ... in accumulator layout
-  if constexpr (MODE == CNP_CHAIN_FWD) {
-    // X = Q[rows] + 2I: rows r0.. are k steps pnl * RP/32 .. of the fragment-ordered planes
-    for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += C::NTH) {
-      const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
-      const u32x4 v = (QL || !pl) ? *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8)
-                                  : u32x4{0u, 0u, 0u, 0u};
-      bf16_t *dst = (pl ? sAl : sAh) + (32 * ks + 8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
+  // X = Q[rows] + 2I: rows r0.. are k steps pnl * RP/32 .. of the fragment-ordered planes
+  for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += C::NTH) {
+    const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
+    const u32x4 v = (QL || !pl) ? *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8)
+                                : u32x4{0u, 0u, 0u, 0u};
+    bf16_t *dst = (pl ? sAl : sAh) + (32 * ks + 8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e * C::A_LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
-    }
-    __syncthreads();
-    if (tid < RP) sAh[tid * C::A_LD + r0 + tid] = 0x4000;  // bf16(2.0); Q has a zero diagonal
-  } else if constexpr (MODE == CNP_CHAIN_BWDA) {
-    const float *G = S.dg + off;
-    for (int q = tid; q < RP * B / 4; q += C::NTH) {
-      const int row = q / (B / 4), c4 = q % (B / 4);
-      const float4 v = *(const float4 *)(G + (int64_t)(r0 + row) * B + c4 * 4);
-      put_split4(sAh + row * C::A_LD + c4 * 4, sAl + row * C::A_LD + c4 * 4, v);
-    }
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j) {
-        const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
-        const float4 v = *(const float4 *)(G + (int64_t)(r0 + m) * B + n);
-        run[i][j] = f32x4{2.f * v.x, 2.f * v.y, 2.f * v.z, 2.f * v.w};
-      }
-  } else {
-    // X = Gb^T[rows]: X[m][k] = Gb[k][r0 + m]
-    const float *G = S.dg + off;
-    for (int q = tid; q < B * RP / 4; q += C::NTH) {
-      const int k = q / (RP / 4), c4 = q % (RP / 4);
-      const float4 v = *(const float4 *)(G + (int64_t)k * B + r0 + c4 * 4);
-      const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint16_t h, lo;
-        split2(e[t], h, lo);
-        sAh[(c4 * 4 + t) * C::A_LD + k] = h;
-        sAl[(c4 * 4 + t) * C::A_LD + k] = lo;
-      }
-    }
+    for (int e = 0; e < 8; ++e) dst[e * C::A_LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
   }
+  __syncthreads();
+  if (tid < RP) sAh[tid * C::A_LD + r0 + tid] = 0x4000;  // bf16(2.0); Q has a zero diagonal
   __syncthreads();
 
   f32x4 acc[C::WM][C::WN];
@@ -449,35 +413,18 @@ __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
           const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
           const int gm = r0 + m;  // row within the block
           f32x4 v = acc[i][j];
-          if constexpr (MODE == CNP_CHAIN_FWD) {
-            const float d = p < 2 ? 2.f : 1.f;
+          const float d = p < 2 ? 2.f : 1.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (gm == n + c) v[c] += d;
-            if (p == 2) {
-              const int64_t e = off + (int64_t)gm * B + n;
-              if (S.out) *(float4 *)(S.out + e) = make_float4(v[0], v[1], v[2], v[3]);
-              if (S.outb) {
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                *(uint2 *)(S.outb + e) = pk;
-              }
-            }
-          } else if constexpr (MODE == CNP_CHAIN_BWDA) {
-            v = -v;                    // K_{p+1} = -X Q
-            const f32x4 r = run[i][j] + v;
-            run[i][j] += 2.f * v;
-            float *R = S.r[p] + off;   // transposed store: R^T[n + c][gm]
-#pragma unroll
-            for (int c = 0; c < 4; ++c) R[(int64_t)(n + c) * B + gm] = r[c];
-          } else {
-            const float4 e = *(const float4 *)(S.r[p] + off + (int64_t)gm * B + n);
-            v[0] += e.x; v[1] += e.y; v[2] += e.z; v[3] += e.w;
-            if (p == 2) {
-              float *O = S.out + off;  // X^T = Qbar
-#pragma unroll
-              for (int c = 0; c < 4; ++c) O[(int64_t)(n + c) * B + gm] = v[c];
+          for (int c = 0; c < 4; ++c)
+            if (gm == n + c) v[c] += d;
+          if (p == 2) {
+            const int64_t e = off + (int64_t)gm * B + n;
+            if (S.out) *(float4 *)(S.out + e) = make_float4(v[0], v[1], v[2], v[3]);
+            if (S.outb) {
+              uint2 pk;
+              pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+              pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+              *(uint2 *)(S.outb + e) = pk;
             }
           }
           if (p < 2)
@@ -501,11 +448,9 @@ __global__ __launch_bounds__(64 * NW) void k_cnp_chain(CnpChainArgs a) {
   }
 }
 
-#define POETX_CHAIN_INST2(B, R, W, QL)                                             \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_FWD, R, W, QL>(CnpChainArgs);  \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDA, R, W, QL>(CnpChainArgs); \
-  template __global__ void k_cnp_chain<B, CNP_CHAIN_BWDB, R, W, QL>(CnpChainArgs);
-#define POETX_CHAIN_INST(B, R, W) POETX_CHAIN_INST2(B, R, W, true) POETX_CHAIN_INST2(B, R, W, false)
+#define POETX_CHAIN_INST(B, R, W)                                      \
+  template __global__ void k_cnp_chain<B, R, W, true>(CnpChainArgs);  \
+  template __global__ void k_cnp_chain<B, R, W, false>(CnpChainArgs);
 POETX_CHAIN_INST(64, 32, 8)
 POETX_CHAIN_INST(128, 32, 8)
 POETX_CHAIN_INST(256, 32, 8)
@@ -518,213 +463,6 @@ POETX_CHAIN_INST(512, 64, 8)
 POETX_CHAIN_INST(128, 128, 16)
 POETX_CHAIN_INST(256, 128, 16)
 #undef POETX_CHAIN_INST
-#undef POETX_CHAIN_INST2
-
-// ========================================================== fused backward ====
-// The adjoint of eq. 9 regrouped so that one workgroup finishes a row panel C of Qbar^T
-// alone.  With U_j = Q^j[C,:] (U_0 = I[C,:]) and W_0 = Gb^T[C,:]:
-//     W_j = W_{j-1} Q + U_j Gb^T   (j = 1, 2, 3),    Qbar^T[C,:] = W_3 + 2 (W_0 + W_1 + W_2)
-// (expanding gives sum_{i+j<=3} c_{i+j+1} U_j Gb^T Q^i, the adjoint of I + sum_k c_k Q^k with
-// c = 2, 2, 2, 1).  Phase j makes W_j and, for j < 3, U_{j+1} = U_j Q: the W and U panels
-// stay in LDS as split planes, both B operands (Q from the fragment-ordered planes, Gb^T
-// read as rows of Gb and split in registers) stream once per phase, and nothing between
-// the phases goes through memory.  Eight products, against six in the two chain launches
-// whose three intermediates R_j^T make a round trip through HBM.
-template <int B, int RP>
-struct FusedCfg {
-  static_assert(RP == 32 || RP == 64, "panel height");
-  static constexpr int NK = B / CTK;
-  static constexpr int NT = B / 16;
-  static constexpr int WM = B >= 128 ? RP / 16 : 1;
-  static constexpr int WN = B >= 128 ? B / 128 : 1;
-  static constexpr int D = RP == 64 ? 2 : 3;  // k steps of both B operands in flight
-  static constexpr int A_LD = B + 8;
-  static constexpr int NP = B / RP;
-};
-
-template <int B, int RP, bool QL>
-__global__ __launch_bounds__(CNTH) void k_cnp_bwd_fused(CnpChainArgs a) {
-  using C = FusedCfg<B, RP>;
-  constexpr int NPL = QL ? 2 : 1;  // Q planes streamed (see k_cnp_chain)
-  extern __shared__ __align__(16) bf16_t smem[];
-  bf16_t *sWh = smem, *sWl = smem + RP * C::A_LD;
-  bf16_t *sUh = smem + 2 * RP * C::A_LD, *sUl = smem + 3 * RP * C::A_LD;
-
-  // 1-D grid, all panels of one block on one XCD (workgroup L runs on XCD L % 8)
-  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk, nz8 = nz & ~(int64_t)7;
-  const int64_t L = blockIdx.x;
-  int64_t z, pnl;
-  if (L < nz8 * C::NP) {
-    const int64_t slot = L >> 3;
-    z = (L & 7) + 8 * (slot / C::NP);
-    pnl = slot % C::NP;
-  } else {
-    z = L / C::NP;
-    pnl = L % C::NP;
-  }
-  int sg = 0;
-  if (z >= a.seg[0].nblk) { z -= a.seg[0].nblk; sg = 1; }
-  const CnpChainSeg &S = a.seg[sg];
-  const int64_t off = z * (int64_t)B * B;
-  const int r0 = (int)pnl * RP;
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
-  const int mb = B >= 128 ? 0 : 16 * (wave >> 2);
-  const int nb = B >= 128 ? wave * (B / 8) : 16 * (wave & 3);
-
-  // ---- B operands.  Q: chunk (k, t, plane) of 1 KB holds what lane l needs for k step k
-  // and column tile t.  Gb^T: lane l needs Gb[16 t + l%16][32 k + 8 (l/16) + 0..7], 32
-  // contiguous bytes of a row of Gb.
-  const bf16_t *qf = S.qp + 2 * off;
-  const float *G = S.dg + off;
-  const __amdgpu_buffer_rsrc_t rq =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(qf), (short)0, 4 * B * B, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rg =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(G), (short)0, 4 * B * B, 0x00020000);
-  const int voff = l * 16 + (nb / 16) * 2048;
-  const int goff = ((nb + (l & 15)) * B + 8 * (l >> 4)) * 4;
-  u32x4 fq[C::D][C::WN][NPL], fg[C::D][C::WN][2];
-  auto fload = [&](int slot, int k) {
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) {
-#pragma unroll
-      for (int pl = 0; pl < NPL; ++pl)
-        fq[slot][j][pl] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff, (k * C::NT + j) * 2048 + pl * 1024, 0));
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        fg[slot][j][h] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, goff, (16 * j * B + k * CTK) * 4 + 16 * h, 0));
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < C::D; ++s) fload(s, s % C::NK);
-
-  // ---- start panels: U_1 = Q[rows] (k steps pnl * RP/32 .. of the planes), W_0 = Gb^T[rows]
-  for (int q = tid; q < (RP / 32) * C::NT * 2 * 64; q += CNTH) {
-    const int ln = q & 63, pl = (q >> 6) & 1, t = (q >> 7) % C::NT, ks = (q >> 7) / C::NT;
-    const u32x4 v = (QL || !pl) ? *(const u32x4 *)(qf + (((pnl * (RP / 32) + ks) * C::NT + t) * 2 + pl) * 512 + ln * 8)
-                                : u32x4{0u, 0u, 0u, 0u};
-    bf16_t *dst = (pl ? sUl : sUh) + (32 * ks + 8 * (ln >> 4)) * C::A_LD + 16 * t + (ln & 15);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dst[e * C::A_LD] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
-  }
-  for (int q = tid; q < B * RP / 4; q += CNTH) {  // W_0[m][k] = Gb[k][r0 + m]
-    const int k = q / (RP / 4), c4 = q % (RP / 4);
-    const float4 v = *(const float4 *)(G + (int64_t)k * B + r0 + c4 * 4);
-    const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint16_t h, lo;
-      split2(e[t], h, lo);
-      sWh[(c4 * 4 + t) * C::A_LD + k] = h;
-      sWl[(c4 * 4 + t) * C::A_LD + k] = lo;
-    }
-  }
-  // running 2 (W_0 + W_1 + ...) in accumulator layout, starting at 2 W_0
-  f32x4 run[C::WM][C::WN];
-#pragma unroll
-  for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) {
-      const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) run[i][j][c] = 2.f * G[(int64_t)(n + c) * B + r0 + m];
-    }
-  __syncthreads();
-
-  f32x4 accW[C::WM][C::WN], accU[C::WM][C::WN];
-#pragma unroll
-  for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) accW[i][j] = accU[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  constexpr int NS = 3 * C::NK;
-  auto step = [&](const int st, const int p) {
-    const int g = p * C::NK + st;
-    const int u = C::NK % C::D == 0 ? st % C::D : g % C::D;
-    bf16x8 qh[C::WN], ql[C::WN], gh[C::WN], gl[C::WN];
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) {
-      qh[j] = __builtin_bit_cast(bf16x8, fq[u][j][0]);
-      if constexpr (QL) ql[j] = __builtin_bit_cast(bf16x8, fq[u][j][NPL - 1]);
-      // whole vectors are reinterpreted, then indexed: a bit cast of one element of a
-      // vector (bit_cast(float, v[i])) reads element 0 whatever i is with this compiler
-      const f32x4 g0 = __builtin_bit_cast(f32x4, fg[u][j][0]), g1 = __builtin_bit_cast(f32x4, fg[u][j][1]);
-      u32x4 hv, lv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint32_t h, lo;
-        split_pk(e < 2 ? g0[2 * e] : g1[2 * e - 4], e < 2 ? g0[2 * e + 1] : g1[2 * e - 3], h, lo);
-        hv[e] = h;
-        lv[e] = lo;
-      }
-      gh[j] = __builtin_bit_cast(bf16x8, hv);
-      gl[j] = __builtin_bit_cast(bf16x8, lv);
-    }
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i) {
-      const bf16x8 wh = frag_a_ld(sWh, C::A_LD, mb + 16 * i, st * CTK);
-      const bf16x8 wl = frag_a_ld(sWl, C::A_LD, mb + 16 * i, st * CTK);
-      const bf16x8 uh = frag_a_ld(sUh, C::A_LD, mb + 16 * i, st * CTK);
-      const bf16x8 ul = frag_a_ld(sUl, C::A_LD, mb + 16 * i, st * CTK);
-      // operands swapped: lane l holds C[m = l%16][n = 4*(l/16) + 0..3]
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j) {
-        f32x4 w = accW[i][j];
-        if constexpr (QL) w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j], wh, w, 0, 0, 0);
-        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gl[j], uh, w, 0, 0, 0);
-        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], wl, w, 0, 0, 0);
-        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gh[j], ul, w, 0, 0, 0);
-        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], wh, w, 0, 0, 0);
-        w = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gh[j], uh, w, 0, 0, 0);
-        accW[i][j] = w;
-        if (p < 2) {
-          f32x4 v = accU[i][j];
-          if constexpr (QL) v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j], uh, v, 0, 0, 0);
-          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], ul, v, 0, 0, 0);
-          v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j], uh, v, 0, 0, 0);
-          accU[i][j] = v;
-        }
-      }
-    }
-    if (g + C::D < NS) fload(u, (st + C::D) % C::NK);  // refill the slot just consumed
-
-    if (st == C::NK - 1) {
-      // ---- end of phase p: every wave is done with both panels before they are replaced
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::WN; ++j) {
-          const int m = mb + 16 * i + (l & 15), n = nb + 16 * j + 4 * (l >> 4);
-          const f32x4 w = accW[i][j];
-          if (p < 2) {
-            run[i][j] += 2.f * w;
-            const f32x4 v = accU[i][j];
-            put_split4(sWh + m * C::A_LD + n, sWl + m * C::A_LD + n, make_float4(w[0], w[1], w[2], w[3]));
-            put_split4(sUh + m * C::A_LD + n, sUl + m * C::A_LD + n, make_float4(v[0], v[1], v[2], v[3]));
-          } else {
-            const f32x4 o = w + run[i][j];
-            float *O = S.out + off;  // Qbar^T[r0 + m][n + c] = Qbar[n + c][r0 + m]
-#pragma unroll
-            for (int c = 0; c < 4; ++c) O[(int64_t)(n + c) * B + r0 + m] = o[c];
-          }
-          accW[i][j] = accU[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      if (p < 2) __syncthreads();
-    }
-  };
-#pragma unroll
-  for (int p = 0; p < 3; ++p)
-#pragma unroll
-    for (int st = 0; st < C::NK; ++st) step(st, p);
-}
-template __global__ void k_cnp_bwd_fused<64, 32, true>(CnpChainArgs);
-template __global__ void k_cnp_bwd_fused<128, 64, true>(CnpChainArgs);
-template __global__ void k_cnp_bwd_fused<256, 64, true>(CnpChainArgs);
-template __global__ void k_cnp_bwd_fused<64, 32, false>(CnpChainArgs);
-template __global__ void k_cnp_bwd_fused<128, 64, false>(CnpChainArgs);
-template __global__ void k_cnp_bwd_fused<256, 64, false>(CnpChainArgs);
 
 // ===================================================== five-product backward ====
 // dtheta reads only the skew part D = Qbar - Qbar^T of the adjoint of eq. 9.  The adjoint
@@ -741,8 +479,10 @@ template __global__ void k_cnp_bwd_fused<256, 64, false>(CnpChainArgs);
 //   2   J[C] Q             (J[C] replaces Q[C] in LDS)
 //   3   F[C] Q             (F[C] replaces H[C]); E[C] = K[C] + F[C] Q is stored row-major.
 // The pack reads E as it reads Qbar (dtheta_rc = E_rc - E_cr).  Five products in four
-// passes over k against the eight of k_cnp_bwd_fused: 15 MFMAs per 16 x 16 tile and k step
-// instead of 24 (10 instead of 19 when Q is exact in bf16).
+// passes over k: 15 MFMAs per 16 x 16 tile and k step (10 when Q is exact in bf16).  A
+// regrouping that keeps Qbar itself needs eight (each row panel then also has to form
+// Q^j[C,:] for j = 2, 3), and two launches with the six products of Horner in Q send three
+// b x b intermediates through HBM.
 #ifndef POETX_BWD5_DG
 #define POETX_BWD5_DG 2
 #endif
@@ -900,7 +640,8 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd5(CnpChainArgs a) {
     bf16x8 hh[WN], hl[WN], kh[WN], kl[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      // whole vectors are reinterpreted, then indexed (see k_cnp_bwd_fused)
+      // whole vectors are reinterpreted, then indexed: a bit cast of one element of a
+      // vector (bit_cast(float, v[i])) reads element 0 whatever i is with this compiler
       const f32x4 g0 = __builtin_bit_cast(f32x4, grw[u][j][0]), g1 = __builtin_bit_cast(f32x4, grw[u][j][1]);
       u32x4 vh, vl, wh, wl;
 #pragma unroll
@@ -1061,16 +802,6 @@ POETX_BWD5_INST(512, 32)
 #define POETX_CHAIN512 1
 #endif
 bool cnp_chain_supported(int64_t b) { return b == 64 || b == 128 || b == 256 || (POETX_CHAIN512 && b == 512); }
-// The fused backward takes over once the blocks give 4 workgroups of 64-row panels per CU
-// (32-row at b = 64): below that its three phases in one workgroup are a longer chain of
-// dependent products than the two launches' three each (measured: 45 against 41 us at
-// 32 blocks of 256; 3.3 against 4.1 ms at 4096).
-bool cnp_bwd_fused_supported(int64_t b, int64_t nz) {
-  const int cus = device_cus() > 0 ? device_cus() : 256;
-  if (b == 64) return nz >= 4 * (int64_t)cus;
-  return (b == 128 || b == 256) && nz * (b / 64) >= 4 * (int64_t)cus;
-}
-
 namespace {
 template <int B, int RP, int NW = 8>
 int chain_run(const CnpChainArgs &a, hipStream_t s) {
@@ -1079,59 +810,16 @@ int chain_run(const CnpChainArgs &a, hipStream_t s) {
   const int64_t nwg = nz * C::NP;
   if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
   const size_t lds = (size_t)2 * RP * C::A_LD * sizeof(bf16_t);
-  static std::atomic<uint64_t> attr[6];  // dynamic LDS above 64 KB, per kernel and device
+  static std::atomic<uint64_t> attr[2];  // dynamic LDS above 64 KB, per kernel and device
   auto go = [&](void (*kern)(CnpChainArgs), int id) -> int {
     POETX_TRY(lds_limit((const void *)kern, lds, attr[id]));
     return launch_k(a.name, s, kern, dim3((unsigned)nwg), C::NTH, lds, a);
   };
-  const bool ql = a.qlo != 0;
-  switch (a.mode) {
-    case CNP_CHAIN_FWD:
-      return ql ? go(k_cnp_chain<B, CNP_CHAIN_FWD, RP, NW, true>, 0) : go(k_cnp_chain<B, CNP_CHAIN_FWD, RP, NW, false>, 3);
-    case CNP_CHAIN_BWDA:
-      return ql ? go(k_cnp_chain<B, CNP_CHAIN_BWDA, RP, NW, true>, 1) : go(k_cnp_chain<B, CNP_CHAIN_BWDA, RP, NW, false>, 4);
-    case CNP_CHAIN_BWDB:
-      return ql ? go(k_cnp_chain<B, CNP_CHAIN_BWDB, RP, NW, true>, 2) : go(k_cnp_chain<B, CNP_CHAIN_BWDB, RP, NW, false>, 5);
-    default: return POETX_ERR_INVALID_ARG;
-  }
+  return a.qlo ? go(k_cnp_chain<B, RP, NW, true>, 0) : go(k_cnp_chain<B, RP, NW, false>, 1);
 }
 }  // namespace
 
-namespace {
-template <int B, int RP>
-int fused_run(const CnpChainArgs &a, hipStream_t s) {
-  using C = FusedCfg<B, RP>;
-  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
-  const int64_t nwg = nz * C::NP;
-  if (nwg > 0x7fffffff) return POETX_ERR_UNSUPPORTED;
-  const size_t lds = (size_t)4 * RP * C::A_LD * sizeof(bf16_t);
-  static std::atomic<uint64_t> attr[2];  // dynamic LDS above 64 KB, per kernel and device
-  if (a.qlo) {
-    POETX_TRY(lds_limit((const void *)k_cnp_bwd_fused<B, RP, true>, lds, attr[0]));
-    return launch_k(a.name, s, k_cnp_bwd_fused<B, RP, true>, dim3((unsigned)nwg), CNTH, lds, a);
-  }
-  POETX_TRY(lds_limit((const void *)k_cnp_bwd_fused<B, RP, false>, lds, attr[1]));
-  return launch_k(a.name, s, k_cnp_bwd_fused<B, RP, false>, dim3((unsigned)nwg), CNTH, lds, a);
-}
-}  // namespace
-
-int cnp_bwd_fused(const CnpChainArgs &a, hipStream_t s) {
-  const int64_t nz = a.seg[0].nblk + a.seg[1].nblk;
-  if (nz <= 0) return POETX_OK;
-  switch (a.b) {
-    case 64: return fused_run<64, 32>(a, s);
-    case 128: return fused_run<128, 64>(a, s);
-    case 256: return fused_run<256, 64>(a, s);
-    default: return POETX_ERR_UNSUPPORTED;
-  }
-}
-
-// The five-product backward (k_cnp_bwd5) for every b of the chains; off, the fused
-// eight-product kernel or the two chain launches take the backward.
-#ifndef POETX_BWD5
-#define POETX_BWD5 1
-#endif
-bool cnp_bwd5_supported(int64_t b) { return POETX_BWD5 && (b == 64 || b == 128 || b == 256 || b == 512); }
+bool cnp_bwd5_supported(int64_t b) { return b == 64 || b == 128 || b == 256 || b == 512; }
 
 namespace {
 template <int B, int RP>

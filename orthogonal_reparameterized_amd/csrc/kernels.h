@@ -170,40 +170,27 @@ struct CnpMMArgs {
 int cnp_mm(const CnpMMArgs &a, hipStream_t s);
 
 // Row-panel chains of products by one b x b matrix Q per block (b in {64, 128, 256,
-// 512}), float32-accurate through split-bf16 MFMA, Q given as its bf16 planes
-// qp[n][2][b][b] (the unpack's planes layout).  One workgroup keeps a 32-row panel X of its block resident and runs
-// X <- X.Q three times; the mode fixes the start panel and what happens between
-// products (all matrices [n][b][b] row-major float32 unless noted):
-//   CNP_CHAIN_FWD : X = Q + 2I; X <- XQ + 2I; X <- XQ + 2I; G = XQ + I   -> g (f32 or bf16)
-//   CNP_CHAIN_BWDA: X = Gb; K_s = -XQ, X <- K_s; writes, transposed, r[0] = (2Gb + K1)^T,
-//                   r[1] = (2Gb + 2K1 + K2)^T, r[2] = (2Gb + 2K1 + 2K2 + K3)^T
-//   CNP_CHAIN_BWDB: X = Gb^T; X <- XQ + r[0]; X <- XQ + r[1]; X <- XQ + r[2]; writes X^T
-//                   (that is Qbar) -> out
-enum { CNP_CHAIN_FWD = 0, CNP_CHAIN_BWDA = 1, CNP_CHAIN_BWDB = 2 };
+// 512}), float32-accurate through split-bf16 MFMA, Q given as its hi and lo bf16 planes,
+// 2 b^2 values per block in MFMA fragment order (cnp_frag_off, the unpack's planes).
+//   cnp_chain (the forward): one workgroup keeps a panel X of rows of its block resident
+//     and runs X = Q + 2I; X <- XQ + 2I; X <- XQ + 2I; G = XQ + I -> out (f32) or outb (bf16)
+//   cnp_bwd5 (the backward): reads qp and dg (fp32 [b][b] row-major), writes to out a
+//     matrix E with E - E^T = Qbar - Qbar^T (all that dtheta needs), fp32 row-major.
 struct CnpChainSeg {
   const bf16_t *qp = nullptr;
   const float *dg = nullptr;
-  float *r[3] = {nullptr, nullptr, nullptr};
   float *out = nullptr;
   bf16_t *outb = nullptr;
   int64_t nblk = 0;
 };
 struct CnpChainArgs {
-  int b = 0, mode = CNP_CHAIN_FWD;
+  int b = 0;
   int qlo = 1;  // 0: Q's planes have no lo part (bf16 theta: Q is exact in bf16)
   CnpChainSeg seg[2];
   const char *name = "cnp_chain";
 };
 bool cnp_chain_supported(int64_t b);
 int cnp_chain(const CnpChainArgs &a, hipStream_t s);
-// The whole CNP backward of every block in one launch (mode unused): reads qp (Q's
-// planes) and dg, writes Qbar (fp32 [b][b]) to out; r unused.  b in {64, 128, 256}, and
-// taken for nz blocks in all (both segments) when cnp_bwd_fused_supported(b, nz).
-bool cnp_bwd_fused_supported(int64_t b, int64_t nz);
-int cnp_bwd_fused(const CnpChainArgs &a, hipStream_t s);
-// The CNP backward in five products (mode and r unused): reads qp and dg, writes to out a
-// matrix E with E - E^T = Qbar - Qbar^T (all that dtheta needs), fp32 [b][b] row-major.
-// b in {64, 128, 256, 512}.
 bool cnp_bwd5_supported(int64_t b);
 int cnp_bwd5(const CnpChainArgs &a, hipStream_t s);
 

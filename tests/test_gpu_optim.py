@@ -76,8 +76,8 @@ def test_cnp_bf16_theta(B, n, b):
 
 @pytest.mark.parametrize("n,b", [(600, 256), (1100, 64), (40, 128)])
 def test_cnp_bf16_theta_many_blocks(B, n, b):
-    """bf16 theta where the backward runs the fused kernel (600 blocks of 256, 1100 of 64) and
-    the 64-row chains' neighbour (40 blocks of 128: two chain launches).  With bf16 theta the
+    """bf16 theta where the row-panel kernels take many blocks (600 of 256 and 1100 of 64:
+    64- and 32-row panels) and few (40 of 128: 32-row panels).  With bf16 theta the
     kernels drop Q's lo plane and its MFMA pass (Q is exact in bf16); sampled blocks against
     the oracle, and the saved-Q backward bitwise equal to the one that unpacks theta."""
     theta, dg = WL.make_cnp_inputs(n, b, 0.02, seed=700 + b)

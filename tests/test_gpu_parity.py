@@ -45,16 +45,15 @@ def _say(*a):
 
 # ------------------------------------------------------------------- CNP ----
 
-# b = 64..512 run the row-panel chains (n = 11 and 19 also cover the blocks past the
-# last full group of 8 in the workgroup order), b = 192 the per-product MFMA path,
-# b = 32 and 48 the float32 vector-ALU path
+# b = 64..512 run the row-panel kernels (the forward chain, the five-product backward;
+# n = 11 and 19 also cover the blocks past the last full group of 8 in the workgroup order),
+# b = 192 the per-product MFMA path, b = 32 and 48 the float32 vector-ALU path
 CNP_CASES = [(8, 32, 0.02), (11, 64, 0.03), (19, 128, 0.02), (3, 192, 0.01), (3, 256, 0.01),
              (2, 512, 0.01), (2, 1024, 0.005),
              # enough blocks for the 64-row panels (4 workgroups per CU): 517 = 8 * 64 + 5
              # also leaves blocks past the last full group of 8
              (517, 128, 0.02), (256, 256, 0.01),
-             # enough blocks for the 128-row forward panels (b = 256) and the 64-row b = 512
-             # forward and second backward chains
+             # more blocks of 256 and 512 (several rounds of workgroups)
              (600, 256, 0.01), (40, 512, 0.01)]
 
 
@@ -122,10 +121,9 @@ def test_cnp_workload2_sampled(B):
     assert rel_fro_per_block(to_host_f64(d[torch.from_numpy(idx).cuda()]), ref_d) <= TOL_CNP_F32
 
 
-def test_layer_fused_cnp_backward_two_sides(B):
+def test_layer_cnp_backward_two_sides_one_launch(B):
     """A layer wide enough (32768 -> 32768, b = 256: 128 + 128 blocks) that its CNP backward
-    runs one launch over both sides (the five-product kernel; the fused eight-product one
-    when that is switched off).  The layer's dtheta on sampled
+    runs the five-product kernel over both sides in one launch of 64-row panels.  The layer's dtheta on sampled
     blocks of each side against the oracle's CNP backward of the dG the layer itself
     reports; W, x and dz are drawn on the GPU (their values do not enter the check)."""
     torch.manual_seed(11)
@@ -142,7 +140,7 @@ def test_layer_fused_cnp_backward_two_sides(B):
     L = B.Layer(w, tr, tp, g_r, g_p, b, act_dtype=torch.bfloat16, variant=B.POETX_FAST)
     x = torch.randn(n, d, device="cuda", dtype=torch.bfloat16)
     dz = torch.randn(n, d, device="cuda", dtype=torch.bfloat16)
-    _say("fused cnp backward, two sides: layer 32768 -> 32768")
+    _say("cnp backward, two sides in one launch: layer 32768 -> 32768")
     _, sb = B.poetx_forward(L, x)
     torch.cuda.synchronize()
     B.prof_read()
@@ -150,8 +148,7 @@ def test_layer_fused_cnp_backward_two_sides(B):
     out = B.poetx_backward(L, x, dz, sb, want_dg=True)
     torch.cuda.synchronize()
     B.prof_enable(False)
-    rec = B.prof_read()
-    assert "cnp_bwd5" in rec or "cnp_bwd_fused" in rec  # the one-launch backward this test is for
+    assert "cnp_bwd5" in B.prof_read()  # the launch this test is for
     idx = np.array([0, 1, 77, nb - 1])
     for th, key_g, key_t in ((th_r, "dg_r", "dtheta_r"), (th_p, "dg_p", "dtheta_p")):
         dg = out[key_g][torch.from_numpy(idx).cuda()].double().cpu().numpy()
@@ -164,8 +161,8 @@ def test_layer_fused_cnp_backward_two_sides(B):
 def test_cnp_saved_q_is_transparent(B, n, b):
     """poetx_cnp's qsave (Q's planes kept by the forward, read by the backward instead of
     unpacking theta again) changes nothing: G and dtheta are bitwise those of calls without
-    it, on the chain paths (40 blocks of 256: two backward launches; 600: the fused
-    backward; b = 64, 512), and where qsave is ignored (b = 96 and 48, which take the
+    it, on the row-panel paths (40 blocks of 256: 32-row panels; 600: 64-row panels;
+    b = 64, 512), and where qsave is ignored (b = 96 and 48, which take the
     per-product and the vector-ALU paths)."""
     _say(f"cnp saved Q n={n} b={b}")
     theta, dg = WL.make_cnp_inputs(n, b, 0.01, seed=900 + b)
