@@ -151,7 +151,8 @@ int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64
  * operand of the pages' fused kernel, which loads Q and Q^2 on chip.  Here it holds Q
  * itself, as the split-bf16 planes
  * in MFMA fragment order that the CNP kernels read (an internal layout, n * b * b * 4
- * bytes, 16-byte aligned); every higher power is recomputed inside the kernels.  FWD
+ * bytes, 16-byte aligned): the forward's chain and the backward's five products are all
+ * products by Q (or by the symmetric and skew parts of dG), so no power of Q is kept.  FWD
  * writes it; BWD with qsave reads Q from it instead of unpacking theta again, and theta
  * must then be the theta of the FWD call that wrote it.  Results are the same with or
  * without it.
