@@ -489,6 +489,9 @@ POETX_CHAIN_INST(256, 128, 16)
 #ifndef POETX_BWD5_DQ
 #define POETX_BWD5_DQ 4
 #endif
+#ifndef POETX_BWD5_ROLL256
+#define POETX_BWD5_ROLL256 0
+#endif
 template <int B, int RP>
 struct Bwd5Cfg {
   static_assert(RP == 32 || (RP == 64 && B >= 128 && B <= 256), "panel height");
@@ -509,6 +512,10 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd5(CnpChainArgs a) {
   using C = Bwd5Cfg<B, RP>;
   constexpr int NPL = QL ? 2 : 1;  // Q planes streamed (see k_cnp_chain)
   constexpr int NK = C::NK, WM = C::WM, WN = C::WN, DQ = C::DQ, DG = C::DG, LD = C::A_LD;
+  // ROLL: the k loops are rolled (one round of slots unrolled) instead of fully unrolled, so
+  // that the kernel's code fits the instruction cache (b = 512: 2600 instructions against
+  // 8900, 283 -> 263 us at workload 4)
+  constexpr bool ROLL = B >= 512 ? true : (B >= 256 && POETX_BWD5_ROLL256);
   extern __shared__ __align__(16) bf16_t smem[];
   // slot A: Q[C], then J[C]; slot B: H[C], then F[C] (hi and lo planes, RP rows each)
   bf16_t *sAh = smem, *sAl = smem + RP * LD;
@@ -632,11 +639,10 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd5(CnpChainArgs a) {
       acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  // ---- 1a: Q[C] H and Q[C] K; the first DQ k steps of Q go out over the last steps
+  // ---- 1a: Q[C] H and Q[C] K; the first DQ k steps of Q go out over the last steps (after
+  // 1a when its loop is rolled)
   constexpr int QS0 = NK >= DQ ? NK - DQ : 0;
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    const int u = kk % DG;
+  auto step1a = [&](const int kk, const int u) {
     bf16x8 hh[WN], hl[WN], kh[WN], kl[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
@@ -663,9 +669,11 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd5(CnpChainArgs a) {
       if constexpr (QL) ql[i] = frag_a_ld(sAl, LD, mb + 16 * i, kk * CTK);
     }
     if (kk + DG < NK) gload(u, kk + DG);
+    if constexpr (!ROLL) {
 #pragma unroll
-    for (int s = 0; s < DQ; ++s)
-      if (NK >= DQ ? kk == QS0 + s : kk == 0) qload(s, s % NK);
+      for (int s = 0; s < DQ; ++s)
+        if (NK >= DQ ? kk == QS0 + s : kk == 0) qload(s, s % NK);
+    }
     // operands swapped: lane l holds C[m = l%16][n = 4*(l/16) + 0..3]
 #pragma unroll
     for (int i = 0; i < WM; ++i)
@@ -690,13 +698,26 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd5(CnpChainArgs a) {
         accQH[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hh[j], qh[i], accQH[i][j], 0, 0, 0);
         accQK[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh[j], qh[i], accQK[i][j], 0, 0, 0);
       }
+  };
+  if constexpr (ROLL) {
+    // a loop over rounds of the DG slots (one k step per slot), each round unrolled
+    static_assert(NK % DG == 0 && NK % DQ == 0, "rolled loops need whole rounds of slots");
+    constexpr int U1 = DG == 1 ? 2 : DG;
+#pragma unroll 1
+    for (int kb = 0; kb < NK; kb += U1)
+#pragma unroll
+      for (int c = 0; c < U1; ++c) step1a(kb + c, c % DG);
+#pragma unroll
+    for (int s = 0; s < DQ; ++s) qload(s, s % NK);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) step1a(kk, kk % DG);
   }
 
   // ---- 1b, 2, 3: X Q for X = H[C], J[C], F[C], one k step at a time
   constexpr int NS = 3 * NK;
-  auto qstep = [&](const int st, const int p) {
+  auto qstep = [&](const int st, const int p, const int u) {
     const int g = p * NK + st;
-    const int u = NK % DQ == 0 ? st % DQ : g % DQ;
     const bf16_t *xh = p == 1 ? sAh : sBh, *xl = p == 1 ? sAl : sBl;
     bf16x8 ah[WM], al[WM], fbh[WN], fbl[WN];
 #pragma unroll
@@ -771,17 +792,19 @@ __global__ __launch_bounds__(CNTH) void k_cnp_bwd5(CnpChainArgs a) {
       }
     }
   };
-  if constexpr (B >= 512) {
-    static_assert(NK % DQ == 0, "slots must not depend on p");
+  if constexpr (ROLL) {
+    // slot u of k step st is st % DQ: the inner loop over one round of slots is unrolled
 #pragma unroll 1
     for (int p = 0; p < 3; ++p)
+#pragma unroll 1
+      for (int sb = 0; sb < NK; sb += DQ)
 #pragma unroll
-      for (int st = 0; st < NK; ++st) qstep(st, p);
+        for (int su = 0; su < DQ; ++su) qstep(sb + su, p, su);
   } else {
 #pragma unroll
     for (int p = 0; p < 3; ++p)
 #pragma unroll
-      for (int st = 0; st < NK; ++st) qstep(st, p);
+      for (int st = 0; st < NK; ++st) qstep(st, p, NK % DQ == 0 ? st % DQ : (p * NK + st) % DQ);
   }
 }
 #define POETX_BWD5_INST(B, R)                                              \
