@@ -27,6 +27,10 @@
 #define POETX_EPI_LDS 1
 #endif
 
+#ifndef POETX_NT_LATE
+#define POETX_NT_LATE 0
+#endif
+
 // Two-stage NT loop that frees a stage with a second barrier once it has been read and
 // issues the loads two k steps ahead there (off: 236 against 218 us per W' product at
 // workload 3 on one box).
@@ -172,6 +176,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   // wave has read it: a second barrier there lets the loads two steps ahead go out a step
   // sooner than the load of the next stage at the top of the step would
   constexpr bool EARLY = POETX_NT_EARLY && !BI8 && NST == 2 && ROLE == MFMA_GEMM_NT;
+  // LATE: the next stage's loads go out after this step's fragment reads instead of right
+  // after the barrier, so the reads do not queue behind them.  On for the block gradients
+  // (b = 512 at workload 4: 118 -> 106 us); measured flat for the W' products and 2.5 us
+  // slower for the batched block products, so off there.
+  constexpr bool LATE = !EARLY && !BI8 && (POETX_NT_LATE || ROLE == MFMA_BLOCK_GRAD);
   if constexpr (EARLY) {
     if (nk > 0) issue(0, kbeg);
     if (nk > 1) issue(1, kbeg + BKT);
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
       if (t + PF <= nk) wait_vmcnt<(PF - 1) * LPS>();
       else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // everyone's stage t is in LDS; stage t-1 is no longer read
-      if (t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
+      if (!LATE && t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
     }
     const int cur = t % NST;
     const bf16_t *ta = smem + cur * A_ELEMS, *tb = smem + NST * A_ELEMS + cur * B_ELEMS;
@@ -242,6 +251,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
       __syncthreads();  // every wave's reads of stage t have returned: its buffer takes stage t+2
       if (t + 2 < nk) issue(cur, kbeg + (int64_t)(t + 2) * BKT);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (LATE) {
+      if (t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
     }
 #pragma unroll
     for (int h = 0; h < KH; ++h)
