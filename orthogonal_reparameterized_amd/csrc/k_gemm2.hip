@@ -30,6 +30,11 @@
 #ifndef POETX_NT_LATE
 #define POETX_NT_LATE 0
 #endif
+// The k-contiguous products' fragment reads interleaved with their MFMAs (below; off: all
+// reads before the first MFMA).  W' product at workload 3: 206.5 -> 201.4 us.
+#ifndef POETX_NT_ILV
+#define POETX_NT_ILV 1
+#endif
 
 // Two-stage NT loop that frees a stage with a second barrier once it has been read and
 // issues the loads two k steps ahead there (off: 236 against 218 us per W' product at
@@ -232,21 +237,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
         }
       continue;
     }
-    // All fragments of the step are requested before the first MFMA (a scheduling
-    // barrier keeps the compiler from sinking the second half's reads into the MFMA
-    // chain), so LDS latency is paid once per step instead of once per fragment pair.
+    // Fragment reads.  ILV (k-contiguous tiles, two 32-deep halves): the B fragments and the
+    // first A fragment go out first, since the first MFMAs need them, then one read per MFMA
+    // until the whole step's fragments are in flight (scheduling groups below); otherwise all
+    // reads go out before the first MFMA, a scheduling barrier keeping the compiler from
+    // sinking them into the MFMA chain.
     constexpr int KH = BKT / 32;
+    constexpr bool ILV = POETX_NT_ILV && KH == 2 && !AKM && !BKM;
     bf16x8 fa[KH][FM], fb[KH][FN];
 #pragma unroll
     for (int h = 0; h < KH; ++h) {
+      if constexpr (ILV) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[h][j] = frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
         fa[h][i] = AKM ? frag_km<BM>(ta, wm + 16 * i, 32 * h) : frag_kc<BKT>(ta, wm + 16 * i, 32 * h);
+      if constexpr (!ILV) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[h][j] = BKM ? frag_km<BN>(tb, wn + 16 * j, 32 * h) : frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
+        for (int j = 0; j < FN; ++j)
+          fb[h][j] = BKM ? frag_km<BN>(tb, wn + 16 * j, 32 * h) : frag_kc<BKT>(tb, wn + 16 * j, 32 * h);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!ILV) __builtin_amdgcn_sched_barrier(0);
     if constexpr (EARLY) {
       __syncthreads();  // every wave's reads of stage t have returned: its buffer takes stage t+2
       if (t + 2 < nk) issue(cur, kbeg + (int64_t)(t + 2) * BKT);
@@ -263,6 +277,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
         for (int j = 0; j < FN; ++j)
           // operands swapped: lane l then holds C[m = l%16][n = 4*(l/16) + 0..3]
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h][j], fa[h][i], acc[i][j], 0, 0, 0);
+    if constexpr (ILV) {
+      // DS reads: FN + 1 first, then one after each MFMA; then the remaining MFMAs
+      constexpr int NR = KH * (FM + FN), NM = KH * FM * FN, FIRST = FN + 1;
+      __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
+#pragma unroll
+      for (int q = 0; q < NR - FIRST; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - FIRST), 0);
+    }
   }
 
   if constexpr (BM == 256 && BN == 256) {  // only the W' products split tiles
