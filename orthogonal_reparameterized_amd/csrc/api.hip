@@ -463,10 +463,12 @@ int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *
                  bool transposed, const float *scaleN, hipStream_t s, const void *Gt = nullptr) {
   if (p.N == 0 || nb == 0) return POETX_OK;
   const bool mfma = blk_mfma(p, bs);
+  if (mfma && block_stream_supported(bs, ld, nb, p.N))
+    return block_stream((const bf16_t *)X, (const bf16_t *)G, (bf16_t *)Y, p.N, ld, nb, bs, transposed, scaleN,
+                        transposed ? "block_apply_t" : "block_apply", s);
   if (mfma && bs == 512) {
-    // At b = 512 each block product is a K = N = 512 GEMM: the 256 x 256 W' kernels,
-    // batched over blocks, read X twice (two column tiles); a block kernel with a
-    // 64-column G slice in LDS read it once per slice and was L2-bound
+    // Shapes the streaming kernel does not take: each block product at b = 512 is a
+    // K = N = 512 GEMM on the 256 x 256 W' kernels, batched over blocks
     const bool kc = transposed || Gt;  // B k-contiguous: G^T of the blocks, or G itself for the transposed product
     MfmaDesc m;
     m.M = p.N; m.N = bs; m.K = bs; m.batch = nb;
@@ -478,9 +480,6 @@ int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *
     m.role = kc ? MFMA_GEMM_NT : MFMA_GEMM_NN;
     if (mfma2_supported(m)) return gemm_mfma2(m, s);
   }
-  if (mfma && block_stream_supported(bs, ld, nb, p.N))
-    return block_stream((const bf16_t *)X, (const bf16_t *)G, (bf16_t *)Y, p.N, ld, nb, bs, transposed, scaleN,
-                        transposed ? "block_apply_t" : "block_apply", s);
   if (mfma && bs % 128 == 0) {
     MfmaDesc m;
     m.M = p.N; m.N = bs; m.K = bs; m.batch = nb;
@@ -713,7 +712,10 @@ struct FwdBufs {
 };
 
 // b = 512 on the MFMA kernels: the plain block products read G^T k-contiguous
-bool wants_gt(const Plan &p) { return p.mfma && p.b == 512 && p.gdt == POETX_BF16; }
+// G^T copies serve the plain b = 512 products that the streaming kernel does not take
+bool wants_gt(const Plan &p, int64_t d, int64_t nb) {
+  return p.mfma && p.b == 512 && p.gdt == POETX_BF16 && !block_stream_supported(p.b, d, nb, p.N);
+}
 
 // G^T of a side's nb full blocks into gt; *out = gt, or null where there is no buffer or G
 // is not 16-byte aligned (the product then reads G n-major).
@@ -732,9 +734,9 @@ int transposed_g(const Plan &p, const void *g, void *gt, int64_t nb, hipStream_t
 void carve_fwd(Arena &ar, const Plan &p, const poetx_layer *L, bool want_b, void *saved_x, FwdBufs &f,
                bool fwd = true) {
   size_t xin = (size_t)p.N * p.din * p.ae, xout = (size_t)p.N * p.dout * p.ae;
-  if (wants_gt(p) && p.N > 0) {
-    if (p.nr && (fwd || p.mem)) f.gt_r = ar.take((size_t)p.nr * p.b * p.b * 2);
-    if (p.np && fwd) f.gt_p = ar.take((size_t)p.np * p.b * p.b * 2);
+  if (p.N > 0) {
+    if (p.nr && (fwd || p.mem) && wants_gt(p, p.din, p.nr)) f.gt_r = ar.take((size_t)p.nr * p.b * p.b * 2);
+    if (p.np && fwd && wants_gt(p, p.dout, p.np)) f.gt_p = ar.take((size_t)p.np * p.b * p.b * 2);
   }
   if (L->perm_in) f.xg = saved_x ? saved_x : ar.take(xin);
   f.a = ar.take(xin);

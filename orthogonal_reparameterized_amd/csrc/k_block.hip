@@ -168,6 +168,166 @@ template __global__ void k_block_reg<128, 64, 4, true>(BSArgs);
 template __global__ void k_block_reg<256, 32, 7, false, 8>(BSArgs);
 template __global__ void k_block_reg<256, 32, 7, true, 8>(BSArgs);
 
+// b = 512: a block's G (512 KB) is more than the registers of one CU hold, so a workgroup covers
+// one 256-column half of block j's output.  Its eight waves keep that half of G_j (or G_j^T)
+// as MFMA operand fragments in registers, 512 x 32 each (128 VGPRs), and issue their own
+// direct-to-LDS loads of T-token tiles of X_j (all 512 input columns) into an NST-stage
+// ring.  The two halves of a block read the same token tiles in the same order on the
+// same XCD (workgroups u and u ^ 8), so the second read of a tile is an L2 hit and X is
+// read from HBM about once.  G's half is staged through LDS in two k halves at the start.
+template <int T, int NST, bool TRANS>
+__global__ __launch_bounds__(512) void k_block_half512(BSArgs a) {
+  constexpr int B = 512, CS = 256, NW = 8, KH = 256;
+  constexpr int NTW = CS / (16 * NW), NKS = B / 32, FM = T / 16;
+  constexpr int A_ELEMS = T * B;
+  constexpr int OW = CS / NW, OCH = OW / 8, O_ELEMS = T * OW;
+  static_assert(NTW == 2 && NKS % 2 == 0, "wave layout");
+  extern __shared__ __align__(16) bf16_t smem[];
+  // workgroup u: half = bit 3, (token partition, block) from the other bits
+  const int u = blockIdx.x;
+  const int half = (u >> 3) & 1, q = (u & 7) | ((u >> 4) << 3);
+  if (q >= a.nb * a.P) return;
+  const int p = q / a.nb, j = q % a.nb;
+  const int64_t ntile = (a.N + T - 1) / T;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int c0 = half * CS, n0 = wave * OW;  // the half's first column; the wave's within it
+
+  // ---- this wave's 32 columns of the half, all 512 k, into registers (two k halves)
+  bf16x8 gf[NTW][NKS];
+  {
+    const bf16_t *Gj = a.G + (int64_t)j * B * B;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gj, (int64_t)B * B * 2);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      if constexpr (TRANS) {
+        LoaderKC<CS, NW, KH> lg;  // rows n of G_j (k contiguous): G_j^T fragments via frag_kc
+        lg.init(B, c0);
+        lg.issue(rg, kh * KH, B, smem);
+      } else {
+        LoaderKM<CS, NW, KH> lg;  // rows k of G_j, the half's columns: G_j fragments via frag_km
+        lg.init(B, c0);
+        lg.issue(rg, kh * KH, B, smem);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int s = 0; s < NKS / 2; ++s)
+          gf[t][kh * (NKS / 2) + s] = TRANS ? frag_kc<KH>(smem, n0 + 16 * t, 32 * s) : frag_km<CS>(smem, n0 + 16 * t, 32 * s);
+      __syncthreads();  // the next k half (or the ring) may now overwrite the staging
+    }
+  }
+
+  using LXT = LoaderKC<T, NW, B>;
+  constexpr int LX = LXT::INSTR;
+  LXT lx;
+  const bf16_t *Xj = a.X + (int64_t)j * B;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(Xj, a.N * a.d * 2);
+  lx.init(a.d, 0);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) {
+    const int64_t tl = p + (int64_t)s * a.P;
+    if (tl < ntile) lx.issue(rx, tl * T * a.d, a.d, smem + s * A_ELEMS);
+  }
+  bf16_t *so = smem + NST * A_ELEMS + wave * O_ELEMS;
+  int64_t tile = p;
+  for (int it = 0; tile < ntile; ++it, tile += a.P) {
+    // tiles it+1 .. it+NST-2 may still be in flight behind tile it (loads complete in order;
+    // the epilogue's stores, also counted, only make the wait longer)
+    const int64_t later = (ntile - 1 - tile) / a.P;
+    wait_tiles<LX, NST - 2>((int)(later < NST - 2 ? later : NST - 2));
+    __syncthreads();  // every wave's share of tile it is in LDS; tile it-1's stage is free
+    const int64_t nx = tile + (int64_t)(NST - 1) * a.P;
+    if (nx < ntile) lx.issue(rx, nx * T * a.d, a.d, smem + ((it + NST - 1) % NST) * A_ELEMS);
+    const bf16_t *ta = smem + (it % NST) * A_ELEMS;
+    f32x4 acc[FM][NTW];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fa[2][2][FM];
+    auto read_pair = [&](int qq, int s2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[qq][h][i] = frag_kc<B>(ta, 16 * i, 32 * (s2 + h));
+    };
+    read_pair(0, 0);
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; s2 += 2) {
+      const int qq = (s2 / 2) & 1;
+      if (s2 + 2 < NKS) read_pair(qq ^ 1, s2 + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int t = 0; t < NTW; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[t][s2 + h], fa[qq][h][i], acc[i][t], 0, 0, 0);
+    }
+    // epilogue as in k_block_reg: lane holds Y[m = l%16][n = 4*(l/16) + 0..3] of each patch;
+    // the wave's T x 32 tile is restaged (chunks XOR-swizzled by row) and leaves 16 bytes per lane
+    const int64_t col0 = (int64_t)j * B + c0 + n0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int row = 16 * i + (l & 15), col = 16 * t + 4 * (l >> 4);
+        f32x4 v = acc[i][t];
+        if (a.scaleN) {
+          float4 sc = *(const float4 *)(a.scaleN + col0 + col);
+          v[0] *= sc.x; v[1] *= sc.y; v[2] *= sc.z; v[3] *= sc.w;
+        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        const int pch = (col >> 3) ^ (row & (OCH - 1));
+        *(uint2 *)(so + row * OW + pch * 8 + (col & 7)) = pk;
+      }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < T * OCH / 64; ++k) {
+      const int qr = l + 64 * k, row = qr / OCH, c = qr % OCH;
+      const int64_t m = tile * T + row;
+      const uint4 v = *(const uint4 *)(so + row * OW + ((c ^ (row & (OCH - 1))) * 8));
+      if (m < a.N) *(uint4 *)(a.Y + m * a.d + col0 + c * 8) = v;
+    }
+    __builtin_amdgcn_wave_barrier();  // the staging rows are rewritten next iteration
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
+}
+// 32-token tiles and a 4-stage ring (144 KB of LDS with the output staging): at workload 4's
+// P side (28 blocks, 8192 tokens) 142 us, against 179 us with 16-token tiles and 6 stages
+// and 163 us for the batched 256 x 256 GEMM tiles
+#ifndef POETX_H512_T
+#define POETX_H512_T 32
+#endif
+#ifndef POETX_H512_NST
+#define POETX_H512_NST 4
+#endif
+template __global__ void k_block_half512<POETX_H512_T, POETX_H512_NST, false>(BSArgs);
+template __global__ void k_block_half512<POETX_H512_T, POETX_H512_NST, true>(BSArgs);
+
+template <bool TRANS>
+static int run_h512(BSArgs a, const char *name, hipStream_t s) {
+  constexpr int T = POETX_H512_T, NST = POETX_H512_NST;
+  const size_t ring = (size_t)NST * T * 512 * 2 + (size_t)8 * T * 32 * 2, stage_g = (size_t)256 * 256 * 2;
+  const size_t lds = ring > stage_g ? ring : stage_g;
+  static std::atomic<uint64_t> attr{0};
+  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_block_half512<T, NST, TRANS>), lds, attr));
+  // one workgroup per CU: (token partition, block) pairs times two halves, in groups of 16
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const int64_t ntile = (a.N + T - 1) / T;
+  int64_t P = cus / (2 * a.nb);
+  if (P > ntile) P = ntile;
+  a.P = (int)(P < 1 ? 1 : P);
+  const int64_t q = (int64_t)a.nb * a.P;
+  const dim3 grid((unsigned)(16 * ((q + 7) / 8)));
+  return launch_k(name, s, k_block_half512<T, NST, TRANS>, grid, 512, lds, a);
+}
+
 template <int B, int T, int NST, bool TRANS, int NCW = 4>
 static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
   const size_t lds = (size_t)(NST + 1) * T * B * 2;  // ring + NCW output staging tiles
@@ -178,7 +338,7 @@ static int run_br(const BSArgs &a, const char *name, hipStream_t s) {
 }
 
 bool block_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens) {
-  if (b != 64 && b != 128 && b != 256) return false;
+  if (b != 64 && b != 128 && b != 256 && b != 512) return false;
   if (nb < 1 || nb * b > ld || ld % 8) return false;
   return (n_tokens + 64) * ld * 2 < 0x7fffffff;
 }
@@ -190,6 +350,7 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
   BSArgs a;
   a.N = n_tokens; a.d = ld; a.nb = (int)nb;
   a.X = X; a.G = G; a.Y = Y; a.scaleN = scaleN;
+  if (b == 512) return transposed ? run_h512<true>(a, name, s) : run_h512<false>(a, name, s);
   const int cus = device_cus() > 0 ? device_cus() : 256;
   if (b == 64 || b == 128 || b == 256) {
     // one workgroup per (token partition, block), about one per CU in total

@@ -125,7 +125,8 @@ bool mfma2_supported(const MfmaDesc &d);
 size_t gemm_tail_ws_bytes(int64_t M, int64_t N, int64_t K);  // 0: no tile would be split
 int device_cus();  // compute units of the current device, 0 if unknown
 int gemm_mfma2(const MfmaDesc &d, hipStream_t s);   // direct-to-LDS kernel (bf16 operands)
-// Streaming block-diagonal product over the first nb blocks (b in {64, 128, 256}; G in registers):
+// Streaming block-diagonal product over the first nb blocks (b in {64, 128, 256, 512}; G in
+// registers, at b = 512 one 256-column half of a block per workgroup):
 //   Y[:, jb:(j+1)b] = X[:, jb:(j+1)b] . G[j]  (transposed: . G[j]^T), times scaleN[col],
 // j < nb.  X, Y token-major with row stride ld (>= nb*b, a multiple of 8) bf16,
 // G [nb][b][b] bf16.
