@@ -71,9 +71,8 @@ struct TileSel {
   int L, tail, part;
   int64_t kbeg, kend;
 };
-__device__ inline TileSel select_tile(const G2Args &a, int64_t kz) {
+__device__ inline TileSel select_tile(const G2Args &a, int64_t kz, int L) {
   TileSel t;
-  int L = blockIdx.x;
   if (L >= a.full_tiles) {
     const int u = L - a.full_tiles;
     t.tail = u / a.tail_splits;
@@ -90,6 +89,22 @@ __device__ inline TileSel select_tile(const G2Args &a, int64_t kz) {
     t.kend = t.kbeg + a.Kc < a.K ? t.kbeg + a.Kc : a.K;
   }
   return t;
+}
+
+// (tile, batch/split entry) of this workgroup.  Workgroups go to the XCDs round-robin in
+// linear order (x fastest).  A batched launch with fewer than 8 whole tiles per entry (the
+// b = 512 block gradients: 2 x 2 tiles of 256 per block and token part) would put the tiles
+// of one entry, which share their operand panels, on different XCDs; they are instead
+// placed on one XCD, so a panel's second read is an L2 hit.
+__device__ inline void batch_coords(const G2Args &a, int &bx, int64_t &bz) {
+  bx = blockIdx.x;
+  bz = blockIdx.z;
+  const int ft = (int)gridDim.x;
+  if (a.full_tiles == ft && ft < 8 && gridDim.y == 1 && gridDim.z % 8 == 0) {
+    const int64_t lin = blockIdx.x + (int64_t)ft * blockIdx.z, slot = lin / 8;
+    bz = lin % 8 + 8 * (slot / ft);
+    bx = (int)(slot % ft);
+  }
 }
 
 // (m, n) tile of tile-order index L: groups of 4 m-tiles sweep over n, so the
@@ -139,8 +154,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   // stage s: A tile at smem + s*A_ELEMS, B tile at smem + NST*A_ELEMS + s*B_ELEMS
 
   // ---- tile mapping: batch/split in z; (m, n) from an XCD-aware order of blockIdx.x
-  const int64_t z = blockIdx.z, bidx = z / a.splits, kz = z % a.splits;
-  const TileSel sel = select_tile(a, kz);
+  int bx;
+  int64_t z;
+  batch_coords(a, bx, z);
+  const int64_t bidx = z / a.splits, kz = z % a.splits;
+  const TileSel sel = select_tile(a, kz, bx);
   int tm, tn;
   tile_coords(a, sel.L, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -382,7 +400,7 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
   extern __shared__ __align__(16) bf16_t smem[];
 
   const int64_t z = blockIdx.z, bidx = z / a.splits, kz = z % a.splits;
-  const TileSel sel = select_tile(a, kz);
+  const TileSel sel = select_tile(a, kz, (int)blockIdx.x);
   int tm, tn;
   tile_coords(a, sel.L, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -556,7 +574,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void k_gemm4(G2Args a) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;  // 32 x 32 tiles per wave
   extern __shared__ __align__(16) bf16_t smem[];
 
-  const TileSel sel = select_tile(a, 0);
+  const TileSel sel = select_tile(a, 0, (int)blockIdx.x);
   int tm, tn;
   tile_coords(a, sel.L, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
