@@ -101,9 +101,9 @@ __device__ inline void batch_coords(const G2Args &a, int &bx, int64_t &bz) {
   bz = blockIdx.z;
   const int ft = (int)gridDim.x;
   if (a.full_tiles == ft && ft < 8 && gridDim.y == 1 && gridDim.z % 8 == 0) {
-    const int64_t lin = blockIdx.x + (int64_t)ft * blockIdx.z, slot = lin / 8;
-    bz = lin % 8 + 8 * (slot / ft);
-    bx = (int)(slot % ft);
+    const int lin = (int)blockIdx.x + ft * (int)blockIdx.z, slot = lin >> 3;
+    bz = __builtin_amdgcn_readfirstlane((lin & 7) + 8 * (slot / ft));
+    bx = __builtin_amdgcn_readfirstlane(slot % ft);
   }
 }
 
@@ -157,7 +157,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   int bx;
   int64_t z;
   batch_coords(a, bx, z);
-  const int64_t bidx = z / a.splits, kz = z % a.splits;
+  // batch entry and k split as wave-uniform 32-bit values (a 64-bit division is expanded
+  // into vector code, and operand bases derived from it would count as divergent)
+  const int64_t bidx = __builtin_amdgcn_readfirstlane((int)z / a.splits),
+                kz = __builtin_amdgcn_readfirstlane((int)z % a.splits);
   const TileSel sel = select_tile(a, kz, bx);
   int tm, tn;
   tile_coords(a, sel.L, tm, tn);

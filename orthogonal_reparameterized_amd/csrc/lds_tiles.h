@@ -69,8 +69,10 @@ struct LoaderKC {
   }
   // k0 is added to the per-lane offset: the raw-buffer range check covers only the
   // lane offset (not soffset), and rows past the valid extent must read as zero.
+  // the wave index through readfirstlane: the LDS destination (M0) is then known to be
+  // uniform, and no operand of the loads needs a waterfall loop
   __device__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t k0, int64_t ld, bf16_t *tile) const {
-    const int w = (threadIdx.x >> 6) - WOFF;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) - WOFF;
     const int kb = (int)(k0 * 2);
 #pragma unroll
     for (int i = 0; i < INSTR; ++i)
@@ -117,7 +119,7 @@ struct LoaderKM {
     }
   }
   __device__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t k0, int64_t ld, bf16_t *tile) const {
-    const int w = (threadIdx.x >> 6) - WOFF;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) - WOFF;
     const int kb = (int)(k0 * ld * 2);
 #pragma unroll
     for (int i = 0; i < INSTR; ++i)
