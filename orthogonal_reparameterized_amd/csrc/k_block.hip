@@ -85,12 +85,14 @@ __global__ __launch_bounds__(64 * (NCW + 2)) void k_block_reg(BSArgs a) {
     }
   }
   int64_t tile = p;
+  // this workgroup's tile count, once: the tiles after tile `it` are then cnt - 1 - it
+  const int cnt = tile < ntile ? (int)((ntile - 1 - tile) / a.P) + 1 : 0;
   for (int it = 0; tile < ntile; ++it, tile += a.P) {
     if (producer) {
       // tiles it .. it + NST - 2 may be in flight (loads complete in order): wait for
       // tile it only
-      const int64_t later = (ntile - 1 - tile) / a.P;
-      wait_tiles<LX, NST - 2>((int)(later < NST - 2 ? later : NST - 2));
+      const int later = cnt - 1 - it;
+      wait_tiles<LX, NST - 2>(later < NST - 2 ? later : NST - 2);
     }
     __syncthreads();  // tile it is in LDS; the stage read in iteration it-1 is free
     if (producer) {
@@ -232,11 +234,13 @@ __global__ __launch_bounds__(512) void k_block_half512(BSArgs a) {
   }
   bf16_t *so = smem + NST * A_ELEMS + wave * O_ELEMS;
   int64_t tile = p;
+  // this workgroup's tile count, once: the tiles after tile `it` are then cnt - 1 - it
+  const int cnt = tile < ntile ? (int)((ntile - 1 - tile) / a.P) + 1 : 0;
   for (int it = 0; tile < ntile; ++it, tile += a.P) {
     // tiles it+1 .. it+NST-2 may still be in flight behind tile it (loads complete in order;
     // the epilogue's stores, also counted, only make the wait longer)
-    const int64_t later = (ntile - 1 - tile) / a.P;
-    wait_tiles<LX, NST - 2>((int)(later < NST - 2 ? later : NST - 2));
+    const int later = cnt - 1 - it;
+    wait_tiles<LX, NST - 2>(later < NST - 2 ? later : NST - 2);
     __syncthreads();  // every wave's share of tile it is in LDS; tile it-1's stage is free
     const int64_t nx = tile + (int64_t)(NST - 1) * a.P;
     if (nx < ntile) lx.issue(rx, nx * T * a.d, a.d, smem + ((it + NST - 1) % NST) * A_ELEMS);
@@ -423,12 +427,14 @@ __global__ __launch_bounds__(64 * (4 + NPW)) void k_block_grad_stream(BGArgs a) 
     for (int jj = 0; jj < F; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   int64_t tile = p;
+  // this workgroup's tile count, once: the tiles after tile `it` are then cnt - 1 - it
+  const int cnt = tile < ntile ? (int)((ntile - 1 - tile) / a.P) + 1 : 0;
   for (int it = 0; tile < ntile; ++it, tile += a.P) {
     if (producer) {
       // tiles it .. it + NST - 2 may be in flight (loads complete in order): wait for
       // tile it only
-      const int64_t later = (ntile - 1 - tile) / a.P;
-      wait_tiles<LPT, NST - 2>((int)(later < NST - 2 ? later : NST - 2));
+      const int later = cnt - 1 - it;
+      wait_tiles<LPT, NST - 2>(later < NST - 2 ? later : NST - 2);
     }
     __syncthreads();
     if (producer) {

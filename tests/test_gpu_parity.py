@@ -467,12 +467,16 @@ def test_layer_b1024(B, variant):
     _compare(st, out, ref, TOL_BF16, f"b=1024 {variant}")
 
 
-def test_layer_int8_small(B):
-    wl = WL.Workload(92, "small int8", 200, 512, 768, 256, "bf16", "i8", "bf16", 0.01, 512, variants=("mem",))
+@pytest.mark.parametrize("d_in,d_out,b", [(512, 768, 256), (1024, 1536, 512)])
+def test_layer_int8_small(B, d_in, d_out, b):
+    """int8 W' with per-row scales (mem).  The scales enter the backward's P-side block
+    product as per-column factors; at b = 512 that is the streaming half-block kernel (3
+    blocks: 42 of its 48 workgroups busy, a ragged last token tile)."""
+    wl = WL.Workload(92, "small int8", 200, d_in, d_out, b, "bf16", "i8", "bf16", 0.01, d_in, variants=("mem",))
     inp = WL.make_layer_inputs(wl)
     ref = oracle_layer(inp, wl)
     st, out = _run_step(wl, inp, "mem")
-    _compare(st, out, ref, TOL_BF16, "int8 small")
+    _compare(st, out, ref, TOL_BF16, f"int8 small b={b}")
 
 
 def test_int8_fast_rejected(B):
