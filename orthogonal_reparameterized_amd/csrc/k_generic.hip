@@ -151,16 +151,15 @@ __global__ __launch_bounds__(256) void k_permute_cols(const T *__restrict__ in, 
 // streamed with nontemporal loads and stores: the stores then leave no dirty lines in L2
 // whose write-back would compete with the next kernels (measured: the block gradient that
 // reads a gathered activation runs 42 -> 37 us at 8192 x 4096 bf16).
-// Requires cols % (16 / sizeof(T)) == 0 and cols / (16 / sizeof(T)) <= 4 * blockDim.
-// (512 threads, 2 rows per pass and about two workgroups per CU measured fastest:
-// 5.6 TB/s on a 8192 x 4096 bf16 gather.)
-template <typename T, int RB>
+// Requires cols % (16 / sizeof(T)) == 0 and cols / (16 / sizeof(T)) <= MAXC * blockDim.
+// (512 threads and about two workgroups per CU measured fastest; rows per pass and MAXC
+// are picked per row width below.)
+template <typename T, int RB, int MAXC>
 __global__ __launch_bounds__(512) void k_permute_cols_v(const T *__restrict__ in, T *__restrict__ out,
                                                         int64_t rows, int64_t cols,
                                                         const int32_t *__restrict__ rperm,
                                                         const int32_t *__restrict__ cperm, int scatter) {
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
-  constexpr int MAXC = 4;            // chunks per thread per row
   extern __shared__ __align__(16) unsigned char lds_raw[];
   T *buf = (T *)lds_raw;
   const int64_t nch = cols / V;
@@ -231,12 +230,35 @@ __global__ __launch_bounds__(512) void k_permute_cols_v(const T *__restrict__ in
   }
 }
 
+template <typename T, int RB, int MAXC>
+static int permute_rbm(const void *in, void *out, int64_t rows, int64_t cols, const int32_t *rperm,
+                       const int32_t *cperm, int sc, hipStream_t s) {
+  const size_t row_bytes = (size_t)cols * sizeof(T);
+  const unsigned grid = (unsigned)(cdiv(rows, RB) < 512 ? cdiv(rows, RB) : 512);
+  return launch_k("permute_cols", s, k_permute_cols_v<T, RB, MAXC>, grid, 512, row_bytes * RB, (const T *)in,
+                  (T *)out, rows, cols, rperm, cperm, sc);
+}
+
+// A thread's chunk slots per row (MAXC) sized to the row: at 4096 bf16 columns one slot
+// instead of four frees about half the registers (63 instead of 127 at 2 rows per pass), so
+// 4 rows per pass fit at 2 workgroups per CU: 25.7 -> 23.4 us per 8192 x 4096 bf16 pass
+// (2 rows per pass, and 256, 384 or 768 workgroups, were slower; 8 rows slower still).
+template <typename T, int RB>
+static int permute_rb(const void *in, void *out, int64_t rows, int64_t cols, const int32_t *rperm,
+                      const int32_t *cperm, int sc, hipStream_t s) {
+  const int64_t nch = cols / (16 / sizeof(T));
+  if (nch <= 512) return permute_rbm<T, RB, 1>(in, out, rows, cols, rperm, cperm, sc, s);
+  if (nch <= 1024) return permute_rbm<T, RB, 2>(in, out, rows, cols, rperm, cperm, sc, s);
+  return permute_rbm<T, RB, 4>(in, out, rows, cols, rperm, cperm, sc, s);
+}
+
+// 4 rows per pass where they fit the 64 KB of LDS a launch gets without an attribute, else 2
 template <typename T>
 static int permute_v(const void *in, void *out, int64_t rows, int64_t cols, const int32_t *rperm,
                      const int32_t *cperm, int sc, hipStream_t s) {
   const size_t row_bytes = (size_t)cols * sizeof(T);
-  const unsigned grid = (unsigned)(cdiv(rows, 2) < 512 ? cdiv(rows, 2) : 512);
-  return launch_k("permute_cols", s, k_permute_cols_v<T, 2>, grid, 512, row_bytes * 2, (const T *)in, (T *)out, rows, cols, rperm, cperm, sc);
+  if (row_bytes * 4 <= 65536) return permute_rb<T, 4>(in, out, rows, cols, rperm, cperm, sc, s);
+  return permute_rb<T, 2>(in, out, rows, cols, rperm, cperm, sc, s);
 }
 
 int permute_cols(const void *in, void *out, int64_t rows, int64_t cols, int esize,
