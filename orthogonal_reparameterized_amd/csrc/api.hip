@@ -602,26 +602,38 @@ struct GradParts {
   float *full = nullptr, *last = nullptr;
 };
 
+// A single partial (P = 1) is the gradient itself: it is written straight into dG and
+// takes no workspace.
 void carve_grad_parts(Arena &ar, const Plan &p, int64_t d, GradParts &g) {
   const int64_t b = p.b, nb = d / b, bl = d % b;
   g.P = grad_parts(p, d, nb, b);
-  g.full = (float *)ar.take((size_t)g.P * nb * b * b * 4);
+  g.full = g.P > 1 ? (float *)ar.take((size_t)g.P * nb * b * b * 4) : nullptr;
   g.Pl = bl ? grad_parts(p, d, 1, bl) : 1;
-  g.last = bl ? (float *)ar.take((size_t)g.Pl * bl * bl * 4) : nullptr;
+  g.last = bl && g.Pl > 1 ? (float *)ar.take((size_t)g.Pl * bl * bl * 4) : nullptr;
 }
 
-// dG of every block of a side into dg ([nb][b][b] then [bl][bl]), via the partials.
+// dG of every block of a side into dg ([nb][b][b] then [bl][bl]), via the partials when
+// there are several.
 int block_grad(const Plan &p, int64_t d, const void *X, const void *Y, const GradParts &gp, float *dg,
                hipStream_t s) {
   const int64_t b = p.b, nb = d / b, bl = d % b;
   if (nb) {
-    POETX_TRY(grad_blocks(p, d, nb, b, X, Y, gp.full, s));
-    POETX_TRY(reduce_parts(gp.full, dg, nb * b * b, gp.P, nb * b * b, s));
+    if (gp.P == 1) {
+      POETX_TRY(grad_blocks(p, d, nb, b, X, Y, dg, s));
+    } else {
+      POETX_TRY(grad_blocks(p, d, nb, b, X, Y, gp.full, s));
+      POETX_TRY(reduce_parts(gp.full, dg, nb * b * b, gp.P, nb * b * b, s));
+    }
   }
   if (bl) {
     const int64_t c = nb * b;
-    POETX_TRY(grad_blocks(p, d, 1, bl, col_off(p, X, c), col_off(p, Y, c), gp.last, s));
-    POETX_TRY(reduce_parts(gp.last, dg + nb * b * b, bl * bl, gp.Pl, bl * bl, s));
+    float *dgl = dg + nb * b * b;
+    if (gp.Pl == 1) {
+      POETX_TRY(grad_blocks(p, d, 1, bl, col_off(p, X, c), col_off(p, Y, c), dgl, s));
+    } else {
+      POETX_TRY(grad_blocks(p, d, 1, bl, col_off(p, X, c), col_off(p, Y, c), gp.last, s));
+      POETX_TRY(reduce_parts(gp.last, dgl, bl * bl, gp.Pl, bl * bl, s));
+    }
   }
   return POETX_OK;
 }

@@ -27,6 +27,11 @@ struct BSArgs {
 // G is staged once through the ring's LDS at the start.  Workgroup u covers block
 // j = u % nb and token tiles p, p + P, ... with p = u / nb, so the blocks of the
 // same token rows run side by side.
+// b = 256 block products: tokens per ring stage and ring stages
+#ifndef POETX_BR256_T
+#define POETX_BR256_T 32
+#define POETX_BR256_NST 7
+#endif
 template <int B, int T, int NST, bool TRANS, int NCW = 4>
 __global__ __launch_bounds__(64 * (NCW + 2)) void k_block_reg(BSArgs a) {
   constexpr int NPW = 2;
@@ -167,8 +172,8 @@ template __global__ void k_block_reg<64, 64, 4, false>(BSArgs);
 template __global__ void k_block_reg<64, 64, 4, true>(BSArgs);
 template __global__ void k_block_reg<128, 64, 4, false>(BSArgs);
 template __global__ void k_block_reg<128, 64, 4, true>(BSArgs);
-template __global__ void k_block_reg<256, 32, 7, false, 8>(BSArgs);
-template __global__ void k_block_reg<256, 32, 7, true, 8>(BSArgs);
+template __global__ void k_block_reg<256, POETX_BR256_T, POETX_BR256_NST, false, 8>(BSArgs);
+template __global__ void k_block_reg<256, POETX_BR256_T, POETX_BR256_NST, true, 8>(BSArgs);
 
 // b = 512: a block's G (512 KB) is more than the registers of one CU hold, so a workgroup covers
 // one 256-column half of block j's output.  Its eight waves keep that half of G_j (or G_j^T)
@@ -365,7 +370,8 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
     a.P = (int)(P < 1 ? 1 : P);
     if (b == 64) return transposed ? run_br<64, 64, 4, true>(a, name, s) : run_br<64, 64, 4, false>(a, name, s);
     if (b == 128) return transposed ? run_br<128, 64, 4, true>(a, name, s) : run_br<128, 64, 4, false>(a, name, s);
-    return transposed ? run_br<256, 32, 7, true, 8>(a, name, s) : run_br<256, 32, 7, false, 8>(a, name, s);
+    return transposed ? run_br<256, POETX_BR256_T, POETX_BR256_NST, true, 8>(a, name, s)
+                      : run_br<256, POETX_BR256_T, POETX_BR256_NST, false, 8>(a, name, s);
   }
   return POETX_ERR_UNSUPPORTED;
 }
@@ -374,20 +380,24 @@ int block_stream(const bf16_t *X, const bf16_t *G, bf16_t *Y, int64_t n_tokens, 
 // Streaming block gradient: parts[p][j][r][c] = sum over the token tiles t = p, p+P, ...
 // of Xs_j[t]^T dY_j[t], for every b x b block j (r indexes columns of Xs_j, c of dY_j).
 // Each workgroup owns one S x S slice (rs, cs) of one block's gradient, S = min(b, 128),
-// and keeps it in registers while T-token tiles of both operands stream through a 4-stage LDS ring
-// (two producer waves that only issue the global->LDS loads).  The P partials per block are summed later in
-// a fixed order.
+// and keeps it in registers while T-token tiles of both operands stream through an NST-stage
+// LDS ring (two producer waves that only issue the global->LDS loads).  The P partials per
+// block are summed later in a fixed order; with P = 1 the slices are the gradient itself.
+// The (b/S)^2 slices of a block run on one XCD, so that an operand column slice, which b/S
+// workgroups read, can come from HBM once.
 struct BGArgs {
   int64_t N, d;
   int nb, P;
   const bf16_t *Xs; const bf16_t *dY; float *parts;  // parts: [P][nb][b][b]
 };
 
-template <int B, int NST, int T, int NPW>
+template <int B, int S, int NST, int T, int NPW>
 __global__ __launch_bounds__(64 * (4 + NPW)) void k_block_grad_stream(BGArgs a) {
-  constexpr int NCW = 4, S = B < 128 ? B : 128, KH = T / 32;
+  static_assert(S == 64 || S == 128, "slice width");
+  static_assert(B % S == 0, "whole slices");
+  constexpr int NCW = 4, KH = T / 32;
   constexpr int NSL = (B / S) * (B / S);
-  constexpr int WT = S / 2, F = WT / 16;  // 2 x 2 waves of 64 x 64
+  constexpr int WT = S / 2, F = WT / 16;  // 2 x 2 waves of S/2 x S/2
   constexpr int TILE = T * S;             // elements per operand tile
   extern __shared__ __align__(16) bf16_t smem[];
 
@@ -474,11 +484,22 @@ __global__ __launch_bounds__(64 * (4 + NPW)) void k_block_grad_stream(BGArgs a) 
   __builtin_amdgcn_s_waitcnt(0);  // no load into LDS may outlive the workgroup
 }
 // ring of BG_NST stages of two BG_T-token operand tiles, BG_NPW producer waves
-constexpr int BG_NST = 4, BG_T = 64, BG_NPW = 2;
-template __global__ void k_block_grad_stream<64, BG_NST, BG_T, BG_NPW>(BGArgs);
-template __global__ void k_block_grad_stream<128, BG_NST, BG_T, BG_NPW>(BGArgs);
-template __global__ void k_block_grad_stream<256, BG_NST, BG_T, BG_NPW>(BGArgs);
-template __global__ void k_block_grad_stream<512, BG_NST, BG_T, BG_NPW>(BGArgs);
+#ifndef POETX_BG_NST
+#define POETX_BG_NST 4
+#endif
+#ifndef POETX_BG_T
+#define POETX_BG_T 64
+#endif
+#ifndef POETX_BG_NPW
+#define POETX_BG_NPW 2
+#endif
+constexpr int BG_NST = POETX_BG_NST, BG_T = POETX_BG_T, BG_NPW = POETX_BG_NPW;
+#define POETX_BG_INST(B, S) template __global__ void k_block_grad_stream<B, S, BG_NST, BG_T, BG_NPW>(BGArgs);
+POETX_BG_INST(64, 64)
+POETX_BG_INST(128, 128)
+POETX_BG_INST(256, 128)
+POETX_BG_INST(512, 128)
+#undef POETX_BG_INST
 
 template <int B>
 static int run_bg(const BGArgs &a, hipStream_t s) {
@@ -487,8 +508,8 @@ static int run_bg(const BGArgs &a, hipStream_t s) {
   const int64_t units = (int64_t)a.nb * a.P;
   dim3 grid((unsigned)(((units + 7) / 8) * 8 * NSL));
   static std::atomic<uint64_t> attr{0};
-  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_block_grad_stream<B, BG_NST, BG_T, BG_NPW>), lds, attr));
-  return launch_k("block_grad", s, k_block_grad_stream<B, BG_NST, BG_T, BG_NPW>, grid, 64 * (4 + BG_NPW), lds, a);
+  POETX_TRY(lds_limit(reinterpret_cast<const void *>(&k_block_grad_stream<B, S, BG_NST, BG_T, BG_NPW>), lds, attr));
+  return launch_k("block_grad", s, k_block_grad_stream<B, S, BG_NST, BG_T, BG_NPW>, grid, 64 * (4 + BG_NPW), lds, a);
 }
 
 bool block_grad_stream_supported(int64_t b, int64_t ld, int64_t nb, int64_t n_tokens) {
