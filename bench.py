@@ -821,7 +821,7 @@ def main():
     del inputs
     if not args.only_head:
         others = {}
-        for key in (4, 5, 6):
+        for key in (1, 4, 5, 6):
             if key != args.workload:
                 others[str(key)] = layer_summary(WL.WORKLOADS[key], max(5, args.steps // 2), 3)
         others["2"] = cnp_bench(WL.WORKLOADS[2], max(5, args.steps // 2), 2)

@@ -50,9 +50,11 @@
  *    last block of size d % b.  A side's theta holds the blocks' packed vectors one
  *    after another ([d/b][b(b-1)/2], then (d%b)(d%b-1)/2 values) and its G the
  *    blocks one after another ([d/b][b][b], then [d%b][d%b]).  A block of size 1 has
- *    no parameters and G = [1].  The MFMA kernels serve bf16 layers with b, d_in
- *    and d_out multiples of 128 (a last block of such a layer too); every other
- *    shape runs on the float32 vector-ALU product.
+ *    no parameters and G = [1].  Kernel paths: the W' products of a bf16 layer run
+ *    on MFMA when d_in and d_out are multiples of 128, or (bf16 weights) of 8; the
+ *    block products on MFMA for b = 64 or a multiple of 128 (a last block of such a
+ *    size too); every other shape, and every float32 layer, runs on the float32
+ *    vector-ALU product.
  */
 #ifndef POETX_H
 #define POETX_H

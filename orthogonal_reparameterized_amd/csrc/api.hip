@@ -166,8 +166,27 @@ GemmDesc with_terms(GemmDesc g, const float *D, float beta, float alpha) {
 
 bool cnp_use_mfma(int64_t b) { return b % 64 == 0; }
 
+// Block sizes between 64 and 512 that are not multiples of 64 have no MFMA kernels of
+// their own: their CNP runs on blocks of the next row-panel size (128, 256 or 512) with Q
+// embedded as diag(Q, 0), which gives diag(G, I), and dG as diag(dG, 0), whose packed
+// gradient restricted to Q's entries is Q's (a polynomial of a block-diagonal matrix is
+// block-diagonal).  0: no padding.
+int64_t cnp_pad_to(int64_t b) {
+  if (b <= 64 || b >= 512 || b % 64 == 0) return 0;
+  return b <= 128 ? 128 : b <= 256 ? 256 : 512;
+}
+
 size_t cnp_ws_bytes(int dir, int64_t n, int64_t b) {
   Arena ar(nullptr);
+  const int64_t bp = cnp_pad_to(b);
+  if (bp) {
+    const size_t pk = (size_t)n * (bp * (bp - 1) / 2) * 4, sq = (size_t)n * bp * bp * 4;
+    ar.take(pk);                                   // padded theta
+    ar.take(sq);                                   // padded G, or padded dG
+    if (dir == POETX_CNP_BWD) ar.take(pk);         // padded dtheta
+    ar.take(cnp_ws_bytes(dir, n, bp));
+    return ar.used;
+  }
   size_t blk = (size_t)n * b * b * 4;
   int bufs = dir == POETX_CNP_FWD ? 4 : 6;
   for (int i = 0; i < bufs; ++i) ar.take(blk);
@@ -180,6 +199,14 @@ bool al16(const void *q) { return ((uintptr_t)q & 15) == 0; }
 int cnp_fwd_impl(int64_t n, int64_t b, const void *theta, int theta_bf16, void *g, int g_dtype, void *qsave,
                  void *ws, hipStream_t s) {
   Arena ar(ws);
+  if (const int64_t bp = cnp_pad_to(b)) {
+    void *tp = ar.take((size_t)n * (bp * (bp - 1) / 2) * 4);
+    void *gp = ar.take((size_t)n * bp * bp * 4);
+    void *inner = ar.take(cnp_ws_bytes(POETX_CNP_FWD, n, bp));
+    POETX_TRY(cnp_pad(CNP_PAD_THETA, n, b, bp, theta_bf16 ? 2 : 4, theta, tp, s));
+    POETX_TRY(cnp_fwd_impl(n, bp, tp, theta_bf16, gp, g_dtype, nullptr, inner, s));
+    return cnp_pad(CNP_CUT_G, n, b, bp, g_dtype == POETX_F32 ? 4 : 2, gp, g, s);
+  }
   size_t blk = (size_t)n * b * b * 4;
   // the chain and MFMA paths store G with 8- and 16-byte stores; a G that is only
   // element-aligned takes the vector-ALU path
@@ -293,6 +320,26 @@ int cnp_bwd5_path(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, 
 
 int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h, void *ws,
                  hipStream_t s) {
+  if (const int64_t bp = h ? 0 : cnp_pad_to(b)) {
+    // padded blocks (the fused Adam update keeps the vector-ALU path below)
+    Arena ar(ws);
+    CnpBwdSide ps[2];
+    int64_t nall = 0;
+    for (int i = 0; i < nside; ++i) {
+      const int64_t n = side[i].n;
+      nall += n;
+      void *tp = ar.take((size_t)n * (bp * (bp - 1) / 2) * 4);
+      void *dgp = ar.take((size_t)n * bp * bp * 4);
+      void *dtp = ar.take((size_t)n * (bp * (bp - 1) / 2) * 4);
+      POETX_TRY(cnp_pad(CNP_PAD_THETA, n, b, bp, theta_bf16 ? 2 : 4, side[i].theta, tp, s));
+      POETX_TRY(cnp_pad(CNP_PAD_DG, n, b, bp, 4, side[i].dg, dgp, s));
+      ps[i].n = n; ps[i].theta = tp; ps[i].dg = (const float *)dgp; ps[i].dtheta = (float *)dtp;
+    }
+    POETX_TRY(cnp_bwd_impl(bp, ps, nside, theta_bf16, nullptr, ar.take(cnp_ws_bytes(POETX_CNP_BWD, nall, bp)), s));
+    for (int i = 0; i < nside; ++i)
+      POETX_TRY(cnp_pad(CNP_CUT_DTHETA, side[i].n, b, bp, 4, ps[i].dtheta, side[i].dtheta, s));
+    return POETX_OK;
+  }
   // the chain and MFMA paths read dG with vector loads: an only element-aligned dG
   // takes the vector-ALU path
   bool vec = true;
@@ -443,9 +490,12 @@ int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
   p.act = L->act_dtype; p.w = L->w_dtype; p.gdt = L->g_dtype;
   p.mem = L->variant == POETX_MEM;
   p.ae = dtype_size(p.act);
-  // the W' products run on MFMA whenever both widths tile by 128, whatever b is; each
-  // block product picks its own kernel by its block size (blk_mfma)
-  p.mfma = p.act == POETX_BF16 && p.din % 128 == 0 && p.dout % 128 == 0;
+  // the W' products run on MFMA whenever both widths tile by 128, whatever b is, and for
+  // bf16 weights whenever both are multiples of 8 (the NT kernel's tail form); each block
+  // product picks its own kernel by its block size (blk_mfma)
+  const bool tiles128 = p.din % 128 == 0 && p.dout % 128 == 0;
+  p.mfma = p.act == POETX_BF16 &&
+           (tiles128 || (p.w == POETX_BF16 && p.din % 8 == 0 && p.dout % 8 == 0));
   return POETX_OK;
 }
 
@@ -538,14 +588,16 @@ bool grad_engine(const Plan &p, int64_t bs) { return blk_mfma(p, bs) && bs % 128
 int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of the split-k kernel
   if (p.N == 0) return 1;
   if (!grad_engine(p, bs)) {
-    // vector-ALU product, one launch per chunk: chunks of 1024 tokens keep each float32
-    // accumulation short (a sum over millions of tokens in one chain loses digits), with
-    // at most 4096 partials and 256 MB of them
-    const int64_t part_bytes = nb * bs * bs * 4;
+    // vector-ALU product: chunks of 1024 tokens keep each float32 accumulation short (a sum
+    // over millions of tokens in one chain loses digits), with at most 4096 partials and
+    // 256 MB of them.  A single block (the last, smaller block of a side) runs all its
+    // chunks in one launch, 256 tokens each, so that its few output tiles are spread over
+    // many workgroups.
+    const int64_t part_bytes = nb * bs * bs * 4, kmin = nb == 1 ? 256 : 1024;
     int64_t pmax = ((int64_t)256 << 20) / (part_bytes > 0 ? part_bytes : 1);
     pmax = pmax < 1 ? 1 : pmax > 4096 ? 4096 : pmax;
     const int64_t kc = cdiv(p.N, pmax);
-    return p.N <= 1024 ? p.N : kc > 1024 ? kc : 1024;
+    return p.N <= kmin ? p.N : kc > kmin ? kc : kmin;
   }
   // about one round of workgroups: 256 x 256 tiles where b allows (fp32 partials of a
   // whole b x b per split, so no more splits than the CUs need)
@@ -581,9 +633,26 @@ int grad_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *X
     m.role = MFMA_BLOCK_GRAD;
     return gemm_mfma_best(m, s);
   }
-  // vector-ALU product, one launch per token chunk (a batch over the blocks) into
-  // partial c of [P][nb][bs][bs]
+  // vector-ALU product into partial c of [P][nb][bs][bs]: one launch per token chunk (a
+  // batch over the blocks), or for a single block one launch over its whole chunks (a
+  // batch over the chunks) and one for a shorter last chunk
   const int64_t kc = grad_chunk(p, nb, bs);
+  if (nb == 1 && p.N >= kc) {
+    const int64_t whole = p.N / kc;
+    GemmDesc g;
+    g.M = bs; g.N = bs; g.K = kc; g.batch = whole;
+    g.A = X; g.a_dt = p.act; g.sAb = kc * ld; g.sAm = 1; g.sAk = ld;
+    g.B = Y; g.b_dt = p.act; g.sBb = kc * ld; g.sBk = ld; g.sBn = 1;
+    g.C = parts; g.c_dt = POETX_F32; g.sCb = bs * bs; g.sCm = bs; g.sCn = 1;
+    g.name = "block_grad_generic";
+    POETX_TRY(gemm_generic(g, s));
+    if (whole * kc == p.N) return POETX_OK;
+    g.K = p.N - whole * kc; g.batch = 1;
+    g.A = col_off(p, X, whole * kc * ld);
+    g.B = col_off(p, Y, whole * kc * ld);
+    g.C = parts + whole * bs * bs;
+    return gemm_generic(g, s);
+  }
   for (int64_t c = 0, t0 = 0; t0 < p.N; ++c, t0 += kc) {
     GemmDesc g;
     g.M = bs; g.N = bs; g.K = p.N - t0 < kc ? p.N - t0 : kc; g.batch = nb;
@@ -670,9 +739,12 @@ int gemm_fwd(const Plan &p, const poetx_layer *L, const void *A, void *B, void *
 // Without a kept W'^T, the backward product still runs on the k-contiguous NT kernel when
 // that kernel tiles the shape: W' is transposed into the workspace first (one pass over
 // the weight, much less than what reading W' n-major costs the product).
+// Widths that the NT kernel tiles only in its tail form (bf16) always take this route: the
+// n-major kernels need whole tiles.
 bool bwd_transposes_w(const Plan &p, const poetx_layer *L) {
-  return p.mfma && p.N > 0 && !L->w_merged_t && (p.w == POETX_BF16 || p.w == POETX_I8) && p.din % 256 == 0 &&
-         p.dout % 64 == 0;
+  if (!p.mfma || p.N == 0 || L->w_merged_t) return false;
+  const bool tiles = p.din % 256 == 0 && p.dout % 64 == 0;
+  return p.w == POETX_BF16 ? tiles || p.din % 128 || p.dout % 128 : p.w == POETX_I8 && tiles;
 }
 
 // `wt`: workspace for W'^T when bwd_transposes_w, else null.

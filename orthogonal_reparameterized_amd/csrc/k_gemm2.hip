@@ -141,10 +141,16 @@ __device__ inline void tail_store(const f32x4 (&acc)[FM][FN], const G2Args &a, i
 // order, identically on both operands: lane group g (lanes 16g .. 16g+15) of the h-th
 // MFMA covers k = 16g + 8h + 0..7, so one 16-byte LDS read of a B row (k = 16g .. +15)
 // feeds both MFMAs of the step, and the A reads take bf16 chunk 2g + h.
+//
+// TAIL (k-contiguous bf16 operands): N need not be a multiple of BN nor K of BKT, only of 8.
+// The last n tile's columns past N are not stored (W' rows past N read as zero through the
+// buffer range), and the last k step's chunks past K, which the loads fill from the next
+// rows, are zeroed in LDS before they are read.
 template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32,
-          bool BI8 = false>
+          bool BI8 = false, bool TAIL = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   static_assert(!BI8 || (!AKM && !BKM && BKT == 64), "int8 B: k-contiguous operands, 64-deep steps");
+  static_assert(!TAIL || (!AKM && !BKM && !BI8), "tails: k-contiguous bf16 operands");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 16, FN = WTN / 16;
   constexpr int EB = BI8 ? 1 : 2;  // bytes per B element
@@ -227,6 +233,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
       else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // everyone's stage t is in LDS; stage t-1 is no longer read
       if (!LATE && t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
+      if constexpr (TAIL) {
+        const int kr = (int)(kend - kbeg - (int64_t)t * BKT);  // valid k of this step
+        if (kr < BKT) {
+          bf16_t *za = smem + (t % NST) * A_ELEMS, *zb = smem + NST * A_ELEMS + (t % NST) * B_ELEMS;
+          constexpr int CR = BKT / 8;
+          const int c0 = kr / 8;
+          for (int q = threadIdx.x; q < (BM + BN) * CR; q += 64 * NW) {
+            const int r = q / CR, c = q % CR;
+            if (c < c0) continue;
+            bf16_t *row = r < BM ? za + r * BKT : zb + (r - BM) * BKT;
+            const int rr = r < BM ? r : r - BM;
+            *(uint4 *)(row + (c ^ kc_key<BKT>(rr)) * 8) = make_uint4(0u, 0u, 0u, 0u);
+          }
+          __syncthreads();
+        }
+      }
     }
     const int cur = t % NST;
     const bf16_t *ta = smem + cur * A_ELEMS, *tb = smem + NST * A_ELEMS + cur * B_ELEMS;
@@ -351,7 +373,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
 #pragma unroll
       for (int r = threadIdx.x >> 5; r < BM; r += RPP) {
         const int64_t m = m0 + r;
-        if (m < a.M) *(uint4 *)(Cb + (m * a.ldc + n0 + ch * 8) * 2) = *(const uint4 *)(st + r * EPI_LD + ch * 16);
+        if (m < a.M && (!TAIL || n0 + ch * 8 < a.N))
+          *(uint4 *)(Cb + (m * a.ldc + n0 + ch * 8) * 2) = *(const uint4 *)(st + r * EPI_LD + ch * 16);
       }
       return;
     }
@@ -363,6 +386,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = n0 + wn + 16 * j + 4 * (l >> 4);
+      if (TAIL && n >= a.N) continue;
       f32x4 v = acc[i][j];
       if (a.scaleN) {
         float4 sc = *(const float4 *)(a.scaleN + bidx * a.sSNb + n);
@@ -525,7 +549,8 @@ __global__ __launch_bounds__(512) void k_gemm_pp(G2Args a) {
 #pragma unroll
       for (int r = threadIdx.x >> 5; r < BM; r += RPP) {
         const int64_t m = m0 + r;
-        if (m < a.M) *(uint4 *)(Cb + (m * a.ldc + n0 + ch * 8) * 2) = *(const uint4 *)(st + r * EPI_LD + ch * 16);
+        if (m < a.M)
+          *(uint4 *)(Cb + (m * a.ldc + n0 + ch * 8) * 2) = *(const uint4 *)(st + r * EPI_LD + ch * 16);
       }
       return;
     }
@@ -794,6 +819,7 @@ POETX_G2_INST(MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true)
 POETX_G2_INST(MFMA_BLOCK_GRAD, 256, 256, 2, 4, 64, 2, true, true)
 #undef POETX_G2_INST
 template __global__ void k_gemm2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, true>(G2Args);
+template __global__ void k_gemm2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, false, true>(G2Args);
 template __global__ void k_gemm4<POETX_G4_WGM, POETX_G4_WGN, POETX_G4_BK, POETX_G4_NST>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, true>(G2Args);
@@ -894,24 +920,27 @@ static int run_pp(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
 }
 
 template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32,
-          bool BI8 = false>
+          bool BI8 = false, bool TAIL = false>
 static int run2o(const G2Args &a, const char *name, dim3 grid, size_t lds, hipStream_t s) {
   constexpr int NT = 64 * WGM * WGN;
-  auto kern = &k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8>;
+  auto kern = &k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8, TAIL>;
   static std::atomic<uint64_t> attr{0};  // dynamic-LDS limit, per device
   POETX_TRY(lds_limit(reinterpret_cast<const void *>(kern), lds, attr));
-  return launch_k(name, s, k_gemm2<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, OUTF32, BI8>, grid, NT, lds, a);
+  return launch_k(name, s, kern, grid, NT, lds, a);
 }
 
-template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool BI8 = false>
+template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool BI8 = false,
+          bool TAIL = false>
 static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
   size_t lds = (size_t)NST * (BM * 2 + BN * (BI8 ? 1 : 2)) * BKT;
   if (BM == 256 && BN == 256 && POETX_EPI_LDS && lds < (size_t)BM * (BN * 2 + 16))
     lds = (size_t)BM * (BN * 2 + 16);  // the staged bf16 epilogue tile
-  if (d.M <= 0 || d.N % BN || d.K % BKT && (!AKM || !BKM)) return POETX_ERR_UNSUPPORTED;
+  if (TAIL ? (d.M <= 0 || d.N % 8 || d.K % 8 || d.batch != 1 || d.splits != 1)
+           : (d.M <= 0 || d.N % BN || (d.K % BKT && (!AKM || !BKM))))
+    return POETX_ERR_UNSUPPORTED;
   G2Args a = k;
   a.tiles_m = (int)cdiv(d.M, BM);
-  a.tiles_n = (int)(d.N / BN);
+  a.tiles_n = (int)(TAIL ? cdiv(d.N, BN) : d.N / BN);
   plan_tail(a, d, BM, BN);
   dim3 grid((unsigned)(a.full_tiles + (a.tiles_m * a.tiles_n - a.full_tiles) * a.tail_splits), 1,
             (unsigned)(d.batch * d.splits));
@@ -920,9 +949,14 @@ static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
     POETX_TRY((run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false, true>(a, d.name, grid, lds, s)));
     return tail_reduce(a, d, s);
   }
-  if (d.c_dt == POETX_F32) return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, true>(a, d.name, grid, lds, s);
-  POETX_TRY((run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false>(a, d.name, grid, lds, s)));
-  return tail_reduce(a, d, s);
+  if constexpr (TAIL) {  // bf16 results, whole-k tiles only (plan_tail splits none of these shapes)
+    if (d.c_dt != POETX_BF16 || a.full_tiles != a.tiles_m * a.tiles_n) return POETX_ERR_UNSUPPORTED;
+    return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false, false, true>(a, d.name, grid, lds, s);
+  } else {
+    if (d.c_dt == POETX_F32) return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, true>(a, d.name, grid, lds, s);
+    POETX_TRY((run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false>(a, d.name, grid, lds, s)));
+    return tail_reduce(a, d, s);
+  }
 }
 
 // The four-wave W' product: whole tiles only (a plan that splits leftover tiles along k
@@ -955,12 +989,21 @@ bool mfma2_supported(const MfmaDesc &d) {
   if (d.c_dt != POETX_BF16 && d.c_dt != POETX_F32) return false;
   if (d.splits < 1 || d.batch * d.splits > 65535) return false;
   if (d.splits > 1 && (d.kchunk <= 0 || d.kchunk % 64 || cdiv(d.K, d.kchunk) != d.splits)) return false;
-  if ((!d.a_km || !d.b_km) && d.K % 64) return false;
+  // W' products whose widths do not tile (multiples of 8): the TAIL form of the NT kernel
+  const bool tail = d.role == MFMA_GEMM_NT && !d.a_km && !d.b_km && (d.N % 256 || d.K % 64);
+  if (tail) {
+    if (d.b_dt != POETX_BF16 || d.c_dt != POETX_BF16 || d.batch != 1 || d.splits != 1) return false;
+    if (d.N % 8 || d.K % 8 || d.lda % 8 || d.ldb % 8 || d.ldc % 8) return false;
+    if ((((uintptr_t)d.A | (uintptr_t)d.B | (uintptr_t)d.C) & 15) != 0) return false;
+  } else if ((!d.a_km || !d.b_km) && d.K % 64) {
+    return false;
+  }
   // 32-bit buffer offsets, with room for the rows a last partial tile addresses
   const int64_t a_ext = ((d.a_km ? d.K : d.M) + 256) * d.lda * 2, b_ext = ((d.b_km ? d.K : d.N) + 256) * d.ldb * 2;
   if (a_ext > 0x7fffffff || b_ext > 0x7fffffff) return false;
   switch (d.role) {
-    case MFMA_GEMM_NT: case MFMA_GEMM_NN: return d.N % 256 == 0 && cdiv(d.M, 256) * (d.N / 256) < (1 << 30);
+    case MFMA_GEMM_NT: return (tail || d.N % 256 == 0) && cdiv(d.M, 256) * cdiv(d.N, 256) < (1 << 30);
+    case MFMA_GEMM_NN: return d.N % 256 == 0 && cdiv(d.M, 256) * (d.N / 256) < (1 << 30);
     default: return d.N % 128 == 0 && (!d.a_km || d.M % 128 == 0);
   }
 }
@@ -982,6 +1025,7 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s) {
     case MFMA_GEMM_NT:
       if (d.a_km || d.b_km) return POETX_ERR_UNSUPPORTED;
       if (i8) return run2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, true>(k, d, s);
+      if (d.N % 256 || d.K % 64) return run2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, true>(k, d, s);
       if (d.batch == 1 && d.splits == 1 && kUseGemm4) {
         bool done = false;
         POETX_TRY(run4(k, d, s, &done));

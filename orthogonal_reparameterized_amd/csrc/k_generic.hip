@@ -900,6 +900,55 @@ __global__ void k_fill_one(void *out, int64_t n, int bf) {
   else ((float *)out)[i] = 1.f;
 }
 
+// ==================================================== padded CNP blocks ====
+// A b x b block embedded in a bp x bp one (bp > b) with zeros elsewhere: Q_p = diag(Q, 0),
+// so G_p = diag(G, I) and, for dG_p = diag(dG, 0), the packed gradient of Q_p restricted
+// to the entries r < c < b is the packed gradient of Q.  One workgroup per row r of a
+// padded block z, its lanes over the columns:
+//   CNP_PAD_THETA : packed theta (esize 4 or 2) of size b -> of size bp (zeros past b)
+//   CNP_CUT_G     : G [b][b] <- G_p [bp][bp] (esize 4 or 2)
+//   CNP_PAD_DG    : dG [b][b] fp32 -> dG_p [bp][bp] (zeros past b)
+//   CNP_CUT_DTHETA: packed dtheta fp32 of size bp -> of size b
+namespace {
+__device__ inline int64_t tri_at(int64_t B, int64_t r, int64_t c) { return r * (B - 1) - r * (r - 1) / 2 + (c - r - 1); }
+template <typename T>
+__global__ __launch_bounds__(64) void k_cnp_pad(int mode, int b, int bp, const T *__restrict__ in,
+                                                T *__restrict__ out) {
+  const int64_t z = blockIdx.x / bp;
+  const int r = (int)(blockIdx.x % bp);
+  const int64_t pb = (int64_t)b * (b - 1) / 2, pbp = (int64_t)bp * (bp - 1) / 2;
+  switch (mode) {
+    case CNP_PAD_THETA:
+      for (int c = r + 1 + (int)threadIdx.x; c < bp; c += 64)
+        out[z * pbp + tri_at(bp, r, c)] = c < b ? in[z * pb + tri_at(b, r, c)] : (T)0;
+      break;
+    case CNP_CUT_G:
+      if (r < b)
+        for (int c = threadIdx.x; c < b; c += 64) out[(z * b + r) * b + c] = in[(z * bp + r) * bp + c];
+      break;
+    case CNP_PAD_DG:
+      for (int c = threadIdx.x; c < bp; c += 64)
+        out[(z * bp + r) * bp + c] = r < b && c < b ? in[(z * b + r) * b + c] : (T)0;
+      break;
+    default:  // CNP_CUT_DTHETA
+      if (r < b)
+        for (int c = r + 1 + (int)threadIdx.x; c < b; c += 64) out[z * pb + tri_at(b, r, c)] = in[z * pbp + tri_at(bp, r, c)];
+      break;
+  }
+}
+}  // namespace
+
+int cnp_pad(int mode, int64_t n, int64_t b, int64_t bp, int esize, const void *in, void *out, hipStream_t s) {
+  if (n <= 0) return POETX_OK;
+  if (bp <= b || n * bp > 0x7fffffff || (esize != 2 && esize != 4)) return POETX_ERR_UNSUPPORTED;
+  const unsigned grid = (unsigned)(n * bp);
+  if (esize == 2)
+    return launch_k("cnp_pad", s, k_cnp_pad<uint16_t>, grid, 64, 0, mode, (int)b, (int)bp, (const uint16_t *)in,
+                    (uint16_t *)out);
+  return launch_k("cnp_pad", s, k_cnp_pad<uint32_t>, grid, 64, 0, mode, (int)b, (int)bp, (const uint32_t *)in,
+                  (uint32_t *)out);
+}
+
 int fill_one(void *out, int64_t n, int dt, hipStream_t s) {
   if (n <= 0) return POETX_OK;
   return launch_k("fill_one", s, k_fill_one, (unsigned)cdiv(n, 256), 256, 0, out, n, dt == POETX_BF16 ? 1 : 0);

@@ -87,6 +87,12 @@ int lincomb(float *out, int64_t n, int64_t b, float cI, const float *X0, float c
             hipStream_t s);
 // out[e] = sum_{p < parts} in[p * stride + e], in a fixed order (deterministic)
 int fill_one(void *out, int64_t n, int dt, hipStream_t s);  // n values 1 (F32 or BF16)
+// n blocks of size b embedded in blocks of size bp > b, zeros elsewhere, and back (the
+// CNP of a block size without MFMA kernels runs at bp): modes below, esize 4 or 2 for the
+// theta and G copies, 4 for dG and dtheta.
+enum { CNP_PAD_THETA = 0, CNP_CUT_G = 1, CNP_PAD_DG = 2, CNP_CUT_DTHETA = 3 };
+int cnp_pad(int mode, int64_t n, int64_t b, int64_t bp, int esize, const void *in, void *out, hipStream_t s);
+
 int reduce_parts(const float *in, float *out, int64_t elems, int64_t parts, int64_t stride,
                  hipStream_t s);
 

@@ -47,14 +47,17 @@ def _say(*a):
 
 # b = 64..512 run the row-panel kernels (the forward chain, the five-product backward;
 # n = 11 and 19 also cover the blocks past the last full group of 8 in the workgroup order),
-# b = 192 the per-product MFMA path, b = 32 and 48 the float32 vector-ALU path
+# b = 192 the per-product MFMA path, b = 100, 200 and 300 the row-panel kernels on blocks
+# padded to 128, 256 and 512, b = 32 and 48 the float32 vector-ALU path
 CNP_CASES = [(8, 32, 0.02), (11, 64, 0.03), (19, 128, 0.02), (3, 192, 0.01), (3, 256, 0.01),
              (2, 512, 0.01), (2, 1024, 0.005),
              # enough blocks for the 64-row panels (4 workgroups per CU): 517 = 8 * 64 + 5
              # also leaves blocks past the last full group of 8
              (517, 128, 0.02), (256, 256, 0.01),
              # more blocks of 256 and 512 (several rounds of workgroups)
-             (600, 256, 0.01), (40, 512, 0.01)]
+             (600, 256, 0.01), (40, 512, 0.01),
+             # block sizes without kernels of their own (padded blocks)
+             (3, 100, 0.02), (9, 200, 0.01), (2, 300, 0.01)]
 
 
 @pytest.mark.parametrize("n,b,std", CNP_CASES + [(5, 48, 0.05)])
@@ -66,7 +69,7 @@ def test_cnp_forward_f32(B, n, b, std):
     assert rel_fro_per_block(to_host_f64(g), ref) <= TOL_CNP_F32
 
 
-@pytest.mark.parametrize("n,b", [(9, 64), (4, 128), (4, 256), (2, 512)])
+@pytest.mark.parametrize("n,b", [(9, 64), (4, 128), (4, 256), (2, 512), (3, 160)])
 def test_cnp_forward_bf16_ulp(B, n, b):
     _say(f"cnp fwd bf16 n={n} b={b}")
     theta, _ = WL.make_cnp_inputs(n, b, 0.01, seed=200 + b)
@@ -162,8 +165,8 @@ def test_cnp_saved_q_is_transparent(B, n, b):
     """poetx_cnp's qsave (Q's planes kept by the forward, read by the backward instead of
     unpacking theta again) changes nothing: G and dtheta are bitwise those of calls without
     it, on the row-panel paths (40 blocks of 256: 32-row panels; 600: 64-row panels;
-    b = 64, 512), and where qsave is ignored (b = 96 and 48, which take the
-    per-product and the vector-ALU paths)."""
+    b = 64, 512), and where qsave is ignored (b = 96 and 48, which take the padded
+    row-panel and the vector-ALU paths)."""
     _say(f"cnp saved Q n={n} b={b}")
     theta, dg = WL.make_cnp_inputs(n, b, 0.01, seed=900 + b)
     th = torch.from_numpy(theta).cuda()
@@ -384,7 +387,8 @@ SMALL_BF16 = [
     (130, 1024, 512, 512, True),
     (64, 256, 256, 128, False),
     (1, 384, 256, 128, True),
-    # b = 64: streaming block kernels at 64 columns, W' products on MFMA (or, at 576, not)
+    # b = 64: streaming block kernels at 64 columns, W' products on MFMA (at 576 and 320 on
+    # the tail form of the NT kernel)
     (257, 512, 768, 64, True),
     (130, 576, 320, 64, True),
     (33, 256, 256, 64, False),
@@ -412,7 +416,8 @@ def test_layer_bf16_transposed_weight(B, n, d_in, d_out, b):
 
 
 def test_layer_bf16_generic_block(B):
-    """b = 48 (not a multiple of 128) goes through the vector-ALU path."""
+    """b = 48 (not a multiple of 128): vector-ALU block products and CNP; the W' products
+    (96 and 144 wide) on the NT kernel's tail form."""
     wl = WL.Workload(91, "small bf16 b48", 70, 96, 144, 48, "bf16", "bf16", "bf16", 0.02, 96)
     inp = WL.make_layer_inputs(wl)
     ref = oracle_layer(inp, wl)
@@ -424,8 +429,12 @@ RAGGED = [
     # (n_tokens, d_in, d_out, b, dtype): ceil(d/b) blocks, the last one smaller
     (257, 640, 896, 256, "bf16"),   # last blocks 128 | 128 on the MFMA kernels
     (100, 384, 640, 512, "bf16"),   # input side narrower than b (one block of 384)
-    (70, 576, 320, 256, "bf16"),    # 128 does not divide d_in: vector-ALU W' products; the
-                                    # 256-blocks and the last blocks of 64 on the MFMA block kernels
+    (70, 576, 320, 256, "bf16"),    # 128 does not divide d_in: the W' products on the NT
+                                    # kernel's tail form; the 256-blocks and the last blocks of
+                                    # 64 on the MFMA block kernels
+    (777, 1000, 2040, 256, "bf16"), # neither width tiles: a k tail (40, 56) and a partial
+                                    # n tile in both W' products; last blocks 232 | 248
+    (300, 1288, 776, 64, "bf16"),   # b = 64 with last blocks of 8
     (64, 200, 150, 32, "f32"),      # last blocks 8 | 22
     (33, 97, 70, 32, "f32"),        # a last block of size 1 (no parameters) | 6
 ]
