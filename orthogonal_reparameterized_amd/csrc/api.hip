@@ -464,6 +464,12 @@ struct Plan {
 // bs is 64 or a multiple of 128 (the streaming kernels, or the batched MFMA engines for
 // other multiples of 128); every other size on the float32 vector-ALU product.
 bool blk_mfma(const Plan &p, int64_t bs) { return p.act == POETX_BF16 && (bs == 64 || bs % 128 == 0); }
+// A lone bf16 block (a side's last block) of another size that is a multiple of 8: its
+// products and gradient take the tail forms of the 128 x 128 MFMA block kernels where the
+// operands are 16-byte aligned, else the vector-ALU product.
+bool lone_block(const Plan &p, int64_t nb, int64_t bs) {
+  return p.act == POETX_BF16 && p.gdt == POETX_BF16 && nb == 1 && !blk_mfma(p, bs) && bs % 8 == 0;
+}
 
 int validate(const poetx_layer *L, int64_t n_tokens, Plan &p) {
   if (!L || n_tokens < 0) return POETX_ERR_INVALID_ARG;
@@ -541,6 +547,18 @@ int apply_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *
     m.role = transposed ? MFMA_BLOCK_APPLY_T : MFMA_BLOCK_APPLY;
     return gemm_mfma_best(m, s);
   }
+  if (lone_block(p, nb, bs)) {
+    // a last block of a size with no block kernel: the tail form of the 128 x 128 kernels
+    MfmaDesc m;
+    m.M = p.N; m.N = bs; m.K = bs;
+    m.A = X; m.a_km = false; m.lda = ld;
+    m.B = G; m.b_km = !transposed; m.b_dt = POETX_BF16; m.ldb = bs;
+    m.C = Y; m.c_dt = p.act; m.ldc = ld;
+    m.scaleN = scaleN;
+    m.name = transposed ? "block_apply_t" : "block_apply";
+    m.role = transposed ? MFMA_BLOCK_APPLY_T : MFMA_BLOCK_APPLY;
+    if (mfma2_supported(m)) return gemm_mfma2(m, s);
+  }
   GemmDesc g;
   g.M = p.N; g.N = bs; g.K = bs; g.batch = nb;
   g.A = X; g.a_dt = p.act; g.sAb = bs; g.sAm = ld; g.sAk = 1;
@@ -587,7 +605,7 @@ bool grad_engine(const Plan &p, int64_t bs) { return blk_mfma(p, bs) && bs % 128
 
 int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of the split-k kernel
   if (p.N == 0) return 1;
-  if (!grad_engine(p, bs)) {
+  if (!grad_engine(p, bs) && !lone_block(p, nb, bs)) {
     // vector-ALU product: chunks of 1024 tokens keep each float32 accumulation short (a sum
     // over millions of tokens in one chain loses digits), with at most 4096 partials and
     // 256 MB of them.  A single block (the last, smaller block of a side) runs all its
@@ -602,7 +620,7 @@ int64_t grad_chunk(const Plan &p, int64_t nb, int64_t bs) {  // token chunk of t
   // about one round of workgroups: 256 x 256 tiles where b allows (fp32 partials of a
   // whole b x b per split, so no more splits than the CUs need)
   const int64_t t = bs % 256 == 0 ? 256 : 128;
-  const int64_t tiles = nb * (bs / t) * (bs / t);
+  const int64_t tiles = nb * cdiv(bs, t) * cdiv(bs, t);
   const int cus = device_cus() > 0 ? device_cus() : 256;
   const int64_t want = t == 256 ? (cus / tiles > 1 ? cus / tiles : 1) : cdiv(512, tiles);
   int64_t kc = cdiv(cdiv(p.N, want), 64) * 64;
@@ -621,7 +639,7 @@ int grad_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *X
   if (nb == 0) return POETX_OK;
   if (grad_streams(p, ld, nb, bs))
     return block_grad_stream((const bf16_t *)X, (const bf16_t *)Y, parts, p.N, ld, nb, bs, s);
-  if (grad_engine(p, bs)) {
+  if (grad_engine(p, bs) || lone_block(p, nb, bs)) {
     const int64_t kc = grad_chunk(p, nb, bs);
     MfmaDesc m;
     m.M = bs; m.N = bs; m.K = p.N; m.batch = nb;
@@ -631,7 +649,9 @@ int grad_blocks(const Plan &p, int64_t ld, int64_t nb, int64_t bs, const void *X
     m.C = parts; m.c_dt = POETX_F32; m.ldc = bs; m.sCb = bs * bs; m.sCsplit = nb * bs * bs;
     m.name = "block_grad";
     m.role = MFMA_BLOCK_GRAD;
-    return gemm_mfma_best(m, s);
+    if (grad_engine(p, bs)) return gemm_mfma_best(m, s);
+    if (mfma2_supported(m)) return gemm_mfma2(m, s);
+    // an unaligned lone block: the vector-ALU product below, with the same token chunks
   }
   // vector-ALU product into partial c of [P][nb][bs][bs]: one launch per token chunk (a
   // batch over the blocks), or for a single block one launch over its whole chunks (a

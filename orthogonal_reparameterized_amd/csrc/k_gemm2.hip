@@ -142,15 +142,16 @@ __device__ inline void tail_store(const f32x4 (&acc)[FM][FN], const G2Args &a, i
 // MFMA covers k = 16g + 8h + 0..7, so one 16-byte LDS read of a B row (k = 16g .. +15)
 // feeds both MFMAs of the step, and the A reads take bf16 chunk 2g + h.
 //
-// TAIL (k-contiguous bf16 operands): N need not be a multiple of BN nor K of BKT, only of 8.
-// The last n tile's columns past N are not stored (W' rows past N read as zero through the
-// buffer range), and the last k step's chunks past K, which the loads fill from the next
-// rows, are zeroed in LDS before they are read.
+// TAIL (bf16 operands, batch 1): M, N and K need only be multiples of 8.  Rows past M and
+// columns past N are not stored; a k-contiguous operand's last k step has its chunks past K,
+// which the loads fill from the next rows, zeroed in LDS before they are read, while a
+// k-major operand's rows past K read as zero through the buffer range.  Operand rows or
+// columns past M or N only reach outputs that are not stored.
 template <int ROLE, int BM, int BN, int WGM, int WGN, int BKT, int NST, bool AKM, bool BKM, bool OUTF32,
           bool BI8 = false, bool TAIL = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
   static_assert(!BI8 || (!AKM && !BKM && BKT == 64), "int8 B: k-contiguous operands, 64-deep steps");
-  static_assert(!TAIL || (!AKM && !BKM && !BI8), "tails: k-contiguous bf16 operands");
+  static_assert(!TAIL || !BI8, "tails: bf16 operands");
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 16, FN = WTN / 16;
   constexpr int EB = BI8 ? 1 : 2;  // bytes per B element
@@ -233,17 +234,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm2(G2Args a) {
       else __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // everyone's stage t is in LDS; stage t-1 is no longer read
       if (!LATE && t + PF < nk) issue((t + PF) % NST, kbeg + (int64_t)(t + PF) * BKT);
-      if constexpr (TAIL) {
+      if constexpr (TAIL && (!AKM || !BKM)) {
         const int kr = (int)(kend - kbeg - (int64_t)t * BKT);  // valid k of this step
         if (kr < BKT) {
+          // the k-contiguous tiles' chunks past K (k-major tiles are zero there already)
           bf16_t *za = smem + (t % NST) * A_ELEMS, *zb = smem + NST * A_ELEMS + (t % NST) * B_ELEMS;
-          constexpr int CR = BKT / 8;
+          constexpr int CR = BKT / 8, RA = AKM ? 0 : BM, RB = BKM ? 0 : BN;
           const int c0 = kr / 8;
-          for (int q = threadIdx.x; q < (BM + BN) * CR; q += 64 * NW) {
+          for (int q = threadIdx.x; q < (RA + RB) * CR; q += 64 * NW) {
             const int r = q / CR, c = q % CR;
             if (c < c0) continue;
-            bf16_t *row = r < BM ? za + r * BKT : zb + (r - BM) * BKT;
-            const int rr = r < BM ? r : r - BM;
+            bf16_t *row = r < RA ? za + r * BKT : zb + (r - RA) * BKT;
+            const int rr = r < RA ? r : r - RA;
             *(uint4 *)(row + (c ^ kc_key<BKT>(rr)) * 8) = make_uint4(0u, 0u, 0u, 0u);
           }
           __syncthreads();
@@ -820,6 +822,9 @@ POETX_G2_INST(MFMA_BLOCK_GRAD, 256, 256, 2, 4, 64, 2, true, true)
 #undef POETX_G2_INST
 template __global__ void k_gemm2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, true>(G2Args);
 template __global__ void k_gemm2<MFMA_GEMM_NT, 256, 256, 2, 4, 64, 2, false, false, false, false, true>(G2Args);
+template __global__ void k_gemm2<MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true, false, false, true>(G2Args);
+template __global__ void k_gemm2<MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false, false, false, true>(G2Args);
+template __global__ void k_gemm2<MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true, true, false, true>(G2Args);
 template __global__ void k_gemm4<POETX_G4_WGM, POETX_G4_WGN, POETX_G4_BK, POETX_G4_NST>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, false>(G2Args);
 template __global__ void k_gemm_pp<MFMA_GEMM_NN, false, true, true>(G2Args);
@@ -935,7 +940,7 @@ static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
   size_t lds = (size_t)NST * (BM * 2 + BN * (BI8 ? 1 : 2)) * BKT;
   if (BM == 256 && BN == 256 && POETX_EPI_LDS && lds < (size_t)BM * (BN * 2 + 16))
     lds = (size_t)BM * (BN * 2 + 16);  // the staged bf16 epilogue tile
-  if (TAIL ? (d.M <= 0 || d.N % 8 || d.K % 8 || d.batch != 1 || d.splits != 1)
+  if (TAIL ? (d.M <= 0 || d.N % 8 || d.K % 8 || d.batch != 1 || (ROLE == MFMA_BLOCK_GRAD && d.M % 8))
            : (d.M <= 0 || d.N % BN || (d.K % BKT && (!AKM || !BKM))))
     return POETX_ERR_UNSUPPORTED;
   G2Args a = k;
@@ -949,9 +954,15 @@ static int run2(const G2Args &k, const MfmaDesc &d, hipStream_t s) {
     POETX_TRY((run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false, true>(a, d.name, grid, lds, s)));
     return tail_reduce(a, d, s);
   }
-  if constexpr (TAIL) {  // bf16 results, whole-k tiles only (plan_tail splits none of these shapes)
-    if (d.c_dt != POETX_BF16 || a.full_tiles != a.tiles_m * a.tiles_n) return POETX_ERR_UNSUPPORTED;
-    return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false, false, true>(a, d.name, grid, lds, s);
+  if constexpr (TAIL) {  // whole-k tiles only (plan_tail splits none of these shapes)
+    if (a.full_tiles != a.tiles_m * a.tiles_n) return POETX_ERR_UNSUPPORTED;
+    if constexpr (ROLE == MFMA_BLOCK_GRAD) {  // fp32 partials
+      if (d.c_dt != POETX_F32) return POETX_ERR_UNSUPPORTED;
+      return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, true, false, true>(a, d.name, grid, lds, s);
+    } else {  // bf16 products
+      if (d.c_dt != POETX_BF16) return POETX_ERR_UNSUPPORTED;
+      return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false, false, true>(a, d.name, grid, lds, s);
+    }
   } else {
     if (d.c_dt == POETX_F32) return run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, true>(a, d.name, grid, lds, s);
     POETX_TRY((run2o<ROLE, BM, BN, WGM, WGN, BKT, NST, AKM, BKM, false>(a, d.name, grid, lds, s)));
@@ -989,11 +1000,19 @@ bool mfma2_supported(const MfmaDesc &d) {
   if (d.c_dt != POETX_BF16 && d.c_dt != POETX_F32) return false;
   if (d.splits < 1 || d.batch * d.splits > 65535) return false;
   if (d.splits > 1 && (d.kchunk <= 0 || d.kchunk % 64 || cdiv(d.K, d.kchunk) != d.splits)) return false;
-  // W' products whose widths do not tile (multiples of 8): the TAIL form of the NT kernel
-  const bool tail = d.role == MFMA_GEMM_NT && !d.a_km && !d.b_km && (d.N % 256 || d.K % 64);
+  // shapes that do not tile (multiples of 8), batch 1: the TAIL forms of the NT kernel (W'
+  // products, bf16 results) and of the 128 x 128 block kernels (a last block of a size with
+  // no block kernel: its products, bf16, and its gradient, fp32 parts)
+  const bool tail = d.batch == 1 &&
+                    ((d.role == MFMA_GEMM_NT && !d.a_km && !d.b_km && (d.N % 256 || d.K % 64)) ||
+                     (d.role == MFMA_BLOCK_APPLY && !d.a_km && d.b_km && (d.N % 128 || d.K % 64)) ||
+                     (d.role == MFMA_BLOCK_APPLY_T && !d.a_km && !d.b_km && (d.N % 128 || d.K % 64)) ||
+                     (d.role == MFMA_BLOCK_GRAD && d.a_km && d.b_km && (d.M % 128 || d.N % 128)));
   if (tail) {
-    if (d.b_dt != POETX_BF16 || d.c_dt != POETX_BF16 || d.batch != 1 || d.splits != 1) return false;
+    if (d.b_dt != POETX_BF16) return false;
+    if (d.role == MFMA_BLOCK_GRAD ? d.c_dt != POETX_F32 : (d.c_dt != POETX_BF16 || d.splits != 1)) return false;
     if (d.N % 8 || d.K % 8 || d.lda % 8 || d.ldb % 8 || d.ldc % 8) return false;
+    if (d.role == MFMA_BLOCK_GRAD && d.M % 8) return false;
     if ((((uintptr_t)d.A | (uintptr_t)d.B | (uintptr_t)d.C) & 15) != 0) return false;
   } else if ((!d.a_km || !d.b_km) && d.K % 64) {
     return false;
@@ -1004,7 +1023,7 @@ bool mfma2_supported(const MfmaDesc &d) {
   switch (d.role) {
     case MFMA_GEMM_NT: return (tail || d.N % 256 == 0) && cdiv(d.M, 256) * cdiv(d.N, 256) < (1 << 30);
     case MFMA_GEMM_NN: return d.N % 256 == 0 && cdiv(d.M, 256) * (d.N / 256) < (1 << 30);
-    default: return d.N % 128 == 0 && (!d.a_km || d.M % 128 == 0);
+    default: return tail || (d.N % 128 == 0 && (!d.a_km || d.M % 128 == 0));
   }
 }
 
@@ -1041,12 +1060,15 @@ int gemm_mfma2(const MfmaDesc &d, hipStream_t s) {
       return run_pp<MFMA_GEMM_NN, false, true>(k, d, s);
     case MFMA_BLOCK_APPLY:
       if (d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
+      if (d.N % 128 || d.K % 64) return run2<MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true, false, true>(k, d, s);
       return run2<MFMA_BLOCK_APPLY, 128, 128, 2, 2, 64, 2, false, true>(k, d, s);
     case MFMA_BLOCK_APPLY_T:
       if (d.a_km || d.b_km) return POETX_ERR_UNSUPPORTED;
+      if (d.N % 128 || d.K % 64) return run2<MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false, false, true>(k, d, s);
       return run2<MFMA_BLOCK_APPLY_T, 128, 128, 2, 2, 64, 2, false, false>(k, d, s);
     case MFMA_BLOCK_GRAD:
       if (!d.a_km || !d.b_km) return POETX_ERR_UNSUPPORTED;
+      if (d.M % 128 || d.N % 128) return run2<MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true, false, true>(k, d, s);
       // blocks of a multiple of 256: 256 x 256 tiles, each operand slice read by two of them
       if (d.M % 256 == 0 && d.N % 256 == 0) return run2<MFMA_BLOCK_GRAD, 256, 256, 2, 4, 64, 2, true, true>(k, d, s);
       return run2<MFMA_BLOCK_GRAD, 128, 128, 2, 2, 64, 2, true, true>(k, d, s);
