@@ -183,7 +183,10 @@ size_t cnp_ws_bytes(int dir, int64_t n, int64_t b) {
     const size_t pk = (size_t)n * (bp * (bp - 1) / 2) * 4, sq = (size_t)n * bp * bp * 4;
     ar.take(pk);                                   // padded theta
     ar.take(sq);                                   // padded G, or padded dG
-    if (dir == POETX_CNP_BWD) ar.take(pk);         // padded dtheta
+    if (dir == POETX_CNP_BWD) {
+      ar.take(pk);                                 // padded dtheta
+      ar.take((size_t)n * (b * (b - 1) / 2) * 4);  // dtheta for a fused update without one
+    }
     ar.take(cnp_ws_bytes(dir, n, bp));
     return ar.used;
   }
@@ -320,10 +323,11 @@ int cnp_bwd5_path(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, 
 
 int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, const AdamEpi *h, void *ws,
                  hipStream_t s) {
-  if (const int64_t bp = h ? 0 : cnp_pad_to(b)) {
-    // padded blocks (the fused Adam update keeps the vector-ALU path below)
+  if (const int64_t bp = cnp_pad_to(b)) {
+    // padded blocks; a fused Adam update then runs as its own pass on the cut-out dtheta
     Arena ar(ws);
     CnpBwdSide ps[2];
+    float *dt[2] = {nullptr, nullptr};
     int64_t nall = 0;
     for (int i = 0; i < nside; ++i) {
       const int64_t n = side[i].n;
@@ -331,13 +335,24 @@ int cnp_bwd_impl(int64_t b, const CnpBwdSide *side, int nside, int theta_bf16, c
       void *tp = ar.take((size_t)n * (bp * (bp - 1) / 2) * 4);
       void *dgp = ar.take((size_t)n * bp * bp * 4);
       void *dtp = ar.take((size_t)n * (bp * (bp - 1) / 2) * 4);
+      float *own = (float *)ar.take((size_t)n * (b * (b - 1) / 2) * 4);
+      dt[i] = side[i].dtheta ? side[i].dtheta : own;
       POETX_TRY(cnp_pad(CNP_PAD_THETA, n, b, bp, theta_bf16 ? 2 : 4, side[i].theta, tp, s));
       POETX_TRY(cnp_pad(CNP_PAD_DG, n, b, bp, 4, side[i].dg, dgp, s));
       ps[i].n = n; ps[i].theta = tp; ps[i].dg = (const float *)dgp; ps[i].dtheta = (float *)dtp;
     }
     POETX_TRY(cnp_bwd_impl(bp, ps, nside, theta_bf16, nullptr, ar.take(cnp_ws_bytes(POETX_CNP_BWD, nall, bp)), s));
-    for (int i = 0; i < nside; ++i)
-      POETX_TRY(cnp_pad(CNP_CUT_DTHETA, side[i].n, b, bp, 4, ps[i].dtheta, side[i].dtheta, s));
+    for (int i = 0; i < nside; ++i) {
+      POETX_TRY(cnp_pad(CNP_CUT_DTHETA, side[i].n, b, bp, 4, ps[i].dtheta, dt[i], s));
+      if (!h) continue;
+      const int64_t np = side[i].n * (b * (b - 1) / 2);
+      if (side[i].theta_out != side[i].theta &&
+          hipMemcpyAsync(side[i].theta_out, side[i].theta, (size_t)np * (theta_bf16 ? 2 : 4), hipMemcpyDeviceToDevice,
+                         s) != hipSuccess)
+        return POETX_ERR_HIP;
+      POETX_TRY(adam_step(np, side[i].theta_out, theta_bf16 ? POETX_BF16 : POETX_F32, dt[i], side[i].m, side[i].v,
+                          *h, s));
+    }
     return POETX_OK;
   }
   // the chain and MFMA paths read dG with vector loads: an only element-aligned dG

@@ -54,7 +54,7 @@ def _bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-@pytest.mark.parametrize("n,b", [(11, 64), (5, 256), (2, 512), (6, 48)])
+@pytest.mark.parametrize("n,b", [(11, 64), (5, 256), (2, 512), (6, 48), (3, 160)])
 def test_cnp_bf16_theta(B, n, b):
     """CNP forward (fp32 and bf16 G) and backward from a bf16 theta: the oracle on the same
     (exactly widened) values."""
@@ -187,6 +187,9 @@ FUSED = [
     ((257, 512, 768, 256, "bf16"), "f32"),
     ((257, 512, 768, 256, "bf16"), "bf16"),
     ((130, 640, 896, 256, "bf16"), "f32"),
+    # last blocks of 232 and 248 (padded CNP blocks; the update as its own pass)
+    ((200, 1000, 2040, 256, "bf16"), "f32"),
+    ((200, 1000, 2040, 256, "bf16"), "bf16"),
     ((64, 256, 256, 32, "f32"), "f32"),
 ]
 
