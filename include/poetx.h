@@ -143,7 +143,8 @@ int poetx_merge_perm(const void *w, const float *w_scale, int32_t w_dtype, int64
  *     ([n][b][b], dg_dtype F32), the exact adjoint of eq. 9 (the page leaves
  *     its eq. 10 unprinted); g unused.
  * Products are evaluated to float32 accuracy (split-bf16 MFMA passes), whatever
- * g_dtype is.  Workspace: query with ws == NULL.  A layer whose b does not divide a
+ * g_dtype is; a b between 64 and 512 that is not a multiple of 64 runs on blocks padded
+ * to 128, 256 or 512 (Q embedded as diag(Q, 0), which leaves G and dtheta exact).  Workspace: query with ws == NULL.  A layer whose b does not divide a
  * width calls this once for the side's full blocks and once for its last block (at
  * that block's size).  theta, dtheta, g and dg need only be aligned to their element
  * size (a last block sits at an offset of whole blocks); g and dg that are not
