@@ -435,6 +435,7 @@ RAGGED = [
     (777, 1000, 2040, 256, "bf16"), # neither width tiles: a k tail (40, 56) and a partial
                                     # n tile in both W' products; last blocks 232 | 248
     (300, 1288, 776, 64, "bf16"),   # b = 64 with last blocks of 8
+    (513, 4000, 3000, 256, "bf16"), # many tiles with k and n tails; last blocks 160 | 184
     (64, 200, 150, 32, "f32"),      # last blocks 8 | 22
     (33, 97, 70, 32, "f32"),        # a last block of size 1 (no parameters) | 6
 ]
